@@ -1,0 +1,208 @@
+"""fp64 oracle: ctypes wrapper of kda_oracle.c plus a NumPy twin.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+# Gate floor and tile length ("Kimi K3 internal structure analysis", section
+# "Sequence mixing: 3 KDA layers per global MLA layer": gmin = -5; the
+# cumulative log-decay of a 16-token tile stays inside (-80, 0)).
+GMIN = -5.0
+TILE = 16
+
+_lib_handle = None
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile kda_oracle.c into libkda_oracle.so with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB):
+            build_oracle(force=True)
+        L = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        L.kda_oracle_gate.argtypes = [dp, dp, dp, i64, i64, i64, i64]
+        L.kda_oracle_gate.restype = None
+        L.kda_oracle_forward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                         i64, i64, i64, i64, i64, i64, ctypes.c_int]
+        L.kda_oracle_forward.restype = None
+        L.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                             i64, i64, i64, i64]
+        L.kda_oracle_decode_step.restype = None
+        L.kda_oracle_max_threads.argtypes = []
+        L.kda_oracle_max_threads.restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def _f64(x) -> np.ndarray:
+    """Any tensor/array -> C-contiguous float64 numpy array (exact for bf16/fp32)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+        x = x.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def max_threads() -> int:
+    return int(_lib().kda_oracle_max_threads())
+
+
+def rho(x, ref) -> float:
+    """Parity metric max|x - ref| / max|ref| (whole tensor)."""
+    x = _f64(x)
+    ref = _f64(ref)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den
+
+
+# ----------------------------------------------------------------------------
+# C oracle wrappers
+# ----------------------------------------------------------------------------
+
+def gate(z, A) -> np.ndarray:
+    """g = -5 sigmoid(exp(A) z); z [B,T,H,dk] (or [N,H,dk]), A [H,dk]."""
+    z = _f64(z)
+    A = _f64(A)
+    H, dk = A.shape
+    assert z.shape[-1] == dk and z.shape[-2] == H
+    rows = int(np.prod(z.shape[:-2])) if z.ndim > 2 else 1
+    g = np.empty_like(z)
+    _lib().kda_oracle_gate(_ptr(z), _ptr(A), _ptr(g), 1, rows, H, dk)
+    return g
+
+
+def forward(q, k, v, g, beta, S0=None, want_o: bool = True,
+            col_block: Optional[int] = None, nthreads: int = 0
+            ) -> Tuple[Optional[np.ndarray], np.ndarray]:
+    """Token-by-token fp64 recurrence.  Returns (o [B,T,H,dv] or None, S_T [B,H,dk,dv])."""
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape == g.shape and v.shape == (B, T, H, dv)
+    assert beta.shape == (B, T, H)
+    S0 = _f64(S0)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, T, H, dv)) if want_o else None
+    ST = np.empty((B, H, dk, dv))
+    if col_block is None:
+        col_block = dv
+    _lib().kda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                              _ptr(o), _ptr(ST), B, T, H, dk, dv, int(col_block),
+                              int(nthreads))
+    return o, ST
+
+
+def decode_step(q, k, v, z, A, beta, state) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step.  Returns (o [N,H,dv], new state [N,H,dk,dv]); inputs untouched."""
+    q, k, v, z, A, beta = (_f64(x) for x in (q, k, v, z, A, beta))
+    S = _f64(state).copy()
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    o = np.empty((N, H, dv))
+    _lib().kda_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta),
+                                  _ptr(S), _ptr(o), N, H, dk, dv)
+    return o, S
+
+
+# ----------------------------------------------------------------------------
+# NumPy twin (plain loops over tokens; for small cases and cross-checks)
+# ----------------------------------------------------------------------------
+
+def _sigmoid_np(x: np.ndarray) -> np.ndarray:
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def gate_np(z, A) -> np.ndarray:
+    z = _f64(z)
+    A = _f64(A)
+    return GMIN * _sigmoid_np(np.exp(A) * z)
+
+
+def forward_np(q, k, v, g, beta, S0=None) -> Tuple[np.ndarray, np.ndarray]:
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    S0 = _f64(S0)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[b, h].copy()
+            for t in range(T):
+                S = np.exp(g[b, t, h])[:, None] * S          # retention first
+                u = beta[b, t, h] * (v[b, t, h] - S.T @ k[b, t, h])
+                S = S + np.outer(k[b, t, h], u)              # delta-rule write
+                o[b, t, h] = S.T @ q[b, t, h]                # post-update read
+            ST[b, h] = S
+    return o, ST
+
+
+def decode_step_np(q, k, v, z, A, beta, state) -> Tuple[np.ndarray, np.ndarray]:
+    q, k, v, z, beta = (_f64(x) for x in (q, k, v, z, beta))
+    S = _f64(state).copy()
+    g = gate_np(z, A)
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv))
+    for n in range(N):
+        for h in range(H):
+            Sh = np.exp(g[n, h])[:, None] * S[n, h]
+            u = beta[n, h] * (v[n, h] - Sh.T @ k[n, h])
+            Sh = Sh + np.outer(k[n, h], u)
+            o[n, h] = Sh.T @ q[n, h]
+            S[n, h] = Sh
+    return o, S
+
+
+def tile_log_decay_sums(g, tile: int = TILE) -> np.ndarray:
+    """Sum of g over each aligned `tile`-token tile, per (b, h, channel).
+
+    g [B,T,H,dk] -> [B, ceil(T/tile), H, dk].  Tiles are aligned to token 0;
+    the last tile may be partial.
+    """
+    g = _f64(g)
+    B, T, H, dk = g.shape
+    nt = (T + tile - 1) // tile
+    pad = nt * tile - T
+    if pad:
+        g = np.concatenate([g, np.zeros((B, pad, H, dk))], axis=1)
+    return g.reshape(B, nt, tile, H, dk).sum(axis=2)
