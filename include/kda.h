@@ -1,0 +1,143 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) forward hot path for AMD MI355X (gfx950).
+ *
+ * KDA is a recurrent linear attention whose fixed-size per-head state
+ * S in R^{dk x dv} replaces a growing KV cache ("Kimi K3 internal structure
+ * analysis", section "Sequence mixing: 3 KDA layers per global MLA layer";
+ * the studioglobal.ai summary of the Kimi K3 report, section on KDA: memory
+ * and decoding work stay fixed as the context grows).  Per token t:
+ *
+ *     g_t   = -5 * sigmoid(exp(A) * z_t)            (gate, floor gmin = -5)
+ *     S'    = Diag(exp(g_t)) S_{t-1}                (channel-wise retention, first)
+ *     u_t   = beta_t (v_t - S'^T k_t)
+ *     S_t   = S' + k_t u_t^T                        (delta-rule write)
+ *     o_t   = S_t^T q_t
+ *
+ * Every entry point takes the state in and hands the state out, so a sequence
+ * can be cut anywhere and resumed (the page's "Infrastructure for a 3T-class
+ * MoE" section: a segment acts on its incoming state and emits a state).
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    row-major in the layouts stated per call, with 16-byte aligned bases.
+ *    The library never allocates or frees device memory.
+ *  - `dtype` selects the element type of q, k, v, z, beta and o:
+ *    KDA_F32 (IEEE fp32) or KDA_BF16 (bfloat16).  A, g and the state are fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work on it and return; faults inside kernels surface at the caller's
+ *    next synchronisation with that stream, as usual in HIP.
+ *  - Return value: KDA_OK or a negative error code.  Host-side validation runs
+ *    before any HIP call, so an invalid call touches no device memory.
+ *    kda_last_error() describes the most recent failure of the calling thread.
+ *  - Sizes: B, T, H, N >= 1; dk, dv in {32, 64, 128}.  fp32 inputs support
+ *    dk in {32, 64} for kda_chunk_fwd (its on-chip tiles for dk = 128 exceed
+ *    the 160 KiB of LDS); every other combination is supported.
+ *  - No scaling or normalisation is applied to q or k; that is the caller's.
+ *  - Concurrent calls that share an output buffer race; the library keeps no
+ *    global state of its own.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = -1, /* null pointer, size <= 0, overflow, misalignment, small workspace */
+    KDA_ERR_UNSUPPORTED = -2,      /* dk/dv outside {32,64,128}, unknown dtype, fp32 with dk = 128 (chunk) */
+    KDA_ERR_HIP = -3,              /* a HIP runtime call or kernel launch failed */
+    KDA_ERR_RANGE = -4             /* KDA_FLAG_CHECK_RANGE found g outside [-5, 0] or a 16-token sum < -80 */
+};
+
+/* Flags for kda_chunk_fwd. */
+enum {
+    /* Before the forward pass, check on the device that every g lies in
+     * [-5, 0] and every 16-token tile sum (tiles aligned to token 0 of the
+     * call) lies in [-80, 0] -- the range the gate's floor guarantees and the
+     * chunked kernel relies on.  Synchronises the stream; debugging only. */
+    KDA_FLAG_CHECK_RANGE = 1u
+};
+
+/*
+ * kda_gate -- the K3 gate, g = -5 * sigmoid(exp(A[h,c]) * z[b,t,h,c]).
+ *   ("Kimi K3 internal structure analysis", section "Sequence mixing: 3 KDA
+ *   layers per global MLA layer": the retention parameterisation with g_min = -5.)
+ *   z : [B, T, H, dk]  dtype            (input)
+ *   A : [H, dk]        fp32             (input)
+ *   g : [B, T, H, dk]  fp32             (output; may not alias z)
+ * The result lies in [-5, 0]; alpha = exp(g) is the per-channel retention.
+ */
+int kda_gate(const void *z, const float *A, float *g,
+             int64_t B, int64_t T, int64_t H, int64_t dk,
+             int dtype, void *stream);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (a small constant; it
+ * holds the range-check counter).  Returns 0 for invalid sizes.
+ */
+size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                    int64_t dk, int64_t dv, int dtype);
+
+/*
+ * kda_chunk_fwd -- chunkwise prefill over T tokens for B x H independent
+ * chains, 64-token chunks built from four 16-token subtiles.
+ *   ("Kimi K3 internal structure analysis", section "Sequence mixing: 3 KDA
+ *   layers per global MLA layer": the gate floor keeps each 16-token tile's
+ *   cumulative log-decay inside (-80, 0), so the diagonal and the
+ *   off-diagonal causal tiles are all dense matrix products.)
+ *   q, k          : [B, T, H, dk] dtype
+ *   v             : [B, T, H, dv] dtype
+ *   g             : [B, T, H, dk] fp32, each value in [-5, 0] (e.g. from kda_gate)
+ *   beta          : [B, T, H]     dtype
+ *   initial_state : [B, H, dk, dv] fp32, or NULL for a zero state
+ *   final_state   : [B, H, dk, dv] fp32, or NULL if not wanted; it may equal
+ *                   initial_state (in-place continuation)
+ *   o             : [B, T, H, dv] dtype (output; must not alias any input)
+ *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size()
+ *                   bytes; required only with KDA_FLAG_CHECK_RANGE (else may be NULL)
+ * Chunks and 16-token tiles are aligned to token 0 of the call; the last
+ * chunk may be partial.  Accumulation and the carried state are fp32.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                  const void *beta, const float *initial_state, float *final_state,
+                  void *o, void *workspace, size_t workspace_bytes,
+                  int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                  int dtype, unsigned flags, void *stream);
+
+/*
+ * kda_decode_step -- one token for each of N independent sequences x H heads,
+ * with the gate fused and the state updated IN PLACE (read once, written once).
+ *   (The studioglobal.ai summary of the Kimi K3 report, KDA section: a
+ *   fixed-size recurrent state, so the work per decoded token does not grow
+ *   with the context.)
+ *   q, k, z : [N, H, dk] dtype
+ *   v       : [N, H, dv] dtype
+ *   beta    : [N, H]     dtype
+ *   A       : [H, dk]    fp32
+ *   state   : [N, H, dk, dv] fp32, read and overwritten with the new state
+ *   o       : [N, H, dv] dtype (output; must not alias any input)
+ */
+int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
+                    const float *A, const void *beta, float *state, void *o,
+                    int64_t N, int64_t H, int64_t dk, int64_t dv,
+                    int dtype, void *stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *kda_last_error(void);
+
+/* Library version string. */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,157 @@
+"""Thin ctypes binding of libkda.so (see include/kda.h for the contract).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_HIP = -3
+KDA_ERR_RANGE = -4
+KDA_FLAG_CHECK_RANGE = 1
+
+EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
+            "kda_last_error", "kda_version")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libkda error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m linear_attention_sequence_gate_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.kda_gate.argtypes = [vp, vp, vp, i64, i64, i64, i64, c_int, vp]
+    L.kda_gate.restype = c_int
+    L.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
+    L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd.restype = c_int
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp]
+    L.kda_decode_step.restype = c_int
+    L.kda_last_error.argtypes = []
+    L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_version.argtypes = []
+    L.kda_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != KDA_OK:
+        raise KdaError(code, load_library().kda_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libkda takes device tensors only")
+            if not t.is_contiguous():
+                raise ValueError("libkda takes contiguous tensors only")
+
+
+def kda_version() -> str:
+    return load_library().kda_version().decode()
+
+
+def kda_last_error() -> str:
+    return load_library().kda_last_error().decode()
+
+
+def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """g = -5 * sigmoid(exp(A) * z).  z [B,T,H,dk] (bf16/fp32), A [H,dk] fp32 -> g fp32."""
+    _dev(z, A, g)
+    B, T, H, dk = z.shape
+    if g is None:
+        g = torch.empty(z.shape, device=z.device, dtype=torch.float32)
+    _check(load_library().kda_gate(_ptr(z), _ptr(A), _ptr(g), B, T, H, dk, _dtype_code(z),
+                                   _stream(stream)))
+    return g
+
+
+def kda_chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                  want_final_state: bool = True, flags: int = 0, workspace=None,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise prefill.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    _dev(q, k, v, g, beta, initial_state, final_state, o, workspace)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, dk, dv), device=q.device, dtype=torch.float32)
+    ws_bytes = 0
+    if workspace is None and (flags & KDA_FLAG_CHECK_RANGE):
+        ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dt)
+        workspace = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
+    elif workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(final_state),
+        _ptr(o), _ptr(workspace), ws_bytes, B, T, H, dk, dv, dt, flags, _stream(stream)))
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, z, A, beta, state, o=None, stream=None) -> torch.Tensor:
+    """One decode step; `state` [N,H,dk,dv] fp32 is updated in place.  Returns o [N,H,dv]."""
+    _dev(q, k, v, z, A, beta, state, o)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), device=q.device, dtype=q.dtype)
+    _check(load_library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(state), _ptr(o),
+        N, H, dk, dv, _dtype_code(q), _stream(stream)))
+    return o

@@ -1,0 +1,174 @@
+// C ABI of libkda: argument validation, error reporting, dispatch to the
+// kernel launchers.  Declarations and the contract live in include/kda.h.
+#include "kda.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dim(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+// a * b * ... without signed overflow, capped well below INT64_MAX
+bool mul_ok(int64_t &acc, int64_t x) {
+    int64_t r;
+    if (__builtin_mul_overflow(acc, x, &r) || r > (int64_t(1) << 60)) return false;
+    acc = r;
+    return true;
+}
+
+int check_dtype(int dtype) {
+    if (dtype != KDA_F32 && dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "unknown dtype %d (expected KDA_F32=0 or KDA_BF16=1)", dtype);
+    return KDA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+const char *kda_version(void) { return "libkda 0.1 (gfx950)"; }
+
+int kda_gate(const void *z, const float *A, float *g, int64_t B, int64_t T, int64_t H, int64_t dk,
+             int dtype, void *stream) {
+    if (int e = check_dtype(dtype)) return e;
+    if (!z || !A || !g) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: null pointer");
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: sizes must be positive");
+    if (!valid_dim(dk)) return fail(KDA_ERR_UNSUPPORTED, "kda_gate: dk=%lld not in {32,64,128}", (long long)dk);
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: element count overflows");
+    if (!aligned16(z) || !aligned16(A) || !aligned16(g))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: pointers must be 16-byte aligned");
+    if (static_cast<const void *>(g) == z)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g must not alias z");
+    hipError_t e = kda::launch_gate(z, A, g, n, (int)H, (int)dk, dtype == KDA_BF16,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_gate launch");
+    return ok();
+}
+
+size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    int dtype) {
+    if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return 256;  // range-check counter (rounded up)
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                  const float *initial_state, float *final_state, void *o, void *workspace,
+                  size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                  int dtype, unsigned flags, void *stream) {
+    if (int e = check_dtype(dtype)) return e;
+    if (!q || !k || !v || !g || !beta || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: null pointer (q, k, v, g, beta, o are required)");
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: sizes must be positive");
+    if (!valid_dim(dk) || !valid_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dk=%lld dv=%lld must be in {32,64,128}",
+                    (long long)dk, (long long)dv);
+    if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs support dk in {32,64} only");
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: unknown flag bits 0x%x", flags);
+    int64_t nk = B, nv = B, ns = B;
+    if (!mul_ok(nk, T) || !mul_ok(nk, H) || !mul_ok(nk, dk) || !mul_ok(nv, T) || !mul_ok(nv, H) ||
+        !mul_ok(nv, dv) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: element count overflows");
+    if (B * H > (int64_t(1) << 24))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: B*H=%lld too large", (long long)(B * H));
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: pointers must be 16-byte aligned");
+    const void *ins[] = {q, k, v, g, beta, initial_state};
+    for (const void *p : ins)
+        if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: o must not alias an input");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (flags & KDA_FLAG_CHECK_RANGE) {
+        if (!workspace || workspace_bytes < kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "kda_chunk_fwd: KDA_FLAG_CHECK_RANGE needs a workspace of %zu bytes",
+                        kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype));
+        unsigned int *bad = static_cast<unsigned int *>(workspace);
+        hipError_t e = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd range check memset");
+        e = kda::launch_range_check(g, B, T, H, dk, bad, s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd range check launch");
+        unsigned int nbad = 0;
+        e = hipMemcpyAsync(&nbad, bad, sizeof nbad, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd range check readback");
+        if (nbad)
+            return fail(KDA_ERR_RANGE,
+                        "kda_chunk_fwd: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]",
+                        nbad);
+    }
+    hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
+                                         (int)dk, (int)dv, dtype == KDA_BF16, s);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+    return ok();
+}
+
+int kda_decode_step(const void *q, const void *k, const void *v, const void *z, const float *A,
+                    const void *beta, float *state, void *o, int64_t N, int64_t H, int64_t dk,
+                    int64_t dv, int dtype, void *stream) {
+    if (int e = check_dtype(dtype)) return e;
+    if (!q || !k || !v || !z || !A || !beta || !state || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: null pointer");
+    if (N <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: sizes must be positive");
+    if (!valid_dim(dk) || !valid_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: dk=%lld dv=%lld must be in {32,64,128}",
+                    (long long)dk, (long long)dv);
+    int64_t ns = N;
+    if (!mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: element count overflows");
+    if (N * H > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: N*H too large");
+    const void *ptrs[] = {q, k, v, z, A, beta, state, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: pointers must be 16-byte aligned");
+    const void *ins[] = {q, k, v, z, A, beta, state};
+    for (const void *p : ins)
+        if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o must not alias an input");
+    hipError_t e = kda::launch_decode_step(q, k, v, z, A, beta, state, o, N, H, (int)dk, (int)dv,
+                                           dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+    return ok();
+}
+
+}  // extern "C"

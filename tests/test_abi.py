@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, and host-side validation rejects bad calls with the
+documented codes before any HIP call is made (only fake, never-dereferenced
+pointers are passed, and every call here fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_sequence_gate_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+P = ctypes.c_void_p(0x100000)      # 16-byte aligned fake device addresses
+P2 = ctypes.c_void_p(0x200000)
+P3 = ctypes.c_void_p(0x300000)
+BAD = ctypes.c_void_p(0x100008)    # misaligned
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
+              "kda_last_error", "kda_version"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_version(L):
+    assert "gfx950" in _lib.kda_version()
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load_library(str(tmp_path / "nope.so"))
+
+
+def chunk(L, q=P, k=P, v=P, g=P, beta=P, S0=NULL, ST=NULL, o=P2, ws=NULL, wsb=0,
+          B=1, T=64, H=1, dk=32, dv=32, dt=1, flags=0):
+    return L.kda_chunk_fwd(q, k, v, g, beta, S0, ST, o, ws, wsb, B, T, H, dk, dv, dt, flags, None)
+
+
+def test_chunk_validation(L):
+    E = _lib
+    assert chunk(L, q=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "null" in _lib.kda_last_error()
+    assert chunk(L, o=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert chunk(L, T=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert chunk(L, B=-1) == E.KDA_ERR_INVALID_ARGUMENT
+    assert chunk(L, dk=48) == E.KDA_ERR_UNSUPPORTED
+    assert chunk(L, dv=256) == E.KDA_ERR_UNSUPPORTED
+    assert chunk(L, dt=7) == E.KDA_ERR_UNSUPPORTED
+    assert chunk(L, dt=0, dk=128) == E.KDA_ERR_UNSUPPORTED       # fp32 with dk = 128
+    assert chunk(L, B=1 << 30, T=1 << 30) == E.KDA_ERR_INVALID_ARGUMENT   # overflow
+    assert chunk(L, k=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
+    assert chunk(L, o=P) == E.KDA_ERR_INVALID_ARGUMENT            # o aliases q
+    assert chunk(L, flags=2) == E.KDA_ERR_INVALID_ARGUMENT        # unknown flag
+    assert chunk(L, flags=1) == E.KDA_ERR_INVALID_ARGUMENT        # range check needs workspace
+    assert chunk(L, flags=1, ws=P3, wsb=8) == E.KDA_ERR_INVALID_ARGUMENT  # too small
+    assert "workspace" in _lib.kda_last_error()
+
+
+def test_workspace_query(L):
+    assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 32, 32, 1) >= 4
+    assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
+    assert L.kda_chunk_fwd_workspace_size(0, 64, 1, 32, 32, 1) == 0
+    assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 32, 32, 5) == 0
+
+
+def test_gate_validation(L):
+    E = _lib
+    assert L.kda_gate(NULL, P, P2, 1, 1, 1, 32, 1, None) == E.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_gate(P, P3, P2, 1, 1, 1, 40, 1, None) == E.KDA_ERR_UNSUPPORTED
+    assert L.kda_gate(P, P3, P2, 1, 0, 1, 32, 1, None) == E.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_gate(P, P3, P2, 1, 1, 1, 32, 9, None) == E.KDA_ERR_UNSUPPORTED
+    assert L.kda_gate(P, P3, P, 1, 1, 1, 32, 1, None) == E.KDA_ERR_INVALID_ARGUMENT   # g aliases z
+    assert L.kda_gate(BAD, P3, P2, 1, 1, 1, 32, 1, None) == E.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_validation(L):
+    E = _lib
+
+    def dec(q=P, k=P, v=P, z=P, A=P3, beta=P, S=P3, o=P2, N=4, H=2, dk=32, dv=32, dt=1):
+        return L.kda_decode_step(q, k, v, z, A, beta, S, o, N, H, dk, dv, dt, None)
+
+    assert dec(S=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(N=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(dv=96) == E.KDA_ERR_UNSUPPORTED
+    assert dec(dt=3) == E.KDA_ERR_UNSUPPORTED
+    assert dec(o=P) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(z=BAD) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(N=1 << 40, H=1 << 30) == E.KDA_ERR_INVALID_ARGUMENT
