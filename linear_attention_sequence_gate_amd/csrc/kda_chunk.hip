@@ -13,26 +13,30 @@
 // running sum of g inside the chunk, all per key channel):
 //     A_rs = beta_r sum_c k_rc k_sc e^{b_rc - b_sc}      (s < r)
 //     P_rs = sum_c q_rc k_sc e^{b_rc - b_sc}             (s <= r)
-//     T    = (I + A)^{-1} Diag(beta)                     (UT / WY form)
-//     W    = T (K * e^b),   U' = T V,   U = U' - W S     (delta-rule writes)
-//     O    = (Q * e^b) S + P U
-//     S   <- Diag(e^{b_C}) S + (K * e^{b_C - b})^T U
+//     X    = (I + A)^{-1}                               (UT / WY form)
+//     W    = X (beta K e^b),  U' = X (beta V),  U = U' - W S   (delta-rule writes)
+//     O    = (Q e^b) S + P U
+//     S   <- Diag(e^{b_C}) S + (K e^{b_C - b})^T U
 // Decay factors are referenced to 16-token subtile boundaries so that every
 // factor fed to a product lies in [e^-80, e^80] (the page's bound):
 //     lam_r = running sum of g inside r's subtile (in [-80, 0]),
 //     Lam_I = the subtile total.  For rows r in subtile I and columns s in J:
-//       J == I : e^{lam_r} * e^{-lam_s}                     (<= 1 * <= e^80)
-//       J <  I : e^{lam_r} * e^{Lam_J - lam_s} * e^{sum_{J<K<I} Lam_K}  (all <= 1)
+//       J == I : e^{lam_r} * e^{-lam_s}                               (<= 1 * <= e^80)
+//       J <  I : e^{lam_r} * e^{Lam_J - lam_s} * e^{sum_{J<K<I} Lam_K}   (all <= 1)
 //
-// Data flow per chunk (all on chip, the fp32 state lives in MFMA accumulator
-// registers across chunks, a bf16/fp32 copy of it in LDS as an operand):
-//   A  prep:    g -> lam, Lam; decayed operand tiles into LDS
-//   B  scores:  A and P on MFMA (20 tiles of 16x16)
-//   C  inverse: (I + A)^-1 by 16x16 blocks (forward substitution on the
-//               diagonal blocks, block substitution below), then T
-//   D  W = T K~, U' = T V on MFMA
-//   E  U = U' - W S
-//   F  O = Q~ S + P U (to HBM), S <- e^{b_C} S + K^^T U
+// Work per chunk (one workgroup of 4 waves; wave w owns subtile w in the
+// intra-chunk stages and dv column block(s) w, w+4, .. in the state pass):
+//   A  prep     raw q/k/v/g/beta (prefetched into registers one chunk ahead
+//               with 8/16-byte loads) -> in-wave running sums -> decayed
+//               operand tiles in LDS (beta folded into K and V rows)
+//   B  scores   A and P, 20 16x16 tiles on MFMA; P kept as bf16 hi + lo
+//   C  inverse  X = (I + A)^-1 on MFMA: diagonal 16x16 blocks by the product
+//               (I+N)(I+N^2)(I+N^4)(I+N^8) with N = -A_II (A_II^16 = 0), the
+//               blocks below by block substitution, one level per barrier
+//   D  W, U'    on MFMA
+//   E  state    per wave, no barrier: U = U' - W S (kept as bf16 hi + lo),
+//               O = Q~ S + P U to HBM, S <- e^{b_C} S + K^^T U (fp32 state in
+//               MFMA accumulator registers, a bf16 copy in LDS as an operand)
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -49,33 +53,46 @@ struct ChunkArgs {
     int H, DV, nslice, nbh, xcd_map;
 };
 
-// LDS plan (byte offsets).  LDK: pitch of token rows with channels contiguous;
-// LDT: pitch of channel rows with tokens contiguous; LDF: fp32 64x64 pitch.
+// Four consecutive elements of T in one register group.
+template <typename T> struct Quad;
+template <> struct Quad<bf16> { typedef bf16x4 type; };
+template <> struct Quad<float> { typedef floatx4 type; };
+
+__device__ __forceinline__ floatx4 to_f4(bf16x4 x) {
+    return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ floatx4 to_f4(floatx4 x) { return x; }
+
+// LDS plan (byte offsets).  LDK: pitch of token rows (channels contiguous);
+// LDT: pitch of channel rows (tokens contiguous).
 template <typename T, int DK, int NV> struct ChunkLds {
     static constexpr int E = sizeof(T);
     static constexpr int PAD = 16 / E;
     static constexpr int LDK = DK + PAD;
     static constexpr int LDT = kChunk + PAD;
-    static constexpr int LDF = kChunk + 4;
-    static constexpr int LDY = 20;
-    // region 1, phases A-B: decayed score operands
+    static constexpr int TILE64 = 64 * LDT * E;          // one [64][LDT] matrix
+    static constexpr bool SPLIT = sizeof(T) == 2;        // bf16 keeps P and U as hi + lo
+    // region 1, stages A-B: decayed score operands
     static constexpr int QR = 0;
     static constexpr int KR = QR + 64 * LDK * E;
-    static constexpr int KC = KR + 64 * LDK * E;           // 10 tiles of 16 rows
+    static constexpr int KC = KR + 64 * LDK * E;          // 10 tiles of 16 rows
     static constexpr int R1_OPS = KC + 160 * LDK * E;
-    // region 1, phases B-D: A, X = (I+A)^-1, block temporaries, P, T
-    static constexpr int AF = 0;
-    static constexpr int XF = AF + 64 * LDF * 4;
-    static constexpr int YF = XF + 64 * LDF * 4;
-    static constexpr int P = YF + 3 * 16 * LDY * 4;
-    static constexpr int TT = P + 64 * LDT * E;
-    static constexpr int R1_INV = TT + 64 * LDT * E;
-    // region 1, phases D-F: -W and U^T (over A and X, which are dead by then)
-    static constexpr int WN = 0;
-    static constexpr int UT = WN + 64 * LDK * E;
-    static constexpr int R1_W = UT + NV * LDT * E;
-    static_assert(R1_W <= P, "-W / U^T must not overlap P and T");
-    static constexpr int R1 = R1_OPS > R1_INV ? R1_OPS : R1_INV;
+    // region 1, stages B-E: P (hi, lo), X row- and column-major, A
+    static constexpr int PH = 0;
+    static constexpr int PL = PH + TILE64;
+    static constexpr int XR = PL + (SPLIT ? TILE64 : 0);
+    static constexpr int XC = XR + TILE64;
+    static constexpr int AB = XC + TILE64;
+    static constexpr int R1_INV = AB + TILE64;
+    // stage D on: -W over XC and AB (dead by then); stage E: U^T hi over XR
+    // (dead after stage D), U^T lo after AB
+    static constexpr int WN = XC;
+    static constexpr int UTH = XR;
+    static constexpr int UTL = R1_INV;
+    static_assert(64 * LDK * E <= 2 * TILE64, "-W must fit over X^c and A");
+    static_assert(NV * LDT * E <= TILE64, "U^T hi must fit over X");
+    static constexpr int R1_E = UTL + (SPLIT ? NV * LDT * E : 0);
+    static constexpr int R1 = R1_OPS > R1_E ? R1_OPS : R1_E;
     // region 2: operands of the state pass, the state copy, small tables
     static constexpr int QT = R1;
     static constexpr int KTT = QT + 64 * LDK * E;
@@ -96,40 +113,88 @@ template <typename T> __device__ __forceinline__ int kround(int I) {
     return ((16 * (I + 1) + ks - 1) / ks) * ks;
 }
 
-__device__ __forceinline__ void store16(bf16 *p, const float *x) {
-    bf16x8 a, b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { a[j] = (bf16)x[j]; b[j] = (bf16)x[8 + j]; }
-    reinterpret_cast<bf16x8 *>(p)[0] = a;
-    reinterpret_cast<bf16x8 *>(p)[1] = b;
+// ---------------------------------------------------------------------------
+// 16x16x16 products in the accumulator ("L") layout: lane l holds
+// M[4*(l/16) + j][l % 16] in element j.  mma16(L(X^T), L(Y)) = L(X Y).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ floatx4 mma16(bf16, floatx4 a, floatx4 b, floatx4 c) {
+    bf16x4 ab = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    bf16x4 bb = {(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, c, 0, 0, 0);
 }
-__device__ __forceinline__ void store16(float *p, const float *x) {
+__device__ __forceinline__ floatx4 mma16(float, floatx4 a, floatx4 b, floatx4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+}
+
+// Four consecutive T values from LDS as fp32, and back.
+__device__ __forceinline__ floatx4 lds_load4(const bf16 *p) {
+    return to_f4(*reinterpret_cast<const bf16x4 *>(p));
+}
+__device__ __forceinline__ floatx4 lds_load4(const float *p) {
+    return *reinterpret_cast<const floatx4 *>(p);
+}
+template <typename T> __device__ __forceinline__ void store4v(T *p, floatx4 x) {
+    store4(p, x[0], x[1], x[2], x[3]);
+}
+
+// N consecutive values (channel-major rows: tokens contiguous).
+template <int N> __device__ __forceinline__ void storeN(bf16 *p, const float *x) {
+    if constexpr (N == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<bf16x2 *>(p) = bf16x2{(bf16)x[0], (bf16)x[1]};
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        reinterpret_cast<floatx4 *>(p)[j] = floatx4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+        for (int i = 0; i < N; i += 4) store4(p + i, x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+}
+template <int N> __device__ __forceinline__ void storeN(float *p, const float *x) {
+    if constexpr (N == 2) {
+        typedef float floatx2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<floatx2 *>(p) = floatx2{x[0], x[1]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) store4(p + i, x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+}
+
+// Order this wave's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <typename T, int DK, int NV>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     using Lds = ChunkLds<T, DK, NV>;
-    constexpr int LDK = Lds::LDK, LDT = Lds::LDT, LDF = Lds::LDF, LDY = Lds::LDY;
-    constexpr int NITEM = (4 * DK + 255) / 256;     // (channel, subtile) items per thread
-    constexpr int NU = NV / 16;                      // U / O tiles per wave
+    using T4 = typename Quad<T>::type;
+    constexpr int LDK = Lds::LDK, LDT = Lds::LDT;
+    constexpr bool kSplit = Lds::SPLIT;              // keep P and U as bf16 hi + lo
+    // prep mapping: thread = (channel quad cq, token group tg); wave w <-> subtile w
+    constexpr int NQ = DK / 4;                       // channel quads
+    constexpr int TPT = DK / 16;                     // tokens per thread (8, 4, 2)
+    constexpr int NVQ = NV / 4;                      // dv quads of the slice
+    constexpr int TPV = NV / 16;                     // v tokens per thread
     constexpr int NSB = NV / 16;                     // state column blocks
-    constexpr int NS = (DK / 16) * NSB / 4;          // state tiles per wave
-    static_assert(NS >= 1 && (DK / 16) * NSB % 4 == 0, "state tiles");
+    constexpr int NOWN = (NSB + 3) / 4;              // column blocks owned per wave
+    constexpr int NCB = DK / 16;                     // state row blocks
+    static_assert(256 == NQ * (64 / TPT) && 256 == NVQ * (64 / TPV), "prep mapping");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::TOTAL];
     T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
     T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
     T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
-    float *sAf = reinterpret_cast<float *>(smem + Lds::AF);
-    float *sXf = reinterpret_cast<float *>(smem + Lds::XF);
-    float *sYf = reinterpret_cast<float *>(smem + Lds::YF);
-    T *sP = reinterpret_cast<T *>(smem + Lds::P);
-    T *sT = reinterpret_cast<T *>(smem + Lds::TT);
+    T *sPh = reinterpret_cast<T *>(smem + Lds::PH);
+    T *sPl = reinterpret_cast<T *>(smem + Lds::PL);
+    T *sXr = reinterpret_cast<T *>(smem + Lds::XR);
+    T *sXc = reinterpret_cast<T *>(smem + Lds::XC);
+    T *sA = reinterpret_cast<T *>(smem + Lds::AB);
     T *sWn = reinterpret_cast<T *>(smem + Lds::WN);
-    T *sUT = reinterpret_cast<T *>(smem + Lds::UT);
+    T *sUh = reinterpret_cast<T *>(smem + Lds::UTH);
+    T *sUl = reinterpret_cast<T *>(smem + Lds::UTL);
     T *sQt = reinterpret_cast<T *>(smem + Lds::QT);
     T *sKtT = reinterpret_cast<T *>(smem + Lds::KTT);
     T *sKhT = reinterpret_cast<T *>(smem + Lds::KHT);
@@ -139,19 +204,21 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     float *sEbC = reinterpret_cast<float *>(smem + Lds::EBC);
     float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA);
 
-    const T *__restrict__ q = static_cast<const T *>(a.q);
-    const T *__restrict__ k = static_cast<const T *>(a.k);
-    const T *__restrict__ v = static_cast<const T *>(a.v);
-    const T *__restrict__ beta = static_cast<const T *>(a.beta);
-    const float *__restrict__ g = a.g;
-    T *__restrict__ o = static_cast<T *>(a.o);
+    const T *__restrict__ qp = static_cast<const T *>(a.q);
+    const T *__restrict__ kp = static_cast<const T *>(a.k);
+    const T *__restrict__ vp = static_cast<const T *>(a.v);
+    const T *__restrict__ bp = static_cast<const T *>(a.beta);
+    const float *__restrict__ gp = a.g;
+    T *__restrict__ op = static_cast<T *>(a.o);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
+    const int cq = tid % NQ, tg = tid / NQ, pos = lane / NQ;   // pos: rank inside the subtile
+    const int vq = tid % NVQ, tv = tid / NVQ;
 
-    // Work item: (chain bh, dv slice).  With the XCD mapping, the slices of
-    // one chain land on the same XCD (workgroups are dealt round-robin over
-    // the 8 XCDs) and share its L2 for q, k, g.
+    // Work item (chain bh, dv slice).  With the XCD mapping the slices of one
+    // chain land on one XCD (workgroups are dealt round-robin over 8 XCDs) and
+    // share its L2 for q, k, g.
     int bh, slice;
     {
         const int id = blockIdx.x;
@@ -168,291 +235,373 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const int b = bh / H, h = bh % H;
     const int64_t T_ = a.T;
     const int vcol0 = slice * NV;
+    const int64_t nchunk = (T_ + kChunk - 1) / kChunk;
 
-    // ---- state: fp32 accumulator tiles owned by this wave ----------------
-    floatx4 sacc[NS];
+    // ---- raw chunk inputs, prefetched one chunk ahead ---------------------
+    floatx4 rg[TPT];
+    T4 rk[TPT], rq[TPT], rv[TPV];
+    float rbeta = 0.0f;
+    auto load_raw = [&](int64_t ch) {
+        const int64_t t0 = ch * kChunk;
+        const int L = (int)((T_ - t0) < kChunk ? (T_ - t0) : kChunk);
+        const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        const int ti = wave + 4 * i, cb = ti / NSB, nb = ti % NSB;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
-            sacc[i][j] = a.S0 ? a.S0[((int64_t)bh * DK + c) * DV + n] : 0.0f;
+        for (int i = 0; i < TPT; ++i) {
+            const int tl = tg * TPT + i;
+            const int tc = tl < L ? tl : L - 1;          // clamp: never read past the end
+            const int64_t e = (tok0 + (int64_t)tc * H) * DK + 4 * cq;
+            rg[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(gp + e));
+            rk[i] = *reinterpret_cast<const T4 *>(kp + e);
+            rq[i] = *reinterpret_cast<const T4 *>(qp + e);
         }
-        store4(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[i][0], sacc[i][1], sacc[i][2],
-               sacc[i][3]);
+#pragma unroll
+        for (int i = 0; i < TPV; ++i) {
+            const int tl = tv * TPV + i;
+            const int tc = tl < L ? tl : L - 1;
+            rv[i] = *reinterpret_cast<const T4 *>(vp + (tok0 + (int64_t)tc * H) * DV + vcol0 + 4 * vq);
+        }
+        if (tid < 64) rbeta = to_f32(bp[tok0 + (int64_t)(tid < L ? tid : L - 1) * H]);
+    };
+
+    // ---- state: fp32 accumulator tiles of the owned column blocks ----------
+    floatx4 sacc[NOWN][NCB];
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+        const int nb = wave + 4 * m;
+        if (nb < NSB) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
+                    sacc[m][cb][j] = a.S0 ? a.S0[((int64_t)bh * DK + c) * DV + n] : 0.0f;
+                }
+                store4v(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[m][cb]);
+            }
+        }
     }
 
-    const int64_t nchunk = (T_ + kChunk - 1) / kChunk;
+    load_raw(0);
     for (int64_t ch = 0; ch < nchunk; ++ch) {
         const int64_t t0 = ch * kChunk;
         const int L = (int)((T_ - t0) < kChunk ? (T_ - t0) : kChunk);
-        const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;   // token t0 + r -> tok0 + r*H
+        const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
+        const int I = wave;                              // this wave's subtile
 
-        // ---- A1: running log-decay inside each 16-token subtile -----------
-        float lam[NITEM][16], kx[NITEM][16], qx[NITEM][16];
+        // ---- A1: running log-decay inside the subtile (in-wave scan) --------
+        floatx4 lam[TPT];
+        floatx4 run = {0, 0, 0, 0};
 #pragma unroll
-        for (int it = 0; it < NITEM; ++it) {
-            const int item = tid + 256 * it;
-            if (item < 4 * DK) {
-                const int c = item % DK, I = item / DK;
-                float run = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int tl = 16 * I + r;
-                    float gv = 0.0f, kv = 0.0f, qv = 0.0f;
-                    if (tl < L) {
-                        const int64_t e = (tok0 + (int64_t)tl * H) * DK + c;
-                        gv = g[e];
-                        kv = to_f32(k[e]);
-                        qv = to_f32(q[e]);
-                    }
-                    run += gv;
-                    lam[it][r] = run;
-                    kx[it][r] = kv;
-                    qx[it][r] = qv;
-                }
-                sLam[I * DK + c] = run;
-            }
+        for (int i = 0; i < TPT; ++i) {
+            const bool ok = tg * TPT + i < L;
+            run += ok ? rg[i] : floatx4{0, 0, 0, 0};
+            lam[i] = run;
         }
-        if (tid < 64) sBeta[tid] = (tid < L) ? to_f32(beta[tok0 + (int64_t)tid * H]) : 0.0f;
-        for (int item = tid; item < NV * 4; item += 256) {
-            const int n = item % NV, I = item / NV;
-            float vv[16];
+        floatx4 pre = {0, 0, 0, 0};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tl = 16 * I + r;
-                vv[r] = (tl < L) ? to_f32(v[(tok0 + (int64_t)tl * H) * DV + vcol0 + n]) : 0.0f;
-            }
-            store16(sVT + n * LDT + 16 * I, vv);
+        for (int s = 1; s < 64 / NQ; ++s) {
+            floatx4 other;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) other[j] = __shfl(run[j], lane - s * NQ);
+            if (pos >= s) pre += other;
         }
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) lam[i] += pre;
+        if (pos == 64 / NQ - 1)
+            *reinterpret_cast<floatx4 *>(sLam + I * DK + 4 * cq) = lam[TPT - 1];
+        if (tid < 64) sBeta[tid] = tid < L ? rbeta : 0.0f;
         __syncthreads();
 
-        // ---- A2: decayed operand tiles -----------------------------------
+        // ---- A2: decayed operand tiles -------------------------------------
+        {
+            const floatx4 L0 = *reinterpret_cast<const floatx4 *>(sLam + 4 * cq);
+            const floatx4 L1 = *reinterpret_cast<const floatx4 *>(sLam + DK + 4 * cq);
+            const floatx4 L2 = *reinterpret_cast<const floatx4 *>(sLam + 2 * DK + 4 * cq);
+            const floatx4 L3 = *reinterpret_cast<const floatx4 *>(sLam + 3 * DK + 4 * cq);
+            const floatx4 pre1 = L0, pre2 = L0 + L1, pre3 = pre2 + L2, pre4 = pre3 + L3;
+            const floatx4 preI = I == 0 ? floatx4{0, 0, 0, 0} : I == 1 ? pre1 : I == 2 ? pre2 : pre3;
+            const floatx4 LamI = I == 0 ? L0 : I == 1 ? L1 : I == 2 ? L2 : L3;
+            const floatx4 preI1 = preI + LamI;             // b at the end of subtile I
+            floatx4 ePre, eNegLam, eHat, eOff1, eOff2, eOff3;
 #pragma unroll
-        for (int it = 0; it < NITEM; ++it) {
-            const int item = tid + 256 * it;
-            if (item < 4 * DK) {
-                const int c = item % DK, I = item / DK;
-                const float L0 = sLam[c], L1 = sLam[DK + c], L2 = sLam[2 * DK + c],
-                            L3 = sLam[3 * DK + c];
-                const float pre1 = L0, pre2 = L0 + L1, pre3 = L0 + L1 + L2, pre4 = pre3 + L3;
-                const float preI = I == 0 ? 0.0f : I == 1 ? pre1 : I == 2 ? pre2 : pre3;
-                const float LamI = I == 0 ? L0 : I == 1 ? L1 : I == 2 ? L2 : L3;
-                const float preI1 = preI + LamI;        // b at the end of subtile I
-                const float ePre = __expf(preI);        // e^{b before subtile I}   <= 1
-                const float eNegLam = __expf(-LamI);    // e^{-Lam_I}              <= e^80
-                const float eHat = __expf(pre4 - preI1); // e^{b_C - b_end(I)}     <= 1
-                const float eOff1 = __expf(pre1 - preI1);   // only used for I2 > I
-                const float eOff2 = __expf(pre2 - preI1);
-                const float eOff3 = __expf(pre3 - preI1);
-                if (I == 0) sEbC[c] = __expf(pre4);
-                float kt[16], kh[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int s = 16 * I + r;
-                    const float lr_ = lam[it][r];
-                    const float R = __expf(lr_);            // e^{lam_r}           in [e^-80, 1]
-                    const float Et = __expf(LamI - lr_);    // e^{Lam_I - lam_r}   in [e^-75, 1]
-                    const float kv = kx[it][r], qv = qx[it][r];
-                    sKr[s * LDK + c] = from_f32<T>(kv * R);
-                    sQr[s * LDK + c] = from_f32<T>(qv * R);
-                    // diagonal pair (I, I): column factor e^{-lam_s} = Et * e^{-Lam_I}
-                    sKc[((I * (I + 1)) / 2 + I) * 16 * LDK + r * LDK + c] =
-                        from_f32<T>(kv * (Et * eNegLam));
-                    // off-diagonal pairs (I2, I), I2 > I
-                    if (I < 1) sKc[(1 + I) * 16 * LDK + r * LDK + c] = from_f32<T>(kv * Et * eOff1);
-                    if (I < 2) sKc[(3 + I) * 16 * LDK + r * LDK + c] = from_f32<T>(kv * Et * eOff2);
-                    if (I < 3) sKc[(6 + I) * 16 * LDK + r * LDK + c] = from_f32<T>(kv * Et * eOff3);
-                    const float eb = R * ePre;                  // e^{b_r}  <= 1
-                    sQt[s * LDK + c] = from_f32<T>(qv * eb);
-                    kt[r] = kv * eb;
-                    kh[r] = kv * Et * eHat;                     // e^{b_C - b_r} <= 1
-                }
-                store16(sKtT + c * LDT + 16 * I, kt);
-                store16(sKhT + c * LDT + 16 * I, kh);
+            for (int j = 0; j < 4; ++j) {
+                ePre[j] = __expf(preI[j]);                 // e^{b before subtile I}  <= 1
+                eNegLam[j] = __expf(-LamI[j]);             // <= e^80
+                eHat[j] = __expf(pre4[j] - preI1[j]);      // e^{b_C - b_end(I)}    <= 1
+                // e^{sum_{I<K<I2} Lam_K}, used only for I2 > I
+                eOff1[j] = __expf(I < 1 ? pre1[j] - preI1[j] : 0.0f);
+                eOff2[j] = __expf(I < 2 ? pre2[j] - preI1[j] : 0.0f);
+                eOff3[j] = __expf(I < 3 ? pre3[j] - preI1[j] : 0.0f);
             }
+            if (I == 0 && pos == 0) {
+                floatx4 ebc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ebc[j] = __expf(pre4[j]);
+                *reinterpret_cast<floatx4 *>(sEbC + 4 * cq) = ebc;
+            }
+            float ktb[4][TPT], kh[4][TPT];
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                const int tl = tg * TPT + i;               // token inside the chunk
+                const int r = tl - 16 * I;                 // row inside the subtile
+                const bool ok = tl < L;
+                const floatx4 kv = ok ? to_f4(rk[i]) : floatx4{0, 0, 0, 0};
+                const floatx4 qv = ok ? to_f4(rq[i]) : floatx4{0, 0, 0, 0};
+                const float bt = sBeta[tl];
+                floatx4 R, Et;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    R[j] = __expf(lam[i][j]);              // e^{lam_r}          in [e^-80, 1]
+                    Et[j] = __expf(LamI[j] - lam[i][j]);   // e^{Lam_I - lam_r}  in [e^-75, 1]
+                }
+                const floatx4 kEt = kv * Et;
+                store4v(sKr + tl * LDK + 4 * cq, kv * R * bt);
+                store4v(sQr + tl * LDK + 4 * cq, qv * R);
+                // column operands: diagonal pair (I,I) and off-diagonal pairs (I2,I), I2 > I
+                store4v(sKc + (((I * (I + 1)) / 2 + I) * 16 + r) * LDK + 4 * cq, kEt * eNegLam);
+                if (I < 1) store4v(sKc + ((1 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff1);
+                if (I < 2) store4v(sKc + ((3 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff2);
+                if (I < 3) store4v(sKc + ((6 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff3);
+                const floatx4 eb = R * ePre;               // e^{b_r} <= 1
+                store4v(sQt + tl * LDK + 4 * cq, qv * eb);
+                const floatx4 kt = kv * eb * bt, khv = kEt * eHat;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ktb[j][i] = kt[j];
+                    kh[j][i] = khv[j];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                storeN<TPT>(sKtT + (4 * cq + j) * LDT + tg * TPT, ktb[j]);
+                storeN<TPT>(sKhT + (4 * cq + j) * LDT + tg * TPT, kh[j]);
+            }
+            float vt[4][TPV];
+#pragma unroll
+            for (int i = 0; i < TPV; ++i) {
+                const int tl = tv * TPV + i;
+                const float bt = sBeta[tl];                // 0 past the end of the sequence
+                const floatx4 vv = to_f4(rv[i]) * bt;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vt[j][i] = tl < L ? vv[j] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) storeN<TPV>(sVT + (4 * vq + j) * LDT + tv * TPV, vt[j]);
         }
+        if (ch + 1 < nchunk) load_raw(ch + 1);            // lands during stages B-E
         __syncthreads();
 
-        // ---- B: A and P tiles (10 causal subtile pairs each) ---------------
+        // ---- B: A and P tiles (10 causal subtile pairs each) -----------------
         floatx4 sc[5];
+        {
+            const T *xs[5], *ys[5];
 #pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int ti = wave + 4 * u, p = ti >> 1;
-            const int I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-            sc[u] = floatx4{0, 0, 0, 0};
-            tile_mma<T>(sc[u], sKc + p * 16 * LDK, LDK, ((ti & 1) ? sQr : sKr) + 16 * I * LDK,
-                        LDK, DK, lane);
+            for (int u = 0; u < 5; ++u) {
+                const int ti = wave + 4 * u, p = ti >> 1;
+                const int Ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
+                sc[u] = floatx4{0, 0, 0, 0};
+                xs[u] = sKc + p * 16 * LDK + lr * LDK + (lane >> 4) * (Mma<T>::kStep / 4);
+                ys[u] = ((ti & 1) ? sQr : sKr) + (16 * Ib + lr) * LDK + (lane >> 4) * (Mma<T>::kStep / 4);
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += Mma<T>::kStep)
+#pragma unroll
+                for (int u = 0; u < 5; ++u) Mma<T>::step(sc[u], xs[u] + k0, ys[u] + k0);
         }
         __syncthreads();   // region 1 is rewritten below
 #pragma unroll
         for (int u = 0; u < 5; ++u) {
             const int ti = wave + 4 * u, p = ti >> 1;
-            const int I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-            const int J = p - (I * (I + 1)) / 2;
+            const int Ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
+            const int J = p - (Ib * (Ib + 1)) / 2;
             const bool isP = ti & 1;
-            float val[4];
+            floatx4 val;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int s = lg4 + j;                  // column inside block J
-                const bool keep = (J < I) || (isP ? (s <= lr) : (s < lr));
+                const int s = lg4 + j;                     // column inside block J
+                const bool keep = (J < Ib) || (isP ? (s <= lr) : (s < lr));
                 val[j] = keep ? sc[u][j] : 0.0f;
             }
-            const int r = 16 * I + lr;
+            const int r = 16 * Ib + lr;
             if (isP) {
-                store4(sP + r * LDT + 16 * J + lg4, val[0], val[1], val[2], val[3]);
+                store4v(sPh + r * LDT + 16 * J + lg4, val);
+                if constexpr (kSplit) {
+                    floatx4 lo;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lo[j] = val[j] - (float)(bf16)val[j];
+                    store4v(sPl + r * LDT + 16 * J + lg4, lo);
+                }
             } else {
-                const float bt = sBeta[r];
-                store4(sAf + r * LDF + 16 * J + lg4, bt * val[0], bt * val[1], bt * val[2],
-                       bt * val[3]);
+                store4v(sA + r * LDT + 16 * J + lg4, val);
             }
         }
-        // zero the blocks above the diagonal of P and T (read by the rounded-up
-        // causal products)
+        // zero the blocks above the diagonal of P (hi, lo) and X (read by the
+        // rounded-up causal products)
         for (int e = tid; e < 6 * 64; e += 256) {
             const int blk = e >> 6, q4 = e & 63, rr = q4 >> 2, cc = (q4 & 3) * 4;
-            const int I = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-            const int J = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-            store4(sP + (16 * I + rr) * LDT + 16 * J + cc, 0.f, 0.f, 0.f, 0.f);
-            store4(sT + (16 * I + rr) * LDT + 16 * J + cc, 0.f, 0.f, 0.f, 0.f);
+            const int Iu = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+            const int Ju = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+            const int off = (16 * Iu + rr) * LDT + 16 * Ju + cc;
+            store4(sPh + off, 0.f, 0.f, 0.f, 0.f);
+            if constexpr (kSplit) store4(sPl + off, 0.f, 0.f, 0.f, 0.f);
+            store4(sXr + off, 0.f, 0.f, 0.f, 0.f);
         }
         __syncthreads();
 
-        // ---- C1: diagonal blocks of (I + A)^-1, forward substitution ----------
-        if (wave == 0) {
-            const int I = lane >> 4, jc = lane & 15;
-            const float *Ab = sAf + 16 * I * LDF + 16 * I;
-            float x[16];
+        // ---- C: X = (I + A)^-1 ----------------------------------------------
+        floatx4 xT;                                        // L(X_II^T) of this wave's block
+        {
+            const T tz = T(0);
+            auto addI = [&](floatx4 m) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = 0.0f;
+                for (int j = 0; j < 4; ++j) m[j] += (lg4 + j == lr) ? 1.0f : 0.0f;
+                return m;
+            };
+            const floatx4 z4 = {0, 0, 0, 0};
+            // N = -A_II in both layouts
+            const floatx4 nT = -lds_load4(sA + (16 * I + lr) * LDT + 16 * I + lg4);
+            floatx4 n;
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(Ab[i * LDF + m], x[m], acc);
-                x[i] = (i < jc) ? 0.0f : ((i == jc) ? 1.0f : -acc);
-            }
-            float *Xb = sXf + 16 * I * LDF + 16 * I;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Xb[i * LDF + jc] = x[i];
-        }
-        __syncthreads();
-
-        // ---- C2: blocks below the diagonal, X_IJ = -X_II sum_K A_IK X_KJ ---------
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            const int nblk = 4 - d;
-            const int bi = tid >> 6, e = tid & 63, i = e >> 2, j4 = (e & 3) * 4;
-            const int J = bi, I = J + d;
-            if (bi < nblk) {
-                floatx4 y = {0, 0, 0, 0};
-                for (int K = J; K < I; ++K) {
-#pragma unroll
-                    for (int m = 0; m < 16; ++m) {
-                        const float av = sAf[(16 * I + i) * LDF + 16 * K + m];
-                        const floatx4 xv =
-                            *reinterpret_cast<const floatx4 *>(sXf + (16 * K + m) * LDF + 16 * J + j4);
-                        y += av * xv;
-                    }
-                }
-                *reinterpret_cast<floatx4 *>(sYf + (bi * 16 + i) * LDY + j4) = y;
-            }
+            for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * I + lg4 + j) * LDT + 16 * I + lr]);
+            const floatx4 n2 = mma16(tz, nT, n, z4);
+            const floatx4 n2T = mma16(tz, n, nT, z4);
+            const floatx4 n4 = mma16(tz, n2T, n2, z4);
+            const floatx4 n4T = mma16(tz, n2, n2T, z4);
+            const floatx4 n8 = mma16(tz, n4T, n4, z4);
+            const floatx4 p1 = mma16(tz, addI(nT), addI(n2), z4);
+            const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);
+            (void)p1;
+            const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);
+            const floatx4 p2 = mma16(tz, p1T, addI(n4), z4);
+            (void)p2;
+            const floatx4 x = mma16(tz, p2T, addI(n8), z4);
+            xT = mma16(tz, addI(n8), p2T, z4);
+            store4v(sXc + (16 * I + lr) * LDT + 16 * I + lg4, x);
+            store4v(sXr + (16 * I + lr) * LDT + 16 * I + lg4, xT);
             __syncthreads();
-            if (bi < nblk) {
-                floatx4 xn = {0, 0, 0, 0};
-                for (int m = 0; m <= i; ++m) {
-                    const float xa = sXf[(16 * I + i) * LDF + 16 * I + m];
-                    const floatx4 yv = *reinterpret_cast<const floatx4 *>(sYf + (bi * 16 + m) * LDY + j4);
-                    xn += xa * yv;
+            // blocks below the diagonal, one level per barrier:
+            // X_IJ = -X_II sum_{K=J}^{I-1} A_IK X_KJ, computed by the wave of row block I
+#pragma unroll
+            for (int d = 1; d < 4; ++d) {
+                if (I >= d) {
+                    const int J = I - d;
+                    floatx4 y = z4;
+                    for (int K = J; K < I; ++K)
+                        y = mma16(tz, lds_load4(sA + (16 * I + lr) * LDT + 16 * K + lg4),
+                                  lds_load4(sXc + (16 * J + lr) * LDT + 16 * K + lg4), y);
+                    const floatx4 xij = -mma16(tz, xT, y, z4);
+                    const floatx4 xijT = -mma16(tz, y, xT, z4);
+                    store4v(sXc + (16 * J + lr) * LDT + 16 * I + lg4, xij);
+                    store4v(sXr + (16 * I + lr) * LDT + 16 * J + lg4, xijT);
                 }
-                *reinterpret_cast<floatx4 *>(sXf + (16 * I + i) * LDF + 16 * J + j4) = -xn;
-            }
-            __syncthreads();
-        }
-
-        // ---- C3: T = X Diag(beta) on and below the diagonal blocks --------
-        for (int e = tid; e < 64 * 16; e += 256) {
-            const int r = e >> 4, s4 = (e & 15) * 4;
-            if ((s4 >> 4) <= (r >> 4)) {
-                const floatx4 xv = *reinterpret_cast<const floatx4 *>(sXf + r * LDF + s4);
-                store4(sT + r * LDT + s4, xv[0] * sBeta[s4], xv[1] * sBeta[s4 + 1],
-                       xv[2] * sBeta[s4 + 2], xv[3] * sBeta[s4 + 3]);
+                __syncthreads();
             }
         }
+
+        // ---- D: -W = -X (beta K~) into LDS; U' = X (beta V) into registers ----
+        {
+            floatx4 wacc[NCB];
+            const T *xs = sXr + (16 * I + lr) * LDT + (lane >> 4) * (Mma<T>::kStep / 4);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) wacc[cb] = floatx4{0, 0, 0, 0};
+            const int KI = kround<T>(I);
+            for (int k0 = 0; k0 < KI; k0 += Mma<T>::kStep)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    Mma<T>::step(wacc[cb],
+                                 sKtT + (16 * cb + lr) * LDT + (lane >> 4) * (Mma<T>::kStep / 4) + k0,
+                                 xs + k0);
+            // lane holds W^T[c = 16cb + lg4 + j][r = 16I + lr]
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                store4v(sWn + (16 * I + lr) * LDK + 16 * cb + lg4, -wacc[cb]);
+        }
+        floatx4 uacc[NOWN][4];
+#pragma unroll
+        for (int m = 0; m < NOWN; ++m) {
+            const int nb = wave + 4 * m;
+            if (nb < NSB) {
+#pragma unroll
+                for (int Is = 0; Is < 4; ++Is) {
+                    uacc[m][Is] = floatx4{0, 0, 0, 0};
+                    tile_mma<T>(uacc[m][Is], sXr + 16 * Is * LDT, LDT, sVT + 16 * nb * LDT, LDT,
+                                kround<T>(Is), lane);
+                }
+            }
+        }
         __syncthreads();
 
-        // ---- D: -W = -T K~ into LDS; U' = T V into registers ---------------
-        for (int ti = wave; ti < DK / 4; ti += 4) {
-            const int cb = ti >> 2, I = ti & 3;
-            floatx4 acc = {0, 0, 0, 0};
-            tile_mma<T>(acc, sKtT + 16 * cb * LDT, LDT, sT + 16 * I * LDT, LDT, kround<T>(I), lane);
-            store4(sWn + (16 * I + lr) * LDK + 16 * cb + lg4, -acc[0], -acc[1], -acc[2], -acc[3]);
-        }
-        floatx4 uacc[NU];
+        // ---- E: state pass of the owned column blocks (no barrier) ----------
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ti = wave + 4 * u, Is = ti & 3, nb = ti >> 2;
-            uacc[u] = floatx4{0, 0, 0, 0};
-            tile_mma<T>(uacc[u], sT + 16 * Is * LDT, LDT, sVT + 16 * nb * LDT, LDT, kround<T>(Is),
-                        lane);
-        }
-        __syncthreads();
-
-        // ---- E: U = U' - W S, stored transposed (tokens contiguous) -----------
+        for (int m = 0; m < NOWN; ++m) {
+            const int nb = wave + 4 * m;
+            if (nb >= NSB) continue;
+            // U = U' - W S, kept as hi + lo (tokens contiguous)
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ti = wave + 4 * u, Is = ti & 3, nb = ti >> 2;
-            tile_mma<T>(uacc[u], sWn + 16 * Is * LDK, LDK, sST + 16 * nb * LDK, LDK, DK, lane);
-            store4(sUT + (16 * nb + lr) * LDT + 16 * Is + lg4, uacc[u][0], uacc[u][1], uacc[u][2],
-                   uacc[u][3]);
-        }
-        __syncthreads();
-
-        // ---- F: outputs, then the state update ------------------------------
+            for (int Is = 0; Is < 4; ++Is) {
+                tile_mma<T>(uacc[m][Is], sWn + 16 * Is * LDK, LDK, sST + 16 * nb * LDK, LDK, DK,
+                            lane);
+                store4v(sUh + (16 * nb + lr) * LDT + 16 * Is + lg4, uacc[m][Is]);
+                if constexpr (kSplit) {
+                    floatx4 lo;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ti = wave + 4 * u, Ir = ti & 3, nb = ti >> 2;
-            floatx4 acc = {0, 0, 0, 0};
-            tile_mma<T>(acc, sST + 16 * nb * LDK, LDK, sQt + 16 * Ir * LDK, LDK, DK, lane);
-            tile_mma<T>(acc, sUT + 16 * nb * LDT, LDT, sP + 16 * Ir * LDT, LDT, kround<T>(Ir), lane);
-            const int r = 16 * Ir + lr;
-            if (r < L)
-                store4(o + (tok0 + (int64_t)r * H) * DV + vcol0 + 16 * nb + lg4, acc[0], acc[1],
-                       acc[2], acc[3]);
-        }
+                    for (int j = 0; j < 4; ++j) lo[j] = uacc[m][Is][j] - (float)(bf16)uacc[m][Is][j];
+                    store4v(sUl + (16 * nb + lr) * LDT + 16 * Is + lg4, lo);
+                }
+            }
+            wave_lds_sync();
+            // O = Q~ S + P U for the 64 rows of this column block
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int ti = wave + 4 * i, cb = ti / NSB, nb = ti % NSB;
+            for (int Ir = 0; Ir < 4; ++Ir) {
+                floatx4 acc = {0, 0, 0, 0};
+                tile_mma<T>(acc, sST + 16 * nb * LDK, LDK, sQt + 16 * Ir * LDK, LDK, DK, lane);
+                const int KI = kround<T>(Ir);
+                tile_mma<T>(acc, sUh + 16 * nb * LDT, LDT, sPh + 16 * Ir * LDT, LDT, KI, lane);
+                if constexpr (kSplit) {
+                    tile_mma<T>(acc, sUl + 16 * nb * LDT, LDT, sPh + 16 * Ir * LDT, LDT, KI, lane);
+                    tile_mma<T>(acc, sUh + 16 * nb * LDT, LDT, sPl + 16 * Ir * LDT, LDT, KI, lane);
+                }
+                const int r = 16 * Ir + lr;
+                if (r < L)
+                    store4v(op + (tok0 + (int64_t)r * H) * DV + vcol0 + 16 * nb + lg4, acc);
+            }
+            // S <- Diag(e^{b_C}) S + K^^T U
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sacc[i][j] *= sEbC[16 * cb + lg4 + j];
-            tile_mma<T>(sacc[i], sKhT + 16 * cb * LDT, LDT, sUT + 16 * nb * LDT, LDT, kChunk, lane);
-        }
-        __syncthreads();
+            for (int cb = 0; cb < NCB; ++cb) {
+                const floatx4 e = *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
+                sacc[m][cb] *= e;
+                tile_mma<T>(sacc[m][cb], sKhT + 16 * cb * LDT, LDT, sUh + 16 * nb * LDT, LDT,
+                            kChunk, lane);
+            }
+            wave_lds_sync();   // this wave's reads of the old state copy are done
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int ti = wave + 4 * i, cb = ti / NSB, nb = ti % NSB;
-            store4(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[i][0], sacc[i][1], sacc[i][2],
-                   sacc[i][3]);
+            for (int cb = 0; cb < NCB; ++cb)
+                store4v(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[m][cb]);
         }
     }
 
     if (a.ST) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int ti = wave + 4 * i, cb = ti / NSB, nb = ti % NSB;
+        for (int m = 0; m < NOWN; ++m) {
+            const int nb = wave + 4 * m;
+            if (nb >= NSB) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
-                a.ST[((int64_t)bh * DK + c) * DV + n] = sacc[i][j];
-            }
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
+                    a.ST[((int64_t)bh * DK + c) * DV + n] = sacc[m][cb][j];
+                }
         }
     }
 }
 
-// dv-slice width per workgroup for each (dtype, dk): the widest that fits LDS.
+// dv-slice width per workgroup: four 16-column blocks (one per wave) where
+// the LDS plan allows it.
 static int slice_width(int dk, int dv, int is_bf16) {
-    int nv = is_bf16 ? 64 : 32;
+    int nv = 64;
+    if (!is_bf16 && dk == 64) nv = 32;   // fp32 tiles at dk = 64 leave room for 32 columns
     if (nv > dv) nv = dv;
-    (void)dk;
     return nv;
 }
 
@@ -492,6 +641,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     }
     switch (dk * 1000 + nv) {
     case 32032: return launch_inst<float, 32, 32>(args, nblocks, s);
+    case 32064: return launch_inst<float, 32, 64>(args, nblocks, s);
     case 64032: return launch_inst<float, 64, 32>(args, nblocks, s);
     default: return hipErrorInvalidValue;
     }
