@@ -108,6 +108,9 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: element count overflows");
     if (B * H > (int64_t(1) << 24))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: B*H=%lld too large", (long long)(B * H));
+    // the kernel addresses the tokens of one 64-token chunk with 32-bit byte offsets
+    if (H * (dk > dv ? dk : dv) * 64 * 4 >= (int64_t(1) << 32))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: H=%lld too large", (long long)H);
     const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p))

@@ -13,30 +13,36 @@
 // running sum of g inside the chunk, all per key channel):
 //     A_rs = beta_r sum_c k_rc k_sc e^{b_rc - b_sc}      (s < r)
 //     P_rs = sum_c q_rc k_sc e^{b_rc - b_sc}             (s <= r)
-//     X    = (I + A)^{-1}                               (UT / WY form)
-//     W    = X (beta K e^b),  U' = X (beta V),  U = U' - W S   (delta-rule writes)
+//     X    = (I + A)^{-1},  T = X Diag(beta)            (UT / WY form)
+//     W    = T (K e^b),  U' = T V,  U = U' - W S        (delta-rule writes)
 //     O    = (Q e^b) S + P U
 //     S   <- Diag(e^{b_C}) S + (K e^{b_C - b})^T U
 // Decay factors are referenced to 16-token subtile boundaries so that every
-// factor fed to a product lies in [e^-80, e^80] (the page's bound):
-//     lam_r = running sum of g inside r's subtile (in [-80, 0]),
-//     Lam_I = the subtile total.  For rows r in subtile I and columns s in J:
+// factor fed to a product lies in [e^-80, e^80] (the page's bound).  With
+// lam_r the running sum of g inside r's subtile and Lam_I the subtile total,
+// rows r in subtile I and columns s in subtile J use
 //       J == I : e^{lam_r} * e^{-lam_s}                               (<= 1 * <= e^80)
 //       J <  I : e^{lam_r} * e^{Lam_J - lam_s} * e^{sum_{J<K<I} Lam_K}   (all <= 1)
+// All of them are products of alpha = exp(g) over token ranges of at most 16
+// tokens (>= e^-80, no underflow) and of subtile totals, so the kernel takes
+// one exponential per element and forms the factors as running products.
 //
-// Work per chunk (one workgroup of 4 waves; wave w owns subtile w in the
-// intra-chunk stages and dv column block(s) w, w+4, .. in the state pass):
-//   A  prep     raw q/k/v/g/beta (prefetched into registers one chunk ahead
-//               with 8/16-byte loads) -> in-wave running sums -> decayed
-//               operand tiles in LDS (beta folded into K and V rows)
+// Work per chunk, one workgroup of NW waves (8 for bf16 at dk = 128: two
+// waves per SIMD, so one wave's LDS/MFMA/barrier waits overlap the other's
+// work; the LDS plan allows one workgroup per CU).  NW/4 waves share each
+// 16-token subtile in the prep stage; wave w owns dv column block(s)
+// w, w+NW, .. in the state pass:
+//   A  prep     raw q/k/v/g/beta (prefetched into registers one chunk ahead)
+//               -> alpha, running products (in-wave) -> decayed operand
+//               tiles in LDS
 //   B  scores   A and P, 20 16x16 tiles on MFMA; P kept as bf16 hi + lo
 //   C  inverse  X = (I + A)^-1 on MFMA: diagonal 16x16 blocks by the product
 //               (I+N)(I+N^2)(I+N^4)(I+N^8) with N = -A_II (A_II^16 = 0), the
 //               blocks below by block substitution, one level per barrier
 //   D  W, U'    on MFMA
-//   E  state    per wave, no barrier: U = U' - W S (kept as bf16 hi + lo),
-//               O = Q~ S + P U to HBM, S <- e^{b_C} S + K^^T U (fp32 state in
-//               MFMA accumulator registers, a bf16 copy in LDS as an operand)
+//   E  state    per wave, no barrier: U = U' - W S (hi + lo), O = Q~ S + P U
+//               to HBM, S <- e^{b_C} S + K^^T U; S and U stay in MFMA
+//               accumulator registers and enter products from registers
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -63,6 +69,21 @@ __device__ __forceinline__ floatx4 to_f4(bf16x4 x) {
 }
 __device__ __forceinline__ floatx4 to_f4(floatx4 x) { return x; }
 
+__device__ __forceinline__ floatx4 exp2_4(floatx4 x) {
+    return floatx4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]),
+                   __builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3])};
+}
+__device__ __forceinline__ floatx4 rcp_4(floatx4 x) {
+    return floatx4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]),
+                   __builtin_amdgcn_rcpf(x[2]), __builtin_amdgcn_rcpf(x[3])};
+}
+
+// Physical LDS row of channel-major row c (rows hold tokens contiguously).
+// The prep stage writes rows 4 apart from neighbouring lanes and the MFMA
+// fragments read 16 consecutive rows; shifting by one row every 8 rows puts
+// both patterns on distinct bank groups.
+__device__ __forceinline__ int crow(int c) { return c + (c >> 3); }
+
 // LDS plan (byte offsets).  LDK: pitch of token rows (channels contiguous);
 // LDT: pitch of channel rows (tokens contiguous).
 template <typename T, int DK, int NV> struct ChunkLds {
@@ -84,23 +105,17 @@ template <typename T, int DK, int NV> struct ChunkLds {
     static constexpr int XC = XR + TILE64;
     static constexpr int AB = XC + TILE64;
     static constexpr int R1_INV = AB + TILE64;
-    // stage D on: -W over XC and AB (dead by then); stage E: U^T hi over XR
-    // (dead after stage D), U^T lo after AB
+    // stage D on: -W over XC and AB (dead by then)
     static constexpr int WN = XC;
-    static constexpr int UTH = XR;
-    static constexpr int UTL = R1_INV;
     static_assert(64 * LDK * E <= 2 * TILE64, "-W must fit over X^c and A");
-    static_assert(NV * LDT * E <= TILE64, "U^T hi must fit over X");
-    static constexpr int R1_E = UTL + (SPLIT ? NV * LDT * E : 0);
-    static constexpr int R1 = R1_OPS > R1_E ? R1_OPS : R1_E;
-    // region 2: operands of the state pass, the state copy, small tables
+    static constexpr int R1 = R1_OPS > R1_INV ? R1_OPS : R1_INV;
+    // region 2: operands of the state pass, small tables
     static constexpr int QT = R1;
     static constexpr int KTT = QT + 64 * LDK * E;
-    static constexpr int KHT = KTT + DK * LDT * E;
-    static constexpr int VT = KHT + DK * LDT * E;
-    static constexpr int ST = VT + NV * LDT * E;
-    static constexpr int LAM = ST + NV * LDK * E;
-    static constexpr int EBC = LAM + 4 * DK * 4;
+    static constexpr int KHT = KTT + (DK + DK / 8) * LDT * E;
+    static constexpr int VT = KHT + (DK + DK / 8) * LDT * E;
+    static constexpr int EL = VT + (NV + NV / 8) * LDT * E;
+    static constexpr int EBC = EL + 4 * DK * 4;
     static constexpr int BETA = EBC + DK * 4;
     static constexpr int TOTAL = BETA + 64 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -108,9 +123,8 @@ template <typename T, int DK, int NV> struct ChunkLds {
 
 // k extent of the causal product for row block I, rounded to the MFMA k step
 // (the blocks above the diagonal inside that extent hold zeros).
-template <typename T> __device__ __forceinline__ int kround(int I) {
-    constexpr int ks = Mma<T>::kStep;
-    return ((16 * (I + 1) + ks - 1) / ks) * ks;
+template <typename T> __host__ __device__ constexpr int kround(int I) {
+    return ((16 * (I + 1) + Mma<T>::kStep - 1) / Mma<T>::kStep) * Mma<T>::kStep;
 }
 
 // ---------------------------------------------------------------------------
@@ -160,28 +174,163 @@ template <int N> __device__ __forceinline__ void storeN(float *p, const float *x
     }
 }
 
-// Order this wave's earlier LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// ---------------------------------------------------------------------------
+// Fragment loaders.
+// Kc: the k-contiguous form (8 consecutive bf16 / 4 fp32 per lane), used by
+// products whose two operands both come from LDS.
+// Perm: "register-layout" k fragments.  An accumulator tile holds, in lane l,
+// rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.  Feeding those k positions
+// (of two adjacent tiles for the 32-deep bf16 instruction) as one operand and
+// the same k positions of an LDS row as the other contracts the right pairs
+// whatever order the instruction visits k in, so the fp32 state and U enter
+// products straight from registers.
+// ---------------------------------------------------------------------------
+template <typename T> struct Kc;
+template <> struct Kc<bf16> {
+    typedef bf16x8 frag;
+    static constexpr int kStep = 32;
+    __device__ __forceinline__ static frag load(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ static void mma(floatx4 &acc, frag x, frag y) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+    }
+};
+template <> struct Kc<float> {
+    typedef floatx4 frag;
+    static constexpr int kStep = 16;
+    __device__ __forceinline__ static frag load(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+    __device__ __forceinline__ static void mma(floatx4 &acc, frag x, frag y) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[0], y[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[1], y[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[2], y[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[3], y[3], acc, 0, 0, 0);
+    }
+};
+
+template <typename T> struct Perm;
+template <> struct Perm<bf16> {
+    static constexpr int kStep = 32;              // k per instruction = two 16-row tiles
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static frag lds(const bf16 *row, int k0, int g4) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row + k0 + g4);
+        const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row + k0 + 16 + g4);
+        return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    __device__ __forceinline__ static frag regs(const floatx4 *t) {
+        return frag{(bf16)t[0][0], (bf16)t[0][1], (bf16)t[0][2], (bf16)t[0][3],
+                    (bf16)t[1][0], (bf16)t[1][1], (bf16)t[1][2], (bf16)t[1][3]};
+    }
+    // the rounding residual of regs(t), as a second bf16 fragment
+    __device__ __forceinline__ static frag regs_lo(const floatx4 *t) {
+        frag f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[j] = (bf16)(t[0][j] - (float)(bf16)t[0][j]);
+            f[4 + j] = (bf16)(t[1][j] - (float)(bf16)t[1][j]);
+        }
+        return f;
+    }
+    __device__ __forceinline__ static void mma(floatx4 &acc, frag x, frag y) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+    }
+};
+template <> struct Perm<float> {
+    static constexpr int kStep = 16;              // k per step = one 16-row tile
+    typedef floatx4 frag;
+    __device__ __forceinline__ static frag lds(const float *row, int k0, int g4) {
+        return *reinterpret_cast<const floatx4 *>(row + k0 + g4);
+    }
+    __device__ __forceinline__ static frag regs(const floatx4 *t) { return t[0]; }
+    __device__ __forceinline__ static frag regs_lo(const floatx4 *) { return floatx4{0, 0, 0, 0}; }
+    __device__ __forceinline__ static void mma(floatx4 &acc, frag x, frag y) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[0], y[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[1], y[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[2], y[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[3], y[3], acc, 0, 0, 0);
+    }
+};
+
+// NT independent 16x16 tiles, NS k steps each, with the fragments of step
+// s + 1 requested from LDS before the MFMAs of step s are issued (one wave per
+// SIMD leaves no other wave to hide LDS latency).  xp(i, s) / yp(i, s) return
+// lane row pointers already offset to step s.
+template <typename F, int NT, int NS, typename XP, typename YP>
+__device__ __forceinline__ void group_mma(floatx4 (&acc)[NT], XP xp, YP yp) {
+    typename F::frag xa[NT], ya[NT], xb[NT], yb[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) { xa[i] = F::load(xp(i, 0)); ya[i] = F::load(yp(i, 0)); }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        if (st + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) { xb[i] = F::load(xp(i, st + 1)); yb[i] = F::load(yp(i, st + 1)); }
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) F::mma(acc[i], xa[i], ya[i]);
+        if (st + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) { xa[i] = xb[i]; ya[i] = yb[i]; }
+        }
+    }
 }
 
-template <typename T, int DK, int NV>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
+// As group_mma, for tiles that share their second operand: it is fetched
+// once per k step.
+template <typename F, int NT, int NS, typename XP, typename YP>
+__device__ __forceinline__ void group_mma_shared_y(floatx4 (&acc)[NT], XP xp, YP yp) {
+    typename F::frag xa[NT], xb[NT], ya, yb;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) xa[i] = F::load(xp(i, 0));
+    ya = F::load(yp(0));
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        if (st + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) xb[i] = F::load(xp(i, st + 1));
+            yb = F::load(yp(st + 1));
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) F::mma(acc[i], xa[i], ya);
+        if (st + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) xa[i] = xb[i];
+            ya = yb;
+        }
+    }
+}
+
+// Byte offset from a base pointer (offsets of one chunk fit in 32 bits).
+template <typename P> __device__ __forceinline__ const P *at(const void *base, unsigned bytes) {
+    return reinterpret_cast<const P *>(static_cast<const char *>(base) + bytes);
+}
+
+template <typename T, int DK, int NV, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
     using Lds = ChunkLds<T, DK, NV>;
     using T4 = typename Quad<T>::type;
+    using KF = Kc<T>;
+    using PF = Perm<T>;
     constexpr int LDK = Lds::LDK, LDT = Lds::LDT;
     constexpr bool kSplit = Lds::SPLIT;              // keep P and U as bf16 hi + lo
-    // prep mapping: thread = (channel quad cq, token group tg); wave w <-> subtile w
+    // prep mapping: a wave covers one 16-token subtile x QPW channel quads;
+    // lane = (token group pos, quad); a thread holds TPT tokens x 4 channels
+    constexpr int NTH = NW * 64;
     constexpr int NQ = DK / 4;                       // channel quads
-    constexpr int TPT = DK / 16;                     // tokens per thread (8, 4, 2)
+    constexpr int TPT = DK / (4 * NW);               // tokens per thread
+    constexpr int SUBT = 16 / TPT;                   // threads along one subtile column quad
+    constexpr int QPW = 64 / SUBT;                   // channel quads per wave
+    constexpr int WPS = NW / 4;                      // waves per subtile
     constexpr int NVQ = NV / 4;                      // dv quads of the slice
-    constexpr int TPV = NV / 16;                     // v tokens per thread
+    constexpr int TPV = NV * 16 / NTH;               // v tokens per thread
     constexpr int NSB = NV / 16;                     // state column blocks
-    constexpr int NOWN = (NSB + 3) / 4;              // column blocks owned per wave
+    constexpr int NOWN = (NSB + NW - 1) / NW;        // column blocks owned per wave
+    constexpr int NSC = (20 + NW - 1) / NW;          // score tiles per wave
     constexpr int NCB = DK / 16;                     // state row blocks
-    static_assert(256 == NQ * (64 / TPT) && 256 == NVQ * (64 / TPV), "prep mapping");
+    constexpr int NKS = DK / PF::kStep;              // k steps over channels
+    constexpr int NKT = kChunk / PF::kStep;          // k steps over tokens
+    constexpr int TPS = PF::kStep / 16;              // accumulator tiles per k step
+    constexpr float kLog2e = 1.4426950408889634f;
+    static_assert(TPT >= 1 && NQ == QPW * WPS && NW % 4 == 0, "prep mapping");
+    static_assert(TPV >= 2 && NTH == NVQ * (64 / TPV), "v mapping");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::TOTAL];
     T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
@@ -193,14 +342,11 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     T *sXc = reinterpret_cast<T *>(smem + Lds::XC);
     T *sA = reinterpret_cast<T *>(smem + Lds::AB);
     T *sWn = reinterpret_cast<T *>(smem + Lds::WN);
-    T *sUh = reinterpret_cast<T *>(smem + Lds::UTH);
-    T *sUl = reinterpret_cast<T *>(smem + Lds::UTL);
     T *sQt = reinterpret_cast<T *>(smem + Lds::QT);
     T *sKtT = reinterpret_cast<T *>(smem + Lds::KTT);
     T *sKhT = reinterpret_cast<T *>(smem + Lds::KHT);
     T *sVT = reinterpret_cast<T *>(smem + Lds::VT);
-    T *sST = reinterpret_cast<T *>(smem + Lds::ST);
-    float *sLam = reinterpret_cast<float *>(smem + Lds::LAM);
+    float *sEL = reinterpret_cast<float *>(smem + Lds::EL);
     float *sEbC = reinterpret_cast<float *>(smem + Lds::EBC);
     float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA);
 
@@ -213,8 +359,12 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
-    const int cq = tid % NQ, tg = tid / NQ, pos = lane / NQ;   // pos: rank inside the subtile
+    const int I = wave / WPS;                                    // this wave's prep subtile
+    const int pos = lane / QPW;                                  // rank inside the subtile
+    const int cq = (wave % WPS) * QPW + lane % QPW;              // channel quad
+    const int tb = 16 * I + pos * TPT;                           // first token of this thread
     const int vq = tid % NVQ, tv = tid / NVQ;
+    const int IB = wave;                                         // inverse / W row block (waves < 4)
 
     // Work item (chain bh, dv slice).  With the XCD mapping the slices of one
     // chain land on one XCD (workgroups are dealt round-robin over 8 XCDs) and
@@ -236,48 +386,54 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const int64_t T_ = a.T;
     const int vcol0 = slice * NV;
     const int64_t nchunk = (T_ + kChunk - 1) / kChunk;
+    const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
 
     // ---- raw chunk inputs, prefetched one chunk ahead ---------------------
+    // Uniform chunk bases plus 32-bit lane offsets; the token index is clamped
+    // only in a partial last chunk.
     floatx4 rg[TPT];
     T4 rk[TPT], rq[TPT], rv[TPV];
-    float rbeta = 0.0f;
+    T rbeta;
     auto load_raw = [&](int64_t ch) {
         const int64_t t0 = ch * kChunk;
         const int L = (int)((T_ - t0) < kChunk ? (T_ - t0) : kChunk);
         const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
+        const void *gb = gp + tok0 * DK;
+        const void *kb = kp + tok0 * DK, *qb = qp + tok0 * DK;
+        const void *vb = vp + tok0 * DV + vcol0;
+        const void *bb = bp + tok0;
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
-            const int tl = tg * TPT + i;
-            const int tc = tl < L ? tl : L - 1;          // clamp: never read past the end
-            const int64_t e = (tok0 + (int64_t)tc * H) * DK + 4 * cq;
-            rg[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(gp + e));
-            rk[i] = *reinterpret_cast<const T4 *>(kp + e);
-            rq[i] = *reinterpret_cast<const T4 *>(qp + e);
+            int tl = tb + i;
+            if (L < kChunk) tl = tl < L ? tl : L - 1;
+            const unsigned e = (unsigned)tl * HDK + 4 * cq;
+            rg[i] = __builtin_nontemporal_load(at<floatx4>(gb, e * 4u));
+            rk[i] = *at<T4>(kb, e * (unsigned)sizeof(T));
+            rq[i] = *at<T4>(qb, e * (unsigned)sizeof(T));
         }
 #pragma unroll
         for (int i = 0; i < TPV; ++i) {
-            const int tl = tv * TPV + i;
-            const int tc = tl < L ? tl : L - 1;
-            rv[i] = *reinterpret_cast<const T4 *>(vp + (tok0 + (int64_t)tc * H) * DV + vcol0 + 4 * vq);
+            int tl = tv * TPV + i;
+            if (L < kChunk) tl = tl < L ? tl : L - 1;
+            rv[i] = *at<T4>(vb, ((unsigned)tl * HDV + 4 * vq) * (unsigned)sizeof(T));
         }
-        if (tid < 64) rbeta = to_f32(bp[tok0 + (int64_t)(tid < L ? tid : L - 1) * H]);
+        // every lane loads (no branch), so nothing forces an early wait on the batch
+        rbeta = *at<T>(bb, (unsigned)(lane < L ? lane : L - 1) * (unsigned)H * (unsigned)sizeof(T));
     };
 
     // ---- state: fp32 accumulator tiles of the owned column blocks ----------
     floatx4 sacc[NOWN][NCB];
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
-        const int nb = wave + 4 * m;
+        const int nb = wave + NW * m;
         if (nb < NSB) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
                     sacc[m][cb][j] = a.S0 ? a.S0[((int64_t)bh * DK + c) * DV + n] : 0.0f;
                 }
-                store4v(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[m][cb]);
-            }
         }
     }
 
@@ -285,144 +441,146 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     for (int64_t ch = 0; ch < nchunk; ++ch) {
         const int64_t t0 = ch * kChunk;
         const int L = (int)((T_ - t0) < kChunk ? (T_ - t0) : kChunk);
+        const bool full = L == kChunk;
         const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
-        const int I = wave;                              // this wave's subtile
+        const void *obase = op + tok0 * DV + vcol0;
 
-        // ---- A1: running log-decay inside the subtile (in-wave scan) --------
-        floatx4 lam[TPT];
-        floatx4 run = {0, 0, 0, 0};
+        // ---- A1: alpha and its running products inside the subtile --------
+        // R_i = e^{lam_i} (product up to token i), Et_i = e^{Lam - lam_i}
+        // (product after token i), eLam = e^{Lam} (whole subtile).
+        floatx4 R[TPT], Et[TPT], eLam;
+        {
+            // past the end of the sequence alpha = 1 (g = 0), so e^{b_C} stops
+            // at the last token; beta = 0 there (below) zeroes those rows of A
+            // and of T = X Diag(beta), hence of U, so no other input is masked
+            floatx4 al[TPT];
+            if (full) {
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const bool ok = tg * TPT + i < L;
-            run += ok ? rg[i] : floatx4{0, 0, 0, 0};
-            lam[i] = run;
+                for (int i = 0; i < TPT; ++i) al[i] = exp2_4(rg[i] * kLog2e);
+            } else {
+#pragma unroll
+                for (int i = 0; i < TPT; ++i)
+                    al[i] = tb + i < L ? exp2_4(rg[i] * kLog2e) : floatx4{1, 1, 1, 1};
+            }
+            floatx4 tot = al[0];
+#pragma unroll
+            for (int i = 1; i < TPT; ++i) tot *= al[i];
+            floatx4 pre = {1, 1, 1, 1}, suf = {1, 1, 1, 1};
+#pragma unroll
+            for (int s = 1; s < SUBT; ++s) {
+                floatx4 fw, bw;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    fw[j] = __shfl(tot[j], lane - s * QPW);
+                    bw[j] = __shfl(tot[j], lane + s * QPW);
+                }
+                if (pos >= s) pre *= fw;
+                if (pos + s < SUBT) suf *= bw;
+            }
+            R[0] = pre * al[0];
+#pragma unroll
+            for (int i = 1; i < TPT; ++i) R[i] = R[i - 1] * al[i];
+            Et[TPT - 1] = suf;
+#pragma unroll
+            for (int i = TPT - 2; i >= 0; --i) Et[i] = Et[i + 1] * al[i + 1];
+            eLam = R[TPT - 1] * suf;
         }
-        floatx4 pre = {0, 0, 0, 0};
-#pragma unroll
-        for (int s = 1; s < 64 / NQ; ++s) {
-            floatx4 other;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) other[j] = __shfl(run[j], lane - s * NQ);
-            if (pos >= s) pre += other;
-        }
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) lam[i] += pre;
-        if (pos == 64 / NQ - 1)
-            *reinterpret_cast<floatx4 *>(sLam + I * DK + 4 * cq) = lam[TPT - 1];
-        if (tid < 64) sBeta[tid] = tid < L ? rbeta : 0.0f;
-        __syncthreads();
+        if (pos == 0) *reinterpret_cast<floatx4 *>(sEL + I * DK + 4 * cq) = eLam;
+        if (tid < 64) sBeta[tid] = tid < L ? to_f32(rbeta) : 0.0f;
+        lds_barrier();
 
         // ---- A2: decayed operand tiles -------------------------------------
         {
-            const floatx4 L0 = *reinterpret_cast<const floatx4 *>(sLam + 4 * cq);
-            const floatx4 L1 = *reinterpret_cast<const floatx4 *>(sLam + DK + 4 * cq);
-            const floatx4 L2 = *reinterpret_cast<const floatx4 *>(sLam + 2 * DK + 4 * cq);
-            const floatx4 L3 = *reinterpret_cast<const floatx4 *>(sLam + 3 * DK + 4 * cq);
-            const floatx4 pre1 = L0, pre2 = L0 + L1, pre3 = pre2 + L2, pre4 = pre3 + L3;
-            const floatx4 preI = I == 0 ? floatx4{0, 0, 0, 0} : I == 1 ? pre1 : I == 2 ? pre2 : pre3;
-            const floatx4 LamI = I == 0 ? L0 : I == 1 ? L1 : I == 2 ? L2 : L3;
-            const floatx4 preI1 = preI + LamI;             // b at the end of subtile I
-            floatx4 ePre, eNegLam, eHat, eOff1, eOff2, eOff3;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ePre[j] = __expf(preI[j]);                 // e^{b before subtile I}  <= 1
-                eNegLam[j] = __expf(-LamI[j]);             // <= e^80
-                eHat[j] = __expf(pre4[j] - preI1[j]);      // e^{b_C - b_end(I)}    <= 1
-                // e^{sum_{I<K<I2} Lam_K}, used only for I2 > I
-                eOff1[j] = __expf(I < 1 ? pre1[j] - preI1[j] : 0.0f);
-                eOff2[j] = __expf(I < 2 ? pre2[j] - preI1[j] : 0.0f);
-                eOff3[j] = __expf(I < 3 ? pre3[j] - preI1[j] : 0.0f);
-            }
-            if (I == 0 && pos == 0) {
-                floatx4 ebc;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ebc[j] = __expf(pre4[j]);
-                *reinterpret_cast<floatx4 *>(sEbC + 4 * cq) = ebc;
-            }
-            float ktb[4][TPT], kh[4][TPT];
+            const floatx4 e0 = *reinterpret_cast<const floatx4 *>(sEL + 4 * cq);
+            const floatx4 e1 = *reinterpret_cast<const floatx4 *>(sEL + DK + 4 * cq);
+            const floatx4 e2 = *reinterpret_cast<const floatx4 *>(sEL + 2 * DK + 4 * cq);
+            const floatx4 e3 = *reinterpret_cast<const floatx4 *>(sEL + 3 * DK + 4 * cq);
+            const floatx4 one = {1, 1, 1, 1};
+            // e^{b before subtile I}, e^{b_C - b_end(I)}: products of subtile totals
+            const floatx4 ePre = I == 0 ? one : I == 1 ? e0 : I == 2 ? e0 * e1 : e0 * e1 * e2;
+            const floatx4 eHat = I == 0 ? e1 * e2 * e3 : I == 1 ? e2 * e3 : I == 2 ? e3 : one;
+            const floatx4 eNegLam = rcp_4(eLam);                 // e^{-Lam_I} <= e^80
+            // e^{sum_{I<K<I2} Lam_K} for the column tiles of pairs (I2, I), I2 > I
+            const floatx4 eOff2 = I == 0 ? e1 : one;
+            const floatx4 eOff3 = I == 0 ? e1 * e2 : I == 1 ? e2 : one;
+            if (I == 0 && pos == 0)
+                *reinterpret_cast<floatx4 *>(sEbC + 4 * cq) = e0 * e1 * e2 * e3;
+            float kt[4][TPT], kh[4][TPT];
 #pragma unroll
             for (int i = 0; i < TPT; ++i) {
-                const int tl = tg * TPT + i;               // token inside the chunk
+                const int tl = tb + i;                     // token inside the chunk
                 const int r = tl - 16 * I;                 // row inside the subtile
-                const bool ok = tl < L;
-                const floatx4 kv = ok ? to_f4(rk[i]) : floatx4{0, 0, 0, 0};
-                const floatx4 qv = ok ? to_f4(rq[i]) : floatx4{0, 0, 0, 0};
-                const float bt = sBeta[tl];
-                floatx4 R, Et;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    R[j] = __expf(lam[i][j]);              // e^{lam_r}          in [e^-80, 1]
-                    Et[j] = __expf(LamI[j] - lam[i][j]);   // e^{Lam_I - lam_r}  in [e^-75, 1]
-                }
-                const floatx4 kEt = kv * Et;
-                store4v(sKr + tl * LDK + 4 * cq, kv * R * bt);
-                store4v(sQr + tl * LDK + 4 * cq, qv * R);
+                const floatx4 kv = to_f4(rk[i]), qv = to_f4(rq[i]);
+                const floatx4 kR = kv * R[i], qR = qv * R[i];
+                store4v(sKr + tl * LDK + 4 * cq, kR);
+                store4v(sQr + tl * LDK + 4 * cq, qR);
+                const floatx4 kEt = kv * Et[i];
                 // column operands: diagonal pair (I,I) and off-diagonal pairs (I2,I), I2 > I
                 store4v(sKc + (((I * (I + 1)) / 2 + I) * 16 + r) * LDK + 4 * cq, kEt * eNegLam);
-                if (I < 1) store4v(sKc + ((1 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff1);
+                if (I < 1) store4v(sKc + ((1 + I) * 16 + r) * LDK + 4 * cq, kEt);
                 if (I < 2) store4v(sKc + ((3 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff2);
                 if (I < 3) store4v(sKc + ((6 + I) * 16 + r) * LDK + 4 * cq, kEt * eOff3);
-                const floatx4 eb = R * ePre;               // e^{b_r} <= 1
-                store4v(sQt + tl * LDK + 4 * cq, qv * eb);
-                const floatx4 kt = kv * eb * bt, khv = kEt * eHat;
+                store4v(sQt + tl * LDK + 4 * cq, qR * ePre);   // q e^{b_r}
+                const floatx4 ktv = kR * ePre, khv = kEt * eHat; // k e^{b_r}, k e^{b_C - b_r}
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    ktb[j][i] = kt[j];
+                    kt[j][i] = ktv[j];
                     kh[j][i] = khv[j];
                 }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                storeN<TPT>(sKtT + (4 * cq + j) * LDT + tg * TPT, ktb[j]);
-                storeN<TPT>(sKhT + (4 * cq + j) * LDT + tg * TPT, kh[j]);
+                storeN<TPT>(sKtT + crow(4 * cq + j) * LDT + tb, kt[j]);
+                storeN<TPT>(sKhT + crow(4 * cq + j) * LDT + tb, kh[j]);
             }
             float vt[4][TPV];
 #pragma unroll
             for (int i = 0; i < TPV; ++i) {
-                const int tl = tv * TPV + i;
-                const float bt = sBeta[tl];                // 0 past the end of the sequence
-                const floatx4 vv = to_f4(rv[i]) * bt;
+                const floatx4 vv = to_f4(rv[i]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vt[j][i] = tl < L ? vv[j] : 0.0f;
+                for (int j = 0; j < 4; ++j) vt[j][i] = vv[j];
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) storeN<TPV>(sVT + (4 * vq + j) * LDT + tv * TPV, vt[j]);
+            for (int j = 0; j < 4; ++j) storeN<TPV>(sVT + crow(4 * vq + j) * LDT + tv * TPV, vt[j]);
         }
         if (ch + 1 < nchunk) load_raw(ch + 1);            // lands during stages B-E
-        __syncthreads();
+        lds_barrier();
 
         // ---- B: A and P tiles (10 causal subtile pairs each) -----------------
-        floatx4 sc[5];
+        floatx4 sc[NSC];
         {
-            const T *xs[5], *ys[5];
+            const int koff = (lane >> 4) * (KF::kStep / 4);
+            const T *xs[NSC], *ys[NSC];
 #pragma unroll
-            for (int u = 0; u < 5; ++u) {
-                const int ti = wave + 4 * u, p = ti >> 1;
+            for (int u = 0; u < NSC; ++u) {
+                const int ti = wave + NW * u < 20 ? wave + NW * u : 0;   // tiles past 20: unused
+                const int p = ti >> 1;
                 const int Ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
                 sc[u] = floatx4{0, 0, 0, 0};
-                xs[u] = sKc + p * 16 * LDK + lr * LDK + (lane >> 4) * (Mma<T>::kStep / 4);
-                ys[u] = ((ti & 1) ? sQr : sKr) + (16 * Ib + lr) * LDK + (lane >> 4) * (Mma<T>::kStep / 4);
+                xs[u] = sKc + (p * 16 + lr) * LDK + koff;
+                ys[u] = ((ti & 1) ? sQr : sKr) + (16 * Ib + lr) * LDK + koff;
             }
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += Mma<T>::kStep)
-#pragma unroll
-                for (int u = 0; u < 5; ++u) Mma<T>::step(sc[u], xs[u] + k0, ys[u] + k0);
+            group_mma<KF, NSC, DK / KF::kStep>(
+                sc, [&](int i, int st) { return xs[i] + st * KF::kStep; },
+                [&](int i, int st) { return ys[i] + st * KF::kStep; });
         }
-        __syncthreads();   // region 1 is rewritten below
+        lds_barrier();   // region 1 is rewritten below
 #pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int ti = wave + 4 * u, p = ti >> 1;
+        for (int u = 0; u < NSC; ++u) {
+            const int ti = wave + NW * u, p = ti >> 1;
+            if (ti >= 20) break;
             const int Ib = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
             const int J = p - (Ib * (Ib + 1)) / 2;
             const bool isP = ti & 1;
+            const int r = 16 * Ib + lr;
+            const float rowscale = isP ? 1.0f : sBeta[r];   // A_rs carries beta_r
             floatx4 val;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int s = lg4 + j;                     // column inside block J
                 const bool keep = (J < Ib) || (isP ? (s <= lr) : (s < lr));
-                val[j] = keep ? sc[u][j] : 0.0f;
+                val[j] = keep ? sc[u][j] * rowscale : 0.0f;
             }
-            const int r = 16 * Ib + lr;
             if (isP) {
                 store4v(sPh + r * LDT + 16 * J + lg4, val);
                 if constexpr (kSplit) {
@@ -437,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
         }
         // zero the blocks above the diagonal of P (hi, lo) and X (read by the
         // rounded-up causal products)
-        for (int e = tid; e < 6 * 64; e += 256) {
+        for (int e = tid; e < 6 * 64; e += NTH) {
             const int blk = e >> 6, q4 = e & 63, rr = q4 >> 2, cc = (q4 & 3) * 4;
             const int Iu = blk < 3 ? 0 : blk < 5 ? 1 : 2;
             const int Ju = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
@@ -446,11 +604,11 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
             if constexpr (kSplit) store4(sPl + off, 0.f, 0.f, 0.f, 0.f);
             store4(sXr + off, 0.f, 0.f, 0.f, 0.f);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- C: X = (I + A)^-1 ----------------------------------------------
         floatx4 xT;                                        // L(X_II^T) of this wave's block
-        {
+        if (IB < 4) {
             const T tz = T(0);
             auto addI = [&](floatx4 m) {
 #pragma unroll
@@ -459,131 +617,173 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
             };
             const floatx4 z4 = {0, 0, 0, 0};
             // N = -A_II in both layouts
-            const floatx4 nT = -lds_load4(sA + (16 * I + lr) * LDT + 16 * I + lg4);
+            const floatx4 nT = -lds_load4(sA + (16 * IB + lr) * LDT + 16 * IB + lg4);
             floatx4 n;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * I + lg4 + j) * LDT + 16 * I + lr]);
+            for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * IB + lg4 + j) * LDT + 16 * IB + lr]);
             const floatx4 n2 = mma16(tz, nT, n, z4);
             const floatx4 n2T = mma16(tz, n, nT, z4);
             const floatx4 n4 = mma16(tz, n2T, n2, z4);
             const floatx4 n4T = mma16(tz, n2, n2T, z4);
             const floatx4 n8 = mma16(tz, n4T, n4, z4);
-            const floatx4 p1 = mma16(tz, addI(nT), addI(n2), z4);
-            const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);
-            (void)p1;
-            const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);
-            const floatx4 p2 = mma16(tz, p1T, addI(n4), z4);
-            (void)p2;
-            const floatx4 x = mma16(tz, p2T, addI(n8), z4);
+            const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);    // ((I+N)(I+N^2))^T
+            const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);         // (P1 (I+N^4))^T
+            const floatx4 x = mma16(tz, p2T, addI(n8), z4);           // P2 (I+N^8)
             xT = mma16(tz, addI(n8), p2T, z4);
-            store4v(sXc + (16 * I + lr) * LDT + 16 * I + lg4, x);
-            store4v(sXr + (16 * I + lr) * LDT + 16 * I + lg4, xT);
-            __syncthreads();
+            // X^c keeps X itself; the row-major copy feeds W and U' and carries
+            // Diag(beta) on its columns: T = X Diag(beta)
+            const floatx4 bI = *reinterpret_cast<const floatx4 *>(sBeta + 16 * IB + lg4);
+            store4v(sXc + (16 * IB + lr) * LDT + 16 * IB + lg4, x);
+            store4v(sXr + (16 * IB + lr) * LDT + 16 * IB + lg4, xT * bI);
+        }
+        lds_barrier();
+        {
+            const T tz = T(0);
+            const floatx4 z4 = {0, 0, 0, 0};
             // blocks below the diagonal, one level per barrier:
             // X_IJ = -X_II sum_{K=J}^{I-1} A_IK X_KJ, computed by the wave of row block I
 #pragma unroll
             for (int d = 1; d < 4; ++d) {
-                if (I >= d) {
-                    const int J = I - d;
+                if (IB < 4 && IB >= d) {
+                    const int J = IB - d;
                     floatx4 y = z4;
-                    for (int K = J; K < I; ++K)
-                        y = mma16(tz, lds_load4(sA + (16 * I + lr) * LDT + 16 * K + lg4),
+                    for (int K = J; K < IB; ++K)
+                        y = mma16(tz, lds_load4(sA + (16 * IB + lr) * LDT + 16 * K + lg4),
                                   lds_load4(sXc + (16 * J + lr) * LDT + 16 * K + lg4), y);
                     const floatx4 xij = -mma16(tz, xT, y, z4);
                     const floatx4 xijT = -mma16(tz, y, xT, z4);
-                    store4v(sXc + (16 * J + lr) * LDT + 16 * I + lg4, xij);
-                    store4v(sXr + (16 * I + lr) * LDT + 16 * J + lg4, xijT);
+                    const floatx4 bJ = *reinterpret_cast<const floatx4 *>(sBeta + 16 * J + lg4);
+                    store4v(sXc + (16 * J + lr) * LDT + 16 * IB + lg4, xij);
+                    store4v(sXr + (16 * IB + lr) * LDT + 16 * J + lg4, xijT * bJ);
                 }
-                __syncthreads();
+                lds_barrier();
             }
         }
 
-        // ---- D: -W = -X (beta K~) into LDS; U' = X (beta V) into registers ----
+        // ---- D: -W = -T K~ into LDS; U' = T V into registers ---------------
         {
-            floatx4 wacc[NCB];
-            const T *xs = sXr + (16 * I + lr) * LDT + (lane >> 4) * (Mma<T>::kStep / 4);
+            const int koff = (lane >> 4) * (KF::kStep / 4);
+            constexpr int NWT = NCB * 4 / NW;              // W tiles per wave
+            const int IW = wave % 4, cb0 = wave / 4;       // tiles (cb0 + (NW/4) u, IW)
+            floatx4 wacc[NWT];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) wacc[cb] = floatx4{0, 0, 0, 0};
-            const int KI = kround<T>(I);
-            for (int k0 = 0; k0 < KI; k0 += Mma<T>::kStep)
+            for (int u = 0; u < NWT; ++u) wacc[u] = floatx4{0, 0, 0, 0};
+            const T *ys = sXr + (16 * IW + lr) * LDT + koff;
+            auto xp = [&](int u, int st) {
+                return sKtT + crow(16 * (cb0 + (NW / 4) * u) + lr) * LDT + koff + st * KF::kStep;
+            };
+            auto yp = [&](int st) { return ys + st * KF::kStep; };
+            // k extent of row block IW in whole MFMA steps (blocks above the
+            // diagonal inside it are zero): bf16 1 or 2 steps, fp32 IW + 1 steps
+            const int nst = kround<T>(IW) / KF::kStep;
+            if (nst == 1) group_mma_shared_y<KF, NWT, 1>(wacc, xp, yp);
+            else if (nst == 2) group_mma_shared_y<KF, NWT, 2>(wacc, xp, yp);
+            else if constexpr (KF::kStep == 16) {
+                if (nst == 3) group_mma_shared_y<KF, NWT, 3>(wacc, xp, yp);
+                else group_mma_shared_y<KF, NWT, 4>(wacc, xp, yp);
+            }
+            // lane holds W^T[c = 16cb + lg4 + j][r = 16IW + lr]
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    Mma<T>::step(wacc[cb],
-                                 sKtT + (16 * cb + lr) * LDT + (lane >> 4) * (Mma<T>::kStep / 4) + k0,
-                                 xs + k0);
-            // lane holds W^T[c = 16cb + lg4 + j][r = 16I + lr]
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                store4v(sWn + (16 * I + lr) * LDK + 16 * cb + lg4, -wacc[cb]);
+            for (int u = 0; u < NWT; ++u)
+                store4v(sWn + (16 * IW + lr) * LDK + 16 * (cb0 + (NW / 4) * u) + lg4, -wacc[u]);
         }
         floatx4 uacc[NOWN][4];
 #pragma unroll
         for (int m = 0; m < NOWN; ++m) {
-            const int nb = wave + 4 * m;
+            const int nb = wave + NW * m;
             if (nb < NSB) {
+                const int koff = (lane >> 4) * (KF::kStep / 4);
+                const T *vr = sVT + crow(16 * nb + lr) * LDT + koff;
 #pragma unroll
                 for (int Is = 0; Is < 4; ++Is) {
                     uacc[m][Is] = floatx4{0, 0, 0, 0};
-                    tile_mma<T>(uacc[m][Is], sXr + 16 * Is * LDT, LDT, sVT + 16 * nb * LDT, LDT,
-                                kround<T>(Is), lane);
+                    const T *xr = sXr + (16 * Is + lr) * LDT + koff;
+#pragma unroll
+                    for (int k0 = 0; k0 < kround<T>(Is); k0 += KF::kStep)
+                        KF::mma(uacc[m][Is], KF::load(xr + k0), KF::load(vr + k0));
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- E: state pass of the owned column blocks (no barrier) ----------
+        // S and U stay in accumulator registers and enter the products as
+        // register-layout fragments; only W, Q~, P and K^ come from LDS.
 #pragma unroll
         for (int m = 0; m < NOWN; ++m) {
-            const int nb = wave + 4 * m;
+            const int nb = wave + NW * m;
             if (nb >= NSB) continue;
-            // U = U' - W S, kept as hi + lo (tokens contiguous)
+            typename PF::frag sf[NKS];                    // S^T rows of this column block
 #pragma unroll
-            for (int Is = 0; Is < 4; ++Is) {
-                tile_mma<T>(uacc[m][Is], sWn + 16 * Is * LDK, LDK, sST + 16 * nb * LDK, LDK, DK,
-                            lane);
-                store4v(sUh + (16 * nb + lr) * LDT + 16 * Is + lg4, uacc[m][Is]);
-                if constexpr (kSplit) {
-                    floatx4 lo;
+            for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[m][TPS * t]);
+            // U = U' - W S: four row tiles
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) lo[j] = uacc[m][Is][j] - (float)(bf16)uacc[m][Is][j];
-                    store4v(sUl + (16 * nb + lr) * LDT + 16 * Is + lg4, lo);
-                }
+            for (int t = 0; t < NKS; ++t) {
+                typename PF::frag wf[4];
+#pragma unroll
+                for (int Is = 0; Is < 4; ++Is) wf[Is] = PF::lds(sWn + (16 * Is + lr) * LDK, t * PF::kStep, lg4);
+#pragma unroll
+                for (int Is = 0; Is < 4; ++Is) PF::mma(uacc[m][Is], wf[Is], sf[t]);
             }
-            wave_lds_sync();
-            // O = Q~ S + P U for the 64 rows of this column block
+            typename PF::frag uh[NKT], ul[NKT];
 #pragma unroll
-            for (int Ir = 0; Ir < 4; ++Ir) {
-                floatx4 acc = {0, 0, 0, 0};
-                tile_mma<T>(acc, sST + 16 * nb * LDK, LDK, sQt + 16 * Ir * LDK, LDK, DK, lane);
-                const int KI = kround<T>(Ir);
-                tile_mma<T>(acc, sUh + 16 * nb * LDT, LDT, sPh + 16 * Ir * LDT, LDT, KI, lane);
-                if constexpr (kSplit) {
-                    tile_mma<T>(acc, sUl + 16 * nb * LDT, LDT, sPh + 16 * Ir * LDT, LDT, KI, lane);
-                    tile_mma<T>(acc, sUh + 16 * nb * LDT, LDT, sPl + 16 * Ir * LDT, LDT, KI, lane);
+            for (int t = 0; t < NKT; ++t) {
+                uh[t] = PF::regs(&uacc[m][TPS * t]);
+                if constexpr (kSplit) ul[t] = PF::regs_lo(&uacc[m][TPS * t]);
+            }
+            // O = Q~ S + P U for the 64 rows of this column block
+            {
+                floatx4 oacc[4];
+#pragma unroll
+                for (int Ir = 0; Ir < 4; ++Ir) oacc[Ir] = floatx4{0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < NKS; ++t) {
+                    typename PF::frag qf[4];
+#pragma unroll
+                    for (int Ir = 0; Ir < 4; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDK, t * PF::kStep, lg4);
+#pragma unroll
+                    for (int Ir = 0; Ir < 4; ++Ir) PF::mma(oacc[Ir], sf[t], qf[Ir]);
                 }
-                const int r = 16 * Ir + lr;
-                if (r < L)
-                    store4v(op + (tok0 + (int64_t)r * H) * DV + vcol0 + 16 * nb + lg4, acc);
+                // causal part: token step t reaches row tiles Ir with kround(Ir) > t * kStep
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int Ir = 0; Ir < 4; ++Ir)
+                        if (t * PF::kStep < kround<T>(Ir)) {
+                            const typename PF::frag ph = PF::lds(sPh + (16 * Ir + lr) * LDT, t * PF::kStep, lg4);
+                            PF::mma(oacc[Ir], uh[t], ph);
+                            if constexpr (kSplit) {
+                                PF::mma(oacc[Ir], ul[t], ph);
+                                PF::mma(oacc[Ir], uh[t], PF::lds(sPl + (16 * Ir + lr) * LDT, t * PF::kStep, lg4));
+                            }
+                        }
+#pragma unroll
+                for (int Ir = 0; Ir < 4; ++Ir) {
+                    const int r = 16 * Ir + lr;
+                    if (full || r < L)
+                        store4v(const_cast<T *>(at<T>(obase, ((unsigned)r * HDV + 16 * nb + lg4) *
+                                                                     (unsigned)sizeof(T))),
+                                oacc[Ir]);
+                }
             }
             // S <- Diag(e^{b_C}) S + K^^T U
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const floatx4 e = *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
-                sacc[m][cb] *= e;
-                tile_mma<T>(sacc[m][cb], sKhT + 16 * cb * LDT, LDT, sUh + 16 * nb * LDT, LDT,
-                            kChunk, lane);
-            }
-            wave_lds_sync();   // this wave's reads of the old state copy are done
+                typename PF::frag kf[NKT];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                store4v(sST + (16 * nb + lr) * LDK + 16 * cb + lg4, sacc[m][cb]);
+                for (int t = 0; t < NKT; ++t)
+                    kf[t] = PF::lds(sKhT + crow(16 * cb + lr) * LDT, t * PF::kStep, lg4);
+                sacc[m][cb] *= *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) PF::mma(sacc[m][cb], kf[t], uh[t]);
+            }
         }
     }
 
     if (a.ST) {
 #pragma unroll
         for (int m = 0; m < NOWN; ++m) {
-            const int nb = wave + 4 * m;
+            const int nb = wave + NW * m;
             if (nb >= NSB) continue;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
@@ -596,8 +796,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     }
 }
 
-// dv-slice width per workgroup: four 16-column blocks (one per wave) where
-// the LDS plan allows it.
+// dv-slice width per workgroup: 64 columns (fp32 at dk = 64: 32); bf16 at
+// dk = 128 runs 8 waves per workgroup, the other shapes 4.
 static int slice_width(int dk, int dv, int is_bf16) {
     int nv = 64;
     if (!is_bf16 && dk == 64) nv = 32;   // fp32 tiles at dk = 64 leave room for 32 columns
@@ -610,9 +810,9 @@ bool chunk_fwd_supported(int dk, int dv, int is_bf16) {
     return dk_ok && (dv == 32 || dv == 64 || dv == 128);
 }
 
-template <typename T, int DK, int NV>
+template <typename T, int DK, int NV, int NW = 4>
 static hipError_t launch_inst(const ChunkArgs &args, int nblocks, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_fwd_kernel<T, DK, NV>), dim3(nblocks), dim3(256), 0, s, args);
+    hipLaunchKernelGGL((chunk_fwd_kernel<T, DK, NV, NW>), dim3(nblocks), dim3(NW * 64), 0, s, args);
     return hipGetLastError();
 }
 
@@ -635,7 +835,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         case 64032: return launch_inst<bf16, 64, 32>(args, nblocks, s);
         case 64064: return launch_inst<bf16, 64, 64>(args, nblocks, s);
         case 128032: return launch_inst<bf16, 128, 32>(args, nblocks, s);
-        case 128064: return launch_inst<bf16, 128, 64>(args, nblocks, s);
+        case 128064: return launch_inst<bf16, 128, 64, 8>(args, nblocks, s);
+        case 128128: return launch_inst<bf16, 128, 128, 8>(args, nblocks, s);
         default: return hipErrorInvalidValue;
         }
     }

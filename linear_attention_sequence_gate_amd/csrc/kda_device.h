@@ -80,6 +80,15 @@ template <> struct Mma<float> {
     }
 };
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// and meets the other waves, but leaves global loads in flight (a plain
+// __syncthreads also drains them, which would expose the latency of loads
+// prefetched for a later stage).  No global memory is exchanged between the
+// threads of a workgroup in these kernels.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // K must be a multiple of Mma<T>::kStep.
 template <typename T>
 __device__ __forceinline__ void tile_mma(floatx4 &acc, const T *X, int ldx, const T *Y, int ldy,
