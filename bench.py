@@ -4,22 +4,40 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 A timed step is one pass of the prefill hot path over the synthetic batch
-B4 H32 T32768 d128 bf16 (half of the heads with the gate near its floor):
+B4 H32 T32768 d128 bf16 (heads 16..31 with the gate near its floor):
 kda_gate (z -> g) followed by kda_chunk_fwd (q, k, v, g, beta -> o, final
 state).  The decode step (256 sequences x H32, d128, fp32 state of 512 MiB
 updated in place) is timed in the same run over 1000 consecutive steps with
 fresh pre-generated inputs, and reported in the same JSON line.
 
-value   = prefill tokens/s (B*T tokens, all 32 heads, per wall-clock step)
-roofline= the chunked-prefill kernel against HBM (its arithmetic intensity,
-          ~99 flop/B, is below the MI355X ridge of ~312 flop/B)
-cpu_baseline = the fp64 oracle timed on this host on a bounded sample.
+value        prefill tokens/s (B*T tokens, all 32 heads, per wall-clock step)
+roofline     the chunked-prefill kernel against HBM: its arithmetic intensity
+             (~99 flop/B) is below the MI355X ridge (~312 flop/B)
+cpu_baseline the fp64 oracle timed on this host on a bounded sample of the same
+             workload (a reported baseline, not a target)
+
+    python bench.py --ingest-pmc FETCH_DIR WRITE_DIR
+
+reads the counter CSVs of two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+runs of this script, scales each kernel's counters by what they read for the
+plain 1 GiB device copy the script times, and writes profiles/hbm_traffic_*.md;
+later runs report those bytes as `traffic` while the kernel sources still hash
+to the recorded values.
+
+    python bench.py --ingest-trace TRACE_DIR
+
+summarises the kernel_trace.csv of a `rocprofv3 --kernel-trace --stats` run of
+this script into profiles/kernel_trace_*.md.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,33 +50,99 @@ from linear_attention_sequence_gate_amd import _lib, inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 
 PREFILL = inputs.WORKLOADS["prefill_b4_h32_t32k"]
 DECODE = inputs.WORKLOADS["decode_256x32"]
 
+CSRC = os.path.join(ROOT, "linear_attention_sequence_gate_amd", "csrc")
+PROFILE_TAG = "prefill_b4h32t32k_decode256x32"
+TRAFFIC_MD = os.path.join(ROOT, "profiles", f"hbm_traffic_{PROFILE_TAG}.md")
+TRACE_MD = os.path.join(ROOT, "profiles", f"kernel_trace_{PROFILE_TAG}.md")
+# kernel -> (name fragment in a profiler trace, sources that define it)
+KERNELS = {
+    "chunk_fwd": ("chunk_fwd_kernel", ("kda_chunk.hip", "kda_device.h")),
+    "decode_step": ("decode_step_kernel", ("kda_decode.hip", "kda_device.h")),
+    "gate": ("gate_kernel", ("kda_gate.hip", "kda_device.h")),
+}
+
+# UT inverse of one 64-token chunk, per head-token (block substitution over
+# 16x16 blocks; the same constant as the flop model of the scope table).
+INV_FLOPS_PER_HT = 2218
+
 
 def prefill_work(w, B=None, T=None, H=None):
-    """Algorithmic bytes and flops of one kda_chunk_fwd call (and of the gate)."""
+    """Algorithmic bytes and flops of one kda_chunk_fwd call (and of the gate).
+
+    Bytes: q, k, v, beta and o once in the input dtype, g once in fp32, the
+    final state (and the initial one when given) in fp32.
+    Flops per head-token (C = 64, dense 16-token diagonal subtiles, mean causal
+    length Lbar = (64 + 16) / 2 = 40): 6 dk dv for W S, Q~ S and K^T U; 2 Lbar
+    dk each for A, P and W; 2 Lbar dv each for U' and P U; the UT inverse."""
     B, T, H = B or w.B, T or w.T, H or w.H
     dk, dv = w.dk, w.dv
     e = 2 if w.dtype == torch.bfloat16 else 4
     ht = B * T * H                                   # head-tokens
-    chunk_bytes = ht * ((2 * dk + dv) * e + dk * 4 + e + dv * e)   # q,k,v + g + beta + o
-    chunk_bytes += B * H * dk * dv * 4 * (2 if w.s0_std > 0 else 1)  # state out (and in)
-    Lbar = (64 + 16) / 2                             # mean causal length with dense diagonal tiles
-    flops_per_ht = 6 * dk * dv + 2 * 2 * Lbar * dk + 2 * 2 * Lbar * dv + 2 * Lbar * dv
-    # = 6 d^2 (W S, Q S, K^T U) + A, P (2 L d each) + W, U' (2 L d each) + P U (2 L d);
-    # plus the UT inverse (~ C^2 * 16 / 3 per chunk ~ 1.4k per head-token at C=64)
-    flops_per_ht += 64 * 64 * 16 / 3 / 64 * 4
+    chunk_bytes = ht * ((2 * dk + dv) * e + dk * 4 + e + dv * e)
+    chunk_bytes += B * H * dk * dv * 4 * (2 if w.s0_std > 0 else 1)
+    Lbar = (64 + 16) / 2
+    flops_per_ht = 6 * dk * dv + 2 * Lbar * (3 * dk + 2 * dv) + INV_FLOPS_PER_HT
     gate_bytes = ht * dk * (e + 4)
     return dict(head_tokens=ht, chunk_bytes=chunk_bytes, chunk_flops=flops_per_ht * ht,
-                gate_bytes=gate_bytes)
+                flops_per_head_token=flops_per_ht, gate_bytes=gate_bytes)
 
 
 def decode_bytes(w):
+    """State read + written once, q/k/v/z/beta read, o written, A read."""
     N, H, dk, dv = w.B, w.H, w.dk, w.dv
     e = 2
     return N * H * (2 * dk * dv * 4 + (3 * dk + dv) * e + e + dv * e) + H * dk * 4
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Per-launch HBM bytes from the recorded counter summary for kernels whose
+    sources are unchanged since the counters were taken (else None)."""
+    out = {k: None for k in KERNELS}
+    try:
+        text = open(TRAFFIC_MD).read()
+    except OSError:
+        return out
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return out
+    rec = json.loads(m.group(1))
+    for k, (_, srcs) in KERNELS.items():
+        r = rec.get("kernels", {}).get(k)
+        if r and r.get("source_sha256") == source_hash(srcs):
+            out[k] = r["traffic_bytes"]
+    return out
+
+
+def time_copy(reps=5):
+    """Plain device copy of 1 GiB (the HBM calibration kernel for the counters)."""
+    src = torch.empty(COPY_BYTES // 4, device="cuda", dtype=torch.float32).normal_()
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / s / 1e9
 
 
 def time_prefill(steps, warmup):
@@ -68,7 +152,7 @@ def time_prefill(steps, warmup):
     g = torch.empty(x["z"].shape, device=dev, dtype=torch.float32)
     o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
     ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.current_stream()     # both kernels are launched on it
 
     def step(evs=None):
         if evs: evs[0].record(stream)
@@ -123,7 +207,7 @@ def parity_sample(res, n_tokens=2048):
     """rho of sampled chains of the last timed prefill output against the oracle
     (first n_tokens of one ordinary head and one decay-stress head)."""
     import oracle
-    x, w = res["x"], PREFILL
+    x = res["x"]
     out = {}
     for (b, h) in ((0, 3), (3, 29)):
         sl = lambda a: a[b:b + 1, :n_tokens, h:h + 1].contiguous()
@@ -135,24 +219,154 @@ def parity_sample(res, n_tokens=2048):
     return out
 
 
-def cpu_baseline(chains=8, tokens=4096):
-    """The fp64 oracle (as it stands) on a bounded sample of the prefill workload."""
+def cpu_baseline(x, budget_s=15.0, window=4096):
+    """The fp64 oracle (as it stands: gate, then the token recurrence with o) on
+    the workload's own inputs, all B*H chains, over successive token windows
+    (each window starts from the state the previous one ended in), until about
+    budget_s seconds of oracle time are spent.  Host copies are made outside
+    the timed region."""
     import oracle
     w = PREFILL
-    x = inputs.make_prefill_inputs(1, tokens, chains, w.dk, w.dv, w.dtype, w.seed,
-                                   stress_heads_mean=w.stress_heads_mean)
     threads = min(os.cpu_count() or 1, 16)
-    t0 = time.perf_counter()
-    g = oracle.gate(x["z"], x["A"])
-    oracle.forward(x["q"], x["k"], x["v"], g, x["beta"], None, col_block=w.dv // 8,
-                   nthreads=threads)
-    dt = time.perf_counter() - t0
-    head_tokens = chains * tokens
-    return {"value": head_tokens / w.H / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"gate + token recurrence in fp64 on {chains} heads x {tokens} tokens "
-                      f"of the B4 H32 T32768 d128 workload ({head_tokens} head-tokens, "
-                      f"{dt:.1f} s); tokens/s = head-tokens/s / 32 heads"}
+    A = x["A"].double().cpu()
+    S, spent, done, t_end = None, 0.0, 0, 0
+    for t0 in range(0, w.T, window):
+        sl = slice(t0, min(t0 + window, w.T))
+        h64 = {n: x[n][:, sl].double().cpu().numpy() for n in ("q", "k", "v", "z", "beta")}
+        t = time.perf_counter()
+        g = oracle.gate(h64["z"], A)
+        _, S = oracle.forward(h64["q"], h64["k"], h64["v"], g, h64["beta"], S,
+                              col_block=w.dv // 8, nthreads=threads)
+        spent += time.perf_counter() - t
+        done += w.B * w.H * (sl.stop - sl.start)
+        t_end = sl.stop
+        del h64, g
+        if spent >= budget_s:
+            break
+    return {"value": done / spent / w.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 gate + token recurrence (with outputs) over tokens 0..{t_end} of all "
+                      f"{w.B * w.H} chains of B4 H32 T32768 d128 ({done} head-tokens, "
+                      f"{spent:.1f} s on {threads} threads); tokens/s = head-tokens/s / 32"}
+
+
+# ---------------------------------------------------------------------------
+# counter ingestion (CPU only)
+# ---------------------------------------------------------------------------
+def _pmc_rows(d, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 counter_collection.csv."""
+    rows = []
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (f, r.get("Dispatch_Id", r.get("Correlation_Id")))
+                rows.append((key, r["Kernel_Name"], float(r["Counter_Value"])))
+    # sum the per-instance values of one dispatch
+    agg = {}
+    for key, name, val in rows:
+        n, v = agg.get(key, (name, 0.0))
+        agg[key] = (n, v + val)
+    return list(agg.values())
+
+
+def ingest_pmc(fetch_dir, write_dir):
+    cal = {}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)                 # values in KiB
+        # the 1 GiB device-to-device copies are the runtime's largest copyBuffer
+        # dispatches in the run
+        cb = [v * 1024 for n, v in rows if "copyBuffer" in n]
+        copies = [v for v in cb if v >= 0.9 * max(cb, default=0.0)]
+        if not copies or max(copies) < 0.25 * COPY_BYTES:
+            raise SystemExit(f"{counter}: no 1 GiB copy dispatch found in {d}")
+        cal[counter] = COPY_BYTES / (sum(copies) / len(copies))
+        for k, (frag, _) in KERNELS.items():
+            vals = [v * 1024 for n, v in rows if frag in n]
+            if vals:
+                per.setdefault(k, {})[counter] = (sum(vals) / len(vals), len(vals))
+    rec = {"copy_factor": {"fetch": cal["FETCH_SIZE"], "write": cal["WRITE_SIZE"]}, "kernels": {}}
+    for k, (_, srcs) in KERNELS.items():
+        if k not in per or len(per[k]) < 2:
+            continue
+        f = per[k]["FETCH_SIZE"][0] * cal["FETCH_SIZE"]
+        wb = per[k]["WRITE_SIZE"][0] * cal["WRITE_SIZE"]
+        rec["kernels"][k] = {"fetch_bytes": round(f), "write_bytes": round(wb),
+                             "traffic_bytes": round(f + wb),
+                             "dispatches": per[k]["FETCH_SIZE"][1],
+                             "source_sha256": source_hash(srcs)}
+    w = PREFILL
+    work = prefill_work(w)
+    alg = {"chunk_fwd": work["chunk_bytes"], "decode_step": decode_bytes(DECODE),
+           "gate": work["gate_bytes"]}
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Workloads: prefill B4 H32 T32768 d128 bf16 (gate + chunk), decode 256x32 d128.",
+             "Each counter is scaled by the factor that maps its reading for a plain",
+             "1 GiB device copy (torch `copy_` -> the runtime's copyBuffer kernel, timed",
+             "in the same script) to 1 GiB.", "",
+             "Commands (from the repository root):", "",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- "
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- "
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity",
+             "    python3 bench.py --ingest-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+             f"Copy factors: FETCH {cal['FETCH_SIZE']:.4f}, WRITE {cal['WRITE_SIZE']:.4f}", "",
+             "| kernel | fetch (MB) | write (MB) | traffic (MB) | algorithmic (MB) | traffic / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    for k, r in rec["kernels"].items():
+        lines.append(f"| {KERNELS[k][0]} | {r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} "
+                     f"| {r['traffic_bytes'] / 1e6:.1f} | {alg[k] / 1e6:.1f} "
+                     f"| {r['traffic_bytes'] / alg[k]:.3f} |")
+    lines += ["", "Machine-readable record (read by bench.py; a kernel's entry is used only",
+              "while its sources hash to `source_sha256`):", "", "```json",
+              json.dumps(rec, indent=1), "```", ""]
+    os.makedirs(os.path.dirname(TRAFFIC_MD), exist_ok=True)
+    with open(TRAFFIC_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o bench -- "
+             "python3 -u bench.py --steps 10 --warmup 3 --decode-steps 200 --no-cpu-baseline --no-parity")
+
+
+def ingest_trace(d):
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# Kernel durations (rocprofv3 kernel trace)", "",
+             "Workloads: prefill B4 H32 T32768 d128 bf16 (gate + chunk per step, 3 warm-up",
+             "and 10 timed steps), decode 256x32 d128 (20 warm-up + 200 steps), plus the",
+             "1 GiB calibration copy.  Durations from the trace's start/end timestamps.", "",
+             "Command (from the repository root):", "", "    " + TRACE_CMD,
+             "    python3 bench.py --ingest-trace gpurun_out/ktrace", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | avg without first call (us) |",
+             "|---|---|---|---|---|---|"]
+    frags = dict((k, v[0]) for k, v in KERNELS.items())
+    frags["copy (calibration)"] = "copyBuffer"
+    for label, frag in frags.items():
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+              for r in rows if frag in r["Kernel_Name"]]
+        if not us:
+            continue
+        names = sorted({r["Kernel_Name"] for r in rows if frag in r["Kernel_Name"]})
+        rest = us[1:] or us
+        lines.append(f"| {label}: `{names[0][:70]}` | {len(us)} | {sum(us) / len(us):.1f} "
+                     f"| {min(us):.1f} | {max(us):.1f} | {sum(rest) / len(rest):.1f} |")
+    lines.append("")
+    os.makedirs(os.path.dirname(TRACE_MD), exist_ok=True)
+    with open(TRACE_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def main():
@@ -163,7 +377,17 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
+    if args.ingest_trace:
+        ingest_trace(args.ingest_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the (batch, head) chains shard across GPUs without communication, so the "
@@ -172,6 +396,7 @@ def main():
     _lib.load_library()
     torch.cuda.init()
 
+    copy_gbs = time_copy()
     res = time_prefill(args.steps, args.warmup)
     w = PREFILL
     work = prefill_work(w)
@@ -182,15 +407,18 @@ def main():
     gate_ms = res["gate_ms"]
     chunk_gbs = work["chunk_bytes"] / chunk_s / 1e9
     chunk_tflops = work["chunk_flops"] / chunk_s / 1e12
+    ai = work["chunk_flops"] / work["chunk_bytes"]
+    attainable_tflops = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+
+    parity = {} if args.no_parity else parity_sample(res)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(res["x"], budget_s=args.cpu_budget)
+    del res
+    torch.cuda.empty_cache()
 
     dec = time_decode(args.decode_steps)
     dbytes = decode_bytes(DECODE)
     dec_gbs = dbytes / (dec["us_per_step"] * 1e-6) / 1e9
-
-    parity = {} if args.no_parity else parity_sample(res)
-    del res
-    torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    traffic = recorded_traffic()
 
     line = {
         "metric": "KDA chunkwise prefill tokens/s + decode-step HBM GB/s, % of roofline",
@@ -210,20 +438,26 @@ def main():
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "dk": w.dk, "dv": w.dv,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": chunk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": chunk_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_kernel<bf16,128,64>",
+                     "frac": chunk_gbs / HBM_PEAK_GBS, "traffic": traffic["chunk_fwd"],
+                     "kernel": "chunk_fwd_kernel<bf16,128,64,8>",
                      "bytes_per_launch": work["chunk_bytes"], "avg_ms": chunk_s * 1e3},
         "prefill": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
                     "gate_gbs": work["gate_bytes"] / (gate_ms / 1e3) / 1e9,
+                    "gate_traffic": traffic["gate"],
                     "chunk_alg_tflops": chunk_tflops,
+                    "chunk_flops_per_head_token": work["flops_per_head_token"],
+                    "chunk_arith_intensity": ai,
                     "mfma_frac_of_bf16_peak": chunk_tflops / BF16_PEAK_TFLOPS,
+                    "roofline_frac_of_attainable": chunk_tflops / attainable_tflops,
                     "head_tokens": work["head_tokens"]},
         "decode": {"us_per_step": dec["us_per_step"], "steps": dec["steps"],
                    "tokens_per_s": DECODE.B / (dec["us_per_step"] * 1e-6),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+                                "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                                "traffic": traffic["decode_step"],
                                 "kernel": "decode_step_kernel<bf16,128,128>",
                                 "bytes_per_launch": dbytes}},
+        "hbm_copy_gbs": copy_gbs,
         "parity": parity,
         "cpu_baseline": cpu,
     }

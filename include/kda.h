@@ -33,6 +33,9 @@
  *  - Sizes: B, T, H, N >= 1; dk, dv in {32, 64, 128}.  fp32 inputs support
  *    dk in {32, 64} for kda_chunk_fwd (its on-chip tiles for dk = 128 exceed
  *    the 160 KiB of LDS); every other combination is supported.
+ *    Index-width limits (INVALID_ARGUMENT beyond them): kda_gate H*dk <= 2^28;
+ *    kda_chunk_fwd B*H <= 2^24 and H*max(dk,dv)*256 < 2^32; kda_decode_step
+ *    N*H < 2^31.
  *  - No scaling or normalisation is applied to q or k; that is the caller's.
  *  - Concurrent calls that share an output buffer race; the library keeps no
  *    global state of its own.

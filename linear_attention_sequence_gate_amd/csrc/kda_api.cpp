@@ -69,6 +69,8 @@ int kda_gate(const void *z, const float *A, float *g, int64_t B, int64_t T, int6
     int64_t n = B;
     if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: element count overflows");
+    if (H * dk > (int64_t(1) << 28))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: H*dk=%lld too large", (long long)(H * dk));
     if (!aligned16(z) || !aligned16(A) || !aligned16(g))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: pointers must be 16-byte aligned");
     if (static_cast<const void *>(g) == z)

@@ -3,45 +3,52 @@
 // Gate ("Kimi K3 internal structure analysis", section "Sequence mixing: 3 KDA
 // layers per global MLA layer"): g = -5 * sigmoid(exp(A[h,c]) * z[b,t,h,c]).
 // Purely elementwise and HBM-bound: it reads z (2 or 4 B) and writes g (4 B)
-// per element, so each thread moves 8 elements with 16/32-byte vector
-// accesses and exp(A) is recomputed from the small, L2-resident A table.
+// per element with coalesced vector accesses; exp(A) is recomputed from the
+// small, L2-resident A table.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-// Eight consecutive inputs as fp32 (16-byte loads; bases are 16-byte aligned).
-__device__ __forceinline__ void load8(const bf16 *p, float *out) {
-    bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) out[j] = (float)v[j];
+// Four consecutive inputs as fp32 (8- or 16-byte loads; bases are aligned).
+__device__ __forceinline__ floatx4 load4(const bf16 *p) {
+    const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4 *>(p));
+    return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
-__device__ __forceinline__ void load8(const float *p, float *out) {
-    floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
-    floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p) + 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { out[j] = a[j]; out[4 + j] = b[j]; }
+__device__ __forceinline__ floatx4 load4(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
 }
 
+// Element groups of four: a wave handles 128 consecutive groups per pass, lane
+// l groups l and l + 64, so every load and store instruction of the wave
+// covers one contiguous span (partial cache-line writes would cost extra
+// HBM traffic).  The [H, dk] table index of a group is kept incrementally.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ z,
                                                    const float *__restrict__ A,
-                                                   float *__restrict__ g, int64_t n8,
-                                                   int HD) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-        float zv[8];
-        load8(z + i * 8, zv);
-        // 8 consecutive elements share the head and sit at channels c..c+7 of
-        // the [H, dk] table (dk is a multiple of 8).
-        const float *a = A + (int)((i * 8) % HD);
-        float out[8];
+                                                   float *__restrict__ g, int64_t n4, int HD4) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t step = (((int64_t)gridDim.x * blockDim.x) >> 6) * 128;
+    const int dstep = (int)(step % HD4);
+    int64_t q = wave * 128 + lane;
+    int c0 = (int)(q % HD4), c1 = (int)((q + 64) % HD4);
+    for (; q < n4; q += step) {
+        const bool two = q + 64 < n4;
+        const floatx4 z0 = load4(z + 4 * q);
+        const floatx4 z1 = two ? load4(z + 4 * (q + 64)) : floatx4{0, 0, 0, 0};
+        const floatx4 a0 = *reinterpret_cast<const floatx4 *>(A + 4 * c0);
+        const floatx4 a1 = *reinterpret_cast<const floatx4 *>(A + 4 * c1);
+        floatx4 g0, g1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            out[j] = gate_value(a[j], zv[j]);
-        floatx4 *gp = reinterpret_cast<floatx4 *>(g + i * 8);
-        __builtin_nontemporal_store(floatx4{out[0], out[1], out[2], out[3]}, gp);
-        __builtin_nontemporal_store(floatx4{out[4], out[5], out[6], out[7]}, gp + 1);
+        for (int j = 0; j < 4; ++j) {
+            g0[j] = gate_value(a0[j], z0[j]);
+            g1[j] = gate_value(a1[j], z1[j]);
+        }
+        __builtin_nontemporal_store(g0, reinterpret_cast<floatx4 *>(g + 4 * q));
+        if (two) __builtin_nontemporal_store(g1, reinterpret_cast<floatx4 *>(g + 4 * (q + 64)));
+        c0 += dstep; if (c0 >= HD4) c0 -= HD4;
+        c1 += dstep; if (c1 >= HD4) c1 -= HD4;
     }
 }
 
@@ -83,14 +90,16 @@ static int grid_for(int64_t work, int block) {
 
 hipError_t launch_gate(const void *z, const float *A, float *g, int64_t n_elems, int H, int dk,
                        int is_bf16, hipStream_t s) {
-    const int64_t n8 = n_elems / 8;
-    const int grid = grid_for(n8, 256);
+    // n_elems and H * dk are multiples of dk, itself a multiple of 32
+    const int64_t n4 = n_elems / 4;
+    const int grid = grid_for((n4 + 1) / 2, 256);
+    const int HD4 = H * dk / 4;
     if (is_bf16)
         hipLaunchKernelGGL(gate_kernel<bf16>, dim3(grid), dim3(256), 0, s,
-                           static_cast<const bf16 *>(z), A, g, n8, H * dk);
+                           static_cast<const bf16 *>(z), A, g, n4, HD4);
     else
         hipLaunchKernelGGL(gate_kernel<float>, dim3(grid), dim3(256), 0, s,
-                           static_cast<const float *>(z), A, g, n8, H * dk);
+                           static_cast<const float *>(z), A, g, n4, HD4);
     return hipGetLastError();
 }
 

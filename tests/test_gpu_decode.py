@@ -31,6 +31,26 @@ def test_decode_steps_match_oracle(dtype, dk, dv):
         assert rho(S, S_ref) <= TOL[dtype], (t, rho(S, S_ref))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 32), (128, 64)])
+def test_decode_persistent_grid_heads(dtype, dk, dv):
+    """More heads than the persistent grid's 1024 workgroups, not a multiple of
+    it (37 x 40 = 1480): workgroups walk several heads and prefetch the next
+    head's state while writing the current one.  Two steps, every head."""
+    N, H = 37, 40
+    say("decode persistent grid", dtype, dk, dv)
+    st = inputs.make_decode_state(N, H, dk, dv, 79, device="cuda")
+    S = st["S"].clone()
+    S_ref = st["S"].double().cpu().numpy()
+    for t in range(2):
+        x = _step_inputs(N, H, dk, dv, dtype, 79, t)
+        o = kda_decode_step(x["q"], x["k"], x["v"], x["z"], st["A"], x["beta"], S)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], x["z"], st["A"], x["beta"], S_ref)
+        assert rho(o, o_ref) <= TOL[dtype], (t, rho(o, o_ref))
+        assert rho(S, S_ref) <= TOL[dtype], (t, rho(S, S_ref))
+
+
 def test_decode_matches_prefill_on_gpu():
     """T decode steps equal one chunked prefill of the same T tokens (gate fused
     in decode, separate in prefill): the state is the whole carry."""
