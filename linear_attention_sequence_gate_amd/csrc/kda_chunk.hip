@@ -132,8 +132,8 @@ template <typename T> __host__ __device__ constexpr int kround(int I) {
 // M[4*(l/16) + j][l % 16] in element j.  mma16(L(X^T), L(Y)) = L(X Y).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ floatx4 mma16(bf16, floatx4 a, floatx4 b, floatx4 c) {
-    bf16x4 ab = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    bf16x4 bb = {(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    const bf16x4 ab = to_bf16x4(a);
+    const bf16x4 bb = to_bf16x4(b);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, bb, c, 0, 0, 0);
 }
 __device__ __forceinline__ floatx4 mma16(float, floatx4 a, floatx4 b, floatx4 c) {
@@ -157,8 +157,7 @@ template <typename T> __device__ __forceinline__ void store4v(T *p, floatx4 x) {
 // N consecutive values (channel-major rows: tokens contiguous).
 template <int N> __device__ __forceinline__ void storeN(bf16 *p, const float *x) {
     if constexpr (N == 2) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<bf16x2 *>(p) = bf16x2{(bf16)x[0], (bf16)x[1]};
+        *reinterpret_cast<bf16x2 *>(p) = __builtin_convertvector(floatx2{x[0], x[1]}, bf16x2);
     } else {
 #pragma unroll
         for (int i = 0; i < N; i += 4) store4(p + i, x[i], x[i + 1], x[i + 2], x[i + 3]);
@@ -166,7 +165,6 @@ template <int N> __device__ __forceinline__ void storeN(bf16 *p, const float *x)
 }
 template <int N> __device__ __forceinline__ void storeN(float *p, const float *x) {
     if constexpr (N == 2) {
-        typedef float floatx2 __attribute__((ext_vector_type(2)));
         *reinterpret_cast<floatx2 *>(p) = floatx2{x[0], x[1]};
     } else {
 #pragma unroll
@@ -216,8 +214,9 @@ template <> struct Perm<bf16> {
         return frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
     __device__ __forceinline__ static frag regs(const floatx4 *t) {
-        return frag{(bf16)t[0][0], (bf16)t[0][1], (bf16)t[0][2], (bf16)t[0][3],
-                    (bf16)t[1][0], (bf16)t[1][1], (bf16)t[1][2], (bf16)t[1][3]};
+        const bf16x4 a = to_bf16x4(t[0]);
+        const bf16x4 b = to_bf16x4(t[1]);
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     // the rounding residual of regs(t), as a second bf16 fragment
     __device__ __forceinline__ static frag regs_lo(const floatx4 *t) {
@@ -357,7 +356,9 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
     const float *__restrict__ gp = a.g;
     T *__restrict__ op = static_cast<T *>(a.o);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: keep it scalar so role branches stay scalar
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
     const int I = wave / WPS;                                    // this wave's prep subtile
     const int pos = lane / QPW;                                  // rank inside the subtile
@@ -796,6 +797,549 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
     }
 }
 
+// ===========================================================================
+// Pipelined variant (bf16, dk in {64, 128}, 64-column dv slices): 32-token
+// chunks of two 16-token subtiles, eight waves in two roles.
+//
+//   prep waves (4..7) build chunk c: decay products, operand tiles, the A and
+//       P scores of the three causal subtile pairs, and X = (I + A)^-1 with
+//       T = X Diag(beta);
+//   state waves (0..3) run the state pass of chunk c - 1, one 16-column block
+//       each, from a second copy of the handoff buffers.
+//
+// The state pass does not need W = T K~: since W S = T (K~ S),
+//     U = U' - W S = T (V - K~ S),
+// so a state wave forms Z = K~ S, subtracts it from V (loaded straight into
+// the accumulator layout) and multiplies by T.  One period = one chunk for
+// each role, three workgroup barriers; the handoff buffers alternate between
+// two slots, so the prep waves never overwrite what the state waves read.
+// ===========================================================================
+constexpr int kPipeChunk = 32;
+
+// Loads whose completion is waited for by hand.  The compiler's wait-count
+// analysis cannot keep a load in flight across loop iterations (it waits
+// for freshly issued prefetches at the back-edge), so the prefetches of the
+// pipelined kernel are issued here and each consumer waits with an explicit
+// vmcnt: vector-memory operations complete in issue order, and the waves
+// that use these issue no other vector-memory loads in between.  The memory
+// clobber keeps other memory operations from moving across them.
+__device__ __forceinline__ floatx4 vm_load16_nt(const void *p) {
+    floatx4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ bf16x4 vm_load8(const void *p) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 r;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ unsigned vm_load_u16(const void *p) {
+    unsigned r;
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N> __device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Channel-major rows of the 32-token tiles: one spare row every 16 rows keeps
+// both the prep stores (rows 4 apart) and the MFMA fragment reads (16
+// consecutive rows) free of bank conflicts at a pitch of 40 elements.
+__device__ __forceinline__ int crow16(int c) { return c + (c >> 4); }
+
+template <int DK> struct PipeLds {
+    static constexpr int LDK = DK + 8;              // token-row pitch (elements)
+    static constexpr int LDT = 40;                  // 32-column pitch (elements)
+    static constexpr int NCR = DK + DK / 16;        // channel rows after crow16
+    static constexpr int TOK = 32 * LDK * 2;        // 32 token rows, bytes
+    static constexpr int SQ = 32 * LDT * 2;         // 32 x 32 tile, bytes
+    // prep-only buffers
+    static constexpr int QR = 0;                    // q e^{lam}       (subtile-referenced)
+    static constexpr int KR = QR + TOK;             // k e^{lam}
+    static constexpr int KC = KR + TOK;             // column tiles of the pairs (0,0), (1,0), (1,1)
+    static constexpr int AB = KC + 48 * LDK * 2;    // A (row-major, beta on rows)
+    static constexpr int EL = AB + SQ;              // subtile decay totals, 2 x DK fp32
+    static constexpr int BETA = EL + 2 * DK * 4;    // 32 fp32
+    static constexpr int PREP = BETA + 32 * 4;
+    // one handoff slot
+    static constexpr int S_KT = 0;                  // K~ = k e^{b} rows
+    static constexpr int S_QT = S_KT + TOK;         // Q~ = q e^{b} rows
+    static constexpr int S_KH = S_QT + TOK;         // K^T = (k e^{b_C - b})^T channel rows
+    static constexpr int S_PH = S_KH + NCR * LDT * 2;
+    static constexpr int S_PL = S_PH + SQ;
+    static constexpr int S_XR = S_PL + SQ;          // T = X Diag(beta), row-major
+    static constexpr int S_EBC = S_XR + SQ;         // e^{b_C}, DK fp32
+    static constexpr int SLOT = S_EBC + DK * 4;
+    static constexpr int TOTAL = PREP + 2 * SLOT;
+    static_assert(PREP % 16 == 0 && SLOT % 16 == 0, "alignment");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+template <int DK>
+__global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
+    constexpr int NV = 64;
+    using Lds = PipeLds<DK>;
+    using PF = Perm<bf16>;
+    using KF = Kc<bf16>;
+    using T = bf16;
+    constexpr int LDK = Lds::LDK, LDT = Lds::LDT;
+    constexpr int NKS = DK / 32;                    // 32-deep k steps over channels
+    constexpr int NCB = DK / 16;                    // state row tiles
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::TOTAL];
+    // the wave index is uniform: keep it scalar so role branches stay scalar
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg4 = (lane >> 4) * 4;
+
+    int bh, slice;
+    {
+        const int id = blockIdx.x;
+        if (a.xcd_map) {
+            const int x = id & 7, j = id >> 3;
+            bh = (j / a.nslice) * 8 + x;
+            slice = j % a.nslice;
+        } else {
+            bh = id / a.nslice;
+            slice = id % a.nslice;
+        }
+    }
+    const int H = a.H, DV = a.DV;
+    const int b = bh / H, h = bh % H;
+    const int64_t T_ = a.T;
+    const int vcol0 = slice * NV;
+    const int64_t nchunk = (T_ + kPipeChunk - 1) / kPipeChunk;
+    const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
+    unsigned char *const slot_base = smem + Lds::PREP;
+
+    if (wave >= 4) {
+        // =================================================================
+        // prep role
+        // =================================================================
+        constexpr int QPW = DK / 8;                 // channel quads per wave (two waves per subtile)
+        constexpr int SUBT = 64 / QPW;              // lanes along one subtile's tokens
+        constexpr int TPT = 16 / SUBT;              // tokens per lane
+        const int p = wave - 4;
+        const int I = p >> 1;                       // subtile of this wave
+        const int pos = lane / QPW;
+        const int cq = (p & 1) * QPW + lane % QPW;  // channel quad
+        const int tb = 16 * I + pos * TPT;          // first token of this lane (in the chunk)
+        T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
+        T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
+        T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
+        T *sA = reinterpret_cast<T *>(smem + Lds::AB);
+        float *sEL = reinterpret_cast<float *>(smem + Lds::EL);
+        float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA);
+
+        const T *__restrict__ qp = static_cast<const T *>(a.q);
+        const T *__restrict__ kp = static_cast<const T *>(a.k);
+        const T *__restrict__ bp = static_cast<const T *>(a.beta);
+        const float *__restrict__ gp = a.g;
+
+        floatx4 eye;                                // this lane's entries of I (L layout)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eye[j] = lg4 + j == lr ? 1.0f : 0.0f;
+
+        // the blocks above the diagonal of P (hi, lo) and T in both slots are
+        // read by the 32-deep products and never written: zero them once
+        for (int e = lane + 64 * p; e < 2 * 3 * 64; e += 256) {
+            const int s_ = e / 192, m = (e / 64) % 3, q4 = e & 63;
+            T *tile = reinterpret_cast<T *>(slot_base + s_ * Lds::SLOT +
+                                            (m == 0 ? Lds::S_PH : m == 1 ? Lds::S_PL : Lds::S_XR));
+            store4(tile + (q4 >> 2) * LDT + 16 + (q4 & 3) * 4, 0.f, 0.f, 0.f, 0.f);
+        }
+
+        // raw inputs of one chunk; two sets, so a chunk's loads are issued two
+        // periods before its use (one 32-token period is shorter than the
+        // memory latency under load)
+        struct Raw {
+            floatx4 g[TPT];
+            bf16x4 k[TPT], q[TPT];
+            unsigned beta;                          // bf16 bits, zero-extended
+        };
+        Raw raw0, raw1;
+        constexpr int NRAW = 3 * TPT + 1;           // loads per set
+        auto load_raw = [&](int64_t ch, Raw &r) {
+            const int64_t t0 = ch * kPipeChunk;
+            const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+            const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
+            const void *gb = gp + tok0 * DK;
+            const void *kb = kp + tok0 * DK, *qb = qp + tok0 * DK;
+            const void *bb = bp + tok0;
+#pragma unroll
+            for (int i = 0; i < TPT; ++i) {
+                int tl = tb + i;
+                if (L < kPipeChunk) tl = tl < L ? tl : L - 1;
+                const unsigned e = (unsigned)tl * HDK + 4 * cq;
+                r.g[i] = vm_load16_nt(at<floatx4>(gb, e * 4u));
+                r.k[i] = vm_load8(at<bf16x4>(kb, e * 2u));
+                r.q[i] = vm_load8(at<bf16x4>(qb, e * 2u));
+            }
+            const int bl = lane & 31;
+            r.beta = vm_load_u16(at<unsigned short>(bb, (unsigned)(bl < L ? bl : L - 1) * (unsigned)H * 2u));
+        };
+
+        auto period = [&](int64_t c, Raw &raw) {
+            const bool live = c < nchunk;
+            const int64_t t0 = c * kPipeChunk;
+            const int L = live ? (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk) : 0;
+            unsigned char *slot = slot_base + (int)(c & 1) * Lds::SLOT;
+            T *sKt = reinterpret_cast<T *>(slot + Lds::S_KT);
+            T *sQt = reinterpret_cast<T *>(slot + Lds::S_QT);
+            T *sKh = reinterpret_cast<T *>(slot + Lds::S_KH);
+            T *sPh = reinterpret_cast<T *>(slot + Lds::S_PH);
+            T *sPl = reinterpret_cast<T *>(slot + Lds::S_PL);
+            T *sXr = reinterpret_cast<T *>(slot + Lds::S_XR);
+            float *sEbC = reinterpret_cast<float *>(slot + Lds::S_EBC);
+
+            // values carried from P1 to P2
+            floatx4 kR[TPT], qR[TPT], kEt[TPT];
+            if (live) {
+                // this chunk's raw loads were issued two periods ago; the next
+                // chunk's (one set, NRAW loads) may still be in flight
+                if (c + 1 < nchunk) vm_wait<NRAW>();
+                else vm_wait<0>();
+                // ---- P1: alpha and running products; subtile-local tiles ---
+                floatx4 R[TPT], Et[TPT], eLam;
+                {
+                    // past the end of the sequence alpha = 1 (g = 0): e^{b_C} stops at
+                    // the last token; beta = 0 there zeroes those rows of A and T
+                    floatx4 al[TPT];
+                    if (L == kPipeChunk) {
+#pragma unroll
+                        for (int i = 0; i < TPT; ++i) al[i] = exp2_4(raw.g[i] * kLog2e);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < TPT; ++i) {
+                            const floatx4 e = exp2_4(raw.g[i] * kLog2e);
+                            const bool in = tb + i < L;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) al[i][j] = in ? e[j] : 1.0f;
+                        }
+                    }
+                    floatx4 tot = al[0];
+#pragma unroll
+                    for (int i = 1; i < TPT; ++i) tot *= al[i];
+                    floatx4 pre = {1, 1, 1, 1}, suf = {1, 1, 1, 1};
+#pragma unroll
+                    for (int s = 1; s < SUBT; ++s) {
+                        const bool use_fw = pos >= s, use_bw = pos + s < SUBT;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float fw = __shfl(tot[j], lane - s * QPW);
+                            const float bw = __shfl(tot[j], lane + s * QPW);
+                            pre[j] *= use_fw ? fw : 1.0f;
+                            suf[j] *= use_bw ? bw : 1.0f;
+                        }
+                    }
+                    R[0] = pre * al[0];
+#pragma unroll
+                    for (int i = 1; i < TPT; ++i) R[i] = R[i - 1] * al[i];
+                    Et[TPT - 1] = suf;
+#pragma unroll
+                    for (int i = TPT - 2; i >= 0; --i) Et[i] = Et[i + 1] * al[i + 1];
+                    eLam = R[TPT - 1] * suf;
+                }
+                if (pos == 0) *reinterpret_cast<floatx4 *>(sEL + I * DK + 4 * cq) = eLam;
+                {
+                    const float bv = lane < L ? __uint_as_float(raw.beta << 16) : 0.0f;
+                    if (p == 0 && lane < 32) sBeta[lane] = bv;
+                }
+                const floatx4 eNegLam = rcp_4(eLam);
+                float kh[4][TPT];
+#pragma unroll
+                for (int i = 0; i < TPT; ++i) {
+                    const int tl = tb + i, r = tl - 16 * I;
+                    const floatx4 kv = to_f4(raw.k[i]), qv = to_f4(raw.q[i]);
+                    kR[i] = kv * R[i];
+                    qR[i] = qv * R[i];
+                    kEt[i] = kv * Et[i];
+                    store4v(sKr + tl * LDK + 4 * cq, kR[i]);
+                    store4v(sQr + tl * LDK + 4 * cq, qR[i]);
+                    // diagonal pair column tile: k e^{-lam}
+                    store4v(sKc + ((I == 0 ? 0 : 32) + r) * LDK + 4 * cq, kEt[i] * eNegLam);
+                    if (I == 0) {
+                        store4v(sKc + (16 + r) * LDK + 4 * cq, kEt[i]);   // pair (1, 0)
+                        store4v(sKt + tl * LDK + 4 * cq, kR[i]);          // b = lam in subtile 0
+                        store4v(sQt + tl * LDK + 4 * cq, qR[i]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) kh[j][i] = kEt[i][j];  // b_C - b = Lam_1 - lam
+                    }
+                }
+                if (I == 1) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) storeN<TPT>(sKh + crow16(4 * cq + j) * LDT + tb, kh[j]);
+                }
+                if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
+            }
+            lds_barrier();                                  // BAR1
+
+            if (live) {
+                // ---- P2: scores; tiles that need the other subtile's total
+                // tiles: 0 A(0,0) 1 P(0,0) 2 A(1,0) 3 P(1,0) 4 A(1,1) 5 P(1,1)
+                floatx4 sc[2];
+                {
+                    const int koff = (lane >> 4) * (KF::kStep / 4);
+                    const T *xs[2], *ys[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int ti = u == 0 ? p : (p + 4 < 6 ? p + 4 : p);
+                        const int pi = ti >> 1;
+                        const int Ib = pi == 0 ? 0 : 1;
+                        sc[u] = floatx4{0, 0, 0, 0};
+                        xs[u] = sKc + (16 * pi + lr) * LDK + koff;
+                        ys[u] = ((ti & 1) ? sQr : sKr) + (16 * Ib + lr) * LDK + koff;
+                    }
+                    auto xp = [&](int i, int st) { return xs[i] + st * KF::kStep; };
+                    auto yp = [&](int i, int st) { return ys[i] + st * KF::kStep; };
+                    if (p < 2) {
+                        group_mma<KF, 2, DK / 32>(sc, xp, yp);
+                    } else {
+                        floatx4(&sc1)[1] = *reinterpret_cast<floatx4(*)[1]>(&sc[0]);
+                        group_mma<KF, 1, DK / 32>(sc1, xp, yp);
+                    }
+                }
+                {
+                    const floatx4 e0 = *reinterpret_cast<const floatx4 *>(sEL + 4 * cq);
+                    const floatx4 e1 = *reinterpret_cast<const floatx4 *>(sEL + DK + 4 * cq);
+                    if (I == 1) {
+#pragma unroll
+                        for (int i = 0; i < TPT; ++i) {
+                            store4v(sKt + (tb + i) * LDK + 4 * cq, kR[i] * e0);
+                            store4v(sQt + (tb + i) * LDK + 4 * cq, qR[i] * e0);
+                        }
+                    } else {
+                        float kh[4][TPT];
+#pragma unroll
+                        for (int i = 0; i < TPT; ++i) {
+                            const floatx4 v = kEt[i] * e1;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) kh[j][i] = v[j];
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) storeN<TPT>(sKh + crow16(4 * cq + j) * LDT + tb, kh[j]);
+                        if (pos == 0) *reinterpret_cast<floatx4 *>(sEbC + 4 * cq) = e0 * e1;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (u == 1 && p >= 2) break;
+                    const int ti = u == 0 ? p : p + 4;
+                    const int pi = ti >> 1;
+                    const int Ib = pi == 0 ? 0 : 1, J = pi == 2 ? 1 : 0;
+                    const bool isP = ti & 1;
+                    const int r = 16 * Ib + lr;
+                    const float br = sBeta[r];
+                    const float rowscale = isP ? 1.0f : br;
+                    // causal mask of the pair: everything below the diagonal block,
+                    // s <= r (P) or s < r (A) inside it
+                    const int lim = J < Ib ? 16 : (isP ? lr + 1 : lr);
+                    floatx4 val;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = sc[u][j] * rowscale;
+                        val[j] = lg4 + j < lim ? x : 0.0f;
+                    }
+                    if (isP) {
+                        floatx4 lo;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) lo[j] = val[j] - (float)(bf16)val[j];
+                        store4v(sPh + r * LDT + 16 * J + lg4, val);
+                        store4v(sPl + r * LDT + 16 * J + lg4, lo);
+                    } else {
+                        store4v(sA + r * LDT + 16 * J + lg4, val);
+                    }
+                }
+            }
+            lds_barrier();                                  // BAR2
+
+            if (live && p == 0) {
+                // ---- P3: X = (I + A)^-1 and T = X Diag(beta) ----------------
+                const T tz = T(0);
+                const floatx4 z4 = {0, 0, 0, 0};
+                auto addI = [&](floatx4 m) { return m + eye; };
+                floatx4 x[2], xT[2];
+#pragma unroll
+                for (int IB = 0; IB < 2; ++IB) {
+                    // N = -A_II in both layouts; A_II^16 = 0, so (I + A_II)^-1 =
+                    // (I + N)(I + N^2)(I + N^4)(I + N^8)
+                    const floatx4 nT = -lds_load4(sA + (16 * IB + lr) * LDT + 16 * IB + lg4);
+                    floatx4 n;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * IB + lg4 + j) * LDT + 16 * IB + lr]);
+                    const floatx4 n2 = mma16(tz, nT, n, z4);
+                    const floatx4 n2T = mma16(tz, n, nT, z4);
+                    const floatx4 n4 = mma16(tz, n2T, n2, z4);
+                    const floatx4 n4T = mma16(tz, n2, n2T, z4);
+                    const floatx4 n8 = mma16(tz, n4T, n4, z4);
+                    const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);
+                    const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);
+                    x[IB] = mma16(tz, p2T, addI(n8), z4);
+                    xT[IB] = mma16(tz, addI(n8), p2T, z4);
+                }
+                // X_10 = -X_11 A_10 X_00
+                const floatx4 y = mma16(tz, lds_load4(sA + (16 + lr) * LDT + lg4), x[0], z4);
+                const floatx4 x10T = -mma16(tz, y, xT[1], z4);
+                const floatx4 b0 = *reinterpret_cast<const floatx4 *>(sBeta + lg4);
+                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(sBeta + 16 + lg4);
+                store4v(sXr + lr * LDT + lg4, xT[0] * b0);
+                store4v(sXr + (16 + lr) * LDT + 16 + lg4, xT[1] * b1);
+                store4v(sXr + (16 + lr) * LDT + lg4, x10T * b0);
+            }
+            lds_barrier();                                  // BAR3
+        };
+        load_raw(0, raw0);
+        if (nchunk > 1) load_raw(1, raw1);
+        for (int64_t c = 0; c <= nchunk; c += 2) {
+            period(c, raw0);
+            if (c + 1 <= nchunk) period(c + 1, raw1);
+        }
+    } else {
+        // =================================================================
+        // state role: column block s of the slice, chunk c - 1 in period c
+        // =================================================================
+        const int s = wave;
+        const T *__restrict__ vp = static_cast<const T *>(a.v);
+        T *__restrict__ op = static_cast<T *>(a.o);
+        const int ncol = vcol0 + 16 * s + lr;          // this lane's state / v column
+
+        floatx4 sacc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cc = 16 * cb + lg4 + j;
+                sacc[cb][j] = a.S0 ? a.S0[((int64_t)bh * DK + cc) * DV + ncol] : 0.0f;
+            }
+        typename PF::frag sf[NKS];
+#pragma unroll
+        for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
+
+        // v of one chunk in the accumulator layout: tile i, element j is
+        // token 16 i + lg4 + j, column ncol
+        unsigned vv0[2][4], vv1[2][4];                  // v of alternate chunks (bf16 bits)
+        auto load_v = [&](int64_t ch, unsigned (&dst)[2][4]) {
+            const int64_t t0 = ch * kPipeChunk;
+            const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+            const void *vb = vp + (((int64_t)b * T_ + t0) * H + h) * DV + ncol;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    int tl = 16 * i + lg4 + j;
+                    if (L < kPipeChunk) tl = tl < L ? tl : L - 1;
+                    dst[i][j] = vm_load_u16(at<unsigned short>(vb, (unsigned)tl * HDV * 2u));
+                }
+        };
+        // period c: chunk c - 1 from cur, chunk c requested into nxt
+        auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) {
+            if (c >= 1) {
+                const int64_t ch = c - 1;
+                const int64_t t0 = ch * kPipeChunk;
+                const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+                const unsigned char *slot = slot_base + (int)(ch & 1) * Lds::SLOT;
+                const T *sKt = reinterpret_cast<const T *>(slot + Lds::S_KT);
+                const T *sQt = reinterpret_cast<const T *>(slot + Lds::S_QT);
+                const T *sKh = reinterpret_cast<const T *>(slot + Lds::S_KH);
+                const T *sPh = reinterpret_cast<const T *>(slot + Lds::S_PH);
+                const T *sPl = reinterpret_cast<const T *>(slot + Lds::S_PL);
+                const T *sXr = reinterpret_cast<const T *>(slot + Lds::S_XR);
+                const float *sEbC = reinterpret_cast<const float *>(slot + Lds::S_EBC);
+
+                // cur was requested a period ago; nothing newer is outstanding
+                // except the previous period's o stores
+                vm_wait<0>();
+                floatx4 vcur[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vcur[i][j] = __uint_as_float(cur[i][j] << 16);
+                if (c < nchunk) load_v(c, nxt);
+
+                // Z = K~ S, then D = V - Z (token rows, this column block)
+                floatx4 zacc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+#pragma unroll
+                for (int t = 0; t < NKS; ++t) {
+                    typename PF::frag kf[2];
+#pragma unroll
+                    for (int Is = 0; Is < 2; ++Is) kf[Is] = PF::lds(sKt + (16 * Is + lr) * LDK, t * 32, lg4);
+#pragma unroll
+                    for (int Is = 0; Is < 2; ++Is) PF::mma(zacc[Is], kf[Is], sf[t]);
+                }
+                floatx4 dm[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) dm[i] = vcur[i] - zacc[i];
+                const typename PF::frag dh = PF::regs(dm), dl = PF::regs_lo(dm);
+                // U = T D
+                floatx4 uacc[2];
+#pragma unroll
+                for (int Ir = 0; Ir < 2; ++Ir) {
+                    const typename PF::frag tf = PF::lds(sXr + (16 * Ir + lr) * LDT, 0, lg4);
+                    uacc[Ir] = floatx4{0, 0, 0, 0};
+                    PF::mma(uacc[Ir], tf, dh);
+                    PF::mma(uacc[Ir], tf, dl);
+                }
+                const typename PF::frag uh = PF::regs(uacc), ul = PF::regs_lo(uacc);
+                // O = Q~ S + P U
+                floatx4 oacc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+#pragma unroll
+                for (int t = 0; t < NKS; ++t) {
+                    typename PF::frag qf[2];
+#pragma unroll
+                    for (int Ir = 0; Ir < 2; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDK, t * 32, lg4);
+#pragma unroll
+                    for (int Ir = 0; Ir < 2; ++Ir) PF::mma(oacc[Ir], sf[t], qf[Ir]);
+                }
+#pragma unroll
+                for (int Ir = 0; Ir < 2; ++Ir) {
+                    const typename PF::frag ph = PF::lds(sPh + (16 * Ir + lr) * LDT, 0, lg4);
+                    const typename PF::frag pl = PF::lds(sPl + (16 * Ir + lr) * LDT, 0, lg4);
+                    PF::mma(oacc[Ir], uh, ph);
+                    PF::mma(oacc[Ir], ul, ph);
+                    PF::mma(oacc[Ir], uh, pl);
+                }
+                const void *obase = op + (((int64_t)b * T_ + t0) * H + h) * DV + vcol0 + 16 * s;
+#pragma unroll
+                for (int Ir = 0; Ir < 2; ++Ir) {
+                    const int r = 16 * Ir + lr;
+                    if (r < L)
+                        store4v(const_cast<T *>(at<T>(obase, ((unsigned)r * HDV + lg4) * 2u)), oacc[Ir]);
+                }
+                // S <- Diag(e^{b_C}) S + K^T U
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const typename PF::frag kf = PF::lds(sKh + crow16(16 * cb + lr) * LDT, 0, lg4);
+                    sacc[cb] *= *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
+                    PF::mma(sacc[cb], kf, uh);
+                }
+#pragma unroll
+                for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
+            }
+            lds_barrier();                                  // BAR1
+            lds_barrier();                                  // BAR2
+            lds_barrier();                                  // BAR3
+        };
+        load_v(0, vv0);
+        for (int64_t c = 0; c <= nchunk; c += 2) {
+            period(c, vv1, vv0);
+            if (c + 1 <= nchunk) period(c + 1, vv0, vv1);
+        }
+        if (a.ST) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int cc = 16 * cb + lg4 + j;
+                    a.ST[((int64_t)bh * DK + cc) * DV + ncol] = sacc[cb][j];
+                }
+        }
+    }
+}
+
 // dv-slice width per workgroup: 64 columns (fp32 at dk = 64: 32); bf16 at
 // dk = 128 runs 8 waves per workgroup, the other shapes 4.
 static int slice_width(int dk, int dv, int is_bf16) {
@@ -820,7 +1364,9 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
-    const int nv = slice_width(dk, dv, is_bf16);
+    // bf16 with dk, dv in {64, 128}: the pipelined 32-token kernel
+    const bool pipe = is_bf16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
     args.S0 = S0; args.ST = ST; args.o = o;
@@ -828,6 +1374,13 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.nbh = (int)(B * H);
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
     const int nblocks = args.nbh * args.nslice;
+    if (pipe) {
+        if (dk == 128)
+            hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(512), 0, s, args);
+        else
+            hipLaunchKernelGGL(chunk32_kernel<64>, dim3(nblocks), dim3(512), 0, s, args);
+        return hipGetLastError();
+    }
     if (is_bf16) {
         switch (dk * 1000 + nv) {
         case 32032: return launch_inst<bf16, 32, 32>(args, nblocks, s);

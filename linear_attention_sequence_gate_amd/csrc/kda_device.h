@@ -28,12 +28,20 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 -> bf16 (round to nearest even).
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
+    return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
 // Store four consecutive values (8 B for bf16, 16 B for fp32); p must be aligned.
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
     *reinterpret_cast<floatx4 *>(p) = floatx4{a, b, c, d};
 }
 __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float d) {
-    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(floatx4{a, b, c, d});
 }
 
 // ---------------------------------------------------------------------------
