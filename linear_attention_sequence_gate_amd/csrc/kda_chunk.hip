@@ -801,18 +801,18 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
 // Pipelined variant (bf16, dk in {64, 128}, 64-column dv slices): 32-token
 // chunks of two 16-token subtiles, eight waves in two roles.
 //
-//   prep waves (4..7) build chunk c: decay products, operand tiles, the A and
-//       P scores of the three causal subtile pairs, and X = (I + A)^-1 with
-//       T = X Diag(beta);
-//   state waves (0..3) run the state pass of chunk c - 1, one 16-column block
-//       each, from a second copy of the handoff buffers.
+//   prep waves (4..7) build chunk c: decay products, operand tiles, and the A
+//       and P scores of the three causal subtile pairs;
+//   state waves (0..3) run the state pass of chunk c - 2, one 16-column block
+//       each; after it, state wave 0 forms X = (I + A)^-1 and T = X Diag(beta)
+//       of chunk c - 1, off the prep waves' critical path.
 //
 // The state pass does not need W = T K~: since W S = T (K~ S),
 //     U = U' - W S = T (V - K~ S),
 // so a state wave forms Z = K~ S, subtracts it from V (loaded straight into
 // the accumulator layout) and multiplies by T.  One period = one chunk for
-// each role, three workgroup barriers; the handoff buffers alternate between
-// two slots, so the prep waves never overwrite what the state waves read.
+// each role, two workgroup barriers; the handoff buffers rotate over three
+// slots (and A, beta over two), so no wave overwrites what another reads.
 // ===========================================================================
 constexpr int kPipeChunk = 32;
 
@@ -859,10 +859,10 @@ template <int DK> struct PipeLds {
     static constexpr int QR = 0;                    // q e^{lam}       (subtile-referenced)
     static constexpr int KR = QR + TOK;             // k e^{lam}
     static constexpr int KC = KR + TOK;             // column tiles of the pairs (0,0), (1,0), (1,1)
-    static constexpr int AB = KC + 48 * LDK * 2;    // A (row-major, beta on rows)
-    static constexpr int EL = AB + SQ;              // subtile decay totals, 2 x DK fp32
-    static constexpr int BETA = EL + 2 * DK * 4;    // 32 fp32
-    static constexpr int PREP = BETA + 32 * 4;
+    static constexpr int AB = KC + 48 * LDK * 2;    // A (row-major, beta on rows), two chunks
+    static constexpr int EL = AB + 2 * SQ;          // subtile decay totals, 2 x DK fp32
+    static constexpr int BETA = EL + 2 * DK * 4;    // beta, 32 fp32, two chunks
+    static constexpr int PREP = BETA + 2 * 32 * 4;
     // one handoff slot
     static constexpr int S_KT = 0;                  // K~ = k e^{b} rows
     static constexpr int S_QT = S_KT + TOK;         // Q~ = q e^{b} rows
@@ -872,7 +872,8 @@ template <int DK> struct PipeLds {
     static constexpr int S_XR = S_PL + SQ;          // T = X Diag(beta), row-major
     static constexpr int S_EBC = S_XR + SQ;         // e^{b_C}, DK fp32
     static constexpr int SLOT = S_EBC + DK * 4;
-    static constexpr int TOTAL = PREP + 2 * SLOT;
+    static constexpr int NSLOT = 3;                 // chunks c (built), c-1 (inverse), c-2 (state)
+    static constexpr int TOTAL = PREP + NSLOT * SLOT;
     static_assert(PREP % 16 == 0 && SLOT % 16 == 0, "alignment");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -930,22 +931,16 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
         T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
         T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
-        T *sA = reinterpret_cast<T *>(smem + Lds::AB);
         float *sEL = reinterpret_cast<float *>(smem + Lds::EL);
-        float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA);
 
         const T *__restrict__ qp = static_cast<const T *>(a.q);
         const T *__restrict__ kp = static_cast<const T *>(a.k);
         const T *__restrict__ bp = static_cast<const T *>(a.beta);
         const float *__restrict__ gp = a.g;
 
-        floatx4 eye;                                // this lane's entries of I (L layout)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) eye[j] = lg4 + j == lr ? 1.0f : 0.0f;
-
-        // the blocks above the diagonal of P (hi, lo) and T in both slots are
+        // the blocks above the diagonal of P (hi, lo) and T in every slot are
         // read by the 32-deep products and never written: zero them once
-        for (int e = lane + 64 * p; e < 2 * 3 * 64; e += 256) {
+        for (int e = lane + 64 * p; e < Lds::NSLOT * 3 * 64; e += 256) {
             const int s_ = e / 192, m = (e / 64) % 3, q4 = e & 63;
             T *tile = reinterpret_cast<T *>(slot_base + s_ * Lds::SLOT +
                                             (m == 0 ? Lds::S_PH : m == 1 ? Lds::S_PL : Lds::S_XR));
@@ -986,13 +981,14 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             const bool live = c < nchunk;
             const int64_t t0 = c * kPipeChunk;
             const int L = live ? (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk) : 0;
-            unsigned char *slot = slot_base + (int)(c & 1) * Lds::SLOT;
+            unsigned char *slot = slot_base + (int)(c % Lds::NSLOT) * Lds::SLOT;
+            T *sA = reinterpret_cast<T *>(smem + Lds::AB + (int)(c & 1) * Lds::SQ);
+            float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA + (int)(c & 1) * 128);
             T *sKt = reinterpret_cast<T *>(slot + Lds::S_KT);
             T *sQt = reinterpret_cast<T *>(slot + Lds::S_QT);
             T *sKh = reinterpret_cast<T *>(slot + Lds::S_KH);
             T *sPh = reinterpret_cast<T *>(slot + Lds::S_PH);
             T *sPl = reinterpret_cast<T *>(slot + Lds::S_PL);
-            T *sXr = reinterpret_cast<T *>(slot + Lds::S_XR);
             float *sEbC = reinterpret_cast<float *>(slot + Lds::S_EBC);
 
             // values carried from P1 to P2
@@ -1157,46 +1153,12 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             }
             lds_barrier();                                  // BAR2
 
-            if (live && p == 0) {
-                // ---- P3: X = (I + A)^-1 and T = X Diag(beta) ----------------
-                const T tz = T(0);
-                const floatx4 z4 = {0, 0, 0, 0};
-                auto addI = [&](floatx4 m) { return m + eye; };
-                floatx4 x[2], xT[2];
-#pragma unroll
-                for (int IB = 0; IB < 2; ++IB) {
-                    // N = -A_II in both layouts; A_II^16 = 0, so (I + A_II)^-1 =
-                    // (I + N)(I + N^2)(I + N^4)(I + N^8)
-                    const floatx4 nT = -lds_load4(sA + (16 * IB + lr) * LDT + 16 * IB + lg4);
-                    floatx4 n;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * IB + lg4 + j) * LDT + 16 * IB + lr]);
-                    const floatx4 n2 = mma16(tz, nT, n, z4);
-                    const floatx4 n2T = mma16(tz, n, nT, z4);
-                    const floatx4 n4 = mma16(tz, n2T, n2, z4);
-                    const floatx4 n4T = mma16(tz, n2, n2T, z4);
-                    const floatx4 n8 = mma16(tz, n4T, n4, z4);
-                    const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);
-                    const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);
-                    x[IB] = mma16(tz, p2T, addI(n8), z4);
-                    xT[IB] = mma16(tz, addI(n8), p2T, z4);
-                }
-                // X_10 = -X_11 A_10 X_00
-                const floatx4 y = mma16(tz, lds_load4(sA + (16 + lr) * LDT + lg4), x[0], z4);
-                const floatx4 x10T = -mma16(tz, y, xT[1], z4);
-                const floatx4 b0 = *reinterpret_cast<const floatx4 *>(sBeta + lg4);
-                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(sBeta + 16 + lg4);
-                store4v(sXr + lr * LDT + lg4, xT[0] * b0);
-                store4v(sXr + (16 + lr) * LDT + 16 + lg4, xT[1] * b1);
-                store4v(sXr + (16 + lr) * LDT + lg4, x10T * b0);
-            }
-            lds_barrier();                                  // BAR3
         };
         load_raw(0, raw0);
         if (nchunk > 1) load_raw(1, raw1);
-        for (int64_t c = 0; c <= nchunk; c += 2) {
+        for (int64_t c = 0; c <= nchunk + 1; c += 2) {
             period(c, raw0);
-            if (c + 1 <= nchunk) period(c + 1, raw1);
+            if (c + 1 <= nchunk + 1) period(c + 1, raw1);
         }
     } else {
         // =================================================================
@@ -1206,6 +1168,9 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         const T *__restrict__ vp = static_cast<const T *>(a.v);
         T *__restrict__ op = static_cast<T *>(a.o);
         const int ncol = vcol0 + 16 * s + lr;          // this lane's state / v column
+        floatx4 eye;                                // this lane's entries of I (L layout)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eye[j] = lg4 + j == lr ? 1.0f : 0.0f;
 
         floatx4 sacc[NCB];
 #pragma unroll
@@ -1235,13 +1200,26 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                     dst[i][j] = vm_load_u16(at<unsigned short>(vb, (unsigned)tl * HDV * 2u));
                 }
         };
-        // period c: chunk c - 1 from cur, chunk c requested into nxt
+        // period c: state pass of chunk c - 2 (v from cur), v of chunk c - 1
+        // requested into nxt, inverse of chunk c - 1 (wave 0)
         auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) {
-            if (c >= 1) {
-                const int64_t ch = c - 1;
+            const bool pass = c >= 2 && c - 2 < nchunk;
+            if (pass) {
+                // cur was requested a period ago; nothing newer is outstanding
+                // except the previous period's o stores
+                vm_wait<0>();
+            }
+            floatx4 vcur[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vcur[i][j] = __uint_as_float(cur[i][j] << 16);
+            if (c >= 1 && c - 1 < nchunk) load_v(c - 1, nxt);
+            if (pass) {
+                const int64_t ch = c - 2;
                 const int64_t t0 = ch * kPipeChunk;
                 const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
-                const unsigned char *slot = slot_base + (int)(ch & 1) * Lds::SLOT;
+                const unsigned char *slot = slot_base + (int)(ch % Lds::NSLOT) * Lds::SLOT;
                 const T *sKt = reinterpret_cast<const T *>(slot + Lds::S_KT);
                 const T *sQt = reinterpret_cast<const T *>(slot + Lds::S_QT);
                 const T *sKh = reinterpret_cast<const T *>(slot + Lds::S_KH);
@@ -1250,15 +1228,6 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                 const T *sXr = reinterpret_cast<const T *>(slot + Lds::S_XR);
                 const float *sEbC = reinterpret_cast<const float *>(slot + Lds::S_EBC);
 
-                // cur was requested a period ago; nothing newer is outstanding
-                // except the previous period's o stores
-                vm_wait<0>();
-                floatx4 vcur[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) vcur[i][j] = __uint_as_float(cur[i][j] << 16);
-                if (c < nchunk) load_v(c, nxt);
 
                 // Z = K~ S, then D = V - Z (token rows, this column block)
                 floatx4 zacc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
@@ -1320,13 +1289,48 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                 for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
             }
             lds_barrier();                                  // BAR1
+            if (s == 0 && c >= 1 && c - 1 < nchunk) {
+                // ---- X = (I + A)^-1 and T = X Diag(beta) of chunk c - 1 ------
+                const int64_t ch = c - 1;
+                const T *sA = reinterpret_cast<const T *>(smem + Lds::AB + (int)(ch & 1) * Lds::SQ);
+                const float *sBeta = reinterpret_cast<const float *>(smem + Lds::BETA + (int)(ch & 1) * 128);
+                T *sXr = reinterpret_cast<T *>(slot_base + (int)(ch % Lds::NSLOT) * Lds::SLOT + Lds::S_XR);
+                const T tz = T(0);
+                const floatx4 z4 = {0, 0, 0, 0};
+                auto addI = [&](floatx4 m) { return m + eye; };
+                floatx4 x[2], xT[2];
+#pragma unroll
+                for (int IB = 0; IB < 2; ++IB) {
+                    // N = -A_II in both layouts; A_II^16 = 0, so (I + A_II)^-1 =
+                    // (I + N)(I + N^2)(I + N^4)(I + N^8)
+                    const floatx4 nT = -lds_load4(sA + (16 * IB + lr) * LDT + 16 * IB + lg4);
+                    floatx4 n;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) n[j] = -to_f32(sA[(16 * IB + lg4 + j) * LDT + 16 * IB + lr]);
+                    const floatx4 n2 = mma16(tz, nT, n, z4);
+                    const floatx4 n2T = mma16(tz, n, nT, z4);
+                    const floatx4 n4 = mma16(tz, n2T, n2, z4);
+                    const floatx4 n4T = mma16(tz, n2, n2T, z4);
+                    const floatx4 n8 = mma16(tz, n4T, n4, z4);
+                    const floatx4 p1T = mma16(tz, addI(n2), addI(nT), z4);
+                    const floatx4 p2T = mma16(tz, addI(n4), p1T, z4);
+                    x[IB] = mma16(tz, p2T, addI(n8), z4);
+                    xT[IB] = mma16(tz, addI(n8), p2T, z4);
+                }
+                // X_10 = -X_11 A_10 X_00
+                const floatx4 y = mma16(tz, lds_load4(sA + (16 + lr) * LDT + lg4), x[0], z4);
+                const floatx4 x10T = -mma16(tz, y, xT[1], z4);
+                const floatx4 b0 = *reinterpret_cast<const floatx4 *>(sBeta + lg4);
+                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(sBeta + 16 + lg4);
+                store4v(sXr + lr * LDT + lg4, xT[0] * b0);
+                store4v(sXr + (16 + lr) * LDT + 16 + lg4, xT[1] * b1);
+                store4v(sXr + (16 + lr) * LDT + lg4, x10T * b0);
+            }
             lds_barrier();                                  // BAR2
-            lds_barrier();                                  // BAR3
         };
-        load_v(0, vv0);
-        for (int64_t c = 0; c <= nchunk; c += 2) {
-            period(c, vv1, vv0);
-            if (c + 1 <= nchunk) period(c + 1, vv0, vv1);
+        for (int64_t c = 0; c <= nchunk + 1; c += 2) {
+            period(c, vv0, vv1);
+            if (c + 1 <= nchunk + 1) period(c + 1, vv1, vv0);
         }
         if (a.ST) {
 #pragma unroll
