@@ -823,6 +823,11 @@ constexpr int kPipeChunk = 32;
 // vmcnt: vector-memory operations complete in issue order, and the waves
 // that use these issue no other vector-memory loads in between.  The memory
 // clobber keeps other memory operations from moving across them.
+// Contract: the compiler takes an asm output as written when the asm issues,
+// so a destination register must stay untouched until its wait; every value
+// loaded here is used after its wait (never dead, never copied before), and
+// each role waits for everything before it ends.  A CPU test scans the
+// compiled kernel for instructions that touch such a register too early.
 __device__ __forceinline__ floatx4 vm_load16_nt(const void *p) {
     floatx4 r;
     asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
@@ -834,6 +839,16 @@ __device__ __forceinline__ bf16x4 vm_load8(const void *p) {
     asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return __builtin_bit_cast(bf16x4, r);
 }
+__device__ __forceinline__ floatx2 vm_load8_nt(const void *p) {
+    floatx2 r;
+    asm volatile("global_load_dwordx2 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ unsigned vm_load4(const void *p) {
+    unsigned r;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
 __device__ __forceinline__ unsigned vm_load_u16(const void *p) {
     unsigned r;
     asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
@@ -843,17 +858,45 @@ __device__ __forceinline__ unsigned vm_load_u16(const void *p) {
 template <int N> __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// register fence: after a wait, every use of x depends on this statement,
+// so the compiler cannot move a use of a hand-waited load above its wait
+template <typename V> __device__ __forceinline__ void vm_fence(V &x) { asm volatile("" : "+v"(x)); }
+// as vm_wait<N> when `more` is set, else as vm_wait<0>; one asm block, so
+// every path through it has passed a wait
+template <int N> __device__ __forceinline__ void vm_wait_or_all(bool more) {
+    asm volatile("s_cmp_eq_u32 %0, 0\n\t"
+                 "s_cbranch_scc1 .Lvm_all_%=\n\t"
+                 "s_waitcnt vmcnt(%1)\n\t"
+                 "s_branch .Lvm_done_%=\n"
+                 ".Lvm_all_%=:\n\t"
+                 "s_waitcnt vmcnt(0)\n"
+                 ".Lvm_done_%=:" ::"s"(__builtin_amdgcn_readfirstlane((unsigned)more)), "n"(N)
+                 : "memory", "scc");
+}
 
-// Channel-major rows of the 32-token tiles: one spare row every 16 rows keeps
-// both the prep stores (rows 4 apart) and the MFMA fragment reads (16
-// consecutive rows) free of bank conflicts at a pitch of 40 elements.
-__device__ __forceinline__ int crow16(int c) { return c + (c >> 4); }
+// two bf16 (packed in 32 bits) -> fp32, and back; eight bf16 as two 8-byte stores
+__device__ __forceinline__ floatx2 unpack2(unsigned u) {
+    return floatx2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+}
+__device__ __forceinline__ void store2v(bf16 *p, floatx2 v) {
+    *reinterpret_cast<bf16x2 *>(p) = bf16x2{(bf16)v[0], (bf16)v[1]};
+}
+__device__ __forceinline__ void store8(bf16 *p, const float *x) {
+    store4(p, x[0], x[1], x[2], x[3]);
+    store4(p + 4, x[4], x[5], x[6], x[7]);
+}
 
+// LDS plan.  Row pitches are chosen for the access widths that read each
+// buffer (banks of 4 bytes, 128 bytes per cycle): rows read as 8-byte MFMA
+// fragments by 16 lanes have a pitch of 2 mod 4 dwords, rows read as 16-byte
+// fragments by 8 lanes a pitch of 4 mod 8 dwords; both are then conflict
+// free, and so are the prep waves' stores.
 template <int DK> struct PipeLds {
-    static constexpr int LDK = DK + 8;              // token-row pitch (elements)
-    static constexpr int LDT = 40;                  // 32-column pitch (elements)
-    static constexpr int NCR = DK + DK / 16;        // channel rows after crow16
-    static constexpr int TOK = 32 * LDK * 2;        // 32 token rows, bytes
+    static constexpr int LDK = DK + 8;              // prep token rows (16-byte reads)
+    static constexpr int LDKE = DK + 4;             // handoff token rows (8-byte reads)
+    static constexpr int LDT = 36;                  // 32-column tiles and channel rows
+    static constexpr int TOK = 32 * LDK * 2;
+    static constexpr int TOKE = 32 * LDKE * 2;
     static constexpr int SQ = 32 * LDT * 2;         // 32 x 32 tile, bytes
     // prep-only buffers
     static constexpr int QR = 0;                    // q e^{lam}       (subtile-referenced)
@@ -865,9 +908,9 @@ template <int DK> struct PipeLds {
     static constexpr int PREP = BETA + 2 * 32 * 4;
     // one handoff slot
     static constexpr int S_KT = 0;                  // K~ = k e^{b} rows
-    static constexpr int S_QT = S_KT + TOK;         // Q~ = q e^{b} rows
-    static constexpr int S_KH = S_QT + TOK;         // K^T = (k e^{b_C - b})^T channel rows
-    static constexpr int S_PH = S_KH + NCR * LDT * 2;
+    static constexpr int S_QT = S_KT + TOKE;        // Q~ = q e^{b} rows
+    static constexpr int S_KH = S_QT + TOKE;        // K^T = (k e^{b_C - b})^T channel rows
+    static constexpr int S_PH = S_KH + DK * LDT * 2;
     static constexpr int S_PL = S_PH + SQ;
     static constexpr int S_XR = S_PL + SQ;          // T = X Diag(beta), row-major
     static constexpr int S_EBC = S_XR + SQ;         // e^{b_C}, DK fp32
@@ -885,7 +928,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
     using PF = Perm<bf16>;
     using KF = Kc<bf16>;
     using T = bf16;
-    constexpr int LDK = Lds::LDK, LDT = Lds::LDT;
+    constexpr int LDK = Lds::LDK, LDKE = Lds::LDKE, LDT = Lds::LDT;
     constexpr int NKS = DK / 32;                    // 32-deep k steps over channels
     constexpr int NCB = DK / 16;                    // state row tiles
     constexpr float kLog2e = 1.4426950408889634f;
@@ -920,14 +963,15 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         // =================================================================
         // prep role
         // =================================================================
-        constexpr int QPW = DK / 8;                 // channel quads per wave (two waves per subtile)
-        constexpr int SUBT = 64 / QPW;              // lanes along one subtile's tokens
-        constexpr int TPT = 16 / SUBT;              // tokens per lane
+        // a prep wave covers one subtile's 16 tokens x 64 channels; lane =
+        // (token half pos, channel pair): 8 tokens x 2 channels, so the
+        // running products inside the subtile need one exchange (lane ^ 32)
+        constexpr int TPL = 8;                      // tokens per lane
         const int p = wave - 4;
         const int I = p >> 1;                       // subtile of this wave
-        const int pos = lane / QPW;
-        const int cq = (p & 1) * QPW + lane % QPW;  // channel quad
-        const int tb = 16 * I + pos * TPT;          // first token of this lane (in the chunk)
+        const int pos = lane >> 5;
+        const int c0 = (p & 1) * 64 + 2 * (lane & 31);   // this lane's first channel
+        const int tb = 16 * I + TPL * pos;          // first token of this lane (in the chunk)
         T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
         T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
         T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
@@ -951,12 +995,12 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         // periods before its use (one 32-token period is shorter than the
         // memory latency under load)
         struct Raw {
-            floatx4 g[TPT];
-            bf16x4 k[TPT], q[TPT];
+            floatx2 g[TPL];
+            unsigned k[TPL], q[TPL];                // two bf16 each
             unsigned beta;                          // bf16 bits, zero-extended
         };
         Raw raw0, raw1;
-        constexpr int NRAW = 3 * TPT + 1;           // loads per set
+        constexpr int NRAW = 3 * TPL + 1;           // loads per set
         auto load_raw = [&](int64_t ch, Raw &r) {
             const int64_t t0 = ch * kPipeChunk;
             const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
@@ -965,13 +1009,13 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             const void *kb = kp + tok0 * DK, *qb = qp + tok0 * DK;
             const void *bb = bp + tok0;
 #pragma unroll
-            for (int i = 0; i < TPT; ++i) {
+            for (int i = 0; i < TPL; ++i) {
                 int tl = tb + i;
                 if (L < kPipeChunk) tl = tl < L ? tl : L - 1;
-                const unsigned e = (unsigned)tl * HDK + 4 * cq;
-                r.g[i] = vm_load16_nt(at<floatx4>(gb, e * 4u));
-                r.k[i] = vm_load8(at<bf16x4>(kb, e * 2u));
-                r.q[i] = vm_load8(at<bf16x4>(qb, e * 2u));
+                const unsigned e = (unsigned)tl * HDK + c0;
+                r.g[i] = vm_load8_nt(at<floatx2>(gb, e * 4u));
+                r.k[i] = vm_load4(at<unsigned>(kb, e * 2u));
+                r.q[i] = vm_load4(at<unsigned>(qb, e * 2u));
             }
             const int bl = lane & 31;
             r.beta = vm_load_u16(at<unsigned short>(bb, (unsigned)(bl < L ? bl : L - 1) * (unsigned)H * 2u));
@@ -991,84 +1035,82 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             T *sPl = reinterpret_cast<T *>(slot + Lds::S_PL);
             float *sEbC = reinterpret_cast<float *>(slot + Lds::S_EBC);
 
+            // this chunk's raw loads were issued two periods ago; the next
+            // chunk's (one set, NRAW loads) may still be in flight
+            vm_wait_or_all<NRAW>(c + 1 < nchunk);
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                vm_fence(raw.g[i]);
+                vm_fence(raw.k[i]);
+                vm_fence(raw.q[i]);
+            }
+            vm_fence(raw.beta);
             // values carried from P1 to P2
-            floatx4 kR[TPT], qR[TPT], kEt[TPT];
+            floatx2 kR[TPL], qR[TPL], kEt[TPL];
             if (live) {
-                // this chunk's raw loads were issued two periods ago; the next
-                // chunk's (one set, NRAW loads) may still be in flight
-                if (c + 1 < nchunk) vm_wait<NRAW>();
-                else vm_wait<0>();
                 // ---- P1: alpha and running products; subtile-local tiles ---
-                floatx4 R[TPT], Et[TPT], eLam;
+                floatx2 R[TPL], Et[TPL], eLam;
                 {
                     // past the end of the sequence alpha = 1 (g = 0): e^{b_C} stops at
                     // the last token; beta = 0 there zeroes those rows of A and T
-                    floatx4 al[TPT];
-                    if (L == kPipeChunk) {
+                    floatx2 al[TPL];
 #pragma unroll
-                        for (int i = 0; i < TPT; ++i) al[i] = exp2_4(raw.g[i] * kLog2e);
-                    } else {
+                    for (int i = 0; i < TPL; ++i) {
+                        const floatx2 x = raw.g[i] * kLog2e;
+                        al[i] = floatx2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
+                    }
+                    if (L < kPipeChunk) {
 #pragma unroll
-                        for (int i = 0; i < TPT; ++i) {
-                            const floatx4 e = exp2_4(raw.g[i] * kLog2e);
+                        for (int i = 0; i < TPL; ++i) {
                             const bool in = tb + i < L;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) al[i][j] = in ? e[j] : 1.0f;
+                            al[i] = floatx2{in ? al[i][0] : 1.0f, in ? al[i][1] : 1.0f};
                         }
                     }
-                    floatx4 tot = al[0];
+                    floatx2 tot = al[0];
 #pragma unroll
-                    for (int i = 1; i < TPT; ++i) tot *= al[i];
-                    floatx4 pre = {1, 1, 1, 1}, suf = {1, 1, 1, 1};
-#pragma unroll
-                    for (int s = 1; s < SUBT; ++s) {
-                        const bool use_fw = pos >= s, use_bw = pos + s < SUBT;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float fw = __shfl(tot[j], lane - s * QPW);
-                            const float bw = __shfl(tot[j], lane + s * QPW);
-                            pre[j] *= use_fw ? fw : 1.0f;
-                            suf[j] *= use_bw ? bw : 1.0f;
-                        }
-                    }
+                    for (int i = 1; i < TPL; ++i) tot *= al[i];
+                    // the other token half's product: before (pos 1) or after (pos 0)
+                    const floatx2 other = {__shfl_xor(tot[0], 32), __shfl_xor(tot[1], 32)};
+                    const floatx2 one = {1.0f, 1.0f};
+                    const floatx2 pre = pos ? other : one, suf = pos ? one : other;
                     R[0] = pre * al[0];
 #pragma unroll
-                    for (int i = 1; i < TPT; ++i) R[i] = R[i - 1] * al[i];
-                    Et[TPT - 1] = suf;
+                    for (int i = 1; i < TPL; ++i) R[i] = R[i - 1] * al[i];
+                    Et[TPL - 1] = suf;
 #pragma unroll
-                    for (int i = TPT - 2; i >= 0; --i) Et[i] = Et[i + 1] * al[i + 1];
-                    eLam = R[TPT - 1] * suf;
+                    for (int i = TPL - 2; i >= 0; --i) Et[i] = Et[i + 1] * al[i + 1];
+                    eLam = R[TPL - 1] * suf;
                 }
-                if (pos == 0) *reinterpret_cast<floatx4 *>(sEL + I * DK + 4 * cq) = eLam;
+                if (pos == 0) *reinterpret_cast<floatx2 *>(sEL + I * DK + c0) = eLam;
                 {
                     const float bv = lane < L ? __uint_as_float(raw.beta << 16) : 0.0f;
                     if (p == 0 && lane < 32) sBeta[lane] = bv;
                 }
-                const floatx4 eNegLam = rcp_4(eLam);
-                float kh[4][TPT];
+                const floatx2 eNegLam = {__builtin_amdgcn_rcpf(eLam[0]), __builtin_amdgcn_rcpf(eLam[1])};
+                float kh[2][TPL];
 #pragma unroll
-                for (int i = 0; i < TPT; ++i) {
+                for (int i = 0; i < TPL; ++i) {
                     const int tl = tb + i, r = tl - 16 * I;
-                    const floatx4 kv = to_f4(raw.k[i]), qv = to_f4(raw.q[i]);
+                    const floatx2 kv = unpack2(raw.k[i]), qv = unpack2(raw.q[i]);
                     kR[i] = kv * R[i];
                     qR[i] = qv * R[i];
                     kEt[i] = kv * Et[i];
-                    store4v(sKr + tl * LDK + 4 * cq, kR[i]);
-                    store4v(sQr + tl * LDK + 4 * cq, qR[i]);
+                    store2v(sKr + tl * LDK + c0, kR[i]);
+                    store2v(sQr + tl * LDK + c0, qR[i]);
                     // diagonal pair column tile: k e^{-lam}
-                    store4v(sKc + ((I == 0 ? 0 : 32) + r) * LDK + 4 * cq, kEt[i] * eNegLam);
+                    store2v(sKc + ((I == 0 ? 0 : 32) + r) * LDK + c0, kEt[i] * eNegLam);
                     if (I == 0) {
-                        store4v(sKc + (16 + r) * LDK + 4 * cq, kEt[i]);   // pair (1, 0)
-                        store4v(sKt + tl * LDK + 4 * cq, kR[i]);          // b = lam in subtile 0
-                        store4v(sQt + tl * LDK + 4 * cq, qR[i]);
+                        store2v(sKc + (16 + r) * LDK + c0, kEt[i]);   // pair (1, 0)
+                        store2v(sKt + tl * LDKE + c0, kR[i]);          // b = lam in subtile 0
+                        store2v(sQt + tl * LDKE + c0, qR[i]);
                     } else {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) kh[j][i] = kEt[i][j];  // b_C - b = Lam_1 - lam
+                        kh[0][i] = kEt[i][0];                           // b_C - b = Lam_1 - lam
+                        kh[1][i] = kEt[i][1];
                     }
                 }
                 if (I == 1) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) storeN<TPT>(sKh + crow16(4 * cq + j) * LDT + tb, kh[j]);
+                    store8(sKh + c0 * LDT + tb, kh[0]);
+                    store8(sKh + (c0 + 1) * LDT + tb, kh[1]);
                 }
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
@@ -1100,25 +1142,25 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                     }
                 }
                 {
-                    const floatx4 e0 = *reinterpret_cast<const floatx4 *>(sEL + 4 * cq);
-                    const floatx4 e1 = *reinterpret_cast<const floatx4 *>(sEL + DK + 4 * cq);
+                    const floatx2 e0 = *reinterpret_cast<const floatx2 *>(sEL + c0);
+                    const floatx2 e1 = *reinterpret_cast<const floatx2 *>(sEL + DK + c0);
                     if (I == 1) {
 #pragma unroll
-                        for (int i = 0; i < TPT; ++i) {
-                            store4v(sKt + (tb + i) * LDK + 4 * cq, kR[i] * e0);
-                            store4v(sQt + (tb + i) * LDK + 4 * cq, qR[i] * e0);
+                        for (int i = 0; i < TPL; ++i) {
+                            store2v(sKt + (tb + i) * LDKE + c0, kR[i] * e0);
+                            store2v(sQt + (tb + i) * LDKE + c0, qR[i] * e0);
                         }
                     } else {
-                        float kh[4][TPT];
+                        float kh[2][TPL];
 #pragma unroll
-                        for (int i = 0; i < TPT; ++i) {
-                            const floatx4 v = kEt[i] * e1;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) kh[j][i] = v[j];
+                        for (int i = 0; i < TPL; ++i) {
+                            const floatx2 v = kEt[i] * e1;
+                            kh[0][i] = v[0];
+                            kh[1][i] = v[1];
                         }
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) storeN<TPT>(sKh + crow16(4 * cq + j) * LDT + tb, kh[j]);
-                        if (pos == 0) *reinterpret_cast<floatx4 *>(sEbC + 4 * cq) = e0 * e1;
+                        store8(sKh + c0 * LDT + tb, kh[0]);
+                        store8(sKh + (c0 + 1) * LDT + tb, kh[1]);
+                        if (pos == 0) *reinterpret_cast<floatx2 *>(sEbC + c0) = e0 * e1;
                     }
                 }
 #pragma unroll
@@ -1160,6 +1202,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             period(c, raw0);
             if (c + 1 <= nchunk + 1) period(c + 1, raw1);
         }
+        vm_wait<0>();                               // no load outlives the wave
     } else {
         // =================================================================
         // state role: column block s of the slice, chunk c - 1 in period c
@@ -1204,16 +1247,17 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         // requested into nxt, inverse of chunk c - 1 (wave 0)
         auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) {
             const bool pass = c >= 2 && c - 2 < nchunk;
-            if (pass) {
-                // cur was requested a period ago; nothing newer is outstanding
-                // except the previous period's o stores
-                vm_wait<0>();
-            }
+            // cur was requested a period ago; nothing newer is outstanding
+            // except the previous period's o stores
+            vm_wait<0>();
             floatx4 vcur[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vcur[i][j] = __uint_as_float(cur[i][j] << 16);
+                for (int j = 0; j < 4; ++j) {
+                    vm_fence(cur[i][j]);
+                    vcur[i][j] = __uint_as_float(cur[i][j] << 16);
+                }
             if (c >= 1 && c - 1 < nchunk) load_v(c - 1, nxt);
             if (pass) {
                 const int64_t ch = c - 2;
@@ -1235,7 +1279,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                 for (int t = 0; t < NKS; ++t) {
                     typename PF::frag kf[2];
 #pragma unroll
-                    for (int Is = 0; Is < 2; ++Is) kf[Is] = PF::lds(sKt + (16 * Is + lr) * LDK, t * 32, lg4);
+                    for (int Is = 0; Is < 2; ++Is) kf[Is] = PF::lds(sKt + (16 * Is + lr) * LDKE, t * 32, lg4);
 #pragma unroll
                     for (int Is = 0; Is < 2; ++Is) PF::mma(zacc[Is], kf[Is], sf[t]);
                 }
@@ -1259,7 +1303,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                 for (int t = 0; t < NKS; ++t) {
                     typename PF::frag qf[2];
 #pragma unroll
-                    for (int Ir = 0; Ir < 2; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDK, t * 32, lg4);
+                    for (int Ir = 0; Ir < 2; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDKE, t * 32, lg4);
 #pragma unroll
                     for (int Ir = 0; Ir < 2; ++Ir) PF::mma(oacc[Ir], sf[t], qf[Ir]);
                 }
@@ -1281,7 +1325,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                 // S <- Diag(e^{b_C}) S + K^T U
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    const typename PF::frag kf = PF::lds(sKh + crow16(16 * cb + lr) * LDT, 0, lg4);
+                    const typename PF::frag kf = PF::lds(sKh + (16 * cb + lr) * LDT, 0, lg4);
                     sacc[cb] *= *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
                     PF::mma(sacc[cb], kf, uh);
                 }
@@ -1332,6 +1376,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
             period(c, vv0, vv1);
             if (c + 1 <= nchunk + 1) period(c + 1, vv1, vv0);
         }
+        vm_wait<0>();                               // no load outlives the wave
         if (a.ST) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
@@ -1368,8 +1413,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
-    // bf16 with dk, dv in {64, 128}: the pipelined 32-token kernel
-    const bool pipe = is_bf16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
+    const bool pipe = is_bf16 && dk == 128 && (dv == 64 || dv == 128);
     const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
@@ -1379,10 +1424,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
     const int nblocks = args.nbh * args.nslice;
     if (pipe) {
-        if (dk == 128)
-            hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(512), 0, s, args);
-        else
-            hipLaunchKernelGGL(chunk32_kernel<64>, dim3(nblocks), dim3(512), 0, s, args);
+        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(512), 0, s, args);
         return hipGetLastError();
     }
     if (is_bf16) {

@@ -1,0 +1,101 @@
+"""Static check of hand-waited loads in compiled gfx950 assembly.
+
+The pipelined chunk kernel issues some global loads as inline asm and waits
+for them with explicit `s_waitcnt vmcnt`.  The compiler takes an asm output as
+written when the asm issues, so it could reuse or copy a destination register
+before the data arrives; the late return would then corrupt the register
+(a corrupted address faults the GPU).  This check walks every path of the
+compiled kernel (each inline-asm block is one step) from each such load and
+reports any instruction that reads or writes the load's destination registers
+before an inline-asm block containing a vmcnt wait, and any path that ends
+the program first.
+"""
+from __future__ import annotations
+
+import re
+from typing import List, Tuple
+
+
+def _regs(op: str) -> set:
+    out = set()
+    for m in re.finditer(r"v\[(\d+):(\d+)\]|v(\d+)\b", op):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def function_body(asm_text: str, symbol: str) -> List[str]:
+    lines = asm_text.splitlines()
+    start = next(i for i, l in enumerate(lines) if l.startswith(symbol + ":"))
+    end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
+    return lines[start:end]
+
+
+def hazards(lines: List[str]) -> Tuple[int, List[str]]:
+    """Returns (number of asm loads, list of hazard descriptions)."""
+    steps = []          # ("label", name) | ("inst", idx, text) | ("asm", idx, [texts])
+    i = 0
+    while i < len(lines):
+        t = lines[i].strip()
+        if t.startswith(";;#ASMSTART"):
+            body = []
+            i += 1
+            while not lines[i].strip().startswith(";;#ASMEND"):
+                u = lines[i].strip()
+                if u and not u.startswith(";"):
+                    body.append(u)
+                i += 1
+            steps.append(("asm", i, body))
+            i += 1
+            continue
+        m = re.match(r"^(\.LBB\d+_\d+):", t)
+        if m:
+            steps.append(("label", m.group(1)))
+        elif t and not t.startswith(";") and not t.startswith("."):
+            steps.append(("inst", i, t))
+        i += 1
+    labels = {st[1]: k for k, st in enumerate(steps) if st[0] == "label"}
+    found, nloads = [], 0
+    for k, st in enumerate(steps):
+        if st[0] != "asm":
+            continue
+        for a in st[2]:
+            if not a.startswith("global_load"):
+                continue
+            nloads += 1
+            dregs = _regs(a.split()[1].rstrip(","))
+            stack, visited, bad = [k + 1], set(), None
+            while stack and bad is None:
+                j = stack.pop()
+                while j < len(steps):
+                    if j in visited:
+                        break
+                    visited.add(j)
+                    sj = steps[j]
+                    if sj[0] == "label":
+                        j += 1
+                        continue
+                    if sj[0] == "asm":
+                        if any(x.startswith("s_waitcnt vmcnt") for x in sj[2]):
+                            break
+                        j += 1
+                        continue
+                    text = sj[2]
+                    parts = text.split(None, 1)
+                    if len(parts) > 1 and _regs(parts[1]) & dregs:
+                        bad = text
+                        break
+                    if text.startswith("s_endpgm"):
+                        bad = text
+                        break
+                    if text.startswith("s_branch"):
+                        stack.append(labels[text.split()[1]])
+                        break
+                    if text.startswith("s_cbranch"):
+                        stack.append(labels[text.split()[1]])
+                    j += 1
+            if bad is not None:
+                found.append(f"{a}  ->  {bad}")
+    return nloads, found

@@ -1,0 +1,64 @@
+"""The pipelined chunk kernel's hand-waited loads, checked in its compiled
+gfx950 assembly (host-only: hipcc cross-compiles, nothing runs on a GPU)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from asm_load_check import function_body, hazards
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "linear_attention_sequence_gate_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.fixture(scope="module")
+def chunk_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "kda_chunk.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "kda_chunk.hip")]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def test_no_register_touched_before_its_wait(chunk_asm):
+    body = function_body(chunk_asm, "_ZN3kda14chunk32_kernelILi128EEEvNS_9ChunkArgsE")
+    nloads, found = hazards(body)
+    assert nloads > 50, nloads          # the prefetch loads are present
+    assert not found, "\n".join(found[:10])
+
+
+def test_checker_flags_an_early_reuse():
+    """A load whose destination is overwritten before any wait is reported."""
+    text = """_Zk:
+	;;#ASMSTART
+	global_load_dword v4, v[0:1], off
+	;;#ASMEND
+	v_mov_b32_e32 v4, 0
+	;;#ASMSTART
+	s_waitcnt vmcnt(0)
+	;;#ASMEND
+	s_endpgm
+.Lfunc_end0:"""
+    n, found = hazards(function_body(text, "_Zk"))
+    assert n == 1 and len(found) == 1
+
+
+def test_checker_accepts_a_waited_use_and_flags_exit():
+    ok = """_Zk:
+	;;#ASMSTART
+	global_load_dword v4, v[0:1], off
+	;;#ASMEND
+	;;#ASMSTART
+	s_waitcnt vmcnt(0)
+	;;#ASMEND
+	v_add_u32_e32 v5, v4, v4
+	s_endpgm
+.Lfunc_end0:"""
+    assert hazards(function_body(ok, "_Zk")) == (1, [])
+    early_exit = ok.replace("\t;;#ASMSTART\n\ts_waitcnt vmcnt(0)\n\t;;#ASMEND\n", "", 1)
+    assert len(hazards(function_body(early_exit, "_Zk"))[1]) == 1
