@@ -59,12 +59,16 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_gate_amd", "csrc")
 PROFILE_TAG = "prefill_b4h32t32k_decode256x32"
 TRAFFIC_MD = os.path.join(ROOT, "profiles", f"hbm_traffic_{PROFILE_TAG}.md")
 TRACE_MD = os.path.join(ROOT, "profiles", f"kernel_trace_{PROFILE_TAG}.md")
-# kernel -> (name fragment in a profiler trace, sources that define it)
+# kernel -> (name fragments in a profiler trace, sources that define it)
 KERNELS = {
-    "chunk_fwd": ("chunk_fwd_kernel", ("kda_chunk.hip", "kda_device.h")),
-    "decode_step": ("decode_step_kernel", ("kda_decode.hip", "kda_device.h")),
-    "gate": ("gate_kernel", ("kda_gate.hip", "kda_device.h")),
+    "chunk_fwd": (("chunk32_kernel", "chunk_fwd_kernel"), ("kda_chunk.hip", "kda_device.h")),
+    "decode_step": (("decode_step_kernel",), ("kda_decode.hip", "kda_device.h")),
+    "gate": (("gate_kernel",), ("kda_gate.hip", "kda_device.h")),
 }
+
+
+def _matches(name, frags):
+    return any(f in name for f in frags)
 
 # UT inverse of one 64-token chunk, per head-token (block substitution over
 # 16x16 blocks; the same constant as the flop model of the scope table).
@@ -286,7 +290,7 @@ def ingest_pmc(fetch_dir, write_dir):
             raise SystemExit(f"{counter}: no 1 GiB copy dispatch found in {d}")
         cal[counter] = COPY_BYTES / (sum(copies) / len(copies))
         for k, (frag, _) in KERNELS.items():
-            vals = [v * 1024 for n, v in rows if frag in n]
+            vals = [v * 1024 for n, v in rows if _matches(n, frag)]
             if vals:
                 per.setdefault(k, {})[counter] = (sum(vals) / len(vals), len(vals))
     rec = {"copy_factor": {"fetch": cal["FETCH_SIZE"], "write": cal["WRITE_SIZE"]}, "kernels": {}}
@@ -318,7 +322,7 @@ def ingest_pmc(fetch_dir, write_dir):
              "| kernel | fetch (MB) | write (MB) | traffic (MB) | algorithmic (MB) | traffic / algorithmic |",
              "|---|---|---|---|---|---|"]
     for k, r in rec["kernels"].items():
-        lines.append(f"| {KERNELS[k][0]} | {r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} "
+        lines.append(f"| {KERNELS[k][0][0]} | {r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} "
                      f"| {r['traffic_bytes'] / 1e6:.1f} | {alg[k] / 1e6:.1f} "
                      f"| {r['traffic_bytes'] / alg[k]:.3f} |")
     lines += ["", "Machine-readable record (read by bench.py; a kernel's entry is used only",
@@ -352,13 +356,13 @@ def ingest_trace(d):
              "| kernel | calls | avg (us) | min (us) | max (us) | avg without first call (us) |",
              "|---|---|---|---|---|---|"]
     frags = dict((k, v[0]) for k, v in KERNELS.items())
-    frags["copy (calibration)"] = "copyBuffer"
+    frags["copy (calibration)"] = ("copyBuffer",)
     for label, frag in frags.items():
         us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-              for r in rows if frag in r["Kernel_Name"]]
+              for r in rows if _matches(r["Kernel_Name"], frag)]
         if not us:
             continue
-        names = sorted({r["Kernel_Name"] for r in rows if frag in r["Kernel_Name"]})
+        names = sorted({r["Kernel_Name"] for r in rows if _matches(r["Kernel_Name"], frag)})
         rest = us[1:] or us
         lines.append(f"| {label}: `{names[0][:70]}` | {len(us)} | {sum(us) / len(us):.1f} "
                      f"| {min(us):.1f} | {max(us):.1f} | {sum(rest) / len(rest):.1f} |")
@@ -439,7 +443,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": chunk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": chunk_gbs / HBM_PEAK_GBS, "traffic": traffic["chunk_fwd"],
-                     "kernel": "chunk_fwd_kernel<bf16,128,64,8>",
+                     "kernel": "chunk32_kernel<128> (64-column dv slices)",
                      "bytes_per_launch": work["chunk_bytes"], "avg_ms": chunk_s * 1e3},
         "prefill": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
                     "gate_gbs": work["gate_bytes"] / (gate_ms / 1e3) / 1e9,
