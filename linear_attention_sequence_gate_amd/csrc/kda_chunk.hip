@@ -43,6 +43,8 @@
 //   E  state    per wave, no barrier: U = U' - W S (hi + lo), O = Q~ S + P U
 //               to HBM, S <- e^{b_C} S + K^^T U; S and U stay in MFMA
 //               accumulator registers and enter products from registers
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -799,10 +801,10 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
 
 // ===========================================================================
 // Pipelined variant (bf16, dk in {64, 128}, 64-column dv slices): 32-token
-// chunks of two 16-token subtiles, eight waves in two roles.
+// chunks of two 16-token subtiles, twelve waves in two roles.
 //
-//   prep waves (4..7) build chunk c: decay products, operand tiles, and the A
-//       and P scores of the three causal subtile pairs;
+//   prep waves (4..11, two per SIMD) build chunk c: decay products, operand
+//       tiles, and the A and P scores of the three causal subtile pairs;
 //   state waves (0..3) run the state pass of chunk c - 2, one 16-column block
 //       each; after it, state wave 0 forms X = (I + A)^-1 and T = X Diag(beta)
 //       of chunk c - 1, off the prep waves' critical path.
@@ -922,7 +924,7 @@ template <int DK> struct PipeLds {
 };
 
 template <int DK>
-__global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     constexpr int NV = 64;
     using Lds = PipeLds<DK>;
     using PF = Perm<bf16>;
@@ -963,14 +965,16 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
         // =================================================================
         // prep role
         // =================================================================
-        // a prep wave covers one subtile's 16 tokens x 64 channels; lane =
-        // (token half pos, channel pair): 8 tokens x 2 channels, so the
-        // running products inside the subtile need one exchange (lane ^ 32)
-        constexpr int TPL = 8;                      // tokens per lane
+        // eight prep waves, four per subtile: a wave covers one subtile's 16
+        // tokens x 32 channels; lane = (token group pos, channel pair), 4
+        // tokens x 2 channels, so each SIMD runs two prep waves whose
+        // dependency stalls interleave
+        constexpr int TPL = 4;                      // tokens per lane
+        constexpr int NPOS = 16 / TPL;              // token groups per subtile
         const int p = wave - 4;
-        const int I = p >> 1;                       // subtile of this wave
-        const int pos = lane >> 5;
-        const int c0 = (p & 1) * 64 + 2 * (lane & 31);   // this lane's first channel
+        const int I = p >> 2;                       // subtile of this wave
+        const int pos = lane >> 4;
+        const int c0 = (p & 3) * 32 + 2 * (lane & 15);   // this lane's first channel
         const int tb = 16 * I + TPL * pos;          // first token of this lane (in the chunk)
         T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
         T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
 
         // the blocks above the diagonal of P (hi, lo) and T in every slot are
         // read by the 32-deep products and never written: zero them once
-        for (int e = lane + 64 * p; e < Lds::NSLOT * 3 * 64; e += 256) {
+        for (int e = lane + 64 * p; e < Lds::NSLOT * 3 * 64; e += 512) {
             const int s_ = e / 192, m = (e / 64) % 3, q4 = e & 63;
             T *tile = reinterpret_cast<T *>(slot_base + s_ * Lds::SLOT +
                                             (m == 0 ? Lds::S_PH : m == 1 ? Lds::S_PL : Lds::S_XR));
@@ -1069,10 +1073,19 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                     floatx2 tot = al[0];
 #pragma unroll
                     for (int i = 1; i < TPL; ++i) tot *= al[i];
-                    // the other token half's product: before (pos 1) or after (pos 0)
-                    const floatx2 other = {__shfl_xor(tot[0], 32), __shfl_xor(tot[1], 32)};
-                    const floatx2 one = {1.0f, 1.0f};
-                    const floatx2 pre = pos ? other : one, suf = pos ? one : other;
+                    // products of the other token groups before / after this one
+                    floatx2 pre = {1.0f, 1.0f}, suf = {1.0f, 1.0f};
+#pragma unroll
+                    for (int s = 1; s < NPOS; ++s) {
+                        const bool use_fw = pos >= s, use_bw = pos + s < NPOS;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const float fw = __shfl(tot[j], lane - 16 * s);
+                            const float bw = __shfl(tot[j], lane + 16 * s);
+                            pre[j] *= use_fw ? fw : 1.0f;
+                            suf[j] *= use_bw ? bw : 1.0f;
+                        }
+                    }
                     R[0] = pre * al[0];
 #pragma unroll
                     for (int i = 1; i < TPL; ++i) R[i] = R[i - 1] * al[i];
@@ -1087,59 +1100,58 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                     if (p == 0 && lane < 32) sBeta[lane] = bv;
                 }
                 const floatx2 eNegLam = {__builtin_amdgcn_rcpf(eLam[0]), __builtin_amdgcn_rcpf(eLam[1])};
-                float kh[2][TPL];
+                // one straight-line copy per subtile, so the tokens' work can be
+                // interleaved by the scheduler
+                auto tiles = [&](auto sub) {
+                    constexpr int IS = decltype(sub)::value;
+                    float kh[2][TPL];
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    const int tl = tb + i, r = tl - 16 * I;
-                    const floatx2 kv = unpack2(raw.k[i]), qv = unpack2(raw.q[i]);
-                    kR[i] = kv * R[i];
-                    qR[i] = qv * R[i];
-                    kEt[i] = kv * Et[i];
-                    store2v(sKr + tl * LDK + c0, kR[i]);
-                    store2v(sQr + tl * LDK + c0, qR[i]);
-                    // diagonal pair column tile: k e^{-lam}
-                    store2v(sKc + ((I == 0 ? 0 : 32) + r) * LDK + c0, kEt[i] * eNegLam);
-                    if (I == 0) {
-                        store2v(sKc + (16 + r) * LDK + c0, kEt[i]);   // pair (1, 0)
-                        store2v(sKt + tl * LDKE + c0, kR[i]);          // b = lam in subtile 0
-                        store2v(sQt + tl * LDKE + c0, qR[i]);
-                    } else {
-                        kh[0][i] = kEt[i][0];                           // b_C - b = Lam_1 - lam
-                        kh[1][i] = kEt[i][1];
+                    for (int i = 0; i < TPL; ++i) {
+                        const int tl = tb + i, r = tl - 16 * IS;
+                        const floatx2 kv = unpack2(raw.k[i]), qv = unpack2(raw.q[i]);
+                        kR[i] = kv * R[i];
+                        qR[i] = qv * R[i];
+                        kEt[i] = kv * Et[i];
+                        store2v(sKr + tl * LDK + c0, kR[i]);
+                        store2v(sQr + tl * LDK + c0, qR[i]);
+                        // diagonal pair column tile: k e^{-lam}
+                        store2v(sKc + (32 * IS + r) * LDK + c0, kEt[i] * eNegLam);
+                        if constexpr (IS == 0) {
+                            store2v(sKc + (16 + r) * LDK + c0, kEt[i]);   // pair (1, 0)
+                            store2v(sKt + tl * LDKE + c0, kR[i]);          // b = lam in subtile 0
+                            store2v(sQt + tl * LDKE + c0, qR[i]);
+                        } else {
+                            kh[0][i] = kEt[i][0];                           // b_C - b = Lam_1 - lam
+                            kh[1][i] = kEt[i][1];
+                        }
                     }
-                }
-                if (I == 1) {
-                    store8(sKh + c0 * LDT + tb, kh[0]);
-                    store8(sKh + (c0 + 1) * LDT + tb, kh[1]);
-                }
+                    if constexpr (IS == 1) {
+                        storeN<TPL>(sKh + c0 * LDT + tb, kh[0]);
+                        storeN<TPL>(sKh + (c0 + 1) * LDT + tb, kh[1]);
+                    }
+                };
+                if (I == 0) tiles(std::integral_constant<int, 0>{});
+                else tiles(std::integral_constant<int, 1>{});
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
             lds_barrier();                                  // BAR1
 
             if (live) {
                 // ---- P2: scores; tiles that need the other subtile's total
-                // tiles: 0 A(0,0) 1 P(0,0) 2 A(1,0) 3 P(1,0) 4 A(1,1) 5 P(1,1)
-                floatx4 sc[2];
-                {
+                // tiles: 0 A(0,0) 1 P(0,0) 2 A(1,0) 3 P(1,0) 4 A(1,1) 5 P(1,1),
+                // prep wave p < 6 computes tile p
+                const int ti = p < 6 ? p : 0;
+                const int pi = ti >> 1;
+                const int Ib = pi == 0 ? 0 : 1, J = pi == 2 ? 1 : 0;
+                const bool isP = ti & 1;
+                floatx4 sc[1] = {floatx4{0, 0, 0, 0}};
+                if (p < 6) {
                     const int koff = (lane >> 4) * (KF::kStep / 4);
-                    const T *xs[2], *ys[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int ti = u == 0 ? p : (p + 4 < 6 ? p + 4 : p);
-                        const int pi = ti >> 1;
-                        const int Ib = pi == 0 ? 0 : 1;
-                        sc[u] = floatx4{0, 0, 0, 0};
-                        xs[u] = sKc + (16 * pi + lr) * LDK + koff;
-                        ys[u] = ((ti & 1) ? sQr : sKr) + (16 * Ib + lr) * LDK + koff;
-                    }
-                    auto xp = [&](int i, int st) { return xs[i] + st * KF::kStep; };
-                    auto yp = [&](int i, int st) { return ys[i] + st * KF::kStep; };
-                    if (p < 2) {
-                        group_mma<KF, 2, DK / 32>(sc, xp, yp);
-                    } else {
-                        floatx4(&sc1)[1] = *reinterpret_cast<floatx4(*)[1]>(&sc[0]);
-                        group_mma<KF, 1, DK / 32>(sc1, xp, yp);
-                    }
+                    const T *xs = sKc + (16 * pi + lr) * LDK + koff;
+                    const T *ys = (isP ? sQr : sKr) + (16 * Ib + lr) * LDK + koff;
+                    group_mma<KF, 1, DK / 32>(
+                        sc, [&](int, int st) { return xs + st * KF::kStep; },
+                        [&](int, int st) { return ys + st * KF::kStep; });
                 }
                 {
                     const floatx2 e0 = *reinterpret_cast<const floatx2 *>(sEL + c0);
@@ -1158,18 +1170,12 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                             kh[0][i] = v[0];
                             kh[1][i] = v[1];
                         }
-                        store8(sKh + c0 * LDT + tb, kh[0]);
-                        store8(sKh + (c0 + 1) * LDT + tb, kh[1]);
+                        storeN<TPL>(sKh + c0 * LDT + tb, kh[0]);
+                        storeN<TPL>(sKh + (c0 + 1) * LDT + tb, kh[1]);
                         if (pos == 0) *reinterpret_cast<floatx2 *>(sEbC + c0) = e0 * e1;
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    if (u == 1 && p >= 2) break;
-                    const int ti = u == 0 ? p : p + 4;
-                    const int pi = ti >> 1;
-                    const int Ib = pi == 0 ? 0 : 1, J = pi == 2 ? 1 : 0;
-                    const bool isP = ti & 1;
+                if (p < 6) {
                     const int r = 16 * Ib + lr;
                     const float br = sBeta[r];
                     const float rowscale = isP ? 1.0f : br;
@@ -1179,7 +1185,7 @@ __global__ __launch_bounds__(512, 1) void chunk32_kernel(ChunkArgs a) {
                     floatx4 val;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float x = sc[u][j] * rowscale;
+                        const float x = sc[0][j] * rowscale;
                         val[j] = lg4 + j < lim ? x : 0.0f;
                     }
                     if (isP) {
@@ -1424,7 +1430,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
     const int nblocks = args.nbh * args.nslice;
     if (pipe) {
-        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(512), 0, s, args);
+        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(768), 0, s, args);
         return hipGetLastError();
     }
     if (is_bf16) {
