@@ -33,7 +33,23 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // Four fp32 -> bf16 (round to nearest even).
 __device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
-    return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    // pairwise, so each pair maps onto one packed conversion
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_convertvector(floatx2{x[0], x[1]}, bf16x2);
+    const bf16x2 b = __builtin_convertvector(floatx2{x[2], x[3]}, bf16x2);
+    return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)});
+}
+
+// x = hi + lo to about 2^-17 relative: hi = bf16(x), lo = bf16(x - hi).  hi
+// is widened back to fp32 from its packed bits (two bf16 per dword) instead
+// of being converted a second time.
+__device__ __forceinline__ void split_bf16(floatx4 x, bf16x4 &hi, bf16x4 &lo) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    hi = __builtin_convertvector(x, bf16x4);
+    const u32x2 w = __builtin_bit_cast(u32x2, hi);
+    const floatx4 hf = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                        __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+    lo = __builtin_convertvector(x - hf, bf16x4);
 }
 
 // Store four consecutive values (8 B for bf16, 16 B for fp32); p must be aligned.

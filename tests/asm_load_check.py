@@ -99,3 +99,51 @@ def hazards(lines: List[str]) -> Tuple[int, List[str]]:
             if bad is not None:
                 found.append(f"{a}  ->  {bad}")
     return nloads, found
+
+
+_SEXT_OPS = ("s_bfe_i64", "s_bfe_i32", "s_ashr_i64", "s_ashr_i32", "s_sext_i32_i8", "s_sext_i32_i16")
+
+
+def _sregs(op: str) -> set:
+    out = set()
+    for m in re.finditer(r"s\[(\d+):(\d+)\]|\bs(\d+)\b", op):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def sign_extended_bases(lines: List[str]) -> Tuple[int, List[str]]:
+    """Loads whose scalar 64-bit base was last written by a sign extension.
+
+    A global load with a scalar base adds a zero-extended 32-bit lane offset
+    to the full 64-bit base, so the base must carry the pointer's own upper
+    half; a base built by sign-extending a 32-bit value is a truncated
+    pointer.  For each such load the nearest earlier instruction in program
+    text that writes any of the base registers is inspected.  Returns
+    (number of scalar-base loads, list of offending loads).
+    """
+    insts = []
+    for l in lines:
+        t = l.split(";")[0].strip()
+        if t and not t.startswith(".") and not t.endswith(":"):
+            insts.append(t)
+    n, found = 0, []
+    for i, t in enumerate(insts):
+        m = re.match(r"global_load_\w+\s+[^,]+,\s*v\d+,\s*(s\[\d+:\d+\])", t)
+        if not m:
+            continue
+        n += 1
+        base = _sregs(m.group(1))
+        for j in range(i - 1, -1, -1):
+            w = insts[j]
+            op = w.split()[0]
+            if not op.startswith("s_") or len(w.split()) < 2:
+                continue
+            dst = _sregs(w.split(None, 1)[1].split(",")[0])
+            if dst & base:
+                if op in _SEXT_OPS:
+                    found.append(f"{t}  <-  {w}")
+                break
+    return n, found

@@ -6,7 +6,7 @@ import subprocess
 
 import pytest
 
-from asm_load_check import function_body, hazards
+from asm_load_check import function_body, hazards, sign_extended_bases
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_sequence_gate_amd", "csrc")
@@ -30,6 +30,28 @@ def test_no_register_touched_before_its_wait(chunk_asm):
     nloads, found = hazards(body)
     assert nloads > 50, nloads          # the prefetch loads are present
     assert not found, "\n".join(found[:10])
+
+
+def test_scalar_load_bases_are_full_pointers(chunk_asm):
+    """Scalar bases of the hand-issued loads are never a sign-extended 32-bit
+    value (a truncated pointer: a 32-bit read-first-lane of a 64-bit address
+    produces one)."""
+    body = function_body(chunk_asm, "_ZN3kda14chunk32_kernelILi128EEEvNS_9ChunkArgsE")
+    n, found = sign_extended_bases(body)
+    assert n > 50, n
+    assert not found, "\n".join(found[:10])
+
+
+def test_base_checker_flags_a_sign_extended_base():
+    text = """_Zk:
+	s_load_dwordx2 s[4:5], s[0:1], 0x0
+	s_bfe_i64 s[6:7], s[4:5], 0x200000
+	global_load_dword v4, v1, s[6:7]
+	global_load_dword v5, v1, s[4:5]
+	s_endpgm
+.Lfunc_end0:"""
+    n, found = sign_extended_bases(function_body(text, "_Zk"))
+    assert n == 2 and len(found) == 1 and "v4" in found[0]
 
 
 def test_checker_flags_an_early_reuse():
