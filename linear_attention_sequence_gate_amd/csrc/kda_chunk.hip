@@ -966,6 +966,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         // =================================================================
         // prep role
         // =================================================================
+        // the second prep wave of each SIMD is the youngest of its three
+        // waves; equal priority with the first lets the older waves take the
+        // issue slots and leaves it last to reach each barrier
+        if (wave >= 8) __builtin_amdgcn_s_setprio(1);
         // eight prep waves, four per subtile: a wave covers one subtile's 16
         // tokens x 32 channels; lane = (token group pos, channel pair), 4
         // tokens x 2 channels, so each SIMD runs two prep waves whose
