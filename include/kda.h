@@ -66,8 +66,15 @@ enum {
      * [-5, 0] and every 16-token tile sum (tiles aligned to token 0 of the
      * call) lies in [-80, 0] -- the range the gate's floor guarantees and the
      * chunked kernel relies on.  Synchronises the stream; debugging only. */
-    KDA_FLAG_CHECK_RANGE = 1u
+    KDA_FLAG_CHECK_RANGE = 1u,
+    /* Bits 8..15: segments per sequence for the sequence-parallel path
+     * (bf16, dk = 128, dv in {64, 128}): 0 = chosen by the library, 1 = never
+     * split, n >= 2 = split into n segments (the count a 32-token-aligned
+     * segment length gives).  See kda_chunk_fwd. */
+    KDA_FLAG_SEGMENTS_SHIFT = 8,
+    KDA_FLAG_SEGMENTS_MASK = 0xff00u
 };
+#define KDA_FLAG_SEGMENTS(n) ((unsigned)(n) << KDA_FLAG_SEGMENTS_SHIFT)
 
 /*
  * kda_gate -- the K3 gate, g = -5 * sigmoid(exp(A[h,c]) * z[b,t,h,c]).
@@ -83,11 +90,31 @@ int kda_gate(const void *z, const float *A, float *g,
              int dtype, void *stream);
 
 /*
- * Workspace bytes kda_chunk_fwd needs for these sizes (a small constant; it
- * holds the range-check counter).  Returns 0 for invalid sizes.
+ * Workspace bytes kda_chunk_fwd needs for these sizes with the segment count
+ * the library picks (flags without segment bits): 256 bytes for the
+ * range-check counter, plus, when the sizes take the sequence-parallel path,
+ * its per-segment states and transitions (fp32: (P-1) B H dk dv for the
+ * segments' initial states, (P-2) B H (dk dv + dk dk) for the middle
+ * segments' zero-start states and transition matrices, P segments).
+ * Returns 0 for invalid sizes.
  */
 size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
                                     int64_t dk, int64_t dv, int dtype);
+
+/*
+ * Segments per sequence kda_chunk_fwd uses for these sizes when the flags
+ * leave the choice to the library (1 = one pass); 0 for invalid sizes.
+ */
+int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H,
+                                int64_t dk, int64_t dv, int dtype);
+
+/*
+ * As kda_chunk_fwd_workspace_size for an explicit segment count (the value
+ * of the KDA_FLAG_SEGMENTS bits: 0 = the library's choice, 1 = no split).
+ * Returns 0 for invalid sizes or a count above 255.
+ */
+size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
+                                             int64_t dk, int64_t dv, int dtype, int nseg);
 
 /*
  * kda_chunk_fwd -- chunkwise prefill over T tokens for B x H independent
@@ -105,9 +132,29 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
  *                   initial_state (in-place continuation)
  *   o             : [B, T, H, dv] dtype (output; must not alias any input)
  *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size()
- *                   bytes; required only with KDA_FLAG_CHECK_RANGE (else may be NULL)
+ *                   bytes (..._size_segments() for an explicit segment count);
+ *                   required with KDA_FLAG_CHECK_RANGE or explicit segments.
+ *                   May be NULL otherwise: the call then runs in one pass.
  * Chunks and 16-token tiles are aligned to token 0 of the call; the last
  * chunk may be partial.  Accumulation and the carried state are fp32.
+ *
+ * Sequence-parallel path ("Kimi K3 internal structure analysis", section
+ * "Infrastructure for a 3T-class MoE": a sequence segment maps an incoming
+ * state to an outgoing one).  With few chains (B H dv/64 workgroups below a
+ * quarter of the GPU) and long sequences, each sequence is cut into P
+ * segments of equal 32-token-aligned length (the count minimises a model of
+ * the wall time: rounds of workgroups per launch times the segment length,
+ * plus the chaining steps).  The recurrence is affine in the
+ * state, S_end = M S_start + L, so three stream-ordered launches give the
+ * same result as one pass up to fp32 rounding:
+ *   1. segment 0 from initial_state (its o is final); every middle segment
+ *      from a zero state (L) and its transition M (v = 0, identity start);
+ *   2. the segments' initial states, chained as M S + L;
+ *   3. segments 1 .. P-1 again from their initial states, writing o and
+ *      (last segment) final_state.
+ * The library picks P; KDA_FLAG_SEGMENTS(n) forces it (tests).  The split
+ * uses the workspace; without one large enough, the automatic choice falls
+ * back to one pass.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   const void *beta, const float *initial_state, float *final_state,

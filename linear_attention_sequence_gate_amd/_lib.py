@@ -23,9 +23,17 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_HIP = -3
 KDA_ERR_RANGE = -4
 KDA_FLAG_CHECK_RANGE = 1
+KDA_FLAG_SEGMENTS_SHIFT = 8
+KDA_FLAG_SEGMENTS_MASK = 0xFF00
 
-EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
-            "kda_last_error", "kda_version")
+
+def kda_flag_segments(n: int) -> int:
+    """Flag bits that request n segments per sequence (0 = library's choice, 1 = no split)."""
+    return (int(n) << KDA_FLAG_SEGMENTS_SHIFT) & KDA_FLAG_SEGMENTS_MASK
+
+EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+            "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
+            "kda_decode_step", "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -51,6 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_gate.restype = c_int
     L.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_chunk_fwd_workspace_size_segments.argtypes = [i64, i64, i64, i64, i64, c_int, c_int]
+    L.kda_chunk_fwd_workspace_size_segments.restype = ctypes.c_size_t
+    L.kda_chunk_fwd_auto_segments.argtypes = [i64, i64, i64, i64, i64, c_int]
+    L.kda_chunk_fwd_auto_segments.restype = c_int
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd.restype = c_int
@@ -116,8 +128,18 @@ def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
     return g
 
 
-def kda_chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int) -> int:
-    return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
+def kda_chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
+                                 nseg: Optional[int] = None) -> int:
+    """Workspace bytes for these sizes; nseg is an explicit segment count (None: the library's)."""
+    L = load_library()
+    if nseg is None:
+        return int(L.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
+    return int(L.kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, nseg))
+
+
+def kda_chunk_fwd_auto_segments(B: int, T: int, H: int, dk: int, dv: int, dtype: int) -> int:
+    """Segments per sequence the library picks for these sizes (1 = one pass)."""
+    return int(load_library().kda_chunk_fwd_auto_segments(B, T, H, dk, dv, dtype))
 
 
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
@@ -132,12 +154,13 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
         o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
     if final_state is None and want_final_state:
         final_state = torch.empty((B, H, dk, dv), device=q.device, dtype=torch.float32)
-    ws_bytes = 0
-    if workspace is None and (flags & KDA_FLAG_CHECK_RANGE):
-        ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dt)
-        workspace = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
-    elif workspace is not None:
-        ws_bytes = workspace.numel() * workspace.element_size()
+    if workspace is None:
+        # the range-check counter and, when the sizes take the sequence-split
+        # path, its per-segment states
+        nseg = (flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT
+        ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dt, nseg)
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(final_state),
         _ptr(o), _ptr(workspace), ws_bytes, B, T, H, dk, dv, dt, flags, _stream(stream)))

@@ -81,11 +81,31 @@ int kda_gate(const void *z, const float *A, float *g, int64_t B, int64_t T, int6
     return ok();
 }
 
-size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                    int dtype) {
+// The workspace: the range-check counter (256 bytes), then the buffers of the
+// sequence split when it is used.
+static constexpr size_t kCounterBytes = 256;
+
+size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                             int64_t dv, int dtype, int nseg) {
     if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
-    return 256;  // range-check counter (rounded up)
+    if (nseg < 0 || nseg > 255) return 0;
+    if (nseg == 0) nseg = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16);
+    if (nseg < 2 || !kda::seq_split_supported((int)dk, (int)dv, dtype == KDA_BF16)) return kCounterBytes;
+    return kCounterBytes + kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, nseg);
+}
+
+int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                int dtype) {
+    if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16);
+    return P >= 2 ? kda::seq_split_effective(T, P) : 1;
+}
+
+size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    int dtype) {
+    return kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, 0);
 }
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
@@ -102,8 +122,13 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                     (long long)dk, (long long)dv);
     if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs support dk in {32,64} only");
-    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE))
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_SEGMENTS_MASK))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: unknown flag bits 0x%x", flags);
+    const bool is_bf16 = dtype == KDA_BF16;
+    const int req_seg = (int)((flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT);
+    if (req_seg >= 2 && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "kda_chunk_fwd: a sequence split needs bf16 inputs, dk = 128, dv in {64, 128}");
     int64_t nk = B, nv = B, ns = B;
     if (!mul_ok(nk, T) || !mul_ok(nk, H) || !mul_ok(nk, dk) || !mul_ok(nv, T) || !mul_ok(nv, H) ||
         !mul_ok(nv, dv) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
@@ -141,8 +166,23 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                         "kda_chunk_fwd: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]",
                         nbad);
     }
+    // sequence split: requested, or picked for these sizes when the workspace
+    // holds its buffers (else one pass)
+    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16) : req_seg;
+    void *split_ws = nullptr;
+    if (nseg >= 2) {
+        const size_t need = kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, nseg);
+        if (workspace && workspace_bytes >= need) {
+            split_ws = static_cast<char *>(workspace) + kCounterBytes;
+        } else if (req_seg >= 2) {
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "kda_chunk_fwd: a %d-segment split needs a workspace of %zu bytes", nseg, need);
+        } else {
+            nseg = 1;
+        }
+    }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
-                                         (int)dk, (int)dv, dtype == KDA_BF16, s);
+                                         (int)dk, (int)dv, is_bf16, nseg, split_ws, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }

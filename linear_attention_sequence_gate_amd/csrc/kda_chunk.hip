@@ -57,8 +57,20 @@ struct ChunkArgs {
     const float *S0;
     float *ST;
     void *o;
-    int64_t T;
+    int64_t T;                  // tokens per sequence (also the batch stride)
     int H, DV, nslice, nbh, xcd_map;
+    // Sequence split (chunk32_kernel only).  A launch covers segments seg0 ..
+    // of nseg, seg_len tokens each (the last ends at T); nbh chains per
+    // segment, nslice slices per chain, the first nsl_v of them v columns.
+    //   phase 0: no split (one segment)
+    //   phase 1: segment 0 from S0, writing o and its final state to Sin;
+    //            segments p >= 1 from a zero state into Lb[p-1], and slices
+    //            nsl_v.. run the dk columns of the transition (v = 0, initial
+    //            state I) into Mb[p-1]
+    //   phase 3: segments p >= 1 from Sin[p-1], writing o (and ST for the last)
+    int64_t seg_len;
+    int phase, seg0, nseg, nsl_v;
+    float *Sin, *Lb, *Mb;
 };
 
 // Four consecutive elements of T in one register group.
@@ -942,23 +954,31 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
 
-    int bh, slice;
+    // block -> (unit, slice), unit -> (segment, chain); with the XCD map the
+    // slices of one unit share an XCD (and its L2 for q, k, g)
+    int unit, slice;
     {
         const int id = blockIdx.x;
         if (a.xcd_map) {
             const int x = id & 7, j = id >> 3;
-            bh = (j / a.nslice) * 8 + x;
+            unit = (j / a.nslice) * 8 + x;
             slice = j % a.nslice;
         } else {
-            bh = id / a.nslice;
+            unit = id / a.nslice;
             slice = id % a.nslice;
         }
     }
+    const int seg = a.seg0 + unit / a.nbh, bh = unit % a.nbh;
+    // transition columns: segment 0 needs none (it starts from the given state)
+    const bool mcols = slice >= a.nsl_v;
+    if (mcols && seg == 0) return;
     const int H = a.H, DV = a.DV;
     const int b = bh / H, h = bh % H;
     const int64_t T_ = a.T;
-    const int vcol0 = slice * NV;
-    const int64_t nchunk = (T_ + kPipeChunk - 1) / kPipeChunk;
+    const int64_t tbeg = (int64_t)seg * a.seg_len;
+    const int64_t tend = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
+    const int vcol0 = (mcols ? slice - a.nsl_v : slice) * NV;
+    const int64_t nchunk = (tend - tbeg + kPipeChunk - 1) / kPipeChunk;
     const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
     unsigned char *const slot_base = smem + Lds::PREP;
 
@@ -1015,8 +1035,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         const unsigned off_kq = ((unsigned)tb * HDK + (unsigned)c0) * 2u;
         const unsigned off_b = (unsigned)(lane & 31) * (unsigned)H * 2u;
         auto load_raw = [&](int64_t ch, Raw &r) {
-            const int64_t t0 = ch * kPipeChunk;
-            const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+            const int64_t t0 = tbeg + ch * kPipeChunk;
+            const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
             const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
             const char *gb = uniform_base(gp + tok0 * DK);
             const char *kb = uniform_base(kp + tok0 * DK), *qb = uniform_base(qp + tok0 * DK);
@@ -1050,8 +1070,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 
         auto period = [&](int64_t c, Raw &raw) {
             const bool live = c < nchunk;
-            const int64_t t0 = c * kPipeChunk;
-            const int L = live ? (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk) : 0;
+            const int64_t t0 = tbeg + c * kPipeChunk;
+            const int L = live ? (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk) : 0;
             unsigned char *slot = slot_base + (int)(c % Lds::NSLOT) * Lds::SLOT;
             T *sA = reinterpret_cast<T *>(smem + Lds::AB + (int)(c & 1) * Lds::SQ);
             float *sBeta = reinterpret_cast<float *>(smem + Lds::BETA + (int)(c & 1) * 128);
@@ -1239,8 +1259,30 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         // state role: column block s of the slice, chunk c - 1 in period c
         // =================================================================
         const int s = wave;
+        // this block's state endpoints and output (uniform): the initial
+        // state is read from s0 (zero when null) or is the identity, the
+        // final one goes to st (row pitch spitch) when st is set, and o is
+        // written when ob is set; transition columns read no v
+        const float *s0 = a.S0;
+        float *st = a.ST;
+        void *ob = a.o;
+        int spitch = DV;
+        const bool vzero = mcols;
+        if (a.phase == 1) {
+            const size_t vsz = (size_t)a.nbh * DK * DV, msz = (size_t)a.nbh * DK * DK;
+            if (mcols) {
+                s0 = nullptr; st = a.Mb + (size_t)(seg - 1) * msz; spitch = DK; ob = nullptr;
+            } else if (seg == 0) {
+                st = a.Sin;
+            } else {
+                s0 = nullptr; st = a.Lb + (size_t)(seg - 1) * vsz; ob = nullptr;
+            }
+        } else if (a.phase == 3) {
+            s0 = a.Sin + (size_t)(seg - 1) * a.nbh * DK * DV;
+            st = seg == a.nseg - 1 ? a.ST : nullptr;
+        }
         const T *__restrict__ vp = static_cast<const T *>(a.v);
-        T *__restrict__ op = static_cast<T *>(a.o);
+        T *__restrict__ op = static_cast<T *>(ob);
         const int ncol = vcol0 + 16 * s + lr;          // this lane's state / v column
         // this lane's diagonal entries (L layout) as a mask over packed bf16
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -1255,7 +1297,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int cc = 16 * cb + lg4 + j;
-                sacc[cb][j] = a.S0 ? a.S0[((int64_t)bh * DK + cc) * DV + ncol] : 0.0f;
+                sacc[cb][j] = vzero ? (cc == ncol ? 1.0f : 0.0f)
+                                    : s0 ? s0[((int64_t)bh * DK + cc) * spitch + ncol] : 0.0f;
             }
         typename PF::frag sf[NKS];
 #pragma unroll
@@ -1266,8 +1309,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         unsigned vv0[2][4], vv1[2][4];                  // v of alternate chunks (bf16 bits)
         const unsigned off_v = ((unsigned)lg4 * HDV + (unsigned)ncol) * 2u;
         auto load_v = [&](int64_t ch, unsigned (&dst)[2][4]) {
-            const int64_t t0 = ch * kPipeChunk;
-            const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+            const int64_t t0 = tbeg + ch * kPipeChunk;
+            const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
             const char *vb = uniform_base(vp + (((int64_t)b * T_ + t0) * H + h) * DV);
             // full chunk: token 16 i + lg4 + j is a scalar step of 16 i + j
             // rows from the lane's first row; last chunk: per-lane offsets
@@ -1301,19 +1344,21 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             // cur was requested a period ago; nothing newer is outstanding
             // except the previous period's o stores
             vm_wait<0>();
-            floatx4 vcur[2];
+            floatx4 vcur[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+            if (!vzero) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    vm_fence(cur[i][j]);
-                    vcur[i][j] = __uint_as_float(cur[i][j] << 16);
-                }
-            if (c >= 1 && c - 1 < nchunk) load_v(c - 1, nxt);
+                    for (int j = 0; j < 4; ++j) {
+                        vm_fence(cur[i][j]);
+                        vcur[i][j] = __uint_as_float(cur[i][j] << 16);
+                    }
+                if (c >= 1 && c - 1 < nchunk) load_v(c - 1, nxt);
+            }
             if (pass) {
                 const int64_t ch = c - 2;
-                const int64_t t0 = ch * kPipeChunk;
-                const int L = (int)((T_ - t0) < kPipeChunk ? (T_ - t0) : kPipeChunk);
+                const int64_t t0 = tbeg + ch * kPipeChunk;
+                const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
                 const unsigned char *slot = slot_base + (int)(ch % Lds::NSLOT) * Lds::SLOT;
                 const T *sKt = reinterpret_cast<const T *>(slot + Lds::S_KT);
                 const T *sQt = reinterpret_cast<const T *>(slot + Lds::S_QT);
@@ -1350,30 +1395,32 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 }
                 typename PF::frag uh, ul;
                 PF::regs_split(uacc, uh, ul);
-                // O = Q~ S + P U
-                floatx4 oacc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+                // O = Q~ S + P U (blocks that write no output skip it)
+                if (op) {
+                    floatx4 oacc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
 #pragma unroll
-                for (int t = 0; t < NKS; ++t) {
-                    typename PF::frag qf[2];
+                    for (int t = 0; t < NKS; ++t) {
+                        typename PF::frag qf[2];
 #pragma unroll
-                    for (int Ir = 0; Ir < 2; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDKE, t * 32, lg4);
+                        for (int Ir = 0; Ir < 2; ++Ir) qf[Ir] = PF::lds(sQt + (16 * Ir + lr) * LDKE, t * 32, lg4);
 #pragma unroll
-                    for (int Ir = 0; Ir < 2; ++Ir) PF::mma(oacc[Ir], sf[t], qf[Ir]);
-                }
+                        for (int Ir = 0; Ir < 2; ++Ir) PF::mma(oacc[Ir], sf[t], qf[Ir]);
+                    }
 #pragma unroll
-                for (int Ir = 0; Ir < 2; ++Ir) {
-                    const typename PF::frag ph = PF::lds(sPh + (16 * Ir + lr) * LDT, 0, lg4);
-                    const typename PF::frag pl = PF::lds(sPl + (16 * Ir + lr) * LDT, 0, lg4);
-                    PF::mma(oacc[Ir], uh, ph);
-                    PF::mma(oacc[Ir], ul, ph);
-                    PF::mma(oacc[Ir], uh, pl);
-                }
-                const void *obase = op + (((int64_t)b * T_ + t0) * H + h) * DV + vcol0 + 16 * s;
+                    for (int Ir = 0; Ir < 2; ++Ir) {
+                        const typename PF::frag ph = PF::lds(sPh + (16 * Ir + lr) * LDT, 0, lg4);
+                        const typename PF::frag pl = PF::lds(sPl + (16 * Ir + lr) * LDT, 0, lg4);
+                        PF::mma(oacc[Ir], uh, ph);
+                        PF::mma(oacc[Ir], ul, ph);
+                        PF::mma(oacc[Ir], uh, pl);
+                    }
+                    const void *obase = op + (((int64_t)b * T_ + t0) * H + h) * DV + vcol0 + 16 * s;
 #pragma unroll
-                for (int Ir = 0; Ir < 2; ++Ir) {
-                    const int r = 16 * Ir + lr;
-                    if (r < L)
-                        store4v(const_cast<T *>(at<T>(obase, ((unsigned)r * HDV + lg4) * 2u)), oacc[Ir]);
+                    for (int Ir = 0; Ir < 2; ++Ir) {
+                        const int r = 16 * Ir + lr;
+                        if (r < L)
+                            store4v(const_cast<T *>(at<T>(obase, ((unsigned)r * HDV + lg4) * 2u)), oacc[Ir]);
+                    }
                 }
                 // S <- Diag(e^{b_C}) S + K^T U
 #pragma unroll
@@ -1445,14 +1492,60 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             if (c + 1 <= nchunk + 1) period(c + 1, vv1, vv0);
         }
         vm_wait<0>();                               // no load outlives the wave
-        if (a.ST) {
+        if (st) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cc = 16 * cb + lg4 + j;
-                    a.ST[((int64_t)bh * DK + cc) * DV + ncol] = sacc[cb][j];
+                    st[((int64_t)bh * DK + cc) * spitch + ncol] = sacc[cb][j];
                 }
+        }
+    }
+}
+
+// ===========================================================================
+// Sequence split: chaining the segments' affine maps.  A segment maps its
+// initial state S to M S + L (the recurrence is affine in S: retention and
+// the delta rule act on S linearly, and v enters additively), so with the
+// transition M_p and zero-start state L_p of each middle segment,
+//     Sin[p] = M_p Sin[p-1] + L_p,   p = 1 .. nseg - 2,
+// is the state entering segment p + 1 (Sin[0], segment 0's final state from
+// the given initial state, is written by the first phase).  One workgroup per
+// (chain, 64-column block); the running block stays in LDS between steps.
+// ===========================================================================
+template <int DK>
+__global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
+                                                        const float *__restrict__ Lb,
+                                                        const float *__restrict__ Mb, int nbh,
+                                                        int DV, int nseg) {
+    __shared__ float sM[DK][DK + 1];
+    __shared__ float sS[DK][64];
+    const int ncb = DV / 64;
+    const int bh = blockIdx.x / ncb, col = (blockIdx.x % ncb) * 64;
+    const int tid = threadIdx.x, n = tid & 63;
+    const int r0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (DK / 4);   // this wave's 32 rows
+    const size_t vsz = (size_t)nbh * DK * DV, msz = (size_t)nbh * DK * DK;
+    for (int r = tid >> 6; r < DK; r += 4) sS[r][n] = Sin[((size_t)bh * DK + r) * DV + col + n];
+    for (int p = 1; p <= nseg - 2; ++p) {
+        const float *M = Mb + (size_t)(p - 1) * msz + (size_t)bh * DK * DK;
+        const float *L = Lb + (size_t)(p - 1) * vsz + (size_t)bh * DK * DV + col;
+        float *out = Sin + (size_t)p * vsz + (size_t)bh * DK * DV + col;
+        for (int e = tid; e < DK * DK; e += 256) sM[e / DK][e % DK] = M[e];
+        __syncthreads();
+        float acc[DK / 4];
+#pragma unroll
+        for (int i = 0; i < DK / 4; ++i) acc[i] = L[(size_t)(r0 + i) * DV + n];
+        for (int kk = 0; kk < DK; ++kk) {
+            const float sv = sS[kk][n];
+#pragma unroll
+            for (int i = 0; i < DK / 4; ++i) acc[i] = fmaf(sM[r0 + i][kk], sv, acc[i]);
+        }
+        __syncthreads();                            // every read of sS and sM is done
+#pragma unroll
+        for (int i = 0; i < DK / 4; ++i) {
+            sS[r0 + i][n] = acc[i];
+            out[(size_t)(r0 + i) * DV + n] = acc[i];
         }
     }
 }
@@ -1477,12 +1570,63 @@ static hipError_t launch_inst(const ChunkArgs &args, int nblocks, hipStream_t s)
     return hipGetLastError();
 }
 
+bool seq_split_supported(int dk, int dv, int is_bf16) {
+    return is_bf16 && dk == 128 && (dv == 64 || dv == 128);
+}
+
+int64_t seq_split_segment_len(int64_t T, int nseg) {
+    const int64_t per = (T + nseg - 1) / nseg;
+    return (per + kPipeChunk - 1) / kPipeChunk * kPipeChunk;
+}
+
+int seq_split_effective(int64_t T, int nseg) {
+    if (nseg < 2) return 1;
+    const int64_t len = seq_split_segment_len(T, nseg);
+    return (int)((T + len - 1) / len);
+}
+
+// The count minimising a model of the wall time: every workgroup of a launch
+// runs its segment in about the same time, so a launch of W workgroups takes
+// ceil(W / CUs) rounds of one segment; a split adds the chaining steps.
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16) {
+    constexpr int64_t kCUs = 256;             // MI355X compute units
+    constexpr int64_t kMinSegTokens = 4096;   // shorter segments do not repay the extra passes
+    constexpr int64_t kChainStepTokens = 160; // one chaining step costs about five 32-token periods
+    if (!seq_split_supported(dk, dv, is_bf16)) return 1;
+    const int64_t bh = B * H, nsl_v = dv / 64, nsl_m = dk / 64;
+    auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
+    // a split must beat one pass by 10%
+    double best = 0.9 * (double)T * (double)rounds(bh * nsl_v);
+    int best_p = 1;
+    int64_t pmax = T / kMinSegTokens;
+    if (pmax > 255) pmax = 255;
+    for (int P = 3; P <= pmax; ++P) {
+        const int64_t pe = seq_split_effective(T, P), len = seq_split_segment_len(T, P);
+        const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
+        const double cost = (double)len * (double)(rounds(w1) + rounds(w3)) +
+                            (double)kChainStepTokens * (double)(pe - 2);
+        if (cost < best) {
+            best = cost;
+            best_p = P;
+        }
+    }
+    return best_p;
+}
+
+size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg) {
+    const int P = seq_split_effective(T, nseg);
+    if (P < 2) return 0;
+    const size_t vsz = (size_t)B * H * dk * dv * 4, msz = (size_t)B * H * dk * dk * 4;
+    return (size_t)(P - 1) * vsz + (size_t)(P - 2) * (vsz + msz);
+}
+
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
-                            int64_t T, int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
+                            int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
+                            void *split_ws, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
-    const bool pipe = is_bf16 && dk == 128 && (dv == 64 || dv == 128);
+    const bool pipe = seq_split_supported(dk, dv, is_bf16);
     const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
@@ -1490,6 +1634,39 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.T = T; args.H = (int)H; args.DV = dv; args.nslice = dv / nv;
     args.nbh = (int)(B * H);
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
+    args.seg_len = T; args.phase = 0; args.seg0 = 0; args.nseg = 1; args.nsl_v = args.nslice;
+    args.Sin = args.Lb = args.Mb = nullptr;
+    const int P = pipe ? seq_split_effective(T, nseg) : 1;
+    if (pipe && P >= 2) {
+        if (!split_ws) return hipErrorInvalidValue;
+        const size_t vsz = (size_t)args.nbh * dk * dv;
+        args.Sin = static_cast<float *>(split_ws);
+        args.Lb = args.Sin + (size_t)(P - 1) * vsz;
+        args.Mb = args.Lb + (size_t)(P - 2) * vsz;
+        args.seg_len = seq_split_segment_len(T, P);
+        args.nseg = P;
+        // first phase: segment 0 from S0; segments 1 .. P-2 from zero, plus
+        // their transitions (the last segment needs neither)
+        const int units = (P - 1) * args.nbh;
+        args.phase = 1;
+        args.nslice = args.nsl_v + dk / 64;
+        args.xcd_map = units % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(units * args.nslice), dim3(768), 0, s, args);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (P >= 3) {
+            hipLaunchKernelGGL(seg_chain_kernel<128>, dim3(args.nbh * (dv / 64)), dim3(256), 0, s,
+                               args.Sin, args.Lb, args.Mb, args.nbh, dv, P);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        // last phase: segments 1 .. P-1 from their true initial states
+        args.phase = 3;
+        args.seg0 = 1;
+        args.nslice = args.nsl_v;
+        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(units * args.nslice), dim3(768), 0, s, args);
+        return hipGetLastError();
+    }
     const int nblocks = args.nbh * args.nslice;
     if (pipe) {
         hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(768), 0, s, args);

@@ -14,9 +14,23 @@ hipError_t launch_range_check(const float *g, int64_t B, int64_t T, int64_t H, i
                               unsigned int *bad, hipStream_t s);
 
 // Returns hipErrorInvalidValue when no kernel instance exists for (dk, dtype).
+// nseg >= 2 splits each sequence into that many segments (pipelined path
+// only; split_ws must hold seq_split_workspace() bytes), else one pass.
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
-                            int64_t T, int64_t H, int dk, int dv, int is_bf16, hipStream_t s);
+                            int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
+                            void *split_ws, hipStream_t s);
+
+// Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
+bool seq_split_supported(int dk, int dv, int is_bf16);
+// Segment length for nseg segments (a multiple of the 32-token chunk) and the
+// number of segments that length gives.
+int64_t seq_split_segment_len(int64_t T, int nseg);
+int seq_split_effective(int64_t T, int nseg);
+// Segment count picked for these sizes (1 = no split).
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16);
+// Device bytes the split needs (0 when it does not split).
+size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg);
 
 bool chunk_fwd_supported(int dk, int dv, int is_bf16);
 

@@ -34,8 +34,9 @@ def L():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
-              "kda_last_error", "kda_version"):
+    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+              "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
+              "kda_decode_step", "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -89,6 +90,52 @@ def test_workspace_query(L):
     assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
     assert L.kda_chunk_fwd_workspace_size(0, 64, 1, 32, 32, 1) == 0
     assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 32, 32, 5) == 0
+
+
+def test_sequence_split_workspace_and_policy(L):
+    ws = L.kda_chunk_fwd_workspace_size
+    wss = L.kda_chunk_fwd_workspace_size_segments
+    auto = L.kda_chunk_fwd_auto_segments
+
+    def split_bytes(B, H, dv, P):       # (P-1) initial states, (P-2) zero-start states + transitions
+        vsz, msz = B * H * 128 * dv * 4, B * H * 128 * 128 * 4
+        return 256 + (P - 1) * vsz + (P - 2) * (vsz + msz)
+
+    # B4 H32 T32K: 256 workgroups of 64 columns fill the GPU in one pass
+    assert auto(4, 32768, 32, 128, 128, 1) == 1
+    assert ws(4, 32768, 32, 128, 128, 1) == 256
+    # B1 H32 T1M: 64 workgroups in one pass; the split takes a few segments
+    P = auto(1, 1 << 20, 32, 128, 128, 1)
+    assert 3 <= P <= 9, P
+    assert ws(1, 1 << 20, 32, 128, 128, 1) == split_bytes(1, 32, 128, P)
+    assert wss(1, 1 << 20, 32, 128, 128, 1, 0) == ws(1, 1 << 20, 32, 128, 128, 1)
+    # one chain: many more segments
+    P1 = auto(1, 1 << 20, 1, 128, 128, 1)
+    assert P1 > 4 * P, (P1, P)
+    assert ws(1, 1 << 20, 1, 128, 128, 1) == split_bytes(1, 1, 128, P1)
+    # short sequences and shapes without the pipelined kernel run in one pass
+    assert auto(1, 8192, 1, 128, 128, 1) == 1 and ws(1, 8192, 1, 128, 128, 1) == 256
+    assert auto(1, 1 << 20, 1, 64, 64, 1) == 1
+    assert auto(1, 1 << 20, 1, 32, 32, 0) == 1
+    assert auto(0, 64, 1, 128, 128, 1) == 0
+    assert wss(1, 4096, 2, 32, 32, 0, 4) == 256           # fp32: no split path
+    assert wss(1, 4096, 2, 128, 128, 1, 1) == 256         # 1 = never split
+    # explicit counts: the 32-token-aligned segment length decides how many
+    assert wss(1, 1000, 2, 128, 64, 1, 3) == split_bytes(1, 2, 64, 3)   # 352 + 352 + 296
+    assert wss(1, 64, 2, 128, 64, 1, 3) == split_bytes(1, 2, 64, 2)     # two 32-token segments
+    assert wss(1, 1000, 2, 128, 64, 1, 256) == 0
+
+
+def test_sequence_split_validation(L):
+    E = _lib
+    seg3 = _lib.kda_flag_segments(3)
+    # fp32 or dk != 128 have no split path
+    assert chunk(L, flags=seg3) == E.KDA_ERR_UNSUPPORTED
+    assert "split" in _lib.kda_last_error()
+    # an explicit split needs its workspace
+    assert chunk(L, dk=128, dv=128, T=4096, flags=seg3) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
+    assert chunk(L, dk=128, dv=128, T=4096, flags=seg3, ws=P3, wsb=256) == E.KDA_ERR_INVALID_ARGUMENT
 
 
 def test_gate_validation(L):

@@ -1,0 +1,85 @@
+"""GPU parity of the sequence-parallel prefill path (each sequence cut into
+segments; segment transitions chained as S -> M S + L) against the oracle and
+against the one-pass kernel on the same inputs: forced segment counts with
+ragged last segments, initial states, in-place continuation, the automatic
+choice for a long few-chain input, and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_gate_amd import _lib, kda_chunk_fwd, kda_gate
+from kda_testutil import TOL, oracle_gate_f32, prefill_device, rho, say
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+
+
+def _split(x, g, nseg, **kw):
+    return kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"],
+                         flags=_lib.kda_flag_segments(nseg), **kw)
+
+
+@pytest.mark.parametrize("nseg,B,T,H,dv", [
+    (2, 1, 70, 2, 128),       # 64 + 6 tokens
+    (3, 2, 1000, 2, 64),      # 352, 352, 296
+    (5, 1, 777, 3, 128),      # four of 160, then 137
+    (4, 1, 4096, 2, 128),
+    (9, 1, 2000, 1, 128),     # seven middle segments chained
+])
+def test_forced_split_matches_oracle_and_one_pass(nseg, B, T, H, dv):
+    say("split", f"nseg={nseg} B={B} T={T} H={H} dv={dv}")
+    x = prefill_device(B, T, H, 128, dv, BF16, 400 + nseg, s0_std=0.02, stress=3.0)
+    g_f32 = oracle_gate_f32(x["z"], x["A"])
+    g = g_f32.cuda()
+    o_s, S_s = _split(x, g, nseg)
+    o_1, S_1 = _split(x, g, 1)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], x["S0"])
+    ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
+    r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
+    print(f"    vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}", flush=True)
+    assert np.isfinite(o_s.float().cpu().numpy()).all()
+    assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
+    assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (r1o, r1s)
+
+
+def test_split_in_place_state_zero_start_and_determinism():
+    say("split in-place / zero start / determinism")
+    x = prefill_device(1, 900, 2, 128, 128, BF16, 410, s0_std=0.02)
+    g_f32 = oracle_gate_f32(x["z"], x["A"])
+    g = g_f32.cuda()
+    o1, S1 = _split(x, g, 3)
+    o2, S2 = _split(x, g, 3)
+    S_in = x["S0"].clone()
+    o3, _ = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], S_in, final_state=S_in,
+                          flags=_lib.kda_flag_segments(3))
+    oz, Sz = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], None,
+                           flags=_lib.kda_flag_segments(3))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, S_in)
+    oz_ref, Sz_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], None)
+    assert rho(oz, oz_ref) <= TOL[BF16] and rho(Sz, Sz_ref) <= TOL[BF16]
+
+
+def test_automatic_split_for_a_long_few_chain_input():
+    """B1 H2 T12400: 4 workgroups in one pass, so the library splits on its own
+    (three segments of 4,160 tokens); the whole path gate -> chunk against the
+    oracle."""
+    say("automatic split B1 H2 T12400")
+    B, T, H = 1, 12400, 2
+    assert _lib.kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 1) > 256
+    x = prefill_device(B, T, H, 128, 128, BF16, 411, s0_std=0.02, stress=3.0)
+    g = kda_gate(x["z"], x["A"])
+    o, S = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+    o_1, S_1 = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"],
+                             flags=_lib.kda_flag_segments(1))
+    torch.cuda.synchronize()
+    g_ref = oracle.gate(x["z"], x["A"])
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_ref, x["beta"], x["S0"])
+    ro, rs = rho(o, o_ref), rho(S, S_ref)
+    print(f"    rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {rho(o, o_1):.3e} {rho(S, S_1):.3e}",
+          flush=True)
+    assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
