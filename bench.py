@@ -181,6 +181,48 @@ def time_prefill(steps, warmup):
     return dict(x=x, g=g, o=o, ST=ST, wall_s=wall, gate_ms=gate_ms, chunk_ms=chunk_ms)
 
 
+LONG = inputs.WORKLOADS["prefill_h32_t1m"]
+
+
+def time_long_prefill(reps=3):
+    """kda_chunk_fwd on the few-chain long workload (B1 H32 T1M: 64 workgroups
+    in one pass) in one pass and with the library's sequence split."""
+    w = LONG
+    dev = torch.device("cuda")
+    x = inputs.workload_prefill_inputs(w, device=dev)
+    g = _lib.kda_gate(x["z"], x["A"])
+    del x["z"]
+    o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
+    ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+    nseg = _lib.kda_chunk_fwd_auto_segments(w.B, w.T, w.H, w.dk, w.dv, 1)
+    ws = torch.empty(_lib.kda_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 1),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for label, n in (("one_pass", 1), ("split", nseg)):
+        def run():
+            _lib.kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], final_state=ST, o=o,
+                               workspace=ws, flags=_lib.kda_flag_segments(n), stream=stream)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[label + "_ms"] = e0.elapsed_time(e1) / reps
+    work = prefill_work(w)
+    s_ = out["split_ms"] / 1e3
+    out.update(segments=nseg, speedup=out["one_pass_ms"] / out["split_ms"],
+               tokens_per_s=w.B * w.T / s_,
+               hbm_frac_of_roofline=work["chunk_bytes"] / s_ / 1e9 / HBM_PEAK_GBS,
+               workload=w.note)
+    del x, g, o, ST, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_decode(nsteps=1000, warmup=20):
     w = DECODE
     dev = torch.device("cuda")
@@ -314,9 +356,9 @@ def ingest_pmc(fetch_dir, write_dir):
              "in the same script) to 1 GiB.", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- "
-             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity",
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-long",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- "
-             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity",
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-long",
              "    python3 bench.py --ingest-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
              f"Copy factors: FETCH {cal['FETCH_SIZE']:.4f}, WRITE {cal['WRITE_SIZE']:.4f}", "",
              "| kernel | fetch (MB) | write (MB) | traffic (MB) | algorithmic (MB) | traffic / algorithmic |",
@@ -335,7 +377,11 @@ def ingest_pmc(fetch_dir, write_dir):
 
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o bench -- "
-             "python3 -u bench.py --steps 10 --warmup 3 --decode-steps 200 --no-cpu-baseline --no-parity")
+             "python3 -u bench.py --steps 10 --warmup 3 --decode-steps 200 --no-cpu-baseline --no-parity "
+             "--no-long")
+LONG_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace_long -o long "
+                  "-- python3 -u bench.py --long-only")
+LONG_TRACE_MD = os.path.join(ROOT, "profiles", "kernel_trace_prefill_b1h32t1m_split.md")
 
 
 def ingest_trace(d):
@@ -373,6 +419,46 @@ def ingest_trace(d):
     print("\n".join(lines))
 
 
+def ingest_trace_long(d):
+    """Kernel durations of the few-chain long workload, one pass and split,
+    grouped by kernel and workgroup count (the split's phases differ in it)."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if not _matches(name, ("chunk32_kernel", "seg_chain_kernel", "gate_kernel")):
+            continue
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, wgs), []).append(us)
+    w = LONG
+    lines = ["# Kernel durations, few-chain long prefill (rocprofv3 kernel trace)", "",
+             f"Workload: {w.note}. `bench.py --long-only` runs kda_gate once, then",
+             "kda_chunk_fwd in one pass (1 warm-up + 3 timed calls) and with the library's",
+             "sequence split (the same).  A split call is three launches: chunk32_kernel",
+             "phase 1 (segment 0, the middle segments from zero and their transitions),",
+             "seg_chain_kernel, and chunk32_kernel phase 3 (segments 1..P-1); the",
+             "workgroup count tells the launches apart.", "",
+             "Command (from the repository root):", "", "    " + LONG_TRACE_CMD,
+             "    python3 bench.py --ingest-trace-long gpurun_out/ktrace_long", "",
+             "| kernel | workgroups | calls | avg (ms) | min (ms) | max (ms) |",
+             "|---|---|---|---|---|---|"]
+    for (name, wgs), us in sorted(groups.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        short = name.split("(")[0].replace("void ", "")[:40]
+        lines.append(f"| `{short}` | {wgs} | {len(us)} | {sum(us) / len(us) / 1e3:.3f} "
+                     f"| {min(us) / 1e3:.3f} | {max(us) / 1e3:.3f} |")
+    lines.append("")
+    with open(LONG_TRACE_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,16 +467,24 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the few-chain long-sequence prefill line (B1 H32 T1M)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
+    ap.add_argument("--ingest-trace-long", metavar="TRACE_DIR")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the few-chain long-sequence prefill and print its record")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
         return
     if args.ingest_trace:
         ingest_trace(args.ingest_trace)
+        return
+    if args.ingest_trace_long:
+        ingest_trace_long(args.ingest_trace_long)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -399,6 +493,9 @@ def main():
         sys.exit(2)
     _lib.load_library()
     torch.cuda.init()
+    if args.long_only:
+        print(json.dumps(time_long_prefill()), flush=True)
+        return
 
     copy_gbs = time_copy()
     res = time_prefill(args.steps, args.warmup)
@@ -419,6 +516,7 @@ def main():
     del res
     torch.cuda.empty_cache()
 
+    long_res = None if args.no_long else time_long_prefill()
     dec = time_decode(args.decode_steps)
     dbytes = decode_bytes(DECODE)
     dec_gbs = dbytes / (dec["us_per_step"] * 1e-6) / 1e9
@@ -454,6 +552,7 @@ def main():
                     "mfma_frac_of_bf16_peak": chunk_tflops / BF16_PEAK_TFLOPS,
                     "roofline_frac_of_attainable": chunk_tflops / attainable_tflops,
                     "head_tokens": work["head_tokens"]},
+        "prefill_long": long_res,
         "decode": {"us_per_step": dec["us_per_step"], "steps": dec["steps"],
                    "tokens_per_s": DECODE.B / (dec["us_per_step"] * 1e-6),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
