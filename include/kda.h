@@ -180,6 +180,47 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
                     int64_t N, int64_t H, int64_t dk, int64_t dv,
                     int dtype, void *stream);
 
+/*
+ * State pool for serving ("Kimi K3 internal structure analysis", section
+ * "Serving two incompatible cache types": the KDA layers keep a fixed-size
+ * recurrent state per sequence beside the MLA layers' growing cache).  A pool
+ * holds n_slots states, [n_slots, H, dk, dv] fp32; each call names the slot
+ * of each of its sequences in an int32 device array `slots` (4-byte aligned).
+ * The pooled calls compute exactly what their plain counterparts compute on
+ * the states gathered from those slots, and write the new states back to the
+ * same slots in place.  A slot outside [0, n_slots) skips its sequence: none
+ * of its state or output is read or written.  Two sequences of one call must
+ * not share a slot (their writes would race); the library does not check.
+ */
+
+/* Zero the states of the n slots listed in `slots` (a sequence starting). */
+int kda_state_pool_reset(float *state_pool, const int32_t *slots, int64_t n,
+                         int64_t n_slots, int64_t H, int64_t dk, int64_t dv,
+                         void *stream);
+
+/*
+ * kda_chunk_fwd with each sequence's initial and final state in the pool:
+ * sequence b (of B, all T tokens long) starts from slot slots[b] and leaves
+ * its final state there.  q, k, v, g, beta, o, workspace, flags as in
+ * kda_chunk_fwd (the sequence split applies as well).
+ */
+int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g,
+                         const void *beta, float *state_pool, const int32_t *slots,
+                         void *o, void *workspace, size_t workspace_bytes,
+                         int64_t B, int64_t T, int64_t n_slots, int64_t H,
+                         int64_t dk, int64_t dv, int dtype, unsigned flags, void *stream);
+
+/*
+ * kda_decode_step for N sequences whose states live in the pool: sequence n
+ * reads and updates slot slots[n] in place (continuous batching: the set of
+ * slots may change from step to step).  q, k, v, z, A, beta, o as in
+ * kda_decode_step.
+ */
+int kda_decode_step_pooled(const void *q, const void *k, const void *v, const void *z,
+                           const float *A, const void *beta, float *state_pool,
+                           const int32_t *slots, void *o, int64_t N, int64_t n_slots,
+                           int64_t H, int64_t dk, int64_t dv, int dtype, void *stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char *kda_last_error(void);
 

@@ -6,8 +6,10 @@ this package holds its ctypes binding (`_lib`), the in-tree build script
 
     from linear_attention_sequence_gate_amd import kda_gate, kda_chunk_fwd, kda_decode_step
 """
-__all__ = ["kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_decode_step",
-           "kda_last_error", "kda_version", "KdaError"]
+__all__ = ["kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_fwd_auto_segments", "kda_decode_step", "kda_state_pool_reset",
+           "kda_chunk_fwd_pooled", "kda_decode_step_pooled", "kda_last_error", "kda_version",
+           "KdaError"]
 
 
 def __getattr__(name):

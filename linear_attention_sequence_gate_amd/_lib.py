@@ -33,7 +33,8 @@ def kda_flag_segments(n: int) -> int:
 
 EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
-            "kda_decode_step", "kda_last_error", "kda_version")
+            "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
+            "kda_decode_step_pooled", "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -68,6 +69,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd.restype = c_int
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp]
     L.kda_decode_step.restype = c_int
+    L.kda_state_pool_reset.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp]
+    L.kda_state_pool_reset.restype = c_int
+    L.kda_chunk_fwd_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                       i64, i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd_pooled.restype = c_int
+    L.kda_decode_step_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                         i64, c_int, vp]
+    L.kda_decode_step_pooled.restype = c_int
     L.kda_last_error.argtypes = []
     L.kda_last_error.restype = ctypes.c_char_p
     L.kda_version.argtypes = []
@@ -177,4 +186,60 @@ def kda_decode_step(q, k, v, z, A, beta, state, o=None, stream=None) -> torch.Te
     _check(load_library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(state), _ptr(o),
         N, H, dk, dv, _dtype_code(q), _stream(stream)))
+    return o
+
+
+def _slots(slots: torch.Tensor) -> torch.Tensor:
+    if slots.dtype != torch.int32 or not slots.is_cuda or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous int32 CUDA tensor")
+    return slots
+
+
+def kda_state_pool_reset(state_pool, slots, stream=None) -> None:
+    """Zero the listed slots of a state pool [n_slots, H, dk, dv] fp32."""
+    _dev(state_pool)
+    slots = _slots(slots)
+    n_slots, H, dk, dv = state_pool.shape
+    _check(load_library().kda_state_pool_reset(
+        _ptr(state_pool), _ptr(slots), slots.numel(), n_slots, H, dk, dv, _stream(stream)))
+
+
+def kda_chunk_fwd_pooled(q, k, v, g, beta, state_pool, slots, o=None, flags: int = 0,
+                         workspace=None, stream=None) -> torch.Tensor:
+    """Chunkwise prefill of B sequences whose states live in `state_pool`
+    [n_slots, H, dk, dv] fp32 at `slots` [B] int32 (read, then overwritten
+    with the final states).  Returns o [B,T,H,dv]."""
+    _dev(q, k, v, g, beta, state_pool, o, workspace)
+    slots = _slots(slots)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n_slots = state_pool.shape[0]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
+    if workspace is None:
+        nseg = (flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT
+        ws_bytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dt, nseg)
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().kda_chunk_fwd_pooled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots), _ptr(o),
+        _ptr(workspace), ws_bytes, B, T, n_slots, H, dk, dv, dt, flags, _stream(stream)))
+    return o
+
+
+def kda_decode_step_pooled(q, k, v, z, A, beta, state_pool, slots, o=None,
+                           stream=None) -> torch.Tensor:
+    """One decode step for N sequences whose states live in `state_pool`
+    [n_slots, H, dk, dv] fp32 at `slots` [N] int32, updated in place.
+    Returns o [N,H,dv]."""
+    _dev(q, k, v, z, A, beta, state_pool, o)
+    slots = _slots(slots)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), device=q.device, dtype=q.dtype)
+    _check(load_library().kda_decode_step_pooled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(state_pool), _ptr(slots),
+        _ptr(o), N, state_pool.shape[0], H, dk, dv, _dtype_code(q), _stream(stream)))
     return o

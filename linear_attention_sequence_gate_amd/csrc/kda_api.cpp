@@ -108,10 +108,17 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
     return kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, 0);
 }
 
-int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
-                  const float *initial_state, float *final_state, void *o, void *workspace,
-                  size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                  int dtype, unsigned flags, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_fwd and kda_chunk_fwd_pooled; `who` names the entry point in errors
+int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v, const float *g,
+                   const void *beta, const float *initial_state, float *final_state, void *o,
+                   void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                   int64_t dk, int64_t dv, int dtype, unsigned flags, const int32_t *slots,
+                   int64_t n_slots, void *stream) {
+    (void)who;
     if (int e = check_dtype(dtype)) return e;
     if (!q || !k || !v || !g || !beta || !o)
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: null pointer (q, k, v, g, beta, o are required)");
@@ -182,14 +189,52 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
         }
     }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
-                                         (int)dk, (int)dv, is_bf16, nseg, split_ws, s);
+                                         (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }
 
-int kda_decode_step(const void *q, const void *k, const void *v, const void *z, const float *A,
-                    const void *beta, float *state, void *o, int64_t N, int64_t H, int64_t dk,
-                    int64_t dv, int dtype, void *stream) {
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                  const float *initial_state, float *final_state, void *o, void *workspace,
+                  size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                  int dtype, unsigned flags, void *stream) {
+    return chunk_fwd_impl("kda_chunk_fwd", q, k, v, g, beta, initial_state, final_state, o,
+                          workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, nullptr, 0,
+                          stream);
+}
+
+int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g,
+                         const void *beta, float *state_pool, const int32_t *slots, void *o,
+                         void *workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                         int64_t n_slots, int64_t H, int64_t dk, int64_t dv, int dtype,
+                         unsigned flags, void *stream) {
+    if (!state_pool || !slots)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: null state_pool or slots");
+    if (n_slots <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: n_slots must be positive");
+    int64_t np = n_slots;
+    if (!mul_ok(np, H) || !mul_ok(np, dk) || !mul_ok(np, dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: pool size overflows");
+    if (reinterpret_cast<uintptr_t>(slots) & 3u)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: slots must be 4-byte aligned");
+    if (static_cast<const void *>(slots) == o || static_cast<const void *>(state_pool) == o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: o must not alias an input");
+    return chunk_fwd_impl("kda_chunk_fwd_pooled", q, k, v, g, beta, state_pool, state_pool, o,
+                          workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, slots,
+                          n_slots, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const void *q, const void *k, const void *v, const void *z, const float *A,
+                     const void *beta, float *state, void *o, int64_t N, int64_t H, int64_t dk,
+                     int64_t dv, int dtype, const int32_t *slots, int64_t n_slots, void *stream) {
     if (int e = check_dtype(dtype)) return e;
     if (!q || !k || !v || !z || !A || !beta || !state || !o)
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: null pointer");
@@ -211,8 +256,60 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z, 
     for (const void *p : ins)
         if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o must not alias an input");
     hipError_t e = kda::launch_decode_step(q, k, v, z, A, beta, state, o, N, H, (int)dk, (int)dv,
-                                           dtype == KDA_BF16, static_cast<hipStream_t>(stream));
+                                           dtype == KDA_BF16, slots, n_slots,
+                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+    return ok();
+}
+
+// pool [n_slots, H, dk, dv] and slot table checks shared by the pooled entry points
+int check_pool(const char *who, const float *pool, const int32_t *slots, int64_t n_slots,
+               int64_t H, int64_t dk, int64_t dv) {
+    if (!pool || !slots) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null state_pool or slots", who);
+    if (n_slots <= 0 || H <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
+    if (!valid_dim(dk) || !valid_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
+                    (long long)dk, (long long)dv);
+    int64_t np = n_slots;
+    if (!mul_ok(np, H) || !mul_ok(np, dk) || !mul_ok(np, dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pool size overflows", who);
+    if (n_slots * H > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots*H too large", who);
+    if (!aligned16(pool)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool must be 16-byte aligned", who);
+    if (reinterpret_cast<uintptr_t>(slots) & 3u)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slots must be 4-byte aligned", who);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step(const void *q, const void *k, const void *v, const void *z, const float *A,
+                    const void *beta, float *state, void *o, int64_t N, int64_t H, int64_t dk,
+                    int64_t dv, int dtype, void *stream) {
+    return decode_step_impl(q, k, v, z, A, beta, state, o, N, H, dk, dv, dtype, nullptr, 0, stream);
+}
+
+int kda_decode_step_pooled(const void *q, const void *k, const void *v, const void *z,
+                           const float *A, const void *beta, float *state_pool,
+                           const int32_t *slots, void *o, int64_t N, int64_t n_slots, int64_t H,
+                           int64_t dk, int64_t dv, int dtype, void *stream) {
+    if (int e = check_pool("kda_decode_step_pooled", state_pool, slots, n_slots, H, dk, dv)) return e;
+    if (static_cast<const void *>(slots) == o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step_pooled: o must not alias an input");
+    return decode_step_impl(q, k, v, z, A, beta, state_pool, o, N, H, dk, dv, dtype, slots, n_slots,
+                            stream);
+}
+
+int kda_state_pool_reset(float *state_pool, const int32_t *slots, int64_t n, int64_t n_slots,
+                         int64_t H, int64_t dk, int64_t dv, void *stream) {
+    if (int e = check_pool("kda_state_pool_reset", state_pool, slots, n_slots, H, dk, dv)) return e;
+    if (n <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_pool_reset: n must be positive");
+    if (n > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_state_pool_reset: n too large");
+    hipError_t e = kda::launch_pool_reset(state_pool, slots, n, n_slots, H * dk * dv,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_state_pool_reset launch");
     return ok();
 }
 

@@ -71,7 +71,19 @@ struct ChunkArgs {
     int64_t seg_len;
     int phase, seg0, nseg, nsl_v;
     float *Sin, *Lb, *Mb;
+    // state pool: when set, S0 and ST are [n_slots, H, dk, dv] and sequence
+    // b uses slot slots[b] (a slot outside the pool skips the sequence)
+    const int *slots;
+    int64_t n_slots;
 };
+
+// Row of a sequence's state (b, h) in S0/ST: b * H + h, or with a slot table
+// slots[b] * H + h; -1 when the slot lies outside the pool.
+__device__ __forceinline__ int64_t user_state_row(const ChunkArgs &a, int b, int h) {
+    if (!a.slots) return (int64_t)b * a.H + h;
+    const int sl = a.slots[b];
+    return (sl >= 0 && sl < a.n_slots) ? (int64_t)sl * a.H + h : -1;
+}
 
 // Four consecutive elements of T in one register group.
 template <typename T> struct Quad;
@@ -399,6 +411,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
     }
     const int H = a.H, DV = a.DV;
     const int b = bh / H, h = bh % H;
+    const int64_t srow = user_state_row(a, b, h);
+    if (srow < 0) return;                        // slot outside the pool: skipped
     const int64_t T_ = a.T;
     const int vcol0 = slice * NV;
     const int64_t nchunk = (T_ + kChunk - 1) / kChunk;
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
-                    sacc[m][cb][j] = a.S0 ? a.S0[((int64_t)bh * DK + c) * DV + n] : 0.0f;
+                    sacc[m][cb][j] = a.S0 ? a.S0[(srow * DK + c) * DV + n] : 0.0f;
                 }
         }
     }
@@ -806,7 +820,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = 16 * cb + lg4 + j, n = vcol0 + 16 * nb + lr;
-                    a.ST[((int64_t)bh * DK + c) * DV + n] = sacc[m][cb][j];
+                    a.ST[(srow * DK + c) * DV + n] = sacc[m][cb][j];
                 }
         }
     }
@@ -974,6 +988,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     if (mcols && seg == 0) return;
     const int H = a.H, DV = a.DV;
     const int b = bh / H, h = bh % H;
+    const int64_t urow = user_state_row(a, b, h);   // row in the caller's S0 / ST
+    if (urow < 0) return;                           // slot outside the pool: skipped
     const int64_t T_ = a.T;
     const int64_t tbeg = (int64_t)seg * a.seg_len;
     const int64_t tend = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
@@ -1267,18 +1283,22 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         float *st = a.ST;
         void *ob = a.o;
         int spitch = DV;
+        int64_t s0row = urow, strow = urow;         // caller's rows; workspace rows are bh
         const bool vzero = mcols;
         if (a.phase == 1) {
             const size_t vsz = (size_t)a.nbh * DK * DV, msz = (size_t)a.nbh * DK * DK;
             if (mcols) {
                 s0 = nullptr; st = a.Mb + (size_t)(seg - 1) * msz; spitch = DK; ob = nullptr;
+                strow = bh;
             } else if (seg == 0) {
-                st = a.Sin;
+                st = a.Sin; strow = bh;
             } else {
                 s0 = nullptr; st = a.Lb + (size_t)(seg - 1) * vsz; ob = nullptr;
+                strow = bh;
             }
         } else if (a.phase == 3) {
             s0 = a.Sin + (size_t)(seg - 1) * a.nbh * DK * DV;
+            s0row = bh;
             st = seg == a.nseg - 1 ? a.ST : nullptr;
         }
         const T *__restrict__ vp = static_cast<const T *>(a.v);
@@ -1298,7 +1318,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const int cc = 16 * cb + lg4 + j;
                 sacc[cb][j] = vzero ? (cc == ncol ? 1.0f : 0.0f)
-                                    : s0 ? s0[((int64_t)bh * DK + cc) * spitch + ncol] : 0.0f;
+                                    : s0 ? s0[(s0row * DK + cc) * spitch + ncol] : 0.0f;
             }
         typename PF::frag sf[NKS];
 #pragma unroll
@@ -1498,7 +1518,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cc = 16 * cb + lg4 + j;
-                    st[((int64_t)bh * DK + cc) * spitch + ncol] = sacc[cb][j];
+                    st[(strow * DK + cc) * spitch + ncol] = sacc[cb][j];
                 }
         }
     }
@@ -1623,7 +1643,7 @@ size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
-                            void *split_ws, hipStream_t s) {
+                            void *split_ws, const int *slots, int64_t n_slots, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
@@ -1636,6 +1656,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
     args.seg_len = T; args.phase = 0; args.seg0 = 0; args.nseg = 1; args.nsl_v = args.nslice;
     args.Sin = args.Lb = args.Mb = nullptr;
+    args.slots = slots;
+    args.n_slots = n_slots;
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
     if (pipe && P >= 2) {
         if (!split_ws) return hipErrorInvalidValue;

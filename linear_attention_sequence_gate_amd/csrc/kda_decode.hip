@@ -44,7 +44,8 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ z, const float *__restrict__ A, const T *__restrict__ beta,
-    float *__restrict__ state, T *__restrict__ o, int H, int64_t NH) {
+    float *__restrict__ state, T *__restrict__ o, int H, int64_t NH,
+    const int *__restrict__ slots, int64_t n_slots) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int NCG = Sh::NCG, RG = Sh::RG, ROWS = Sh::ROWS, NWV = Sh::NWV;
 
@@ -56,6 +57,15 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % NCG, rg = tid / NCG;
     int64_t nh = blockIdx.x;                     // the grid never exceeds NH
+    // the state of head nh: row nh of the state array, or with a slot table
+    // row slots[n] * H + h of the pool; -1 for a slot outside the pool (the
+    // head is skipped: nothing of it is read or written but q..beta)
+    auto state_row = [&](int64_t i) -> int64_t {
+        if (!slots) return i;
+        const int64_t n = i / H;
+        const int sl = slots[n];
+        return (sl >= 0 && sl < n_slots) ? (int64_t)sl * H + (i - n * H) : -1;
+    };
 
     // this head's state and small inputs are in registers when an iteration
     // starts; the next head's are requested before this head's write
@@ -71,15 +81,19 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel
         if (tid < DV) v_ = ld1(v + n * DV + tid);
         b_ = ld1(beta + n);
     };
+    int64_t row = state_row(nh);
     {
-        const floatx4 *Sp = reinterpret_cast<const floatx4 *>(state + nh * (int64_t)(DK * DV));
+        // a skipped head's address is kept inside the pool (row 0) as well
+        const floatx4 *Sp = reinterpret_cast<const floatx4 *>(state + (row >= 0 ? row : 0) * (int64_t)(DK * DV));
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) s[i] = ld_state(Sp + (rg + RG * i) * NCG + cg);
+        for (int i = 0; i < ROWS; ++i)
+            s[i] = row >= 0 ? ld_state(Sp + (rg + RG * i) * NCG + cg) : floatx4{0, 0, 0, 0};
         load_small(nh, kk, qq, zz, vv, bt);
     }
     for (; nh < NH; nh += gridDim.x) {
         const int h = (int)(nh % H);
-        floatx4 *Sp = reinterpret_cast<floatx4 *>(state + nh * (int64_t)(DK * DV));
+        const bool live = row >= 0;
+        floatx4 *Sp = reinterpret_cast<floatx4 *>(state + (live ? row : 0) * (int64_t)(DK * DV));
 
         // per-channel gate, key and query, and the partial k . q
         float kq = 0.0f;
@@ -134,40 +148,47 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel
 
         // next head's state in flight before this head's write
         const int64_t nxt = nh + gridDim.x;
+        const int64_t nrow = nxt < NH ? state_row(nxt) : -1;
         float nk = 0.0f, nq = 0.0f, nz = 0.0f, nv = 0.0f, nb = 0.0f;
         if (nxt < NH) {
-            const floatx4 *Np = reinterpret_cast<const floatx4 *>(state + nxt * (int64_t)(DK * DV));
+            const floatx4 *Np = reinterpret_cast<const floatx4 *>(state + (nrow >= 0 ? nrow : 0) * (int64_t)(DK * DV));
 #pragma unroll
-            for (int i = 0; i < ROWS; ++i) sn[i] = ld_state(Np + (rg + RG * i) * NCG + cg);
+            for (int i = 0; i < ROWS; ++i)
+                sn[i] = nrow >= 0 ? ld_state(Np + (rg + RG * i) * NCG + cg) : floatx4{0, 0, 0, 0};
             load_small(nxt, nk, nq, nz, nv, nb);
         }
         // the new state, in place, and the output
+        if (live) {
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const int c = rg + RG * i;
-            st_state(Sp + c * NCG + cg, s[i] + sK[c] * u);
-        }
-        if (rg == 0) {
-            const floatx4 ov = r2 + kappa * u;
-            store4(o + nh * DV + 4 * cg, ov[0], ov[1], ov[2], ov[3]);
+            for (int i = 0; i < ROWS; ++i) {
+                const int c = rg + RG * i;
+                st_state(Sp + c * NCG + cg, s[i] + sK[c] * u);
+            }
+            if (rg == 0) {
+                const floatx4 ov = r2 + kappa * u;
+                store4(o + nh * DV + 4 * cg, ov[0], ov[1], ov[2], ov[3]);
+            }
         }
         __syncthreads();                         // the LDS tables are rewritten next
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) s[i] = sn[i];
         kk = nk; qq = nq; zz = nz; vv = nv; bt = nb;
+        row = nrow;
     }
 }
 
 template <typename T, int DK>
 static hipError_t decode_dv(const void *q, const void *k, const void *v, const void *z,
                             const float *A, const void *beta, float *state, void *o,
-                            int64_t NH, int H, int dv, hipStream_t s) {
+                            int64_t NH, int H, int dv, const int *slots, int64_t n_slots,
+                            hipStream_t s) {
     // persistent grid: about four workgroups per CU, never more than NH
     const unsigned grid = (unsigned)(NH < 1024 ? NH : 1024);
 #define KDA_DECODE(DV)                                                                      \
     hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(grid),                          \
                        dim3(DecodeShape<DK, DV>::TPB), 0, s, (const T *)q, (const T *)k,     \
-                       (const T *)v, (const T *)z, A, (const T *)beta, state, (T *)o, H, NH)
+                       (const T *)v, (const T *)z, A, (const T *)beta, state, (T *)o, H, NH, \
+                       slots, n_slots)
     switch (dv) {
     case 32: KDA_DECODE(32); break;
     case 64: KDA_DECODE(64); break;
@@ -181,22 +202,50 @@ static hipError_t decode_dv(const void *q, const void *k, const void *v, const v
 template <typename T>
 static hipError_t decode_dk(const void *q, const void *k, const void *v, const void *z,
                             const float *A, const void *beta, float *state, void *o,
-                            int64_t NH, int H, int dk, int dv, hipStream_t s) {
+                            int64_t NH, int H, int dk, int dv, const int *slots, int64_t n_slots,
+                            hipStream_t s) {
     switch (dk) {
-    case 32: return decode_dv<T, 32>(q, k, v, z, A, beta, state, o, NH, H, dv, s);
-    case 64: return decode_dv<T, 64>(q, k, v, z, A, beta, state, o, NH, H, dv, s);
-    case 128: return decode_dv<T, 128>(q, k, v, z, A, beta, state, o, NH, H, dv, s);
+    case 32: return decode_dv<T, 32>(q, k, v, z, A, beta, state, o, NH, H, dv, slots, n_slots, s);
+    case 64: return decode_dv<T, 64>(q, k, v, z, A, beta, state, o, NH, H, dv, slots, n_slots, s);
+    case 128: return decode_dv<T, 128>(q, k, v, z, A, beta, state, o, NH, H, dv, slots, n_slots, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode_step(const void *q, const void *k, const void *v, const void *z,
                               const float *A, const void *beta, float *state, void *o,
-                              int64_t N, int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
+                              int64_t N, int64_t H, int dk, int dv, int is_bf16, const int *slots,
+                              int64_t n_slots, hipStream_t s) {
     const int64_t NH = N * H;
     if (is_bf16)
-        return decode_dk<bf16>(q, k, v, z, A, beta, state, o, NH, (int)H, dk, dv, s);
-    return decode_dk<float>(q, k, v, z, A, beta, state, o, NH, (int)H, dk, dv, s);
+        return decode_dk<bf16>(q, k, v, z, A, beta, state, o, NH, (int)H, dk, dv, slots, n_slots, s);
+    return decode_dk<float>(q, k, v, z, A, beta, state, o, NH, (int)H, dk, dv, slots, n_slots, s);
+}
+
+// Zero the states of the listed slots of a pool [n_slots, H, dk, dv] (slots
+// outside the pool are skipped).  One thread per 4 floats.
+__global__ __launch_bounds__(256) void pool_reset_kernel(float *__restrict__ pool,
+                                                         const int *__restrict__ slots, int64_t n,
+                                                         int64_t n_slots, int64_t per_slot4) {
+    const int64_t total = n * per_slot4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / per_slot4, e = i - r * per_slot4;
+        const int sl = slots[r];
+        if (sl < 0 || sl >= n_slots) continue;
+        reinterpret_cast<floatx4 *>(pool)[(int64_t)sl * per_slot4 + e] = floatx4{0, 0, 0, 0};
+    }
+}
+
+hipError_t launch_pool_reset(float *pool, const int *slots, int64_t n, int64_t n_slots,
+                             int64_t per_slot, hipStream_t s) {
+    const int64_t per4 = per_slot / 4, total = n * per4;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(pool_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, s, pool, slots, n,
+                       n_slots, per4);
+    return hipGetLastError();
 }
 
 }  // namespace kda

@@ -16,10 +16,12 @@ hipError_t launch_range_check(const float *g, int64_t B, int64_t T, int64_t H, i
 // Returns hipErrorInvalidValue when no kernel instance exists for (dk, dtype).
 // nseg >= 2 splits each sequence into that many segments (pipelined path
 // only; split_ws must hold seq_split_workspace() bytes), else one pass.
+// slots != nullptr: S0 and ST index a state pool [n_slots, H, dk, dv] by
+// slots[b] (sequences whose slot lies outside the pool are skipped).
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
-                            void *split_ws, hipStream_t s);
+                            void *split_ws, const int *slots, int64_t n_slots, hipStream_t s);
 
 // Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
 bool seq_split_supported(int dk, int dv, int is_bf16);
@@ -34,8 +36,16 @@ size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int 
 
 bool chunk_fwd_supported(int dk, int dv, int is_bf16);
 
+// slots == nullptr: state is [N, H, dk, dv]; else state is a pool
+// [n_slots, H, dk, dv] and sequence n uses slot slots[n] (heads of a slot
+// outside the pool are skipped).
 hipError_t launch_decode_step(const void *q, const void *k, const void *v, const void *z,
                               const float *A, const void *beta, float *state, void *o,
-                              int64_t N, int64_t H, int dk, int dv, int is_bf16, hipStream_t s);
+                              int64_t N, int64_t H, int dk, int dv, int is_bf16, const int *slots,
+                              int64_t n_slots, hipStream_t s);
+
+// Zero the listed slots of a state pool; per_slot = H * dk * dv floats.
+hipError_t launch_pool_reset(float *pool, const int *slots, int64_t n, int64_t n_slots,
+                             int64_t per_slot, hipStream_t s);
 
 }  // namespace kda

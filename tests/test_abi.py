@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
-              "kda_decode_step", "kda_last_error", "kda_version"):
+              "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
+              "kda_decode_step_pooled", "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -161,3 +162,28 @@ def test_decode_validation(L):
     assert dec(o=P) == E.KDA_ERR_INVALID_ARGUMENT
     assert dec(z=BAD) == E.KDA_ERR_INVALID_ARGUMENT
     assert dec(N=1 << 40, H=1 << 30) == E.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_pool_validation(L):
+    E = _lib
+    S4 = ctypes.c_void_p(0x10004)          # 4-byte aligned, not 16
+    reset = lambda pool=P, slots=P3, n=2, ns=4, H=1, dk=32, dv=32: L.kda_state_pool_reset(
+        pool, slots, n, ns, H, dk, dv, None)
+    assert reset(pool=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(slots=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(ns=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(n=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(dk=48) == E.KDA_ERR_UNSUPPORTED
+    assert reset(pool=BAD) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(slots=ctypes.c_void_p(0x10002)) == E.KDA_ERR_INVALID_ARGUMENT
+    assert reset(ns=1 << 40, H=1 << 20) == E.KDA_ERR_INVALID_ARGUMENT   # overflow
+    dec = lambda pool=P, slots=S4, o=P2, N=2, ns=4: L.kda_decode_step_pooled(
+        P, P, P, P, P, P, pool, slots, o, N, ns, 1, 32, 32, 1, None)
+    assert dec(pool=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(ns=-1) == E.KDA_ERR_INVALID_ARGUMENT
+    assert dec(o=S4) == E.KDA_ERR_INVALID_ARGUMENT                        # o aliases slots
+    ch = lambda pool=P, slots=S4, o=P2, ns=4: L.kda_chunk_fwd_pooled(
+        P, P, P, P, P, pool, slots, o, NULL, 0, 1, 64, ns, 1, 32, 32, 1, 0, None)
+    assert ch(slots=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert ch(ns=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert ch(o=P) == E.KDA_ERR_INVALID_ARGUMENT                          # o aliases the pool

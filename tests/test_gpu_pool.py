@@ -1,0 +1,161 @@
+"""GPU checks of the slot-indexed state pool: the pooled calls equal the plain
+calls bit for bit on states gathered from the slots, slots outside the pool
+are skipped, reset zeroes only its slots, and a continuous-batching run
+(requests joining and leaving between decode steps) matches the oracle on
+each request's whole token stream."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_gate_amd import (_lib, inputs, kda_chunk_fwd, kda_chunk_fwd_pooled,
+                                                kda_decode_step, kda_decode_step_pooled, kda_gate,
+                                                kda_state_pool_reset)
+from kda_testutil import TOL, rho, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _pool(n_slots, H, dk, dv, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn(n_slots, H, dk, dv, device="cuda", generator=gen) * 0.02
+
+
+def _slots(lst):
+    return torch.tensor(lst, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128),
+                                         (torch.bfloat16, 32, 64)])
+def test_pooled_decode_equals_plain_on_gathered_states(dtype, dk, dv):
+    say("pooled decode", dtype, dk, dv)
+    n_slots, H = 10, 3
+    slots = [7, 2, 9, 0]
+    pool = _pool(n_slots, H, dk, dv, 500)
+    before = pool.clone()
+    S = pool[slots].clone()
+    A = inputs.make_decode_state(len(slots), H, dk, dv, 501, device="cuda")["A"]
+    for t in range(3):
+        x = inputs.make_decode_step_inputs(len(slots), H, dk, dv, dtype, 501, t, device="cuda")
+        o_ref = kda_decode_step(x["q"], x["k"], x["v"], x["z"], A, x["beta"], S)
+        o = kda_decode_step_pooled(x["q"], x["k"], x["v"], x["z"], A, x["beta"], pool, _slots(slots))
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
+        assert torch.equal(pool[slots], S)
+    others = [i for i in range(n_slots) if i not in slots]
+    assert torch.equal(pool[others], before[others])
+
+
+def test_pooled_decode_skips_slots_outside_the_pool():
+    say("pooled decode, invalid slots")
+    n_slots, H, dk, dv = 6, 2, 64, 64
+    slots = [3, -1, 6, 5]
+    pool = _pool(n_slots, H, dk, dv, 502)
+    before = pool.clone()
+    A = inputs.make_decode_state(4, H, dk, dv, 503, device="cuda")["A"]
+    x = inputs.make_decode_step_inputs(4, H, dk, dv, torch.float32, 503, 0, device="cuda")
+    o = torch.full((4, H, dv), 7.0, device="cuda")
+    kda_decode_step_pooled(x["q"], x["k"], x["v"], x["z"], A, x["beta"], pool, _slots(slots), o=o)
+    S = before[[3, 5]].clone()
+    o_ref = kda_decode_step(x["q"][[0, 3]].contiguous(), x["k"][[0, 3]].contiguous(),
+                            x["v"][[0, 3]].contiguous(), x["z"][[0, 3]].contiguous(), A,
+                            x["beta"][[0, 3]].contiguous(), S)
+    torch.cuda.synchronize()
+    assert torch.equal(o[[0, 3]], o_ref) and torch.equal(pool[[3, 5]], S)
+    assert (o[[1, 2]] == 7.0).all()                      # skipped: output untouched
+    assert torch.equal(pool[[0, 1, 2, 4]], before[[0, 1, 2, 4]])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T,nseg", [(torch.bfloat16, 128, 128, 300, 1),
+                                                (torch.bfloat16, 128, 64, 1000, 3),
+                                                (torch.float32, 64, 64, 200, 1)])
+def test_pooled_prefill_equals_plain_on_gathered_states(dtype, dk, dv, T, nseg):
+    say("pooled prefill", dtype, dk, dv, T, nseg)
+    n_slots, H = 8, 2
+    slots = [4, 1, 6, -3]                                 # the last sequence is skipped
+    x = inputs.make_prefill_inputs(4, T, H, dk, dv, dtype, 504, device="cuda")
+    g = kda_gate(x["z"], x["A"])
+    pool = _pool(n_slots, H, dk, dv, 505)
+    before = pool.clone()
+    flags = _lib.kda_flag_segments(nseg)
+    S0 = pool[slots[:3]].clone()
+    o_ref, S_ref = kda_chunk_fwd(x["q"][:3].contiguous(), x["k"][:3].contiguous(),
+                                 x["v"][:3].contiguous(), g[:3].contiguous(),
+                                 x["beta"][:3].contiguous(), S0, flags=flags)
+    o = torch.zeros(4, T, H, dv, device="cuda", dtype=dtype)
+    kda_chunk_fwd_pooled(x["q"], x["k"], x["v"], g, x["beta"], pool, _slots(slots), o=o, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:3], o_ref) and torch.equal(pool[slots[:3]], S_ref)
+    assert (o[3] == 0).all()
+    assert torch.equal(pool[[0, 2, 3, 5, 7]], before[[0, 2, 3, 5, 7]])
+
+
+def test_pool_reset():
+    say("pool reset")
+    pool = _pool(7, 2, 32, 128, 506)
+    before = pool.clone()
+    kda_state_pool_reset(pool, _slots([5, 1, 9, -2]))
+    torch.cuda.synchronize()
+    assert (pool[[1, 5]] == 0).all()
+    assert torch.equal(pool[[0, 2, 3, 4, 6]], before[[0, 2, 3, 4, 6]])
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 128)])
+def test_continuous_batching_matches_the_oracle(dtype, d):
+    """Three requests share a pool of six slots.  A (prompt 100) and B (prompt
+    37) are prefilled, decode three steps together; C (prompt 64) joins for two
+    steps (the batch order changes); A leaves and B, C decode two more.  Every
+    output of each request is compared with the oracle over its whole stream."""
+    say("continuous batching", dtype, d)
+    H = 2
+    n_slots = 6
+    prompts = {"A": 100, "B": 37, "C": 64}
+    n_dec = {"A": 5, "B": 7, "C": 4}
+    slot_of = {"A": 2, "B": 5, "C": 0}
+    reqs = {}
+    A_gate = None
+    for i, (r, p) in enumerate(prompts.items()):
+        x = inputs.make_prefill_inputs(1, p + n_dec[r], H, d, d, dtype, 510 + i, device="cuda")
+        if A_gate is None:
+            A_gate = x["A"]
+        reqs[r] = dict(x=x, pos=p, out=torch.empty(1, p + n_dec[r], H, d, device="cuda", dtype=dtype))
+    pool = _pool(n_slots, H, d, d, 520)                   # stale contents from earlier requests
+
+    def prefill(r):
+        x, p = reqs[r]["x"], prompts[r]
+        sl = lambda t: t[:, :p].contiguous()
+        kda_state_pool_reset(pool, _slots([slot_of[r]]))
+        g = kda_gate(sl(x["z"]), A_gate)
+        o = kda_chunk_fwd_pooled(sl(x["q"]), sl(x["k"]), sl(x["v"]), g, sl(x["beta"]), pool,
+                                 _slots([slot_of[r]]))
+        reqs[r]["out"][:, :p] = o
+
+    def decode(batch):
+        pos = [reqs[r]["pos"] for r in batch]
+        pick = lambda key: torch.stack([reqs[r]["x"][key][0, t] for r, t in zip(batch, pos)]).contiguous()
+        o = kda_decode_step_pooled(pick("q"), pick("k"), pick("v"), pick("z"), A_gate, pick("beta"),
+                                   pool, _slots([slot_of[r] for r in batch]))
+        for i, r in enumerate(batch):
+            reqs[r]["out"][0, reqs[r]["pos"]] = o[i]
+            reqs[r]["pos"] += 1
+
+    prefill("A")
+    prefill("B")
+    for _ in range(3):
+        decode(["A", "B"])
+    prefill("C")
+    for _ in range(2):
+        decode(["C", "A", "B"])
+    for _ in range(2):
+        decode(["B", "C"])
+    torch.cuda.synchronize()
+    for r, st in reqs.items():
+        L = prompts[r] + n_dec[r]
+        assert st["pos"] == L, (r, st["pos"])
+        x = st["x"]
+        g_ref = oracle.gate(x["z"], A_gate)
+        o_ref, _ = oracle.forward(x["q"], x["k"], x["v"], g_ref, x["beta"], None)
+        ro = rho(st["out"], o_ref)
+        print(f"    {r}: rho(o)={ro:.3e}", flush=True)
+        assert np.isfinite(st["out"].float().cpu().numpy()).all()
+        assert ro <= TOL[dtype], (r, ro)
