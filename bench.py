@@ -223,6 +223,39 @@ def time_long_prefill(reps=3):
     return out
 
 
+def time_pairwise_diagonal(reps=3):
+    """kda_chunk_fwd on the benchmark's prefill workload with the dense MFMA
+    diagonal tiles (what the gate floor allows) and with the position-pair
+    diagonal path the floor made unnecessary, in the same kernel."""
+    w = PREFILL
+    dev = torch.device("cuda")
+    x = inputs.workload_prefill_inputs(w, device=dev)
+    g = _lib.kda_gate(x["z"], x["A"])
+    o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
+    ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for label, fl in (("dense_ms", 0), ("pairwise_ms", _lib.KDA_FLAG_PAIRWISE_DIAGONAL)):
+        def run():
+            _lib.kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], final_state=ST, o=o,
+                               flags=fl, stream=stream)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[label] = e0.elapsed_time(e1) / reps
+    out.update(pairwise_over_dense=out["pairwise_ms"] / out["dense_ms"],
+               workload=w.note.split(";")[0])
+    del x, g, o, ST
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_decode(nsteps=1000, warmup=20):
     w = DECODE
     dev = torch.device("cuda")
@@ -356,9 +389,9 @@ def ingest_pmc(fetch_dir, write_dir):
              "in the same script) to 1 GiB.", "",
              "Commands (from the repository root):", "",
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- "
-             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-long",
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-extras",
              "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- "
-             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-long",
+             "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-parity --no-extras",
              "    python3 bench.py --ingest-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
              f"Copy factors: FETCH {cal['FETCH_SIZE']:.4f}, WRITE {cal['WRITE_SIZE']:.4f}", "",
              "| kernel | fetch (MB) | write (MB) | traffic (MB) | algorithmic (MB) | traffic / algorithmic |",
@@ -378,10 +411,25 @@ def ingest_pmc(fetch_dir, write_dir):
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o bench -- "
              "python3 -u bench.py --steps 10 --warmup 3 --decode-steps 200 --no-cpu-baseline --no-parity "
-             "--no-long")
-LONG_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace_long -o long "
-                  "-- python3 -u bench.py --long-only")
-LONG_TRACE_MD = os.path.join(ROOT, "profiles", "kernel_trace_prefill_b1h32t1m_split.md")
+             "--no-extras")
+EXTRA_TRACES = {
+    # name: (bench.py --only value, profile file, what the run holds)
+    "long": ("long", "kernel_trace_prefill_b1h32t1m_split.md",
+             "kda_gate once, then kda_chunk_fwd on B1 H32 T1048576 d128 bf16 in one pass "
+             "(1 warm-up + 3 timed calls) and with the library's sequence split (the same). "
+             "A split call is three launches: chunk32_kernel phase 1 (segment 0, the middle "
+             "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
+             "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
+    "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
+                 "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
+                 "MFMA diagonal tiles (2 warm-up + 3 timed calls) and with the position-pair "
+                 "diagonal path (the same), in that order."),
+}
+
+
+def extra_trace_cmd(name):
+    return (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace_{name} "
+            f"-o {name} -- python3 -u bench.py --only {EXTRA_TRACES[name][0]}")
 
 
 def ingest_trace(d):
@@ -419,9 +467,11 @@ def ingest_trace(d):
     print("\n".join(lines))
 
 
-def ingest_trace_long(d):
-    """Kernel durations of the few-chain long workload, one pass and split,
-    grouped by kernel and workgroup count (the split's phases differ in it)."""
+def ingest_trace_extra(name, d):
+    """Kernel durations of one extra run (bench.py --only NAME).  chunk32_kernel
+    launches are grouped by workgroup count, and in the position-pair run by
+    mode (its first half of launches is the dense path, the second the
+    position-pair path)."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {d}")
@@ -429,32 +479,29 @@ def ingest_trace_long(d):
     for f in files:
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel"))]
+    chunk_rows = [r for r in rows if "chunk32_kernel" in r["Kernel_Name"]]
     groups = {}
     for r in rows:
-        name = r["Kernel_Name"]
-        if not _matches(name, ("chunk32_kernel", "seg_chain_kernel", "gate_kernel")):
-            continue
+        kname = r["Kernel_Name"].split("(")[0].replace("void ", "")[:40]
         wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        label = ""
+        if name == "pairwise" and r in chunk_rows:
+            label = "dense" if chunk_rows.index(r) < len(chunk_rows) // 2 else "position pairs"
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        groups.setdefault((name, wgs), []).append(us)
-    w = LONG
-    lines = ["# Kernel durations, few-chain long prefill (rocprofv3 kernel trace)", "",
-             f"Workload: {w.note}. `bench.py --long-only` runs kda_gate once, then",
-             "kda_chunk_fwd in one pass (1 warm-up + 3 timed calls) and with the library's",
-             "sequence split (the same).  A split call is three launches: chunk32_kernel",
-             "phase 1 (segment 0, the middle segments from zero and their transitions),",
-             "seg_chain_kernel, and chunk32_kernel phase 3 (segments 1..P-1); the",
-             "workgroup count tells the launches apart.", "",
-             "Command (from the repository root):", "", "    " + LONG_TRACE_CMD,
-             "    python3 bench.py --ingest-trace-long gpurun_out/ktrace_long", "",
-             "| kernel | workgroups | calls | avg (ms) | min (ms) | max (ms) |",
-             "|---|---|---|---|---|---|"]
-    for (name, wgs), us in sorted(groups.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
-        short = name.split("(")[0].replace("void ", "")[:40]
-        lines.append(f"| `{short}` | {wgs} | {len(us)} | {sum(us) / len(us) / 1e3:.3f} "
+        groups.setdefault((kname, label, wgs), []).append(us)
+    only, fname, what = EXTRA_TRACES[name]
+    lines = [f"# Kernel durations, `bench.py --only {only}` (rocprofv3 kernel trace)", "",
+             what, "", "Command (from the repository root):", "", "    " + extra_trace_cmd(name),
+             f"    python3 bench.py --ingest-trace-extra {name} gpurun_out/ktrace_{name}", "",
+             "| kernel | mode | workgroups | calls | avg (ms) | min (ms) | max (ms) |",
+             "|---|---|---|---|---|---|---|"]
+    for (kname, label, wgs), us in groups.items():
+        lines.append(f"| `{kname}` | {label} | {wgs} | {len(us)} | {sum(us) / len(us) / 1e3:.3f} "
                      f"| {min(us) / 1e3:.3f} | {max(us) / 1e3:.3f} |")
     lines.append("")
-    with open(LONG_TRACE_MD, "w") as fh:
+    with open(os.path.join(ROOT, "profiles", fname), "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -467,15 +514,15 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--no-long", action="store_true",
-                    help="skip the few-chain long-sequence prefill line (B1 H32 T1M)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra lines (few-chain long prefill, position-pair diagonal)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
-    ap.add_argument("--ingest-trace-long", metavar="TRACE_DIR")
-    ap.add_argument("--long-only", action="store_true",
-                    help="time only the few-chain long-sequence prefill and print its record")
+    ap.add_argument("--ingest-trace-extra", nargs=2, metavar=("NAME", "TRACE_DIR"))
+    ap.add_argument("--only", choices=("long", "pairwise"),
+                    help="time only one extra line and print its record")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
@@ -483,8 +530,8 @@ def main():
     if args.ingest_trace:
         ingest_trace(args.ingest_trace)
         return
-    if args.ingest_trace_long:
-        ingest_trace_long(args.ingest_trace_long)
+    if args.ingest_trace_extra:
+        ingest_trace_extra(*args.ingest_trace_extra)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -493,8 +540,9 @@ def main():
         sys.exit(2)
     _lib.load_library()
     torch.cuda.init()
-    if args.long_only:
-        print(json.dumps(time_long_prefill()), flush=True)
+    if args.only:
+        rec = time_long_prefill() if args.only == "long" else time_pairwise_diagonal()
+        print(json.dumps(rec), flush=True)
         return
 
     copy_gbs = time_copy()
@@ -516,7 +564,8 @@ def main():
     del res
     torch.cuda.empty_cache()
 
-    long_res = None if args.no_long else time_long_prefill()
+    long_res = None if args.no_extras else time_long_prefill()
+    pair_res = None if args.no_extras else time_pairwise_diagonal()
     dec = time_decode(args.decode_steps)
     dbytes = decode_bytes(DECODE)
     dec_gbs = dbytes / (dec["us_per_step"] * 1e-6) / 1e9
@@ -553,6 +602,7 @@ def main():
                     "roofline_frac_of_attainable": chunk_tflops / attainable_tflops,
                     "head_tokens": work["head_tokens"]},
         "prefill_long": long_res,
+        "prefill_pairwise_diagonal": pair_res,
         "decode": {"us_per_step": dec["us_per_step"], "steps": dec["steps"],
                    "tokens_per_s": DECODE.B / (dec["us_per_step"] * 1e-6),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,

@@ -67,6 +67,15 @@ enum {
      * call) lies in [-80, 0] -- the range the gate's floor guarantees and the
      * chunked kernel relies on.  Synchronises the stream; debugging only. */
     KDA_FLAG_CHECK_RANGE = 1u,
+    /* Compute the diagonal 16-token tiles of A and P by position pairs,
+     * sum_c x_rc k_sc 2^(lam_rc - lam_sc) with the log-decay lam kept in log
+     * space, instead of dense MFMA tiles of decay-scaled operands.  This is
+     * the path the gate floor made unnecessary ("Kimi K3 internal structure
+     * analysis", section "Sequence mixing: 3 KDA layers per global MLA
+     * layer": without a floor the reciprocal cumulative decay inside a
+     * diagonal tile can overflow).  With it, g may lie anywhere <= 0 (no
+     * 16-token range bound).  bf16, dk = 128, dv in {64, 128}; slower. */
+    KDA_FLAG_PAIRWISE_DIAGONAL = 2u,
     /* Bits 8..15: segments per sequence for the sequence-parallel path
      * (bf16, dk = 128, dv in {64, 128}): 0 = chosen by the library, 1 = never
      * split, n >= 2 = split into n segments (the count a 32-token-aligned

@@ -23,6 +23,7 @@ KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_HIP = -3
 KDA_ERR_RANGE = -4
 KDA_FLAG_CHECK_RANGE = 1
+KDA_FLAG_PAIRWISE_DIAGONAL = 2
 KDA_FLAG_SEGMENTS_SHIFT = 8
 KDA_FLAG_SEGMENTS_MASK = 0xFF00
 

@@ -129,9 +129,17 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
                     (long long)dk, (long long)dv);
     if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
         return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs support dk in {32,64} only");
-    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_SEGMENTS_MASK))
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: unknown flag bits 0x%x", flags);
     const bool is_bf16 = dtype == KDA_BF16;
+    const bool pairwise = (flags & KDA_FLAG_PAIRWISE_DIAGONAL) != 0;
+    if (pairwise && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "kda_chunk_fwd: the position-pair diagonal path needs bf16 inputs, dk = 128, "
+                    "dv in {64, 128}");
+    if (pairwise && (flags & KDA_FLAG_CHECK_RANGE))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "kda_chunk_fwd: the position-pair diagonal path has no decay range to check");
     const int req_seg = (int)((flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT);
     if (req_seg >= 2 && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
         return fail(KDA_ERR_UNSUPPORTED,
@@ -189,7 +197,8 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         }
     }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
-                                         (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots, s);
+                                         (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
+                                         pairwise ? 1 : 0, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }

@@ -75,6 +75,9 @@ struct ChunkArgs {
     // b uses slot slots[b] (a slot outside the pool skips the sequence)
     const int *slots;
     int64_t n_slots;
+    // chunk32_kernel: diagonal 16-token tiles by position pairs in log space
+    // (no assumption on the decay range) instead of dense MFMA tiles
+    int pairwise;
 };
 
 // Row of a sequence's state (b, h) in S0/ST: b * H + h, or with a slot table
@@ -934,7 +937,12 @@ template <int DK> struct PipeLds {
     static constexpr int AB = KC + 48 * LDK * 2;    // A (row-major, beta on rows), two chunks
     static constexpr int EL = AB + 2 * SQ;          // subtile decay totals, 2 x DK fp32
     static constexpr int BETA = EL + 2 * DK * 4;    // beta, 32 fp32, two chunks
-    static constexpr int PREP = BETA + 2 * 32 * 4;
+    // position-pair diagonal tiles only: log-decay rows (times log2 e) and
+    // the two channel halves' partial 16x16 tiles (A00, P00, A11, P11)
+    static constexpr int LDL = DK + 4;
+    static constexpr int LAM = BETA + 2 * 32 * 4;
+    static constexpr int DPART = LAM + 32 * LDL * 4;
+    static constexpr int PREP = DPART + 2 * 4 * 256 * 4;
     // one handoff slot
     static constexpr int S_KT = 0;                  // K~ = k e^{b} rows
     static constexpr int S_QT = S_KT + TOKE;        // Q~ = q e^{b} rows
@@ -995,6 +1003,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const int64_t tend = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
     const int vcol0 = (mcols ? slice - a.nsl_v : slice) * NV;
     const int64_t nchunk = (tend - tbeg + kPipeChunk - 1) / kPipeChunk;
+    const bool pw = __builtin_amdgcn_readfirstlane(a.pairwise) != 0;
     const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
     unsigned char *const slot_base = smem + Lds::PREP;
 
@@ -1021,6 +1030,9 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
         T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
         float *sEL = reinterpret_cast<float *>(smem + Lds::EL);
+        float *sLam = reinterpret_cast<float *>(smem + Lds::LAM);
+        float *sDpart = reinterpret_cast<float *>(smem + Lds::DPART);
+        constexpr int LDL = Lds::LDL;
 
         const T *__restrict__ qp = static_cast<const T *>(a.q);
         const T *__restrict__ kp = static_cast<const T *>(a.k);
@@ -1158,11 +1170,39 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                     const float bv = lane < L ? __uint_as_float(raw.beta << 16) : 0.0f;
                     if (p == 0 && lane < 32) sBeta[lane] = bv;
                 }
+                if (pw) {
+                    // position-pair path: the subtile-local log-decay itself
+                    // (in log2 units), summed, never exponentiated here
+                    floatx2 gl[TPL];
+#pragma unroll
+                    for (int i = 0; i < TPL; ++i) {
+                        const bool in = tb + i < L;
+                        gl[i] = in ? raw.g[i] * kLog2e : floatx2{0.0f, 0.0f};
+                    }
+                    floatx2 totg = gl[0];
+#pragma unroll
+                    for (int i = 1; i < TPL; ++i) totg += gl[i];
+                    floatx2 lam = {0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 1; s < NPOS; ++s) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const float fw = __shfl(totg[j], lane - 16 * s);
+                            lam[j] += pos >= s ? fw : 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < TPL; ++i) {
+                        lam += gl[i];
+                        *reinterpret_cast<floatx2 *>(sLam + (tb + i) * LDL + c0) = lam;
+                    }
+                }
                 const floatx2 eNegLam = {__builtin_amdgcn_rcpf(eLam[0]), __builtin_amdgcn_rcpf(eLam[1])};
-                // one straight-line copy per subtile, so the tokens' work can be
-                // interleaved by the scheduler
-                auto tiles = [&](auto sub) {
+                // one straight-line copy per subtile (and path), so the
+                // tokens' work can be interleaved by the scheduler
+                auto tiles = [&](auto sub, auto pair_path) {
                     constexpr int IS = decltype(sub)::value;
+                    constexpr bool PW = decltype(pair_path)::value;
                     float kh[2][TPL];
 #pragma unroll
                     for (int i = 0; i < TPL; ++i) {
@@ -1171,10 +1211,23 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                         kR[i] = kv * R[i];
                         qR[i] = qv * R[i];
                         kEt[i] = kv * Et[i];
-                        store2v(sKr + tl * LDK + c0, kR[i]);
-                        store2v(sQr + tl * LDK + c0, qR[i]);
-                        // diagonal pair column tile: k e^{-lam}
-                        store2v(sKc + (32 * IS + r) * LDK + c0, kEt[i] * eNegLam);
+                        if constexpr (PW) {
+                            // the diagonal tiles take raw k (columns) and raw
+                            // q / k (rows) in the rows their dense tiles used
+                            *reinterpret_cast<unsigned *>(sKc + (32 * IS + r) * LDK + c0) = raw.k[i];
+                            if constexpr (IS == 0) {
+                                *reinterpret_cast<unsigned *>(sQr + r * LDK + c0) = raw.q[i];
+                            } else {
+                                store2v(sKr + tl * LDK + c0, kR[i]);
+                                store2v(sQr + tl * LDK + c0, qR[i]);
+                                *reinterpret_cast<unsigned *>(sKr + r * LDK + c0) = raw.q[i];
+                            }
+                        } else {
+                            store2v(sKr + tl * LDK + c0, kR[i]);
+                            store2v(sQr + tl * LDK + c0, qR[i]);
+                            // diagonal pair column tile: k e^{-lam}
+                            store2v(sKc + (32 * IS + r) * LDK + c0, kEt[i] * eNegLam);
+                        }
                         if constexpr (IS == 0) {
                             store2v(sKc + (16 + r) * LDK + c0, kEt[i]);   // pair (1, 0)
                             store2v(sKt + tl * LDKE + c0, kR[i]);          // b = lam in subtile 0
@@ -1189,8 +1242,13 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                         storeN<TPL>(sKh + (c0 + 1) * LDT + tb, kh[1]);
                     }
                 };
-                if (I == 0) tiles(std::integral_constant<int, 0>{});
-                else tiles(std::integral_constant<int, 1>{});
+                if (!pw) {
+                    if (I == 0) tiles(std::integral_constant<int, 0>{}, std::false_type{});
+                    else tiles(std::integral_constant<int, 1>{}, std::false_type{});
+                } else {
+                    if (I == 0) tiles(std::integral_constant<int, 0>{}, std::true_type{});
+                    else tiles(std::integral_constant<int, 1>{}, std::true_type{});
+                }
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
             lds_barrier();                                  // BAR1
@@ -1201,8 +1259,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 // Waves i and i + 4 share a SIMD; the two prep waves next to
                 // state wave 3 (which forms the inverse meanwhile) take none,
                 // the other six take one each.
-                const bool has_tile = (p & 3) != 3;
-                const int ti = p < 3 ? p : (p > 3 && p < 7 ? p - 1 : 0);
+                // Position-pair path: prep waves 0 and 1 take the dense tiles
+                // 2 and 3; the diagonal tiles are below.
+                const bool has_tile = pw ? p < 2 : (p & 3) != 3;
+                const int ti = pw ? 2 + (p & 1) : (p < 3 ? p : (p > 3 && p < 7 ? p - 1 : 0));
                 const int pi = ti >> 1;
                 const int Ib = pi == 0 ? 0 : 1, J = pi == 2 ? 1 : 0;
                 const bool isP = ti & 1;
@@ -1237,6 +1297,36 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                         if (pos == 0) *reinterpret_cast<floatx2 *>(sEbC + c0) = e0 * e1;
                     }
                 }
+                if (pw) {
+                    // Position pairs of one diagonal tile (D: A00, P00, A11,
+                    // P11) over one half of the channels:
+                    //   sum_c x_rc k_sc 2^(lam_rc - lam_sc),  lane: row lr, columns lg4 + j,
+                    // the exponent of a difference, at most 0 where s <= r
+                    // (larger, masked, entries are clamped to 0 first)
+                    const int D = p >> 1, half = p & 1, Is = D >> 1;
+                    const bool dP = D & 1;
+                    const T *xr = (dP ? (Is == 0 ? sQr : sKr) + lr * LDK : sKc + (32 * Is + lr) * LDK);
+                    const T *ys = sKc + 32 * Is * LDK;
+                    const float *lr_ = sLam + (16 * Is + lr) * LDL;
+                    const float *ls_ = sLam + 16 * Is * LDL;
+                    floatx4 acc = {0, 0, 0, 0};
+                    for (int cc = 64 * half; cc < 64 * half + 64; cc += 4) {
+                        const floatx4 x4 = to_f4(*reinterpret_cast<const bf16x4 *>(xr + cc));
+                        const floatx4 l4 = *reinterpret_cast<const floatx4 *>(lr_ + cc);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int sj = lg4 + j;
+                            const floatx4 y4 = to_f4(*reinterpret_cast<const bf16x4 *>(ys + sj * LDK + cc));
+                            const floatx4 m4 = *reinterpret_cast<const floatx4 *>(ls_ + sj * LDL + cc);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float d = fminf(l4[e] - m4[e], 0.0f);
+                                acc[j] = fmaf(x4[e] * y4[e], __builtin_amdgcn_exp2f(d), acc[j]);
+                            }
+                        }
+                    }
+                    *reinterpret_cast<floatx4 *>(sDpart + (half * 4 + D) * 256 + lr * 16 + lg4) = acc;
+                }
                 if (has_tile) {
                     const int r = 16 * Ib + lr;
                     const float br = sBeta[r];
@@ -1257,6 +1347,34 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                         *reinterpret_cast<bf16x4 *>(sPl + r * LDT + 16 * J + lg4) = lo;
                     } else {
                         store4v(sA + r * LDT + 16 * J + lg4, val);
+                    }
+                }
+            }
+            if (pw) {
+                lds_barrier();                              // the diagonal partials are complete
+                if (live && p < 4) {
+                    // diagonal tile D = p: the two channel halves, beta on
+                    // A's rows, causal mask (s < r for A, s <= r for P)
+                    const int Is = p >> 1;
+                    const bool dP = p & 1;
+                    const floatx4 v0 = *reinterpret_cast<const floatx4 *>(sDpart + p * 256 + lr * 16 + lg4);
+                    const floatx4 v1 = *reinterpret_cast<const floatx4 *>(sDpart + (4 + p) * 256 + lr * 16 + lg4);
+                    const int r = 16 * Is + lr;
+                    const float rowscale = dP ? 1.0f : sBeta[r];
+                    const int lim = dP ? lr + 1 : lr;
+                    floatx4 val;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = (v0[j] + v1[j]) * rowscale;
+                        val[j] = lg4 + j < lim ? x : 0.0f;
+                    }
+                    if (dP) {
+                        bf16x4 hi, lo;
+                        split_bf16(val, hi, lo);
+                        *reinterpret_cast<bf16x4 *>(sPh + r * LDT + 16 * Is + lg4) = hi;
+                        *reinterpret_cast<bf16x4 *>(sPl + r * LDT + 16 * Is + lg4) = lo;
+                    } else {
+                        store4v(sA + r * LDT + 16 * Is + lg4, val);
                     }
                 }
             }
@@ -1505,6 +1623,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 store4v(sXr + (16 + lr) * LDT + 16 + lg4, xT[1] * b1);
                 store4v(sXr + (16 + lr) * LDT + lg4, x10T * b0);
             }
+            if (pw) lds_barrier();                          // position-pair path: partials complete
             lds_barrier();                                  // BAR2
         };
         for (int64_t c = 0; c <= nchunk + 1; c += 2) {
@@ -1643,7 +1762,8 @@ size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
-                            void *split_ws, const int *slots, int64_t n_slots, hipStream_t s) {
+                            void *split_ws, const int *slots, int64_t n_slots, int pairwise,
+                            hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
@@ -1658,6 +1778,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.Sin = args.Lb = args.Mb = nullptr;
     args.slots = slots;
     args.n_slots = n_slots;
+    args.pairwise = pipe && pairwise ? 1 : 0;
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
     if (pipe && P >= 2) {
         if (!split_ws) return hipErrorInvalidValue;

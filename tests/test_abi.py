@@ -80,7 +80,11 @@ def test_chunk_validation(L):
     assert chunk(L, B=1 << 30, T=1 << 30) == E.KDA_ERR_INVALID_ARGUMENT   # overflow
     assert chunk(L, k=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
     assert chunk(L, o=P) == E.KDA_ERR_INVALID_ARGUMENT            # o aliases q
-    assert chunk(L, flags=2) == E.KDA_ERR_INVALID_ARGUMENT        # unknown flag
+    assert chunk(L, flags=4) == E.KDA_ERR_INVALID_ARGUMENT        # unknown flag
+    assert chunk(L, flags=E.KDA_FLAG_PAIRWISE_DIAGONAL) == E.KDA_ERR_UNSUPPORTED   # dk = 32
+    assert "position-pair" in _lib.kda_last_error()
+    assert chunk(L, dk=128, dv=128, flags=E.KDA_FLAG_PAIRWISE_DIAGONAL | E.KDA_FLAG_CHECK_RANGE,
+                 ws=P3, wsb=4096) == E.KDA_ERR_INVALID_ARGUMENT
     assert chunk(L, flags=1) == E.KDA_ERR_INVALID_ARGUMENT        # range check needs workspace
     assert chunk(L, flags=1, ws=P3, wsb=8) == E.KDA_ERR_INVALID_ARGUMENT  # too small
     assert "workspace" in _lib.kda_last_error()
