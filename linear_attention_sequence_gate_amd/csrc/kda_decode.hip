@@ -40,7 +40,7 @@ template <int DK, int DV> struct DecodeShape {
     static_assert(ROWS >= 1 && DK % RG == 0 && TPB % 64 == 0 && NCG <= 64, "decode shape");
 };
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool POOLED>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ z, const float *__restrict__ A, const T *__restrict__ beta,
@@ -61,7 +61,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::TPB)) void decode_step_kernel
     // row slots[n] * H + h of the pool; -1 for a slot outside the pool (the
     // head is skipped: nothing of it is read or written but q..beta)
     auto state_row = [&](int64_t i) -> int64_t {
-        if (!slots) return i;
+        if constexpr (!POOLED) return i;
         const int64_t n = i / H;
         const int sl = slots[n];
         return (sl >= 0 && sl < n_slots) ? (int64_t)sl * H + (i - n * H) : -1;
@@ -185,10 +185,16 @@ static hipError_t decode_dv(const void *q, const void *k, const void *v, const v
     // persistent grid: about four workgroups per CU, never more than NH
     const unsigned grid = (unsigned)(NH < 1024 ? NH : 1024);
 #define KDA_DECODE(DV)                                                                      \
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(grid),                          \
-                       dim3(DecodeShape<DK, DV>::TPB), 0, s, (const T *)q, (const T *)k,     \
-                       (const T *)v, (const T *)z, A, (const T *)beta, state, (T *)o, H, NH, \
-                       slots, n_slots)
+    if (slots)                                                                               \
+        hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, true>), dim3(grid),                \
+                           dim3(DecodeShape<DK, DV>::TPB), 0, s, (const T *)q, (const T *)k, \
+                           (const T *)v, (const T *)z, A, (const T *)beta, state, (T *)o, H, \
+                           NH, slots, n_slots);                                              \
+    else                                                                                     \
+        hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, false>), dim3(grid),               \
+                           dim3(DecodeShape<DK, DV>::TPB), 0, s, (const T *)q, (const T *)k, \
+                           (const T *)v, (const T *)z, A, (const T *)beta, state, (T *)o, H, \
+                           NH, nullptr, 0)
     switch (dv) {
     case 32: KDA_DECODE(32); break;
     case 64: KDA_DECODE(64); break;
