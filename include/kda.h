@@ -220,6 +220,22 @@ int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const floa
                          int64_t dk, int64_t dv, int dtype, unsigned flags, void *stream);
 
 /*
+ * kda_chunk_fwd_pooled for B sequences of different lengths packed along the
+ * token axis: q, k [total_tokens, H, dk], v, o [total_tokens, H, dv], g
+ * [total_tokens, H, dk] fp32, beta [total_tokens, H]; sequence b is rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens: B+1 int64 on the device,
+ * non-decreasing from 0; values outside [0, total_tokens] are clamped there,
+ * so a bad table cannot address outside the tensors).  An empty sequence
+ * leaves its slot unchanged.  bf16, dk = 128, dv in {64, 128}; one pass (no
+ * sequence split, no range check); the position-pair flag applies.
+ */
+int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, const float *g,
+                                const void *beta, float *state_pool, const int32_t *slots,
+                                const int64_t *cu_seqlens, void *o, int64_t B,
+                                int64_t total_tokens, int64_t n_slots, int64_t H, int64_t dk,
+                                int64_t dv, int dtype, unsigned flags, void *stream);
+
+/*
  * kda_decode_step for N sequences whose states live in the pool: sequence n
  * reads and updates slot slots[n] in place (continuous batching: the set of
  * slots may change from step to step).  q, k, v, z, A, beta, o as in

@@ -35,7 +35,8 @@ def kda_flag_segments(n: int) -> int:
 EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
             "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
-            "kda_decode_step_pooled", "kda_last_error", "kda_version")
+            "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_last_error",
+            "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -77,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_pooled.restype = c_int
     L.kda_decode_step_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                          i64, c_int, vp]
+    L.kda_chunk_fwd_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                              i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd_varlen_pooled.restype = c_int
     L.kda_decode_step_pooled.restype = c_int
     L.kda_last_error.argtypes = []
     L.kda_last_error.restype = ctypes.c_char_p
@@ -243,4 +247,26 @@ def kda_decode_step_pooled(q, k, v, z, A, beta, state_pool, slots, o=None,
     _check(load_library().kda_decode_step_pooled(
         _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(state_pool), _ptr(slots),
         _ptr(o), N, state_pool.shape[0], H, dk, dv, _dtype_code(q), _stream(stream)))
+    return o
+
+
+def kda_chunk_fwd_varlen_pooled(q, k, v, g, beta, state_pool, slots, cu_seqlens, o=None,
+                                flags: int = 0, stream=None) -> torch.Tensor:
+    """Prefill of B sequences of different lengths packed along the token axis
+    (q, k, g [total,H,dk], v [total,H,dv], beta [total,H]; sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1, cu_seqlens int64 [B+1] on the device),
+    with states in `state_pool` at `slots` [B].  Returns o [total,H,dv]."""
+    _dev(q, k, v, g, beta, state_pool, o)
+    slots = _slots(slots)
+    if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int64 CUDA tensor")
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    B = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((total, H, dv), device=q.device, dtype=q.dtype)
+    _check(load_library().kda_chunk_fwd_varlen_pooled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+        _ptr(cu_seqlens), _ptr(o), B, total, state_pool.shape[0], H, dk, dv, _dtype_code(q), flags,
+        _stream(stream)))
     return o

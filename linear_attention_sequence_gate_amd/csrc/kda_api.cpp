@@ -51,6 +51,25 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// pool [n_slots, H, dk, dv] and slot table checks shared by the pooled entry points
+int check_pool(const char *who, const float *pool, const int32_t *slots, int64_t n_slots,
+               int64_t H, int64_t dk, int64_t dv) {
+    if (!pool || !slots) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null state_pool or slots", who);
+    if (n_slots <= 0 || H <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
+    if (!valid_dim(dk) || !valid_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
+                    (long long)dk, (long long)dv);
+    int64_t np = n_slots;
+    if (!mul_ok(np, H) || !mul_ok(np, dk) || !mul_ok(np, dv))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pool size overflows", who);
+    if (n_slots * H > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots*H too large", who);
+    if (!aligned16(pool)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool must be 16-byte aligned", who);
+    if (reinterpret_cast<uintptr_t>(slots) & 3u)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slots must be 4-byte aligned", who);
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,55 +136,50 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
                    const void *beta, const float *initial_state, float *final_state, void *o,
                    void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
                    int64_t dk, int64_t dv, int dtype, unsigned flags, const int32_t *slots,
-                   int64_t n_slots, void *stream) {
-    (void)who;
+                   int64_t n_slots, const int64_t *cu_seqlens, void *stream) {
     if (int e = check_dtype(dtype)) return e;
     if (!q || !k || !v || !g || !beta || !o)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: null pointer (q, k, v, g, beta, o are required)");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (q, k, v, g, beta, o are required)", who);
     if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: sizes must be positive");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
     if (!valid_dim(dk) || !valid_dim(dv))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: dk=%lld dv=%lld must be in {32,64,128}",
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
                     (long long)dk, (long long)dv);
     if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd: fp32 inputs support dk in {32,64} only");
+        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs support dk in {32,64} only", who);
     if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: unknown flag bits 0x%x", flags);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
     const bool is_bf16 = dtype == KDA_BF16;
     const bool pairwise = (flags & KDA_FLAG_PAIRWISE_DIAGONAL) != 0;
     if (pairwise && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
-        return fail(KDA_ERR_UNSUPPORTED,
-                    "kda_chunk_fwd: the position-pair diagonal path needs bf16 inputs, dk = 128, "
-                    "dv in {64, 128}");
+        return fail(KDA_ERR_UNSUPPORTED, "%s: the position-pair diagonal path needs bf16 inputs, dk = 128, "
+                    "dv in {64, 128}", who);
     if (pairwise && (flags & KDA_FLAG_CHECK_RANGE))
-        return fail(KDA_ERR_INVALID_ARGUMENT,
-                    "kda_chunk_fwd: the position-pair diagonal path has no decay range to check");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the position-pair diagonal path has no decay range to check", who);
     const int req_seg = (int)((flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT);
     if (req_seg >= 2 && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
-        return fail(KDA_ERR_UNSUPPORTED,
-                    "kda_chunk_fwd: a sequence split needs bf16 inputs, dk = 128, dv in {64, 128}");
+        return fail(KDA_ERR_UNSUPPORTED, "%s: a sequence split needs bf16 inputs, dk = 128, dv in {64, 128}", who);
     int64_t nk = B, nv = B, ns = B;
     if (!mul_ok(nk, T) || !mul_ok(nk, H) || !mul_ok(nk, dk) || !mul_ok(nv, T) || !mul_ok(nv, H) ||
         !mul_ok(nv, dv) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: element count overflows");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: element count overflows", who);
     if (B * H > (int64_t(1) << 24))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: B*H=%lld too large", (long long)(B * H));
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H=%lld too large", who, (long long)(B * H));
     // the kernel addresses the tokens of one 64-token chunk with 32-bit byte offsets
     if (H * (dk > dv ? dk : dv) * 64 * 4 >= (int64_t(1) << 32))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: H=%lld too large", (long long)H);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: H=%lld too large", who, (long long)H);
     const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: pointers must be 16-byte aligned");
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", who);
     const void *ins[] = {q, k, v, g, beta, initial_state};
     for (const void *p : ins)
-        if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd: o must not alias an input");
+        if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o must not alias an input", who);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (flags & KDA_FLAG_CHECK_RANGE) {
         if (!workspace || workspace_bytes < kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
-            return fail(KDA_ERR_INVALID_ARGUMENT,
-                        "kda_chunk_fwd: KDA_FLAG_CHECK_RANGE needs a workspace of %zu bytes",
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: KDA_FLAG_CHECK_RANGE needs a workspace of %zu bytes", who,
                         kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype));
         unsigned int *bad = static_cast<unsigned int *>(workspace);
         hipError_t e = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
@@ -177,8 +191,7 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd range check readback");
         if (nbad)
-            return fail(KDA_ERR_RANGE,
-                        "kda_chunk_fwd: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]",
+            return fail(KDA_ERR_RANGE, "%s: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]", who,
                         nbad);
     }
     // sequence split: requested, or picked for these sizes when the workspace
@@ -190,15 +203,14 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         if (workspace && workspace_bytes >= need) {
             split_ws = static_cast<char *>(workspace) + kCounterBytes;
         } else if (req_seg >= 2) {
-            return fail(KDA_ERR_INVALID_ARGUMENT,
-                        "kda_chunk_fwd: a %d-segment split needs a workspace of %zu bytes", nseg, need);
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a %d-segment split needs a workspace of %zu bytes", who, nseg, need);
         } else {
             nseg = 1;
         }
     }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
                                          (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
-                                         pairwise ? 1 : 0, s);
+                                         pairwise ? 1 : 0, cu_seqlens, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }
@@ -213,7 +225,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   int dtype, unsigned flags, void *stream) {
     return chunk_fwd_impl("kda_chunk_fwd", q, k, v, g, beta, initial_state, final_state, o,
                           workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, nullptr, 0,
-                          stream);
+                          nullptr, stream);
 }
 
 int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g,
@@ -234,7 +246,32 @@ int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const floa
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: o must not alias an input");
     return chunk_fwd_impl("kda_chunk_fwd_pooled", q, k, v, g, beta, state_pool, state_pool, o,
                           workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, slots,
-                          n_slots, stream);
+                          n_slots, nullptr, stream);
+}
+
+int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, const float *g,
+                                const void *beta, float *state_pool, const int32_t *slots,
+                                const int64_t *cu_seqlens, void *o, int64_t B,
+                                int64_t total_tokens, int64_t n_slots, int64_t H, int64_t dk,
+                                int64_t dv, int dtype, unsigned flags, void *stream) {
+    const char *who = "kda_chunk_fwd_varlen_pooled";
+    if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null cu_seqlens", who);
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens must be 8-byte aligned", who);
+    if (!kda::seq_split_supported((int)dk, (int)dv, dtype == KDA_BF16))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: needs bf16 inputs, dk = 128, dv in {64, 128}", who);
+    if (flags & (KDA_FLAG_CHECK_RANGE | KDA_FLAG_SEGMENTS_MASK))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: the range check and the sequence split take the [B, T, H] layout", who);
+    if (int e = check_pool(who, state_pool, slots, n_slots, H, dk, dv)) return e;
+    if (static_cast<const void *>(slots) == o || static_cast<const void *>(state_pool) == o ||
+        static_cast<const void *>(cu_seqlens) == o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o must not alias an input", who);
+    // one pass (no split), the packed tokens as T of a single batch row for
+    // the size checks; the kernel reads sequence b's rows from cu_seqlens
+    return chunk_fwd_impl(who, q, k, v, g, beta, state_pool, state_pool, o, nullptr, 0, B,
+                          total_tokens, H, dk, dv, dtype, flags | KDA_FLAG_SEGMENTS(1), slots,
+                          n_slots, cu_seqlens, stream);
 }
 
 }  // extern "C"
@@ -269,25 +306,6 @@ int decode_step_impl(const void *q, const void *k, const void *v, const void *z,
                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
     return ok();
-}
-
-// pool [n_slots, H, dk, dv] and slot table checks shared by the pooled entry points
-int check_pool(const char *who, const float *pool, const int32_t *slots, int64_t n_slots,
-               int64_t H, int64_t dk, int64_t dv) {
-    if (!pool || !slots) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null state_pool or slots", who);
-    if (n_slots <= 0 || H <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
-    if (!valid_dim(dk) || !valid_dim(dv))
-        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
-                    (long long)dk, (long long)dv);
-    int64_t np = n_slots;
-    if (!mul_ok(np, H) || !mul_ok(np, dk) || !mul_ok(np, dv))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pool size overflows", who);
-    if (n_slots * H > 0x7fffffffLL)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: n_slots*H too large", who);
-    if (!aligned16(pool)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool must be 16-byte aligned", who);
-    if (reinterpret_cast<uintptr_t>(slots) & 3u)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slots must be 4-byte aligned", who);
-    return KDA_OK;
 }
 
 }  // namespace

@@ -78,6 +78,10 @@ struct ChunkArgs {
     // chunk32_kernel: diagonal 16-token tiles by position pairs in log space
     // (no assumption on the decay range) instead of dense MFMA tiles
     int pairwise;
+    // chunk32_kernel, variable lengths: sequence b holds tokens
+    // cu_seqlens[b] .. cu_seqlens[b+1] - 1 of a packed [T, H, ...] layout
+    // (T = all tokens); null for the [B, T, H, ...] layout
+    const int64_t *cu_seqlens;
 };
 
 // Row of a sequence's state (b, h) in S0/ST: b * H + h, or with a slot table
@@ -998,7 +1002,15 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const int b = bh / H, h = bh % H;
     const int64_t urow = user_state_row(a, b, h);   // row in the caller's S0 / ST
     if (urow < 0) return;                           // slot outside the pool: skipped
-    const int64_t T_ = a.T;
+    // this sequence's first token row in memory and its length (packed
+    // offsets are clamped to the a.T rows that exist)
+    int64_t tok_base = (int64_t)b * a.T, T_ = a.T;
+    if (a.cu_seqlens) {
+        const int64_t lo = a.cu_seqlens[b], hi = a.cu_seqlens[b + 1];
+        tok_base = lo < 0 ? 0 : (lo > a.T ? a.T : lo);
+        const int64_t end = hi < tok_base ? tok_base : (hi > a.T ? a.T : hi);
+        T_ = end - tok_base;
+    }
     const int64_t tbeg = (int64_t)seg * a.seg_len;
     const int64_t tend = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
     const int vcol0 = (mcols ? slice - a.nsl_v : slice) * NV;
@@ -1065,7 +1077,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         auto load_raw = [&](int64_t ch, Raw &r) {
             const int64_t t0 = tbeg + ch * kPipeChunk;
             const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
-            const int64_t tok0 = ((int64_t)b * T_ + t0) * H + h;
+            const int64_t tok0 = (tok_base + t0) * H + h;
             const char *gb = uniform_base(gp + tok0 * DK);
             const char *kb = uniform_base(kp + tok0 * DK), *qb = uniform_base(qp + tok0 * DK);
             const char *bb = uniform_base(bp + tok0);
@@ -1381,7 +1393,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             lds_barrier();                                  // BAR2
 
         };
-        load_raw(0, raw0);
+        if (nchunk > 0) load_raw(0, raw0);         // an empty sequence loads nothing
         if (nchunk > 1) load_raw(1, raw1);
         for (int64_t c = 0; c <= nchunk + 1; c += 2) {
             period(c, raw0);
@@ -1449,7 +1461,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         auto load_v = [&](int64_t ch, unsigned (&dst)[2][4]) {
             const int64_t t0 = tbeg + ch * kPipeChunk;
             const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
-            const char *vb = uniform_base(vp + (((int64_t)b * T_ + t0) * H + h) * DV);
+            const char *vb = uniform_base(vp + ((tok_base + t0) * H + h) * DV);
             // full chunk: token 16 i + lg4 + j is a scalar step of 16 i + j
             // rows from the lane's first row; last chunk: per-lane offsets
             // from row 0, rows past the end re-reading the last row
@@ -1552,7 +1564,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                         PF::mma(oacc[Ir], ul, ph);
                         PF::mma(oacc[Ir], uh, pl);
                     }
-                    const void *obase = op + (((int64_t)b * T_ + t0) * H + h) * DV + vcol0 + 16 * s;
+                    const void *obase = op + ((tok_base + t0) * H + h) * DV + vcol0 + 16 * s;
 #pragma unroll
                     for (int Ir = 0; Ir < 2; ++Ir) {
                         const int r = 16 * Ir + lr;
@@ -1763,7 +1775,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
-                            hipStream_t s) {
+                            const int64_t *cu_seqlens, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
@@ -1779,6 +1791,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.slots = slots;
     args.n_slots = n_slots;
     args.pairwise = pipe && pairwise ? 1 : 0;
+    args.cu_seqlens = cu_seqlens;
+    if (cu_seqlens && (!pipe || nseg >= 2)) return hipErrorInvalidValue;
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
     if (pipe && P >= 2) {
         if (!split_ws) return hipErrorInvalidValue;

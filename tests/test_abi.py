@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
               "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
-              "kda_decode_step_pooled", "kda_last_error", "kda_version"):
+              "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_last_error",
+              "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -191,3 +192,13 @@ def test_pool_validation(L):
     assert ch(slots=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(ns=0) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(o=P) == E.KDA_ERR_INVALID_ARGUMENT                          # o aliases the pool
+
+    vl = lambda cu=P3, dk=128, dv=128, dt=1, flags=0, pool=P, o=P2: L.kda_chunk_fwd_varlen_pooled(
+        P, P, P, P, P, pool, S4, cu, o, 2, 100, 4, 1, dk, dv, dt, flags, None)
+    assert vl(cu=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert vl(cu=ctypes.c_void_p(0x300004)) == E.KDA_ERR_INVALID_ARGUMENT   # not 8-byte aligned
+    assert vl(dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert vl(dt=0) == E.KDA_ERR_UNSUPPORTED
+    assert vl(flags=E.KDA_FLAG_CHECK_RANGE) == E.KDA_ERR_INVALID_ARGUMENT
+    assert vl(flags=_lib.kda_flag_segments(3)) == E.KDA_ERR_INVALID_ARGUMENT
+    assert vl(o=P) == E.KDA_ERR_INVALID_ARGUMENT                           # o aliases the pool

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 from linear_attention_sequence_gate_amd import (_lib, inputs, kda_chunk_fwd, kda_chunk_fwd_pooled,
-                                                kda_decode_step, kda_decode_step_pooled, kda_gate,
+                                                kda_chunk_fwd_varlen_pooled, kda_decode_step,
+                                                kda_decode_step_pooled, kda_gate,
                                                 kda_state_pool_reset)
 from kda_testutil import TOL, rho, say
 
@@ -159,3 +160,45 @@ def test_continuous_batching_matches_the_oracle(dtype, d):
         print(f"    {r}: rho(o)={ro:.3e}", flush=True)
         assert np.isfinite(st["out"].float().cpu().numpy()).all()
         assert ro <= TOL[dtype], (r, ro)
+
+
+@pytest.mark.parametrize("dv,flags", [(128, 0), (64, 0), (128, _lib.KDA_FLAG_PAIRWISE_DIAGONAL)])
+def test_varlen_pooled_prefill_equals_per_sequence_calls(dv, flags):
+    """Five prompts of 37, 0, 300, 64 and 1 tokens packed in one call equal
+    five separate pooled calls bit for bit (the empty one leaves its slot as
+    it was); one sequence is also checked against the oracle."""
+    say("varlen pooled prefill", dv, flags)
+    lens = [37, 0, 300, 64, 1]
+    H, total = 2, sum(lens)
+    x = inputs.make_prefill_inputs(1, total, H, 128, dv, torch.bfloat16, 530, device="cuda")
+    g = kda_gate(x["z"], x["A"])
+    q, k, v = x["q"][0], x["k"][0], x["v"][0]
+    gg, beta = g[0], x["beta"][0]
+    cu_list = [0]
+    for L in lens:
+        cu_list.append(cu_list[-1] + L)
+    cu = torch.tensor(cu_list, dtype=torch.int64, device="cuda")
+    slots = [3, 6, 0, 7, 5]
+    pool = _pool(8, H, 128, dv, 531)
+    before = pool.clone()
+    o = kda_chunk_fwd_varlen_pooled(q, k, v, gg, beta, pool, _slots(slots), cu, flags=flags)
+    ref_pool = before.clone()
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        a_, e_ = cu_list[b], cu_list[b + 1]
+        sl = lambda t: t[a_:e_].unsqueeze(0).clone()      # own, aligned allocation
+        ob = kda_chunk_fwd_pooled(sl(q), sl(k), sl(v), sl(gg), sl(beta), ref_pool, _slots([slots[b]]),
+                                  flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a_:e_], ob[0]), b
+    torch.cuda.synchronize()
+    assert torch.equal(pool, ref_pool)
+    assert torch.equal(pool[6], before[6])               # the empty sequence's slot
+    a_, e_ = cu_list[2], cu_list[3]
+    S0 = before[0].unsqueeze(0)
+    o_ref, S_ref = oracle.forward(q[a_:e_].unsqueeze(0).clone(), k[a_:e_].unsqueeze(0).clone(),
+                                  v[a_:e_].unsqueeze(0).clone(), gg[a_:e_].unsqueeze(0).float().cpu(),
+                                  beta[a_:e_].unsqueeze(0).clone(), S0)
+    assert rho(o[a_:e_].unsqueeze(0), o_ref) <= TOL[torch.bfloat16]
+    assert rho(pool[0].unsqueeze(0), S_ref) <= TOL[torch.bfloat16]
