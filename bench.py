@@ -506,6 +506,69 @@ def ingest_trace_extra(name, d):
     print("\n".join(lines))
 
 
+SQ_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_ACTIVE_INST_VALU "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_ANY",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_WAIT_INST_LDS SQ_WAIT_ANY SQ_ACTIVE_INST_LDS "
+    "SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_INST_LEVEL_LDS",
+)
+SQ_MD = os.path.join(ROOT, "profiles", "sq_counters_chunk32_b4h32t32k.md")
+
+
+def sq_cmd(i):
+    return (f"rocprofv3 --pmc {SQ_PASSES[i]} --output-format csv -d gpurun_out/sq{i} -- "
+            "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline "
+            "--no-parity --no-extras")
+
+
+def ingest_sq(dirs):
+    """Shader-sequencer counters of chunk32_kernel on the benchmark workload,
+    averaged per dispatch, and unit-free figures per SIMD and 32-token period."""
+    vals = {}
+    counters = [c for ps in SQ_PASSES for c in ps.split()]
+    for d in dirs:
+        for ctr in counters:
+            try:
+                rows = _pmc_rows(d, ctr)
+            except SystemExit:
+                continue
+            v = [x for n, x in rows if "chunk32_kernel" in n]
+            if v:
+                vals[ctr] = sum(v) / len(v)
+    w = PREFILL
+    periods = (w.T + 31) // 32 + 2                 # pipeline periods per workgroup
+    wgs = w.B * w.H * (w.dv // 64)
+    simd_periods = wgs * 4 * periods
+    lines = ["# Shader-sequencer counters, chunk32_kernel (rocprofv3 --pmc)", "",
+             "Workload: prefill B4 H32 T32768 d128 bf16, 256 workgroups of 12 waves, "
+             f"{periods} periods of 32 tokens each.", "",
+             "Commands (from the repository root):", ""]
+    lines += ["    " + sq_cmd(i) for i in range(len(SQ_PASSES))]
+    lines += ["    python3 bench.py --ingest-sq " + " ".join(f"gpurun_out/sq{i}" for i in range(len(SQ_PASSES))), "",
+              "| counter | per dispatch |", "|---|---|"]
+    for k in sorted(vals):
+        lines.append(f"| {k} | {vals[k]:.4g} |")
+    derived = []
+    if "SQ_INSTS_VALU" in vals:
+        derived.append(f"| VALU instructions per SIMD per period (MFMA included) | {vals['SQ_INSTS_VALU'] / simd_periods:.0f} |")
+    if "SQ_INSTS_LDS" in vals:
+        derived.append(f"| LDS instructions per SIMD per period | {vals['SQ_INSTS_LDS'] / simd_periods:.0f} |")
+    if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_INSTS_LDS" in vals:
+        derived.append(f"| LDS bank-conflict cycles per LDS instruction | "
+                       f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.2f} |")
+    if "SQ_WAIT_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        derived.append(f"| share of wave time waiting (any) | {vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.2f} |")
+    if "SQ_ACTIVE_INST_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        derived.append(f"| share of wave time issuing | {vals['SQ_ACTIVE_INST_ANY'] / vals['SQ_WAVE_CYCLES']:.2f} |")
+    if derived:
+        lines += ["", "Derived (counts are summed over waves; the shares divide counters kept in "
+                  "the same unit):", "", "| figure | value |", "|---|---|"] + derived
+    lines.append("")
+    with open(SQ_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -521,6 +584,7 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
     ap.add_argument("--ingest-trace-extra", nargs=2, metavar=("NAME", "TRACE_DIR"))
+    ap.add_argument("--ingest-sq", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--only", choices=("long", "pairwise"),
                     help="time only one extra line and print its record")
     args = ap.parse_args()
@@ -532,6 +596,9 @@ def main():
         return
     if args.ingest_trace_extra:
         ingest_trace_extra(*args.ingest_trace_extra)
+        return
+    if args.ingest_sq:
+        ingest_sq(args.ingest_sq)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
