@@ -7,7 +7,10 @@ imports, links or calls it, and the two share no code.
 Two implementations of the same definition:
   * `kda_oracle.c` (fp64, OpenMP), wrapped here by `gate`, `forward`,
     `decode_step`;
-  * a NumPy twin (`gate_np`, `forward_np`, `decode_step_np`) for small cases.
+  * a NumPy twin (`gate_np`, `forward_np`, `decode_step_np`) for small cases;
+  * `backward_np`: the reverse mode of the same token loop (gradients of
+    <o, do> + <S_T, dS_T> with respect to q, k, v, g, beta and S_0), pinned by
+    central finite differences of `forward_np`.
 
 The definition they follow ("Kimi K3 internal structure analysis", section
 "Sequence mixing: 3 KDA layers per global MLA layer"; recurrence as written in
@@ -23,6 +26,7 @@ forms, brute-force unrolled products and invariants; see tests/test_oracle_*.py.
 from .core import (  # noqa: F401
     GMIN,
     TILE,
+    backward_np,
     build_oracle,
     decode_step,
     decode_step_np,

@@ -206,3 +206,63 @@ def tile_log_decay_sums(g, tile: int = TILE) -> np.ndarray:
     if pad:
         g = np.concatenate([g, np.zeros((B, pad, H, dk))], axis=1)
     return g.reshape(B, nt, tile, H, dk).sum(axis=2)
+
+
+# ----------------------------------------------------------------------------
+# Reverse mode of the recurrence (plain loops over tokens, fp64)
+# ----------------------------------------------------------------------------
+
+def backward_np(q, k, v, g, beta, S0=None, do=None, dST=None) -> dict:
+    """Gradients of L = <o, do> + <S_T, dST> through the token recurrence.
+
+    Each token's step is differentiated as written (retention, delta-rule
+    write, post-update read), walking the tokens in reverse:
+        dS_t += q_t do_t^T;             dq_t = S_t do_t
+        du = dS_t^T k_t;                dk_t = dS_t u_t (+ below)
+        dbeta_t = du . (v_t - w);       dv_t = beta_t du;   dw = -beta_t du
+        dS' = dS_t + k_t dw^T;          dk_t += S' dw       (w = S'^T k_t)
+        da = rowsum(S_{t-1} * dS');     dg_t = a * da       (a = exp(g_t))
+        dS_{t-1} = Diag(a) dS'
+    Returns dq, dk, dv, dg, dbeta (input shapes) and dS0 [B,H,dk,dv].
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    S0 = _f64(S0)
+    do = np.zeros((B, T, H, dv)) if do is None else _f64(do)
+    dST = None if dST is None else _f64(dST)
+    out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g),
+                                            ("dbeta", beta))}
+    out["dS0"] = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else S0[b, h].copy()
+            states = [S]                                   # states[t] = S before token t
+            for t in range(T):
+                S = np.exp(g[b, t, h])[:, None] * S
+                u = beta[b, t, h] * (v[b, t, h] - S.T @ k[b, t, h])
+                S = S + np.outer(k[b, t, h], u)
+                states.append(S)
+            dS = np.zeros((dk, dv)) if dST is None else dST[b, h].copy()
+            for t in range(T - 1, -1, -1):
+                a = np.exp(g[b, t, h])
+                kt, qt, vt, bt = k[b, t, h], q[b, t, h], v[b, t, h], beta[b, t, h]
+                Sp = a[:, None] * states[t]                 # S'
+                w = Sp.T @ kt
+                u = bt * (vt - w)
+                St = states[t + 1]
+                dS = dS + np.outer(qt, do[b, t, h])
+                out["dq"][b, t, h] = St @ do[b, t, h]
+                du = dS.T @ kt
+                dkt = dS @ u
+                out["dbeta"][b, t, h] = du @ (vt - w)
+                out["dv"][b, t, h] = bt * du
+                dw = -bt * du
+                dSp = dS + np.outer(kt, dw)
+                dkt = dkt + Sp @ dw
+                out["dk"][b, t, h] = dkt
+                da = np.sum(states[t] * dSp, axis=1)
+                out["dg"][b, t, h] = a * da
+                dS = a[:, None] * dSp
+            out["dS0"][b, h] = dS
+    return out
