@@ -256,6 +256,45 @@ def time_pairwise_diagonal(reps=3):
     return out
 
 
+FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, vendor figure
+# reverse mode, fp32 flops per head-token counted once (no recomputation):
+# the forward step (decay, k projection, write: 5 d^2) and the reverse step
+# (q do^T, dq, du, dk (two terms), dS', the decay sum, dS = a dS', S_t: 18 d^2)
+BWD_FLOPS_PER_D2 = 23
+
+
+def time_backward(reps=2):
+    """kda_chunk_bwd on B4 H32 d128 bf16 with T = 4096 (the benchmark's chain
+    count; T cut so the checkpoints, 64 KiB per 8 tokens per chain, take 4 GiB)."""
+    B, T, H, d = 4, 4096, 32, 128
+    dev = torch.device("cuda")
+    x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02)
+    g = _lib.kda_gate(x["z"], x["A"])
+    d_o = torch.randn(B, T, H, d, device=dev).to(torch.bfloat16)
+    ws = torch.empty(_lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, 1), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    run = lambda: _lib.kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, None,
+                                     workspace=ws, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ht = B * T * H
+    tflops = BWD_FLOPS_PER_D2 * d * d * ht / (ms / 1e3) / 1e12
+    del x, g, d_o, ws
+    torch.cuda.empty_cache()
+    return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16 (gradients fp32)",
+            "head_tokens_per_s": ht / (ms / 1e3),
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS,
+                         "flops_per_head_token": BWD_FLOPS_PER_D2 * d * d}}
+
+
 def time_decode(nsteps=1000, warmup=20):
     w = DECODE
     dev = torch.device("cuda")
@@ -420,6 +459,10 @@ EXTRA_TRACES = {
              "A split call is three launches: chunk32_kernel phase 1 (segment 0, the middle "
              "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
+    "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
+                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (1 warm-up + 2 "
+                 "timed calls): bwd_ckpt_kernel (forward with a checkpoint every 8 tokens) and "
+                 "bwd_kernel (reverse walk) per call."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (2 warm-up + 3 timed calls) and with the position-pair "
@@ -480,7 +523,8 @@ def ingest_trace_extra(name, d):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel"))]
+    rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel",
+                                                           "bwd_ckpt_kernel", "bwd_kernel"))]
     chunk_rows = [r for r in rows if "chunk32_kernel" in r["Kernel_Name"]]
     groups = {}
     for r in rows:
@@ -585,7 +629,7 @@ def main():
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
     ap.add_argument("--ingest-trace-extra", nargs=2, metavar=("NAME", "TRACE_DIR"))
     ap.add_argument("--ingest-sq", nargs="+", metavar="PMC_DIR")
-    ap.add_argument("--only", choices=("long", "pairwise"),
+    ap.add_argument("--only", choices=("long", "pairwise", "backward"),
                     help="time only one extra line and print its record")
     args = ap.parse_args()
     if args.ingest_pmc:
@@ -608,7 +652,8 @@ def main():
     _lib.load_library()
     torch.cuda.init()
     if args.only:
-        rec = time_long_prefill() if args.only == "long" else time_pairwise_diagonal()
+        rec = {"long": time_long_prefill, "pairwise": time_pairwise_diagonal,
+               "backward": time_backward}[args.only]()
         print(json.dumps(rec), flush=True)
         return
 
@@ -633,6 +678,7 @@ def main():
 
     long_res = None if args.no_extras else time_long_prefill()
     pair_res = None if args.no_extras else time_pairwise_diagonal()
+    bwd_res = None if args.no_extras else time_backward()
     dec = time_decode(args.decode_steps)
     dbytes = decode_bytes(DECODE)
     dec_gbs = dbytes / (dec["us_per_step"] * 1e-6) / 1e9
@@ -670,6 +716,7 @@ def main():
                     "head_tokens": work["head_tokens"]},
         "prefill_long": long_res,
         "prefill_pairwise_diagonal": pair_res,
+        "prefill_backward": bwd_res,
         "decode": {"us_per_step": dec["us_per_step"], "steps": dec["steps"],
                    "tokens_per_s": DECODE.B / (dec["us_per_step"] * 1e-6),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,

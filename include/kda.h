@@ -190,6 +190,34 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
                     int dtype, void *stream);
 
 /*
+ * kda_chunk_bwd -- gradients of L = <o, d_o> + <S_T, d_final_state> through
+ * the recurrence kda_chunk_fwd computes (same inputs and layouts), with
+ * respect to q, k, v, g, beta and the initial state.  The step it reverses
+ * is the one of "Kimi K3 internal structure analysis", section "Sequence
+ * mixing: 3 KDA layers per global MLA layer" (retention, delta-rule write,
+ * read after the write); the pages say nothing of training, so the reverse
+ * mode is derived from that step.  Token by token: one workgroup per chain
+ * stores the state every 8 tokens in the workspace, then walks the tokens
+ * backwards, recomputing the state before each from its checkpoint.
+ *   d_o             : [B, T, H, dv] dtype
+ *   d_final_state   : [B, H, dk, dv] fp32, or NULL (zero)
+ *   dq, dk, dg      : [B, T, H, dk] fp32 (outputs)
+ *   dv              : [B, T, H, dv] fp32 (output)
+ *   dbeta           : [B, T, H]     fp32 (output)
+ *   d_initial_state : [B, H, dk, dv] fp32, or NULL if not wanted
+ *   workspace       : kda_chunk_bwd_workspace_size() bytes (the checkpoints)
+ * Outputs must not alias inputs.  g is taken as given (any value <= 0).
+ */
+size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                    int64_t dk, int64_t dv, int dtype);
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
+                  const void *beta, const float *initial_state, const void *d_o,
+                  const float *d_final_state, float *dq, float *dk, float *dv, float *dg,
+                  float *dbeta, float *d_initial_state, void *workspace, size_t workspace_bytes,
+                  int64_t B, int64_t T, int64_t H, int64_t dk_dim, int64_t dv_dim,
+                  int dtype, void *stream);
+
+/*
  * State pool for serving ("Kimi K3 internal structure analysis", section
  * "Serving two incompatible cache types": the KDA layers keep a fixed-size
  * recurrent state per sequence beside the MLA layers' growing cache).  A pool

@@ -35,8 +35,8 @@ def kda_flag_segments(n: int) -> int:
 EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
             "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
-            "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_last_error",
-            "kda_version")
+            "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
+            "kda_chunk_bwd_workspace_size", "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -81,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                               i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd_varlen_pooled.restype = c_int
+    L.kda_chunk_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
+    L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int, vp]
+    L.kda_chunk_bwd.restype = c_int
     L.kda_decode_step_pooled.restype = c_int
     L.kda_last_error.argtypes = []
     L.kda_last_error.restype = ctypes.c_char_p
@@ -270,3 +274,32 @@ def kda_chunk_fwd_varlen_pooled(q, k, v, g, beta, state_pool, slots, cu_seqlens,
         _ptr(cu_seqlens), _ptr(o), B, total, state_pool.shape[0], H, dk, dv, _dtype_code(q), flags,
         _stream(stream)))
     return o
+
+
+def kda_chunk_bwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int) -> int:
+    return int(load_library().kda_chunk_bwd_workspace_size(B, T, H, dk, dv, dtype))
+
+
+def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
+                  want_d_initial_state: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of <o, d_o> + <S_T, d_final_state> through kda_chunk_fwd's
+    recurrence.  Returns dict dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta
+    [B,T,H] and d_initial_state [B,H,dk,dv] (fp32; the last None if not wanted)."""
+    _dev(q, k, v, g, beta, initial_state, d_o, d_final_state, workspace)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    f32 = dict(device=q.device, dtype=torch.float32)
+    out = dict(dq=torch.empty(B, T, H, dk, **f32), dk=torch.empty(B, T, H, dk, **f32),
+               dv=torch.empty(B, T, H, dv, **f32), dg=torch.empty(B, T, H, dk, **f32),
+               dbeta=torch.empty(B, T, H, **f32),
+               d_initial_state=torch.empty(B, H, dk, dv, **f32) if want_d_initial_state else None)
+    if workspace is None:
+        workspace = torch.empty(max(kda_chunk_bwd_workspace_size(B, T, H, dk, dv, dt), 256),
+                                device=q.device, dtype=torch.uint8)
+    _check(load_library().kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
+        _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+        _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), B, T, H, dk, dv, dt, _stream(stream)))
+    return out

@@ -312,6 +312,57 @@ int decode_step_impl(const void *q, const void *k, const void *v, const void *z,
 
 extern "C" {
 
+size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    int dtype) {
+    if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk) || !mul_ok(n, dv)) return 0;
+    return kda::bwd_workspace_bytes(B, T, H, (int)dk, (int)dv);
+}
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
+                  const float *initial_state, const void *d_o, const float *d_final_state,
+                  float *dq, float *dk, float *dv, float *dg, float *dbeta,
+                  float *d_initial_state, void *workspace, size_t workspace_bytes, int64_t B,
+                  int64_t T, int64_t H, int64_t dk_dim, int64_t dv_dim, int dtype, void *stream) {
+    const char *who = "kda_chunk_bwd";
+    if (int e = check_dtype(dtype)) return e;
+    if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta || !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (all but initial_state, "
+                    "d_final_state and d_initial_state are required)", who);
+    if (B <= 0 || T <= 0 || H <= 0 || dk_dim <= 0 || dv_dim <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
+    if (!valid_dim(dk_dim) || !valid_dim(dv_dim))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
+                    (long long)dk_dim, (long long)dv_dim);
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk_dim) || !mul_ok(n, dv_dim))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: element count overflows", who);
+    if (B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H too large", who);
+    const size_t need = kda::bwd_workspace_bytes(B, T, H, (int)dk_dim, (int)dv_dim);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of %zu bytes", who, need);
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
+                          dbeta, d_initial_state, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", who);
+    const void *outs[] = {dq, dk, dv, dg, dbeta, d_initial_state, workspace};
+    const void *ins[] = {q, k, v, g, beta, initial_state, d_o, d_final_state};
+    for (const void *po : outs)
+        for (const void *pi : ins)
+            if (po && po == pi)
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s: outputs must not alias inputs", who);
+    hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state, dq,
+                                         dk, dv, dg, dbeta, d_initial_state,
+                                         static_cast<float *>(workspace), B, T, H, (int)dk_dim,
+                                         (int)dv_dim, dtype == KDA_BF16,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd launch");
+    return ok();
+}
+
 int kda_decode_step(const void *q, const void *k, const void *v, const void *z, const float *A,
                     const void *beta, float *state, void *o, int64_t N, int64_t H, int64_t dk,
                     int64_t dv, int dtype, void *stream) {

@@ -52,4 +52,14 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
 hipError_t launch_pool_reset(float *pool, const int *slots, int64_t n, int64_t n_slots,
                              int64_t per_slot, hipStream_t s);
 
+// Reverse mode of the recurrence (token by token, states recomputed from
+// checkpoints every 8 tokens kept in `ckpt`, bwd_workspace_bytes() long).
+// Gradients are fp32; dST and dS0 may be null.
+hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
+                            const void *beta, const float *S0, const void *dout, const float *dST,
+                            float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                            float *ckpt, int64_t B, int64_t T, int64_t H, int dk_, int dv_,
+                            int is_bf16, hipStream_t s);
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
+
 }  // namespace kda

@@ -37,8 +37,8 @@ def test_header_declares_the_boundary():
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
               "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
-              "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_last_error",
-              "kda_version"):
+              "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
+              "kda_chunk_bwd_workspace_size", "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -202,3 +202,23 @@ def test_pool_validation(L):
     assert vl(flags=E.KDA_FLAG_CHECK_RANGE) == E.KDA_ERR_INVALID_ARGUMENT
     assert vl(flags=_lib.kda_flag_segments(3)) == E.KDA_ERR_INVALID_ARGUMENT
     assert vl(o=P) == E.KDA_ERR_INVALID_ARGUMENT                           # o aliases the pool
+
+
+def test_backward_validation(L):
+    E = _lib
+    assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 8 * 32 * 32 * 4
+    assert L.kda_chunk_bwd_workspace_size(2, 9, 3, 128, 64, 0) == 2 * 3 * 2 * 128 * 64 * 4
+    assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
+    bwd = lambda ws=Q[14], wsb=1 << 20, dq=Q[8], T=64, dk=32, dt=1, S0=None: L.kda_chunk_bwd(
+        Q[0], Q[1], Q[2], Q[3], Q[4], S0, Q[6], None, dq, Q[9], Q[10], Q[11], Q[12], None,
+        ws, wsb, 1, T, 1, dk, 32, dt, None)
+    assert bwd(dq=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(ws=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(wsb=100) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
+    assert bwd(dk=48) == E.KDA_ERR_UNSUPPORTED
+    assert bwd(dt=5) == E.KDA_ERR_UNSUPPORTED
+    assert bwd(T=0) == E.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(dq=Q[0]) == E.KDA_ERR_INVALID_ARGUMENT         # output aliases q
+    assert bwd(S0=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
