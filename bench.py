@@ -461,8 +461,9 @@ EXTRA_TRACES = {
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
     "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
                  "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (1 warm-up + 2 "
-                 "timed calls): bwd_ckpt_kernel (forward with a checkpoint every 8 tokens) and "
-                 "bwd_kernel (reverse walk) per call."),
+                 "timed calls): per call bwd_ckpt_kernel (forward with a state checkpoint every 8 "
+                 "tokens), bwd_kernel (reverse walk, one workgroup per chain and 32-column value "
+                 "slice) and bwd_sum_kernel (sums the slices' partial key-side gradients)."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (2 warm-up + 3 timed calls) and with the position-pair "
@@ -524,7 +525,7 @@ def ingest_trace_extra(name, d):
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel",
-                                                           "bwd_ckpt_kernel", "bwd_kernel"))]
+                                                           "bwd_ckpt_kernel", "bwd_kernel", "bwd_sum_kernel"))]
     chunk_rows = [r for r in rows if "chunk32_kernel" in r["Kernel_Name"]]
     groups = {}
     for r in rows:

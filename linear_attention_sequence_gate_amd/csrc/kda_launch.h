@@ -52,9 +52,10 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
 hipError_t launch_pool_reset(float *pool, const int *slots, int64_t n, int64_t n_slots,
                              int64_t per_slot, hipStream_t s);
 
-// Reverse mode of the recurrence (token by token, states recomputed from
-// checkpoints every 8 tokens kept in `ckpt`, bwd_workspace_bytes() long).
-// Gradients are fp32; dST and dS0 may be null.
+// Reverse mode of the recurrence (token by token over 32-column slices,
+// states recomputed from checkpoints every 8 tokens; `ckpt` is the
+// workspace, bwd_workspace_bytes() long).  Gradients are fp32; dST and dS0
+// may be null.
 hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, const void *dout, const float *dST,
                             float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,

@@ -207,7 +207,10 @@ def test_pool_validation(L):
 def test_backward_validation(L):
     E = _lib
     assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 8 * 32 * 32 * 4
-    assert L.kda_chunk_bwd_workspace_size(2, 9, 3, 128, 64, 0) == 2 * 3 * 2 * 128 * 64 * 4
+    # checkpoints (2 per chain) plus, with two 32-column slices, their partial
+    # row gradients (dq, dk, dg, dbeta) per token row
+    assert L.kda_chunk_bwd_workspace_size(2, 9, 3, 128, 64, 0) == (
+        2 * 3 * 2 * 128 * 64 * 4 + 2 * (2 * 9 * 3) * (3 * 128 + 1) * 4)
     assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
     bwd = lambda ws=Q[14], wsb=1 << 20, dq=Q[8], T=64, dk=32, dt=1, S0=None: L.kda_chunk_bwd(
