@@ -256,16 +256,23 @@ def time_pairwise_diagonal(reps=3):
     return out
 
 
-FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, vendor figure
-# reverse mode, fp32 flops per head-token counted once (no recomputation):
-# the forward step (decay, k projection, write: 5 d^2) and the reverse step
-# (q do^T, dq, du, dk (two terms), dS', the decay sum, dS = a dS', S_t: 18 d^2)
-BWD_FLOPS_PER_D2 = 23
+FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 (matrix and vector), vendor figure
+BWD_CHUNK = 16
+# chunked reverse mode, flops per head-token with every product counted once
+# (C = 16-token chunks, d = dk = dv):
+#   d^2 terms: forward state pass K~S, K^T U (4); reverse pass K^ dN, Q~^T dO,
+#              K~^T dW (6); dQ~ = dO S^T, dK~ = dW S^T, dK^ = U dN^T (6)
+#   C d terms: At, P (4); U, dU's P^T dO, dW (6); dT, dP (4); pair terms dQ',
+#              dK', dK" (two) (8)
+def bwd_chunk_flops(d):
+    return 16 * d * d + 22 * BWD_CHUNK * d
 
 
-def time_backward(reps=2):
+def time_backward(reps=3):
     """kda_chunk_bwd on B4 H32 d128 bf16 with T = 4096 (the benchmark's chain
-    count; T cut so the checkpoints, 64 KiB per 8 tokens per chain, take 4 GiB)."""
+    count; T cut so the workspace -- the state entering and the gradient
+    leaving each 16-token chunk, 2 x 64 KiB per 16 tokens per chain -- takes
+    4 GiB), on the chunked path; the token-level path timed beside it."""
     B, T, H, d = 4, 4096, 32, 128
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02)
@@ -273,26 +280,32 @@ def time_backward(reps=2):
     d_o = torch.randn(B, T, H, d, device=dev).to(torch.bfloat16)
     ws = torch.empty(_lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, 1), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    run = lambda: _lib.kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, None,
-                                     workspace=ws, stream=stream)
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+
+    def timed(flags, n):
+        run = lambda: _lib.kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, None,
+                                         workspace=ws, flags=flags, stream=stream)
         run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(0, reps)
+    ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1)
     ht = B * T * H
-    tflops = BWD_FLOPS_PER_D2 * d * d * ht / (ms / 1e3) / 1e12
+    tflops = bwd_chunk_flops(d) * ht / (ms / 1e3) / 1e12
     del x, g, d_o, ws
     torch.cuda.empty_cache()
     return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16 (gradients fp32)",
-            "head_tokens_per_s": ht / (ms / 1e3),
-            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
+            "head_tokens_per_s": ht / (ms / 1e3), "token_path_ms": ms_token,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS,
-                         "flops_per_head_token": BWD_FLOPS_PER_D2 * d * d}}
+                         "flops_per_head_token": bwd_chunk_flops(d),
+                         "scope": "whole call (four launches), fp32 matrix-core peak"}}
 
 
 def time_decode(nsteps=1000, warmup=20):
@@ -460,10 +473,12 @@ EXTRA_TRACES = {
              "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
     "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
-                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (1 warm-up + 2 "
-                 "timed calls): per call bwd_ckpt_kernel (forward with a state checkpoint every 8 "
-                 "tokens), bwd_kernel (reverse walk, one workgroup per chain and 32-column value "
-                 "slice) and bwd_sum_kernel (sums the slices' partial key-side gradients)."),
+                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16: the chunked path "
+                 "(1 warm-up + 3 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
+                 "chunk), cb_fwd_kernel (state entering each chunk), cb_bwd_kernel (gradient "
+                 "leaving each chunk) and cb_grad_kernel (token gradients, all chunks at once)), "
+                 "then the token-level path (1 warm-up + 1 timed call; bwd_ckpt_kernel, "
+                 "bwd_kernel, bwd_sum_kernel)."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (2 warm-up + 3 timed calls) and with the position-pair "
@@ -525,7 +540,9 @@ def ingest_trace_extra(name, d):
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel",
-                                                           "bwd_ckpt_kernel", "bwd_kernel", "bwd_sum_kernel"))]
+                                                           "bwd_ckpt_kernel", "bwd_kernel", "bwd_sum_kernel",
+                                                           "cb_prep_kernel", "cb_fwd_kernel", "cb_bwd_kernel",
+                                                           "cb_grad_kernel"))]
     chunk_rows = [r for r in rows if "chunk32_kernel" in r["Kernel_Name"]]
     groups = {}
     for r in rows:

@@ -60,7 +60,7 @@ enum {
     KDA_ERR_RANGE = -4             /* KDA_FLAG_CHECK_RANGE found g outside [-5, 0] or a 16-token sum < -80 */
 };
 
-/* Flags for kda_chunk_fwd. */
+/* Flags for kda_chunk_fwd (and, where noted, kda_chunk_bwd). */
 enum {
     /* Before the forward pass, check on the device that every g lies in
      * [-5, 0] and every 16-token tile sum (tiles aligned to token 0 of the
@@ -81,7 +81,11 @@ enum {
      * split, n >= 2 = split into n segments (the count a 32-token-aligned
      * segment length gives).  See kda_chunk_fwd. */
     KDA_FLAG_SEGMENTS_SHIFT = 8,
-    KDA_FLAG_SEGMENTS_MASK = 0xff00u
+    KDA_FLAG_SEGMENTS_MASK = 0xff00u,
+    /* kda_chunk_bwd only: take the token-level reverse mode, which assumes
+     * nothing about the decay range (any g <= 0), instead of the chunked one.
+     * Slower. */
+    KDA_FLAG_TOKEN_BACKWARD = 0x10000u
 };
 #define KDA_FLAG_SEGMENTS(n) ((unsigned)(n) << KDA_FLAG_SEGMENTS_SHIFT)
 
@@ -196,17 +200,23 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
  * is the one of "Kimi K3 internal structure analysis", section "Sequence
  * mixing: 3 KDA layers per global MLA layer" (retention, delta-rule write,
  * read after the write); the pages say nothing of training, so the reverse
- * mode is derived from that step.  Token by token: one workgroup per chain
- * stores the state every 8 tokens in the workspace, then walks the tokens
- * backwards, recomputing the state before each from its checkpoint.
+ * mode is derived from that step.
+ * Default path: 16-token chunks with fp32 matrix-core products -- the state
+ * entering each chunk (forward pass) and the gradient leaving it (reverse
+ * pass) go to the workspace, then every chunk's token gradients are formed
+ * at once.  It relies on the range the gate floor guarantees (every 16-token
+ * sum of g from the sequence start >= -80; KDA_FLAG_CHECK_RANGE verifies it
+ * as kda_chunk_fwd does).  KDA_FLAG_TOKEN_BACKWARD selects the token-level
+ * reverse mode (state checkpoints every 8 tokens), which takes any g <= 0.
  *   d_o             : [B, T, H, dv] dtype
  *   d_final_state   : [B, H, dk, dv] fp32, or NULL (zero)
  *   dq, dk, dg      : [B, T, H, dk] fp32 (outputs)
  *   dv              : [B, T, H, dv] fp32 (output)
  *   dbeta           : [B, T, H]     fp32 (output)
  *   d_initial_state : [B, H, dk, dv] fp32, or NULL if not wanted
- *   workspace       : kda_chunk_bwd_workspace_size() bytes (the checkpoints)
- * Outputs must not alias inputs.  g is taken as given (any value <= 0).
+ *   workspace       : kda_chunk_bwd_workspace_size() bytes (either path)
+ *   flags           : KDA_FLAG_CHECK_RANGE (chunked path only), KDA_FLAG_TOKEN_BACKWARD
+ * Outputs must not alias inputs.  KDA_ERR_RANGE as for kda_chunk_fwd.
  */
 size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
                                     int64_t dk, int64_t dv, int dtype);
@@ -215,7 +225,7 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
                   const float *d_final_state, float *dq, float *dk, float *dv, float *dg,
                   float *dbeta, float *d_initial_state, void *workspace, size_t workspace_bytes,
                   int64_t B, int64_t T, int64_t H, int64_t dk_dim, int64_t dv_dim,
-                  int dtype, void *stream);
+                  int dtype, unsigned flags, void *stream);
 
 /*
  * State pool for serving ("Kimi K3 internal structure analysis", section

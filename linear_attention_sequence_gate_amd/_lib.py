@@ -26,6 +26,7 @@ KDA_FLAG_CHECK_RANGE = 1
 KDA_FLAG_PAIRWISE_DIAGONAL = 2
 KDA_FLAG_SEGMENTS_SHIFT = 8
 KDA_FLAG_SEGMENTS_MASK = 0xFF00
+KDA_FLAG_TOKEN_BACKWARD = 0x10000
 
 
 def kda_flag_segments(n: int) -> int:
@@ -83,7 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_varlen_pooled.restype = c_int
     L.kda_chunk_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
-    L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int, vp]
+    L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int,
+                                            ctypes.c_uint, vp]
     L.kda_chunk_bwd.restype = c_int
     L.kda_decode_step_pooled.restype = c_int
     L.kda_last_error.argtypes = []
@@ -281,10 +283,12 @@ def kda_chunk_bwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype
 
 
 def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
-                  want_d_initial_state: bool = True, workspace=None, stream=None) -> dict:
+                  want_d_initial_state: bool = True, workspace=None, flags: int = 0,
+                  stream=None) -> dict:
     """Gradients of <o, d_o> + <S_T, d_final_state> through kda_chunk_fwd's
     recurrence.  Returns dict dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta
-    [B,T,H] and d_initial_state [B,H,dk,dv] (fp32; the last None if not wanted)."""
+    [B,T,H] and d_initial_state [B,H,dk,dv] (fp32; the last None if not wanted).
+    flags: KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD (token-level path)."""
     _dev(q, k, v, g, beta, initial_state, d_o, d_final_state, workspace)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -301,5 +305,6 @@ def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
         _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
         _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), B, T, H, dk, dv, dt, _stream(stream)))
+        workspace.numel() * workspace.element_size(), B, T, H, dk, dv, dt, flags,
+        _stream(stream)))
     return out

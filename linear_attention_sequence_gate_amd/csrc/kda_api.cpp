@@ -318,16 +318,25 @@ size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     int64_t n = B;
     if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk) || !mul_ok(n, dv)) return 0;
-    return kda::bwd_workspace_bytes(B, T, H, (int)dk, (int)dv);
+    // the range-check counter, then the larger of the two paths' buffers
+    const size_t tok = kda::bwd_workspace_bytes(B, T, H, (int)dk, (int)dv);
+    const size_t chk = kda::cbwd_workspace_bytes(B, T, H, (int)dk, (int)dv);
+    return kCounterBytes + (tok > chk ? tok : chk);
 }
 
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
                   const float *initial_state, const void *d_o, const float *d_final_state,
                   float *dq, float *dk, float *dv, float *dg, float *dbeta,
                   float *d_initial_state, void *workspace, size_t workspace_bytes, int64_t B,
-                  int64_t T, int64_t H, int64_t dk_dim, int64_t dv_dim, int dtype, void *stream) {
+                  int64_t T, int64_t H, int64_t dk_dim, int64_t dv_dim, int dtype, unsigned flags,
+                  void *stream) {
     const char *who = "kda_chunk_bwd";
     if (int e = check_dtype(dtype)) return e;
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_TOKEN_BACKWARD))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
+    const bool token = (flags & KDA_FLAG_TOKEN_BACKWARD) != 0;
+    if (token && (flags & KDA_FLAG_CHECK_RANGE))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the token-level path assumes no decay range to check", who);
     if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta || !workspace)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (all but initial_state, "
                     "d_final_state and d_initial_state are required)", who);
@@ -340,7 +349,7 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
     if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk_dim) || !mul_ok(n, dv_dim))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: element count overflows", who);
     if (B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H too large", who);
-    const size_t need = kda::bwd_workspace_bytes(B, T, H, (int)dk_dim, (int)dv_dim);
+    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, dk_dim, dv_dim, dtype);
     if (workspace_bytes < need)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of %zu bytes", who, need);
     const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
@@ -354,11 +363,29 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
         for (const void *pi : ins)
             if (po && po == pi)
                 return fail(KDA_ERR_INVALID_ARGUMENT, "%s: outputs must not alias inputs", who);
-    hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state, dq,
-                                         dk, dv, dg, dbeta, d_initial_state,
-                                         static_cast<float *>(workspace), B, T, H, (int)dk_dim,
-                                         (int)dv_dim, dtype == KDA_BF16,
-                                         static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & KDA_FLAG_CHECK_RANGE) {
+        unsigned int *bad = static_cast<unsigned int *>(workspace);
+        hipError_t e = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd range check memset");
+        e = kda::launch_range_check(g, B, T, H, dk_dim, bad, s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd range check launch");
+        unsigned int nbad = 0;
+        e = hipMemcpyAsync(&nbad, bad, sizeof nbad, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd range check readback");
+        if (nbad)
+            return fail(KDA_ERR_RANGE, "%s: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]", who,
+                        nbad);
+    }
+    float *ws = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+    hipError_t e =
+        token ? kda::launch_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv,
+                                      dg, dbeta, d_initial_state, ws, B, T, H, (int)dk_dim,
+                                      (int)dv_dim, dtype == KDA_BF16, s)
+              : kda::launch_chunk_bwd_chunked(q, k, v, g, beta, initial_state, d_o, d_final_state, dq,
+                                              dk, dv, dg, dbeta, d_initial_state, ws, B, T, H,
+                                              (int)dk_dim, (int)dv_dim, dtype == KDA_BF16, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd launch");
     return ok();
 }

@@ -1,0 +1,763 @@
+// Chunkwise reverse mode of the KDA recurrence: 16-token chunks, every product
+// on the fp32 matrix cores (v_mfma_f32_16x16x4f32), so the gradients keep fp32
+// accuracy.
+//
+// The forward step is the one of "Kimi K3 internal structure analysis",
+// section "Sequence mixing: 3 KDA layers per global MLA layer" (retention,
+// delta-rule write, read after the write).  The pages say nothing of
+// training; the reverse mode below is derived from the chunk form of that
+// step.  For one chain and one chunk of C = 16 tokens, with S the state
+// entering it, b_r the running sum of g inside the chunk, m = b_7 and
+// b_C = b_15 (per key channel):
+//     K~ = k e^b, Q~ = q e^b, K^ = k e^{b_C - b}            (all <= 1)
+//     K' = k e^{b-m}, Q' = q e^{b-m}, K" = k e^{m-b}         (<= e^40 each)
+//     At = K' K"^T,  A = strict_lower(Diag(beta) At),  P = lower(Q' K"^T)
+//     X  = (I + A)^-1,  W = V - K~ S,  U = X Diag(beta) W
+//     O  = Q~ S + P U,  S_next = Diag(e^{b_C}) S + K^^T U
+// Referencing the pair factors to the middle token keeps each operand within
+// e^{+-40} when the 16-token decay sum is >= -80 (the gate floor's bound), so
+// K' K"^T = sum k k e^{b_r - b_s} is formed with no overflow.
+//
+// Reverse, given dO and dN = dL/dS_next:
+//     dU = P^T dO + K^ dN,   dW = Diag(beta) X^T dU,   dv = dW
+//     dS = Diag(e^{b_C}) dN + Q~^T dO - K~^T dW                (to the previous chunk)
+//     dT = dU W^T,   dX = dT Diag(beta),   dbeta_s += sum_r X_rs dT_rs
+//     dA = strict_lower(-X^T dX X^T),   dbeta_r += sum_s dA_rs At_rs,   dAt = Diag(beta) dA
+//     dP = lower(dO U^T)
+//     dQ' = dP K",  dK' = dAt K",  dK" = dAt^T K' + dP^T Q'
+//     dQ~ = dO S^T,  dK~ = -dW S^T,  dK^ = U dN^T
+//     dq = dQ~ e^b + dQ' e^{b-m}
+//     dk = dK~ e^b + dK^ e^{b_C-b} + dK' e^{b-m} + dK" e^{m-b}
+//     db = dQ~ Q~ + dK~ K~ - dK^ K^ + dQ' Q' + dK' K' - dK" K"   (per token)
+//     db_C += sum_r dK^ K^ + e^{b_C} rowsum(S * dN)
+//     dg_t = sum_{r >= t} db_r
+// (m cancels from every output, so its gradient is zero and is not formed.)
+//
+// Four launches:
+//   cb_prep_kernel   one wave per chunk: At, P, X (16x16 each) and the decayed
+//                    operands K~, K^, Q~, e^{b_C} to the workspace
+//   cb_fwd_kernel    per (chain, 16-column slice), chunks in order: the state
+//                    entering each chunk and W to the workspace
+//   cb_bwd_kernel    per (chain, slice), chunks in reverse: dN of each chunk,
+//                    dU, and d(initial state)
+//   cb_grad_kernel   one workgroup per chunk, all chunks at once: every
+//                    token gradient from (S, dN, W, dU, At, X)
+// The two passes carry their state slice in MFMA accumulator registers (lane
+// l holds rows 4(l/16)+i, column l%16 of each 16x16 tile), which is also a
+// valid B operand of the next product once the contraction index is taken in
+// the same order on both operands.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int kCB = 16;                          // tokens per chunk
+constexpr int kCbMat = 3 * kCB * kCB;            // X, P, At per chunk
+
+struct CbArgs {
+    const void *q, *k, *v, *beta, *dout;
+    const float *g, *S0, *dST;
+    float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+    float *st;                                   // [nbh][nc][DK][DV]  state entering each chunk
+    float *dn;                                   // [nbh][nc][DK][DV]  gradient leaving each chunk
+    float *mat;                                  // [nbh][nc][3][16][16]  X, P, At
+    float *ops;                                  // [nbh][nc][cb_ops_floats(DK)]  decayed operands
+    float *w;                                    // [nbh][nc][16][DV]
+    float *du;                                   // [nbh][nc][16][DV]
+    int64_t T;
+    int H, DV, nc, nsl;
+};
+
+// Decayed operands of one chunk, in the layouts the two state passes copy to
+// LDS unchanged: K~ [16][DK], K~^T [DK][16], K^ [16][DK], K^^T [DK][16],
+// Q~^T [DK][16] and e^{b_C} [DK].
+__host__ __device__ constexpr int cb_ops_floats(int DK) { return 81 * DK; }
+enum { kOpKt = 0, kOpKtT = 16, kOpKh = 32, kOpKhT = 48, kOpQtT = 64, kOpEbc = 80 };  // x DK
+
+template <typename T> __device__ __forceinline__ float cb_ld(const void *p, int64_t i) {
+    return to_f32(static_cast<const T *>(p)[i]);
+}
+
+__device__ __forceinline__ floatx4 mfma1(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Row of token 0 of chain bh in the [B, T, H] token layout; token t of the
+// chain is row cb_rowbase + t * H.
+__device__ __forceinline__ int64_t cb_rowbase(const CbArgs &a, int64_t bh) {
+    return (bh / a.H) * a.T * a.H + bh % a.H;
+}
+
+// The 16 values of one channel over the chunk's tokens: element `off` of
+// rows rowbase + (t0 + r) H, row length `ld`.  Padded tokens past the end
+// (r >= n) read the last valid row and are then zeroed, so every load is
+// unconditional and all 16 are in flight together.
+template <typename T>
+__device__ __forceinline__ void cb_load16(const void *p, int64_t rowbase, int64_t t0, int n, int H,
+                                          int ld, int off, float (&x)[kCB]) {
+#pragma unroll
+    for (int r = 0; r < kCB; ++r) {
+        const int rr = r < n ? r : n - 1;
+        x[r] = cb_ld<T>(p, (rowbase + (t0 + rr) * H) * ld + off);
+    }
+#pragma unroll
+    for (int r = 0; r < kCB; ++r) x[r] = r < n ? x[r] : 0.f;
+}
+
+// Running log-decay of one key channel over the chunk (g = 0 past the end).
+__device__ __forceinline__ void cb_cumsum(const float (&gv)[kCB], float (&b)[kCB]) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < kCB; ++r) {
+        s += gv[r];
+        b[r] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// At, P, X of one chunk.  One wave.
+// ---------------------------------------------------------------------------
+template <typename T, int DK>
+__global__ __launch_bounds__(64) void cb_prep_kernel(CbArgs a) {
+    constexpr int LD = DK + 4;
+    __shared__ __attribute__((aligned(16))) float Kp[kCB][LD], Kpp[kCB][LD], Qp[kCB][LD];
+    __shared__ float Am[kCB][kCB + 1], bet[kCB];
+    const int64_t unit = blockIdx.x;
+    const int64_t bh = unit / a.nc;
+    const int c = (int)(unit % a.nc);
+    const int64_t t0 = (int64_t)c * kCB;
+    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+    const int lane = threadIdx.x, j = lane & 15, g4 = lane >> 4;
+    const int64_t rb = cb_rowbase(a, bh);
+    for (int ch = lane; ch < DK; ch += 64) {
+        float gv[kCB], kv[kCB], qv[kCB], b[kCB];
+        cb_load16<float>(a.g, rb, t0, n, a.H, DK, ch, gv);
+        cb_load16<T>(a.k, rb, t0, n, a.H, DK, ch, kv);
+        cb_load16<T>(a.q, rb, t0, n, a.H, DK, ch, qv);
+        cb_cumsum(gv, b);
+        const float m = b[7], bc = b[kCB - 1];
+        float *op = a.ops + unit * cb_ops_floats(DK);
+        float kt[kCB], kh[kCB], qt[kCB];
+#pragma unroll
+        for (int r = 0; r < kCB; ++r) {
+            const float e = expf(b[r] - m), ei = expf(m - b[r]), eb = expf(b[r]);
+            Kp[r][ch] = kv[r] * e;
+            Kpp[r][ch] = kv[r] * ei;
+            Qp[r][ch] = qv[r] * e;
+            kt[r] = kv[r] * eb;
+            kh[r] = kv[r] * expf(bc - b[r]);
+            qt[r] = qv[r] * eb;
+            op[kOpKt * DK + r * DK + ch] = kt[r];
+            op[kOpKh * DK + r * DK + ch] = kh[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kCB; r += 4) {
+            *reinterpret_cast<floatx4 *>(op + kOpKtT * DK + ch * kCB + r) =
+                floatx4{kt[r], kt[r + 1], kt[r + 2], kt[r + 3]};
+            *reinterpret_cast<floatx4 *>(op + kOpKhT * DK + ch * kCB + r) =
+                floatx4{kh[r], kh[r + 1], kh[r + 2], kh[r + 3]};
+            *reinterpret_cast<floatx4 *>(op + kOpQtT * DK + ch * kCB + r) =
+                floatx4{qt[r], qt[r + 1], qt[r + 2], qt[r + 3]};
+        }
+        op[kOpEbc * DK + ch] = expf(bc);
+    }
+    if (lane < kCB) bet[lane] = (lane < n) ? cb_ld<T>(a.beta, rb + (t0 + lane) * a.H) : 0.f;
+    __syncthreads();
+    floatx4 at = {0, 0, 0, 0}, pp = {0, 0, 0, 0};
+    tile_mma<float>(at, &Kp[0][0], LD, &Kpp[0][0], LD, DK, lane);   // at[i] = At[4g4+i][j]
+    tile_mma<float>(pp, &Qp[0][0], LD, &Kpp[0][0], LD, DK, lane);
+    float *mat = a.mat + unit * kCbMat;          // X, P, At
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i;
+        const float atv = (j < r) ? at[i] : 0.f;  // selects: the masked entries may be large
+        mat[2 * kCB * kCB + r * kCB + j] = atv;
+        mat[kCB * kCB + r * kCB + j] = (j <= r) ? pp[i] : 0.f;
+        Am[r][j] = bet[r] * atv;
+    }
+    __syncthreads();
+    // X = (I + A)^-1 by forward substitution, one column per lane.
+    if (lane < kCB) {
+        float x[kCB];
+#pragma unroll
+        for (int r = 0; r < kCB; ++r) {
+            float s = (r == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int q = 0; q < r; ++q) s -= Am[r][q] * x[q];
+            x[r] = s;
+            mat[r * kCB + lane] = s;
+        }
+    }
+}
+
+// block -> (chain, 16-column slice); the slices of a chain share an XCD (and
+// its L2) when the chain count is a multiple of 8.
+__device__ __forceinline__ void cb_slice_block(const CbArgs &a, int64_t nbh, int64_t &bh, int &sl) {
+    const int64_t x = blockIdx.x;
+    if (nbh % 8 == 0) {
+        bh = (x / (8 * a.nsl)) * 8 + x % 8;
+        sl = (int)((x / 8) % a.nsl);
+    } else {
+        bh = x / a.nsl;
+        sl = (int)(x % a.nsl);
+    }
+}
+
+// LDS of the two state passes, double-buffered over chunks.
+template <int DK> struct alignas(16) CbPassLds {
+    float rowm[2][kCB][DK + 4];                  // fwd: K~    bwd: K^          [token][channel]
+    float colm1[2][DK][kCB + 4];                 // fwd: K^ T  bwd: Q~ T       [channel][token]
+    float colm2[2][DK][kCB + 4];                 //            bwd: K~ T
+    float ebc[2][DK];                            // e^{b_C}
+    float vo[2][kCB][kCB + 1];                   // fwd: V slice  bwd: dO slice
+    float X[2][kCB][kCB + 4];
+    float P[2][kCB][kCB + 1];
+    float bet[2][kCB];
+    float red[4][kCB][kCB + 1];
+};
+
+// One chunk's inputs of a state pass, fetched into registers a chunk ahead
+// of their use (the passes are sequential over chunks, so their load latency
+// would otherwise be paid once per chunk).
+template <int DK> struct CbStage {
+    static constexpr int NF = (4 * DK + 255) / 256;   // float4 of one [16][DK] array per thread
+    floatx4 r1[NF], r2[NF], r3[NF], e;
+    float vo, x, p, bet;
+};
+
+__device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+
+// fwd: r1 = K~ (row-major), r2 = K^^T; bwd: r1 = K^, r2 = Q~^T, r3 = K~^T.
+// `vsrc` is v (fwd) or dO (bwd).
+template <typename T, int DK, bool BWD>
+__device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int64_t bh, int64_t rb,
+                                         int col0, int c, CbStage<DK> &st) {
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)c * kCB;
+    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+    const float *op = a.ops + (bh * a.nc + c) * cb_ops_floats(DK);
+#pragma unroll
+    for (int u = 0; u < CbStage<DK>::NF; ++u) {
+        const int idx = tid + 256 * u;
+        if (idx < 4 * DK) {
+            st.r1[u] = ld4(op + (BWD ? kOpKh : kOpKt) * DK + 4 * idx);
+            st.r2[u] = ld4(op + (BWD ? kOpQtT : kOpKhT) * DK + 4 * idx);
+            if (BWD) st.r3[u] = ld4(op + kOpKtT * DK + 4 * idx);
+        }
+    }
+    if (tid < DK / 4) st.e = ld4(op + kOpEbc * DK + 4 * tid);
+    const int r = tid >> 4, cc = tid & 15, rr = r < n ? r : n - 1;
+    st.vo = cb_ld<T>(vsrc, (rb + (t0 + rr) * a.H) * a.DV + col0 + cc);
+    const float *mc = a.mat + (bh * a.nc + c) * kCbMat;
+    st.x = mc[r * kCB + cc];
+    if (BWD) st.p = mc[kCB * kCB + r * kCB + cc];
+    const int tb = (tid & 15) < n ? (tid & 15) : n - 1;
+    st.bet = cb_ld<T>(a.beta, rb + (t0 + tb) * a.H);
+}
+
+template <int DK, bool BWD>
+__device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<DK> &st, int buf,
+                                                int n) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < CbStage<DK>::NF; ++u) {
+        const int idx = tid + 256 * u;
+        if (idx < 4 * DK) {
+            const int f = 4 * idx;
+            *reinterpret_cast<floatx4 *>(&L.rowm[buf][f / DK][f % DK]) = st.r1[u];
+            *reinterpret_cast<floatx4 *>(&L.colm1[buf][f / kCB][f % kCB]) = st.r2[u];
+            if (BWD) *reinterpret_cast<floatx4 *>(&L.colm2[buf][f / kCB][f % kCB]) = st.r3[u];
+        }
+    }
+    if (tid < DK / 4) *reinterpret_cast<floatx4 *>(&L.ebc[buf][4 * tid]) = st.e;
+    const int r = tid >> 4, cc = tid & 15;
+    L.vo[buf][r][cc] = r < n ? st.vo : 0.f;
+    L.X[buf][r][cc] = st.x;
+    if (BWD) L.P[buf][r][cc] = st.p;
+    if (tid < kCB) L.bet[buf][tid] = tid < n ? st.bet : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Forward state pass: the state entering every chunk, and W = V - K~ S.
+// ---------------------------------------------------------------------------
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    __shared__ CbPassLds<DK> L;
+    int64_t bh;
+    int sl;
+    cb_slice_block(a, nbh, bh, sl);
+    const int64_t rb = cb_rowbase(a, bh);
+    const int col0 = sl * 16;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    floatx4 s[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[u][i] = (a.S0 && tt < RT)
+                          ? a.S0[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] : 0.f;
+    }
+    CbStage<DK> stg;
+    cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, 0, stg);
+    for (int c = 0; c < a.nc; ++c) {
+        const int buf = c & 1;
+        const int64_t t0 = (int64_t)c * kCB;
+        const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+        cb_stage_to_lds<DK, false>(L, stg, buf, n);
+        cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, c + 1 < a.nc ? c + 1 : c, stg);
+        float *stc = a.st + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) stc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV] = s[u][i];
+            }
+        }
+        __syncthreads();
+        // this wave's rows of K~ S
+        floatx4 wp = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+                const floatx4 kt = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wp = mfma1(kt[i], s[u][i], wp);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][j] = wp[i];
+        __syncthreads();
+        floatx4 W;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            W[i] = L.vo[buf][r][j] - (L.red[0][r][j] + L.red[1][r][j] + L.red[2][r][j] + L.red[3][r][j]);
+        }
+        if (wave == 0) {
+            float *wc = a.w + ((bh * a.nc + c) * kCB) * a.DV + col0 + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wc[(int64_t)(4 * g4 + i) * a.DV] = W[i];
+        }
+        // U = X Diag(beta) W
+        floatx4 U = {0, 0, 0, 0};
+        const floatx4 xr = ld4(&L.X[buf][j][4 * g4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U = mfma1(xr[i], L.bet[buf][4 * g4 + i] * W[i], U);
+        // S <- Diag(e^{b_C}) S + K^^T U
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[u][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
+                const floatx4 kh = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[u] = mfma1(kh[i], U[i], s[u]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state pass: dN of every chunk, dU, and d(initial state).
+// ---------------------------------------------------------------------------
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    __shared__ CbPassLds<DK> L;
+    int64_t bh;
+    int sl;
+    cb_slice_block(a, nbh, bh, sl);
+    const int64_t rb = cb_rowbase(a, bh);
+    const int col0 = sl * 16;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    floatx4 d[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d[u][i] = (a.dST && tt < RT)
+                          ? a.dST[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] : 0.f;
+    }
+    CbStage<DK> stg;
+    cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, a.nc - 1, stg);
+    for (int c = a.nc - 1; c >= 0; --c) {
+        const int buf = c & 1;
+        const int64_t t0 = (int64_t)c * kCB;
+        const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+        cb_stage_to_lds<DK, true>(L, stg, buf, n);
+        cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, c > 0 ? c - 1 : 0, stg);
+        float *dnc = a.dn + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dnc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV] = d[u][i];
+            }
+        }
+        __syncthreads();
+        // this wave's rows of K^ dN (wave 0 adds P^T dO)
+        floatx4 up = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+                const floatx4 kh = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) up = mfma1(kh[i], d[u][i], up);
+            }
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                up = mfma1(L.P[buf][4 * g4 + i][j], L.vo[buf][4 * g4 + i][j], up);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][j] = up[i];
+        __syncthreads();
+        floatx4 dU;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            dU[i] = L.red[0][r][j] + L.red[1][r][j] + L.red[2][r][j] + L.red[3][r][j];
+        }
+        if (wave == 0) {
+            float *duc = a.du + ((bh * a.nc + c) * kCB) * a.DV + col0 + j;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) duc[(int64_t)(4 * g4 + i) * a.DV] = dU[i];
+        }
+        // dW = Diag(beta) X^T dU
+        floatx4 dW = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dW = mfma1(L.X[buf][4 * g4 + i][j], dU[i], dW);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dW[i] *= -L.bet[buf][4 * g4 + i];   // -dW: enters with K~^T
+        // dN <- Diag(e^{b_C}) dN + Q~^T dO - K~^T dW
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[u][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
+                const floatx4 qt = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
+                const floatx4 kt = ld4(&L.colm2[buf][16 * tt + j][4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[u] = mfma1(qt[i], L.vo[buf][4 * g4 + i][j], d[u]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[u] = mfma1(kt[i], dW[i], d[u]);
+            }
+        }
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.dS0[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] = d[u][i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Token gradients of one chunk.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct alignas(16) CbGradLds {
+    static constexpr int LK = DK + 4, LV = DV + 4, LS = kCB + 4;
+    float q[kCB][LK], k[kCB][LK], bm[kCB][LK];  // bm = b - m
+    float m[DK], bcm[DK], rs[DK];                // m, b_C - m, rowsum(S * dN)
+    float W[kCB][LV], dU[kCB][LV], dO[kCB][LV], U[kCB][LV], dW[kCB][LV];
+    float X[kCB][LS], At[kCB][LS], dX[kCB][LS], Y[kCB][LS], dP[kCB][LS], dAt[kCB][LS];
+    float bet[kCB];
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
+    using Lds = CbGradLds<DK, DV>;
+    constexpr int RT = DK / 16, CT = DV / 16;
+    __shared__ Lds L;
+    const int64_t unit = blockIdx.x;
+    const int64_t bh = unit / a.nc;
+    const int c = (int)(unit % a.nc);
+    const int64_t t0 = (int64_t)c * kCB;
+    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int64_t rb = cb_rowbase(a, bh);
+    // 1. inputs
+    if (tid < DK) {
+        float gv[kCB], kv[kCB], qv[kCB], b[kCB];
+        cb_load16<float>(a.g, rb, t0, n, a.H, DK, tid, gv);
+        cb_load16<T>(a.k, rb, t0, n, a.H, DK, tid, kv);
+        cb_load16<T>(a.q, rb, t0, n, a.H, DK, tid, qv);
+        cb_cumsum(gv, b);
+        const float m = b[7];
+        L.m[tid] = m;
+        L.bcm[tid] = b[kCB - 1] - m;
+#pragma unroll
+        for (int r = 0; r < kCB; ++r) {
+            L.q[r][tid] = qv[r];
+            L.k[r][tid] = kv[r];
+            L.bm[r][tid] = b[r] - m;
+        }
+    }
+    {
+        const float *wc = a.w + unit * kCB * DV;
+        const float *duc = a.du + unit * kCB * DV;
+        for (int e = tid; e < kCB * DV / 4; e += 256) {
+            const int r = (4 * e) / DV, cc = (4 * e) % DV;
+            *reinterpret_cast<floatx4 *>(&L.W[r][cc]) = *reinterpret_cast<const floatx4 *>(wc + 4 * e);
+            *reinterpret_cast<floatx4 *>(&L.dU[r][cc]) = *reinterpret_cast<const floatx4 *>(duc + 4 * e);
+        }
+        for (int e = tid; e < kCB * DV; e += 256) {
+            const int r = e / DV, cc = e % DV;
+            const int rr = r < n ? r : n - 1;
+            const float ov = cb_ld<T>(a.dout, (rb + (t0 + rr) * a.H) * DV + cc);
+            L.dO[r][cc] = r < n ? ov : 0.f;
+        }
+        const float *mc = a.mat + unit * kCbMat;
+        {
+            const int r = tid >> 4, cc = tid & 15;
+            L.X[r][cc] = mc[r * kCB + cc];
+            L.At[r][cc] = mc[2 * kCB * kCB + r * kCB + cc];
+        }
+        if (tid < kCB) L.bet[tid] = (tid < n) ? cb_ld<T>(a.beta, rb + (t0 + tid) * a.H) : 0.f;
+    }
+    __syncthreads();
+
+    // 2. U = X Diag(beta) W and dW = Diag(beta) X^T dU, column tiles over waves
+    for (int ct = wave; ct < CT; ct += 4) {
+        const int cc = 16 * ct + j;
+        floatx4 U = {0, 0, 0, 0}, dW = {0, 0, 0, 0};
+        const floatx4 xr = *reinterpret_cast<const floatx4 *>(&L.X[j][4 * g4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 4 * g4 + i;
+            U = mfma1(xr[i], L.bet[s] * L.W[s][cc], U);
+            dW = mfma1(L.X[s][j], L.dU[s][cc], dW);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            dW[i] *= L.bet[r];
+            L.U[r][cc] = U[i];
+            L.dW[r][cc] = dW[i];
+            if (r < n) a.dv[(rb + (t0 + r) * a.H) * DV + cc] = dW[i];
+        }
+    }
+    __syncthreads();
+
+    // 3a. the 16x16 chunk matrices (waves 0 and 1)
+    if (wave == 0) {
+        floatx4 dT = {0, 0, 0, 0};
+        tile_mma<float>(dT, &L.dU[0][0], Lds::LV, &L.W[0][0], Lds::LV, DV, lane);  // dT[r][s] = dU_r . W_s
+        float dbT = 0.f;                          // sum_r X_rs dT_rs, column s = j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            dbT += L.X[r][j] * dT[i];
+            L.dX[r][j] = dT[i] * L.bet[j];
+        }
+        dbT += __shfl_xor(dbT, 16);
+        dbT += __shfl_xor(dbT, 32);
+        // Y = dX X^T, then dA = -(X^T Y) below the diagonal
+        floatx4 Yt = {0, 0, 0, 0};
+        tile_mma<float>(Yt, &L.dX[0][0], Lds::LS, &L.X[0][0], Lds::LS, kCB, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.Y[4 * g4 + i][j] = Yt[i];
+        floatx4 Z = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Z = mfma1(L.X[4 * g4 + i][j], L.Y[4 * g4 + i][j], Z);
+        float dbA[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            const float dA = (j < r) ? -Z[i] : 0.f;
+            dbA[i] = dA * L.At[r][j];
+            L.dAt[r][j] = L.bet[r] * dA;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dbA[i] += __shfl_xor(dbA[i], 1);
+            dbA[i] += __shfl_xor(dbA[i], 2);
+            dbA[i] += __shfl_xor(dbA[i], 4);
+            dbA[i] += __shfl_xor(dbA[i], 8);
+        }
+        // row r = 4 g4 + i sits in lane j = r of its column (dbT) and in lanes 16 g4.. (dbA)
+        const float rowpart = dbA[0] * (j % 4 == 0) + dbA[1] * (j % 4 == 1) + dbA[2] * (j % 4 == 2) +
+                              dbA[3] * (j % 4 == 3);
+        // lane 16 g4 + j holds dbA of row 4 g4 + (j % 4); gather row r = lane (< 16)
+        const float dbA_r = __shfl(rowpart, 16 * (lane >> 2) + (lane & 3));
+        if (lane < kCB && lane < n) a.dbeta[(rb + (t0 + lane) * a.H)] = dbT + dbA_r;
+    } else if (wave == 1) {
+        floatx4 dp = {0, 0, 0, 0};
+        tile_mma<float>(dp, &L.dO[0][0], Lds::LV, &L.U[0][0], Lds::LV, DV, lane);  // dO_r . U_s
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            L.dP[r][j] = (j <= r) ? dp[i] : 0.f;
+        }
+    }
+
+    // 3b. the state products, channel tiles over waves
+    floatx4 dQt[(RT + 3) / 4], dKt[(RT + 3) / 4], dKh[(RT + 3) / 4];
+    const float *stc = a.st + unit * DK * DV;
+    const float *dnc = a.dn + unit * DK * DV;
+#pragma unroll
+    for (int u = 0; u < (RT + 3) / 4; ++u) {
+        const int ct = wave + 4 * u;
+        dQt[u] = dKt[u] = dKh[u] = floatx4{0, 0, 0, 0};
+        if (ct < RT) {
+            const int cr = 16 * ct + j;
+            float rsum = 0.f;
+#pragma unroll 4
+            for (int k0 = 0; k0 < DV; k0 += 16) {
+                const floatx4 sv = *reinterpret_cast<const floatx4 *>(stc + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 nv = *reinterpret_cast<const floatx4 *>(dnc + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 o4 = *reinterpret_cast<const floatx4 *>(&L.dO[j][k0 + 4 * g4]);
+                const floatx4 w4 = *reinterpret_cast<const floatx4 *>(&L.dW[j][k0 + 4 * g4]);
+                const floatx4 u4 = *reinterpret_cast<const floatx4 *>(&L.U[j][k0 + 4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dQt[u] = mfma1(o4[i], sv[i], dQt[u]);
+                    dKt[u] = mfma1(w4[i], sv[i], dKt[u]);
+                    dKh[u] = mfma1(u4[i], nv[i], dKh[u]);
+                    rsum += sv[i] * nv[i];
+                }
+            }
+            rsum += __shfl_xor(rsum, 16);
+            rsum += __shfl_xor(rsum, 32);
+            if (g4 == 0) L.rs[cr] = rsum;
+        }
+    }
+    __syncthreads();
+
+    // 4. pair terms and the token gradients of this wave's channel tiles
+#pragma unroll
+    for (int u = 0; u < (RT + 3) / 4; ++u) {
+        const int ct = wave + 4 * u;
+        if (ct >= RT) continue;
+        const int ch = 16 * ct + j;
+        floatx4 dQp = {0, 0, 0, 0}, dKp = {0, 0, 0, 0}, dKpp = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 4 * g4 + i;
+            const float bms = L.bm[s][ch], ks = L.k[s][ch], qs = L.q[s][ch];
+            const float e = expf(bms), ei = expf(-bms);
+            const float kpp = ks * ei, kp = ks * e, qp = qs * e;
+            dQp = mfma1(L.dP[j][s], kpp, dQp);
+            dKp = mfma1(L.dAt[j][s], kpp, dKp);
+            dKpp = mfma1(L.dAt[s][j], kp, dKpp);
+            dKpp = mfma1(L.dP[s][j], qp, dKpp);
+        }
+        const float m = L.m[ch], bcm = L.bcm[ch];
+        float db[4], khk = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            const float bmr = L.bm[r][ch], qv = L.q[r][ch], kv = L.k[r][ch];
+            const float e_bm = expf(bmr), e_mb = expf(-bmr);
+            const float e_b = expf(bmr + m), e_cb = expf(bcm - bmr);
+            const float dq = dQt[u][i] * e_b + dQp[i] * e_bm;
+            const float dk = -dKt[u][i] * e_b + dKh[u][i] * e_cb + dKp[i] * e_bm + dKpp[i] * e_mb;
+            const float kh = dKh[u][i] * kv * e_cb;
+            db[i] = dQt[u][i] * qv * e_b - dKt[u][i] * kv * e_b - kh + dQp[i] * qv * e_bm +
+                    dKp[i] * kv * e_bm - dKpp[i] * kv * e_mb;
+            khk += kh;
+            if (r < n) {
+                const int64_t row = (rb + (t0 + r) * a.H);
+                a.dq[row * DK + ch] = dq;
+                a.dk[row * DK + ch] = dk;
+            }
+        }
+        // suffix sums over the chunk's tokens (rows 4 g4 + i live in lane group g4)
+        khk += __shfl_xor(khk, 16);
+        khk += __shfl_xor(khk, 32);
+        const float extra = khk + expf(bcm + m) * L.rs[ch];
+        db[2] += db[3];
+        db[1] += db[2];
+        db[0] += db[1];
+        const float tot = db[0];
+        const float t1 = __shfl(tot, j + 16), t2 = __shfl(tot, j + 32), t3 = __shfl(tot, j + 48);
+        const float later = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            if (r < n) a.dg[(rb + (t0 + r) * a.H) * DK + ch] = db[i] + later + extra;
+        }
+    }
+}
+
+size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t st = r256((size_t)nbh * nc * dk * dv * sizeof(float));
+    const size_t mat = r256((size_t)nbh * nc * kCbMat * sizeof(float));
+    const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
+    const size_t ops = r256((size_t)nbh * nc * cb_ops_floats(dk) * sizeof(float));
+    return 2 * st + mat + 2 * wv + ops;
+}
+
+template <typename T, int DK>
+static hipError_t cb_inst(CbArgs a, int64_t nbh, hipStream_t s) {
+    hipLaunchKernelGGL((cb_prep_kernel<T, DK>), dim3((unsigned)(nbh * a.nc)), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((cb_fwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((cb_bwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 grid((unsigned)(nbh * a.nc));
+    switch (a.DV) {
+    case 32: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 64>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 128>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                                    const void *beta, const float *S0, const void *dout,
+                                    const float *dST, float *dq, float *dk_, float *dv_, float *dg,
+                                    float *dbeta, float *dS0, float *ws, int64_t B, int64_t T,
+                                    int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
+    if (dv % 16 || dk % 16) return hipErrorInvalidValue;
+    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
+    if (nbh * nc > 0x7fffffffLL) return hipErrorInvalidValue;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    char *p = reinterpret_cast<char *>(ws);
+    CbArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout;
+    a.g = g; a.S0 = S0; a.dST = dST;
+    a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    const size_t st = r256((size_t)nbh * nc * dk * dv * sizeof(float));
+    const size_t mat = r256((size_t)nbh * nc * kCbMat * sizeof(float));
+    const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
+    a.st = reinterpret_cast<float *>(p);
+    a.dn = reinterpret_cast<float *>(p + st);
+    a.mat = reinterpret_cast<float *>(p + 2 * st);
+    a.w = reinterpret_cast<float *>(p + 2 * st + mat);
+    a.du = reinterpret_cast<float *>(p + 2 * st + mat + wv);
+    a.ops = reinterpret_cast<float *>(p + 2 * st + mat + 2 * wv);
+    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / 16;
+    switch (dk) {
+    case 32: return is_bf16 ? cb_inst<bf16, 32>(a, nbh, s) : cb_inst<float, 32>(a, nbh, s);
+    case 64: return is_bf16 ? cb_inst<bf16, 64>(a, nbh, s) : cb_inst<float, 64>(a, nbh, s);
+    case 128: return is_bf16 ? cb_inst<bf16, 128>(a, nbh, s) : cb_inst<float, 128>(a, nbh, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -63,4 +63,14 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const f
                             int is_bf16, hipStream_t s);
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
 
+// Reverse mode in 16-token chunks on the fp32 matrix cores (the gate floor's
+// decay range assumed: every 16-token sum of g from the sequence start is
+// >= -80).  `ws` is cbwd_workspace_bytes() long.
+hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                                    const void *beta, const float *S0, const void *dout,
+                                    const float *dST, float *dq, float *dk, float *dv, float *dg,
+                                    float *dbeta, float *dS0, float *ws, int64_t B, int64_t T,
+                                    int64_t H, int dk_, int dv_, int is_bf16, hipStream_t s);
+size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
+
 }  // namespace kda

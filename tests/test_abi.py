@@ -206,16 +206,29 @@ def test_pool_validation(L):
 
 def test_backward_validation(L):
     E = _lib
-    assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 8 * 32 * 32 * 4
-    # checkpoints (2 per chain) plus, with two 32-column slices, their partial
-    # row gradients (dq, dk, dg, dbeta) per token row
-    assert L.kda_chunk_bwd_workspace_size(2, 9, 3, 128, 64, 0) == (
-        2 * 3 * 2 * 128 * 64 * 4 + 2 * (2 * 9 * 3) * (3 * 128 + 1) * 4)
+    # the range-check counter, then the larger of the two paths' buffers:
+    # token path = state checkpoints every 8 tokens per 32-column slice plus,
+    # with several slices, their partial row gradients (dq, dk, dg, dbeta);
+    # chunked path = state entering and gradient leaving each 16-token chunk,
+    # three 16x16 matrices and the decayed operands (81 dk floats) per chunk,
+    # and W, dU per token
+    def chunked(nbh, T, dk, dv):
+        r = lambda x: (x + 255) // 256 * 256
+        nc = (T + 15) // 16
+        return (2 * r(nbh * nc * dk * dv * 4) + r(nbh * nc * 768 * 4) + 2 * r(nbh * nc * 16 * dv * 4)
+                + r(nbh * nc * 81 * dk * 4))
+    assert chunked(1, 64, 32, 32) > 8 * 32 * 32 * 4
+    assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 256 + chunked(1, 64, 32, 32)
+    token = 2 * 3 * 2 * 128 * 64 * 4 + 2 * (2 * 9 * 3) * (3 * 128 + 1) * 4
+    assert L.kda_chunk_bwd_workspace_size(2, 9, 3, 128, 64, 0) == 256 + max(token, chunked(6, 9, 128, 64))
     assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
     Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
-    bwd = lambda ws=Q[14], wsb=1 << 20, dq=Q[8], T=64, dk=32, dt=1, S0=None: L.kda_chunk_bwd(
+    bwd = lambda ws=Q[14], wsb=1 << 20, dq=Q[8], T=64, dk=32, dt=1, S0=None, flags=0: L.kda_chunk_bwd(
         Q[0], Q[1], Q[2], Q[3], Q[4], S0, Q[6], None, dq, Q[9], Q[10], Q[11], Q[12], None,
-        ws, wsb, 1, T, 1, dk, 32, dt, None)
+        ws, wsb, 1, T, 1, dk, 32, dt, flags, None)
+    assert bwd(flags=4) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "flag" in _lib.kda_last_error()
+    assert bwd(flags=E.KDA_FLAG_TOKEN_BACKWARD | E.KDA_FLAG_CHECK_RANGE) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(dq=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(ws=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(wsb=100) == E.KDA_ERR_INVALID_ARGUMENT

@@ -1,25 +1,31 @@
 """GPU parity of kda_chunk_bwd (reverse mode of the recurrence) against the
-oracle's reverse mode on the same inputs: fp32 and bf16, every (dk, dv) family,
-T around the 8-token checkpoint spacing, with and without the initial state
-and the final-state gradient, and with the gate floor removed."""
+oracle's reverse mode on the same inputs, for both paths (16-token chunks on
+the matrix cores, and token by token): fp32 and bf16, every (dk, dv) family,
+T around the 8-token checkpoint and 16-token chunk spacings, with and without
+the initial state and the final-state gradient, the decay at the gate's
+floor, and (token path) with the floor removed."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from linear_attention_sequence_gate_amd import kda_chunk_bwd
+from linear_attention_sequence_gate_amd import KdaError, kda_chunk_bwd
+from linear_attention_sequence_gate_amd._lib import KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD
 from kda_testutil import TOL, oracle_gate_f32, prefill_device, rho, say
 
 pytestmark = pytest.mark.gpu
 
+PATHS = {"chunked": 0, "token": KDA_FLAG_TOKEN_BACKWARD}
 
-def _run(dtype, B, T, H, dk, dv, seed, s0=True, dst=True, g=None):
+
+def _run(dtype, B, T, H, dk, dv, seed, s0=True, dst=True, g=None, path="chunked"):
     x = prefill_device(B, T, H, dk, dv, dtype, seed, s0_std=0.3 if s0 else 0.0)
     g_f32 = oracle_gate_f32(x["z"], x["A"]) if g is None else g
     gen = torch.Generator(device="cuda").manual_seed(seed + 1)
     d_o = torch.randn(B, T, H, dv, device="cuda", generator=gen).to(dtype)
     dST = torch.randn(B, H, dk, dv, device="cuda", generator=gen) if dst else None
-    out = kda_chunk_bwd(x["q"], x["k"], x["v"], g_f32.cuda(), x["beta"], x["S0"], d_o, dST)
+    out = kda_chunk_bwd(x["q"], x["k"], x["v"], g_f32.cuda(), x["beta"], x["S0"], d_o, dST,
+                        flags=PATHS[path])
     torch.cuda.synchronize()
     ref = oracle.backward_np(x["q"], x["k"], x["v"], g_f32, x["beta"], x["S0"], d_o, dST)
     res = {}
@@ -33,22 +39,42 @@ def _run(dtype, B, T, H, dk, dv, seed, s0=True, dst=True, g=None):
         assert r <= TOL[dtype], (name, r)
 
 
-@pytest.mark.parametrize("T", [1, 8, 9, 37])
-def test_backward_f32_small(T):
-    say("backward f32", T)
-    _run(torch.float32, 2, T, 2, 32, 32, 700 + T)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T", [1, 8, 9, 16, 17, 37])
+def test_backward_f32_small(T, path):
+    say("backward f32", path, T)
+    _run(torch.float32, 2, T, 2, 32, 32, 700 + T, path=path)
 
 
-@pytest.mark.parametrize("dk,dv,T", [(64, 128, 20), (128, 64, 17), (32, 64, 24)])
-def test_backward_f32_shapes(dk, dv, T):
-    say("backward f32", dk, dv, T)
-    _run(torch.float32, 1, T, 2, dk, dv, 710 + T, s0=False)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dk,dv,T", [(64, 128, 20), (128, 64, 17), (32, 64, 24), (128, 128, 48)])
+def test_backward_f32_shapes(dk, dv, T, path):
+    say("backward f32", path, dk, dv, T)
+    _run(torch.float32, 1, T, 2, dk, dv, 710 + T, s0=False, path=path)
 
 
-@pytest.mark.parametrize("dk,dv,T", [(128, 128, 70), (32, 64, 13), (64, 32, 33)])
-def test_backward_bf16(dk, dv, T):
-    say("backward bf16", dk, dv, T)
-    _run(torch.bfloat16, 1, T, 3, dk, dv, 720 + T, dst=False)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dk,dv,T", [(128, 128, 70), (32, 64, 13), (64, 32, 33), (32, 128, 40)])
+def test_backward_bf16(dk, dv, T, path):
+    say("backward bf16", path, dk, dv, T)
+    _run(torch.bfloat16, 1, T, 3, dk, dv, 720 + T, dst=False, path=path)
+
+
+def test_backward_chunked_many_chunks():
+    """Several chains of many 16-token chunks and a ragged tail, bf16, d = 128,
+    in the launch shape of the benchmark (chains a multiple of 8)."""
+    say("backward chunked B2 H4 T301 d128")
+    _run(torch.bfloat16, 2, 301, 4, 128, 128, 740)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_decay_at_the_floor(path):
+    """g = -5 everywhere: every 16-token chunk's decay sum is exactly -80, the
+    largest range the chunked path's mid-chunk reference has to cover."""
+    say("backward at the floor", path)
+    T, H, d = 50, 2, 64
+    g = torch.full((1, T, H, d), -5.0)
+    _run(torch.float32, 1, T, H, d, d, 750, g=g, path=path)
 
 
 def test_backward_without_the_floor():
@@ -56,4 +82,19 @@ def test_backward_without_the_floor():
     say("backward without the floor")
     T, H, d = 40, 2, 64
     g = -20.0 * torch.rand(1, T, H, d, generator=torch.Generator().manual_seed(731))
-    _run(torch.float32, 1, T, H, d, d, 730, g=g)
+    _run(torch.float32, 1, T, H, d, d, 730, g=g, path="token")
+
+
+def test_backward_range_check():
+    """The chunked path's range check rejects g below the floor (KDA_ERR_RANGE)."""
+    say("backward range check")
+    x = prefill_device(1, 32, 2, 32, 32, torch.float32, 760)
+    g = torch.full((1, 32, 2, 32), -6.0, device="cuda")
+    d_o = torch.ones(1, 32, 2, 32, device="cuda")
+    with pytest.raises(KdaError) as err:
+        kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], None, d_o, flags=KDA_FLAG_CHECK_RANGE)
+    assert err.value.code == -4
+    g.fill_(-1.0)
+    out = kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], None, d_o, flags=KDA_FLAG_CHECK_RANGE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out["dq"]).all()
