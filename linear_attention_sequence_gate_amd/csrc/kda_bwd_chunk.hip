@@ -34,9 +34,9 @@
 // (m cancels from every output, so its gradient is zero and is not formed.)
 //
 // Four launches:
-//   cb_prep_kernel   one wave per chunk: At, P, X (16x16 each) and the decayed
+//   cb_prep_kernel   per chunk: At, P, X (16x16 each) and the decayed
 //                    operands K~, K^, Q~, e^{b_C} to the workspace
-//   cb_fwd_kernel    per (chain, 16-column slice), chunks in order: the state
+//   cb_fwd_kernel    per (chain, 32-column slice), chunks in order: the state
 //                    entering each chunk and W to the workspace
 //   cb_bwd_kernel    per (chain, slice), chunks in reverse: dN of each chunk,
 //                    dU, and d(initial state)
@@ -115,82 +115,119 @@ __device__ __forceinline__ void cb_cumsum(const float (&gv)[kCB], float (&b)[kCB
 }
 
 // ---------------------------------------------------------------------------
-// At, P, X of one chunk.  One wave.
+// At, P, X and the decayed operands of one chunk.  Four waves: thread t <
+// 2 DK takes channel t % DK over tokens 8 (t / DK) .. +7 (the two halves
+// exchange their decay totals through LDS); then wave 0 forms At and X,
+// wave 1 forms P.
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
-__global__ __launch_bounds__(64) void cb_prep_kernel(CbArgs a) {
-    constexpr int LD = DK + 4;
+__global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
+    constexpr int LD = DK + 4, HT = kCB / 2;
     __shared__ __attribute__((aligned(16))) float Kp[kCB][LD], Kpp[kCB][LD], Qp[kCB][LD];
+    __shared__ float tot[2][DK];
     __shared__ float Am[kCB][kCB + 1], bet[kCB];
     const int64_t unit = blockIdx.x;
     const int64_t bh = unit / a.nc;
     const int c = (int)(unit % a.nc);
     const int64_t t0 = (int64_t)c * kCB;
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
-    const int lane = threadIdx.x, j = lane & 15, g4 = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t rb = cb_rowbase(a, bh);
-    for (int ch = lane; ch < DK; ch += 64) {
-        float gv[kCB], kv[kCB], qv[kCB], b[kCB];
-        cb_load16<float>(a.g, rb, t0, n, a.H, DK, ch, gv);
-        cb_load16<T>(a.k, rb, t0, n, a.H, DK, ch, kv);
-        cb_load16<T>(a.q, rb, t0, n, a.H, DK, ch, qv);
-        cb_cumsum(gv, b);
-        const float m = b[7], bc = b[kCB - 1];
-        float *op = a.ops + unit * cb_ops_floats(DK);
-        float kt[kCB], kh[kCB], qt[kCB];
+    const int ch = tid % DK, half = tid / DK;
+    float gv[HT], kv[HT], qv[HT], b[HT];
+    if (tid < 2 * DK) {
 #pragma unroll
-        for (int r = 0; r < kCB; ++r) {
-            const float e = expf(b[r] - m), ei = expf(m - b[r]), eb = expf(b[r]);
-            Kp[r][ch] = kv[r] * e;
-            Kpp[r][ch] = kv[r] * ei;
-            Qp[r][ch] = qv[r] * e;
+        for (int r = 0; r < HT; ++r) {
+            const int tr = HT * half + r, rr = tr < n ? tr : n - 1;
+            const int64_t off = (rb + (t0 + rr) * a.H) * DK + ch;
+            gv[r] = a.g[off];
+            kv[r] = cb_ld<T>(a.k, off);
+            qv[r] = cb_ld<T>(a.q, off);
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < HT; ++r) {
+            const bool ok = HT * half + r < n;
+            gv[r] = ok ? gv[r] : 0.f;
+            kv[r] = ok ? kv[r] : 0.f;
+            qv[r] = ok ? qv[r] : 0.f;
+            sum += gv[r];
+            b[r] = sum;
+        }
+        tot[half][ch] = sum;
+    }
+    if (tid < kCB) bet[tid] = (tid < n) ? cb_ld<T>(a.beta, rb + (t0 + tid) * a.H) : 0.f;
+    __syncthreads();
+    if (tid < 2 * DK) {
+        const float m = tot[0][ch];                       // b_7
+        const float bc = tot[0][ch] + tot[1][ch];         // b_15
+        const float base = half ? m : 0.f;
+        float *op = a.ops + unit * cb_ops_floats(DK);
+        float kt[HT], kh[HT], qt[HT];
+#pragma unroll
+        for (int r = 0; r < HT; ++r) {
+            const int tr = HT * half + r;
+            const float br = base + b[r];
+            const float e = expf(br - m), ei = expf(m - br), eb = expf(br);
+            Kp[tr][ch] = kv[r] * e;
+            Kpp[tr][ch] = kv[r] * ei;
+            Qp[tr][ch] = qv[r] * e;
             kt[r] = kv[r] * eb;
-            kh[r] = kv[r] * expf(bc - b[r]);
+            kh[r] = kv[r] * expf(bc - br);
             qt[r] = qv[r] * eb;
-            op[kOpKt * DK + r * DK + ch] = kt[r];
-            op[kOpKh * DK + r * DK + ch] = kh[r];
+            op[kOpKt * DK + tr * DK + ch] = kt[r];
+            op[kOpKh * DK + tr * DK + ch] = kh[r];
         }
 #pragma unroll
-        for (int r = 0; r < kCB; r += 4) {
-            *reinterpret_cast<floatx4 *>(op + kOpKtT * DK + ch * kCB + r) =
+        for (int r = 0; r < HT; r += 4) {
+            const int tr = HT * half + r;
+            *reinterpret_cast<floatx4 *>(op + kOpKtT * DK + ch * kCB + tr) =
                 floatx4{kt[r], kt[r + 1], kt[r + 2], kt[r + 3]};
-            *reinterpret_cast<floatx4 *>(op + kOpKhT * DK + ch * kCB + r) =
+            *reinterpret_cast<floatx4 *>(op + kOpKhT * DK + ch * kCB + tr) =
                 floatx4{kh[r], kh[r + 1], kh[r + 2], kh[r + 3]};
-            *reinterpret_cast<floatx4 *>(op + kOpQtT * DK + ch * kCB + r) =
+            *reinterpret_cast<floatx4 *>(op + kOpQtT * DK + ch * kCB + tr) =
                 floatx4{qt[r], qt[r + 1], qt[r + 2], qt[r + 3]};
         }
-        op[kOpEbc * DK + ch] = expf(bc);
+        if (half == 0) op[kOpEbc * DK + ch] = expf(bc);
     }
-    if (lane < kCB) bet[lane] = (lane < n) ? cb_ld<T>(a.beta, rb + (t0 + lane) * a.H) : 0.f;
     __syncthreads();
-    floatx4 at = {0, 0, 0, 0}, pp = {0, 0, 0, 0};
-    tile_mma<float>(at, &Kp[0][0], LD, &Kpp[0][0], LD, DK, lane);   // at[i] = At[4g4+i][j]
-    tile_mma<float>(pp, &Qp[0][0], LD, &Kpp[0][0], LD, DK, lane);
     float *mat = a.mat + unit * kCbMat;          // X, P, At
+    if (wave == 0) {
+        floatx4 at = {0, 0, 0, 0};
+        tile_mma<float>(at, &Kp[0][0], LD, &Kpp[0][0], LD, DK, lane);   // at[i] = At[4g4+i][j]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i;
-        const float atv = (j < r) ? at[i] : 0.f;  // selects: the masked entries may be large
-        mat[2 * kCB * kCB + r * kCB + j] = atv;
-        mat[kCB * kCB + r * kCB + j] = (j <= r) ? pp[i] : 0.f;
-        Am[r][j] = bet[r] * atv;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            const float atv = (j < r) ? at[i] : 0.f;  // selects: the masked entries may be large
+            mat[2 * kCB * kCB + r * kCB + j] = atv;
+            Am[r][j] = bet[r] * atv;
+        }
+    } else if (wave == 1) {
+        floatx4 pp = {0, 0, 0, 0};
+        tile_mma<float>(pp, &Qp[0][0], LD, &Kpp[0][0], LD, DK, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            mat[kCB * kCB + r * kCB + j] = (j <= r) ? pp[i] : 0.f;
+        }
     }
     __syncthreads();
     // X = (I + A)^-1 by forward substitution, one column per lane.
-    if (lane < kCB) {
+    if (tid < kCB) {
         float x[kCB];
 #pragma unroll
         for (int r = 0; r < kCB; ++r) {
-            float s = (r == lane) ? 1.f : 0.f;
+            float sacc = (r == tid) ? 1.f : 0.f;
 #pragma unroll
-            for (int q = 0; q < r; ++q) s -= Am[r][q] * x[q];
-            x[r] = s;
-            mat[r * kCB + lane] = s;
+            for (int q = 0; q < r; ++q) sacc -= Am[r][q] * x[q];
+            x[r] = sacc;
+            mat[r * kCB + tid] = sacc;
         }
     }
 }
 
-// block -> (chain, 16-column slice); the slices of a chain share an XCD (and
+// block -> (chain, column slice); the slices of a chain share an XCD (and
 // its L2) when the chain count is a multiple of 8.
 __device__ __forceinline__ void cb_slice_block(const CbArgs &a, int64_t nbh, int64_t &bh, int &sl) {
     const int64_t x = blockIdx.x;
@@ -203,17 +240,21 @@ __device__ __forceinline__ void cb_slice_block(const CbArgs &a, int64_t nbh, int
     }
 }
 
+// Value columns per workgroup of the two state passes (two 16-column tiles).
+constexpr int kCbNS = 32;
+constexpr int kCbCT = kCbNS / 16;
+
 // LDS of the two state passes, double-buffered over chunks.
 template <int DK> struct alignas(16) CbPassLds {
     float rowm[2][kCB][DK + 4];                  // fwd: K~    bwd: K^          [token][channel]
     float colm1[2][DK][kCB + 4];                 // fwd: K^ T  bwd: Q~ T       [channel][token]
     float colm2[2][DK][kCB + 4];                 //            bwd: K~ T
     float ebc[2][DK];                            // e^{b_C}
-    float vo[2][kCB][kCB + 1];                   // fwd: V slice  bwd: dO slice
+    float vo[2][kCB][kCbNS + 1];                 // fwd: V slice  bwd: dO slice
     float X[2][kCB][kCB + 4];
     float P[2][kCB][kCB + 1];
     float bet[2][kCB];
-    float red[4][kCB][kCB + 1];
+    float red[4][kCB][kCbNS + 1];
 };
 
 // One chunk's inputs of a state pass, fetched into registers a chunk ahead
@@ -221,8 +262,9 @@ template <int DK> struct alignas(16) CbPassLds {
 // would otherwise be paid once per chunk).
 template <int DK> struct CbStage {
     static constexpr int NF = (4 * DK + 255) / 256;   // float4 of one [16][DK] array per thread
+    static constexpr int NV = kCB * kCbNS / 256;      // value (or dO) elements per thread
     floatx4 r1[NF], r2[NF], r3[NF], e;
-    float vo, x, p, bet;
+    float vo[NV], x, p, bet;
 };
 
 __device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
@@ -246,8 +288,12 @@ __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int6
         }
     }
     if (tid < DK / 4) st.e = ld4(op + kOpEbc * DK + 4 * tid);
-    const int r = tid >> 4, cc = tid & 15, rr = r < n ? r : n - 1;
-    st.vo = cb_ld<T>(vsrc, (rb + (t0 + rr) * a.H) * a.DV + col0 + cc);
+#pragma unroll
+    for (int u = 0; u < CbStage<DK>::NV; ++u) {
+        const int e = tid + 256 * u, r = e / kCbNS, cc = e % kCbNS, rr = r < n ? r : n - 1;
+        st.vo[u] = cb_ld<T>(vsrc, (rb + (t0 + rr) * a.H) * a.DV + col0 + cc);
+    }
+    const int r = tid >> 4, cc = tid & 15;
     const float *mc = a.mat + (bh * a.nc + c) * kCbMat;
     st.x = mc[r * kCB + cc];
     if (BWD) st.p = mc[kCB * kCB + r * kCB + cc];
@@ -270,102 +316,249 @@ __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<
         }
     }
     if (tid < DK / 4) *reinterpret_cast<floatx4 *>(&L.ebc[buf][4 * tid]) = st.e;
+#pragma unroll
+    for (int u = 0; u < CbStage<DK>::NV; ++u) {
+        const int e = tid + 256 * u, r = e / kCbNS, cc = e % kCbNS;
+        L.vo[buf][r][cc] = r < n ? st.vo[u] : 0.f;
+    }
     const int r = tid >> 4, cc = tid & 15;
-    L.vo[buf][r][cc] = r < n ? st.vo : 0.f;
     L.X[buf][r][cc] = st.x;
     if (BWD) L.P[buf][r][cc] = st.p;
     if (tid < kCB) L.bet[buf][tid] = tid < n ? st.bet : 0.f;
 }
 
+// Chunks of register prefetch in the two state passes.  The passes' barriers
+// wait for LDS only (lds_barrier), so loads stay in flight across them and
+// the stores of states and W never hold a barrier up.
+constexpr int kCbAhead = 1;
+
 // ---------------------------------------------------------------------------
 // Forward state pass: the state entering every chunk, and W = V - K~ S.
+// Wave w owns row tiles w*TPW .. of the workgroup's 32 value columns.
 // ---------------------------------------------------------------------------
+template <int DK> using CbAcc = floatx4[(DK / 16 + 3) / 4][kCbCT];
+
+template <typename T, int DK>
+__device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, CbStage<DK> &stg,
+                                            int c, int64_t bh, int64_t rb, int col0, int wave,
+                                            CbAcc<DK> &s) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const int buf = c & 1;
+    const int64_t t0 = (int64_t)c * kCB;
+    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+    cb_stage_to_lds<DK, false>(L, stg, buf, n);
+    cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, c + kCbAhead < a.nc ? c + kCbAhead : a.nc - 1, stg);
+    float *stc = a.st + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    stc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV + 16 * v] = s[u][v][i];
+        }
+    }
+    lds_barrier();
+    // this wave's rows of K~ S
+    floatx4 wp[kCbCT];
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v) wp[v] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+            const floatx4 kt = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < kCbCT; ++v) wp[v] = mfma1(kt[i], s[u][v][i], wp[v]);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][16 * v + j] = wp[v][i];
+    lds_barrier();
+    const floatx4 xr = ld4(&L.X[buf][j][4 * g4]);
+    floatx4 U[kCbCT];
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v) {
+        const int cc = 16 * v + j;
+        floatx4 W;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            W[i] = L.vo[buf][r][cc] -
+                   (L.red[0][r][cc] + L.red[1][r][cc] + L.red[2][r][cc] + L.red[3][r][cc]);
+        }
+        if (wave == 0) {
+            float *wc = a.w + ((bh * a.nc + c) * kCB) * a.DV + col0 + cc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wc[(int64_t)(4 * g4 + i) * a.DV] = W[i];
+        }
+        // U = X Diag(beta) W
+        U[v] = floatx4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[v] = mfma1(xr[i], L.bet[buf][4 * g4 + i] * W[i], U[v]);
+    }
+    // S <- Diag(e^{b_C}) S + K^^T U
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+            const floatx4 kh = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[u][v][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[u][v] = mfma1(kh[i], U[v][i], s[u][v]);
+            }
+        }
+    }
+}
+
+// Load (or zero) this wave's tiles of a [B*H, DK, DV] state for the slice.
+template <int DK>
+__device__ __forceinline__ void cb_load_state(const float *src, int64_t bh, int DV, int col0,
+                                              int wave, CbAcc<DK> &s) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+#pragma unroll
+        for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[u][v][i] = (src && tt < RT)
+                                 ? src[(bh * DK + 16 * tt + 4 * g4 + i) * DV + col0 + 16 * v + j] : 0.f;
+    }
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
-    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
     __shared__ CbPassLds<DK> L;
     int64_t bh;
     int sl;
     cb_slice_block(a, nbh, bh, sl);
     const int64_t rb = cb_rowbase(a, bh);
-    const int col0 = sl * 16;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    floatx4 s[TPW];
+    const int col0 = sl * kCbNS;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    CbAcc<DK> s;
+    cb_load_state<DK>(a.S0, bh, a.DV, col0, wave, s);
+    CbStage<DK> stg[kCbAhead];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int tt = wave * TPW + u;
+    for (int q = 0; q < kCbAhead; ++q)
+        cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, q < a.nc ? q : a.nc - 1, stg[q]);
+    for (int c0 = 0; c0 < a.nc; c0 += kCbAhead) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s[u][i] = (a.S0 && tt < RT)
-                          ? a.S0[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] : 0.f;
-    }
-    CbStage<DK> stg;
-    cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, 0, stg);
-    for (int c = 0; c < a.nc; ++c) {
-        const int buf = c & 1;
-        const int64_t t0 = (int64_t)c * kCB;
-        const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
-        cb_stage_to_lds<DK, false>(L, stg, buf, n);
-        cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, c + 1 < a.nc ? c + 1 : c, stg);
-        float *stc = a.st + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) stc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV] = s[u][i];
-            }
-        }
-        __syncthreads();
-        // this wave's rows of K~ S
-        floatx4 wp = {0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-                const floatx4 kt = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wp = mfma1(kt[i], s[u][i], wp);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][j] = wp[i];
-        __syncthreads();
-        floatx4 W;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            W[i] = L.vo[buf][r][j] - (L.red[0][r][j] + L.red[1][r][j] + L.red[2][r][j] + L.red[3][r][j]);
-        }
-        if (wave == 0) {
-            float *wc = a.w + ((bh * a.nc + c) * kCB) * a.DV + col0 + j;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wc[(int64_t)(4 * g4 + i) * a.DV] = W[i];
-        }
-        // U = X Diag(beta) W
-        floatx4 U = {0, 0, 0, 0};
-        const floatx4 xr = ld4(&L.X[buf][j][4 * g4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) U = mfma1(xr[i], L.bet[buf][4 * g4 + i] * W[i], U);
-        // S <- Diag(e^{b_C}) S + K^^T U
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[u][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
-                const floatx4 kh = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[u] = mfma1(kh[i], U[i], s[u]);
-            }
-        }
+        for (int q = 0; q < kCbAhead; ++q)
+            if (c0 + q < a.nc) cb_fwd_step<T, DK>(a, L, stg[q], c0 + q, bh, rb, col0, wave, s);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Reverse state pass: dN of every chunk, dU, and d(initial state).
 // ---------------------------------------------------------------------------
+template <typename T, int DK>
+__device__ __forceinline__ void cb_bwd_step(const CbArgs &a, CbPassLds<DK> &L, CbStage<DK> &stg,
+                                            int c, int64_t bh, int64_t rb, int col0, int wave,
+                                            CbAcc<DK> &d) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const int buf = c & 1;
+    const int64_t t0 = (int64_t)c * kCB;
+    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
+    cb_stage_to_lds<DK, true>(L, stg, buf, n);
+    cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, c >= kCbAhead ? c - kCbAhead : 0, stg);
+    float *dnc = a.dn + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dnc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV + 16 * v] = d[u][v][i];
+        }
+    }
+    lds_barrier();
+    // this wave's rows of K^ dN (wave 0 adds P^T dO)
+    floatx4 up[kCbCT];
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v) up[v] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+            const floatx4 kh = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < kCbCT; ++v) up[v] = mfma1(kh[i], d[u][v][i], up[v]);
+        }
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pv = L.P[buf][4 * g4 + i][j];
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v) up[v] = mfma1(pv, L.vo[buf][4 * g4 + i][16 * v + j], up[v]);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][16 * v + j] = up[v][i];
+    lds_barrier();
+    floatx4 dW[kCbCT];
+#pragma unroll
+    for (int v = 0; v < kCbCT; ++v) {
+        const int cc = 16 * v + j;
+        floatx4 dU;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            dU[i] = L.red[0][r][cc] + L.red[1][r][cc] + L.red[2][r][cc] + L.red[3][r][cc];
+        }
+        if (wave == 0) {
+            float *duc = a.du + ((bh * a.nc + c) * kCB) * a.DV + col0 + cc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) duc[(int64_t)(4 * g4 + i) * a.DV] = dU[i];
+        }
+        // dW = Diag(beta) X^T dU, kept negated: it enters with K~^T
+        dW[v] = floatx4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dW[v] = mfma1(L.X[buf][4 * g4 + i][j], dU[i], dW[v]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dW[v][i] *= -L.bet[buf][4 * g4 + i];
+    }
+    // dN <- Diag(e^{b_C}) dN + Q~^T dO - K~^T dW
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+            const floatx4 qt = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
+            const floatx4 kt = ld4(&L.colm2[buf][16 * tt + j][4 * g4]);
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[u][v][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    d[u][v] = mfma1(qt[i], L.vo[buf][4 * g4 + i][16 * v + j], d[u][v]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[u][v] = mfma1(kt[i], dW[v][i], d[u][v]);
+            }
+        }
+    }
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
     constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
@@ -374,87 +567,19 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
     int sl;
     cb_slice_block(a, nbh, bh, sl);
     const int64_t rb = cb_rowbase(a, bh);
-    const int col0 = sl * 16;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    floatx4 d[TPW];
+    const int col0 = sl * kCbNS;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    CbAcc<DK> d;
+    cb_load_state<DK>(a.dST, bh, a.DV, col0, wave, d);
+    CbStage<DK> stg[kCbAhead];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int tt = wave * TPW + u;
+    for (int q = 0; q < kCbAhead; ++q)
+        cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, a.nc - 1 - q >= 0 ? a.nc - 1 - q : 0, stg[q]);
+    for (int c0 = a.nc - 1; c0 >= 0; c0 -= kCbAhead) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            d[u][i] = (a.dST && tt < RT)
-                          ? a.dST[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] : 0.f;
-    }
-    CbStage<DK> stg;
-    cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, a.nc - 1, stg);
-    for (int c = a.nc - 1; c >= 0; --c) {
-        const int buf = c & 1;
-        const int64_t t0 = (int64_t)c * kCB;
-        const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
-        cb_stage_to_lds<DK, true>(L, stg, buf, n);
-        cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, c > 0 ? c - 1 : 0, stg);
-        float *dnc = a.dn + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dnc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV] = d[u][i];
-            }
-        }
-        __syncthreads();
-        // this wave's rows of K^ dN (wave 0 adds P^T dO)
-        floatx4 up = {0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-                const floatx4 kh = ld4(&L.rowm[buf][j][16 * tt + 4 * g4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) up = mfma1(kh[i], d[u][i], up);
-            }
-        }
-        if (wave == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                up = mfma1(L.P[buf][4 * g4 + i][j], L.vo[buf][4 * g4 + i][j], up);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][j] = up[i];
-        __syncthreads();
-        floatx4 dU;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            dU[i] = L.red[0][r][j] + L.red[1][r][j] + L.red[2][r][j] + L.red[3][r][j];
-        }
-        if (wave == 0) {
-            float *duc = a.du + ((bh * a.nc + c) * kCB) * a.DV + col0 + j;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) duc[(int64_t)(4 * g4 + i) * a.DV] = dU[i];
-        }
-        // dW = Diag(beta) X^T dU
-        floatx4 dW = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dW = mfma1(L.X[buf][4 * g4 + i][j], dU[i], dW);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dW[i] *= -L.bet[buf][4 * g4 + i];   // -dW: enters with K~^T
-        // dN <- Diag(e^{b_C}) dN + Q~^T dO - K~^T dW
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int tt = wave * TPW + u;
-            if (tt < RT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) d[u][i] *= L.ebc[buf][16 * tt + 4 * g4 + i];
-                const floatx4 qt = ld4(&L.colm1[buf][16 * tt + j][4 * g4]);
-                const floatx4 kt = ld4(&L.colm2[buf][16 * tt + j][4 * g4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) d[u] = mfma1(qt[i], L.vo[buf][4 * g4 + i][j], d[u]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) d[u] = mfma1(kt[i], dW[i], d[u]);
-            }
-        }
+        for (int q = 0; q < kCbAhead; ++q)
+            if (c0 - q >= 0) cb_bwd_step<T, DK>(a, L, stg[q], c0 - q, bh, rb, col0, wave, d);
     }
     if (a.dS0) {
 #pragma unroll
@@ -462,8 +587,10 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
             const int tt = wave * TPW + u;
             if (tt < RT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.dS0[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + j] = d[u][i];
+                for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a.dS0[(bh * DK + 16 * tt + 4 * g4 + i) * a.DV + col0 + 16 * v + j] = d[u][v][i];
             }
         }
     }
@@ -495,6 +622,9 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const int64_t rb = cb_rowbase(a, bh);
+    constexpr int NT = (RT + 3) / 4, KB = DV / 16;
+    const float *stc = a.st + unit * DK * DV;
+    const float *dnc = a.dn + unit * DK * DV;
     // 1. inputs
     if (tid < DK) {
         float gv[kCB], kv[kCB], qv[kCB], b[kCB];
@@ -534,7 +664,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
         }
         if (tid < kCB) L.bet[tid] = (tid < n) ? cb_ld<T>(a.beta, rb + (t0 + tid) * a.H) : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // 2. U = X Diag(beta) W and dW = Diag(beta) X^T dU, column tiles over waves
     for (int ct = wave; ct < CT; ct += 4) {
@@ -556,7 +686,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
             if (r < n) a.dv[(rb + (t0 + r) * a.H) * DV + cc] = dW[i];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // 3a. the 16x16 chunk matrices (waves 0 and 1)
     if (wave == 0) {
@@ -611,23 +741,22 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
     }
 
     // 3b. the state products, channel tiles over waves
-    floatx4 dQt[(RT + 3) / 4], dKt[(RT + 3) / 4], dKh[(RT + 3) / 4];
-    const float *stc = a.st + unit * DK * DV;
-    const float *dnc = a.dn + unit * DK * DV;
+    floatx4 dQt[NT], dKt[NT], dKh[NT];
 #pragma unroll
-    for (int u = 0; u < (RT + 3) / 4; ++u) {
+    for (int u = 0; u < NT; ++u) {
         const int ct = wave + 4 * u;
         dQt[u] = dKt[u] = dKh[u] = floatx4{0, 0, 0, 0};
         if (ct < RT) {
             const int cr = 16 * ct + j;
             float rsum = 0.f;
-#pragma unroll 4
-            for (int k0 = 0; k0 < DV; k0 += 16) {
-                const floatx4 sv = *reinterpret_cast<const floatx4 *>(stc + (int64_t)cr * DV + k0 + 4 * g4);
-                const floatx4 nv = *reinterpret_cast<const floatx4 *>(dnc + (int64_t)cr * DV + k0 + 4 * g4);
-                const floatx4 o4 = *reinterpret_cast<const floatx4 *>(&L.dO[j][k0 + 4 * g4]);
-                const floatx4 w4 = *reinterpret_cast<const floatx4 *>(&L.dW[j][k0 + 4 * g4]);
-                const floatx4 u4 = *reinterpret_cast<const floatx4 *>(&L.U[j][k0 + 4 * g4]);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int k0 = 16 * kb;
+                const floatx4 sv = ld4(stc + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 nv = ld4(dnc + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 o4 = ld4(&L.dO[j][k0 + 4 * g4]);
+                const floatx4 w4 = ld4(&L.dW[j][k0 + 4 * g4]);
+                const floatx4 u4 = ld4(&L.U[j][k0 + 4 * g4]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     dQt[u] = mfma1(o4[i], sv[i], dQt[u]);
@@ -641,11 +770,11 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
             if (g4 == 0) L.rs[cr] = rsum;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // 4. pair terms and the token gradients of this wave's channel tiles
 #pragma unroll
-    for (int u = 0; u < (RT + 3) / 4; ++u) {
+    for (int u = 0; u < NT; ++u) {
         const int ct = wave + 4 * u;
         if (ct >= RT) continue;
         const int ch = 16 * ct + j;
@@ -711,7 +840,7 @@ size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
 
 template <typename T, int DK>
 static hipError_t cb_inst(CbArgs a, int64_t nbh, hipStream_t s) {
-    hipLaunchKernelGGL((cb_prep_kernel<T, DK>), dim3((unsigned)(nbh * a.nc)), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((cb_prep_kernel<T, DK>), dim3((unsigned)(nbh * a.nc)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((cb_fwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
@@ -733,7 +862,7 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
                                     const float *dST, float *dq, float *dk_, float *dv_, float *dg,
                                     float *dbeta, float *dS0, float *ws, int64_t B, int64_t T,
                                     int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
-    if (dv % 16 || dk % 16) return hipErrorInvalidValue;
+    if (dv % kCbNS || dk % 16) return hipErrorInvalidValue;
     const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
     if (nbh * nc > 0x7fffffffLL) return hipErrorInvalidValue;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -751,7 +880,7 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
     a.w = reinterpret_cast<float *>(p + 2 * st + mat);
     a.du = reinterpret_cast<float *>(p + 2 * st + mat + wv);
     a.ops = reinterpret_cast<float *>(p + 2 * st + mat + 2 * wv);
-    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / 16;
+    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / kCbNS;
     switch (dk) {
     case 32: return is_bf16 ? cb_inst<bf16, 32>(a, nbh, s) : cb_inst<float, 32>(a, nbh, s);
     case 64: return is_bf16 ? cb_inst<bf16, 64>(a, nbh, s) : cb_inst<float, 64>(a, nbh, s);
