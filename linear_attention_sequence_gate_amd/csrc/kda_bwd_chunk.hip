@@ -250,11 +250,13 @@ template <int DK> struct alignas(16) CbPassLds {
     float colm1[2][DK][kCB + 4];                 // fwd: K^ T  bwd: Q~ T       [channel][token]
     float colm2[2][DK][kCB + 4];                 //            bwd: K~ T
     float ebc[2][DK];                            // e^{b_C}
-    float vo[2][kCB][kCbNS + 1];                 // fwd: V slice  bwd: dO slice
+    // pitches: rows 4 apart land 16 banks apart, so the accumulator-layout
+    // accesses (row 4(l/16)+i, column l%16) of a wave hit distinct banks
+    float vo[2][kCB][kCbNS + 4];                 // fwd: V slice  bwd: dO slice
     float X[2][kCB][kCB + 4];
-    float P[2][kCB][kCB + 1];
+    float P[2][kCB][kCB + 4];
     float bet[2][kCB];
-    float red[4][kCB][kCbNS + 1];
+    float red[4][kCB][kCbNS + 4];
 };
 
 // One chunk's inputs of a state pass, fetched into registers a chunk ahead
@@ -601,9 +603,9 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV> struct alignas(16) CbGradLds {
     static constexpr int LK = DK + 4, LV = DV + 4, LS = kCB + 4;
-    float q[kCB][LK], k[kCB][LK], bm[kCB][LK];  // bm = b - m
+    float bm[kCB][LK];                           // bm = b - m
     float m[DK], bcm[DK], rs[DK];                // m, b_C - m, rowsum(S * dN)
-    float W[kCB][LV], dU[kCB][LV], dO[kCB][LV], U[kCB][LV], dW[kCB][LV];
+    float dO[kCB][LV], U[kCB][LV], dW[kCB][LV];
     float X[kCB][LS], At[kCB][LS], dX[kCB][LS], Y[kCB][LS], dP[kCB][LS], dAt[kCB][LS];
     float bet[kCB];
 };
@@ -626,30 +628,38 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
     const float *stc = a.st + unit * DK * DV;
     const float *dnc = a.dn + unit * DK * DV;
     // 1. inputs
+    const float *wc = a.w + unit * kCB * DV;    // W, dU of the chunk: [16][DV]
+    const float *duc = a.du + unit * kCB * DV;
+    // q, k of this lane's tokens 4 g4 + i and channels 16 ct + j (step 4),
+    // zero past the end; loaded first so that the latency is hidden
+    float qin[NT][4], kin[NT][4];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i, rr = r < n ? r : n - 1;
+            const int64_t off = (rb + (t0 + rr) * a.H) * DK + ch;
+            qin[u][i] = cb_ld<T>(a.q, off);
+            kin[u][i] = cb_ld<T>(a.k, off);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qin[u][i] = 4 * g4 + i < n ? qin[u][i] : 0.f;
+            kin[u][i] = 4 * g4 + i < n ? kin[u][i] : 0.f;
+        }
+    }
     if (tid < DK) {
-        float gv[kCB], kv[kCB], qv[kCB], b[kCB];
+        float gv[kCB], b[kCB];
         cb_load16<float>(a.g, rb, t0, n, a.H, DK, tid, gv);
-        cb_load16<T>(a.k, rb, t0, n, a.H, DK, tid, kv);
-        cb_load16<T>(a.q, rb, t0, n, a.H, DK, tid, qv);
         cb_cumsum(gv, b);
         const float m = b[7];
         L.m[tid] = m;
         L.bcm[tid] = b[kCB - 1] - m;
 #pragma unroll
-        for (int r = 0; r < kCB; ++r) {
-            L.q[r][tid] = qv[r];
-            L.k[r][tid] = kv[r];
-            L.bm[r][tid] = b[r] - m;
-        }
+        for (int r = 0; r < kCB; ++r) L.bm[r][tid] = b[r] - m;
     }
     {
-        const float *wc = a.w + unit * kCB * DV;
-        const float *duc = a.du + unit * kCB * DV;
-        for (int e = tid; e < kCB * DV / 4; e += 256) {
-            const int r = (4 * e) / DV, cc = (4 * e) % DV;
-            *reinterpret_cast<floatx4 *>(&L.W[r][cc]) = *reinterpret_cast<const floatx4 *>(wc + 4 * e);
-            *reinterpret_cast<floatx4 *>(&L.dU[r][cc]) = *reinterpret_cast<const floatx4 *>(duc + 4 * e);
-        }
         for (int e = tid; e < kCB * DV; e += 256) {
             const int r = e / DV, cc = e % DV;
             const int rr = r < n ? r : n - 1;
@@ -674,8 +684,8 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 4 * g4 + i;
-            U = mfma1(xr[i], L.bet[s] * L.W[s][cc], U);
-            dW = mfma1(L.X[s][j], L.dU[s][cc], dW);
+            U = mfma1(xr[i], L.bet[s] * wc[s * DV + cc], U);
+            dW = mfma1(L.X[s][j], duc[s * DV + cc], dW);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -690,8 +700,14 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
 
     // 3a. the 16x16 chunk matrices (waves 0 and 1)
     if (wave == 0) {
-        floatx4 dT = {0, 0, 0, 0};
-        tile_mma<float>(dT, &L.dU[0][0], Lds::LV, &L.W[0][0], Lds::LV, DV, lane);  // dT[r][s] = dU_r . W_s
+        floatx4 dT = {0, 0, 0, 0};                // dT[r][s] = dU_r . W_s
+#pragma unroll
+        for (int kb = 0; kb < DV / 16; ++kb) {
+            const floatx4 x4 = ld4(duc + j * DV + 16 * kb + 4 * g4);
+            const floatx4 y4 = ld4(wc + j * DV + 16 * kb + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dT = mfma1(x4[i], y4[i], dT);
+        }
         float dbT = 0.f;                          // sum_r X_rs dT_rs, column s = j
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -778,11 +794,12 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
         const int ct = wave + 4 * u;
         if (ct >= RT) continue;
         const int ch = 16 * ct + j;
+        const float *qv = qin[u], *kv = kin[u];
         floatx4 dQp = {0, 0, 0, 0}, dKp = {0, 0, 0, 0}, dKpp = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 4 * g4 + i;
-            const float bms = L.bm[s][ch], ks = L.k[s][ch], qs = L.q[s][ch];
+            const float bms = L.bm[s][ch], ks = kv[i], qs = qv[i];
             const float e = expf(bms), ei = expf(-bms);
             const float kpp = ks * ei, kp = ks * e, qp = qs * e;
             dQp = mfma1(L.dP[j][s], kpp, dQp);
@@ -795,14 +812,14 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
-            const float bmr = L.bm[r][ch], qv = L.q[r][ch], kv = L.k[r][ch];
+            const float bmr = L.bm[r][ch], qr = qv[i], kr = kv[i];
             const float e_bm = expf(bmr), e_mb = expf(-bmr);
             const float e_b = expf(bmr + m), e_cb = expf(bcm - bmr);
             const float dq = dQt[u][i] * e_b + dQp[i] * e_bm;
             const float dk = -dKt[u][i] * e_b + dKh[u][i] * e_cb + dKp[i] * e_bm + dKpp[i] * e_mb;
-            const float kh = dKh[u][i] * kv * e_cb;
-            db[i] = dQt[u][i] * qv * e_b - dKt[u][i] * kv * e_b - kh + dQp[i] * qv * e_bm +
-                    dKp[i] * kv * e_bm - dKpp[i] * kv * e_mb;
+            const float kh = dKh[u][i] * kr * e_cb;
+            db[i] = dQt[u][i] * qr * e_b - dKt[u][i] * kr * e_b - kh + dQp[i] * qr * e_bm +
+                    dKp[i] * kr * e_bm - dKpp[i] * kr * e_mb;
             khk += kh;
             if (r < n) {
                 const int64_t row = (rb + (t0 + r) * a.H);
