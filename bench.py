@@ -275,7 +275,8 @@ def time_backward(reps=3):
     4 GiB), on the chunked path; the token-level path timed beside it."""
     B, T, H, d = 4, 4096, 32, 128
     dev = torch.device("cuda")
-    x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02)
+    x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02,
+                                   stress_heads_mean=3.0)
     g = _lib.kda_gate(x["z"], x["A"])
     d_o = torch.randn(B, T, H, d, device=dev).to(torch.bfloat16)
     ws = torch.empty(_lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, 1), device=dev, dtype=torch.uint8)
@@ -300,7 +301,7 @@ def time_backward(reps=3):
     tflops = bwd_chunk_flops(d) * ht / (ms / 1e3) / 1e12
     del x, g, d_o, ws
     torch.cuda.empty_cache()
-    return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16 (gradients fp32)",
+    return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16, heads 16-31 decay-stress (gradients fp32)",
             "head_tokens_per_s": ht / (ms / 1e3), "token_path_ms": ms_token,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS,
@@ -473,7 +474,7 @@ EXTRA_TRACES = {
              "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
     "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
-                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16: the chunked path "
+                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (heads 16-31 decay-stress): the chunked path "
                  "(1 warm-up + 3 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
                  "chunk), cb_fwd_kernel (state entering each chunk), cb_bwd_kernel (gradient "
                  "leaving each chunk) and cb_grad_kernel (token gradients, all chunks at once)), "

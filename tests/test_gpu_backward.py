@@ -98,3 +98,30 @@ def test_backward_range_check():
     out = kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], None, d_o, flags=KDA_FLAG_CHECK_RANGE)
     torch.cuda.synchronize()
     assert torch.isfinite(out["dq"]).all()
+
+
+def test_backward_benchmark_shape_sampled_chains():
+    """The benchmark's backward workload (B4 H32 T4096 d128 bf16, heads 16-31
+    decay-stress), one call in the benchmark's launch configuration; one
+    ordinary and one decay-stress chain compared in full with the oracle."""
+    say("backward chunked B4 H32 T4096 d128 (two chains against the oracle)")
+    B, T, H, d = 4, 4096, 32, 128
+    x = prefill_device(B, T, H, d, d, torch.bfloat16, 4243, s0_std=0.02, stress=3.0)
+    g = oracle_gate_f32(x["z"], x["A"])
+    gen = torch.Generator(device="cuda").manual_seed(4244)
+    d_o = torch.randn(B, T, H, d, device="cuda", generator=gen).to(torch.bfloat16)
+    dST = torch.randn(B, H, d, d, device="cuda", generator=gen)
+    out = kda_chunk_bwd(x["q"], x["k"], x["v"], g.cuda(), x["beta"], x["S0"], d_o, dST)
+    torch.cuda.synchronize()
+    for b, h in ((0, 3), (3, 29)):
+        chain = lambda t: t[b:b + 1, :, h:h + 1].contiguous()
+        ref = oracle.backward_np(chain(x["q"]), chain(x["k"]), chain(x["v"]), chain(g),
+                                 chain(x["beta"]), x["S0"][b:b + 1, h:h + 1].contiguous(),
+                                 chain(d_o), dST[b:b + 1, h:h + 1].contiguous())
+        res = {name: rho(chain(out[name]), ref[rname])
+               for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"),
+                                   ("dbeta", "dbeta"))}
+        res["d_initial_state"] = rho(out["d_initial_state"][b:b + 1, h:h + 1], ref["dS0"])
+        print(f"    b{b} h{h} " + " ".join(f"{k}={v:.1e}" for k, v in res.items()), flush=True)
+        for name, r in res.items():
+            assert r <= TOL[torch.bfloat16], (b, h, name, r)
