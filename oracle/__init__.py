@@ -33,6 +33,7 @@ from .core import (  # noqa: F401
     forward,
     forward_np,
     gate,
+    gate_backward_np,
     gate_np,
     max_threads,
     rho,

@@ -212,6 +212,24 @@ def tile_log_decay_sums(g, tile: int = TILE) -> np.ndarray:
 # Reverse mode of the recurrence (plain loops over tokens, fp64)
 # ----------------------------------------------------------------------------
 
+def gate_backward_np(z, A, dg) -> dict:
+    """Gradients of L = <g, dg> through the gate g = -5 sigmoid(x), x = exp(A) z
+    (the gate of `gate_np`; A [H, dk] is shared by every row of z):
+        dz = -5 sigmoid'(x) exp(A) dg
+        dA = sum over the rows of z of -5 sigmoid'(x) x dg      (dx/dA = x)
+    with sigmoid'(x) = sigmoid(x) sigmoid(-x) = e^{-|x|} / (1 + e^{-|x|})^2,
+    written in the form that stays accurate for large |x|.
+    Returns dz (the shape of z) and dA [H, dk]."""
+    z, A, dg = _f64(z), _f64(A), _f64(dg)
+    H, dk = A.shape
+    assert z.shape == dg.shape and z.shape[-2:] == (H, dk)
+    eA = np.exp(A)
+    x = eA * z
+    e = np.exp(-np.abs(x))
+    t = GMIN * dg * e / (1.0 + e) ** 2
+    return dict(dz=t * eA, dA=(t * x).reshape(-1, H, dk).sum(axis=0))
+
+
 def backward_np(q, k, v, g, beta, S0=None, do=None, dST=None) -> dict:
     """Gradients of L = <o, do> + <S_T, dST> through the token recurrence.
 

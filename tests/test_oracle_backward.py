@@ -77,3 +77,57 @@ def test_backward_beta_zero_is_pure_decay():
         for t in range(4):
             expect = expect + cum[t][:, None] * np.outer(x["q"][0, t, hh], do[0, t, hh])
         assert np.allclose(gr["dS0"][0, hh], expect, rtol=1e-12, atol=1e-14)
+
+
+# --- the gate's reverse mode ------------------------------------------------
+
+def _gate_case(seed, rows=5, H=2, dk=3):
+    r = np.random.default_rng(seed)
+    z = r.normal(scale=2.0, size=(rows, H, dk))
+    z[0, 0, 0] = 30.0                 # deep in the saturated tail
+    z[1, 1, 2] = -25.0
+    A = r.normal(scale=0.5, size=(H, dk))
+    dg = r.normal(size=(rows, H, dk))
+    return z, A, dg
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gate_backward_matches_central_differences(seed):
+    """dz and dA against central differences of <gate(z, A), dg>, with the
+    gate from the C oracle (an independent evaluation of the forward)."""
+    z, A, dg = _gate_case(seed)
+    gr = oracle.gate_backward_np(z, A, dg)
+    loss = lambda zz, AA: float(np.sum(oracle.gate(zz[None], AA)[0] * dg))
+    h = 1e-6
+    for name, x, gx in (("z", z, gr["dz"]), ("A", A, gr["dA"])):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            orig = x[idx]
+            x[idx] = orig + h
+            lp = loss(z, A)
+            x[idx] = orig - h
+            lm = loss(z, A)
+            x[idx] = orig
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - gx)) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
+
+
+def test_gate_backward_closed_forms():
+    """z = 0: sigmoid'(0) = 1/4, so dz = -(5/4) e^A dg and dA = 0 (x = 0).
+    A = 0: dz = -5 sigmoid(z) sigmoid(-z) dg.  Large |x|: the derivative
+    decays like e^{-|x|} and stays finite."""
+    r = np.random.default_rng(7)
+    A = r.normal(scale=0.5, size=(2, 4))
+    dg = r.normal(size=(3, 2, 4))
+    gr = oracle.gate_backward_np(np.zeros((3, 2, 4)), A, dg)
+    assert np.allclose(gr["dz"], -1.25 * np.exp(A) * dg, rtol=1e-15, atol=0)
+    assert np.all(gr["dA"] == 0.0)
+    z = r.normal(scale=3.0, size=(3, 2, 4))
+    gr = oracle.gate_backward_np(z, np.zeros((2, 4)), dg)
+    s = 1.0 / (1.0 + np.exp(-z))
+    assert np.allclose(gr["dz"], -5.0 * s * (1.0 - s) * dg, rtol=1e-12, atol=1e-300)
+    gr = oracle.gate_backward_np(np.full((1, 2, 4), 800.0), np.zeros((2, 4)), np.ones((1, 2, 4)))
+    assert np.all(np.isfinite(gr["dz"])) and np.all(gr["dz"] <= 0.0)
