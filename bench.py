@@ -297,12 +297,28 @@ def time_backward(reps=3):
 
     ms = timed(0, reps)
     ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1)
+    # the gate's reverse mode on the same rows (dz, dA from a dg of that shape)
+    dg = torch.randn(B, T, H, d, device=dev)
+    gws = torch.empty(max(_lib.kda_gate_bwd_workspace_size(B, T, H, d), 256), device=dev,
+                      dtype=torch.uint8)
+    _lib.kda_gate_bwd(x["z"], x["A"], dg, workspace=gws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        _lib.kda_gate_bwd(x["z"], x["A"], dg, workspace=gws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gate_ms = e0.elapsed_time(e1) / reps
+    gate_bytes = B * T * H * d * (2 + 4 + 4)             # z (bf16), dg, dz
+    del dg, gws
     ht = B * T * H
     tflops = bwd_chunk_flops(d) * ht / (ms / 1e3) / 1e12
     del x, g, d_o, ws
     torch.cuda.empty_cache()
     return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16, heads 16-31 decay-stress (gradients fp32)",
             "head_tokens_per_s": ht / (ms / 1e3), "token_path_ms": ms_token,
+            "gate_bwd_ms": gate_ms, "gate_bwd_gbs": gate_bytes / (gate_ms / 1e3) / 1e9,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS,
                          "flops_per_head_token": bwd_chunk_flops(d),

@@ -103,6 +103,28 @@ int kda_gate(const void *z, const float *A, float *g,
              int dtype, void *stream);
 
 /*
+ * kda_gate_bwd -- reverse mode of kda_gate: the gradients of L = <g, dg>
+ * with respect to z and A.  The gate is the one of "Kimi K3 internal
+ * structure analysis", section "Sequence mixing: 3 KDA layers per global MLA
+ * layer"; the pages say nothing of training, so the reverse mode is derived
+ * from it.  With x = exp(A) z:
+ *   dz = -5 sigmoid'(x) exp(A) dg,   dA[h,c] = sum over (b,t) of -5 sigmoid'(x) x dg
+ *   z  : [B, T, H, dk] dtype   (input, as given to kda_gate)
+ *   A  : [H, dk]       fp32    (input)
+ *   dg : [B, T, H, dk] fp32    (input, e.g. kda_chunk_bwd's dg)
+ *   dz : [B, T, H, dk] fp32    (output)
+ *   dA : [H, dk]       fp32    (output, overwritten)
+ *   workspace : kda_gate_bwd_workspace_size() bytes (per-row-range shares of
+ *               dA, added in a fixed order: the result does not depend on
+ *               scheduling)
+ * Outputs must not alias inputs or each other.
+ */
+size_t kda_gate_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk);
+int kda_gate_bwd(const void *z, const float *A, const float *dg, float *dz, float *dA,
+                 void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                 int64_t dk, int dtype, void *stream);
+
+/*
  * Workspace bytes kda_chunk_fwd needs for these sizes with the segment count
  * the library picks (flags without segment bits): 256 bytes for the
  * range-check counter, plus, when the sizes take the sequence-parallel path,

@@ -37,7 +37,8 @@ EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
             "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
-            "kda_chunk_bwd_workspace_size", "kda_last_error", "kda_version")
+            "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
+            "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -87,6 +88,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int,
                                             ctypes.c_uint, vp]
     L.kda_chunk_bwd.restype = c_int
+    L.kda_gate_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    L.kda_gate_bwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_gate_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, c_int, vp]
+    L.kda_gate_bwd.restype = c_int
     L.kda_decode_step_pooled.restype = c_int
     L.kda_last_error.argtypes = []
     L.kda_last_error.restype = ctypes.c_char_p
@@ -306,5 +311,25 @@ def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
         _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
         _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _ptr(workspace),
         workspace.numel() * workspace.element_size(), B, T, H, dk, dv, dt, flags,
+        _stream(stream)))
+    return out
+
+
+def kda_gate_bwd_workspace_size(B: int, T: int, H: int, dk: int) -> int:
+    return int(load_library().kda_gate_bwd_workspace_size(B, T, H, dk))
+
+
+def kda_gate_bwd(z, A, dg, workspace=None, stream=None) -> dict:
+    """Reverse mode of kda_gate: dz [B,T,H,dk] and dA [H,dk] (fp32) of <g, dg>."""
+    _dev(z, A, dg, workspace)
+    B, T, H, dk = z.shape
+    f32 = dict(device=z.device, dtype=torch.float32)
+    out = dict(dz=torch.empty(B, T, H, dk, **f32), dA=torch.empty(H, dk, **f32))
+    if workspace is None:
+        workspace = torch.empty(max(kda_gate_bwd_workspace_size(B, T, H, dk), 256),
+                                device=z.device, dtype=torch.uint8)
+    _check(load_library().kda_gate_bwd(
+        _ptr(z), _ptr(A), _ptr(dg), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), B, T, H, dk, _dtype_code(z),
         _stream(stream)))
     return out

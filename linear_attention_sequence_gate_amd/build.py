@@ -19,8 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
 ARCH = "gfx950"
-SOURCES = ["kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_backward.hip", "kda_bwd_chunk.hip",
-           "kda_api.cpp"]
+SOURCES = ["kda_gate.hip", "kda_gate_bwd.hip", "kda_decode.hip", "kda_chunk.hip", "kda_backward.hip",
+           "kda_bwd_chunk.hip", "kda_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

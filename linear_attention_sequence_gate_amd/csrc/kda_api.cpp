@@ -100,6 +100,49 @@ int kda_gate(const void *z, const float *A, float *g, int64_t B, int64_t T, int6
     return ok();
 }
 
+size_t kda_gate_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk) {
+    if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk)) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk) || H * dk > (int64_t(1) << 28)) return 0;
+    return kda::gate_bwd_workspace_bytes(B * T, (int)(H * dk));
+}
+
+int kda_gate_bwd(const void *z, const float *A, const float *dg, float *dz, float *dA,
+                 void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                 int64_t dk, int dtype, void *stream) {
+    const char *who = "kda_gate_bwd";
+    if (int e = check_dtype(dtype)) return e;
+    if (!z || !A || !dg || !dz || !dA || !workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
+    if (!valid_dim(dk)) return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld not in {32,64,128}", who, (long long)dk);
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: element count overflows", who);
+    if (H * dk > (int64_t(1) << 28))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: H*dk=%lld too large", who, (long long)(H * dk));
+    const size_t need = kda_gate_bwd_workspace_size(B, T, H, dk);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of %zu bytes", who, need);
+    const void *ptrs[] = {z, A, dg, dz, dA, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", who);
+    const void *outs[] = {dz, dA, workspace};
+    const void *ins[] = {z, A, dg};
+    for (const void *po : outs)
+        for (const void *pi : ins)
+            if (po == pi) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: outputs must not alias inputs", who);
+    if (static_cast<const void *>(dz) == dA || static_cast<const void *>(dz) == workspace ||
+        static_cast<const void *>(dA) == workspace)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: outputs must not alias each other", who);
+    hipError_t e = kda::launch_gate_bwd(z, A, dg, dz, dA, static_cast<float *>(workspace), B * T,
+                                        (int)H, (int)dk, dtype == KDA_BF16,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kda_gate_bwd launch");
+    return ok();
+}
+
 // The workspace: the range-check counter (256 bytes), then the buffers of the
 // sequence split when it is used.
 static constexpr size_t kCounterBytes = 256;

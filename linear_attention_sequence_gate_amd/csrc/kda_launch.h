@@ -52,6 +52,12 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
 hipError_t launch_pool_reset(float *pool, const int *slots, int64_t n, int64_t n_slots,
                              int64_t per_slot, hipStream_t s);
 
+// Reverse mode of the gate: dz and dA from dg over `rows` rows of H*dk
+// columns; `part` holds gate_bwd_workspace_bytes() of per-row-range dA shares.
+hipError_t launch_gate_bwd(const void *z, const float *A, const float *dg, float *dz, float *dA,
+                           float *part, int64_t rows, int H, int dk, int is_bf16, hipStream_t s);
+size_t gate_bwd_workspace_bytes(int64_t rows, int C);
+
 // Reverse mode of the recurrence (token by token over 32-column slices,
 // states recomputed from checkpoints every 8 tokens; `ckpt` is the
 // workspace, bwd_workspace_bytes() long).  Gradients are fp32; dST and dS0

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
               "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
               "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
               "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
-              "kda_chunk_bwd_workspace_size", "kda_last_error", "kda_version"):
+              "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
+              "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -238,3 +239,25 @@ def test_backward_validation(L):
     assert bwd(T=0) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(dq=Q[0]) == E.KDA_ERR_INVALID_ARGUMENT         # output aliases q
     assert bwd(S0=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
+
+
+def test_gate_backward_validation(L):
+    E = _lib
+    # per-row-range shares of dA: about 1024 workgroups of 256 columns, at most
+    # 256 ranges, at most one per row
+    assert L.kda_gate_bwd_workspace_size(4, 4096, 32, 128) == 64 * 32 * 128 * 4
+    assert L.kda_gate_bwd_workspace_size(1, 3, 1, 32) == 3 * 32 * 4
+    assert L.kda_gate_bwd_workspace_size(2, 500, 1, 32) == 256 * 32 * 4
+    assert L.kda_gate_bwd_workspace_size(1, 64, 1, 48) == 0
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+    gb = lambda z=Q[0], dz=Q[3], dA=Q[4], ws=Q[5], wsb=1 << 20, dk=32, dt=1: L.kda_gate_bwd(
+        z, Q[1], Q[2], dz, dA, ws, wsb, 2, 8, 1, dk, dt, None)
+    assert gb(z=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert gb(ws=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert gb(wsb=4) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
+    assert gb(dk=48) == E.KDA_ERR_UNSUPPORTED
+    assert gb(dt=7) == E.KDA_ERR_UNSUPPORTED
+    assert gb(dz=Q[2]) == E.KDA_ERR_INVALID_ARGUMENT         # dz aliases dg
+    assert gb(dA=Q[3]) == E.KDA_ERR_INVALID_ARGUMENT         # dA aliases dz
+    assert gb(z=BAD) == E.KDA_ERR_INVALID_ARGUMENT           # misaligned
