@@ -270,9 +270,11 @@ def bwd_chunk_flops(d):
 
 def time_backward(reps=3):
     """kda_chunk_bwd on B4 H32 d128 bf16 with T = 4096 (the benchmark's chain
-    count; T cut so the workspace -- the state entering and the gradient
-    leaving each 16-token chunk, 2 x 64 KiB per 16 tokens per chain -- takes
-    4 GiB), on the chunked path; the token-level path timed beside it."""
+    count; T cut so the workspace -- the state entering each even 16-token
+    chunk and the gradient leaving each odd one, 64 KiB per 16 tokens per
+    chain, and the token path's checkpoints -- stays at a few GiB), on the
+    chunked path; the token-level path and the gate's reverse mode timed
+    beside it."""
     B, T, H, d = 4, 4096, 32, 128
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02,
@@ -492,8 +494,9 @@ EXTRA_TRACES = {
     "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
                  "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (heads 16-31 decay-stress): the chunked path "
                  "(1 warm-up + 3 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
-                 "chunk), cb_fwd_kernel (state entering each chunk), cb_bwd_kernel (gradient "
-                 "leaving each chunk) and cb_grad_kernel (token gradients, all chunks at once)), "
+                 "chunk), cb_fwd_kernel (state entering each even chunk), cb_bwd_kernel (gradient "
+                 "leaving each odd chunk) and cb_grad_kernel (token gradients, one workgroup per "
+                 "chunk pair)), "
                  "then the token-level path (1 warm-up + 1 timed call; bwd_ckpt_kernel, "
                  "bwd_kernel, bwd_sum_kernel)."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",

@@ -224,9 +224,9 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
  * read after the write); the pages say nothing of training, so the reverse
  * mode is derived from that step.
  * Default path: 16-token chunks with fp32 matrix-core products -- the state
- * entering each chunk (forward pass) and the gradient leaving it (reverse
- * pass) go to the workspace, then every chunk's token gradients are formed
- * at once.  It relies on the range the gate floor guarantees (every 16-token
+ * entering every even chunk (forward pass) and the gradient leaving every
+ * odd one (reverse pass) go to the workspace, then the token gradients of
+ * all chunk pairs are formed at once.  It relies on the range the gate floor guarantees (every 16-token
  * sum of g from the sequence start >= -80; KDA_FLAG_CHECK_RANGE verifies it
  * as kda_chunk_fwd does).  KDA_FLAG_TOKEN_BACKWARD selects the token-level
  * reverse mode (state checkpoints every 8 tokens), which takes any g <= 0.

@@ -58,14 +58,15 @@ struct CbArgs {
     const void *q, *k, *v, *beta, *dout;
     const float *g, *S0, *dST;
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
-    float *st;                                   // [nbh][nc][DK][DV]  state entering each chunk
-    float *dn;                                   // [nbh][nc][DK][DV]  gradient leaving each chunk
+    float *st;                                   // [nbh][np][DK][DV]  state entering chunk 2p
+    float *dn;                                   // [nbh][np][DK][DV]  gradient leaving chunk 2p+1
+                                                 //                    (chunk 2p when it is the last)
     float *mat;                                  // [nbh][nc][3][16][16]  X, P, At
     float *ops;                                  // [nbh][nc][cb_ops_floats(DK)]  decayed operands
     float *w;                                    // [nbh][nc][16][DV]
     float *du;                                   // [nbh][nc][16][DV]
     int64_t T;
-    int H, DV, nc, nsl;
+    int H, DV, nc, nsl, np;                      // np = chunk pairs = ceil(nc / 2)
 };
 
 // Decayed operands of one chunk, in the layouts the two state passes copy to
@@ -351,11 +352,12 @@ __device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, C
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
     cb_stage_to_lds<DK, false>(L, stg, buf, n);
     cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, c + kCbAhead < a.nc ? c + kCbAhead : a.nc - 1, stg);
-    float *stc = a.st + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+    // the state entering each even chunk (the gradient kernel forms the odd ones)
+    float *stc = a.st + ((bh * a.np + c / 2) * DK) * a.DV + col0 + j;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int tt = wave * TPW + u;
-        if (tt < RT) {
+        if (tt < RT && (c & 1) == 0) {
 #pragma unroll
             for (int v = 0; v < kCbCT; ++v)
 #pragma unroll
@@ -477,11 +479,14 @@ __device__ __forceinline__ void cb_bwd_step(const CbArgs &a, CbPassLds<DK> &L, C
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
     cb_stage_to_lds<DK, true>(L, stg, buf, n);
     cb_fetch<T, DK, true>(a, a.dout, bh, rb, col0, c >= kCbAhead ? c - kCbAhead : 0, stg);
-    float *dnc = a.dn + ((bh * a.nc + c) * DK) * a.DV + col0 + j;
+    // the gradient leaving each odd chunk, and the last chunk (the gradient
+    // kernel forms those of the other even chunks)
+    float *dnc = a.dn + ((bh * a.np + c / 2) * DK) * a.DV + col0 + j;
+    const bool keep = (c & 1) == 1 || c == a.nc - 1;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int tt = wave * TPW + u;
-        if (tt < RT) {
+        if (tt < RT && keep) {
 #pragma unroll
             for (int v = 0; v < kCbCT; ++v)
 #pragma unroll
@@ -606,28 +611,41 @@ template <int DK, int DV> struct alignas(16) CbGradLds {
     float bm[kCB][LK];                           // bm = b - m
     float m[DK], bcm[DK], rs[DK];                // m, b_C - m, rowsum(S * dN)
     float dO[kCB][LV], U[kCB][LV], dW[kCB][LV];
+    float U0[kCB][LV];                           // U of the pair's first chunk
+    float dO1[kCB][LV], dW1[kCB][LV];            // dO, dW of the pair's second chunk
     float X[kCB][LS], At[kCB][LS], dX[kCB][LS], Y[kCB][LS], dP[kCB][LS], dAt[kCB][LS];
     float bet[kCB];
 };
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
+// Per-lane operands that turn a stored neighbour state into this chunk's:
+// the K^ rows and e^{b_C} of the previous chunk (the state entering this
+// chunk is Diag(e^{b_C}) S + K^^T U of the previous one), or the Q~, K~ rows
+// and e^{b_C} of the next chunk (the gradient leaving this chunk is
+// Diag(e^{b_C}) dN + Q~^T dO - K~^T dW of the next one).
+template <int DK> struct CbNeighbour {
+    floatx4 r1[(DK / 16 + 3) / 4], r2[(DK / 16 + 3) / 4];
+    float e[(DK / 16 + 3) / 4];
+};
+
+enum { kCbPlain = 0, kCbSFromPrev = 1, kCbNFromNext = 2 };
+
+// Token gradients of chunk c of chain bh.  The state entering the chunk is
+// read at sglob and the gradient leaving it at nglob ([DK][DV] each); with
+// kCbSFromPrev sglob holds the state entering the previous chunk (whose U is
+// in L.U0), with kCbNFromNext nglob holds the gradient leaving the next chunk
+// (whose dO, dW are in L.dO1, L.dW1), and each 16x16 block of the state is
+// formed where the products need it.
+template <typename T, int DK, int DV, int MODE>
+__device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV> &L, int64_t bh,
+                                              int c, int wave, const float *sglob,
+                                              const float *nglob, const CbNeighbour<DK> &nb) {
     using Lds = CbGradLds<DK, DV>;
-    constexpr int RT = DK / 16, CT = DV / 16;
-    __shared__ Lds L;
-    const int64_t unit = blockIdx.x;
-    const int64_t bh = unit / a.nc;
-    const int c = (int)(unit % a.nc);
+    constexpr int RT = DK / 16, CT = DV / 16, NT = (RT + 3) / 4, KB = DV / 16;
+    const int64_t unit = bh * a.nc + c;
     const int64_t t0 = (int64_t)c * kCB;
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
     const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
     const int64_t rb = cb_rowbase(a, bh);
-    constexpr int NT = (RT + 3) / 4, KB = DV / 16;
-    const float *stc = a.st + unit * DK * DV;
-    const float *dnc = a.dn + unit * DK * DV;
-    // 1. inputs
     const float *wc = a.w + unit * kCB * DV;    // W, dU of the chunk: [16][DV]
     const float *duc = a.du + unit * kCB * DV;
     // q, k of this lane's tokens 4 g4 + i and channels 16 ct + j (step 4),
@@ -649,6 +667,8 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
             kin[u][i] = 4 * g4 + i < n ? kin[u][i] : 0.f;
         }
     }
+    lds_barrier();                               // the previous chunk is done with LDS
+    // 1. inputs
     if (tid < DK) {
         float gv[kCB], b[kCB];
         cb_load16<float>(a.g, rb, t0, n, a.H, DK, tid, gv);
@@ -768,8 +788,23 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int k0 = 16 * kb;
-                const floatx4 sv = ld4(stc + (int64_t)cr * DV + k0 + 4 * g4);
-                const floatx4 nv = ld4(dnc + (int64_t)cr * DV + k0 + 4 * g4);
+                floatx4 sv = ld4(sglob + (int64_t)cr * DV + k0 + 4 * g4);
+                floatx4 nv = ld4(nglob + (int64_t)cr * DV + k0 + 4 * g4);
+                if constexpr (MODE == kCbSFromPrev) {
+                    // transposed form: rows of the block are value columns,
+                    // columns key channels, as sv is laid out
+                    sv *= nb.e[u];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv = mfma1(L.U0[4 * g4 + i][k0 + j], nb.r1[u][i], sv);
+                }
+                if constexpr (MODE == kCbNFromNext) {
+                    nv *= nb.e[u];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        nv = mfma1(L.dO1[4 * g4 + i][k0 + j], nb.r1[u][i], nv);
+                        nv = mfma1(-L.dW1[4 * g4 + i][k0 + j], nb.r2[u][i], nv);
+                    }
+                }
                 const floatx4 o4 = ld4(&L.dO[j][k0 + 4 * g4]);
                 const floatx4 w4 = ld4(&L.dW[j][k0 + 4 * g4]);
                 const floatx4 u4 = ld4(&L.U[j][k0 + 4 * g4]);
@@ -843,12 +878,82 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
             if (r < n) a.dg[(rb + (t0 + r) * a.H) * DK + ch] = db[i] + later + extra;
         }
     }
+
+}
+
+// Token gradients of the chunk pair (2p, 2p+1) of one chain.  The passes
+// stored the state entering chunk 2p and the gradient leaving chunk 2p+1 (or
+// 2p when it is the last chunk); chunk 2p+1 forms the state entering it from
+// the first, chunk 2p the gradient leaving it from the second.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
+    using Lds = CbGradLds<DK, DV>;
+    constexpr int RT = DK / 16, CT = DV / 16, NT = (RT + 3) / 4;
+    __shared__ Lds L;
+    const int64_t pair = blockIdx.x;
+    const int64_t bh = pair / a.np;
+    const int c0 = 2 * (int)(pair % a.np), c1 = c0 + 1;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float *stp = a.st + pair * DK * DV;
+    const float *dnp = a.dn + pair * DK * DV;
+    CbNeighbour<DK> nb;
+    if (c1 >= a.nc) {
+        cb_grad_chunk<T, DK, DV, kCbPlain>(a, L, bh, c0, wave, stp, dnp, nb);
+        return;
+    }
+    // U of chunk c0 (full: c1 follows it) into L.U0; its K^ rows and e^{b_C}
+    const int64_t rb = cb_rowbase(a, bh);
+    {
+        const int64_t unit0 = bh * a.nc + c0;
+        const float *wc = a.w + unit0 * kCB * DV;
+        const float *mc = a.mat + unit0 * kCbMat;
+        L.X[tid >> 4][tid & 15] = mc[tid];
+        if (tid < kCB) L.bet[tid] = cb_ld<T>(a.beta, rb + ((int64_t)c0 * kCB + tid) * a.H);
+        lds_barrier();
+        for (int ct = wave; ct < CT; ct += 4) {
+            const int cc = 16 * ct + j;
+            floatx4 U = {0, 0, 0, 0};
+            const floatx4 xr = ld4(&L.X[j][4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                U = mfma1(xr[i], L.bet[4 * g4 + i] * wc[(4 * g4 + i) * DV + cc], U);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.U0[4 * g4 + i][cc] = U[i];
+        }
+        const float *op = a.ops + unit0 * cb_ops_floats(DK);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+            nb.r1[u] = ld4(op + kOpKhT * DK + ch * kCB + 4 * g4);   // K^[4 g4 + i][ch]
+            nb.e[u] = op[kOpEbc * DK + ch];
+        }
+    }
+    cb_grad_chunk<T, DK, DV, kCbSFromPrev>(a, L, bh, c1, wave, stp, dnp, nb);
+    // keep chunk c1's dO and dW for chunk c0; its Q~, K~ rows and e^{b_C}
+    lds_barrier();
+    for (int e = tid; e < kCB * DV; e += 256) {
+        const int r = e / DV, cc = e % DV;
+        L.dO1[r][cc] = L.dO[r][cc];
+        L.dW1[r][cc] = L.dW[r][cc];
+    }
+    {
+        const float *op = a.ops + (bh * a.nc + c1) * cb_ops_floats(DK);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+            nb.r1[u] = ld4(op + kOpQtT * DK + ch * kCB + 4 * g4);   // Q~[4 g4 + i][ch]
+            nb.r2[u] = ld4(op + kOpKtT * DK + ch * kCB + 4 * g4);   // K~[4 g4 + i][ch]
+            nb.e[u] = op[kOpEbc * DK + ch];
+        }
+    }
+    cb_grad_chunk<T, DK, DV, kCbNFromNext>(a, L, bh, c0, wave, stp, dnp, nb);
 }
 
 size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
-    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
+    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB, np = (nc + 1) / 2;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t st = r256((size_t)nbh * nc * dk * dv * sizeof(float));
+    const size_t st = r256((size_t)nbh * np * dk * dv * sizeof(float));
     const size_t mat = r256((size_t)nbh * nc * kCbMat * sizeof(float));
     const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
     const size_t ops = r256((size_t)nbh * nc * cb_ops_floats(dk) * sizeof(float));
@@ -864,7 +969,7 @@ static hipError_t cb_inst(CbArgs a, int64_t nbh, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((cb_bwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 grid((unsigned)(nbh * a.nc));
+    const dim3 grid((unsigned)(nbh * a.np));
     switch (a.DV) {
     case 32: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 32>), grid, dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 64>), grid, dim3(256), 0, s, a); break;
@@ -888,7 +993,8 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout;
     a.g = g; a.S0 = S0; a.dST = dST;
     a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
-    const size_t st = r256((size_t)nbh * nc * dk * dv * sizeof(float));
+    const int64_t np = (nc + 1) / 2;
+    const size_t st = r256((size_t)nbh * np * dk * dv * sizeof(float));
     const size_t mat = r256((size_t)nbh * nc * kCbMat * sizeof(float));
     const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
     a.st = reinterpret_cast<float *>(p);
@@ -897,7 +1003,7 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
     a.w = reinterpret_cast<float *>(p + 2 * st + mat);
     a.du = reinterpret_cast<float *>(p + 2 * st + mat + wv);
     a.ops = reinterpret_cast<float *>(p + 2 * st + mat + 2 * wv);
-    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / kCbNS;
+    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / kCbNS; a.np = (int)np;
     switch (dk) {
     case 32: return is_bf16 ? cb_inst<bf16, 32>(a, nbh, s) : cb_inst<float, 32>(a, nbh, s);
     case 64: return is_bf16 ? cb_inst<bf16, 64>(a, nbh, s) : cb_inst<float, 64>(a, nbh, s);

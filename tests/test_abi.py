@@ -210,13 +210,14 @@ def test_backward_validation(L):
     # the range-check counter, then the larger of the two paths' buffers:
     # token path = state checkpoints every 8 tokens per 32-column slice plus,
     # with several slices, their partial row gradients (dq, dk, dg, dbeta);
-    # chunked path = state entering and gradient leaving each 16-token chunk,
-    # three 16x16 matrices and the decayed operands (81 dk floats) per chunk,
-    # and W, dU per token
+    # chunked path = the state entering each even 16-token chunk and the
+    # gradient leaving each odd (or last) one, three 16x16 matrices and the
+    # decayed operands (81 dk floats) per chunk, and W, dU per token
     def chunked(nbh, T, dk, dv):
         r = lambda x: (x + 255) // 256 * 256
         nc = (T + 15) // 16
-        return (2 * r(nbh * nc * dk * dv * 4) + r(nbh * nc * 768 * 4) + 2 * r(nbh * nc * 16 * dv * 4)
+        npair = (nc + 1) // 2
+        return (2 * r(nbh * npair * dk * dv * 4) + r(nbh * nc * 768 * 4) + 2 * r(nbh * nc * 16 * dv * 4)
                 + r(nbh * nc * 81 * dk * 4))
     assert chunked(1, 64, 32, 32) > 8 * 32 * 32 * 4
     assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 256 + chunked(1, 64, 32, 32)
