@@ -5,14 +5,16 @@
 
 A timed step is one pass of the prefill hot path over the synthetic batch
 B4 H32 T32768 d128 bf16 (heads 16..31 with the gate near its floor):
-kda_gate (z -> g) followed by kda_chunk_fwd (q, k, v, g, beta -> o, final
-state).  The decode step (256 sequences x H32, d128, fp32 state of 512 MiB
+kda_chunk_fwd_gated (q, k, v, z, A, beta -> o, final state), the gate
+evaluated inside the chunk kernel.  The two-kernel form of the same step
+(kda_gate z -> g, then kda_chunk_fwd) is timed beside it.  The decode step (256 sequences x H32, d128, fp32 state of 512 MiB
 updated in place) is timed in the same run over 1000 consecutive steps with
 fresh pre-generated inputs, and reported in the same JSON line.
 
 value        prefill tokens/s (B*T tokens, all 32 heads, per wall-clock step)
-roofline     the chunked-prefill kernel against HBM: its arithmetic intensity
-             (~99 flop/B) is below the MI355X ridge (~312 flop/B)
+roofline     the step's one kernel (chunk32_kernel with the gate fused) against
+             HBM: its arithmetic intensity (~118 flop/B) is below the MI355X
+             ridge (~312 flop/B)
 cpu_baseline the fp64 oracle timed on this host on a bounded sample of the same
              workload (a reported baseline, not a target)
 
@@ -61,7 +63,10 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", f"hbm_traffic_{PROFILE_TAG}.md")
 TRACE_MD = os.path.join(ROOT, "profiles", f"kernel_trace_{PROFILE_TAG}.md")
 # kernel -> (name fragments in a profiler trace, sources that define it)
 KERNELS = {
-    "chunk_fwd": (("chunk32_kernel", "chunk_fwd_kernel"), ("kda_chunk.hip", "kda_device.h")),
+    "fused_fwd": (("chunk32_kernel<128, true>", "chunk32_kernelILi128ELb1E"),
+                  ("kda_chunk.hip", "kda_device.h")),
+    "chunk_fwd": (("chunk32_kernel<128, false>", "chunk32_kernelILi128ELb0E", "chunk_fwd_kernel"),
+                  ("kda_chunk.hip", "kda_device.h")),
     "decode_step": (("decode_step_kernel",), ("kda_decode.hip", "kda_device.h")),
     "gate": (("gate_kernel",), ("kda_gate.hip", "kda_device.h")),
 }
@@ -76,10 +81,12 @@ INV_FLOPS_PER_HT = 2218
 
 
 def prefill_work(w, B=None, T=None, H=None):
-    """Algorithmic bytes and flops of one kda_chunk_fwd call (and of the gate).
+    """Algorithmic bytes and flops of one kda_chunk_fwd call (and of the gate,
+    and of the fused call kda_chunk_fwd_gated).
 
     Bytes: q, k, v, beta and o once in the input dtype, g once in fp32, the
-    final state (and the initial one when given) in fp32.
+    final state (and the initial one when given) in fp32.  The fused call reads
+    z in the input dtype instead of g, and the [H, dk] table A.
     Flops per head-token (C = 64, dense 16-token diagonal subtiles, mean causal
     length Lbar = (64 + 16) / 2 = 40): 6 dk dv for W S, Q~ S and K^T U; 2 Lbar
     dk each for A, P and W; 2 Lbar dv each for U' and P U; the UT inverse."""
@@ -92,8 +99,10 @@ def prefill_work(w, B=None, T=None, H=None):
     Lbar = (64 + 16) / 2
     flops_per_ht = 6 * dk * dv + 2 * Lbar * (3 * dk + 2 * dv) + INV_FLOPS_PER_HT
     gate_bytes = ht * dk * (e + 4)
+    fused_bytes = chunk_bytes - ht * dk * (4 - e) + H * dk * 4
     return dict(head_tokens=ht, chunk_bytes=chunk_bytes, chunk_flops=flops_per_ht * ht,
-                flops_per_head_token=flops_per_ht, gate_bytes=gate_bytes)
+                flops_per_head_token=flops_per_ht, gate_bytes=gate_bytes,
+                fused_bytes=fused_bytes)
 
 
 def decode_bytes(w):
@@ -150,13 +159,46 @@ def time_copy(reps=5):
 
 
 def time_prefill(steps, warmup):
+    """The timed step, kda_chunk_fwd_gated: one launch of the chunk kernel with
+    the gate fused (HIP events around each launch on its stream)."""
     w = PREFILL
     dev = torch.device("cuda")
     x = inputs.workload_prefill_inputs(w, device=dev)
+    o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
+    ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
+    ws = torch.empty(max(_lib.kda_chunk_fwd_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 1), 256),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()     # the kernel is launched on it
+
+    def step(evs=None):
+        if evs: evs[0].record(stream)
+        _lib.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
+                                 final_state=ST, o=o, workspace=ws, stream=stream)
+        if evs: evs[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    return dict(x=x, o=o, ST=ST, wall_s=wall, fused_ms=fused_ms)
+
+
+def time_two_kernel(x, steps, warmup=2):
+    """The same step as two launches, kda_gate (z -> g in HBM) then
+    kda_chunk_fwd, each bracketed by HIP events on the launch stream."""
+    w = PREFILL
+    dev = torch.device("cuda")
     g = torch.empty(x["z"].shape, device=dev, dtype=torch.float32)
     o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
     ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
-    stream = torch.cuda.current_stream()     # both kernels are launched on it
+    stream = torch.cuda.current_stream()
 
     def step(evs=None):
         if evs: evs[0].record(stream)
@@ -170,15 +212,14 @@ def time_prefill(steps, warmup):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     gate_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     chunk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    return dict(x=x, g=g, o=o, ST=ST, wall_s=wall, gate_ms=gate_ms, chunk_ms=chunk_ms)
+    del g, o, ST
+    torch.cuda.empty_cache()
+    return dict(gate_ms=gate_ms, chunk_ms=chunk_ms)
 
 
 LONG = inputs.WORKLOADS["prefill_h32_t1m"]
@@ -451,10 +492,11 @@ def ingest_pmc(fetch_dir, write_dir):
                              "source_sha256": source_hash(srcs)}
     w = PREFILL
     work = prefill_work(w)
-    alg = {"chunk_fwd": work["chunk_bytes"], "decode_step": decode_bytes(DECODE),
-           "gate": work["gate_bytes"]}
+    alg = {"fused_fwd": work["fused_bytes"], "chunk_fwd": work["chunk_bytes"],
+           "decode_step": decode_bytes(DECODE), "gate": work["gate_bytes"]}
     lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
-             "Workloads: prefill B4 H32 T32768 d128 bf16 (gate + chunk), decode 256x32 d128.",
+             "Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step, then gate + chunk),",
+             "decode 256x32 d128.",
              "Each counter is scaled by the factor that maps its reading for a plain",
              "1 GiB device copy (torch `copy_` -> the runtime's copyBuffer kernel, timed",
              "in the same script) to 1 GiB.", "",
@@ -521,9 +563,10 @@ def ingest_trace(d):
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     lines = ["# Kernel durations (rocprofv3 kernel trace)", "",
-             "Workloads: prefill B4 H32 T32768 d128 bf16 (gate + chunk per step, 3 warm-up",
-             "and 10 timed steps), decode 256x32 d128 (20 warm-up + 200 steps), plus the",
-             "1 GiB calibration copy.  Durations from the trace's start/end timestamps.", "",
+             "Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step: 3 warm-up and 10",
+             "timed launches; then gate + chunk as two kernels: 2 warm-up and 10 timed steps),",
+             "decode 256x32 d128 (20 warm-up + 200 steps), plus the 1 GiB calibration copy.",
+             "Durations from the trace's start/end timestamps.", "",
              "Command (from the repository root):", "", "    " + TRACE_CMD,
              "    python3 bench.py --ingest-trace gpurun_out/ktrace", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | avg without first call (us) |",
@@ -614,14 +657,14 @@ def ingest_sq(dirs):
                 rows = _pmc_rows(d, ctr)
             except SystemExit:
                 continue
-            v = [x for n, x in rows if "chunk32_kernel" in n]
+            v = [x for n, x in rows if _matches(n, KERNELS["fused_fwd"][0])]
             if v:
                 vals[ctr] = sum(v) / len(v)
     w = PREFILL
     periods = (w.T + 31) // 32 + 2                 # pipeline periods per workgroup
     wgs = w.B * w.H * (w.dv // 64)
     simd_periods = wgs * 4 * periods
-    lines = ["# Shader-sequencer counters, chunk32_kernel (rocprofv3 --pmc)", "",
+    lines = ["# Shader-sequencer counters, chunk32_kernel with the gate fused (rocprofv3 --pmc)", "",
              "Workload: prefill B4 H32 T32768 d128 bf16, 256 workgroups of 12 waves, "
              f"{periods} periods of 32 tokens each.", "",
              "Commands (from the repository root):", ""]
@@ -655,7 +698,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the first ~10 launches of a fresh process run up to 30% slower (clocks
+    # ramping; visible in a kernel trace), so the default warm-up covers them
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -697,17 +742,20 @@ def main():
 
     copy_gbs = time_copy()
     res = time_prefill(args.steps, args.warmup)
+    two = time_two_kernel(res["x"], args.steps)
     w = PREFILL
     work = prefill_work(w)
     ms_per_step = res["wall_s"] * 1e3 / args.steps
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3)
-    chunk_s = res["chunk_ms"] / 1e3
-    gate_ms = res["gate_ms"]
-    chunk_gbs = work["chunk_bytes"] / chunk_s / 1e9
-    chunk_tflops = work["chunk_flops"] / chunk_s / 1e12
-    ai = work["chunk_flops"] / work["chunk_bytes"]
+    fused_s = res["fused_ms"] / 1e3
+    fused_gbs = work["fused_bytes"] / fused_s / 1e9
+    fused_tflops = work["chunk_flops"] / fused_s / 1e12
+    ai = work["chunk_flops"] / work["fused_bytes"]
     attainable_tflops = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+    chunk_s = two["chunk_ms"] / 1e3
+    gate_ms = two["gate_ms"]
+    chunk_gbs = work["chunk_bytes"] / chunk_s / 1e9
 
     parity = {} if args.no_parity else parity_sample(res)
     cpu = None if args.no_cpu_baseline else cpu_baseline(res["x"], budget_s=args.cpu_budget)
@@ -736,22 +784,29 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "KDA prefill B4 H32 T32768 d128 bf16, heads 16-31 decay-stress "
-                               "(gate + chunked prefill per step); decode 256x32 d128 fp32 state",
+                               "(gate + chunked prefill per step, one fused launch); decode "
+                               "256x32 d128 fp32 state",
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "dk": w.dk, "dv": w.dv,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": chunk_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": chunk_gbs / HBM_PEAK_GBS, "traffic": traffic["chunk_fwd"],
-                     "kernel": "chunk32_kernel<128> (64-column dv slices)",
-                     "bytes_per_launch": work["chunk_bytes"], "avg_ms": chunk_s * 1e3},
-        "prefill": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
-                    "gate_gbs": work["gate_bytes"] / (gate_ms / 1e3) / 1e9,
-                    "gate_traffic": traffic["gate"],
-                    "chunk_alg_tflops": chunk_tflops,
-                    "chunk_flops_per_head_token": work["flops_per_head_token"],
-                    "chunk_arith_intensity": ai,
-                    "mfma_frac_of_bf16_peak": chunk_tflops / BF16_PEAK_TFLOPS,
-                    "roofline_frac_of_attainable": chunk_tflops / attainable_tflops,
-                    "head_tokens": work["head_tokens"]},
+        "roofline": {"bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic["fused_fwd"],
+                     "kernel": "chunk32_kernel<128, true> (gate fused, 64-column dv slices)",
+                     "bytes_per_launch": work["fused_bytes"], "avg_ms": fused_s * 1e3},
+        "prefill": {"fused_ms": fused_s * 1e3,
+                    "alg_tflops": fused_tflops,
+                    "flops_per_head_token": work["flops_per_head_token"],
+                    "arith_intensity": ai,
+                    "mfma_frac_of_bf16_peak": fused_tflops / BF16_PEAK_TFLOPS,
+                    "roofline_frac_of_attainable": fused_tflops / attainable_tflops,
+                    "head_tokens": work["head_tokens"],
+                    "two_kernel": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
+                                   "step_ms": gate_ms + chunk_s * 1e3,
+                                   "gate_gbs": work["gate_bytes"] / (gate_ms / 1e3) / 1e9,
+                                   "gate_traffic": traffic["gate"],
+                                   "chunk_gbs": chunk_gbs,
+                                   "chunk_hbm_frac": chunk_gbs / HBM_PEAK_GBS,
+                                   "chunk_bytes_per_launch": work["chunk_bytes"],
+                                   "chunk_traffic": traffic["chunk_fwd"]}},
         "prefill_long": long_res,
         "prefill_pairwise_diagonal": pair_res,
         "prefill_backward": bwd_res,

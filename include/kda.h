@@ -198,6 +198,31 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   int dtype, unsigned flags, void *stream);
 
 /*
+ * kda_chunk_fwd_gated -- kda_gate and kda_chunk_fwd as one call: the gate
+ * g = -5 sigmoid(exp(A) z) of the same section of "Kimi K3 internal structure
+ * analysis" is evaluated where the chunk kernel loads each chunk, so g never
+ * goes through device memory.
+ *   z : [B, T, H, dk] dtype (input, as given to kda_gate)
+ *   A : [H, dk]       fp32  (input)
+ * Every other argument is as for kda_chunk_fwd (g is not taken).  The gate is
+ * evaluated with the hardware base-2 exponential and reciprocal: alpha agrees
+ * with exp(kda_gate's g) to a few fp32 ulp, so o and final_state agree with
+ * kda_gate followed by kda_chunk_fwd to fp32 rounding, not bit for bit.
+ * bf16 inputs with dk = 128 and dv in {64, 128} run fused (the workspace is
+ * then exactly what kda_chunk_fwd takes, including the sequence split and
+ * KDA_FLAG_PAIRWISE_DIAGONAL); other shapes run the gate kernel into the
+ * start of the workspace first.  KDA_FLAG_CHECK_RANGE is rejected
+ * (INVALID_ARGUMENT): the gate's floor bounds g by construction.
+ */
+size_t kda_chunk_fwd_gated_workspace_size(int64_t B, int64_t T, int64_t H,
+                                          int64_t dk, int64_t dv, int dtype);
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *z,
+                        const float *A, const void *beta, const float *initial_state,
+                        float *final_state, void *o, void *workspace, size_t workspace_bytes,
+                        int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                        int dtype, unsigned flags, void *stream);
+
+/*
  * kda_decode_step -- one token for each of N independent sequences x H heads,
  * with the gate fused and the state updated IN PLACE (read once, written once).
  *   (The studioglobal.ai summary of the Kimi K3 report, KDA section: a

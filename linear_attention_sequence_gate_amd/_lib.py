@@ -38,6 +38,7 @@ EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
             "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
+            "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
             "kda_last_error", "kda_version")
 
 
@@ -71,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd.restype = c_int
+    L.kda_chunk_fwd_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
+    L.kda_chunk_fwd_gated_workspace_size.restype = ctypes.c_size_t
+    L.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                      i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd_gated.restype = c_int
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp]
     L.kda_decode_step.restype = c_int
     L.kda_state_pool_reset.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp]
@@ -189,6 +195,39 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
     _check(load_library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(final_state),
         _ptr(o), _ptr(workspace), ws_bytes, B, T, H, dk, dv, dt, flags, _stream(stream)))
+    return o, final_state
+
+
+def kda_chunk_fwd_gated_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
+                                       nseg: Optional[int] = None) -> int:
+    """Workspace bytes for kda_chunk_fwd_gated (nseg: an explicit segment count)."""
+    L = load_library()
+    gated = int(L.kda_chunk_fwd_gated_workspace_size(B, T, H, dk, dv, dtype))
+    return max(gated, kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype, nseg))
+
+
+def kda_chunk_fwd_gated(q, k, v, z, A, beta, initial_state=None, final_state=None, o=None,
+                        want_final_state: bool = True, flags: int = 0, workspace=None,
+                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gate and chunkwise prefill in one call (g from z and A inside it).
+    Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    _dev(q, k, v, z, A, beta, initial_state, final_state, o, workspace)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, dk, dv), device=q.device, dtype=torch.float32)
+    if workspace is None:
+        nseg = (flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT
+        ws_bytes = kda_chunk_fwd_gated_workspace_size(B, T, H, dk, dv, dt, nseg)
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().kda_chunk_fwd_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(initial_state),
+        _ptr(final_state), _ptr(o), _ptr(workspace), ws_bytes, B, T, H, dk, dv, dt, flags,
+        _stream(stream)))
     return o, final_state
 
 

@@ -170,6 +170,23 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
     return kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, 0);
 }
 
+// kda_chunk_fwd_gated: shapes without the fused gate stage g at the start of
+// the workspace, B*T*H*dk fp32 rounded up to 256 bytes
+static size_t gate_stage_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int dtype) {
+    if (kda::seq_split_supported((int)dk, (int)dv, dtype == KDA_BF16)) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk) || !mul_ok(n, 4)) return SIZE_MAX;
+    return ((size_t)n + 255) / 256 * 256;
+}
+
+size_t kda_chunk_fwd_gated_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                          int dtype) {
+    const size_t base = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype);
+    if (base == 0) return 0;
+    const size_t gb = gate_stage_bytes(B, T, H, dk, dv, dtype);
+    return gb == SIZE_MAX ? 0 : gb + base;
+}
+
 }  // extern "C"
 
 namespace {
@@ -179,10 +196,14 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
                    const void *beta, const float *initial_state, float *final_state, void *o,
                    void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
                    int64_t dk, int64_t dv, int dtype, unsigned flags, const int32_t *slots,
-                   int64_t n_slots, const int64_t *cu_seqlens, void *stream) {
+                   int64_t n_slots, const int64_t *cu_seqlens, const void *z, const float *Ag,
+                   void *stream) {
     if (int e = check_dtype(dtype)) return e;
-    if (!q || !k || !v || !g || !beta || !o)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (q, k, v, g, beta, o are required)", who);
+    // gated: g comes from (z, A) inside the call
+    const bool gated = z != nullptr || Ag != nullptr;
+    if (!q || !k || !v || !beta || !o || (gated ? (!z || !Ag) : !g))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (q, k, v, %s, beta, o are required)", who,
+                    gated ? "z, A" : "g");
     if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
     if (!valid_dim(dk) || !valid_dim(dv))
@@ -211,14 +232,37 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     // the kernel addresses the tokens of one 64-token chunk with 32-bit byte offsets
     if (H * (dk > dv ? dk : dv) * 64 * 4 >= (int64_t(1) << 32))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: H=%lld too large", who, (long long)H);
-    const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, workspace};
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, final_state, o, workspace, z, Ag};
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: pointers must be 16-byte aligned", who);
-    const void *ins[] = {q, k, v, g, beta, initial_state};
+    const void *ins[] = {q, k, v, g, beta, initial_state, z, Ag};
     for (const void *p : ins)
-        if (p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o must not alias an input", who);
+        if (p && p == o) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o must not alias an input", who);
+    if (gated && (flags & KDA_FLAG_CHECK_RANGE))
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: g comes from the gate inside the call and lies in [-5, 0] by construction; "
+                    "KDA_FLAG_CHECK_RANGE checks a caller's g", who);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // the fused gate runs in the pipelined kernel; other shapes stage g in
+    // the workspace with the gate kernel first
+    const bool fused = gated && kda::seq_split_supported((int)dk, (int)dv, dtype == KDA_BF16);
+    if (gated && !fused) {
+        const size_t gb = gate_stage_bytes(B, T, H, dk, dv, dtype);
+        if (!workspace || workspace_bytes < gb)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of %zu bytes for g", who,
+                        kda_chunk_fwd_gated_workspace_size(B, T, H, dk, dv, dtype));
+        float *gs = static_cast<float *>(workspace);
+        const void *tens[] = {q, k, v, z, Ag, beta, initial_state, final_state, o};
+        for (const void *p : tens)
+            if (p == static_cast<const void *>(gs))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the workspace must not alias a tensor", who);
+        hipError_t e = kda::launch_gate(z, Ag, gs, B * T * H * dk, (int)H, (int)dk, dtype == KDA_BF16, s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_gated gate launch");
+        g = gs;
+        workspace = static_cast<char *>(workspace) + gb;
+        workspace_bytes -= gb;
+    }
 
     if (flags & KDA_FLAG_CHECK_RANGE) {
         if (!workspace || workspace_bytes < kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
@@ -253,7 +297,8 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
                                          (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
-                                         pairwise ? 1 : 0, cu_seqlens, s);
+                                         pairwise ? 1 : 0, cu_seqlens, fused ? z : nullptr,
+                                         fused ? Ag : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }
@@ -268,7 +313,18 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
                   int dtype, unsigned flags, void *stream) {
     return chunk_fwd_impl("kda_chunk_fwd", q, k, v, g, beta, initial_state, final_state, o,
                           workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, nullptr, 0,
-                          nullptr, stream);
+                          nullptr, nullptr, nullptr, stream);
+}
+
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *z, const float *A,
+                        const void *beta, const float *initial_state, float *final_state, void *o,
+                        void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                        int64_t dk, int64_t dv, int dtype, unsigned flags, void *stream) {
+    if (!z || !A)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_gated: null pointer (z and A are required)");
+    return chunk_fwd_impl("kda_chunk_fwd_gated", q, k, v, nullptr, beta, initial_state, final_state, o,
+                          workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, nullptr, 0,
+                          nullptr, z, A, stream);
 }
 
 int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const float *g,
@@ -289,7 +345,7 @@ int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const floa
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_chunk_fwd_pooled: o must not alias an input");
     return chunk_fwd_impl("kda_chunk_fwd_pooled", q, k, v, g, beta, state_pool, state_pool, o,
                           workspace, workspace_bytes, B, T, H, dk, dv, dtype, flags, slots,
-                          n_slots, nullptr, stream);
+                          n_slots, nullptr, nullptr, nullptr, stream);
 }
 
 int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, const float *g,
@@ -314,7 +370,7 @@ int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, con
     // the size checks; the kernel reads sequence b's rows from cu_seqlens
     return chunk_fwd_impl(who, q, k, v, g, beta, state_pool, state_pool, o, nullptr, 0, B,
                           total_tokens, H, dk, dv, dtype, flags | KDA_FLAG_SEGMENTS(1), slots,
-                          n_slots, cu_seqlens, stream);
+                          n_slots, cu_seqlens, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

@@ -82,6 +82,11 @@ struct ChunkArgs {
     // cu_seqlens[b] .. cu_seqlens[b+1] - 1 of a packed [T, H, ...] layout
     // (T = all tokens); null for the [B, T, H, ...] layout
     const int64_t *cu_seqlens;
+    // chunk32_kernel<DK, true>: the gate is evaluated in the kernel from z
+    // (the input dtype, [.., H, dk] like k) and the [H, dk] table A; g is
+    // then unused
+    const void *z;
+    const float *Ag;
 };
 
 // Row of a sequence's state (b, h) in S0/ST: b * H + h, or with a slot table
@@ -962,7 +967,7 @@ template <int DK> struct PipeLds {
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-template <int DK>
+template <int DK, bool ZIN>
 __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     constexpr int NV = 64;
     using Lds = PipeLds<DK>;
@@ -1050,6 +1055,11 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         const T *__restrict__ kp = static_cast<const T *>(a.k);
         const T *__restrict__ bp = static_cast<const T *>(a.beta);
         const float *__restrict__ gp = a.g;
+        const T *__restrict__ zp = static_cast<const T *>(a.z);
+        // fused gate: -log2(e) e^{A} of this lane's two channels, so that
+        // e^{-e^{A} z} = 2^{zc z}
+        floatx2 zc = {0.0f, 0.0f};
+        if constexpr (ZIN) zc = gate_zscale2(a.Ag + h * DK + c0);
 
         // the blocks above the diagonal of P (hi, lo) and T in every slot are
         // read by the 32-deep products and never written: zero them once
@@ -1064,7 +1074,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         // periods before its use (one 32-token period is shorter than the
         // memory latency under load)
         struct Raw {
-            floatx2 g[TPL];
+            // g (fp32 pair), or z (two bf16) when the gate is fused
+            typename std::conditional<ZIN, unsigned, floatx2>::type g[TPL];
             unsigned k[TPL], q[TPL];                // two bf16 each
             unsigned beta;                          // bf16 bits, zero-extended
         };
@@ -1078,7 +1089,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             const int64_t t0 = tbeg + ch * kPipeChunk;
             const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
             const int64_t tok0 = (tok_base + t0) * H + h;
-            const char *gb = uniform_base(gp + tok0 * DK);
+            const char *gb = ZIN ? uniform_base(zp + tok0 * DK) : uniform_base(gp + tok0 * DK);
             const char *kb = uniform_base(kp + tok0 * DK), *qb = uniform_base(qp + tok0 * DK);
             const char *bb = uniform_base(bp + tok0);
             // full chunk: row i of the lane is a scalar step from its first
@@ -1101,7 +1112,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const unsigned row = tail ? 0u : (unsigned)i * HDK * 2u;
-                r.g[i] = vm_load8_nt(gb + 2u * row, 2u * okq[i]);
+                if constexpr (ZIN) r.g[i] = vm_load4(gb + row, okq[i]);
+                else r.g[i] = vm_load8_nt(gb + 2u * row, 2u * okq[i]);
                 r.k[i] = vm_load4(kb + row, okq[i]);
                 r.q[i] = vm_load4(qb + row, okq[i]);
             }
@@ -1137,15 +1149,20 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             if (live) {
                 // ---- P1: alpha and running products; subtile-local tiles ---
                 floatx2 R[TPL], Et[TPL], eLam;
+                // log2(alpha) = g log2(e) of this lane's elements
+                floatx2 l2a[TPL];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    if constexpr (ZIN) l2a[i] = gate_log2_alpha2(zc, unpack2(raw.g[i]));
+                    else l2a[i] = raw.g[i] * kLog2e;
+                }
                 {
                     // past the end of the sequence alpha = 1 (g = 0): e^{b_C} stops at
                     // the last token; beta = 0 there zeroes those rows of A and T
                     floatx2 al[TPL];
 #pragma unroll
-                    for (int i = 0; i < TPL; ++i) {
-                        const floatx2 x = raw.g[i] * kLog2e;
-                        al[i] = floatx2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
-                    }
+                    for (int i = 0; i < TPL; ++i)
+                        al[i] = floatx2{__builtin_amdgcn_exp2f(l2a[i][0]), __builtin_amdgcn_exp2f(l2a[i][1])};
                     if (L < kPipeChunk) {
 #pragma unroll
                         for (int i = 0; i < TPL; ++i) {
@@ -1189,7 +1206,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int i = 0; i < TPL; ++i) {
                         const bool in = tb + i < L;
-                        gl[i] = in ? raw.g[i] * kLog2e : floatx2{0.0f, 0.0f};
+                        gl[i] = in ? l2a[i] : floatx2{0.0f, 0.0f};
                     }
                     floatx2 totg = gl[0];
 #pragma unroll
@@ -1775,10 +1792,15 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
-                            const int64_t *cu_seqlens, hipStream_t s) {
+                            const int64_t *cu_seqlens, const void *z, const float *Ag,
+                            hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
+    // the gate inside the kernel: pipelined kernel only
+    const bool zin = z != nullptr;
+    if (zin && (!pipe || !Ag)) return hipErrorInvalidValue;
+    auto kern = zin ? chunk32_kernel<128, true> : chunk32_kernel<128, false>;
     const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
@@ -1792,6 +1814,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.n_slots = n_slots;
     args.pairwise = pipe && pairwise ? 1 : 0;
     args.cu_seqlens = cu_seqlens;
+    args.z = z;
+    args.Ag = Ag;
     if (cu_seqlens && (!pipe || nseg >= 2)) return hipErrorInvalidValue;
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
     if (pipe && P >= 2) {
@@ -1808,7 +1832,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         args.phase = 1;
         args.nslice = args.nsl_v + dk / 64;
         args.xcd_map = units % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(units * args.nslice), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(kern, dim3(units * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (P >= 3) {
@@ -1821,12 +1845,12 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         args.phase = 3;
         args.seg0 = 1;
         args.nslice = args.nsl_v;
-        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(units * args.nslice), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(kern, dim3(units * args.nslice), dim3(768), 0, s, args);
         return hipGetLastError();
     }
     const int nblocks = args.nbh * args.nslice;
     if (pipe) {
-        hipLaunchKernelGGL(chunk32_kernel<128>, dim3(nblocks), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(kern, dim3(nblocks), dim3(768), 0, s, args);
         return hipGetLastError();
     }
     if (is_bf16) {

@@ -72,6 +72,28 @@ __device__ __forceinline__ float gate_value(float a, float z) {
     return kGmin * s;
 }
 
+// The same gate for kernels that evaluate it inline on every element, with
+// the hardware's base-2 exponential and reciprocal and the per-channel part
+// taken once: with zc = -log2(e) e^{a},
+//     sigmoid(e^{a} z) = 1 / (1 + 2^{zc z}),   log2(alpha) = -5 log2(e) sigmoid(e^{a} z).
+// A very negative argument overflows 2^{zc z} to +inf and the reciprocal to
+// 0, i.e. g = 0, its limit; a very positive one gives 2^{..} = 0 and g = -5.
+// Each step is within a few ulp of gate_value.
+__device__ __forceinline__ floatx2 gate_zscale2(const float *a) {
+    constexpr float kNegLog2e = -1.4426950408889634f;
+    return floatx2{kNegLog2e * expf(a[0]), kNegLog2e * expf(a[1])};
+}
+__device__ __forceinline__ floatx2 gate_log2_alpha2(floatx2 zc, floatx2 z) {
+    constexpr float kGminLog2e = kGmin * 1.4426950408889634f;
+    floatx2 r;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float t = __builtin_amdgcn_exp2f(zc[j] * z[j]);
+        r[j] = kGminLog2e * __builtin_amdgcn_rcpf(1.0f + t);
+    }
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // 16x16 MFMA tile products in "both operands k-contiguous" form:
 //   out[m][n] += sum_k X[m][k] * Y[n][k]

@@ -21,11 +21,14 @@ hipError_t launch_range_check(const float *g, int64_t B, int64_t T, int64_t H, i
 // pairwise: the diagonal 16-token tiles by position pairs (pipelined path).
 // cu_seqlens != nullptr: variable-length sequences packed along the token
 // axis (pipelined path, one pass; T is then the packed token count).
+// z != nullptr: the gate is evaluated inside the kernel from z (input dtype,
+// laid out like k) and the [H, dk] table Ag; g is not read (pipelined path).
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
-                            const int64_t *cu_seqlens, hipStream_t s);
+                            const int64_t *cu_seqlens, const void *z, const float *Ag,
+                            hipStream_t s);
 
 // Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
 bool seq_split_supported(int dk, int dv, int is_bf16);

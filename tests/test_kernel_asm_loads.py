@@ -25,18 +25,25 @@ def chunk_asm(tmp_path_factory):
     return out.read_text()
 
 
-def test_no_register_touched_before_its_wait(chunk_asm):
-    body = function_body(chunk_asm, "_ZN3kda14chunk32_kernelILi128EEEvNS_9ChunkArgsE")
+# both instances of the pipelined kernel: g loaded, and the gate fused (z loaded)
+KERNELS = ["_ZN3kda14chunk32_kernelILi128ELb0EEEvNS_9ChunkArgsE",
+           "_ZN3kda14chunk32_kernelILi128ELb1EEEvNS_9ChunkArgsE"]
+
+
+@pytest.mark.parametrize("name", KERNELS)
+def test_no_register_touched_before_its_wait(chunk_asm, name):
+    body = function_body(chunk_asm, name)
     nloads, found = hazards(body)
     assert nloads > 50, nloads          # the prefetch loads are present
     assert not found, "\n".join(found[:10])
 
 
-def test_scalar_load_bases_are_full_pointers(chunk_asm):
+@pytest.mark.parametrize("name", KERNELS)
+def test_scalar_load_bases_are_full_pointers(chunk_asm, name):
     """Scalar bases of the hand-issued loads are never a sign-extended 32-bit
     value (a truncated pointer: a 32-bit read-first-lane of a 64-bit address
     produces one)."""
-    body = function_body(chunk_asm, "_ZN3kda14chunk32_kernelILi128EEEvNS_9ChunkArgsE")
+    body = function_body(chunk_asm, name)
     n, found = sign_extended_bases(body)
     assert n > 50, n
     assert not found, "\n".join(found[:10])
