@@ -226,24 +226,24 @@ LONG = inputs.WORKLOADS["prefill_h32_t1m"]
 
 
 def time_long_prefill(reps=3):
-    """kda_chunk_fwd on the few-chain long workload (B1 H32 T1M: 64 workgroups
-    in one pass) in one pass and with the library's sequence split."""
+    """kda_chunk_fwd_gated (gate and chunked prefill, as the main step) on the
+    few-chain long workload (B1 H32 T1M: 64 workgroups in one pass) in one
+    pass and with the library's sequence split."""
     w = LONG
     dev = torch.device("cuda")
     x = inputs.workload_prefill_inputs(w, device=dev)
-    g = _lib.kda_gate(x["z"], x["A"])
-    del x["z"]
     o = torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype)
     ST = torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32)
     nseg = _lib.kda_chunk_fwd_auto_segments(w.B, w.T, w.H, w.dk, w.dv, 1)
-    ws = torch.empty(_lib.kda_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 1),
+    ws = torch.empty(_lib.kda_chunk_fwd_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 1),
                      device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
     out = {}
     for label, n in (("one_pass", 1), ("split", nseg)):
         def run():
-            _lib.kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], final_state=ST, o=o,
-                               workspace=ws, flags=_lib.kda_flag_segments(n), stream=stream)
+            _lib.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
+                                     final_state=ST, o=o, workspace=ws,
+                                     flags=_lib.kda_flag_segments(n), stream=stream)
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -257,9 +257,9 @@ def time_long_prefill(reps=3):
     s_ = out["split_ms"] / 1e3
     out.update(segments=nseg, speedup=out["one_pass_ms"] / out["split_ms"],
                tokens_per_s=w.B * w.T / s_,
-               hbm_frac_of_roofline=work["chunk_bytes"] / s_ / 1e9 / HBM_PEAK_GBS,
-               workload=w.note)
-    del x, g, o, ST, ws
+               hbm_frac_of_roofline=work["fused_bytes"] / s_ / 1e9 / HBM_PEAK_GBS,
+               workload=w.note + "; gate fused (kda_chunk_fwd_gated)")
+    del x, o, ST, ws
     torch.cuda.empty_cache()
     return out
 
@@ -528,8 +528,9 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out
 EXTRA_TRACES = {
     # name: (bench.py --only value, profile file, what the run holds)
     "long": ("long", "kernel_trace_prefill_b1h32t1m_split.md",
-             "kda_gate once, then kda_chunk_fwd on B1 H32 T1048576 d128 bf16 in one pass "
-             "(1 warm-up + 3 timed calls) and with the library's sequence split (the same). "
+             "kda_chunk_fwd_gated (the gate fused into the chunk kernel) on B1 H32 T1048576 "
+             "d128 bf16 in one pass (1 warm-up + 3 timed calls) and with the library's "
+             "sequence split (the same). "
              "A split call is three launches: chunk32_kernel phase 1 (segment 0, the middle "
              "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),

@@ -1,24 +1,31 @@
-"""Full-size prefill workloads, end to end on the GPU (kda_gate -> kda_chunk_fwd
-in the launch configuration the benchmark times), against the oracle's gate
+"""Full-size prefill workloads, end to end on the GPU, against the oracle's gate
 and recurrence on sampled chains (chains are independent, so a sampled chain
-is checked exactly)."""
+is checked exactly).  Both forms of the step run: kda_chunk_fwd_gated (the
+gate inside the chunk kernel, the launch configuration the benchmark times)
+and kda_gate -> kda_chunk_fwd."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from linear_attention_sequence_gate_amd import inputs, kda_chunk_fwd, kda_gate
+from linear_attention_sequence_gate_amd import inputs, kda_chunk_fwd, kda_chunk_fwd_gated, kda_gate
 from kda_testutil import TOL, head_slice, rho, say, to_host64
 
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_run(w):
+PATHS = ["fused", "two_kernel"]
+
+
+def _gpu_run(w, path="fused"):
     x = inputs.workload_prefill_inputs(w, device="cuda")
-    g = kda_gate(x["z"], x["A"])
-    o, ST = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+    if path == "fused":
+        o, ST = kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"])
+    else:
+        g = kda_gate(x["z"], x["A"])
+        o, ST = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"])
+        del g
     torch.cuda.synchronize()
-    del g
     return x, o, ST
 
 
@@ -33,11 +40,12 @@ def _oracle_chain(x, b, h, t1=None, want_o=True):
                           want_o=want_o, col_block=8)
 
 
-def test_prefill_h8_t4k_all_heads():
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_h8_t4k_all_heads(path):
     """B1 H8 T4096 d128 bf16, zero initial state: every head, every token."""
     w = inputs.WORKLOADS["prefill_h8_t4k"]
-    say("full size", w.name)
-    x, o, ST = _gpu_run(w)
+    say("full size", w.name, path)
+    x, o, ST = _gpu_run(w, path)
     worst_o = worst_s = 0.0
     for h in range(w.H):
         o_ref, S_ref = _oracle_chain(x, 0, h)
@@ -47,13 +55,14 @@ def test_prefill_h8_t4k_all_heads():
     assert worst_o <= TOL[w.dtype] and worst_s <= TOL[w.dtype]
 
 
-def test_prefill_b4_h32_t32k_sampled_chains():
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_b4_h32_t32k_sampled_chains(path):
     """B4 H32 T32768 d128 bf16 with heads 16..31 in decay stress: four whole
     chains (two ordinary, two stressed) checked on every token and on the
     final state."""
     w = inputs.WORKLOADS["prefill_b4_h32_t32k"]
-    say("full size", w.name)
-    x, o, ST = _gpu_run(w)
+    say("full size", w.name, path)
+    x, o, ST = _gpu_run(w, path)
     assert torch.isfinite(o).all()
     for (b, h) in ((0, 3), (2, 10), (1, 20), (3, 31)):
         say("  chain", b, h)
@@ -66,13 +75,15 @@ def test_prefill_b4_h32_t32k_sampled_chains():
     torch.cuda.empty_cache()
 
 
-def test_prefill_h32_t1m_first_tokens_and_final_state():
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_h32_t1m_first_tokens_and_final_state(path):
     """B1 H32 T1048576 d128 bf16, initial state ~ N(0, 0.02): outputs of the
     first 8192 tokens on four heads, and the final state of two heads (their
-    oracle runs over all 2^20 tokens)."""
+    oracle runs over all 2^20 tokens).  Both paths take the library's
+    sequence split at this size."""
     w = inputs.WORKLOADS["prefill_h32_t1m"]
-    say("full size", w.name)
-    x, o, ST = _gpu_run(w)
+    say("full size", w.name, path)
+    x, o, ST = _gpu_run(w, path)
     assert torch.isfinite(o[:, :8192]).all() and torch.isfinite(ST).all()
     for h in (0, 9, 17, 30):
         o_ref, _ = _oracle_chain(x, 0, h, t1=8192)
