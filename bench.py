@@ -639,6 +639,23 @@ SQ_PASSES = (
     "SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_INST_LEVEL_LDS",
 )
 SQ_MD = os.path.join(ROOT, "profiles", "sq_counters_chunk32_b4h32t32k.md")
+N_SE, N_SIMD = 32, 1024        # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
+
+
+def recorded_mfma_busy():
+    """MFMA busy share of the fused kernel from the recorded SQ counters, while
+    its sources are unchanged since they were taken (else None)."""
+    try:
+        text = open(SQ_MD).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != source_hash(KERNELS["fused_fwd"][1]):
+        return None
+    return rec.get("mfma_busy_frac")
 
 
 def sq_cmd(i):
@@ -686,9 +703,23 @@ def ingest_sq(dirs):
         derived.append(f"| share of wave time waiting (any) | {vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.2f} |")
     if "SQ_ACTIVE_INST_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
         derived.append(f"| share of wave time issuing | {vals['SQ_ACTIVE_INST_ANY'] / vals['SQ_WAVE_CYCLES']:.2f} |")
+    rec = {}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "SQ_BUSY_CYCLES" in vals:
+        # SQ_BUSY_CYCLES is summed over the shader engines, so per engine it is
+        # the kernel's duration in cycles; the MFMA busy cycles are summed over
+        # every SIMD
+        cycles = vals["SQ_BUSY_CYCLES"] / N_SE
+        rec["mfma_busy_frac"] = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
+        derived.append(f"| kernel cycles (SQ_BUSY_CYCLES / {N_SE} shader engines) | {cycles:.4g} |")
+        derived.append(f"| MFMA busy share of every SIMD's cycles (SQ_VALU_MFMA_BUSY_CYCLES / "
+                       f"(cycles x {N_SIMD} SIMDs)) | {rec['mfma_busy_frac']:.3f} |")
     if derived:
         lines += ["", "Derived (counts are summed over waves; the shares divide counters kept in "
                   "the same unit):", "", "| figure | value |", "|---|---|"] + derived
+    if rec:
+        rec["source_sha256"] = source_hash(KERNELS["fused_fwd"][1])
+        lines += ["", "Machine-readable record (read by bench.py while the kernel's sources hash "
+                  "to `source_sha256`):", "", "```json", json.dumps(rec, indent=1), "```"]
     lines.append("")
     with open(SQ_MD, "w") as fh:
         fh.write("\n".join(lines))
@@ -798,6 +829,7 @@ def main():
                     "flops_per_head_token": work["flops_per_head_token"],
                     "arith_intensity": ai,
                     "mfma_frac_of_bf16_peak": fused_tflops / BF16_PEAK_TFLOPS,
+                    "rocprof_mfma_busy_frac": recorded_mfma_busy(),
                     "roofline_frac_of_attainable": fused_tflops / attainable_tflops,
                     "head_tokens": work["head_tokens"],
                     "two_kernel": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
