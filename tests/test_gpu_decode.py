@@ -116,3 +116,33 @@ def test_decode_full_size_1000_steps_sampled():
     assert rho(S[n_idx, h_idx].unsqueeze(0), S_ref) <= TOL[w.dtype]
     del st, S
     torch.cuda.empty_cache()
+
+
+def test_decode_continues_a_fused_gate_prefill():
+    """bf16, dk = dv = 128: kda_chunk_fwd_gated over T0 tokens, then T1 decode
+    steps, equal one kda_chunk_fwd_gated over all of them (the state is the
+    whole carry; the two paths evaluate the gate by different formulas of the
+    same function)."""
+    from linear_attention_sequence_gate_amd import kda_chunk_fwd_gated
+    N, H, d, T0, T1 = 2, 4, 128, 200, 12
+    say("fused prefill then decode vs one fused prefill")
+    x = inputs.make_prefill_inputs(N, T0 + T1, H, d, d, torch.bfloat16, 79, device="cuda",
+                                   s0_std=0.02, stress_heads_mean=3.0)
+    o_all, S_all = kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"])
+    head = {n: x[n][:, :T0].clone() for n in ("q", "k", "v", "z", "beta")}
+    o_head, S = kda_chunk_fwd_gated(head["q"], head["k"], head["v"], head["z"], x["A"],
+                                    head["beta"], x["S0"])
+    outs = []
+    for t in range(T0, T0 + T1):
+        sl = lambda a: a[:, t].contiguous()
+        outs.append(kda_decode_step(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["z"]), x["A"],
+                                    sl(x["beta"]), S))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1)
+    # the head's last chunk is partial: its decay factors are formed over the
+    # padded subtile, so equal up to rounding (bf16 outputs: a flipped ulp)
+    assert rho(o_head, o_all[:, :T0]) <= TOL[torch.bfloat16]
+    assert rho(o_dec, o_all[:, T0:]) <= TOL[torch.bfloat16]
+    # the chunked path's products take bf16 operands (about 3e-3 from the
+    # oracle on either side), so the two states meet at the bf16 bar
+    assert rho(S, S_all) <= TOL[torch.bfloat16]
