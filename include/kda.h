@@ -321,6 +321,19 @@ int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, con
                                 int64_t dv, int dtype, unsigned flags, void *stream);
 
 /*
+ * kda_chunk_fwd_varlen_pooled with the gate evaluated inside the chunk kernel
+ * (as kda_chunk_fwd_gated): z [total_tokens, H, dk] in the input dtype and A
+ * [H, dk] fp32 instead of g.  Same shapes, layout and rules otherwise
+ * (KDA_FLAG_CHECK_RANGE is rejected, as everywhere the gate is fused).
+ */
+int kda_chunk_fwd_varlen_pooled_gated(const void *q, const void *k, const void *v, const void *z,
+                                      const float *A, const void *beta, float *state_pool,
+                                      const int32_t *slots, const int64_t *cu_seqlens, void *o,
+                                      int64_t B, int64_t total_tokens, int64_t n_slots, int64_t H,
+                                      int64_t dk, int64_t dv, int dtype, unsigned flags,
+                                      void *stream);
+
+/*
  * kda_decode_step for N sequences whose states live in the pool: sequence n
  * reads and updates slot slots[n] in place (continuous batching: the set of
  * slots may change from step to step).  q, k, v, z, A, beta, o as in

@@ -39,7 +39,7 @@ EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
             "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
-            "kda_last_error", "kda_version")
+            "kda_chunk_fwd_varlen_pooled_gated", "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -89,6 +89,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_varlen_pooled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                               i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd_varlen_pooled.restype = c_int
+    L.kda_chunk_fwd_varlen_pooled_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                                    i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd_varlen_pooled_gated.restype = c_int
     L.kda_chunk_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
     L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int,
@@ -317,6 +320,26 @@ def kda_chunk_fwd_varlen_pooled(q, k, v, g, beta, state_pool, slots, cu_seqlens,
         o = torch.empty((total, H, dv), device=q.device, dtype=q.dtype)
     _check(load_library().kda_chunk_fwd_varlen_pooled(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+        _ptr(cu_seqlens), _ptr(o), B, total, state_pool.shape[0], H, dk, dv, _dtype_code(q), flags,
+        _stream(stream)))
+    return o
+
+
+def kda_chunk_fwd_varlen_pooled_gated(q, k, v, z, A, beta, state_pool, slots, cu_seqlens, o=None,
+                                      flags: int = 0, stream=None) -> torch.Tensor:
+    """kda_chunk_fwd_varlen_pooled with the gate inside the chunk kernel: z
+    [total,H,dk] and A [H,dk] instead of g.  Returns o [total,H,dv]."""
+    _dev(q, k, v, z, A, beta, state_pool, o)
+    slots = _slots(slots)
+    if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int64 CUDA tensor")
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    B = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((total, H, dv), device=q.device, dtype=q.dtype)
+    _check(load_library().kda_chunk_fwd_varlen_pooled_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(state_pool), _ptr(slots),
         _ptr(cu_seqlens), _ptr(o), B, total, state_pool.shape[0], H, dk, dv, _dtype_code(q), flags,
         _stream(stream)))
     return o

@@ -348,12 +348,14 @@ int kda_chunk_fwd_pooled(const void *q, const void *k, const void *v, const floa
                           n_slots, nullptr, nullptr, nullptr, stream);
 }
 
-int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, const float *g,
-                                const void *beta, float *state_pool, const int32_t *slots,
-                                const int64_t *cu_seqlens, void *o, int64_t B,
-                                int64_t total_tokens, int64_t n_slots, int64_t H, int64_t dk,
-                                int64_t dv, int dtype, unsigned flags, void *stream) {
-    const char *who = "kda_chunk_fwd_varlen_pooled";
+}  // extern "C"
+
+// kda_chunk_fwd_varlen_pooled and its fused-gate form (z, A instead of g)
+static int varlen_pooled_impl(const char *who, const void *q, const void *k, const void *v,
+                              const float *g, const void *z, const float *A, const void *beta,
+                              float *state_pool, const int32_t *slots, const int64_t *cu_seqlens,
+                              void *o, int64_t B, int64_t total_tokens, int64_t n_slots, int64_t H,
+                              int64_t dk, int64_t dv, int dtype, unsigned flags, void *stream) {
     if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null cu_seqlens", who);
     if (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens must be 8-byte aligned", who);
@@ -370,7 +372,31 @@ int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, con
     // the size checks; the kernel reads sequence b's rows from cu_seqlens
     return chunk_fwd_impl(who, q, k, v, g, beta, state_pool, state_pool, o, nullptr, 0, B,
                           total_tokens, H, dk, dv, dtype, flags | KDA_FLAG_SEGMENTS(1), slots,
-                          n_slots, cu_seqlens, nullptr, nullptr, stream);
+                          n_slots, cu_seqlens, z, A, stream);
+}
+
+extern "C" {
+
+int kda_chunk_fwd_varlen_pooled(const void *q, const void *k, const void *v, const float *g,
+                                const void *beta, float *state_pool, const int32_t *slots,
+                                const int64_t *cu_seqlens, void *o, int64_t B,
+                                int64_t total_tokens, int64_t n_slots, int64_t H, int64_t dk,
+                                int64_t dv, int dtype, unsigned flags, void *stream) {
+    return varlen_pooled_impl("kda_chunk_fwd_varlen_pooled", q, k, v, g, nullptr, nullptr, beta,
+                              state_pool, slots, cu_seqlens, o, B, total_tokens, n_slots, H, dk,
+                              dv, dtype, flags, stream);
+}
+
+int kda_chunk_fwd_varlen_pooled_gated(const void *q, const void *k, const void *v, const void *z,
+                                      const float *A, const void *beta, float *state_pool,
+                                      const int32_t *slots, const int64_t *cu_seqlens, void *o,
+                                      int64_t B, int64_t total_tokens, int64_t n_slots, int64_t H,
+                                      int64_t dk, int64_t dv, int dtype, unsigned flags,
+                                      void *stream) {
+    const char *who = "kda_chunk_fwd_varlen_pooled_gated";
+    if (!z || !A) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer (z and A are required)", who);
+    return varlen_pooled_impl(who, q, k, v, nullptr, z, A, beta, state_pool, slots, cu_seqlens, o,
+                              B, total_tokens, n_slots, H, dk, dv, dtype, flags, stream);
 }
 
 }  // extern "C"

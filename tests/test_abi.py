@@ -40,6 +40,7 @@ def test_header_declares_the_boundary():
               "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
               "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
               "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
+              "kda_chunk_fwd_varlen_pooled_gated",
               "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)

@@ -202,3 +202,44 @@ def test_varlen_pooled_prefill_equals_per_sequence_calls(dv, flags):
                                   beta[a_:e_].unsqueeze(0).clone(), S0)
     assert rho(o[a_:e_].unsqueeze(0), o_ref) <= TOL[torch.bfloat16]
     assert rho(pool[0].unsqueeze(0), S_ref) <= TOL[torch.bfloat16]
+
+
+def test_varlen_pooled_gated_equals_per_sequence_gated_calls():
+    """The fused-gate serving prefill: prompts of 37, 0, 300, 64 and 1 tokens
+    packed in one kda_chunk_fwd_varlen_pooled_gated call equal separate
+    kda_chunk_fwd_gated calls from the slots' states bit for bit (the same
+    kernel instance); one sequence is also checked against the oracle's fp64
+    gate and recurrence."""
+    from linear_attention_sequence_gate_amd import kda_chunk_fwd_gated, kda_chunk_fwd_varlen_pooled_gated
+    say("varlen pooled prefill, gate fused")
+    lens = [37, 0, 300, 64, 1]
+    H, total, dv = 2, sum(lens), 128
+    x = inputs.make_prefill_inputs(1, total, H, 128, dv, torch.bfloat16, 540, device="cuda",
+                                   stress_heads_mean=3.0)
+    q, k, v, z, beta = x["q"][0], x["k"][0], x["v"][0], x["z"][0], x["beta"][0]
+    cu_list = [0]
+    for L in lens:
+        cu_list.append(cu_list[-1] + L)
+    cu = torch.tensor(cu_list, dtype=torch.int64, device="cuda")
+    slots = [3, 6, 0, 7, 5]
+    pool = _pool(8, H, 128, dv, 541)
+    before = pool.clone()
+    o = kda_chunk_fwd_varlen_pooled_gated(q, k, v, z, x["A"], beta, pool, _slots(slots), cu)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        a_, e_ = cu_list[b], cu_list[b + 1]
+        sl = lambda t: t[a_:e_].unsqueeze(0).clone()      # own, aligned allocation
+        S = before[slots[b]].unsqueeze(0).clone()
+        ob, _ = kda_chunk_fwd_gated(sl(q), sl(k), sl(v), sl(z), x["A"], sl(beta), S, final_state=S)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a_:e_], ob[0]), b
+        assert torch.equal(pool[slots[b]], S[0]), b
+    assert torch.equal(pool[6], before[6])               # the empty sequence's slot
+    a_, e_ = cu_list[2], cu_list[3]
+    g64 = oracle.gate(z[a_:e_].unsqueeze(0), x["A"])
+    o_ref, S_ref = oracle.forward(q[a_:e_].unsqueeze(0), k[a_:e_].unsqueeze(0), v[a_:e_].unsqueeze(0),
+                                  g64, beta[a_:e_].unsqueeze(0), before[0].unsqueeze(0))
+    assert rho(o[a_:e_].unsqueeze(0), o_ref) <= TOL[torch.bfloat16]
+    assert rho(pool[0].unsqueeze(0), S_ref) <= TOL[torch.bfloat16]
