@@ -1173,18 +1173,29 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                     floatx2 tot = al[0];
 #pragma unroll
                     for (int i = 1; i < TPL; ++i) tot *= al[i];
-                    // products of the other token groups before / after this one
-                    floatx2 pre = {1.0f, 1.0f}, suf = {1.0f, 1.0f};
+                    // products of the other token groups before / after this
+                    // one.  Group pos is row pos of the wave (16 lanes); the
+                    // other rows' totals come through the row swaps of the
+                    // VALU, not LDS: permlane16_swap(t, t) gives rows
+                    // (0,0,2,2) / (1,1,3,3), permlane32_swap(t, t) rows
+                    // (0,1,0,1) / (2,3,2,3), so a lane picks the total of row
+                    // pos^1, pos^2 and (from the pos^1 values) pos^3.
+                    static_assert(NPOS == 4, "four token groups, one per 16-lane row");
+                    floatx2 pre, suf;
 #pragma unroll
-                    for (int s = 1; s < NPOS; ++s) {
-                        const bool use_fw = pos >= s, use_bw = pos + s < NPOS;
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const float fw = __shfl(tot[j], lane - 16 * s);
-                            const float bw = __shfl(tot[j], lane + 16 * s);
-                            pre[j] *= use_fw ? fw : 1.0f;
-                            suf[j] *= use_bw ? bw : 1.0f;
-                        }
+                    for (int j = 0; j < 2; ++j) {
+                        const unsigned t = __float_as_uint(tot[j]);
+                        const auto a = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+                        const unsigned u1 = (pos & 1) ? a[0] : a[1];
+                        const auto b = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+                        const float p2 = __uint_as_float((pos & 2) ? b[0] : b[1]);
+                        const auto c = __builtin_amdgcn_permlane32_swap(u1, u1, false, false);
+                        const float p3 = __uint_as_float((pos & 2) ? c[0] : c[1]);
+                        const float p1 = __uint_as_float(u1), p23 = p2 * p3;
+                        // rows below pos: pos^1 when pos is odd, pos^2 and
+                        // pos^3 when pos >= 2; rows above: the others
+                        pre[j] = ((pos & 1) ? p1 : 1.0f) * ((pos & 2) ? p23 : 1.0f);
+                        suf[j] = ((pos & 1) ? 1.0f : p1) * ((pos & 2) ? 1.0f : p23);
                     }
                     R[0] = pre * al[0];
 #pragma unroll
