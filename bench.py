@@ -264,7 +264,7 @@ def time_long_prefill(reps=3):
     return out
 
 
-def time_pairwise_diagonal(reps=3):
+def time_pairwise_diagonal(reps=5):
     """kda_chunk_fwd on the benchmark's prefill workload with the dense MFMA
     diagonal tiles (what the gate floor allows) and with the position-pair
     diagonal path the floor made unnecessary, in the same kernel."""
@@ -280,7 +280,7 @@ def time_pairwise_diagonal(reps=3):
         def run():
             _lib.kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], final_state=ST, o=o,
                                flags=fl, stream=stream)
-        for _ in range(2):
+        for _ in range(5):         # past the first launches' clock ramp
             run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -309,7 +309,7 @@ def bwd_chunk_flops(d):
     return 16 * d * d + 22 * BWD_CHUNK * d
 
 
-def time_backward(reps=3):
+def time_backward(reps=5):
     """kda_chunk_bwd on B4 H32 d128 bf16 with T = 4096 (the benchmark's chain
     count; T cut so the workspace -- the state entering each even 16-token
     chunk and the gradient leaving each odd one, 64 KiB per 16 tokens per
@@ -325,10 +325,11 @@ def time_backward(reps=3):
     ws = torch.empty(_lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, 1), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
 
-    def timed(flags, n):
+    def timed(flags, n, warm):
         run = lambda: _lib.kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, None,
                                          workspace=ws, flags=flags, stream=stream)
-        run()
+        for _ in range(warm):      # past the first launches' clock ramp
+            run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -338,13 +339,14 @@ def time_backward(reps=3):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    ms = timed(0, reps)
-    ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1)
+    ms = timed(0, reps, 6)
+    ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1, 1)
     # the gate's reverse mode on the same rows (dz, dA from a dg of that shape)
     dg = torch.randn(B, T, H, d, device=dev)
     gws = torch.empty(max(_lib.kda_gate_bwd_workspace_size(B, T, H, d), 256), device=dev,
                       dtype=torch.uint8)
-    _lib.kda_gate_bwd(x["z"], x["A"], dg, workspace=gws, stream=stream)
+    for _ in range(3):
+        _lib.kda_gate_bwd(x["z"], x["A"], dg, workspace=gws, stream=stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -536,7 +538,7 @@ EXTRA_TRACES = {
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
     "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
                  "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (heads 16-31 decay-stress): the chunked path "
-                 "(1 warm-up + 3 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
+                 "(6 warm-up + 5 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
                  "chunk), cb_fwd_kernel (state entering each even chunk), cb_bwd_kernel (gradient "
                  "leaving each odd chunk) and cb_grad_kernel (token gradients, one workgroup per "
                  "chunk pair)), "
@@ -544,7 +546,7 @@ EXTRA_TRACES = {
                  "bwd_kernel, bwd_sum_kernel)."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
-                 "MFMA diagonal tiles (2 warm-up + 3 timed calls) and with the position-pair "
+                 "MFMA diagonal tiles (5 warm-up + 5 timed calls) and with the position-pair "
                  "diagonal path (the same), in that order."),
 }
 

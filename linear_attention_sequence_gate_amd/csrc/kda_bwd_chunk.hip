@@ -332,8 +332,10 @@ __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<
 
 // Chunks of register prefetch in the two state passes.  The passes' barriers
 // wait for LDS only (lds_barrier), so loads stay in flight across them and
-// the stores of states and W never hold a barrier up.
-constexpr int kCbAhead = 1;
+// the stores of states and W never hold a barrier up.  Two chunks ahead keep
+// both passes at two waves per SIMD (at most 248 of the 512 registers of a
+// lane); three push the reverse pass to one wave per SIMD and run slower.
+constexpr int kCbAhead = 2;
 
 // ---------------------------------------------------------------------------
 // Forward state pass: the state entering every chunk, and W = V - K~ S.
