@@ -54,6 +54,13 @@ namespace kda {
 constexpr int kCB = 16;                          // tokens per chunk
 constexpr int kCbMat = 3 * kCB * kCB;            // X, P, At per chunk
 
+// e^x with the hardware base-2 exponential.  Every exponent here is a
+// difference of cumulative log-decays inside one 16-token chunk, or such a sum
+// from the chunk start: within [-80, 80] under the gate floor, so the result
+// is a normal fp32 number, within a few ulp of expf (the rounding of x log2 e
+// adds at most |x| 2^-24 to the exponent).
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 struct CbArgs {
     const void *q, *k, *v, *beta, *dout;
     const float *g, *S0, *dST;
@@ -170,12 +177,12 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
         for (int r = 0; r < HT; ++r) {
             const int tr = HT * half + r;
             const float br = base + b[r];
-            const float e = expf(br - m), ei = expf(m - br), eb = expf(br);
+            const float e = exp_hw(br - m), ei = exp_hw(m - br), eb = exp_hw(br);
             Kp[tr][ch] = kv[r] * e;
             Kpp[tr][ch] = kv[r] * ei;
             Qp[tr][ch] = qv[r] * e;
             kt[r] = kv[r] * eb;
-            kh[r] = kv[r] * expf(bc - br);
+            kh[r] = kv[r] * exp_hw(bc - br);
             qt[r] = qv[r] * eb;
             op[kOpKt * DK + tr * DK + ch] = kt[r];
             op[kOpKh * DK + tr * DK + ch] = kh[r];
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
             *reinterpret_cast<floatx4 *>(op + kOpQtT * DK + ch * kCB + tr) =
                 floatx4{qt[r], qt[r + 1], qt[r + 2], qt[r + 3]};
         }
-        if (half == 0) op[kOpEbc * DK + ch] = expf(bc);
+        if (half == 0) op[kOpEbc * DK + ch] = exp_hw(bc);
     }
     __syncthreads();
     float *mat = a.mat + unit * kCbMat;          // X, P, At
@@ -837,7 +844,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
         for (int i = 0; i < 4; ++i) {
             const int s = 4 * g4 + i;
             const float bms = L.bm[s][ch], ks = kv[i], qs = qv[i];
-            const float e = expf(bms), ei = expf(-bms);
+            const float e = exp_hw(bms), ei = exp_hw(-bms);
             const float kpp = ks * ei, kp = ks * e, qp = qs * e;
             dQp = mfma1(L.dP[j][s], kpp, dQp);
             dKp = mfma1(L.dAt[j][s], kpp, dKp);
@@ -850,8 +857,8 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
             const float bmr = L.bm[r][ch], qr = qv[i], kr = kv[i];
-            const float e_bm = expf(bmr), e_mb = expf(-bmr);
-            const float e_b = expf(bmr + m), e_cb = expf(bcm - bmr);
+            const float e_bm = exp_hw(bmr), e_mb = exp_hw(-bmr);
+            const float e_b = exp_hw(bmr + m), e_cb = exp_hw(bcm - bmr);
             const float dq = dQt[u][i] * e_b + dQp[i] * e_bm;
             const float dk = -dKt[u][i] * e_b + dKh[u][i] * e_cb + dKp[i] * e_bm + dKpp[i] * e_mb;
             const float kh = dKh[u][i] * kr * e_cb;
@@ -867,7 +874,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
         // suffix sums over the chunk's tokens (rows 4 g4 + i live in lane group g4)
         khk += __shfl_xor(khk, 16);
         khk += __shfl_xor(khk, 32);
-        const float extra = khk + expf(bcm + m) * L.rs[ch];
+        const float extra = khk + exp_hw(bcm + m) * L.rs[ch];
         db[2] += db[3];
         db[1] += db[2];
         db[0] += db[1];
