@@ -264,3 +264,60 @@ def test_gate_backward_validation(L):
     assert gb(dz=Q[2]) == E.KDA_ERR_INVALID_ARGUMENT         # dz aliases dg
     assert gb(dA=Q[3]) == E.KDA_ERR_INVALID_ARGUMENT         # dA aliases dz
     assert gb(z=BAD) == E.KDA_ERR_INVALID_ARGUMENT           # misaligned
+
+
+def gated(L, q=P, k=P, v=P, z=P3, A=P2, beta=P, S0=NULL, ST=NULL, o=ctypes.c_void_p(0x400000),
+          ws=NULL, wsb=0, B=1, T=64, H=1, dk=128, dv=128, dt=1, flags=0):
+    return L.kda_chunk_fwd_gated(q, k, v, z, A, beta, S0, ST, o, ws, wsb, B, T, H, dk, dv, dt, flags,
+                                 None)
+
+
+def test_gated_validation(L):
+    """kda_chunk_fwd_gated: host validation before any HIP call (every call
+    here fails, so no fake pointer is dereferenced)."""
+    E = _lib
+    assert gated(L, z=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "z and A" in _lib.kda_last_error()
+    assert gated(L, A=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert gated(L, q=NULL) == E.KDA_ERR_INVALID_ARGUMENT
+    assert gated(L, z=BAD) == E.KDA_ERR_INVALID_ARGUMENT              # misaligned z
+    assert gated(L, o=P3) == E.KDA_ERR_INVALID_ARGUMENT               # o aliases z
+    assert gated(L, o=P2) == E.KDA_ERR_INVALID_ARGUMENT               # o aliases A
+    assert gated(L, dt=7) == E.KDA_ERR_UNSUPPORTED
+    assert gated(L, dk=48) == E.KDA_ERR_UNSUPPORTED
+    assert gated(L, dt=0) == E.KDA_ERR_UNSUPPORTED                    # fp32 with dk = 128
+    # the range check takes a caller's g; here g is the gate's own output
+    assert gated(L, flags=E.KDA_FLAG_CHECK_RANGE, ws=ctypes.c_void_p(0x500000),
+                 wsb=1 << 20) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "CHECK_RANGE" in _lib.kda_last_error()
+    # shapes without the fused kernel stage g in the workspace: none, or too
+    # small, is rejected before the gate runs
+    assert gated(L, dk=64, dv=64) == E.KDA_ERR_INVALID_ARGUMENT
+    assert gated(L, dk=64, dv=64, ws=ctypes.c_void_p(0x500000), wsb=1024) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
+    # the workspace may not be a tensor
+    assert gated(L, dk=64, dv=64, ws=P, wsb=1 << 20) == E.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_gated_workspace_query(L):
+    q = L.kda_chunk_fwd_gated_workspace_size
+    base = L.kda_chunk_fwd_workspace_size
+    # fused shapes: exactly what kda_chunk_fwd takes (range counter, split buffers)
+    assert q(4, 32768, 32, 128, 128, 1) == base(4, 32768, 32, 128, 128, 1) == 256
+    assert q(1, 1 << 20, 32, 128, 128, 1) == base(1, 1 << 20, 32, 128, 128, 1) > 256
+    # staged shapes: g (B T H dk fp32, rounded to 256 bytes) in front
+    assert q(2, 100, 3, 64, 64, 1) == 256 + (2 * 100 * 3 * 64 * 4 + 255) // 256 * 256
+    assert q(1, 7, 1, 32, 32, 0) == 256 + 1024          # 7*32*4 = 896 -> 1024
+    assert q(0, 64, 1, 128, 128, 1) == 0 and q(1, 64, 1, 48, 128, 1) == 0
+
+
+def test_varlen_pooled_gated_validation(L):
+    E = _lib
+    f = L.kda_chunk_fwd_varlen_pooled_gated
+    cu, pool, slots, o = (ctypes.c_void_p(a) for a in (0x600000, 0x700000, 0x800000, 0x900000))
+    args = lambda z=P3, A=P2, cu_=cu, dk=128, dv=128, flags=0: (
+        P, P, P, z, A, P, pool, slots, cu_, o, 2, 100, 4, 1, dk, dv, 1, flags, None)
+    assert f(*args(z=NULL)) == E.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(cu_=NULL)) == E.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(dk=64, dv=64)) == E.KDA_ERR_UNSUPPORTED             # fused shapes only
+    assert f(*args(flags=E.KDA_FLAG_CHECK_RANGE)) == E.KDA_ERR_INVALID_ARGUMENT
