@@ -631,10 +631,17 @@ template <int DK, int DV> struct alignas(16) CbGradLds {
 // chunk is Diag(e^{b_C}) S + K^^T U of the previous one), or the Q~, K~ rows
 // and e^{b_C} of the next chunk (the gradient leaving this chunk is
 // Diag(e^{b_C}) dN + Q~^T dO - K~^T dW of the next one).
-template <int DK> struct CbNeighbour {
-    floatx4 r1[(DK / 16 + 3) / 4], r2[(DK / 16 + 3) / 4];
-    float e[(DK / 16 + 3) / 4];
+template <int NT> struct CbNeighbour {
+    floatx4 r1[NT], r2[NT];
+    float e[NT];
 };
+
+// Waves of a gradient workgroup: one 16-channel tile each at dk = 128 (eight
+// waves), four otherwise.
+template <int DK> __host__ __device__ constexpr int cb_grad_waves() { return DK >= 128 ? 8 : 4; }
+template <int DK> __host__ __device__ constexpr int cb_grad_tiles() {
+    return (DK / 16 + cb_grad_waves<DK>() - 1) / cb_grad_waves<DK>();
+}
 
 enum { kCbPlain = 0, kCbSFromPrev = 1, kCbNFromNext = 2 };
 
@@ -647,9 +654,10 @@ enum { kCbPlain = 0, kCbSFromPrev = 1, kCbNFromNext = 2 };
 template <typename T, int DK, int DV, int MODE>
 __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV> &L, int64_t bh,
                                               int c, int wave, const float *sglob,
-                                              const float *nglob, const CbNeighbour<DK> &nb) {
+                                              const float *nglob, const CbNeighbour<cb_grad_tiles<DK>()> &nb) {
     using Lds = CbGradLds<DK, DV>;
-    constexpr int RT = DK / 16, CT = DV / 16, NT = (RT + 3) / 4, KB = DV / 16;
+    constexpr int RT = DK / 16, CT = DV / 16, KB = DV / 16;
+    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
     const int64_t unit = bh * a.nc + c;
     const int64_t t0 = (int64_t)c * kCB;
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
@@ -662,7 +670,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
     float qin[NT][4], kin[NT][4];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+        const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i, rr = r < n ? r : n - 1;
@@ -689,14 +697,14 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
         for (int r = 0; r < kCB; ++r) L.bm[r][tid] = b[r] - m;
     }
     {
-        for (int e = tid; e < kCB * DV; e += 256) {
+        for (int e = tid; e < kCB * DV; e += NW * 64) {
             const int r = e / DV, cc = e % DV;
             const int rr = r < n ? r : n - 1;
             const float ov = cb_ld<T>(a.dout, (rb + (t0 + rr) * a.H) * DV + cc);
             L.dO[r][cc] = r < n ? ov : 0.f;
         }
         const float *mc = a.mat + unit * kCbMat;
-        {
+        if (tid < kCB * kCB) {
             const int r = tid >> 4, cc = tid & 15;
             L.X[r][cc] = mc[r * kCB + cc];
             L.At[r][cc] = mc[2 * kCB * kCB + r * kCB + cc];
@@ -706,7 +714,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
     lds_barrier();
 
     // 2. U = X Diag(beta) W and dW = Diag(beta) X^T dU, column tiles over waves
-    for (int ct = wave; ct < CT; ct += 4) {
+    for (int ct = wave; ct < CT; ct += NW) {
         const int cc = 16 * ct + j;
         floatx4 U = {0, 0, 0, 0}, dW = {0, 0, 0, 0};
         const floatx4 xr = *reinterpret_cast<const floatx4 *>(&L.X[j][4 * g4]);
@@ -789,7 +797,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
     floatx4 dQt[NT], dKt[NT], dKh[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        const int ct = wave + 4 * u;
+        const int ct = wave + NW * u;
         dQt[u] = dKt[u] = dKh[u] = floatx4{0, 0, 0, 0};
         if (ct < RT) {
             const int cr = 16 * ct + j;
@@ -835,7 +843,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
     // 4. pair terms and the token gradients of this wave's channel tiles
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-        const int ct = wave + 4 * u;
+        const int ct = wave + NW * u;
         if (ct >= RT) continue;
         const int ch = 16 * ct + j;
         const float *qv = qin[u], *kv = kin[u];
@@ -895,9 +903,10 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
 // 2p when it is the last chunk); chunk 2p+1 forms the state entering it from
 // the first, chunk 2p the gradient leaving it from the second.
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
+__global__ __launch_bounds__(cb_grad_waves<DK>() * 64) void cb_grad_kernel(CbArgs a) {
     using Lds = CbGradLds<DK, DV>;
-    constexpr int RT = DK / 16, CT = DV / 16, NT = (RT + 3) / 4;
+    constexpr int RT = DK / 16, CT = DV / 16;
+    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
     __shared__ Lds L;
     const int64_t pair = blockIdx.x;
     const int64_t bh = pair / a.np;
@@ -906,7 +915,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float *stp = a.st + pair * DK * DV;
     const float *dnp = a.dn + pair * DK * DV;
-    CbNeighbour<DK> nb;
+    CbNeighbour<NT> nb;
     if (c1 >= a.nc) {
         cb_grad_chunk<T, DK, DV, kCbPlain>(a, L, bh, c0, wave, stp, dnp, nb);
         return;
@@ -917,10 +926,10 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
         const int64_t unit0 = bh * a.nc + c0;
         const float *wc = a.w + unit0 * kCB * DV;
         const float *mc = a.mat + unit0 * kCbMat;
-        L.X[tid >> 4][tid & 15] = mc[tid];
+        if (tid < kCB * kCB) L.X[tid >> 4][tid & 15] = mc[tid];
         if (tid < kCB) L.bet[tid] = cb_ld<T>(a.beta, rb + ((int64_t)c0 * kCB + tid) * a.H);
         lds_barrier();
-        for (int ct = wave; ct < CT; ct += 4) {
+        for (int ct = wave; ct < CT; ct += NW) {
             const int cc = 16 * ct + j;
             floatx4 U = {0, 0, 0, 0};
             const floatx4 xr = ld4(&L.X[j][4 * g4]);
@@ -933,7 +942,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
         const float *op = a.ops + unit0 * cb_ops_floats(DK);
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-            const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+            const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
             nb.r1[u] = ld4(op + kOpKhT * DK + ch * kCB + 4 * g4);   // K^[4 g4 + i][ch]
             nb.e[u] = op[kOpEbc * DK + ch];
         }
@@ -941,7 +950,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
     cb_grad_chunk<T, DK, DV, kCbSFromPrev>(a, L, bh, c1, wave, stp, dnp, nb);
     // keep chunk c1's dO and dW for chunk c0; its Q~, K~ rows and e^{b_C}
     lds_barrier();
-    for (int e = tid; e < kCB * DV; e += 256) {
+    for (int e = tid; e < kCB * DV; e += NW * 64) {
         const int r = e / DV, cc = e % DV;
         L.dO1[r][cc] = L.dO[r][cc];
         L.dW1[r][cc] = L.dW[r][cc];
@@ -950,7 +959,7 @@ __global__ __launch_bounds__(256) void cb_grad_kernel(CbArgs a) {
         const float *op = a.ops + (bh * a.nc + c1) * cb_ops_floats(DK);
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-            const int ch = 16 * (wave + 4 * u < RT ? wave + 4 * u : 0) + j;
+            const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
             nb.r1[u] = ld4(op + kOpQtT * DK + ch * kCB + 4 * g4);   // Q~[4 g4 + i][ch]
             nb.r2[u] = ld4(op + kOpKtT * DK + ch * kCB + 4 * g4);   // K~[4 g4 + i][ch]
             nb.e[u] = op[kOpEbc * DK + ch];
@@ -978,11 +987,11 @@ static hipError_t cb_inst(CbArgs a, int64_t nbh, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((cb_bwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 grid((unsigned)(nbh * a.np));
+    const dim3 grid((unsigned)(nbh * a.np)), gblock(cb_grad_waves<DK>() * 64);
     switch (a.DV) {
-    case 32: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 64>), grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 128>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 32>), grid, gblock, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 64>), grid, gblock, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((cb_grad_kernel<T, DK, 128>), grid, gblock, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
