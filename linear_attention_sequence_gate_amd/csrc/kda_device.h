@@ -65,12 +65,14 @@ __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float
 // exponential overflows.  Used by the gate kernel and the fused decode step,
 // so the gate has a single device definition.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float gate_value(float a, float z) {
-    float x = expf(a) * z;
+// ea = exp(a): kernels that reuse one channel's exp(a) take it once
+__device__ __forceinline__ float gate_value_ea(float ea, float z) {
+    float x = ea * z;
     float e = expf(-fabsf(x));              // in (0, 1]
     float s = (x >= 0.0f) ? 1.0f / (1.0f + e) : e / (1.0f + e);
     return kGmin * s;
 }
+__device__ __forceinline__ float gate_value(float a, float z) { return gate_value_ea(expf(a), z); }
 
 // The same gate for kernels that evaluate it inline on every element, with
 // the hardware's base-2 exponential and reciprocal and the per-channel part

@@ -33,22 +33,32 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ z,
     const int dstep = (int)(step % HD4);
     int64_t q = wave * 128 + lane;
     int c0 = (int)(q % HD4), c1 = (int)((q + 64) % HD4);
+    // exp(A) of this lane's two groups; the groups keep their channels from
+    // one pass to the next when the stride is a multiple of H dk (dstep = 0,
+    // the usual case), so it is evaluated again only when they move
+    auto expA = [&](int c) {
+        const floatx4 a = *reinterpret_cast<const floatx4 *>(A + 4 * c);
+        return floatx4{expf(a[0]), expf(a[1]), expf(a[2]), expf(a[3])};
+    };
+    floatx4 ea0 = expA(c0), ea1 = expA(c1);
     for (; q < n4; q += step) {
         const bool two = q + 64 < n4;
         const floatx4 z0 = load4(z + 4 * q);
         const floatx4 z1 = two ? load4(z + 4 * (q + 64)) : floatx4{0, 0, 0, 0};
-        const floatx4 a0 = *reinterpret_cast<const floatx4 *>(A + 4 * c0);
-        const floatx4 a1 = *reinterpret_cast<const floatx4 *>(A + 4 * c1);
         floatx4 g0, g1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            g0[j] = gate_value(a0[j], z0[j]);
-            g1[j] = gate_value(a1[j], z1[j]);
+            g0[j] = gate_value_ea(ea0[j], z0[j]);
+            g1[j] = gate_value_ea(ea1[j], z1[j]);
         }
         __builtin_nontemporal_store(g0, reinterpret_cast<floatx4 *>(g + 4 * q));
         if (two) __builtin_nontemporal_store(g1, reinterpret_cast<floatx4 *>(g + 4 * (q + 64)));
-        c0 += dstep; if (c0 >= HD4) c0 -= HD4;
-        c1 += dstep; if (c1 >= HD4) c1 -= HD4;
+        if (dstep != 0) {
+            c0 += dstep; if (c0 >= HD4) c0 -= HD4;
+            c1 += dstep; if (c1 >= HD4) c1 -= HD4;
+            ea0 = expA(c0);
+            ea1 = expA(c1);
+        }
     }
 }
 
