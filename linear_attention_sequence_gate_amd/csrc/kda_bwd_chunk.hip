@@ -76,11 +76,12 @@ struct CbArgs {
     int H, DV, nc, nsl, np;                      // np = chunk pairs = ceil(nc / 2)
 };
 
-// Decayed operands of one chunk, in the layouts the two state passes copy to
-// LDS unchanged: K~ [16][DK], K~^T [DK][16], K^ [16][DK], K^^T [DK][16],
-// Q~^T [DK][16] and e^{b_C} [DK].
-__host__ __device__ constexpr int cb_ops_floats(int DK) { return 81 * DK; }
-enum { kOpKt = 0, kOpKtT = 16, kOpKh = 32, kOpKhT = 48, kOpQtT = 64, kOpEbc = 80 };  // x DK
+// Decayed operands of one chunk, each once, channel-major: K~^T, K^^T, Q~^T
+// [DK][16] and e^{b_C} [DK].  The state passes copy them to LDS as they are,
+// and also transpose K~ (forward pass) or K^ (reverse pass) into token rows
+// while staging.
+__host__ __device__ constexpr int cb_ops_floats(int DK) { return 49 * DK; }
+enum { kOpKtT = 0, kOpKhT = 16, kOpQtT = 32, kOpEbc = 48 };  // x DK
 
 template <typename T> __device__ __forceinline__ float cb_ld(const void *p, int64_t i) {
     return to_f32(static_cast<const T *>(p)[i]);
@@ -184,8 +185,6 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbArgs a) {
             kt[r] = kv[r] * eb;
             kh[r] = kv[r] * exp_hw(bc - br);
             qt[r] = qv[r] * eb;
-            op[kOpKt * DK + tr * DK + ch] = kt[r];
-            op[kOpKh * DK + tr * DK + ch] = kh[r];
         }
 #pragma unroll
         for (int r = 0; r < HT; r += 4) {
@@ -279,7 +278,8 @@ template <int DK> struct CbStage {
 
 __device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
 
-// fwd: r1 = K~ (row-major), r2 = K^^T; bwd: r1 = K^, r2 = Q~^T, r3 = K~^T.
+// fwd: r1 = K~^T (staged as token rows), r2 = K^^T; bwd: r1 = K^^T (staged as
+// token rows), r2 = Q~^T, r3 = K~^T.
 // `vsrc` is v (fwd) or dO (bwd).
 template <typename T, int DK, bool BWD>
 __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int64_t bh, int64_t rb,
@@ -292,7 +292,7 @@ __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int6
     for (int u = 0; u < CbStage<DK>::NF; ++u) {
         const int idx = tid + 256 * u;
         if (idx < 4 * DK) {
-            st.r1[u] = ld4(op + (BWD ? kOpKh : kOpKt) * DK + 4 * idx);
+            st.r1[u] = ld4(op + (BWD ? kOpKhT : kOpKtT) * DK + 4 * idx);
             st.r2[u] = ld4(op + (BWD ? kOpQtT : kOpKhT) * DK + 4 * idx);
             if (BWD) st.r3[u] = ld4(op + kOpKtT * DK + 4 * idx);
         }
@@ -319,8 +319,9 @@ __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<
     for (int u = 0; u < CbStage<DK>::NF; ++u) {
         const int idx = tid + 256 * u;
         if (idx < 4 * DK) {
-            const int f = 4 * idx;
-            *reinterpret_cast<floatx4 *>(&L.rowm[buf][f / DK][f % DK]) = st.r1[u];
+            const int f = 4 * idx;                  // channel f / 16, tokens f % 16 ..
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.rowm[buf][f % kCB + e][f / kCB] = st.r1[u][e];
             *reinterpret_cast<floatx4 *>(&L.colm1[buf][f / kCB][f % kCB]) = st.r2[u];
             if (BWD) *reinterpret_cast<floatx4 *>(&L.colm2[buf][f / kCB][f % kCB]) = st.r3[u];
         }

@@ -220,7 +220,7 @@ def test_backward_validation(L):
         nc = (T + 15) // 16
         npair = (nc + 1) // 2
         return (2 * r(nbh * npair * dk * dv * 4) + r(nbh * nc * 768 * 4) + 2 * r(nbh * nc * 16 * dv * 4)
-                + r(nbh * nc * 81 * dk * 4))
+                + r(nbh * nc * 49 * dk * 4))
     assert chunked(1, 64, 32, 32) > 8 * 32 * 32 * 4
     assert L.kda_chunk_bwd_workspace_size(1, 64, 1, 32, 32, 1) == 256 + chunked(1, 64, 32, 32)
     token = 2 * 3 * 2 * 128 * 64 * 4 + 2 * (2 * 9 * 3) * (3 * 128 + 1) * 4
