@@ -191,7 +191,10 @@ size_t kda_chunk_fwd_gated_workspace_size(int64_t B, int64_t T, int64_t H, int64
 
 namespace {
 
-// kda_chunk_fwd and kda_chunk_fwd_pooled; `who` names the entry point in errors
+// Every chunked-prefill entry point: kda_chunk_fwd, kda_chunk_fwd_gated (z,
+// Ag set: the gate is evaluated inside the call), and the pooled and
+// variable-length forms (slots, cu_seqlens); `who` names the entry point in
+// errors.  Validation ends before the first HIP call.
 int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v, const float *g,
                    const void *beta, const float *initial_state, float *final_state, void *o,
                    void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
