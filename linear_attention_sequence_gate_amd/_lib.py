@@ -142,6 +142,47 @@ def _dev(*ts):
                 raise ValueError("libkda takes contiguous tensors only")
 
 
+_IN_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype=None) -> None:
+    """Raise ValueError unless `t` (when given) has exactly `shape` and `dtype`.
+
+    The C ABI receives bare pointers and cannot tell a wrong-sized or
+    wrong-typed buffer from a right one, so every wrapper checks each tensor
+    here, before the library is called."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _in_dtype(name: str, t: torch.Tensor) -> torch.dtype:
+    if t.dtype not in _IN_DTYPES:
+        raise ValueError(f"{name} has dtype {t.dtype}; bfloat16 or float32 expected")
+    return t.dtype
+
+
+def _same_device(*ts) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _rank(name: str, t: torch.Tensor, n: int) -> None:
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _workspace(t: Optional[torch.Tensor]) -> None:
+    if t is not None and t.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor, got {t.dtype}")
+
+
 def kda_version() -> str:
     return load_library().kda_version().decode()
 
@@ -153,13 +194,47 @@ def kda_last_error() -> str:
 def kda_gate(z: torch.Tensor, A: torch.Tensor, g: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
     """g = -5 * sigmoid(exp(A) * z).  z [B,T,H,dk] (bf16/fp32), A [H,dk] fp32 -> g fp32."""
-    _dev(z, A, g)
+    _rank("z", z, 4)
     B, T, H, dk = z.shape
+    _in_dtype("z", z)
+    _expect("A", A, (H, dk), torch.float32)
+    _expect("g", g, (B, T, H, dk), torch.float32)
+    _same_device(z, A, g)
+    _dev(z, A, g)
     if g is None:
         g = torch.empty(z.shape, device=z.device, dtype=torch.float32)
     _check(load_library().kda_gate(_ptr(z), _ptr(A), _ptr(g), B, T, H, dk, _dtype_code(z),
                                    _stream(stream)))
     return g
+
+
+def _check_prefill(q, k, v, beta, initial_state, final_state, o, workspace, g=None, z=None,
+                   A=None, d_o=None, d_final_state=None, state_rows=None):
+    """Shapes and dtypes of a prefill-type call: q, k (and z) [B,T,H,dk], v
+    and o [B,T,H,dv], beta [B,T,H], all in q's dtype; g [B,T,H,dk], A [H,dk]
+    and the states [B,H,dk,dv] (or [state_rows,H,dk,dv]) in fp32.  Returns
+    (B, T, H, dk, dv)."""
+    _rank("q", q, 4)
+    B, T, H, dk = q.shape
+    dt = _in_dtype("q", q)
+    _rank("v", v, 4)
+    dv = v.shape[-1]
+    _expect("k", k, (B, T, H, dk), dt)
+    _expect("v", v, (B, T, H, dv), dt)
+    _expect("beta", beta, (B, T, H), dt)
+    _expect("z", z, (B, T, H, dk), dt)
+    _expect("o", o, (B, T, H, dv), dt)
+    _expect("d_o", d_o, (B, T, H, dv), dt)
+    _expect("g", g, (B, T, H, dk), torch.float32)
+    _expect("A", A, (H, dk), torch.float32)
+    rows = B if state_rows is None else state_rows
+    _expect("initial_state", initial_state, (rows, H, dk, dv), torch.float32)
+    _expect("final_state", final_state, (rows, H, dk, dv), torch.float32)
+    _expect("d_final_state", d_final_state, (B, H, dk, dv), torch.float32)
+    _workspace(workspace)
+    _same_device(q, k, v, beta, z, o, d_o, g, A, initial_state, final_state, d_final_state,
+                 workspace)
+    return B, T, H, dk, dv
 
 
 def kda_chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
@@ -180,9 +255,9 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
                   want_final_state: bool = True, flags: int = 0, workspace=None,
                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise prefill.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    B, T, H, dk, dv = _check_prefill(q, k, v, beta, initial_state, final_state, o, workspace,
+                                     g=g)
     _dev(q, k, v, g, beta, initial_state, final_state, o, workspace)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
     dt = _dtype_code(q)
     if o is None:
         o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
@@ -214,9 +289,11 @@ def kda_chunk_fwd_gated(q, k, v, z, A, beta, initial_state=None, final_state=Non
                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Gate and chunkwise prefill in one call (g from z and A inside it).
     Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    B, T, H, dk, dv = _check_prefill(q, k, v, beta, initial_state, final_state, o, workspace,
+                                     z=z, A=A)
+    if z is None or A is None:
+        raise ValueError("z and A are required")
     _dev(q, k, v, z, A, beta, initial_state, final_state, o, workspace)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
     dt = _dtype_code(q)
     if o is None:
         o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
@@ -234,11 +311,37 @@ def kda_chunk_fwd_gated(q, k, v, z, A, beta, initial_state=None, final_state=Non
     return o, final_state
 
 
+def _check_decode(q, k, v, z, A, beta, o, state=None, pool=None):
+    """Shapes and dtypes of a decode call: q, k, z [N,H,dk], v and o [N,H,dv],
+    beta [N,H], all in q's dtype; A [H,dk] and the state [N,H,dk,dv] (or a
+    pool [n_slots,H,dk,dv]) in fp32.  Returns (N, H, dk, dv)."""
+    _rank("q", q, 3)
+    N, H, dk = q.shape
+    dt = _in_dtype("q", q)
+    _rank("v", v, 3)
+    dv = v.shape[-1]
+    _expect("k", k, (N, H, dk), dt)
+    _expect("z", z, (N, H, dk), dt)
+    _expect("v", v, (N, H, dv), dt)
+    _expect("beta", beta, (N, H), dt)
+    _expect("o", o, (N, H, dv), dt)
+    _expect("A", A, (H, dk), torch.float32)
+    if state is not None:
+        _expect("state", state, (N, H, dk, dv), torch.float32)
+    if pool is not None:
+        _rank("state_pool", pool, 4)
+        _expect("state_pool", pool, (pool.shape[0], H, dk, dv), torch.float32)
+    for name, t in (("z", z), ("A", A), ("beta", beta)):
+        if t is None:
+            raise ValueError(f"{name} is required")
+    _same_device(q, k, v, z, A, beta, o, state, pool)
+    return N, H, dk, dv
+
+
 def kda_decode_step(q, k, v, z, A, beta, state, o=None, stream=None) -> torch.Tensor:
     """One decode step; `state` [N,H,dk,dv] fp32 is updated in place.  Returns o [N,H,dv]."""
+    N, H, dk, dv = _check_decode(q, k, v, z, A, beta, o, state=state)
     _dev(q, k, v, z, A, beta, state, o)
-    N, H, dk = q.shape
-    dv = v.shape[-1]
     if o is None:
         o = torch.empty((N, H, dv), device=q.device, dtype=q.dtype)
     _check(load_library().kda_decode_step(
@@ -255,8 +358,12 @@ def _slots(slots: torch.Tensor) -> torch.Tensor:
 
 def kda_state_pool_reset(state_pool, slots, stream=None) -> None:
     """Zero the listed slots of a state pool [n_slots, H, dk, dv] fp32."""
+    _rank("state_pool", state_pool, 4)
+    if state_pool.dtype != torch.float32:
+        raise ValueError(f"state_pool has dtype {state_pool.dtype}, expected torch.float32")
     _dev(state_pool)
     slots = _slots(slots)
+    _same_device(state_pool, slots)
     n_slots, H, dk, dv = state_pool.shape
     _check(load_library().kda_state_pool_reset(
         _ptr(state_pool), _ptr(slots), slots.numel(), n_slots, H, dk, dv, _stream(stream)))
@@ -267,10 +374,13 @@ def kda_chunk_fwd_pooled(q, k, v, g, beta, state_pool, slots, o=None, flags: int
     """Chunkwise prefill of B sequences whose states live in `state_pool`
     [n_slots, H, dk, dv] fp32 at `slots` [B] int32 (read, then overwritten
     with the final states).  Returns o [B,T,H,dv]."""
+    _rank("state_pool", state_pool, 4)
+    B, T, H, dk, dv = _check_prefill(q, k, v, beta, state_pool, None, o, workspace, g=g,
+                                     state_rows=state_pool.shape[0])
     _dev(q, k, v, g, beta, state_pool, o, workspace)
     slots = _slots(slots)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    _expect("slots", slots, (B,))
+    _same_device(q, slots)
     n_slots = state_pool.shape[0]
     dt = _dtype_code(q)
     if o is None:
@@ -291,10 +401,11 @@ def kda_decode_step_pooled(q, k, v, z, A, beta, state_pool, slots, o=None,
     """One decode step for N sequences whose states live in `state_pool`
     [n_slots, H, dk, dv] fp32 at `slots` [N] int32, updated in place.
     Returns o [N,H,dv]."""
+    N, H, dk, dv = _check_decode(q, k, v, z, A, beta, o, pool=state_pool)
     _dev(q, k, v, z, A, beta, state_pool, o)
     slots = _slots(slots)
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    _expect("slots", slots, (N,))
+    _same_device(q, slots)
     if o is None:
         o = torch.empty((N, H, dv), device=q.device, dtype=q.dtype)
     _check(load_library().kda_decode_step_pooled(
@@ -303,19 +414,43 @@ def kda_decode_step_pooled(q, k, v, z, A, beta, state_pool, slots, o=None,
     return o
 
 
+def _check_varlen(q, k, v, beta, state_pool, slots, cu_seqlens, o, g=None, z=None, A=None):
+    """Shapes and dtypes of a packed (variable-length) prefill: q, k (and z)
+    [total,H,dk], v and o [total,H,dv], beta [total,H] in q's dtype; g
+    [total,H,dk], A [H,dk] and the pool [n_slots,H,dk,dv] fp32; slots [B]
+    int32 and cu_seqlens [B+1] int64.  Returns (total, H, dk, dv, B)."""
+    _rank("q", q, 3)
+    total, H, dk = q.shape
+    dt = _in_dtype("q", q)
+    _rank("v", v, 3)
+    dv = v.shape[-1]
+    _expect("k", k, (total, H, dk), dt)
+    _expect("z", z, (total, H, dk), dt)
+    _expect("v", v, (total, H, dv), dt)
+    _expect("beta", beta, (total, H), dt)
+    _expect("o", o, (total, H, dv), dt)
+    _expect("g", g, (total, H, dk), torch.float32)
+    _expect("A", A, (H, dk), torch.float32)
+    _rank("state_pool", state_pool, 4)
+    _expect("state_pool", state_pool, (state_pool.shape[0], H, dk, dv), torch.float32)
+    _rank("cu_seqlens", cu_seqlens, 1)
+    B = cu_seqlens.numel() - 1
+    _expect("slots", slots, (B,))
+    _same_device(q, k, v, beta, z, g, A, o, state_pool, slots, cu_seqlens)
+    return total, H, dk, dv, B
+
+
 def kda_chunk_fwd_varlen_pooled(q, k, v, g, beta, state_pool, slots, cu_seqlens, o=None,
                                 flags: int = 0, stream=None) -> torch.Tensor:
     """Prefill of B sequences of different lengths packed along the token axis
     (q, k, g [total,H,dk], v [total,H,dv], beta [total,H]; sequence b is rows
     cu_seqlens[b] .. cu_seqlens[b+1]-1, cu_seqlens int64 [B+1] on the device),
     with states in `state_pool` at `slots` [B].  Returns o [total,H,dv]."""
+    total, H, dk, dv, B = _check_varlen(q, k, v, beta, state_pool, slots, cu_seqlens, o, g=g)
     _dev(q, k, v, g, beta, state_pool, o)
     slots = _slots(slots)
     if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int64 CUDA tensor")
-    total, H, dk = q.shape
-    dv = v.shape[-1]
-    B = cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty((total, H, dv), device=q.device, dtype=q.dtype)
     _check(load_library().kda_chunk_fwd_varlen_pooled(
@@ -329,13 +464,14 @@ def kda_chunk_fwd_varlen_pooled_gated(q, k, v, z, A, beta, state_pool, slots, cu
                                       flags: int = 0, stream=None) -> torch.Tensor:
     """kda_chunk_fwd_varlen_pooled with the gate inside the chunk kernel: z
     [total,H,dk] and A [H,dk] instead of g.  Returns o [total,H,dv]."""
+    total, H, dk, dv, B = _check_varlen(q, k, v, beta, state_pool, slots, cu_seqlens, o, z=z,
+                                        A=A)
+    if z is None or A is None:
+        raise ValueError("z and A are required")
     _dev(q, k, v, z, A, beta, state_pool, o)
     slots = _slots(slots)
     if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int64 CUDA tensor")
-    total, H, dk = q.shape
-    dv = v.shape[-1]
-    B = cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty((total, H, dv), device=q.device, dtype=q.dtype)
     _check(load_library().kda_chunk_fwd_varlen_pooled_gated(
@@ -356,9 +492,11 @@ def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
     recurrence.  Returns dict dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta
     [B,T,H] and d_initial_state [B,H,dk,dv] (fp32; the last None if not wanted).
     flags: KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD (token-level path)."""
+    B, T, H, dk, dv = _check_prefill(q, k, v, beta, initial_state, None, None, workspace, g=g,
+                                     d_o=d_o, d_final_state=d_final_state)
+    if g is None or d_o is None:
+        raise ValueError("g and d_o are required")
     _dev(q, k, v, g, beta, initial_state, d_o, d_final_state, workspace)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
     dt = _dtype_code(q)
     f32 = dict(device=q.device, dtype=torch.float32)
     out = dict(dq=torch.empty(B, T, H, dk, **f32), dk=torch.empty(B, T, H, dk, **f32),
@@ -383,8 +521,14 @@ def kda_gate_bwd_workspace_size(B: int, T: int, H: int, dk: int) -> int:
 
 def kda_gate_bwd(z, A, dg, workspace=None, stream=None) -> dict:
     """Reverse mode of kda_gate: dz [B,T,H,dk] and dA [H,dk] (fp32) of <g, dg>."""
-    _dev(z, A, dg, workspace)
+    _rank("z", z, 4)
     B, T, H, dk = z.shape
+    _in_dtype("z", z)
+    _expect("A", A, (H, dk), torch.float32)
+    _expect("dg", dg, (B, T, H, dk), torch.float32)
+    _workspace(workspace)
+    _same_device(z, A, dg, workspace)
+    _dev(z, A, dg, workspace)
     f32 = dict(device=z.device, dtype=torch.float32)
     out = dict(dz=torch.empty(B, T, H, dk, **f32), dA=torch.empty(H, dk, **f32))
     if workspace is None:

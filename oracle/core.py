@@ -78,11 +78,23 @@ def max_threads() -> int:
 
 
 def rho(x, ref) -> float:
-    """Parity metric max|x - ref| / max|ref| (whole tensor)."""
+    """Parity metric max|x - ref| / max|ref| over the whole tensor: the largest
+    absolute deviation, relative to the largest magnitude of the reference.
+
+    The two must have the same shape (no broadcasting: a reference for one
+    chain must not be compared against a whole batch).  An all-zero reference
+    gives the absolute deviation; a NaN anywhere gives NaN, which fails every
+    `<=` tolerance check."""
     x = _f64(x)
     ref = _f64(ref)
-    den = float(np.max(np.abs(ref))) if ref.size else 0.0
-    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    if x.shape != ref.shape:
+        raise ValueError(f"rho: shapes differ: {x.shape} vs reference {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(x - ref)))
+    if np.isnan(den) or np.isnan(num):
+        return float("nan")
     if den == 0.0:
         return num
     return num / den
