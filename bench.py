@@ -264,6 +264,57 @@ def time_long_prefill(reps=3):
     return out
 
 
+SMALL = inputs.WORKLOADS["prefill_h8_t4k"]
+
+
+def time_small_prefill(reps=20, copies=5, warmup=10):
+    """kda_chunk_fwd_gated on the few-chain short workload (B1 H8 T4096 d128
+    bf16: 8 chains, 16 workgroups in one pass), with the segment count the
+    library picks.  Its 56 MiB of inputs and outputs would stay in the 256 MB
+    last-level cache across repetitions, so the calls rotate over `copies`
+    independent sets of inputs and outputs."""
+    w = SMALL
+    dev = torch.device("cuda")
+    xs = [inputs.make_prefill_inputs(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.seed + 97 * i,
+                                     device=dev, s0_std=w.s0_std,
+                                     stress_heads_mean=w.stress_heads_mean)
+          for i in range(copies)]
+    os_ = [torch.empty(w.B, w.T, w.H, w.dv, device=dev, dtype=w.dtype) for _ in range(copies)]
+    Ss = [torch.empty(w.B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32) for _ in range(copies)]
+    nseg = _lib.kda_chunk_fwd_auto_segments(w.B, w.T, w.H, w.dk, w.dv, 1)
+    ws = torch.empty(max(_lib.kda_chunk_fwd_gated_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 1), 256),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        x = xs[i % copies]
+        _lib.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
+                                 final_state=Ss[i % copies], o=os_[i % copies], workspace=ws,
+                                 stream=stream)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    work = prefill_work(w)
+    s_ = ms / 1e3
+    out = {"ms": ms, "segments": nseg, "tokens_per_s": w.B * w.T / s_,
+           "head_tokens_per_s": work["head_tokens"] / s_,
+           "hbm_frac_of_roofline": work["fused_bytes"] / s_ / 1e9 / HBM_PEAK_GBS,
+           "bytes_per_call": work["fused_bytes"],
+           "workload": w.note + "; gate fused (kda_chunk_fwd_gated); inputs rotated over "
+                                f"{copies} copies"}
+    del xs, os_, Ss, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_pairwise_diagonal(reps=5):
     """kda_chunk_fwd on the benchmark's prefill workload with the dense MFMA
     diagonal tiles (what the gate floor allows) and with the position-pair
@@ -458,12 +509,18 @@ def _pmc_rows(d, counter):
                     continue
                 key = (f, r.get("Dispatch_Id", r.get("Correlation_Id")))
                 rows.append((key, r["Kernel_Name"], float(r["Counter_Value"])))
-    # sum the per-instance values of one dispatch
+    # sum the per-instance values of one dispatch; dispatches in launch order
     agg = {}
     for key, name, val in rows:
         n, v = agg.get(key, (name, 0.0))
         agg[key] = (n, v + val)
-    return list(agg.values())
+
+    def order(key):
+        try:
+            return (key[0], int(key[1]))
+        except (TypeError, ValueError):
+            return (key[0], 0)
+    return [agg[k] for k in sorted(agg, key=order)]
 
 
 def ingest_pmc(fetch_dir, write_dir):
@@ -524,9 +581,10 @@ def ingest_pmc(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+TRACE_STEPS, TRACE_WARMUP, TRACE_DECODE = 20, 20, 200
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o bench -- "
-             "python3 -u bench.py --steps 10 --warmup 3 --decode-steps 200 --no-cpu-baseline --no-parity "
-             "--no-extras")
+             f"python3 -u bench.py --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} "
+             f"--decode-steps {TRACE_DECODE} --no-cpu-baseline --no-parity --no-extras")
 EXTRA_TRACES = {
     # name: (bench.py --only value, profile file, what the run holds)
     "long": ("long", "kernel_trace_prefill_b1h32t1m_split.md",
@@ -557,6 +615,11 @@ def extra_trace_cmd(name):
 
 
 def ingest_trace(d):
+    """Summarise the kernel trace of TRACE_CMD.  Per kernel: every call, and
+    the calls the benchmark times (the last `steps` launches, after the
+    warm-up whose first launches run while the clocks ramp).  The fused
+    kernel's HBM fraction is computed from the timed calls, as bench.py's
+    `roofline` is."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {d}")
@@ -566,25 +629,42 @@ def ingest_trace(d):
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     lines = ["# Kernel durations (rocprofv3 kernel trace)", "",
-             "Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step: 3 warm-up and 10",
-             "timed launches; then gate + chunk as two kernels: 2 warm-up and 10 timed steps),",
-             "decode 256x32 d128 (20 warm-up + 200 steps), plus the 1 GiB calibration copy.",
-             "Durations from the trace's start/end timestamps.", "",
+             f"Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step: {TRACE_WARMUP} warm-up "
+             f"and {TRACE_STEPS} timed launches; then gate + chunk as two kernels: 2 warm-up and "
+             f"{TRACE_STEPS} timed steps), decode 256x32 d128 (20 warm-up + {TRACE_DECODE} steps), "
+             "plus the 1 GiB calibration copy.  Durations from the trace's start/end timestamps; "
+             "'timed' is the last launches of each kernel, the ones the benchmark times.", "",
              "Command (from the repository root):", "", "    " + TRACE_CMD,
              "    python3 bench.py --ingest-trace gpurun_out/ktrace", "",
-             "| kernel | calls | avg (us) | min (us) | max (us) | avg without first call (us) |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg (us) | min (us) | max (us) | timed calls | timed avg (us) |",
+             "|---|---|---|---|---|---|---|"]
     frags = dict((k, v[0]) for k, v in KERNELS.items())
     frags["copy (calibration)"] = ("copyBuffer",)
+    timed_n = {"fused_fwd": TRACE_STEPS, "chunk_fwd": TRACE_STEPS, "gate": TRACE_STEPS,
+               "decode_step": TRACE_DECODE}
+    rec = {}
     for label, frag in frags.items():
         us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
               for r in rows if _matches(r["Kernel_Name"], frag)]
         if not us:
             continue
         names = sorted({r["Kernel_Name"] for r in rows if _matches(r["Kernel_Name"], frag)})
-        rest = us[1:] or us
+        n = min(timed_n.get(label, len(us)), len(us))
+        timed = us[-n:]
+        rec[label] = sum(timed) / len(timed)
         lines.append(f"| {label}: `{names[0][:70]}` | {len(us)} | {sum(us) / len(us):.1f} "
-                     f"| {min(us):.1f} | {max(us):.1f} | {sum(rest) / len(rest):.1f} |")
+                     f"| {min(us):.1f} | {max(us):.1f} | {n} | {rec[label]:.1f} |")
+    if "fused_fwd" in rec:
+        fb = prefill_work(PREFILL)["fused_bytes"]
+        frac = fb / (rec["fused_fwd"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        lines += ["", f"Fused kernel, timed launches: {fb} algorithmic bytes per launch / "
+                      f"{rec['fused_fwd']:.1f} us = {fb / (rec['fused_fwd'] * 1e-6) / 1e9:.0f} GB/s, "
+                      f"{frac:.4f} of 8 TB/s."]
+    if "decode_step" in rec:
+        db = decode_bytes(DECODE)
+        lines += ["", f"Decode, timed launches: {db} bytes per step / {rec['decode_step']:.1f} us = "
+                      f"{db / (rec['decode_step'] * 1e-6) / 1e9:.0f} GB/s, "
+                      f"{db / (rec['decode_step'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} of 8 TB/s."]
     lines.append("")
     os.makedirs(os.path.dirname(TRACE_MD), exist_ok=True)
     with open(TRACE_MD, "w") as fh:
@@ -660,10 +740,13 @@ def recorded_mfma_busy():
     return rec.get("mfma_busy_frac")
 
 
+SQ_STEPS, SQ_WARMUP = 5, 20
+
+
 def sq_cmd(i):
     return (f"rocprofv3 --pmc {SQ_PASSES[i]} --output-format csv -d gpurun_out/sq{i} -- "
-            "python3 -u bench.py --steps 2 --warmup 1 --decode-steps 20 --no-cpu-baseline "
-            "--no-parity --no-extras")
+            f"python3 -u bench.py --steps {SQ_STEPS} --warmup {SQ_WARMUP} --decode-steps 20 "
+            "--no-cpu-baseline --no-parity --no-extras")
 
 
 def ingest_sq(dirs):
@@ -677,7 +760,8 @@ def ingest_sq(dirs):
                 rows = _pmc_rows(d, ctr)
             except SystemExit:
                 continue
-            v = [x for n, x in rows if _matches(n, KERNELS["fused_fwd"][0])]
+            # the timed dispatches only: the last SQ_STEPS, after the warm-up
+            v = [x for n, x in rows if _matches(n, KERNELS["fused_fwd"][0])][-SQ_STEPS:]
             if v:
                 vals[ctr] = sum(v) / len(v)
     w = PREFILL
@@ -686,7 +770,8 @@ def ingest_sq(dirs):
     simd_periods = wgs * 4 * periods
     lines = ["# Shader-sequencer counters, chunk32_kernel with the gate fused (rocprofv3 --pmc)", "",
              "Workload: prefill B4 H32 T32768 d128 bf16, 256 workgroups of 12 waves, "
-             f"{periods} periods of 32 tokens each.", "",
+             f"{periods} periods of 32 tokens each.  Averaged over the {SQ_STEPS} timed "
+             f"dispatches after {SQ_WARMUP} warm-up ones.", "",
              "Commands (from the repository root):", ""]
     lines += ["    " + sq_cmd(i) for i in range(len(SQ_PASSES))]
     lines += ["    python3 bench.py --ingest-sq " + " ".join(f"gpurun_out/sq{i}" for i in range(len(SQ_PASSES))), "",
@@ -746,7 +831,7 @@ def main():
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
     ap.add_argument("--ingest-trace-extra", nargs=2, metavar=("NAME", "TRACE_DIR"))
     ap.add_argument("--ingest-sq", nargs="+", metavar="PMC_DIR")
-    ap.add_argument("--only", choices=("long", "pairwise", "backward"),
+    ap.add_argument("--only", choices=("long", "pairwise", "backward", "small"),
                     help="time only one extra line and print its record")
     args = ap.parse_args()
     if args.ingest_pmc:
@@ -770,7 +855,7 @@ def main():
     torch.cuda.init()
     if args.only:
         rec = {"long": time_long_prefill, "pairwise": time_pairwise_diagonal,
-               "backward": time_backward}[args.only]()
+               "backward": time_backward, "small": time_small_prefill}[args.only]()
         print(json.dumps(rec), flush=True)
         return
 
@@ -796,6 +881,7 @@ def main():
     del res
     torch.cuda.empty_cache()
 
+    small_res = None if args.no_extras else time_small_prefill()
     long_res = None if args.no_extras else time_long_prefill()
     pair_res = None if args.no_extras else time_pairwise_diagonal()
     bwd_res = None if args.no_extras else time_backward()
@@ -842,6 +928,7 @@ def main():
                                    "chunk_hbm_frac": chunk_gbs / HBM_PEAK_GBS,
                                    "chunk_bytes_per_launch": work["chunk_bytes"],
                                    "chunk_traffic": traffic["chunk_fwd"]}},
+        "prefill_h8_t4k": small_res,
         "prefill_long": long_res,
         "prefill_pairwise_diagonal": pair_res,
         "prefill_backward": bwd_res,

@@ -25,6 +25,7 @@ forms, brute-force unrolled products and invariants; see tests/test_oracle_*.py.
 """
 from .core import (  # noqa: F401
     GMIN,
+    RhoAccumulator,
     TILE,
     backward_np,
     build_oracle,

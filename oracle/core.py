@@ -100,6 +100,37 @@ def rho(x, ref) -> float:
     return num / den
 
 
+class RhoAccumulator:
+    """rho of a tensor compared in pieces (token windows, chain by chain): the
+    running max|x - ref| and max|ref| over every piece seen, so that value()
+    equals rho(x, ref) of the whole tensor whatever the split."""
+
+    def __init__(self):
+        self.num = 0.0
+        self.den = 0.0
+        self.nan = False
+
+    def add(self, x, ref) -> None:
+        x = _f64(x)
+        ref = _f64(ref)
+        if x.shape != ref.shape:
+            raise ValueError(f"RhoAccumulator: shapes differ: {x.shape} vs reference {ref.shape}")
+        if ref.size == 0:
+            return
+        d = float(np.max(np.abs(x - ref)))
+        r = float(np.max(np.abs(ref)))
+        if np.isnan(d) or np.isnan(r):
+            self.nan = True
+            return
+        self.num = max(self.num, d)
+        self.den = max(self.den, r)
+
+    def value(self) -> float:
+        if self.nan:
+            return float("nan")
+        return self.num if self.den == 0.0 else self.num / self.den
+
+
 # ----------------------------------------------------------------------------
 # C oracle wrappers
 # ----------------------------------------------------------------------------
@@ -138,10 +169,19 @@ def forward(q, k, v, g, beta, S0=None, want_o: bool = True,
     return o, ST
 
 
-def decode_step(q, k, v, z, A, beta, state) -> Tuple[np.ndarray, np.ndarray]:
-    """One decode step.  Returns (o [N,H,dv], new state [N,H,dk,dv]); inputs untouched."""
+def decode_step(q, k, v, z, A, beta, state, inplace: bool = False
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step.  Returns (o [N,H,dv], new state [N,H,dk,dv]).  Inputs are
+    untouched, except that with inplace=True a C-contiguous float64 `state` is
+    overwritten with the new state and returned (no copy of a large state)."""
     q, k, v, z, A, beta = (_f64(x) for x in (q, k, v, z, A, beta))
-    S = _f64(state).copy()
+    if inplace:
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous):
+            raise ValueError("inplace decode_step needs a C-contiguous float64 numpy state")
+        S = state
+    else:
+        S = _f64(state).copy()
     N, H, dk = k.shape
     dv = v.shape[-1]
     o = np.empty((N, H, dv))

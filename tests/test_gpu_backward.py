@@ -3,7 +3,9 @@ oracle's reverse mode on the same inputs, for both paths (16-token chunks on
 the matrix cores, and token by token): fp32 and bf16, every (dk, dv) family,
 T around the 8-token checkpoint and 16-token chunk spacings, with and without
 the initial state and the final-state gradient, the decay at the gate's
-floor, and (token path) with the floor removed."""
+floor, and (token path) with the floor removed.  The gradients are fp32
+arithmetic for either input dtype (the oracle reads the same rounded inputs),
+so every case is held to 1e-4."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,7 @@ import torch
 import oracle
 from linear_attention_sequence_gate_amd import KdaError, kda_chunk_bwd
 from linear_attention_sequence_gate_amd._lib import KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD
-from kda_testutil import TOL, oracle_gate_f32, prefill_device, rho, say
+from kda_testutil import GRAD_TOL, oracle_gate_f32, prefill_device, rho, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +38,7 @@ def _run(dtype, B, T, H, dk, dv, seed, s0=True, dst=True, g=None, path="chunked"
         assert np.isfinite(out[name].cpu().numpy()).all(), name
     print("    " + " ".join(f"{k}={v:.1e}" for k, v in res.items()), flush=True)
     for name, r in res.items():
-        assert r <= TOL[dtype], (name, r)
+        assert r <= GRAD_TOL, (name, r)
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -124,4 +126,4 @@ def test_backward_benchmark_shape_sampled_chains():
         res["d_initial_state"] = rho(out["d_initial_state"][b:b + 1, h:h + 1], ref["dS0"])
         print(f"    b{b} h{h} " + " ".join(f"{k}={v:.1e}" for k, v in res.items()), flush=True)
         for name, r in res.items():
-            assert r <= TOL[torch.bfloat16], (b, h, name, r)
+            assert r <= GRAD_TOL, (b, h, name, r)

@@ -88,50 +88,55 @@ def test_decode_full_size_one_step_all_heads():
     torch.cuda.empty_cache()
 
 
-def test_decode_full_size_1000_steps_sampled():
-    """1000 consecutive in-place steps with fresh seeded inputs; a seeded subset
-    of 32 (sequence, head) pairs followed by the oracle through all 1000 steps
-    (pairs are independent, so the subset is exact)."""
+@pytest.mark.timeout(900)
+def test_decode_full_size_1000_steps_all_pairs():
+    """1000 consecutive in-place steps with fresh seeded inputs, every one of
+    the 256 x 32 (sequence, head) pairs followed by the oracle through all
+    1000 steps: every step's outputs and the final states."""
     w = inputs.WORKLOADS["decode_256x32"]
-    say("decode full size, 1000 steps, sampled pairs")
+    say("decode full size, 1000 steps, all pairs")
     st = inputs.make_decode_state(w.B, w.H, w.dk, w.dv, w.seed, device="cuda", s0_std=w.s0_std)
     S = st["S"].clone()
-    pick = torch.randperm(w.B * w.H, generator=torch.Generator().manual_seed(3))[:32]
-    n_idx, h_idx = (pick // w.H).cuda(), (pick % w.H).cuda()
-    # the sampled pairs become the 32 "heads" of one oracle problem, each with its own A row
-    S_ref = st["S"][n_idx, h_idx].double().cpu().numpy()[None]        # [1,32,dk,dv]
-    A_sub = st["A"][h_idx].contiguous()
-    worst_o = 0.0
+    S_ref = np.ascontiguousarray(st["S"].double().cpu().numpy())
+    A_host = st["A"].cpu()
+    acc_o = oracle.RhoAccumulator()
     for t in range(w.decode_steps):
         x = _step_inputs(w.B, w.H, w.dk, w.dv, w.dtype, w.seed, t)
         o = kda_decode_step(x["q"], x["k"], x["v"], x["z"], st["A"], x["beta"], S)
-        sub = {n: x[n][n_idx, h_idx].unsqueeze(0) for n in ("q", "k", "v", "z", "beta")}
-        o_ref, S_ref = oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["z"], A_sub,
-                                          sub["beta"], S_ref)
-        worst_o = max(worst_o, rho(o[n_idx, h_idx].unsqueeze(0), o_ref))
+        o_ref, _ = oracle.decode_step(x["q"], x["k"], x["v"], x["z"], A_host, x["beta"], S_ref,
+                                      inplace=True)
+        acc_o.add(o, o_ref)
         if t % 250 == 0:
-            say("decode step", t, "worst rho(o) so far", worst_o)
+            say("decode step", t, "rho(o) so far", acc_o.value())
     torch.cuda.synchronize()
-    assert worst_o <= TOL[w.dtype]
-    assert rho(S[n_idx, h_idx].unsqueeze(0), S_ref) <= TOL[w.dtype]
+    rs = rho(S, S_ref)
+    print(f"    rho(o) over 1000 steps={acc_o.value():.3e} rho(final S)={rs:.3e}", flush=True)
+    assert acc_o.value() <= TOL[w.dtype]
+    assert rs <= TOL[w.dtype]
     del st, S
     torch.cuda.empty_cache()
 
 
 def test_decode_continues_a_fused_gate_prefill():
     """bf16, dk = dv = 128: kda_chunk_fwd_gated over T0 tokens, then T1 decode
-    steps, equal one kda_chunk_fwd_gated over all of them (the state is the
-    whole carry; the two paths evaluate the gate by different formulas of the
-    same function)."""
+    steps.  Both legs against the oracle:
+      - the prefill's outputs and state, and the decode outputs and state,
+        against the oracle's token loop over all T0 + T1 tokens (bf16 bar);
+      - the decode steps started from the prefill's own GPU state, against
+        the oracle's decode steps started from that same state: the decode
+        kernel's arithmetic is fp32 throughout, so its state meets 1e-4, and
+        its bf16 outputs meet bf16's unit roundoff (2^-8, half an ulp relative
+        to the value) of the largest output plus that: 2^-8 + 1e-4."""
     from linear_attention_sequence_gate_amd import kda_chunk_fwd_gated
     N, H, d, T0, T1 = 2, 4, 128, 200, 12
-    say("fused prefill then decode vs one fused prefill")
+    say("fused prefill then decode, against the oracle")
     x = inputs.make_prefill_inputs(N, T0 + T1, H, d, d, torch.bfloat16, 79, device="cuda",
                                    s0_std=0.02, stress_heads_mean=3.0)
-    o_all, S_all = kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"])
     head = {n: x[n][:, :T0].clone() for n in ("q", "k", "v", "z", "beta")}
     o_head, S = kda_chunk_fwd_gated(head["q"], head["k"], head["v"], head["z"], x["A"],
                                     head["beta"], x["S0"])
+    torch.cuda.synchronize()
+    S_start = np.ascontiguousarray(S.double().cpu().numpy())    # the prefill's own state
     outs = []
     for t in range(T0, T0 + T1):
         sl = lambda a: a[:, t].contiguous()
@@ -139,10 +144,23 @@ def test_decode_continues_a_fused_gate_prefill():
                                     sl(x["beta"]), S))
     torch.cuda.synchronize()
     o_dec = torch.stack(outs, dim=1)
-    # the head's last chunk is partial: its decay factors are formed over the
-    # padded subtile, so equal up to rounding (bf16 outputs: a flipped ulp)
+
+    g_ref = oracle.gate(x["z"], x["A"])
+    o_all, S_all = oracle.forward(x["q"], x["k"], x["v"], g_ref, x["beta"], x["S0"])
     assert rho(o_head, o_all[:, :T0]) <= TOL[torch.bfloat16]
     assert rho(o_dec, o_all[:, T0:]) <= TOL[torch.bfloat16]
-    # the chunked path's products take bf16 operands (about 3e-3 from the
-    # oracle on either side), so the two states meet at the bf16 bar
     assert rho(S, S_all) <= TOL[torch.bfloat16]
+
+    S_ref = S_start
+    o_ref = []
+    A_host = x["A"].cpu()
+    for t in range(T0, T0 + T1):
+        sl = lambda a: a[:, t]
+        o_t, S_ref = oracle.decode_step(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["z"]), A_host,
+                                        sl(x["beta"]), S_ref, inplace=True)
+        o_ref.append(o_t)
+    o_ref = np.stack(o_ref, axis=1)
+    ro, rs = rho(o_dec, o_ref), rho(S, S_ref)
+    print(f"    decode from the prefill's state: rho(o)={ro:.3e} rho(S)={rs:.3e}", flush=True)
+    assert rs <= 1e-4
+    assert ro <= 2.0 ** -8 + 1e-4

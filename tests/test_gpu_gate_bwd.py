@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from linear_attention_sequence_gate_amd import kda_gate_bwd
-from kda_testutil import TOL, prefill_device, rho, say
+from kda_testutil import GRAD_TOL, prefill_device, rho, say
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ def _check(z, A, dg, dtype):
     print("    " + " ".join(f"{k}={v:.1e}" for k, v in r.items()), flush=True)
     for k, v in r.items():
         assert np.isfinite(out[k].cpu().numpy()).all(), k
-        assert v <= TOL[dtype], (k, v)
+        assert v <= GRAD_TOL, (k, v)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

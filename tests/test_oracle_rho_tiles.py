@@ -156,3 +156,46 @@ def test_tile_sums_other_tile_length():
     want = [_series_tile_sum(0, 3, s[0, 0, 0]), _series_tile_sum(4, 7, s[0, 0, 0]),
             _series_tile_sum(8, 9, s[0, 0, 0])]
     np.testing.assert_allclose(got[0, :, 0, 0], want, rtol=1e-14)
+
+
+# ------------------------------------------------------- rho in pieces
+
+def test_rho_accumulator_equals_whole_tensor_rho():
+    rng = np.random.default_rng(9)
+    ref = rng.standard_normal((2, 50, 3, 4))
+    ref[1, 33, 2, 1] = 7.0                      # max|ref| in one piece ...
+    x = ref + 1e-5 * rng.standard_normal(ref.shape)
+    x[0, 2, 0, 0] += 0.05                       # ... the largest deviation in another
+    for cuts in ([0, 50], [0, 7, 8, 33, 34, 50], [0, 25, 50]):
+        acc = oracle.RhoAccumulator()
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            acc.add(x[:, a:b], ref[:, a:b])
+        assert acc.value() == oracle.rho(x, ref)
+    assert oracle.rho(x, ref) == pytest.approx(0.05 / 7.0, rel=1e-2)
+
+
+def test_rho_accumulator_nan_zero_and_shapes():
+    acc = oracle.RhoAccumulator()
+    acc.add(np.zeros(3), np.zeros(3))
+    acc.add(np.array([0.0, 0.5]), np.zeros(2))
+    assert acc.value() == 0.5                  # all-zero reference: absolute deviation
+    acc.add(np.array([np.nan]), np.ones(1))
+    assert not (acc.value() <= 1e-2)
+    with pytest.raises(ValueError, match="shapes differ"):
+        oracle.RhoAccumulator().add(np.ones((2, 3)), np.ones((1, 3)))
+
+
+def test_decode_step_inplace_equals_copy():
+    rng = np.random.default_rng(11)
+    N, H, dk, dv = 3, 2, 8, 5
+    args = [rng.standard_normal((N, H, dk)), rng.standard_normal((N, H, dk)),
+            rng.standard_normal((N, H, dv)), rng.standard_normal((N, H, dk)),
+            rng.standard_normal((H, dk)), rng.random((N, H))]
+    S = rng.standard_normal((N, H, dk, dv))
+    o1, S1 = oracle.decode_step(*args, S)
+    S2 = S.copy()
+    o2, S2r = oracle.decode_step(*args, S2, inplace=True)
+    assert S2r is S2
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+    assert not np.array_equal(S, S1)            # the copying form left its input alone
