@@ -21,7 +21,8 @@
  * -------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
  *    row-major in the layouts stated per call, with 16-byte aligned bases.
- *    The library never allocates or frees device memory.
+ *    The library never allocates or frees device memory.  Its one piece of
+ *    device state is the fixed scratch array of kda_chunk_fwd_gated_noalloc.
  *  - `dtype` selects the element type of q, k, v, z, beta and o:
  *    KDA_F32 (IEEE fp32) or KDA_BF16 (bfloat16).  A, g and the state are fp32.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -37,8 +38,9 @@
  *    kda_chunk_fwd B*H <= 2^24 and H*max(dk,dv)*256 < 2^32; kda_decode_step
  *    N*H < 2^31.
  *  - No scaling or normalisation is applied to q or k; that is the caller's.
- *  - Concurrent calls that share an output buffer race; the library keeps no
- *    global state of its own.
+ *  - Concurrent calls that share an output buffer race.  Apart from
+ *    kda_chunk_fwd_gated_noalloc's scratch array (calls of it that overlap on
+ *    one GPU race), the library keeps no global state of its own.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -221,6 +223,39 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void 
                         float *final_state, void *o, void *workspace, size_t workspace_bytes,
                         int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                         int dtype, unsigned flags, void *stream);
+
+/*
+ * kda_chunk_fwd_gated_noalloc -- kda_chunk_fwd_gated for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same arguments without the workspace;
+ * the call's scratch is a fixed device array inside the library,
+ * KDA_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU it runs on, held from the
+ * first call on that GPU until the process ends.
+ *  - What the scratch holds: the sequence split's per-segment states and
+ *    transitions (bf16, dk = 128, dv in {64, 128}), or the staged g
+ *    (B*T*H*dk*4 bytes) of shapes without the fused gate.
+ *  - Sizes: the automatic segment count is taken only when its buffers fit
+ *    (else one pass, as kda_chunk_fwd_gated does with a workspace too small
+ *    for the split).  An explicit KDA_FLAG_SEGMENTS(n), or a staged g, that
+ *    needs more than the array returns KDA_ERR_INVALID_ARGUMENT before any
+ *    launch; kda_last_error() gives the bytes needed.
+ *  - No call allocates or frees device memory, and no part of the array has
+ *    to start at zero: every word a call reads was written earlier in that
+ *    call.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents: calls that overlap in time on one GPU (other streams or
+ *    host threads without ordering between them) race and give wrong results.
+ *    Order them on one stream.
+ *  - The first call on a GPU looks up the array's address there (on the
+ *    device `stream` belongs to); KDA_ERR_HIP if that fails.
+ * With the same segment count the results equal kda_chunk_fwd_gated's bit
+ * for bit (the same kernels run).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kda_chunk_fwd_gated_noalloc(const void *q, const void *k, const void *v, const void *z,
+                                const float *A, const void *beta, const float *initial_state,
+                                float *final_state, void *o, int64_t B, int64_t T, int64_t H,
+                                int64_t dk, int64_t dv, int dtype, unsigned flags, void *stream);
 
 /*
  * kda_decode_step -- one token for each of N independent sequences x H heads,

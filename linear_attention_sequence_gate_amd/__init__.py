@@ -8,6 +8,7 @@ this package holds its ctypes binding (`_lib`), the in-tree build script
 """
 __all__ = ["kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
+           "kda_chunk_fwd_gated_noalloc",
            "kda_chunk_fwd_varlen_pooled_gated",
            "kda_chunk_fwd_auto_segments", "kda_decode_step", "kda_state_pool_reset",
            "kda_chunk_fwd_pooled", "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled",

@@ -39,7 +39,8 @@ EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
             "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
-            "kda_chunk_fwd_varlen_pooled_gated", "kda_last_error", "kda_version")
+            "kda_chunk_fwd_varlen_pooled_gated", "kda_chunk_fwd_gated_noalloc", "kda_last_error",
+            "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -77,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                       i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd_gated.restype = c_int
+    L.kda_chunk_fwd_gated_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
+    L.kda_chunk_fwd_gated_noalloc.restype = c_int
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, c_int, vp]
     L.kda_decode_step.restype = c_int
     L.kda_state_pool_reset.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp]
@@ -308,6 +312,29 @@ def kda_chunk_fwd_gated(q, k, v, z, A, beta, initial_state=None, final_state=Non
         _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(initial_state),
         _ptr(final_state), _ptr(o), _ptr(workspace), ws_bytes, B, T, H, dk, dv, dt, flags,
         _stream(stream)))
+    return o, final_state
+
+
+KDA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def kda_chunk_fwd_gated_noalloc(q, k, v, z, A, beta, initial_state=None, final_state=None,
+                                o=None, flags: int = 0,
+                                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_gated with the library's fixed device scratch instead of a
+    workspace (the C call allocates nothing; pass `o` and `final_state` to make
+    the whole call allocation-free here too).  Returns (o, final_state)."""
+    B, T, H, dk, dv = _check_prefill(q, k, v, beta, initial_state, final_state, o, None,
+                                     z=z, A=A)
+    if z is None or A is None:
+        raise ValueError("z and A are required")
+    _dev(q, k, v, z, A, beta, initial_state, final_state, o)
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), device=q.device, dtype=q.dtype)
+    _check(load_library().kda_chunk_fwd_gated_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(initial_state),
+        _ptr(final_state), _ptr(o), B, T, H, dk, dv, dt, flags, _stream(stream)))
     return o, final_state
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libkda.so")
 
 ARCH = "gfx950"
 SOURCES = ["kda_gate.hip", "kda_gate_bwd.hip", "kda_decode.hip", "kda_chunk.hip", "kda_backward.hip",
-           "kda_bwd_chunk.hip", "kda_api.cpp"]
+           "kda_bwd_chunk.hip", "kda_noalloc.hip", "kda_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

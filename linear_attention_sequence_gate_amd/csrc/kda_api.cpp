@@ -308,6 +308,24 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
 
 }  // namespace
 
+namespace kda {
+
+// The shared prefill implementation and the error report, for the entry
+// point of kda_noalloc.hip (its own source file holds its device array).
+int chunk_fwd_entry(const char *who, const void *q, const void *k, const void *v, const float *g,
+                    const void *beta, const float *initial_state, float *final_state, void *o,
+                    void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                    int64_t dk, int64_t dv, int dtype, unsigned flags, const void *z,
+                    const float *Ag, void *stream) {
+    return chunk_fwd_impl(who, q, k, v, g, beta, initial_state, final_state, o, workspace,
+                          workspace_bytes, B, T, H, dk, dv, dtype, flags, nullptr, 0, nullptr, z,
+                          Ag, stream);
+}
+
+int report_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
+}  // namespace kda
+
 extern "C" {
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const void *beta,

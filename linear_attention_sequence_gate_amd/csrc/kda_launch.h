@@ -82,4 +82,15 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
                                     int64_t H, int dk_, int dv_, int is_bf16, hipStream_t s);
 size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
 
+// The C ABI's shared chunked-prefill implementation (validation, the gate
+// staging of unfused shapes, the sequence split, the launches) with a caller's
+// workspace, and the error report behind kda_last_error(); defined in
+// kda_api.cpp.
+int chunk_fwd_entry(const char *who, const void *q, const void *k, const void *v, const float *g,
+                    const void *beta, const float *initial_state, float *final_state, void *o,
+                    void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                    int64_t dk, int64_t dv, int dtype, unsigned flags, const void *z,
+                    const float *Ag, void *stream);
+int report_error(int code, const char *msg);
+
 }  // namespace kda
