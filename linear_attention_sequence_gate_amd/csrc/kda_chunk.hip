@@ -1690,41 +1690,88 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 // transition M_p and zero-start state L_p of each middle segment,
 //     Sin[p] = M_p Sin[p-1] + L_p,   p = 1 .. nseg - 2,
 // is the state entering segment p + 1 (Sin[0], segment 0's final state from
-// the given initial state, is written by the first phase).  One workgroup per
-// (chain, 64-column block); the running block stays in LDS between steps.
+// the given initial state, is written by the first phase).
+//
+// One workgroup per (chain, 16-column block), four waves; wave w owns rows
+// 32 w .. 32 w + 31 of the block.  A step is a 128 x 128 by 128 x 16 product
+// on the fp32 matrix cores (v_mfma_f32_16x16x4f32, fp32 products and sums).
+// M_p sits in LDS row-major and the running block S transposed (one row per
+// column), both read as 16-byte fragments: read s of lane l covers
+// k = 16 s + 4 (l / 16) + j, j = 0..3, one instruction per j, the same k on
+// both operands.  The 132-float pitch keeps each 8-lane phase of those reads
+// on distinct banks.  The next step's M and L are loaded into registers while
+// the current step's products run.
 // ===========================================================================
 template <int DK>
 __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
                                                         const float *__restrict__ Lb,
                                                         const float *__restrict__ Mb, int nbh,
                                                         int DV, int nseg) {
-    __shared__ float sM[DK][DK + 1];
-    __shared__ float sS[DK][64];
-    const int ncb = DV / 64;
-    const int bh = blockIdx.x / ncb, col = (blockIdx.x % ncb) * 64;
-    const int tid = threadIdx.x, n = tid & 63;
-    const int r0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (DK / 4);   // this wave's 32 rows
+    constexpr int NC = 16;                          // columns per workgroup
+    constexpr int LDP = DK + 4;                     // LDS pitch (floats) of M rows and S^T rows
+    constexpr int NF = DK * DK / 4 / 256;           // 16-byte loads of M per thread
+    static_assert(DK == 128, "four waves of 32 rows");
+    __shared__ __attribute__((aligned(16))) float sM[DK * LDP];
+    __shared__ __attribute__((aligned(16))) float sST[NC * LDP];
+    const int ncb = DV / NC;
+    const int bh = blockIdx.x / ncb, c0 = (blockIdx.x % ncb) * NC;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
     const size_t vsz = (size_t)nbh * DK * DV, msz = (size_t)nbh * DK * DK;
-    for (int r = tid >> 6; r < DK; r += 4) sS[r][n] = Sin[((size_t)bh * DK + r) * DV + col + n];
+    const size_t sbase = (size_t)bh * DK * DV + c0;     // this block in a [nbh][DK][DV] state
+
+    for (int e = tid; e < DK * NC; e += 256) {
+        const int r = e / NC, c = e % NC;
+        sST[c * LDP + r] = Sin[sbase + (size_t)r * DV + c];
+    }
+    floatx4 mreg[NF];
+    float lreg[2][4];
+    auto load_step = [&](int p) {
+        const floatx4 *M4 =
+            reinterpret_cast<const floatx4 *>(Mb + (size_t)(p - 1) * msz + (size_t)bh * DK * DK);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) mreg[i] = M4[i * 256 + tid];
+        const float *L = Lb + (size_t)(p - 1) * vsz + sbase;
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                lreg[it][j] = L[(size_t)(32 * wave + 16 * it + 4 * lq + j) * DV + lr];
+    };
+    if (nseg >= 3) load_step(1);
     for (int p = 1; p <= nseg - 2; ++p) {
-        const float *M = Mb + (size_t)(p - 1) * msz + (size_t)bh * DK * DK;
-        const float *L = Lb + (size_t)(p - 1) * vsz + (size_t)bh * DK * DV + col;
-        float *out = Sin + (size_t)p * vsz + (size_t)bh * DK * DV + col;
-        for (int e = tid; e < DK * DK; e += 256) sM[e / DK][e % DK] = M[e];
-        __syncthreads();
-        float acc[DK / 4];
+        __syncthreads();                            // the previous step's reads are done
 #pragma unroll
-        for (int i = 0; i < DK / 4; ++i) acc[i] = L[(size_t)(r0 + i) * DV + n];
-        for (int kk = 0; kk < DK; ++kk) {
-            const float sv = sS[kk][n];
-#pragma unroll
-            for (int i = 0; i < DK / 4; ++i) acc[i] = fmaf(sM[r0 + i][kk], sv, acc[i]);
+        for (int i = 0; i < NF; ++i) {
+            const int f = i * 256 + tid, r = f / (DK / 4), c4 = f % (DK / 4);
+            *reinterpret_cast<floatx4 *>(&sM[r * LDP + 4 * c4]) = mreg[i];
         }
-        __syncthreads();                            // every read of sS and sM is done
+        floatx4 acc[2];
 #pragma unroll
-        for (int i = 0; i < DK / 4; ++i) {
-            sS[r0 + i][n] = acc[i];
-            out[(size_t)(r0 + i) * DV + n] = acc[i];
+        for (int it = 0; it < 2; ++it) acc[it] = floatx4{lreg[it][0], lreg[it][1], lreg[it][2], lreg[it][3]};
+        if (p + 1 <= nseg - 2) load_step(p + 1);
+        __syncthreads();                            // M_p is in LDS
+#pragma unroll 4
+        for (int s = 0; s < DK / 16; ++s) {
+            const floatx4 b = *reinterpret_cast<const floatx4 *>(&sST[lr * LDP + 16 * s + 4 * lq]);
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const floatx4 a = *reinterpret_cast<const floatx4 *>(
+                    &sM[(32 * wave + 16 * it + lr) * LDP + 16 * s + 4 * lq]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc[it], 0, 0, 0);
+            }
+        }
+        __syncthreads();                            // every read of S^T is done
+        float *out = Sin + (size_t)p * vsz + sbase;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int r = 32 * wave + 16 * it + 4 * lq;
+            *reinterpret_cast<floatx4 *>(&sST[lr * LDP + r]) = acc[it];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[(size_t)(r + j) * DV + lr] = acc[it][j];
         }
     }
 }
@@ -1764,26 +1811,32 @@ int seq_split_effective(int64_t T, int nseg) {
     return (int)((T + len - 1) / len);
 }
 
-// The count minimising a model of the wall time: every workgroup of a launch
-// runs its segment in about the same time, so a launch of W workgroups takes
-// ceil(W / CUs) rounds of one segment; a split adds the chaining steps.
+// The count minimising a model of the wall time, fitted to measured sweeps
+// of forced counts (B1 H8 T4096 and B1 H32 T1M: every point within 2%).
+// A launch of W workgroups runs ceil(W / CUs) rounds of one segment, and a
+// segment of n tokens costs n + 64 token-times (the pipeline's two fill
+// periods); a split adds 33 token-times per chaining step and 145 for its
+// extra launches.
 int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16) {
     constexpr int64_t kCUs = 256;             // MI355X compute units
-    constexpr int64_t kMinSegTokens = 4096;   // shorter segments do not repay the extra passes
-    constexpr int64_t kChainStepTokens = 160; // one chaining step costs about five 32-token periods
+    constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
+    constexpr int64_t kFillTokens = 64;       // two pipeline periods per segment
+    constexpr int64_t kChainStepTokens = 33;  // one chaining step
+    constexpr int64_t kSplitTokens = 145;     // the two extra launches
     if (!seq_split_supported(dk, dv, is_bf16)) return 1;
     const int64_t bh = B * H, nsl_v = dv / 64, nsl_m = dk / 64;
     auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
     // a split must beat one pass by 10%
-    double best = 0.9 * (double)T * (double)rounds(bh * nsl_v);
+    double best = 0.9 * (double)(T + kFillTokens) * (double)rounds(bh * nsl_v);
     int best_p = 1;
     int64_t pmax = T / kMinSegTokens;
     if (pmax > 255) pmax = 255;
     for (int P = 3; P <= pmax; ++P) {
         const int64_t pe = seq_split_effective(T, P), len = seq_split_segment_len(T, P);
+        if (pe < 3) continue;
         const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
-        const double cost = (double)len * (double)(rounds(w1) + rounds(w3)) +
-                            (double)kChainStepTokens * (double)(pe - 2);
+        const double cost = (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3)) +
+                            (double)kChainStepTokens * (double)(pe - 2) + (double)kSplitTokens;
         if (cost < best) {
             best = cost;
             best_p = P;
@@ -1847,7 +1900,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (P >= 3) {
-            hipLaunchKernelGGL(seg_chain_kernel<128>, dim3(args.nbh * (dv / 64)), dim3(256), 0, s,
+            hipLaunchKernelGGL(seg_chain_kernel<128>, dim3(args.nbh * (dv / 16)), dim3(256), 0, s,
                                args.Sin, args.Lb, args.Mb, args.nbh, dv, P);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
