@@ -78,6 +78,9 @@ def _matches(name, frags):
 # UT inverse of one 64-token chunk, per head-token (block substitution over
 # 16x16 blocks; the same constant as the flop model of the scope table).
 INV_FLOPS_PER_HT = 2218
+# the same count for 32-token chunks: the substitution's work per chunk grows
+# as the cube of the chunk length, per token as its square, so a quarter
+INV_FLOPS_PER_HT_C32 = 554
 
 
 def prefill_work(w, B=None, T=None, H=None):
@@ -87,22 +90,26 @@ def prefill_work(w, B=None, T=None, H=None):
     Bytes: q, k, v, beta and o once in the input dtype, g once in fp32, the
     final state (and the initial one when given) in fp32.  The fused call reads
     z in the input dtype instead of g, and the [H, dk] table A.
-    Flops per head-token (C = 64, dense 16-token diagonal subtiles, mean causal
-    length Lbar = (64 + 16) / 2 = 40): 6 dk dv for W S, Q~ S and K^T U; 2 Lbar
-    dk each for A, P and W; 2 Lbar dv each for U' and P U; the UT inverse."""
+    Flops per head-token of the benchmarked kernel (C = 32-token chunks of two
+    dense 16-token subtiles, mean causal length Lbar = (32 + 16) / 2 = 24):
+    6 dk dv for K~ S, Q~ S and K^T U; 2 Lbar dk each for A and P; 2 Lbar dv
+    each for T (V - K~ S) and P U (W = T K~ is never formed); the UT inverse.
+    The scope table's count for 64-token chunks (Lbar = 40, with W) is
+    reported beside it."""
     B, T, H = B or w.B, T or w.T, H or w.H
     dk, dv = w.dk, w.dv
     e = 2 if w.dtype == torch.bfloat16 else 4
     ht = B * T * H                                   # head-tokens
     chunk_bytes = ht * ((2 * dk + dv) * e + dk * 4 + e + dv * e)
     chunk_bytes += B * H * dk * dv * 4 * (2 if w.s0_std > 0 else 1)
-    Lbar = (64 + 16) / 2
-    flops_per_ht = 6 * dk * dv + 2 * Lbar * (3 * dk + 2 * dv) + INV_FLOPS_PER_HT
+    lbar32, lbar64 = (32 + 16) / 2, (64 + 16) / 2
+    flops_per_ht = 6 * dk * dv + 2 * lbar32 * (2 * dk + 2 * dv) + INV_FLOPS_PER_HT_C32
+    flops_c64 = 6 * dk * dv + 2 * lbar64 * (3 * dk + 2 * dv) + INV_FLOPS_PER_HT
     gate_bytes = ht * dk * (e + 4)
     fused_bytes = chunk_bytes - ht * dk * (4 - e) + H * dk * 4
     return dict(head_tokens=ht, chunk_bytes=chunk_bytes, chunk_flops=flops_per_ht * ht,
-                flops_per_head_token=flops_per_ht, gate_bytes=gate_bytes,
-                fused_bytes=fused_bytes)
+                flops_per_head_token=flops_per_ht, flops_per_head_token_c64=flops_c64,
+                gate_bytes=gate_bytes, fused_bytes=fused_bytes)
 
 
 def decode_bytes(w):
@@ -915,6 +922,7 @@ def main():
         "prefill": {"fused_ms": fused_s * 1e3,
                     "alg_tflops": fused_tflops,
                     "flops_per_head_token": work["flops_per_head_token"],
+                    "flops_per_head_token_c64_model": work["flops_per_head_token_c64"],
                     "arith_intensity": ai,
                     "mfma_frac_of_bf16_peak": fused_tflops / BF16_PEAK_TFLOPS,
                     "rocprof_mfma_busy_frac": recorded_mfma_busy(),
