@@ -122,8 +122,15 @@ def test_sequence_split_workspace_and_policy(L):
     P1 = auto(1, 1 << 20, 1, 128, 128, 1)
     assert P1 > 4 * P, (P1, P)
     assert ws(1, 1 << 20, 1, 128, 128, 1) == split_bytes(1, 1, 128, P1)
-    # short sequences and shapes without the pipelined kernel run in one pass
-    assert auto(1, 8192, 1, 128, 128, 1) == 1 and ws(1, 8192, 1, 128, 128, 1) == 256
+    # few chains of a short sequence split too (segments of >= 128 tokens):
+    # B1 H8 T4096 runs 16 workgroups in one pass
+    P8 = auto(1, 4096, 8, 128, 128, 1)
+    assert 3 <= P8 <= 32, P8
+    assert ws(1, 4096, 8, 128, 128, 1) == split_bytes(1, 8, 128, P8)
+    # enough chains to fill the GPU, or too short for three segments: one pass
+    assert auto(8, 4096, 8, 128, 128, 1) == 1
+    assert auto(1, 383, 1, 128, 128, 1) == 1 and ws(1, 383, 1, 128, 128, 1) == 256
+    # shapes without the pipelined kernel run in one pass
     assert auto(1, 1 << 20, 1, 64, 64, 1) == 1
     assert auto(1, 1 << 20, 1, 32, 32, 0) == 1
     assert auto(0, 64, 1, 128, 128, 1) == 0
