@@ -368,24 +368,27 @@ def bwd_chunk_flops(d):
 
 
 def time_backward(reps=5):
-    """kda_chunk_bwd on B4 H32 d128 bf16 with T = 4096 (the benchmark's chain
-    count; T cut so the workspace -- the state entering each even 16-token
-    chunk and the gradient leaving each odd one, 64 KiB per 16 tokens per
-    chain, and the token path's checkpoints -- stays at a few GiB), on the
-    chunked path; the token-level path and the gate's reverse mode timed
-    beside it."""
-    B, T, H, d = 4, 4096, 32, 128
+    """kda_chunk_bwd on B4 H32 T32768 d128 bf16 (the prefill workload's
+    chains and length; heads 16-31 decay-stress), chunked path: with the
+    whole-sequence workspace (one segment) and with a workspace for
+    4096-token segments (the forward state pass then runs twice); the
+    token-level path and the gate's reverse mode timed beside it."""
+    B, T, H, d = 4, 32768, 32, 128
+    seg = 4096
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(B, T, H, d, d, torch.bfloat16, 4242, device=dev, s0_std=0.02,
                                    stress_heads_mean=3.0)
     g = _lib.kda_gate(x["z"], x["A"])
     d_o = torch.randn(B, T, H, d, device=dev).to(torch.bfloat16)
-    ws = torch.empty(_lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, 1), device=dev, dtype=torch.uint8)
+    ws_whole = _lib.kda_chunk_bwd_workspace_size_flags(B, T, H, d, d, 1, 0, 0)
+    ws_seg = _lib.kda_chunk_bwd_workspace_size_flags(B, T, H, d, d, 1, 0, seg)
+    ws = torch.empty(ws_whole, device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
 
-    def timed(flags, n, warm):
+    def timed(flags, n, warm, nbytes):
+        wsv = ws[:nbytes]
         run = lambda: _lib.kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, None,
-                                         workspace=ws, flags=flags, stream=stream)
+                                         workspace=wsv, flags=flags, stream=stream)
         for _ in range(warm):      # past the first launches' clock ramp
             run()
         torch.cuda.synchronize()
@@ -397,8 +400,15 @@ def time_backward(reps=5):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    ms = timed(0, reps, 6)
-    ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1, 1)
+    ms = timed(0, reps, 3, ws_whole)
+    ms_seg = timed(0, reps, 2, ws_seg)
+    del ws
+    torch.cuda.empty_cache()
+    tok_bytes = _lib.kda_chunk_bwd_workspace_size_flags(B, T, H, d, d, 1, _lib.KDA_FLAG_TOKEN_BACKWARD, 0)
+    ws = torch.empty(tok_bytes, device=dev, dtype=torch.uint8)
+    ms_token = timed(_lib.KDA_FLAG_TOKEN_BACKWARD, 1, 1, tok_bytes)
+    del ws
+    torch.cuda.empty_cache()
     # the gate's reverse mode on the same rows (dz, dA from a dg of that shape)
     dg = torch.randn(B, T, H, d, device=dev)
     gws = torch.empty(max(_lib.kda_gate_bwd_workspace_size(B, T, H, d), 256), device=dev,
@@ -417,10 +427,13 @@ def time_backward(reps=5):
     del dg, gws
     ht = B * T * H
     tflops = bwd_chunk_flops(d) * ht / (ms / 1e3) / 1e12
-    del x, g, d_o, ws
+    del x, g, d_o
     torch.cuda.empty_cache()
     return {"ms": ms, "workload": f"B{B} H{H} T{T} d{d} bf16, heads 16-31 decay-stress (gradients fp32)",
-            "head_tokens_per_s": ht / (ms / 1e3), "token_path_ms": ms_token,
+            "head_tokens_per_s": ht / (ms / 1e3), "workspace_bytes": ws_whole,
+            "segmented": {"segment_tokens": seg, "ms": ms_seg, "workspace_bytes": ws_seg,
+                          "over_one_segment": ms_seg / ms},
+            "token_path_ms": ms_token,
             "gate_bwd_ms": gate_ms, "gate_bwd_gbs": gate_bytes / (gate_ms / 1e3) / 1e9,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS,
@@ -601,14 +614,17 @@ EXTRA_TRACES = {
              "A split call is three launches: chunk32_kernel phase 1 (segment 0, the middle "
              "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
              "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
-    "backward": ("backward", "kernel_trace_backward_b4h32t4096.md",
-                 "kda_gate once, then kda_chunk_bwd on B4 H32 T4096 d128 bf16 (heads 16-31 decay-stress): the chunked path "
-                 "(6 warm-up + 5 timed calls; per call cb_prep_kernel (X, P, At per 16-token "
-                 "chunk), cb_fwd_kernel (state entering each even chunk), cb_bwd_kernel (gradient "
-                 "leaving each odd chunk) and cb_grad_kernel (token gradients, one workgroup per "
-                 "chunk pair)), "
-                 "then the token-level path (1 warm-up + 1 timed call; bwd_ckpt_kernel, "
-                 "bwd_kernel, bwd_sum_kernel)."),
+    "backward": ("backward", "kernel_trace_backward_b4h32t32k.md",
+                 "kda_gate once, then kda_chunk_bwd on B4 H32 T32768 d128 bf16 (heads 16-31 "
+                 "decay-stress): the chunked path with the whole-sequence workspace (3 warm-up + 5 "
+                 "timed calls; per call cb_prep_kernel (X, P, At per 16-token chunk), cb_fwd_kernel "
+                 "(state entering each even chunk), cb_bwd_kernel (gradient leaving each odd chunk) "
+                 "and cb_grad_kernel (token gradients, one workgroup per chunk pair)); the same "
+                 "with a workspace for 4096-token segments (2 + 5 calls; per call a forward sweep of "
+                 "cb_prep_kernel and cb_fwd_kernel over segments 0..6, then the four kernels per "
+                 "segment in reverse; rows labelled by the call their prep launch belongs to); "
+                 "then the token-level path (1 warm-up + 1 timed call; "
+                 "bwd_ckpt_kernel, bwd_kernel, bwd_sum_kernel) and kda_gate_bwd."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (5 warm-up + 5 timed calls) and with the position-pair "
@@ -698,12 +714,22 @@ def ingest_trace_extra(name, d):
                                                            "cb_grad_kernel"))]
     chunk_rows = [r for r in rows if "chunk32_kernel" in r["Kernel_Name"]]
     groups = {}
+    prep_wgs = None
     for r in rows:
         kname = r["Kernel_Name"].split("(")[0].replace("void ", "")[:40]
         wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
         label = ""
         if name == "pairwise" and r in chunk_rows:
             label = "dense" if chunk_rows.index(r) < len(chunk_rows) // 2 else "position pairs"
+        if name == "backward" and "cb_" in kname:
+            # the chunked path's launches belong to the call (whole sequence or
+            # one segment) whose prep launch, with one workgroup per chunk,
+            # precedes them
+            if "cb_prep" in kname:
+                prep_wgs = wgs
+            label = "whole sequence" if prep_wgs == max(
+                int(x["Grid_Size_X"]) // max(1, int(x["Workgroup_Size_X"]))
+                for x in rows if "cb_prep" in x["Kernel_Name"]) else "segment"
         us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         groups.setdefault((kname, label, wgs), []).append(us)
     only, fname, what = EXTRA_TRACES[name]

@@ -296,12 +296,40 @@ int kda_decode_step(const void *q, const void *k, const void *v, const void *z,
  *   dv              : [B, T, H, dv] fp32 (output)
  *   dbeta           : [B, T, H]     fp32 (output)
  *   d_initial_state : [B, H, dk, dv] fp32, or NULL if not wanted
- *   workspace       : kda_chunk_bwd_workspace_size() bytes (either path)
+ *   workspace       : see the sizes below
  *   flags           : KDA_FLAG_CHECK_RANGE (chunked path only), KDA_FLAG_TOKEN_BACKWARD
  * Outputs must not alias inputs.  KDA_ERR_RANGE as for kda_chunk_fwd.
+ *
+ * Workspace.  Both paths keep per-token buffers, so a whole-sequence
+ * workspace grows linearly with T: about 6.8 KiB per token and chain for the
+ * chunked path at dk = dv = 128 (the states entering even 16-token chunks and
+ * the gradients leaving odd ones, X/P/At, W, dU and the decayed operands), and
+ * 8 KiB plus per-slice partial gradients for the token path (a state every 8
+ * tokens).  The chunked path therefore also runs in segments: given less than
+ * the whole-sequence size, it takes the longest segment (a multiple of 32
+ * tokens) whose buffers fit, sweeps the forward state pass over the segments
+ * to get the state entering each, then runs the segments in reverse, carrying
+ * the state gradient back (the forward state pass runs twice).  Its
+ * workspace is then bounded by one segment plus (segments + 1) B H dk dv fp32
+ * states, e.g. B1 H32 T1M d128 in 32768-token segments takes about 7.2 GB
+ * instead of about 230 GB.  The token path needs its whole-sequence size.
+ *   kda_chunk_bwd_workspace_size        : the whole-sequence size of the
+ *                                         larger path (fits every call)
+ *   kda_chunk_bwd_workspace_size_flags  : the size for the path `flags`
+ *                                         selects; segment_tokens = 0 for the
+ *                                         whole sequence in one segment, n > 0
+ *                                         for segments of n tokens (rounded up
+ *                                         to 32; chunked path only), or
+ *                                         KDA_BWD_SEGMENTS_MIN_WORKSPACE for the
+ *                                         smallest over all segment lengths:
+ *                                         the least kda_chunk_bwd accepts
+ *                                         (INVALID_ARGUMENT below it).
  */
+#define KDA_BWD_SEGMENTS_MIN_WORKSPACE ((int64_t)-1)
 size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H,
                                     int64_t dk, int64_t dv, int dtype);
+size_t kda_chunk_bwd_workspace_size_flags(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                          int dtype, unsigned flags, int64_t segment_tokens);
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g,
                   const void *beta, const float *initial_state, const void *d_o,
                   const float *d_final_state, float *dq, float *dk, float *dv, float *dg,

@@ -12,7 +12,8 @@ __all__ = ["kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_varlen_pooled_gated",
            "kda_chunk_fwd_auto_segments", "kda_decode_step", "kda_state_pool_reset",
            "kda_chunk_fwd_pooled", "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled",
-           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_gate_bwd",
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_workspace_size_flags",
+           "kda_gate_bwd",
            "kda_gate_bwd_workspace_size", "kda_last_error", "kda_version",
            "KdaError"]
 

@@ -39,8 +39,8 @@ EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
             "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
-            "kda_chunk_fwd_varlen_pooled_gated", "kda_chunk_fwd_gated_noalloc", "kda_last_error",
-            "kda_version")
+            "kda_chunk_fwd_varlen_pooled_gated", "kda_chunk_fwd_gated_noalloc",
+            "kda_chunk_bwd_workspace_size_flags", "kda_last_error", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -98,6 +98,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_varlen_pooled_gated.restype = c_int
     L.kda_chunk_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_chunk_bwd_workspace_size_flags.argtypes = [i64, i64, i64, i64, i64, c_int, ctypes.c_uint,
+                                                     i64]
+    L.kda_chunk_bwd_workspace_size_flags.restype = ctypes.c_size_t
     L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64, c_int,
                                             ctypes.c_uint, vp]
     L.kda_chunk_bwd.restype = c_int
@@ -512,13 +515,28 @@ def kda_chunk_bwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype
     return int(load_library().kda_chunk_bwd_workspace_size(B, T, H, dk, dv, dtype))
 
 
+KDA_BWD_SEGMENTS_MIN_WORKSPACE = -1
+
+
+def kda_chunk_bwd_workspace_size_flags(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
+                                       flags: int = 0, segment_tokens: int = 0) -> int:
+    """Workspace bytes of the backward path `flags` selects: segment_tokens 0 =
+    the whole sequence in one segment, n > 0 = segments of n tokens (chunked
+    path), KDA_BWD_SEGMENTS_MIN_WORKSPACE = the least kda_chunk_bwd accepts."""
+    return int(load_library().kda_chunk_bwd_workspace_size_flags(B, T, H, dk, dv, dtype, flags,
+                                                                 segment_tokens))
+
+
 def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
                   want_d_initial_state: bool = True, workspace=None, flags: int = 0,
-                  stream=None) -> dict:
+                  segment_tokens: Optional[int] = None, stream=None) -> dict:
     """Gradients of <o, d_o> + <S_T, d_final_state> through kda_chunk_fwd's
     recurrence.  Returns dict dq, dk, dg [B,T,H,dk], dv [B,T,H,dv], dbeta
     [B,T,H] and d_initial_state [B,H,dk,dv] (fp32; the last None if not wanted).
-    flags: KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD (token-level path)."""
+    flags: KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD (token-level path).
+    Without a workspace one is allocated: for segments of `segment_tokens`
+    tokens when given (chunked path; the call then runs the sequence in
+    segments), else for the whole sequence."""
     B, T, H, dk, dv = _check_prefill(q, k, v, beta, initial_state, None, None, workspace, g=g,
                                      d_o=d_o, d_final_state=d_final_state)
     if g is None or d_o is None:
@@ -531,8 +549,10 @@ def kda_chunk_bwd(q, k, v, g, beta, initial_state, d_o, d_final_state=None,
                dbeta=torch.empty(B, T, H, **f32),
                d_initial_state=torch.empty(B, H, dk, dv, **f32) if want_d_initial_state else None)
     if workspace is None:
-        workspace = torch.empty(max(kda_chunk_bwd_workspace_size(B, T, H, dk, dv, dt), 256),
-                                device=q.device, dtype=torch.uint8)
+        ws_bytes = (kda_chunk_bwd_workspace_size(B, T, H, dk, dv, dt) if segment_tokens is None
+                    else kda_chunk_bwd_workspace_size_flags(B, T, H, dk, dv, dt, flags,
+                                                            segment_tokens))
+        workspace = torch.empty(max(ws_bytes, 256), device=q.device, dtype=torch.uint8)
     _check(load_library().kda_chunk_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
         _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),

@@ -470,6 +470,21 @@ size_t kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
     return kCounterBytes + (tok > chk ? tok : chk);
 }
 
+size_t kda_chunk_bwd_workspace_size_flags(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                          int dtype, unsigned flags, int64_t segment_tokens) {
+    if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (segment_tokens < 0 && segment_tokens != KDA_BWD_SEGMENTS_MIN_WORKSPACE) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk) || !mul_ok(n, dv)) return 0;
+    if (flags & KDA_FLAG_TOKEN_BACKWARD)
+        return kCounterBytes + kda::bwd_workspace_bytes(B, T, H, (int)dk, (int)dv);
+    if (segment_tokens == KDA_BWD_SEGMENTS_MIN_WORKSPACE)
+        return kCounterBytes + kda::cbwd_min_workspace_bytes(B, T, H, (int)dk, (int)dv);
+    const int64_t seg = segment_tokens == 0 ? T : (segment_tokens + 31) / 32 * 32;
+    return kCounterBytes + kda::cbwd_workspace_bytes_seg(B, T, H, (int)dk, (int)dv, seg);
+}
+
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const void *beta,
                   const float *initial_state, const void *d_o, const float *d_final_state,
                   float *dq, float *dk, float *dv, float *dg, float *dbeta,
@@ -495,9 +510,12 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
     if (!mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, dk_dim) || !mul_ok(n, dv_dim))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: element count overflows", who);
     if (B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: B*H too large", who);
-    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, dk_dim, dv_dim, dtype);
+    // the token path needs its whole-sequence buffers; the chunked path runs
+    // in the longest segments the workspace holds (at least 32 tokens)
+    const size_t need = kda_chunk_bwd_workspace_size_flags(B, T, H, dk_dim, dv_dim, dtype, flags,
+                                                           token ? 0 : KDA_BWD_SEGMENTS_MIN_WORKSPACE);
     if (workspace_bytes < need)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of %zu bytes", who, need);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: needs a workspace of at least %zu bytes", who, need);
     const void *ptrs[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg,
                           dbeta, d_initial_state, workspace};
     for (const void *p : ptrs)
@@ -530,7 +548,8 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
                                       dg, dbeta, d_initial_state, ws, B, T, H, (int)dk_dim,
                                       (int)dv_dim, dtype == KDA_BF16, s)
               : kda::launch_chunk_bwd_chunked(q, k, v, g, beta, initial_state, d_o, d_final_state, dq,
-                                              dk, dv, dg, dbeta, d_initial_state, ws, B, T, H,
+                                              dk, dv, dg, dbeta, d_initial_state, ws,
+                                              workspace_bytes - kCounterBytes, B, T, H,
                                               (int)dk_dim, (int)dv_dim, dtype == KDA_BF16, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_bwd launch");
     return ok();

@@ -46,6 +46,9 @@
 // l holds rows 4(l/16)+i, column l%16 of each 16x16 tile), which is also a
 // valid B operand of the next product once the contraction index is taken in
 // the same order on both operands.
+#include <math.h>
+#include <stdint.h>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -72,7 +75,10 @@ struct CbArgs {
     float *ops;                                  // [nbh][nc][cb_ops_floats(DK)]  decayed operands
     float *w;                                    // [nbh][nc][16][DV]
     float *du;                                   // [nbh][nc][16][DV]
-    int64_t T;
+    float *sfinal;                               // cb_fwd_kernel: the state after the last
+                                                 // chunk, [nbh][DK][DV] (null: not written)
+    int64_t T;                                   // tokens of this launch (a segment)
+    int64_t tseq, toff;                          // tokens per sequence in memory; first token
     int H, DV, nc, nsl, np;                      // np = chunk pairs = ceil(nc / 2)
 };
 
@@ -91,10 +97,10 @@ __device__ __forceinline__ floatx4 mfma1(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Row of token 0 of chain bh in the [B, T, H] token layout; token t of the
-// chain is row cb_rowbase + t * H.
+// Row of the launch's token 0 (token toff of the sequence) of chain bh in the
+// [B, tseq, H] token layout; token t of the launch is row cb_rowbase + t * H.
 __device__ __forceinline__ int64_t cb_rowbase(const CbArgs &a, int64_t bh) {
-    return (bh / a.H) * a.T * a.H + bh % a.H;
+    return (bh / a.H) * a.tseq * a.H + bh % a.H + a.toff * a.H;
 }
 
 // The 16 values of one channel over the chunk's tokens: element `off` of
@@ -435,6 +441,26 @@ __device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, C
     }
 }
 
+// Store this wave's tiles of the slice into a [B*H, DK, DV] state (the
+// layout cb_load_state reads).
+template <int DK>
+__device__ __forceinline__ void cb_store_state(float *dst, int64_t bh, int DV, int col0, int wave,
+                                               const CbAcc<DK> &s) {
+    constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tt = wave * TPW + u;
+        if (tt < RT) {
+#pragma unroll
+            for (int v = 0; v < kCbCT; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[(bh * DK + 16 * tt + 4 * g4 + i) * DV + col0 + 16 * v + j] = s[u][v][i];
+        }
+    }
+}
+
 // Load (or zero) this wave's tiles of a [B*H, DK, DV] state for the slice.
 template <int DK>
 __device__ __forceinline__ void cb_load_state(const float *src, int64_t bh, int DV, int col0,
@@ -473,6 +499,7 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
         for (int q = 0; q < kCbAhead; ++q)
             if (c0 + q < a.nc) cb_fwd_step<T, DK>(a, L, stg[q], c0 + q, bh, rb, col0, wave, s);
     }
+    if (a.sfinal) cb_store_state<DK>(a.sfinal, bh, a.DV, col0, wave, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -969,7 +996,9 @@ __global__ __launch_bounds__(cb_grad_waves<DK>() * 64) void cb_grad_kernel(CbArg
     cb_grad_chunk<T, DK, DV, kCbNFromNext>(a, L, bh, c0, wave, stp, dnp, nb);
 }
 
-size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+// Workspace of one launch over T tokens: the snapshots of even chunks' states
+// and of odd chunks' gradients, X/P/At, W and dU per chunk, decayed operands.
+static size_t cbwd_segment_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
     const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB, np = (nc + 1) / 2;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t st = r256((size_t)nbh * np * dk * dv * sizeof(float));
@@ -977,6 +1006,63 @@ size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
     const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
     const size_t ops = r256((size_t)nbh * nc * cb_ops_floats(dk) * sizeof(float));
     return 2 * st + mat + 2 * wv + ops;
+}
+
+size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+    return cbwd_segment_bytes(B, T, H, dk, dv);
+}
+
+// Segments of seg tokens (a multiple of 32, so every segment starts a chunk
+// pair): one launch's workspace for a segment, plus the states entering
+// segments 1 .. n-1 and two gradient carries, each [B*H, dk, dv] fp32.
+size_t cbwd_workspace_bytes_seg(int64_t B, int64_t T, int64_t H, int dk, int dv, int64_t seg) {
+    if (seg <= 0 || seg >= T) return cbwd_segment_bytes(B, T, H, dk, dv);
+    const int64_t nseg = (T + seg - 1) / seg;
+    const size_t state = (size_t)B * H * dk * dv * sizeof(float);
+    return cbwd_segment_bytes(B, seg, H, dk, dv) + (size_t)(nseg - 1 + 2) * state;
+}
+
+// As a function of the segment length the workspace is convex: the segment's
+// buffers grow with it and the entering states shrink with it.  The smallest
+// lies near sqrt(state bytes x T / segment bytes per token); lengths are
+// multiples of 32 tokens.
+static int64_t cbwd_min_units(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+    const int64_t umax = (T - 1) / 32;
+    if (umax < 1) return 1;
+    const double per_tok = (double)cbwd_segment_bytes(B, 32 * umax, H, dk, dv) / (32.0 * umax);
+    const double state = (double)B * H * dk * dv * sizeof(float);
+    int64_t u0 = (int64_t)(sqrt(state * (double)T / per_tok) / 32.0);
+    int64_t best = 1;
+    size_t best_b = SIZE_MAX;
+    for (int64_t u = u0 - 4; u <= u0 + 4; ++u) {
+        if (u < 1 || u > umax) continue;
+        const size_t b = cbwd_workspace_bytes_seg(B, T, H, dk, dv, 32 * u);
+        if (b < best_b) { best_b = b; best = u; }
+    }
+    return best;
+}
+
+size_t cbwd_min_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv) {
+    const size_t whole = cbwd_segment_bytes(B, T, H, dk, dv);
+    if (T <= 32) return whole;
+    const size_t seg = cbwd_workspace_bytes_seg(B, T, H, dk, dv, 32 * cbwd_min_units(B, T, H, dk, dv));
+    return seg < whole ? seg : whole;
+}
+
+// The longest segment (a multiple of 32 tokens, or the whole sequence) whose
+// workspace fits in `bytes`; 0 when none does.  Above the smallest point the
+// workspace grows with the length, so a binary search there finds it.
+int64_t cbwd_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, size_t bytes) {
+    if (cbwd_segment_bytes(B, T, H, dk, dv) <= bytes) return T;
+    if (T <= 32) return 0;
+    int64_t lo = cbwd_min_units(B, T, H, dk, dv), hi = (T - 1) / 32;
+    if (cbwd_workspace_bytes_seg(B, T, H, dk, dv, 32 * lo) > bytes) return 0;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (cbwd_workspace_bytes_seg(B, T, H, dk, dv, 32 * mid) <= bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return 32 * lo;
 }
 
 template <typename T, int DK>
@@ -998,21 +1084,9 @@ static hipError_t cb_inst(CbArgs a, int64_t nbh, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
-                                    const void *beta, const float *S0, const void *dout,
-                                    const float *dST, float *dq, float *dk_, float *dv_, float *dg,
-                                    float *dbeta, float *dS0, float *ws, int64_t B, int64_t T,
-                                    int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
-    if (dv % kCbNS || dk % 16) return hipErrorInvalidValue;
-    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
-    if (nbh * nc > 0x7fffffffLL) return hipErrorInvalidValue;
+static void cb_layout(CbArgs &a, char *p, int64_t nbh, int64_t T, int dk, int dv) {
+    const int64_t nc = (T + kCB - 1) / kCB, np = (nc + 1) / 2;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    char *p = reinterpret_cast<char *>(ws);
-    CbArgs a;
-    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout;
-    a.g = g; a.S0 = S0; a.dST = dST;
-    a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
-    const int64_t np = (nc + 1) / 2;
     const size_t st = r256((size_t)nbh * np * dk * dv * sizeof(float));
     const size_t mat = r256((size_t)nbh * nc * kCbMat * sizeof(float));
     const size_t wv = r256((size_t)nbh * nc * kCB * dv * sizeof(float));
@@ -1022,13 +1096,92 @@ hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v,
     a.w = reinterpret_cast<float *>(p + 2 * st + mat);
     a.du = reinterpret_cast<float *>(p + 2 * st + mat + wv);
     a.ops = reinterpret_cast<float *>(p + 2 * st + mat + 2 * wv);
-    a.T = T; a.H = (int)H; a.DV = dv; a.nc = (int)nc; a.nsl = dv / kCbNS; a.np = (int)np;
+    a.T = T; a.nc = (int)nc; a.np = (int)np;
+}
+
+template <typename T, int DK>
+static hipError_t cb_fwd_only(CbArgs a, int64_t nbh, hipStream_t s) {
+    hipLaunchKernelGGL((cb_prep_kernel<T, DK>), dim3((unsigned)(nbh * a.nc)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((cb_fwd_kernel<T, DK>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s, a, nbh);
+    return hipGetLastError();
+}
+
+static hipError_t cb_dispatch(const CbArgs &a, int64_t nbh, int dk, int is_bf16, bool fwd_only,
+                              hipStream_t s) {
     switch (dk) {
-    case 32: return is_bf16 ? cb_inst<bf16, 32>(a, nbh, s) : cb_inst<float, 32>(a, nbh, s);
-    case 64: return is_bf16 ? cb_inst<bf16, 64>(a, nbh, s) : cb_inst<float, 64>(a, nbh, s);
-    case 128: return is_bf16 ? cb_inst<bf16, 128>(a, nbh, s) : cb_inst<float, 128>(a, nbh, s);
+    case 32:
+        if (fwd_only) return is_bf16 ? cb_fwd_only<bf16, 32>(a, nbh, s) : cb_fwd_only<float, 32>(a, nbh, s);
+        return is_bf16 ? cb_inst<bf16, 32>(a, nbh, s) : cb_inst<float, 32>(a, nbh, s);
+    case 64:
+        if (fwd_only) return is_bf16 ? cb_fwd_only<bf16, 64>(a, nbh, s) : cb_fwd_only<float, 64>(a, nbh, s);
+        return is_bf16 ? cb_inst<bf16, 64>(a, nbh, s) : cb_inst<float, 64>(a, nbh, s);
+    case 128:
+        if (fwd_only) return is_bf16 ? cb_fwd_only<bf16, 128>(a, nbh, s) : cb_fwd_only<float, 128>(a, nbh, s);
+        return is_bf16 ? cb_inst<bf16, 128>(a, nbh, s) : cb_inst<float, 128>(a, nbh, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// With a workspace for the whole sequence, one launch of each kernel.  With a
+// smaller one, the sequence runs in segments of `seg` tokens (the longest
+// that fit; every segment starts a 16-token chunk pair, so the chunks and the
+// decay references are those of one pass): a forward sweep over segments
+// 0 .. n-2 (prep and forward state pass) leaves the state entering every
+// later segment, then the segments run in reverse, each a full backward from
+// its entering state, with the gradient of its final state carried from the
+// segment after it.  The forward pass is thus done twice; the workspace is
+// bounded by a segment instead of the sequence.
+hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                                    const void *beta, const float *S0, const void *dout,
+                                    const float *dST, float *dq, float *dk_, float *dv_, float *dg,
+                                    float *dbeta, float *dS0, float *ws, size_t ws_bytes, int64_t B,
+                                    int64_t T, int64_t H, int dk, int dv, int is_bf16, hipStream_t s) {
+    if (dv % kCbNS || dk % 16) return hipErrorInvalidValue;
+    const int64_t nbh = B * H;
+    const int64_t seg = cbwd_segment_tokens(B, T, H, dk, dv, ws_bytes);
+    if (seg <= 0) return hipErrorInvalidValue;
+    if (nbh * ((seg + kCB - 1) / kCB) > 0x7fffffffLL) return hipErrorInvalidValue;
+    CbArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.dout = dout;
+    a.g = g;
+    a.dq = dq; a.dk = dk_; a.dv = dv_; a.dg = dg; a.dbeta = dbeta;
+    a.H = (int)H; a.DV = dv; a.nsl = dv / kCbNS;
+    a.tseq = T;
+    a.sfinal = nullptr;
+    char *p = reinterpret_cast<char *>(ws);
+    if (seg >= T) {
+        cb_layout(a, p, nbh, T, dk, dv);
+        a.toff = 0; a.S0 = S0; a.dST = dST; a.dS0 = dS0;
+        return cb_dispatch(a, nbh, dk, is_bf16, false, s);
+    }
+    const int64_t nseg = (T + seg - 1) / seg;
+    const size_t state = (size_t)nbh * dk * dv;      // floats
+    float *bound = reinterpret_cast<float *>(p);     // state entering segment i at bound[(i-1) state]
+    float *carry = bound + (size_t)(nseg - 1) * state;
+    char *segws = reinterpret_cast<char *>(carry + 2 * state);
+    // forward sweep: the state entering segments 1 .. n-1
+    for (int64_t i = 0; i + 1 < nseg; ++i) {
+        cb_layout(a, segws, nbh, seg, dk, dv);
+        a.toff = i * seg;
+        a.S0 = i == 0 ? S0 : bound + (size_t)(i - 1) * state;
+        a.sfinal = bound + (size_t)i * state;
+        a.dST = nullptr; a.dS0 = nullptr;
+        if (hipError_t e = cb_dispatch(a, nbh, dk, is_bf16, true, s)) return e;
+    }
+    a.sfinal = nullptr;
+    // reverse sweep: each segment's gradients, the state gradient carried back
+    for (int64_t i = nseg - 1; i >= 0; --i) {
+        const int64_t len = i == nseg - 1 ? T - i * seg : seg;
+        cb_layout(a, segws, nbh, len, dk, dv);
+        a.toff = i * seg;
+        a.S0 = i == 0 ? S0 : bound + (size_t)(i - 1) * state;
+        a.dST = i == nseg - 1 ? dST : carry + (size_t)((i + 1) & 1) * state;
+        a.dS0 = i == 0 ? dS0 : carry + (size_t)(i & 1) * state;
+        if (hipError_t e = cb_dispatch(a, nbh, dk, is_bf16, false, s)) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -74,13 +74,21 @@ size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
 
 // Reverse mode in 16-token chunks on the fp32 matrix cores (the gate floor's
 // decay range assumed: every 16-token sum of g from the sequence start is
-// >= -80).  `ws` is cbwd_workspace_bytes() long.
+// >= -80).  `ws` holds ws_bytes: cbwd_workspace_bytes() runs the sequence in
+// one segment; less runs it in the longest segments that fit
+// (cbwd_segment_tokens; hipErrorInvalidValue below 32 tokens).
 hipError_t launch_chunk_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
                                     const void *beta, const float *S0, const void *dout,
                                     const float *dST, float *dq, float *dk, float *dv, float *dg,
-                                    float *dbeta, float *dS0, float *ws, int64_t B, int64_t T,
-                                    int64_t H, int dk_, int dv_, int is_bf16, hipStream_t s);
+                                    float *dbeta, float *dS0, float *ws, size_t ws_bytes, int64_t B,
+                                    int64_t T, int64_t H, int dk_, int dv_, int is_bf16,
+                                    hipStream_t s);
 size_t cbwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
+// Segments of `seg` tokens (a multiple of 32; >= T: one segment).
+size_t cbwd_workspace_bytes_seg(int64_t B, int64_t T, int64_t H, int dk, int dv, int64_t seg);
+int64_t cbwd_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, size_t bytes);
+// The smallest workspace over every segment length (the whole sequence included).
+size_t cbwd_min_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv);
 
 // The C ABI's shared chunked-prefill implementation (validation, the gate
 // staging of unfused shapes, the sequence split, the launches) with a caller's

@@ -40,8 +40,8 @@ def test_header_declares_the_boundary():
               "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
               "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
               "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
-              "kda_chunk_fwd_varlen_pooled_gated",
-              "kda_last_error", "kda_version"):
+              "kda_chunk_fwd_varlen_pooled_gated", "kda_chunk_fwd_gated_noalloc",
+              "kda_chunk_bwd_workspace_size_flags", "kda_last_error", "kda_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -249,6 +249,48 @@ def test_backward_validation(L):
     assert bwd(T=0) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(dq=Q[0]) == E.KDA_ERR_INVALID_ARGUMENT         # output aliases q
     assert bwd(S0=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
+
+
+def test_backward_segmented_workspace(L):
+    """The chunked reverse mode runs in segments when the workspace holds less
+    than the whole sequence: one segment's buffers plus the states entering
+    segments 1 .. n-1 and two gradient carries, [B*H, dk, dv] fp32 each."""
+    E = _lib
+    r = lambda x: (x + 255) // 256 * 256
+
+    def seg_bytes(nbh, T, dk, dv):
+        nc = (T + 15) // 16
+        npair = (nc + 1) // 2
+        return (2 * r(nbh * npair * dk * dv * 4) + r(nbh * nc * 768 * 4) + 2 * r(nbh * nc * 16 * dv * 4)
+                + r(nbh * nc * 49 * dk * 4))
+
+    q = L.kda_chunk_bwd_workspace_size_flags
+    B, T, H, dk, dv = 2, 1000, 3, 64, 32
+    nbh, state = B * H, B * H * dk * dv * 4
+    whole = q(B, T, H, dk, dv, 1, 0, 0)
+    assert whole == 256 + seg_bytes(nbh, T, dk, dv)
+    for seg, nseg in ((64, 16), (100, 8), (500, 2), (992, 2)):       # rounded up to 32 tokens
+        s32 = (seg + 31) // 32 * 32
+        assert q(B, T, H, dk, dv, 1, 0, seg) == 256 + seg_bytes(nbh, s32, dk, dv) + (nseg - 1 + 2) * state
+    assert q(B, T, H, dk, dv, 1, 0, 1000) == whole                   # one segment
+    mn = q(B, T, H, dk, dv, 1, 0, E.KDA_BWD_SEGMENTS_MIN_WORKSPACE)
+    assert mn < whole
+    assert all(mn <= q(B, T, H, dk, dv, 1, 0, 32 * u) for u in range(1, 32))
+    # the token path ignores the segment length and takes its whole-sequence size
+    tok = q(B, T, H, dk, dv, 1, E.KDA_FLAG_TOKEN_BACKWARD, 0)
+    assert tok == q(B, T, H, dk, dv, 1, E.KDA_FLAG_TOKEN_BACKWARD, 64)
+    assert L.kda_chunk_bwd_workspace_size(B, T, H, dk, dv, 1) == max(tok, whole)
+    assert q(B, T, H, dk, dv, 1, 0, -2) == 0
+    # B1 H32 T1M d128: about 230 GB in one segment, under 8 GB in 32768-token ones
+    assert q(1, 1 << 20, 32, 128, 128, 1, 0, 0) > 200e9
+    assert q(1, 1 << 20, 32, 128, 128, 1, 0, 32768) < 8e9
+    assert q(1, 1 << 20, 32, 128, 128, 1, 0, E.KDA_BWD_SEGMENTS_MIN_WORKSPACE) < 2e9
+    # kda_chunk_bwd rejects less than the least any segment length needs
+    Q = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
+    rc = L.kda_chunk_bwd(Q[0], Q[1], Q[2], Q[3], Q[4], None, Q[6], None, Q[8], Q[9], Q[10], Q[11],
+                         Q[12], None, Q[14], mn - 1, B, T, H, dk, dv, 1, 0, None)
+    assert rc == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
 
 
 def test_gate_backward_validation(L):

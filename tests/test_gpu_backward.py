@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from linear_attention_sequence_gate_amd import KdaError, kda_chunk_bwd
+from linear_attention_sequence_gate_amd import KdaError, kda_chunk_bwd, kda_chunk_bwd_workspace_size_flags
 from linear_attention_sequence_gate_amd._lib import KDA_FLAG_CHECK_RANGE, KDA_FLAG_TOKEN_BACKWARD
 from kda_testutil import GRAD_TOL, oracle_gate_f32, prefill_device, rho, say
 
@@ -127,3 +127,95 @@ def test_backward_benchmark_shape_sampled_chains():
         print(f"    b{b} h{h} " + " ".join(f"{k}={v:.1e}" for k, v in res.items()), flush=True)
         for name, r in res.items():
             assert r <= GRAD_TOL, (b, h, name, r)
+
+
+# --------------------------------------------------------------------------
+# Segmented chunked reverse mode (workspace smaller than the whole sequence)
+# --------------------------------------------------------------------------
+
+GRADS = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"),
+         ("d_initial_state", "dS0"))
+
+
+@pytest.mark.parametrize("dtype,B,T,H,dk,dv,seg,slow", [
+    (torch.bfloat16, 2, 301, 4, 128, 128, 64, False),   # 5 segments, ragged last one
+    (torch.float32, 1, 100, 2, 64, 32, 32, False),      # 4 segments, a 4-token last one
+    (torch.float32, 1, 200, 2, 32, 32, 32, True),       # slow decay: gradients cross 7 segments
+    (torch.bfloat16, 1, 130, 2, 128, 64, 32, True),
+])
+def test_backward_segmented_matches_oracle_and_one_segment(dtype, B, T, H, dk, dv, seg, slow):
+    say("backward segmented", dtype, B, T, H, dk, dv, "segments of", seg, "slow" if slow else "")
+    x = prefill_device(B, T, H, dk, dv, dtype, 770 + T, s0_std=0.3)
+    # slow: z - 6 puts g near -0.01, so a state gradient survives hundreds of tokens
+    g = oracle_gate_f32(x["z"].float() - 6.0 if slow else x["z"], x["A"])
+    gen = torch.Generator(device="cuda").manual_seed(771 + T)
+    d_o = torch.randn(B, T, H, dv, device="cuda", generator=gen).to(dtype)
+    dST = torch.randn(B, H, dk, dv, device="cuda", generator=gen)
+    args = (x["q"], x["k"], x["v"], g.cuda(), x["beta"], x["S0"], d_o, dST)
+    one = kda_chunk_bwd(*args)
+    seg_out = kda_chunk_bwd(*args, segment_tokens=seg)
+    torch.cuda.synchronize()
+    ref = oracle.backward_np(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, dST)
+    res = {name: rho(seg_out[name], ref[rname]) for name, rname in GRADS}
+    same = {name: bool(torch.equal(seg_out[name], one[name])) for name, _ in GRADS}
+    print("    " + " ".join(f"{k}={v:.1e}" for k, v in res.items()), "bit-equal to one segment:",
+          all(same.values()), flush=True)
+    for name, _ in GRADS:
+        assert torch.isfinite(seg_out[name]).all(), name
+        assert res[name] <= GRAD_TOL, (name, res[name])
+        assert rho(seg_out[name], one[name]) <= 1e-6, name
+
+
+@pytest.mark.timeout(900)
+def test_backward_t1m_within_a_bounded_workspace():
+    """B1 H32 T1M d128 bf16: about 230 GB of workspace in one segment, run in
+    32768-token segments (under 8 GB).  Two chains are checked against the
+    oracle on three windows: the first 4096 tokens, 4096 tokens around the
+    first segment boundary, and the last 4096.  The gate g = -5 U(0, 1)
+    decays every channel by about e^-2.5 a token, so a state gradient from 512
+    tokens further on is exactly zero in fp64 (e^-1280): each window's oracle
+    runs the forward recurrence from the sequence start (C oracle) and the
+    reverse mode over the window plus 512 tokens, whose final state gradient
+    is then zero (the true one for the last window)."""
+    B, T, H, d = 1, 1 << 20, 32, 128
+    seg = 32768
+    say("backward B1 H32 T1M in 32768-token segments")
+    x = prefill_device(B, T, H, d, d, torch.bfloat16, 4343, s0_std=0.02)
+    del x["z"]
+    gen = torch.Generator(device="cuda").manual_seed(4344)
+    g = -5.0 * torch.rand(B, T, H, d, device="cuda", generator=gen)
+    d_o = torch.randn(B, T, H, d, device="cuda", generator=gen).to(torch.bfloat16)
+    dST = torch.randn(B, H, d, d, device="cuda", generator=gen)
+    ws_bytes = kda_chunk_bwd_workspace_size_flags(B, T, H, d, d, 1, 0, seg)
+    assert ws_bytes < 8e9
+    out = kda_chunk_bwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], d_o, dST, segment_tokens=seg)
+    torch.cuda.synchronize()
+    for name, _ in GRADS:
+        assert torch.isfinite(out[name]).all(), name
+    margin = 512
+    for h in (3, 29):
+        chain = lambda t, a, b: t[:, a:b, h:h + 1].contiguous()
+        for (t0, t1) in ((0, 4096), (seg - 2048, seg + 2048), (T - 4096, T)):
+            say("  chain", h, "window", t0, t1)
+            S_start = x["S0"][:, h:h + 1].contiguous()
+            if t0 > 0:
+                _, S_start = oracle.forward(chain(x["q"], 0, t0), chain(x["k"], 0, t0),
+                                            chain(x["v"], 0, t0), chain(g, 0, t0),
+                                            chain(x["beta"], 0, t0), S_start, want_o=False,
+                                            col_block=8)
+            t2 = min(t1 + margin, T)
+            dS_end = dST[:, h:h + 1].contiguous() if t2 == T else None
+            ref = oracle.backward_np(chain(x["q"], t0, t2), chain(x["k"], t0, t2),
+                                     chain(x["v"], t0, t2), chain(g, t0, t2),
+                                     chain(x["beta"], t0, t2), S_start, chain(d_o, t0, t2), dS_end)
+            n = t1 - t0
+            res = {name: rho(chain(out[name], t0, t1), ref[rname][:, :n])
+                   for name, rname in GRADS[:-1]}
+            if t0 == 0:
+                res["d_initial_state"] = rho(out["d_initial_state"][:, h:h + 1], ref["dS0"])
+            print(f"    h{h} [{t0}, {t1}) " + " ".join(f"{k}={v:.1e}" for k, v in res.items()),
+                  flush=True)
+            for name, r in res.items():
+                assert r <= GRAD_TOL, (h, t0, name, r)
+    del x, g, d_o, out
+    torch.cuda.empty_cache()
