@@ -757,20 +757,25 @@ SQ_MD = os.path.join(ROOT, "profiles", "sq_counters_chunk32_b4h32t32k.md")
 N_SE, N_SIMD = 32, 1024        # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
 
 
-def recorded_mfma_busy():
-    """MFMA busy share of the fused kernel from the recorded SQ counters, while
-    its sources are unchanged since they were taken (else None)."""
+def recorded_sq():
+    """The fused kernel's recorded SQ figures (MFMA busy, VALU active and their
+    sum, the issue share), while its sources are unchanged since they were
+    taken (else an empty dict)."""
     try:
         text = open(SQ_MD).read()
     except OSError:
-        return None
+        return {}
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
-        return None
+        return {}
     rec = json.loads(m.group(1))
     if rec.get("source_sha256") != source_hash(KERNELS["fused_fwd"][1]):
-        return None
-    return rec.get("mfma_busy_frac")
+        return {}
+    return rec
+
+
+def recorded_mfma_busy():
+    return recorded_sq().get("mfma_busy_frac")
 
 
 SQ_STEPS, SQ_WARMUP = 5, 20
@@ -833,6 +838,18 @@ def ingest_sq(dirs):
         derived.append(f"| kernel cycles (SQ_BUSY_CYCLES / {N_SE} shader engines) | {cycles:.4g} |")
         derived.append(f"| MFMA busy share of every SIMD's cycles (SQ_VALU_MFMA_BUSY_CYCLES / "
                        f"(cycles x {N_SIMD} SIMDs)) | {rec['mfma_busy_frac']:.3f} |")
+        if "SQ_ACTIVE_INST_VALU" in vals:
+            # SQ_ACTIVE_INST_VALU counts in units of 4 cycles (as SQ_WAVE_CYCLES,
+            # whose per-wave sum is the kernel's cycles / 4 here)
+            rec["valu_active_frac"] = 4 * vals["SQ_ACTIVE_INST_VALU"] / (cycles * N_SIMD)
+            rec["issue_frac"] = rec["valu_active_frac"] + rec["mfma_busy_frac"]
+            if "SQ_INSTS_VALU" in vals:
+                rec["cycles_per_valu_inst"] = 4 * vals["SQ_ACTIVE_INST_VALU"] / vals["SQ_INSTS_VALU"]
+                derived.append(f"| cycles per VALU instruction (4 SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU) | "
+                               f"{rec['cycles_per_valu_inst']:.2f} |")
+            derived.append(f"| VALU-active share of every SIMD's cycles (4 SQ_ACTIVE_INST_VALU / "
+                           f"(cycles x {N_SIMD} SIMDs)) | {rec['valu_active_frac']:.3f} |")
+            derived.append(f"| issue share: VALU active + MFMA busy | {rec['issue_frac']:.3f} |")
     if derived:
         lines += ["", "Derived (counts are summed over waves; the shares divide counters kept in "
                   "the same unit):", "", "| figure | value |", "|---|---|"] + derived
@@ -952,6 +969,8 @@ def main():
                     "arith_intensity": ai,
                     "mfma_frac_of_bf16_peak": fused_tflops / BF16_PEAK_TFLOPS,
                     "rocprof_mfma_busy_frac": recorded_mfma_busy(),
+                    "rocprof_valu_active_frac": recorded_sq().get("valu_active_frac"),
+                    "rocprof_issue_frac": recorded_sq().get("issue_frac"),
                     "roofline_frac_of_attainable": fused_tflops / attainable_tflops,
                     "head_tokens": work["head_tokens"],
                     "two_kernel": {"gate_ms": gate_ms, "chunk_ms": chunk_s * 1e3,
