@@ -1776,6 +1776,132 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Log-depth chaining for many segments: the affine maps F_p(S) = M_p S + L_p
+// compose associatively, (F_q o F_p)(S) = (M_q M_p) S + (M_q L_p + L_q), so
+// the prefix maps G_p = F_p o .. o F_1 come from ceil(log2(P-2)) levels of an
+// inclusive scan (each level composes every entry with the one `shift`
+// before it, Hillis-Steele), and then Sin[p] = G_p(Sin[0]) for all p at once.
+// Entry x = (p - 1) nbh + bh holds M (dk x dk) and L (dk x dv) contiguously in
+// x.  One workgroup per (x, 16-column block of [M | L]) forms
+//     C = A B + D      (A 128 x 128, B and C 128 x 16 columns of a 128-row
+//                      matrix, D as C or absent)
+// with the product code of seg_chain_kernel; an entry with x < shift is
+// copied.
+// ---------------------------------------------------------------------------
+template <int DK>
+__device__ __forceinline__ void affine_block(const float *__restrict__ A, const float *B, int ldb,
+                                             const float *D, float *C, int ldc, float *sM,
+                                             float *sBT) {
+    constexpr int NC = 16, LDP = DK + 4, NF = DK * DK / 4 / 256;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    const floatx4 *A4 = reinterpret_cast<const floatx4 *>(A);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int f = i * 256 + tid, r = f / (DK / 4), c4 = f % (DK / 4);
+        *reinterpret_cast<floatx4 *>(&sM[r * LDP + 4 * c4]) = A4[f];
+    }
+    for (int e = tid; e < DK * NC; e += 256) {
+        const int r = e / NC, c = e % NC;
+        sBT[c * LDP + r] = B[(size_t)r * ldb + c];
+    }
+    floatx4 acc[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[it][j] = D ? D[(size_t)(32 * wave + 16 * it + 4 * lq + j) * ldc + lr] : 0.0f;
+    __syncthreads();
+#pragma unroll 4
+    for (int s = 0; s < DK / 16; ++s) {
+        const floatx4 b = *reinterpret_cast<const floatx4 *>(&sBT[lr * LDP + 16 * s + 4 * lq]);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const floatx4 a = *reinterpret_cast<const floatx4 *>(
+                &sM[(32 * wave + 16 * it + lr) * LDP + 16 * s + 4 * lq]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc[it], 0, 0, 0);
+        }
+    }
+    // D may be C itself (the final step): every element of D was read above,
+    // by the thread that now writes it
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) C[(size_t)(32 * wave + 16 * it + 4 * lq + j) * ldc + lr] = acc[it][j];
+}
+
+// One scan level: entries x >= shift become F_x o F_{x - shift} (in map
+// order: M_x M_{x-shift}, M_x L_{x-shift} + L_x); entries below are copied.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__ Min,
+                                                       const float *__restrict__ Lin,
+                                                       float *__restrict__ Mout,
+                                                       float *__restrict__ Lout, int64_t nx,
+                                                       int64_t shift, int DV) {
+    constexpr int LDP = DK + 4;
+    __shared__ __attribute__((aligned(16))) float sM[DK * LDP];
+    __shared__ __attribute__((aligned(16))) float sBT[16 * LDP];
+    const int ncb = (DK + DV) / 16;
+    const int64_t x = blockIdx.x / ncb;
+    const int cb = blockIdx.x % ncb;
+    if (x >= nx) return;
+    const bool isM = cb < DK / 16;
+    const int col0 = isM ? 16 * cb : 16 * (cb - DK / 16);
+    const size_t mo = (size_t)x * DK * DK, lo = (size_t)x * DK * DV;
+    if (x < shift) {
+        const float *src = isM ? Min + mo : Lin + lo;
+        float *dst = isM ? Mout + mo : Lout + lo;
+        const int ld = isM ? DK : DV;
+        for (int e = threadIdx.x; e < DK * 16; e += 256)
+            dst[(size_t)(e / 16) * ld + col0 + e % 16] = src[(size_t)(e / 16) * ld + col0 + e % 16];
+        return;
+    }
+    const size_t mb = (size_t)(x - shift) * DK * DK, lb = (size_t)(x - shift) * DK * DV;
+    if (isM)
+        affine_block<DK>(Min + mo, Min + mb + col0, DK, nullptr, Mout + mo + col0, DK, sM, sBT);
+    else
+        affine_block<DK>(Min + mo, Lin + lb + col0, DV, Lin + lo + col0, Lout + lo + col0, DV, sM, sBT);
+}
+
+// Sin[p] = G_p(Sin[0]) = Mg[x] Sin[0] + Lg[x] for every entry x (chain x % nbh).
+template <int DK>
+__global__ __launch_bounds__(256) void seg_apply_kernel(float *__restrict__ Sin,
+                                                        const float *__restrict__ Mg,
+                                                        const float *Lg, int64_t nx, int nbh,
+                                                        int DV) {
+    constexpr int LDP = DK + 4;
+    __shared__ __attribute__((aligned(16))) float sM[DK * LDP];
+    __shared__ __attribute__((aligned(16))) float sBT[16 * LDP];
+    const int ncb = DV / 16;
+    const int64_t x = blockIdx.x / ncb;
+    const int col0 = 16 * (int)(blockIdx.x % ncb);
+    if (x >= nx) return;
+    const size_t vsz = (size_t)nbh * DK * DV;
+    const size_t lo = (size_t)x * DK * DV;
+    affine_block<DK>(Mg + (size_t)x * DK * DK, Sin + (size_t)(x % nbh) * DK * DV + col0, DV,
+                     Lg + lo + col0, Sin + vsz + lo + col0, DV, sM, sBT);
+}
+
+// Whether the log-depth chaining beats P - 2 serial steps.  Measured: a
+// serial step takes about 1.3 us, a round of scan workgroups (two per CU,
+// one launch per level) about 4.8 us; the scan takes ceil(log2(P - 2))
+// levels of nbh (P - 2) (dk + dv) / 16 workgroups plus the final
+// nbh (P - 2) dv / 16.  One chain of 1M tokens (P = 129) gains; two chains
+// of 256K (P = 65) or of 12400 tokens (P = 26) do not.
+static bool seq_split_log_chain(int64_t nbh, int P, int dk, int dv) {
+    const int64_t n = P - 2;
+    if (n < 4) return false;
+    int levels = 0;
+    while ((int64_t(1) << levels) < n) ++levels;
+    auto rounds = [](int64_t w) { return (w + 511) / 512; };
+    const int64_t scan = levels * rounds(nbh * n * (dk + dv) / 16) + rounds(nbh * n * dv / 16);
+    return 48 * scan < 13 * n;
+}
+
 // dv-slice width per workgroup: 64 columns (fp32 at dk = 64: 32); bf16 at
 // dk = 128 runs 8 waves per workgroup, the other shapes 4.
 static int slice_width(int dk, int dv, int is_bf16) {
@@ -1849,7 +1975,10 @@ size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int 
     const int P = seq_split_effective(T, nseg);
     if (P < 2) return 0;
     const size_t vsz = (size_t)B * H * dk * dv * 4, msz = (size_t)B * H * dk * dk * 4;
-    return (size_t)(P - 1) * vsz + (size_t)(P - 2) * (vsz + msz);
+    // the log-depth chaining ping-pongs M through a second buffer (L through
+    // the Sin slots it fills last)
+    const size_t scan = seq_split_log_chain(B * H, P, dk, dv) ? (size_t)(P - 2) * msz : 0;
+    return (size_t)(P - 1) * vsz + (size_t)(P - 2) * (vsz + msz) + scan;
 }
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -1899,7 +2028,24 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         hipLaunchKernelGGL(kern, dim3(units * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (P >= 3) {
+        if (P >= 3 && seq_split_log_chain(args.nbh, P, dk, dv)) {
+            // log-depth: scan levels ping-pong M between Mb and the buffer
+            // after it, L between Lb and Sin[1..]; then Sin[p] = G_p(Sin[0])
+            const int64_t nx = (int64_t)args.nbh * (P - 2);
+            float *Mbuf[2] = {args.Mb, args.Mb + (size_t)nx * dk * dk};
+            float *Lbuf[2] = {args.Lb, args.Sin + (size_t)args.nbh * dk * dv};
+            int cur = 0;
+            for (int64_t shift = args.nbh; shift < nx; shift *= 2) {
+                hipLaunchKernelGGL(seg_scan_kernel<128>, dim3((unsigned)(nx * ((dk + dv) / 16))),
+                                   dim3(256), 0, s, Mbuf[cur], Lbuf[cur], Mbuf[cur ^ 1],
+                                   Lbuf[cur ^ 1], nx, shift, dv);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                cur ^= 1;
+            }
+            hipLaunchKernelGGL(seg_apply_kernel<128>, dim3((unsigned)(nx * (dv / 16))), dim3(256), 0,
+                               s, args.Sin, Mbuf[cur], Lbuf[cur], nx, args.nbh, dv);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else if (P >= 3) {
             hipLaunchKernelGGL(seg_chain_kernel<128>, dim3(args.nbh * (dv / 16)), dim3(256), 0, s,
                                args.Sin, args.Lb, args.Mb, args.nbh, dv, P);
             e = hipGetLastError();

@@ -106,9 +106,11 @@ def test_sequence_split_workspace_and_policy(L):
     wss = L.kda_chunk_fwd_workspace_size_segments
     auto = L.kda_chunk_fwd_auto_segments
 
-    def split_bytes(B, H, dv, P):       # (P-1) initial states, (P-2) zero-start states + transitions
+    def split_bytes(B, H, dv, P, scan=False):
+        # (P-1) initial states, (P-2) zero-start states + transitions, and with
+        # the log-depth chaining a second buffer of (P-2) transitions
         vsz, msz = B * H * 128 * dv * 4, B * H * 128 * 128 * 4
-        return 256 + (P - 1) * vsz + (P - 2) * (vsz + msz)
+        return 256 + (P - 1) * vsz + (P - 2) * (vsz + msz) + (P - 2) * msz * scan
 
     # B4 H32 T32K: 256 workgroups of 64 columns fill the GPU in one pass
     assert auto(4, 32768, 32, 128, 128, 1) == 1
@@ -121,7 +123,7 @@ def test_sequence_split_workspace_and_policy(L):
     # one chain: many more segments
     P1 = auto(1, 1 << 20, 1, 128, 128, 1)
     assert P1 > 4 * P, (P1, P)
-    assert ws(1, 1 << 20, 1, 128, 128, 1) == split_bytes(1, 1, 128, P1)
+    assert ws(1, 1 << 20, 1, 128, 128, 1) == split_bytes(1, 1, 128, P1, scan=True)
     # few chains of a short sequence split too (segments of >= 128 tokens):
     # B1 H8 T4096 runs 16 workgroups in one pass
     P8 = auto(1, 4096, 8, 128, 128, 1)

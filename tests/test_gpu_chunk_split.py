@@ -66,7 +66,7 @@ def test_split_in_place_state_zero_start_and_determinism():
 
 def test_automatic_split_for_a_long_few_chain_input():
     """B1 H2 T12400: 4 workgroups in one pass, so the library splits on its own
-    (three segments of 4,160 tokens); the whole path gate -> chunk against the
+    (26 segments of 480 tokens); the whole path gate -> chunk against the
     oracle."""
     say("automatic split B1 H2 T12400")
     B, T, H = 1, 12400, 2
@@ -83,3 +83,32 @@ def test_automatic_split_for_a_long_few_chain_input():
     print(f"    rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {rho(o, o_1):.3e} {rho(S, S_1):.3e}",
           flush=True)
     assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
+
+
+@pytest.mark.parametrize("nseg,B,T,H", [
+    (5, 1, 900, 2),        # 3 chaining steps
+    (6, 1, 1100, 2),       # 4
+    (12, 2, 2200, 1),      # 10
+    (40, 1, 5000, 1),      # 38 chaining steps
+    (129, 1, 16512, 1),    # 127 entries of 128-token segments: the log-depth scan, 7 levels
+])
+def test_split_with_slow_decay_chains_the_transitions(nseg, B, T, H):
+    """A slowed gate (z - 6: g near -0.01 a token) keeps the state, and so each
+    segment's transition M, far from zero across a whole segment: the chained
+    initial states (serial steps for few segments, the log-depth scan of the
+    affine maps for more) carry real weight.  Against the oracle and against
+    one pass."""
+    say("split, slow decay", f"nseg={nseg} B={B} T={T} H={H}")
+    x = prefill_device(B, T, H, 128, 128, BF16, 420 + nseg, s0_std=0.3)
+    g_f32 = oracle_gate_f32(x["z"].float() - 6.0, x["A"])
+    g = g_f32.cuda()
+    o_s, S_s = _split(x, g, nseg)
+    o_1, S_1 = _split(x, g, 1)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], x["S0"])
+    ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
+    r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
+    print(f"    vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}", flush=True)
+    assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all()
+    assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
+    assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (r1o, r1s)
