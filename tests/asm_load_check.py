@@ -7,8 +7,23 @@ before the data arrives; the late return would then corrupt the register
 (a corrupted address faults the GPU).  This check walks every path of the
 compiled kernel (each inline-asm block is one step) from each such load and
 reports any instruction that reads or writes the load's destination registers
-before an inline-asm block containing a vmcnt wait, and any path that ends
-the program first.
+before a wait that covers the load, and any path that ends the program first.
+
+A wait covers the load only if the count it allows cannot include it.
+`vmcnt(N)` lets the wave go on once at most N vector-memory operations are
+outstanding.  Loads return in issue order, but a store (or atomic) issued
+later may retire before an earlier load, so only later loads can be relied on
+to still be outstanding: `vmcnt(N)` covers the load when at least N loads were
+issued after it on the path that reaches the wait.  Stores issued after the
+load count for nothing.  A wait that does not cover the load (it waits for
+older loads) leaves it in flight, and the walk goes on past it.  Waits the
+compiler inserted count like the inline-asm ones.
+
+One form is taken on trust: an inline-asm block that branches between
+`vmcnt(N)` and `vmcnt(0)` on a flag (the kernel's `vm_wait_or_all`) takes the
+`vmcnt(0)` branch exactly when the N later loads were not issued, so it
+covers the load on every path.  That relation between the flag and the
+issued loads is the kernel's own, stated where it is used.
 """
 from __future__ import annotations
 
@@ -31,6 +46,13 @@ def function_body(asm_text: str, symbol: str) -> List[str]:
     start = next(i for i, l in enumerate(lines) if l.startswith(symbol + ":"))
     end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
     return lines[start:end]
+
+
+_VM_LOADS = ("global_load", "buffer_load", "flat_load", "scratch_load")
+
+
+def _vmcnts(body: List[str]) -> List[int]:
+    return [int(m.group(1)) for x in body for m in [re.search(r"vmcnt\((\d+)\)", x)] if m]
 
 
 def hazards(lines: List[str]) -> Tuple[int, List[str]]:
@@ -58,43 +80,57 @@ def hazards(lines: List[str]) -> Tuple[int, List[str]]:
         i += 1
     labels = {st[1]: k for k, st in enumerate(steps) if st[0] == "label"}
     found, nloads = [], 0
+    cap = 64
     for k, st in enumerate(steps):
         if st[0] != "asm":
             continue
-        for a in st[2]:
+        for ia, a in enumerate(st[2]):
             if not a.startswith("global_load"):
                 continue
             nloads += 1
             dregs = _regs(a.split()[1].rstrip(","))
-            stack, visited, bad = [k + 1], set(), None
+            # loads issued after this one inside the same asm block
+            later0 = sum(1 for x in st[2][ia + 1:] if x.startswith(_VM_LOADS))
+            stack, visited, bad = [(k + 1, later0)], set(), None
             while stack and bad is None:
-                j = stack.pop()
+                j, later = stack.pop()
                 while j < len(steps):
-                    if j in visited:
+                    key = (j, min(later, cap))
+                    if key in visited:
                         break
-                    visited.add(j)
+                    visited.add(key)
                     sj = steps[j]
                     if sj[0] == "label":
                         j += 1
                         continue
                     if sj[0] == "asm":
-                        if any(x.startswith("s_waitcnt vmcnt") for x in sj[2]):
-                            break
+                        waits = _vmcnts(sj[2])
+                        if waits and (max(waits) <= later or (len(waits) > 1 and min(waits) == 0)):
+                            break                   # covered on every branch of the block
+                        later += sum(1 for x in sj[2] if x.startswith(_VM_LOADS))
                         j += 1
                         continue
                     text = sj[2]
+                    if text.startswith("s_waitcnt"):
+                        waits = _vmcnts([text])
+                        if waits and waits[0] <= later:
+                            break
+                        j += 1
+                        continue
                     parts = text.split(None, 1)
                     if len(parts) > 1 and _regs(parts[1]) & dregs:
                         bad = text
                         break
+                    if text.startswith(_VM_LOADS):
+                        later += 1
                     if text.startswith("s_endpgm"):
                         bad = text
                         break
                     if text.startswith("s_branch"):
-                        stack.append(labels[text.split()[1]])
+                        stack.append((labels[text.split()[1]], later))
                         break
                     if text.startswith("s_cbranch"):
-                        stack.append(labels[text.split()[1]])
+                        stack.append((labels[text.split()[1]], later))
                     j += 1
             if bad is not None:
                 found.append(f"{a}  ->  {bad}")

@@ -91,3 +91,66 @@ def test_checker_accepts_a_waited_use_and_flags_exit():
     assert hazards(function_body(ok, "_Zk")) == (1, [])
     early_exit = ok.replace("\t;;#ASMSTART\n\ts_waitcnt vmcnt(0)\n\t;;#ASMEND\n", "", 1)
     assert len(hazards(function_body(early_exit, "_Zk"))[1]) == 1
+
+
+def test_checker_flags_a_wait_that_counts_a_store():
+    """vmcnt(1) after a load and a later store: the store may retire first, so
+    the wait can pass with the load outstanding.  With a later load instead
+    of the store the same wait covers it."""
+    text = """_Zk:
+	;;#ASMSTART
+	global_load_dword v4, v1, s[0:1]
+	;;#ASMEND
+	global_store_dword v2, v3, s[2:3]
+	;;#ASMSTART
+	s_waitcnt vmcnt(1)
+	;;#ASMEND
+	v_add_u32_e32 v5, v4, v4
+	s_endpgm
+.Lfunc_end0:"""
+    n, found = hazards(function_body(text, "_Zk"))
+    assert n == 1 and len(found) == 1 and "v_add" in found[0]
+    ok = text.replace("global_store_dword v2, v3, s[2:3]", "global_load_dword v6, v1, s[2:3]")
+    assert hazards(function_body(ok, "_Zk")) == (1, [])
+
+
+def test_checker_walks_past_a_wait_for_older_loads():
+    """vmcnt(1) right after two loads waits for the first only: a use of the
+    second's register before a further wait is reported, one after vmcnt(0)
+    is not."""
+    text = """_Zk:
+	;;#ASMSTART
+	global_load_dword v4, v1, s[0:1]
+	global_load_dword v6, v1, s[2:3]
+	;;#ASMEND
+	;;#ASMSTART
+	s_waitcnt vmcnt(1)
+	;;#ASMEND
+	v_add_u32_e32 v5, v4, v6
+	s_endpgm
+.Lfunc_end0:"""
+    n, found = hazards(function_body(text, "_Zk"))
+    assert n == 2 and len(found) == 1 and "v6" in found[0].split("->")[0]
+    ok = text.replace("\tv_add_u32_e32 v5, v4, v6\n",
+                      "\tv_mov_b32_e32 v5, v4\n\ts_waitcnt vmcnt(0)\n\tv_add_u32_e32 v5, v5, v6\n")
+    assert hazards(function_body(ok, "_Zk")) == (2, [])
+
+
+def test_checker_counts_loads_per_path():
+    """A wait reached on two paths must be covered on both: here the path that
+    skips the second load reaches vmcnt(1) with no later load."""
+    text = """_Zk:
+	;;#ASMSTART
+	global_load_dword v4, v1, s[0:1]
+	;;#ASMEND
+	s_cbranch_scc1 .LBB0_2
+	global_load_dword v6, v1, s[2:3]
+.LBB0_2:
+	;;#ASMSTART
+	s_waitcnt vmcnt(1)
+	;;#ASMEND
+	v_add_u32_e32 v5, v4, v4
+	s_endpgm
+.Lfunc_end0:"""
+    n, found = hazards(function_body(text, "_Zk"))
+    assert n == 1 and len(found) == 1
