@@ -625,6 +625,13 @@ EXTRA_TRACES = {
                  "segment in reverse; rows labelled by the call their prep launch belongs to); "
                  "then the token-level path (1 warm-up + 1 timed call; "
                  "bwd_ckpt_kernel, bwd_kernel, bwd_sum_kernel) and kda_gate_bwd."),
+    "small": ("small", "kernel_trace_prefill_b1h8t4096_split.md",
+              "kda_chunk_fwd_gated on B1 H8 T4096 d128 bf16 with the library's automatic "
+              "sequence split (9 segments of 480 tokens), inputs rotated over five copies (10 "
+              "warm-up + 20 timed calls).  A call is three launches: chunk32_kernel phase 1 "
+              "(segment 0, the middle segments from zero and their transitions), "
+              "seg_chain_kernel (serial chaining), chunk32_kernel phase 3 (segments 1..8); the "
+              "workgroup count tells the phases apart."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (5 warm-up + 5 timed calls) and with the position-pair "
@@ -708,7 +715,9 @@ def ingest_trace_extra(name, d):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel", "gate_kernel",
+    rows = [r for r in rows if _matches(r["Kernel_Name"], ("chunk32_kernel", "seg_chain_kernel",
+                                                           "seg_scan_kernel", "seg_apply_kernel",
+                                                           "gate_kernel",
                                                            "bwd_ckpt_kernel", "bwd_kernel", "bwd_sum_kernel",
                                                            "cb_prep_kernel", "cb_fwd_kernel", "cb_bwd_kernel",
                                                            "cb_grad_kernel"))]
