@@ -63,9 +63,9 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", f"hbm_traffic_{PROFILE_TAG}.md")
 TRACE_MD = os.path.join(ROOT, "profiles", f"kernel_trace_{PROFILE_TAG}.md")
 # kernel -> (name fragments in a profiler trace, sources that define it)
 KERNELS = {
-    "fused_fwd": (("chunk32_kernel<128, true>", "chunk32_kernelILi128ELb1E"),
+    "fused_fwd": (("chunk32_kernel<128, true,", "chunk32_kernelILi128ELb1E"),
                   ("kda_chunk.hip", "kda_device.h")),
-    "chunk_fwd": (("chunk32_kernel<128, false>", "chunk32_kernelILi128ELb0E", "chunk_fwd_kernel"),
+    "chunk_fwd": (("chunk32_kernel<128, false,", "chunk32_kernelILi128ELb0E", "chunk_fwd_kernel"),
                   ("kda_chunk.hip", "kda_device.h")),
     "decode_step": (("decode_step_kernel",), ("kda_decode.hip", "kda_device.h")),
     "gate": (("gate_kernel",), ("kda_gate.hip", "kda_device.h")),
@@ -969,7 +969,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic["fused_fwd"],
-                     "kernel": "chunk32_kernel<128, true> (gate fused, 64-column dv slices)",
+                     "kernel": "chunk32_kernel<128, true, false> (gate fused, 64-column dv slices)",
                      "bytes_per_launch": work["fused_bytes"], "avg_ms": fused_s * 1e3},
         "prefill": {"fused_ms": fused_s * 1e3,
                     "alg_tflops": fused_tflops,

@@ -82,7 +82,7 @@ struct ChunkArgs {
     // cu_seqlens[b] .. cu_seqlens[b+1] - 1 of a packed [T, H, ...] layout
     // (T = all tokens); null for the [B, T, H, ...] layout
     const int64_t *cu_seqlens;
-    // chunk32_kernel<DK, true>: the gate is evaluated in the kernel from z
+    // chunk32_kernel<DK, true, ..>: the gate is evaluated in the kernel from z
     // (the input dtype, [.., H, dk] like k) and the [H, dk] table A; g is
     // then unused
     const void *z;
@@ -963,11 +963,14 @@ template <int DK> struct PipeLds {
     static constexpr int SLOT = S_EBC + DK * 4;
     static constexpr int NSLOT = 3;                 // chunks c (built), c-1 (inverse), c-2 (state)
     static constexpr int TOTAL = PREP + NSLOT * SLOT;
+    // after TOTAL, in the instances with transition columns only: the state
+    // waves' zero-state posts, one byte each
+    static constexpr int ZPOST = TOTAL, ZPOST_BYTES = 16;
     static_assert(PREP % 16 == 0 && SLOT % 16 == 0, "alignment");
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(TOTAL + ZPOST_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, bool ZIN>
+template <int DK, bool ZIN, bool TRANS>
 __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     constexpr int NV = 64;
     using Lds = PipeLds<DK>;
@@ -979,24 +982,37 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     constexpr int NCB = DK / 16;                    // state row tiles
     constexpr float kLog2e = 1.4426950408889634f;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::TOTAL + (TRANS ? Lds::ZPOST_BYTES : 0)];
     // the wave index is uniform: keep it scalar so role branches stay scalar
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
 
     // block -> (unit, slice), unit -> (segment, chain); with the XCD map the
-    // slices of one unit share an XCD (and its L2 for q, k, g)
+    // slices of one unit share an XCD (and its L2 for q, k, g).  With
+    // transition columns (TRANS) the v slices of every unit come first and
+    // the transition slices after them, so the v workgroups fill the chip
+    // evenly (in a unit-major order a unit's four slices would each keep to
+    // the same quarter of an XCD's compute units) and the transitions, which
+    // usually end within a few chunks, take the compute units the v
+    // workgroups leave.
     int unit, slice;
     {
-        const int id = blockIdx.x;
+        int id = blockIdx.x, ns = a.nslice, s0 = 0;
+        if constexpr (TRANS) {
+            const int nvb = (int)(gridDim.x / a.nslice) * a.nsl_v;   // v-slice workgroups
+            const bool tgroup = id >= nvb;
+            if (tgroup) id -= nvb;
+            ns = tgroup ? a.nslice - a.nsl_v : a.nsl_v;
+            s0 = tgroup ? a.nsl_v : 0;
+        }
         if (a.xcd_map) {
             const int x = id & 7, j = id >> 3;
-            unit = (j / a.nslice) * 8 + x;
-            slice = j % a.nslice;
+            unit = (j / ns) * 8 + x;
+            slice = s0 + j % ns;
         } else {
-            unit = id / a.nslice;
-            slice = id % a.nslice;
+            unit = id / ns;
+            slice = s0 + id % ns;
         }
     }
     const int seg = a.seg0 + unit / a.nbh, bh = unit % a.nbh;
@@ -1023,6 +1039,23 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const bool pw = __builtin_amdgcn_readfirstlane(a.pairwise) != 0;
     const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
     unsigned char *const slot_base = smem + Lds::PREP;
+    // Transition columns (v = 0, initial state I), TRANS instances only: once
+    // every entry of the block's state is exactly zero, every later chunk
+    // leaves it zero for finite inputs (U = T (0 - K~ 0) = 0,
+    // S <- e^{b_C} 0 + K^^T 0), so the workgroup stops there and stores the
+    // zero state.  Each state wave posts (one byte) whether its 16 columns
+    // are all zero before a period's first barrier; every wave reads the
+    // four posts (one dword) right after that barrier and tests them after
+    // the second, when the read has long returned; all waves leave after the
+    // same period pair, so every wave passes the same barriers.  The next
+    // posts are written after the second barrier.  The posts start at zero
+    // (each state wave clears its own before its first period) and only
+    // transition workgroups set them, so the readers need no test of the
+    // workgroup's kind (such a loop-invariant test in a loop with an early
+    // exit gets the whole loop duplicated).  The other instances carry none
+    // of this: an exit test costs the one-pass loop a few percent.
+    unsigned char *const zpost = smem + Lds::ZPOST;
+    constexpr unsigned kAllZero = 0x01010101u;
 
     if (wave >= 4) {
         // =================================================================
@@ -1120,7 +1153,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             r.beta = vm_load_u16(bb, ob);
         };
 
-        auto period = [&](int64_t c, Raw &raw) {
+        auto period = [&](int64_t c, Raw &raw) -> bool {
             const bool live = c < nchunk;
             const int64_t t0 = tbeg + c * kPipeChunk;
             const int L = live ? (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk) : 0;
@@ -1292,6 +1325,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
             lds_barrier();                                  // BAR1
+            unsigned posts = 0;
+            if constexpr (TRANS) posts = *reinterpret_cast<const unsigned *>(zpost);
 
             if (live) {
                 // ---- P2: scores; tiles that need the other subtile's total
@@ -1419,13 +1454,15 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 }
             }
             lds_barrier();                                  // BAR2
-
+            if constexpr (TRANS) return __builtin_amdgcn_readfirstlane(posts) == kAllZero;
+            else return false;
         };
         if (nchunk > 0) load_raw(0, raw0);         // an empty sequence loads nothing
         if (nchunk > 1) load_raw(1, raw1);
-        for (int64_t c = 0; c <= nchunk + 1; c += 2) {
-            period(c, raw0);
-            if (c + 1 <= nchunk + 1) period(c + 1, raw1);
+        bool stop = false;
+        for (int64_t c = 0; c <= nchunk + 1 && !stop; c += 2) {
+            stop = period(c, raw0);
+            if (c + 1 <= nchunk + 1) stop |= period(c + 1, raw1);
         }
         vm_wait<0>();                               // no load outlives the wave
     } else {
@@ -1481,6 +1518,8 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         typename PF::frag sf[NKS];
 #pragma unroll
         for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
+        if constexpr (TRANS)
+            if (lane == 0) zpost[s] = 0;
 
         // v of one chunk in the accumulator layout: tile i, element j is
         // token 16 i + lg4 + j, column ncol
@@ -1517,7 +1556,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         };
         // period c: state pass of chunk c - 2 (v from cur), v of chunk c - 1
         // requested into nxt, inverse of chunk c - 1 (wave 3)
-        auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) {
+        auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) -> bool {
             const bool pass = c >= 2 && c - 2 < nchunk;
             // cur was requested a period ago; nothing newer is outstanding
             // except the previous period's o stores
@@ -1610,7 +1649,20 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
             }
+            if (TRANS && vzero) {
+                // transition columns: post whether the state is zero in all
+                // 64 lanes (either sign; NaN is not)
+                unsigned nz = 0;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nz |= __float_as_uint(sacc[cb][j]) << 1;
+                const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
+                if (lane == 0) zpost[s] = zero ? 1 : 0;
+            }
             lds_barrier();                                  // BAR1
+            unsigned posts = 0;
+            if constexpr (TRANS) posts = *reinterpret_cast<const unsigned *>(zpost);
             if (s == 3 && c >= 1 && c - 1 < nchunk) {
                 // ---- X = (I + A)^-1 and T = X Diag(beta) of chunk c - 1 ------
                 const int64_t ch = c - 1;
@@ -1665,10 +1717,13 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             }
             if (pw) lds_barrier();                          // position-pair path: partials complete
             lds_barrier();                                  // BAR2
+            if constexpr (TRANS) return __builtin_amdgcn_readfirstlane(posts) == kAllZero;
+            else return false;
         };
-        for (int64_t c = 0; c <= nchunk + 1; c += 2) {
-            period(c, vv0, vv1);
-            if (c + 1 <= nchunk + 1) period(c + 1, vv1, vv0);
+        bool stop = false;
+        for (int64_t c = 0; c <= nchunk + 1 && !stop; c += 2) {
+            stop = period(c, vv0, vv1);
+            if (c + 1 <= nchunk + 1) stop |= period(c + 1, vv1, vv0);
         }
         vm_wait<0>();                               // no load outlives the wave
         if (st) {
@@ -1993,7 +2048,9 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     // the gate inside the kernel: pipelined kernel only
     const bool zin = z != nullptr;
     if (zin && (!pipe || !Ag)) return hipErrorInvalidValue;
-    auto kern = zin ? chunk32_kernel<128, true> : chunk32_kernel<128, false>;
+    auto kern = zin ? chunk32_kernel<128, true, false> : chunk32_kernel<128, false, false>;
+    // the first phase of a split, whose transition columns may end early
+    auto kern_tr = zin ? chunk32_kernel<128, true, true> : chunk32_kernel<128, false, true>;
     const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
@@ -2025,7 +2082,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         args.phase = 1;
         args.nslice = args.nsl_v + dk / 64;
         args.xcd_map = units % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(kern, dim3(units * args.nslice), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(kern_tr, dim3(units * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (P >= 3 && seq_split_log_chain(args.nbh, P, dk, dv)) {

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from linear_attention_sequence_gate_amd import _lib, kda_chunk_fwd, kda_gate
+from linear_attention_sequence_gate_amd import _lib, kda_chunk_fwd, kda_chunk_fwd_gated, kda_gate
 from kda_testutil import TOL, oracle_gate_f32, prefill_device, rho, say
 
 pytestmark = pytest.mark.gpu
@@ -112,3 +112,42 @@ def test_split_with_slow_decay_chains_the_transitions(nseg, B, T, H):
     assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all()
     assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
     assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (r1o, r1s)
+
+
+@pytest.mark.parametrize("nseg", [4, 7])
+def test_split_transitions_that_end_early_and_that_run_on(nseg):
+    """A middle segment's transition columns (v = 0, initial state I) stop as
+    soon as their state is exactly zero.  One launch mixes the cases: head 0
+    takes the plain gate (its transitions vanish within a few chunks), head 1
+    a slowed gate (z - 6) on every token (they never vanish), head 2 the
+    slowed gate on the first 1500 tokens only (some stop mid-segment).  v and
+    the initial state are zero over the first 1000 tokens, so v-column
+    workgroups also carry an all-zero state for a while and must not stop.
+    Both the g-input and the fused-gate kernels, against the oracle and
+    against one pass."""
+    say("split, transitions ending early", f"nseg={nseg}")
+    B, T, H = 1, 3000, 3
+    x = prefill_device(B, T, H, 128, 128, BF16, 430 + nseg)
+    x["v"][:, :1000] = 0
+    z = x["z"].float()
+    z[:, :, 1] -= 6.0
+    z[:, :1500, 2] -= 6.0
+    x["z"] = z.to(BF16)
+    g_f32 = oracle_gate_f32(x["z"], x["A"])
+    g = g_f32.cuda()
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], None)
+    fl = _lib.kda_flag_segments
+    runs = {
+        "g input": (_split(x, g, nseg), _split(x, g, 1)),
+        "gate fused": tuple(kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"],
+                                                None, flags=fl(n)) for n in (nseg, 1)),
+    }
+    torch.cuda.synchronize()
+    for name, ((o_s, S_s), (o_1, S_1)) in runs.items():
+        ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
+        r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
+        print(f"    {name}: vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}",
+              flush=True)
+        assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all()
+        assert ro <= TOL[BF16] and rs <= TOL[BF16], (name, ro, rs)
+        assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (name, r1o, r1s)

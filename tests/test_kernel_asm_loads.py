@@ -25,9 +25,12 @@ def chunk_asm(tmp_path_factory):
     return out.read_text()
 
 
-# both instances of the pipelined kernel: g loaded, and the gate fused (z loaded)
-KERNELS = ["_ZN3kda14chunk32_kernelILi128ELb0EEEvNS_9ChunkArgsE",
-           "_ZN3kda14chunk32_kernelILi128ELb1EEEvNS_9ChunkArgsE"]
+# every instance of the pipelined kernel: g loaded or the gate fused (z
+# loaded), each without and with the transition columns' early end
+KERNELS = ["_ZN3kda14chunk32_kernelILi128ELb0ELb0EEEvNS_9ChunkArgsE",
+           "_ZN3kda14chunk32_kernelILi128ELb1ELb0EEEvNS_9ChunkArgsE",
+           "_ZN3kda14chunk32_kernelILi128ELb0ELb1EEEvNS_9ChunkArgsE",
+           "_ZN3kda14chunk32_kernelILi128ELb1ELb1EEEvNS_9ChunkArgsE"]
 
 
 @pytest.mark.parametrize("name", KERNELS)
