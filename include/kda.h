@@ -248,6 +248,10 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void 
  *    Order them on one stream.
  *  - The first call on a GPU looks up the array's address there (on the
  *    device `stream` belongs to); KDA_ERR_HIP if that fails.
+ *  - Under HIP graph capture: make one call on that GPU before capturing (the
+ *    address lookup), and leave out KDA_FLAG_CHECK_RANGE, which clears a
+ *    counter, reads it back to the host and waits for it.  Without it a call
+ *    issues kernel launches only.
  * With the same segment count the results equal kda_chunk_fwd_gated's bit
  * for bit (the same kernels run).
  */
