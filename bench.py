@@ -63,9 +63,9 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", f"hbm_traffic_{PROFILE_TAG}.md")
 TRACE_MD = os.path.join(ROOT, "profiles", f"kernel_trace_{PROFILE_TAG}.md")
 # kernel -> (name fragments in a profiler trace, sources that define it)
 KERNELS = {
-    "fused_fwd": (("chunk32_kernel<128, true,", "chunk32_kernelILi128ELb1E"),
+    "fused_fwd": (("chunk32_kernel<128, true, false>", "chunk32_kernelILi128ELb1ELb0E"),
                   ("kda_chunk.hip", "kda_device.h")),
-    "chunk_fwd": (("chunk32_kernel<128, false,", "chunk32_kernelILi128ELb0E", "chunk_fwd_kernel"),
+    "chunk_fwd": (("chunk32_kernel<128, false, false>", "chunk32_kernelILi128ELb0ELb0E", "chunk_fwd_kernel"),
                   ("kda_chunk.hip", "kda_device.h")),
     "decode_step": (("decode_step_kernel",), ("kda_decode.hip", "kda_device.h")),
     "gate": (("gate_kernel",), ("kda_gate.hip", "kda_device.h")),
