@@ -641,15 +641,17 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbArgs a, int64_t nbh) {
 }
 
 // ---------------------------------------------------------------------------
-// Token gradients of one chunk.
+// Token gradients of one chunk, or of a chunk pair.
 // ---------------------------------------------------------------------------
 template <int DK, int DV> struct alignas(16) CbGradLds {
     static constexpr int LK = DK + 4, LV = DV + 4, LS = kCB + 4;
     float bm[kCB][LK];                           // bm = b - m
     float m[DK], bcm[DK], rs[DK];                // m, b_C - m, rowsum(S * dN)
+    float rs0[DK];                               // rowsum(S * dN) of a pair's first chunk
+    // dO, U, dW of a chunk; of a pair's second chunk when both are held
     float dO[kCB][LV], U[kCB][LV], dW[kCB][LV];
-    float U0[kCB][LV];                           // U of the pair's first chunk
-    float dO1[kCB][LV], dW1[kCB][LV];            // dO, dW of the pair's second chunk
+    // U, dO, dW of a pair's first chunk
+    float U0[kCB][LV], dO1[kCB][LV], dW1[kCB][LV];
     float X[kCB][LS], At[kCB][LS], dX[kCB][LS], Y[kCB][LS], dP[kCB][LS], dAt[kCB][LS];
     float bet[kCB];
 };
@@ -671,52 +673,57 @@ template <int DK> __host__ __device__ constexpr int cb_grad_tiles() {
     return (DK / 16 + cb_grad_waves<DK>() - 1) / cb_grad_waves<DK>();
 }
 
-enum { kCbPlain = 0, kCbSFromPrev = 1, kCbNFromNext = 2 };
+// One chunk's place: chain row base, first token, valid tokens, workspace unit.
+struct CbChunk {
+    int64_t rb, t0, unit;
+    int n;
+};
+__device__ __forceinline__ CbChunk cb_chunk(const CbArgs &a, int64_t bh, int c) {
+    CbChunk k;
+    k.rb = cb_rowbase(a, bh);
+    k.t0 = (int64_t)c * kCB;
+    k.n = (int)(a.T - k.t0 < kCB ? a.T - k.t0 : kCB);
+    k.unit = bh * a.nc + c;
+    return k;
+}
 
-// Token gradients of chunk c of chain bh.  The state entering the chunk is
-// read at sglob and the gradient leaving it at nglob ([DK][DV] each); with
-// kCbSFromPrev sglob holds the state entering the previous chunk (whose U is
-// in L.U0), with kCbNFromNext nglob holds the gradient leaving the next chunk
-// (whose dO, dW are in L.dO1, L.dW1), and each 16x16 block of the state is
-// formed where the products need it.
-template <typename T, int DK, int DV, int MODE>
-__device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV> &L, int64_t bh,
-                                              int c, int wave, const float *sglob,
-                                              const float *nglob, const CbNeighbour<cb_grad_tiles<DK>()> &nb) {
-    using Lds = CbGradLds<DK, DV>;
-    constexpr int RT = DK / 16, CT = DV / 16, KB = DV / 16;
-    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
-    const int64_t unit = bh * a.nc + c;
-    const int64_t t0 = (int64_t)c * kCB;
-    const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
-    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
-    const int64_t rb = cb_rowbase(a, bh);
-    const float *wc = a.w + unit * kCB * DV;    // W, dU of the chunk: [16][DV]
-    const float *duc = a.du + unit * kCB * DV;
-    // q, k of this lane's tokens 4 g4 + i and channels 16 ct + j (step 4),
-    // zero past the end; loaded first so that the latency is hidden
-    float qin[NT][4], kin[NT][4];
+// q, k of this lane's tokens 4 g4 + i and channels 16 ct + j (step 4), zero
+// past the end; loaded first so that the latency is hidden.
+template <typename T, int DK>
+__device__ __forceinline__ void cb_grad_qk(const CbArgs &a, const CbChunk &ck, int wave,
+                                           float (&qin)[cb_grad_tiles<DK>()][4],
+                                           float (&kin)[cb_grad_tiles<DK>()][4]) {
+    constexpr int RT = DK / 16, NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
         const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i, rr = r < n ? r : n - 1;
-            const int64_t off = (rb + (t0 + rr) * a.H) * DK + ch;
+            const int r = 4 * g4 + i, rr = r < ck.n ? r : ck.n - 1;
+            const int64_t off = (ck.rb + (ck.t0 + rr) * a.H) * DK + ch;
             qin[u][i] = cb_ld<T>(a.q, off);
             kin[u][i] = cb_ld<T>(a.k, off);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            qin[u][i] = 4 * g4 + i < n ? qin[u][i] : 0.f;
-            kin[u][i] = 4 * g4 + i < n ? kin[u][i] : 0.f;
+            qin[u][i] = 4 * g4 + i < ck.n ? qin[u][i] : 0.f;
+            kin[u][i] = 4 * g4 + i < ck.n ? kin[u][i] : 0.f;
         }
     }
-    lds_barrier();                               // the previous chunk is done with LDS
-    // 1. inputs
-    if (tid < DK) {
+}
+
+// Step 1, a chunk's inputs in LDS: with `decay` the log-decays (bm, m,
+// b_C - m); X, At and beta; dO into `dO` when given.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_inputs(const CbArgs &a, CbGradLds<DK, DV> &L,
+                                               const CbChunk &ck, bool decay,
+                                               float (*dO)[CbGradLds<DK, DV>::LV]) {
+    constexpr int NW = cb_grad_waves<DK>();
+    const int tid = threadIdx.x;
+    if (decay && tid < DK) {
         float gv[kCB], b[kCB];
-        cb_load16<float>(a.g, rb, t0, n, a.H, DK, tid, gv);
+        cb_load16<float>(a.g, ck.rb, ck.t0, ck.n, a.H, DK, tid, gv);
         cb_cumsum(gv, b);
         const float m = b[7];
         L.m[tid] = m;
@@ -724,46 +731,66 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
 #pragma unroll
         for (int r = 0; r < kCB; ++r) L.bm[r][tid] = b[r] - m;
     }
-    {
+    if (dO) {
         for (int e = tid; e < kCB * DV; e += NW * 64) {
             const int r = e / DV, cc = e % DV;
-            const int rr = r < n ? r : n - 1;
-            const float ov = cb_ld<T>(a.dout, (rb + (t0 + rr) * a.H) * DV + cc);
-            L.dO[r][cc] = r < n ? ov : 0.f;
+            const int rr = r < ck.n ? r : ck.n - 1;
+            const float ov = cb_ld<T>(a.dout, (ck.rb + (ck.t0 + rr) * a.H) * DV + cc);
+            dO[r][cc] = r < ck.n ? ov : 0.f;
         }
-        const float *mc = a.mat + unit * kCbMat;
-        if (tid < kCB * kCB) {
-            const int r = tid >> 4, cc = tid & 15;
-            L.X[r][cc] = mc[r * kCB + cc];
-            L.At[r][cc] = mc[2 * kCB * kCB + r * kCB + cc];
-        }
-        if (tid < kCB) L.bet[tid] = (tid < n) ? cb_ld<T>(a.beta, rb + (t0 + tid) * a.H) : 0.f;
     }
-    lds_barrier();
+    const float *mc = a.mat + ck.unit * kCbMat;
+    if (tid < kCB * kCB) {
+        const int r = tid >> 4, cc = tid & 15;
+        L.X[r][cc] = mc[r * kCB + cc];
+        L.At[r][cc] = mc[2 * kCB * kCB + r * kCB + cc];
+    }
+    if (tid < kCB) L.bet[tid] = (tid < ck.n) ? cb_ld<T>(a.beta, ck.rb + (ck.t0 + tid) * a.H) : 0.f;
+}
 
-    // 2. U = X Diag(beta) W and dW = Diag(beta) X^T dU, column tiles over waves
+// Step 2, U = X Diag(beta) W and dW = Diag(beta) X^T dU into `U` and `dW`,
+// column tiles over waves; dv = dW.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_u_dw(const CbArgs &a, CbGradLds<DK, DV> &L,
+                                             const CbChunk &ck, int wave,
+                                             float (*U)[CbGradLds<DK, DV>::LV],
+                                             float (*dW)[CbGradLds<DK, DV>::LV]) {
+    constexpr int CT = DV / 16, NW = cb_grad_waves<DK>();
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const float *wc = a.w + ck.unit * kCB * DV;    // W, dU of the chunk: [16][DV]
+    const float *duc = a.du + ck.unit * kCB * DV;
     for (int ct = wave; ct < CT; ct += NW) {
         const int cc = 16 * ct + j;
-        floatx4 U = {0, 0, 0, 0}, dW = {0, 0, 0, 0};
+        floatx4 u4 = {0, 0, 0, 0}, w4 = {0, 0, 0, 0};
         const floatx4 xr = *reinterpret_cast<const floatx4 *>(&L.X[j][4 * g4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 4 * g4 + i;
-            U = mfma1(xr[i], L.bet[s] * wc[s * DV + cc], U);
-            dW = mfma1(L.X[s][j], duc[s * DV + cc], dW);
+            u4 = mfma1(xr[i], L.bet[s] * wc[s * DV + cc], u4);
+            w4 = mfma1(L.X[s][j], duc[s * DV + cc], w4);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
-            dW[i] *= L.bet[r];
-            L.U[r][cc] = U[i];
-            L.dW[r][cc] = dW[i];
-            if (r < n) a.dv[(rb + (t0 + r) * a.H) * DV + cc] = dW[i];
+            w4[i] *= L.bet[r];
+            U[r][cc] = u4[i];
+            dW[r][cc] = w4[i];
+            if (r < ck.n) a.dv[(ck.rb + (ck.t0 + r) * a.H) * DV + cc] = w4[i];
         }
     }
-    lds_barrier();
+}
 
-    // 3a. the 16x16 chunk matrices (waves 0 and 1)
+// Step 3a, the 16x16 chunk matrices (waves 0 and 1), with the chunk's dO and
+// U from `dO`, `U`.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_mats(const CbArgs &a, CbGradLds<DK, DV> &L,
+                                             const CbChunk &ck, int wave,
+                                             const float (*dO)[CbGradLds<DK, DV>::LV],
+                                             const float (*U)[CbGradLds<DK, DV>::LV]) {
+    using Lds = CbGradLds<DK, DV>;
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const float *wc = a.w + ck.unit * kCB * DV;
+    const float *duc = a.du + ck.unit * kCB * DV;
     if (wave == 0) {
         floatx4 dT = {0, 0, 0, 0};                // dT[r][s] = dU_r . W_s
 #pragma unroll
@@ -810,65 +837,52 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
                               dbA[3] * (j % 4 == 3);
         // lane 16 g4 + j holds dbA of row 4 g4 + (j % 4); gather row r = lane (< 16)
         const float dbA_r = __shfl(rowpart, 16 * (lane >> 2) + (lane & 3));
-        if (lane < kCB && lane < n) a.dbeta[(rb + (t0 + lane) * a.H)] = dbT + dbA_r;
+        if (lane < kCB && lane < ck.n) a.dbeta[(ck.rb + (ck.t0 + lane) * a.H)] = dbT + dbA_r;
     } else if (wave == 1) {
         floatx4 dp = {0, 0, 0, 0};
-        tile_mma<float>(dp, &L.dO[0][0], Lds::LV, &L.U[0][0], Lds::LV, DV, lane);  // dO_r . U_s
+        tile_mma<float>(dp, &dO[0][0], Lds::LV, &U[0][0], Lds::LV, DV, lane);  // dO_r . U_s
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
             L.dP[r][j] = (j <= r) ? dp[i] : 0.f;
         }
     }
+}
 
-    // 3b. the state products, channel tiles over waves
-    floatx4 dQt[NT], dKt[NT], dKh[NT];
+// Step 3b's products of one 16x16 block of the state S and of the gradient dN
+// (the chunk's own): dQ~ += dO S^T, dK~ += dW S^T, dK^ += U dN^T and the row
+// sums of S * dN.
+template <int DV>
+__device__ __forceinline__ void cb_grad_block(const float (*dO)[DV + 4], const float (*dW)[DV + 4],
+                                              const float (*U)[DV + 4], int k0, floatx4 sv,
+                                              floatx4 nv, floatx4 &dQt, floatx4 &dKt,
+                                              floatx4 &dKh, float &rsum) {
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const floatx4 o4 = ld4(&dO[j][k0 + 4 * g4]);
+    const floatx4 w4 = ld4(&dW[j][k0 + 4 * g4]);
+    const floatx4 u4 = ld4(&U[j][k0 + 4 * g4]);
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-        const int ct = wave + NW * u;
-        dQt[u] = dKt[u] = dKh[u] = floatx4{0, 0, 0, 0};
-        if (ct < RT) {
-            const int cr = 16 * ct + j;
-            float rsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int k0 = 16 * kb;
-                floatx4 sv = ld4(sglob + (int64_t)cr * DV + k0 + 4 * g4);
-                floatx4 nv = ld4(nglob + (int64_t)cr * DV + k0 + 4 * g4);
-                if constexpr (MODE == kCbSFromPrev) {
-                    // transposed form: rows of the block are value columns,
-                    // columns key channels, as sv is laid out
-                    sv *= nb.e[u];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv = mfma1(L.U0[4 * g4 + i][k0 + j], nb.r1[u][i], sv);
-                }
-                if constexpr (MODE == kCbNFromNext) {
-                    nv *= nb.e[u];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        nv = mfma1(L.dO1[4 * g4 + i][k0 + j], nb.r1[u][i], nv);
-                        nv = mfma1(-L.dW1[4 * g4 + i][k0 + j], nb.r2[u][i], nv);
-                    }
-                }
-                const floatx4 o4 = ld4(&L.dO[j][k0 + 4 * g4]);
-                const floatx4 w4 = ld4(&L.dW[j][k0 + 4 * g4]);
-                const floatx4 u4 = ld4(&L.U[j][k0 + 4 * g4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dQt[u] = mfma1(o4[i], sv[i], dQt[u]);
-                    dKt[u] = mfma1(w4[i], sv[i], dKt[u]);
-                    dKh[u] = mfma1(u4[i], nv[i], dKh[u]);
-                    rsum += sv[i] * nv[i];
-                }
-            }
-            rsum += __shfl_xor(rsum, 16);
-            rsum += __shfl_xor(rsum, 32);
-            if (g4 == 0) L.rs[cr] = rsum;
-        }
+    for (int i = 0; i < 4; ++i) {
+        dQt = mfma1(o4[i], sv[i], dQt);
+        dKt = mfma1(w4[i], sv[i], dKt);
+        dKh = mfma1(u4[i], nv[i], dKh);
+        rsum += sv[i] * nv[i];
     }
-    lds_barrier();
+}
 
-    // 4. pair terms and the token gradients of this wave's channel tiles
+// Step 4, the pair terms and the token gradients of this wave's channel
+// tiles, from step 3b's products and row sums `rs`.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_tokens(const CbArgs &a, CbGradLds<DK, DV> &L,
+                                               const CbChunk &ck, int wave,
+                                               const float (&qin)[cb_grad_tiles<DK>()][4],
+                                               const float (&kin)[cb_grad_tiles<DK>()][4],
+                                               const floatx4 (&dQt)[cb_grad_tiles<DK>()],
+                                               const floatx4 (&dKt)[cb_grad_tiles<DK>()],
+                                               const floatx4 (&dKh)[cb_grad_tiles<DK>()],
+                                               const float *rs) {
+    constexpr int RT = DK / 16, NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
         const int ct = wave + NW * u;
@@ -901,8 +915,8 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
             db[i] = dQt[u][i] * qr * e_b - dKt[u][i] * kr * e_b - kh + dQp[i] * qr * e_bm +
                     dKp[i] * kr * e_bm - dKpp[i] * kr * e_mb;
             khk += kh;
-            if (r < n) {
-                const int64_t row = (rb + (t0 + r) * a.H);
+            if (r < ck.n) {
+                const int64_t row = (ck.rb + (ck.t0 + r) * a.H);
                 a.dq[row * DK + ch] = dq;
                 a.dk[row * DK + ch] = dk;
             }
@@ -910,7 +924,7 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
         // suffix sums over the chunk's tokens (rows 4 g4 + i live in lane group g4)
         khk += __shfl_xor(khk, 16);
         khk += __shfl_xor(khk, 32);
-        const float extra = khk + exp_hw(bcm + m) * L.rs[ch];
+        const float extra = khk + exp_hw(bcm + m) * rs[ch];
         db[2] += db[3];
         db[1] += db[2];
         db[0] += db[1];
@@ -920,80 +934,165 @@ __device__ __forceinline__ void cb_grad_chunk(const CbArgs &a, CbGradLds<DK, DV>
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
-            if (r < n) a.dg[(rb + (t0 + r) * a.H) * DK + ch] = db[i] + later + extra;
+            if (r < ck.n) a.dg[(ck.rb + (ck.t0 + r) * a.H) * DK + ch] = db[i] + later + extra;
         }
     }
-
 }
 
-// Token gradients of the chunk pair (2p, 2p+1) of one chain.  The passes
-// stored the state entering chunk 2p and the gradient leaving chunk 2p+1 (or
-// 2p when it is the last chunk); chunk 2p+1 forms the state entering it from
-// the first, chunk 2p the gradient leaving it from the second.
+// Token gradients of a chain's last chunk when it has no pair partner: the
+// state entering it is read at sglob and the gradient leaving it at nglob.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_single(const CbArgs &a, CbGradLds<DK, DV> &L, int64_t bh,
+                                               int c, int wave, const float *sglob,
+                                               const float *nglob) {
+    constexpr int RT = DK / 16, KB = DV / 16;
+    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const CbChunk ck = cb_chunk(a, bh, c);
+    float qin[NT][4], kin[NT][4];
+    cb_grad_qk<T, DK>(a, ck, wave, qin, kin);
+    lds_barrier();
+    cb_grad_inputs<T, DK, DV>(a, L, ck, true, L.dO);
+    lds_barrier();
+    cb_grad_u_dw<T, DK, DV>(a, L, ck, wave, L.U, L.dW);
+    lds_barrier();
+    cb_grad_mats<T, DK, DV>(a, L, ck, wave, L.dO, L.U);
+    // 3b. the state products, channel tiles over waves
+    floatx4 dQt[NT], dKt[NT], dKh[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int ct = wave + NW * u;
+        dQt[u] = dKt[u] = dKh[u] = floatx4{0, 0, 0, 0};
+        if (ct < RT) {
+            const int cr = 16 * ct + j;
+            float rsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int k0 = 16 * kb;
+                const floatx4 sv = ld4(sglob + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 nv = ld4(nglob + (int64_t)cr * DV + k0 + 4 * g4);
+                cb_grad_block<DV>(L.dO, L.dW, L.U, k0, sv, nv, dQt[u], dKt[u], dKh[u], rsum);
+            }
+            rsum += __shfl_xor(rsum, 16);
+            rsum += __shfl_xor(rsum, 32);
+            if (g4 == 0) L.rs[cr] = rsum;
+        }
+    }
+    lds_barrier();
+    cb_grad_tokens<T, DK, DV>(a, L, ck, wave, qin, kin, dQt, dKt, dKh, L.rs);
+}
+
+// Token gradients of the chunk pair (c0, c1) = (2p, 2p+1) of one chain.  The
+// passes stored the state entering c0 (sglob) and the gradient leaving c1
+// (nglob); c1's entering state is formed from the first, c0's leaving
+// gradient from the second, one 16x16 block at a time where the products
+// need it.  Both chunks' products run in one sweep over the two stored
+// blocks, so each is read from memory once.
+template <typename T, int DK, int DV>
+__device__ __forceinline__ void cb_grad_pair(const CbArgs &a, CbGradLds<DK, DV> &L, int64_t bh,
+                                             int c0, int wave, const float *sglob,
+                                             const float *nglob) {
+    constexpr int RT = DK / 16, KB = DV / 16;
+    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
+    const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+    const CbChunk k0c = cb_chunk(a, bh, c0), k1c = cb_chunk(a, bh, c0 + 1);
+    // c0's U, dW (and its dv) and dO, held for the whole pair
+    cb_grad_inputs<T, DK, DV>(a, L, k0c, false, L.dO1);
+    lds_barrier();
+    cb_grad_u_dw<T, DK, DV>(a, L, k0c, wave, L.U0, L.dW1);
+    // ---- c1: inputs, U and dW, chunk matrices
+    lds_barrier();                               // the steps above are done with X, beta
+    cb_grad_inputs<T, DK, DV>(a, L, k1c, true, L.dO);
+    lds_barrier();
+    cb_grad_u_dw<T, DK, DV>(a, L, k1c, wave, L.U, L.dW);
+    // the K^ rows and e^{b_C} of c0 (c1's entering state), the Q~, K~ rows
+    // and e^{b_C} of c1 (c0's leaving gradient), requested before the barrier
+    CbNeighbour<NT> nbs, nbn;
+    {
+        const float *op0 = a.ops + k0c.unit * cb_ops_floats(DK);
+        const float *op1 = a.ops + k1c.unit * cb_ops_floats(DK);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
+            nbs.r1[u] = ld4(op0 + kOpKhT * DK + ch * kCB + 4 * g4);   // K^[4 g4 + i][ch]
+            nbs.e[u] = op0[kOpEbc * DK + ch];
+            nbn.r1[u] = ld4(op1 + kOpQtT * DK + ch * kCB + 4 * g4);   // Q~[4 g4 + i][ch]
+            nbn.r2[u] = ld4(op1 + kOpKtT * DK + ch * kCB + 4 * g4);   // K~[4 g4 + i][ch]
+            nbn.e[u] = op1[kOpEbc * DK + ch];
+        }
+    }
+    lds_barrier();
+    cb_grad_mats<T, DK, DV>(a, L, k1c, wave, L.dO, L.U);
+    // ---- 3b of both chunks, channel tiles over waves
+    floatx4 dQt1[NT], dKt1[NT], dKh1[NT], dQt0[NT], dKt0[NT], dKh0[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int ct = wave + NW * u;
+        dQt1[u] = dKt1[u] = dKh1[u] = dQt0[u] = dKt0[u] = dKh0[u] = floatx4{0, 0, 0, 0};
+        if (ct < RT) {
+            const int cr = 16 * ct + j;
+            float rsum1 = 0.f, rsum0 = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int k0 = 16 * kb;
+                const floatx4 sv = ld4(sglob + (int64_t)cr * DV + k0 + 4 * g4);
+                const floatx4 nv = ld4(nglob + (int64_t)cr * DV + k0 + 4 * g4);
+                // c1: the state entering it, Diag(e^{b_C}) S + K^^T U of c0
+                // (transposed form: rows of the block are value columns,
+                // columns key channels, as sv is laid out)
+                floatx4 sv1 = sv * nbs.e[u];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv1 = mfma1(L.U0[4 * g4 + i][k0 + j], nbs.r1[u][i], sv1);
+                cb_grad_block<DV>(L.dO, L.dW, L.U, k0, sv1, nv, dQt1[u], dKt1[u], dKh1[u], rsum1);
+                // c0: the gradient leaving it, Diag(e^{b_C}) dN + Q~^T dO - K~^T dW of c1
+                floatx4 nv0 = nv * nbn.e[u];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    nv0 = mfma1(L.dO[4 * g4 + i][k0 + j], nbn.r1[u][i], nv0);
+                    nv0 = mfma1(-L.dW[4 * g4 + i][k0 + j], nbn.r2[u][i], nv0);
+                }
+                cb_grad_block<DV>(L.dO1, L.dW1, L.U0, k0, sv, nv0, dQt0[u], dKt0[u], dKh0[u], rsum0);
+            }
+            rsum1 += __shfl_xor(rsum1, 16);
+            rsum1 += __shfl_xor(rsum1, 32);
+            rsum0 += __shfl_xor(rsum0, 16);
+            rsum0 += __shfl_xor(rsum0, 32);
+            if (g4 == 0) {
+                L.rs[cr] = rsum1;
+                L.rs0[cr] = rsum0;
+            }
+        }
+    }
+    float qin[NT][4], kin[NT][4];
+    cb_grad_qk<T, DK>(a, k1c, wave, qin, kin);
+    lds_barrier();
+    cb_grad_tokens<T, DK, DV>(a, L, k1c, wave, qin, kin, dQt1, dKt1, dKh1, L.rs);
+    // ---- c0: inputs but dO (held since the start), chunk matrices, tokens
+    cb_grad_qk<T, DK>(a, k0c, wave, qin, kin);
+    lds_barrier();                               // c1's tokens are done with the chunk arrays
+    cb_grad_inputs<T, DK, DV>(a, L, k0c, true, nullptr);
+    lds_barrier();
+    cb_grad_mats<T, DK, DV>(a, L, k0c, wave, L.dO1, L.U0);
+    lds_barrier();
+    cb_grad_tokens<T, DK, DV>(a, L, k0c, wave, qin, kin, dQt0, dKt0, dKh0, L.rs0);
+}
+
+// Token gradients of the chunk pair (2p, 2p+1) of one chain, or of the last
+// chunk alone when the chain's chunk count is odd.  The passes stored the
+// state entering chunk 2p and the gradient leaving chunk 2p+1 (or 2p when it
+// is the last chunk).
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(cb_grad_waves<DK>() * 64) void cb_grad_kernel(CbArgs a) {
     using Lds = CbGradLds<DK, DV>;
-    constexpr int RT = DK / 16, CT = DV / 16;
-    constexpr int NW = cb_grad_waves<DK>(), NT = cb_grad_tiles<DK>();
     __shared__ Lds L;
     const int64_t pair = blockIdx.x;
     const int64_t bh = pair / a.np;
-    const int c0 = 2 * (int)(pair % a.np), c1 = c0 + 1;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane & 15, g4 = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = 2 * (int)(pair % a.np);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float *stp = a.st + pair * DK * DV;
     const float *dnp = a.dn + pair * DK * DV;
-    CbNeighbour<NT> nb;
-    if (c1 >= a.nc) {
-        cb_grad_chunk<T, DK, DV, kCbPlain>(a, L, bh, c0, wave, stp, dnp, nb);
-        return;
-    }
-    // U of chunk c0 (full: c1 follows it) into L.U0; its K^ rows and e^{b_C}
-    const int64_t rb = cb_rowbase(a, bh);
-    {
-        const int64_t unit0 = bh * a.nc + c0;
-        const float *wc = a.w + unit0 * kCB * DV;
-        const float *mc = a.mat + unit0 * kCbMat;
-        if (tid < kCB * kCB) L.X[tid >> 4][tid & 15] = mc[tid];
-        if (tid < kCB) L.bet[tid] = cb_ld<T>(a.beta, rb + ((int64_t)c0 * kCB + tid) * a.H);
-        lds_barrier();
-        for (int ct = wave; ct < CT; ct += NW) {
-            const int cc = 16 * ct + j;
-            floatx4 U = {0, 0, 0, 0};
-            const floatx4 xr = ld4(&L.X[j][4 * g4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                U = mfma1(xr[i], L.bet[4 * g4 + i] * wc[(4 * g4 + i) * DV + cc], U);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) L.U0[4 * g4 + i][cc] = U[i];
-        }
-        const float *op = a.ops + unit0 * cb_ops_floats(DK);
-#pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
-            nb.r1[u] = ld4(op + kOpKhT * DK + ch * kCB + 4 * g4);   // K^[4 g4 + i][ch]
-            nb.e[u] = op[kOpEbc * DK + ch];
-        }
-    }
-    cb_grad_chunk<T, DK, DV, kCbSFromPrev>(a, L, bh, c1, wave, stp, dnp, nb);
-    // keep chunk c1's dO and dW for chunk c0; its Q~, K~ rows and e^{b_C}
-    lds_barrier();
-    for (int e = tid; e < kCB * DV; e += NW * 64) {
-        const int r = e / DV, cc = e % DV;
-        L.dO1[r][cc] = L.dO[r][cc];
-        L.dW1[r][cc] = L.dW[r][cc];
-    }
-    {
-        const float *op = a.ops + (bh * a.nc + c1) * cb_ops_floats(DK);
-#pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            const int ch = 16 * (wave + NW * u < RT ? wave + NW * u : 0) + j;
-            nb.r1[u] = ld4(op + kOpQtT * DK + ch * kCB + 4 * g4);   // Q~[4 g4 + i][ch]
-            nb.r2[u] = ld4(op + kOpKtT * DK + ch * kCB + 4 * g4);   // K~[4 g4 + i][ch]
-            nb.e[u] = op[kOpEbc * DK + ch];
-        }
-    }
-    cb_grad_chunk<T, DK, DV, kCbNFromNext>(a, L, bh, c0, wave, stp, dnp, nb);
+    if (c0 + 1 >= a.nc) cb_grad_single<T, DK, DV>(a, L, bh, c0, wave, stp, dnp);
+    else cb_grad_pair<T, DK, DV>(a, L, bh, c0, wave, stp, dnp);
 }
 
 // Workspace of one launch over T tokens: the snapshots of even chunks' states
