@@ -796,6 +796,80 @@ def sq_cmd(i):
             "--no-cpu-baseline --no-parity --no-extras")
 
 
+BWD_COUNTERS_MD = os.path.join(ROOT, "profiles", "counters_backward_b4h32t32k.md")
+BWD_PMC_PASSES = SQ_PASSES + ("FETCH_SIZE", "WRITE_SIZE")
+BWD_LAUNCHES = (("prep", "cb_prep_kernel"), ("forward pass", "cb_fwd_kernel"),
+                ("reverse pass", "cb_bwd_kernel"), ("gradients", "cb_grad_kernel"))
+
+
+def bwd_pmc_cmd(i):
+    return (f"rocprofv3 --pmc {BWD_PMC_PASSES[i]} --output-format csv -d gpurun_out/bwd_pmc{i} -- "
+            "python3 -u bench.py --only backward")
+
+
+def _copy_factors():
+    """FETCH_SIZE / WRITE_SIZE scale factors recorded with the HBM traffic profile."""
+    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_MD).read(), re.S)
+    cf = json.loads(m.group(1))["copy_factor"]
+    return {"FETCH_SIZE": cf["fetch"], "WRITE_SIZE": cf["write"]}
+
+
+def ingest_backward_counters(dirs):
+    """Counters of the chunked backward's four launches (bench.py --only
+    backward).  Its first calls use the whole-sequence workspace (3 warm-up,
+    5 timed); each launch's first 8 dispatches are those calls, and the last
+    5 of them are averaged."""
+    cal = _copy_factors()
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = {}
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (f, int(r["Dispatch_Id"]))
+                    ent = rows.setdefault(key, {"name": r["Kernel_Name"], "t": int(r["Start_Timestamp"]), "c": {}})
+                    ent["c"][r["Counter_Name"]] = ent["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        disp = sorted(rows.values(), key=lambda e: e["t"])
+        for label, frag in BWD_LAUNCHES:
+            mine = [e for e in disp if frag in e["name"]][:8][-5:]
+            for e in mine:
+                for ctr, v in e["c"].items():
+                    vals.setdefault(label, {}).setdefault(ctr, []).append(v)
+    avg = {l: {c: sum(v) / len(v) for c, v in cs.items()} for l, cs in vals.items()}
+    lines = ["# Counters of the chunked backward's launches (rocprofv3 --pmc)", "",
+             "Workload: kda_chunk_bwd on B4 H32 T32768 d128 bf16 (heads 16-31 decay-stress), "
+             "whole-sequence workspace; per launch, the average of the 5 timed calls after 3 "
+             "warm-up ones.  FETCH_SIZE and WRITE_SIZE are scaled by the copy calibration of "
+             f"the HBM traffic profile (fetch {cal['FETCH_SIZE']:.4f}, write {cal['WRITE_SIZE']:.4f}).  "
+             f"Shares are of every SIMD's cycles ({N_SIMD} SIMDs; kernel cycles = "
+             f"SQ_BUSY_CYCLES / {N_SE} shader engines).", "",
+             "Commands (from the repository root):", ""]
+    lines += ["    " + bwd_pmc_cmd(i) for i in range(len(BWD_PMC_PASSES))]
+    lines += ["    python3 bench.py --ingest-backward-counters " +
+              " ".join(f"gpurun_out/bwd_pmc{i}" for i in range(len(BWD_PMC_PASSES))), "",
+              "| launch | fetch (GB) | write (GB) | kernel cycles | VALU active | MFMA busy | "
+              "wave time waiting | LDS bank-conflict cycles per LDS instruction |",
+              "|---|---|---|---|---|---|---|---|"]
+    for label, _ in BWD_LAUNCHES:
+        c = avg.get(label, {})
+        f = c.get("FETCH_SIZE", float("nan")) * 1024 * cal["FETCH_SIZE"] / 1e9
+        w = c.get("WRITE_SIZE", float("nan")) * 1024 * cal["WRITE_SIZE"] / 1e9
+        cyc = c.get("SQ_BUSY_CYCLES", float("nan")) / N_SE
+        va = 4 * c.get("SQ_ACTIVE_INST_VALU", float("nan")) / (cyc * N_SIMD)
+        mb = c.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (cyc * N_SIMD)
+        wt = c.get("SQ_WAIT_ANY", float("nan")) / c.get("SQ_WAVE_CYCLES", float("nan"))
+        bc = c.get("SQ_LDS_BANK_CONFLICT", float("nan")) / c.get("SQ_INSTS_LDS", float("nan"))
+        lines.append(f"| {label} | {f:.2f} | {w:.2f} | {cyc:.4g} | {va:.3f} | {mb:.3f} | {wt:.3f} | {bc:.2f} |")
+    lines.append("")
+    os.makedirs(os.path.dirname(BWD_COUNTERS_MD), exist_ok=True)
+    with open(BWD_COUNTERS_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def ingest_sq(dirs):
     """Shader-sequencer counters of chunk32_kernel on the benchmark workload,
     averaged per dispatch, and unit-free figures per SIMD and 32-token period."""
@@ -890,6 +964,7 @@ def main():
     ap.add_argument("--ingest-trace", metavar="TRACE_DIR")
     ap.add_argument("--ingest-trace-extra", nargs=2, metavar=("NAME", "TRACE_DIR"))
     ap.add_argument("--ingest-sq", nargs="+", metavar="PMC_DIR")
+    ap.add_argument("--ingest-backward-counters", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--only", choices=("long", "pairwise", "backward", "small"),
                     help="time only one extra line and print its record")
     args = ap.parse_args()
@@ -904,6 +979,9 @@ def main():
         return
     if args.ingest_sq:
         ingest_sq(args.ingest_sq)
+        return
+    if args.ingest_backward_counters:
+        ingest_backward_counters(args.ingest_backward_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
