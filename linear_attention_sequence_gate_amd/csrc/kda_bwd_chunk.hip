@@ -37,11 +37,14 @@
 //   cb_prep_kernel   per chunk: At, P, X (16x16 each) and the decayed
 //                    operands K~, K^, Q~, e^{b_C} to the workspace
 //   cb_fwd_kernel    per (chain, 32-column slice), chunks in order: the state
-//                    entering each chunk and W to the workspace
-//   cb_bwd_kernel    per (chain, slice), chunks in reverse: dN of each chunk,
-//                    dU, and d(initial state)
-//   cb_grad_kernel   one workgroup per chunk, all chunks at once: every
-//                    token gradient from (S, dN, W, dU, At, X)
+//                    entering each even chunk and W of every chunk to the
+//                    workspace
+//   cb_bwd_kernel    per (chain, slice), chunks in reverse: dN leaving each
+//                    odd chunk (and the last), dU of every chunk, and
+//                    d(initial state)
+//   cb_grad_kernel   one workgroup per chunk pair, all pairs at once: every
+//                    token gradient from (S, dN, W, dU, At, X), the pair's
+//                    state products in one sweep over its two stored tiles
 // The two passes carry their state slice in MFMA accumulator registers (lane
 // l holds rows 4(l/16)+i, column l%16 of each 16x16 tile), which is also a
 // valid B operand of the next product once the contraction index is taken in
