@@ -41,6 +41,31 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ z,
         return floatx4{expf(a[0]), expf(a[1]), expf(a[2]), expf(a[3])};
     };
     floatx4 ea0 = expA(c0), ea1 = expA(c1);
+    // UNR passes per loop trip when the groups keep their channels: every
+    // pass's loads are issued before any pass is computed, so each thread
+    // keeps 2 UNR loads in flight
+    constexpr int UNR = 2;
+    if (dstep == 0) {
+        for (; q + (UNR - 1) * step + 64 < n4; q += UNR * step) {
+            floatx4 z0[UNR], z1[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                z0[u] = load4(z + 4 * (q + u * step));
+                z1[u] = load4(z + 4 * (q + u * step + 64));
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                floatx4 g0, g1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g0[j] = gate_value_ea(ea0[j], z0[u][j]);
+                    g1[j] = gate_value_ea(ea1[j], z1[u][j]);
+                }
+                __builtin_nontemporal_store(g0, reinterpret_cast<floatx4 *>(g + 4 * (q + u * step)));
+                __builtin_nontemporal_store(g1, reinterpret_cast<floatx4 *>(g + 4 * (q + u * step + 64)));
+            }
+        }
+    }
     for (; q < n4; q += step) {
         const bool two = q + 64 < n4;
         const floatx4 z0 = load4(z + 4 * q);
