@@ -235,7 +235,8 @@ LONG = inputs.WORKLOADS["prefill_h32_t1m"]
 def time_long_prefill(reps=3):
     """kda_chunk_fwd_gated (gate and chunked prefill, as the main step) on the
     few-chain long workload (B1 H32 T1M: 64 workgroups in one pass) in one
-    pass and with the library's sequence split."""
+    pass, with the library's sequence split, and with the split whose last
+    phase reruns whole segments (KDA_FLAG_SPLIT_FULL_RERUN), in that order."""
     w = LONG
     dev = torch.device("cuda")
     x = inputs.workload_prefill_inputs(w, device=dev)
@@ -246,11 +247,11 @@ def time_long_prefill(reps=3):
                      device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
     out = {}
-    for label, n in (("one_pass", 1), ("split", nseg)):
+    for label, fl in (("one_pass", _lib.kda_flag_segments(1)), ("split", 0),
+                      ("split_full_rerun", _lib.KDA_FLAG_SPLIT_FULL_RERUN)):
         def run():
             _lib.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
-                                     final_state=ST, o=o, workspace=ws,
-                                     flags=_lib.kda_flag_segments(n), stream=stream)
+                                     final_state=ST, o=o, workspace=ws, flags=fl, stream=stream)
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -609,11 +610,13 @@ EXTRA_TRACES = {
     # name: (bench.py --only value, profile file, what the run holds)
     "long": ("long", "kernel_trace_prefill_b1h32t1m_split.md",
              "kda_chunk_fwd_gated (the gate fused into the chunk kernel) on B1 H32 T1048576 "
-             "d128 bf16 in one pass (1 warm-up + 3 timed calls) and with the library's "
-             "sequence split (the same). "
-             "A split call is three launches: chunk32_kernel phase 1 (segment 0, the middle "
-             "segments from zero and their transitions), seg_chain_kernel, and chunk32_kernel "
-             "phase 3 (segments 1..P-1); the workgroup count tells the launches apart."),
+             "d128 bf16 in one pass (1 warm-up + 3 timed calls), with the library's "
+             "sequence split (the same; P = 4), and with KDA_FLAG_SPLIT_FULL_RERUN (the same; "
+             "P = 5). A split call is three launches: chunk32_kernel phase 1 (the segments "
+             "from their start states, the transitions of segments 1..P-1; the full rerun "
+             "leaves the last segment out), seg_chain_kernel, and chunk32_kernel phase 3 "
+             "(segments 1..P-1: up to where their transitions vanished, or whole with the "
+             "full rerun); the mode and the workgroup count tell the launches apart."),
     "backward": ("backward", "kernel_trace_backward_b4h32t32k.md",
                  "kda_gate once, then kda_chunk_bwd on B4 H32 T32768 d128 bf16 (heads 16-31 "
                  "decay-stress): the chunked path with the whole-sequence workspace (3 warm-up + 5 "
@@ -627,11 +630,12 @@ EXTRA_TRACES = {
                  "bwd_ckpt_kernel, bwd_kernel, bwd_sum_kernel) and kda_gate_bwd."),
     "small": ("small", "kernel_trace_prefill_b1h8t4096_split.md",
               "kda_chunk_fwd_gated on B1 H8 T4096 d128 bf16 with the library's automatic "
-              "sequence split (9 segments of 480 tokens), inputs rotated over five copies (10 "
+              "sequence split (11 segments of 384 tokens), inputs rotated over five copies (10 "
               "warm-up + 20 timed calls).  A call is three launches: chunk32_kernel phase 1 "
-              "(segment 0, the middle segments from zero and their transitions), "
-              "seg_chain_kernel (serial chaining), chunk32_kernel phase 3 (segments 1..8); the "
-              "workgroup count tells the phases apart."),
+              "(segment 0 from the initial state, segments 1..10 from zero, and their "
+              "transitions), seg_chain_kernel (serial chaining), chunk32_kernel phase 3 "
+              "(segments 1..10 up to where their transitions vanished); the workgroup count "
+              "tells the phases apart."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "
                  "MFMA diagonal tiles (5 warm-up + 5 timed calls) and with the position-pair "
@@ -730,6 +734,17 @@ def ingest_trace_extra(name, d):
         label = ""
         if name == "pairwise" and r in chunk_rows:
             label = "dense" if chunk_rows.index(r) < len(chunk_rows) // 2 else "position pairs"
+        if name == "long":
+            # one pass first (the first launch's grid), then the two split
+            # schemes with the same number of launches each
+            first = int(chunk_rows[0]["Grid_Size_X"])
+            split_rows = [x for x in rows if int(x["Grid_Size_X"]) != first
+                          or "chunk32_kernel" not in x["Kernel_Name"]]
+            if r not in split_rows:
+                label = "one pass"
+            else:
+                label = ("stopping split" if split_rows.index(r) < len(split_rows) // 2
+                         else "full rerun")
         if name == "backward" and "cb_" in kname:
             # the chunked path's launches belong to the call (whole sequence or
             # one segment) whose prep launch, with one workgroup per chunk,

@@ -87,7 +87,13 @@ enum {
     /* kda_chunk_bwd only: take the token-level reverse mode, which assumes
      * nothing about the decay range (any g <= 0), instead of the chunked one.
      * Slower. */
-    KDA_FLAG_TOKEN_BACKWARD = 0x10000u
+    KDA_FLAG_TOKEN_BACKWARD = 0x10000u,
+    /* Sequence split: rerun every segment after the first in full in the
+     * last phase, instead of only its chunks up to the point where the
+     * segment's transition became exactly zero (see kda_chunk_fwd).  Faster
+     * when the gates keep memory over more than about half a segment; the
+     * segment count is then chosen for this scheme. */
+    KDA_FLAG_SPLIT_FULL_RERUN = 0x20000u
 };
 #define KDA_FLAG_SEGMENTS(n) ((unsigned)(n) << KDA_FLAG_SEGMENTS_SHIFT)
 
@@ -140,15 +146,17 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
 
 /*
  * Segments per sequence kda_chunk_fwd uses for these sizes when the flags
- * leave the choice to the library (1 = one pass); 0 for invalid sizes.
+ * leave the choice to the library and do not set KDA_FLAG_SPLIT_FULL_RERUN
+ * (1 = one pass); 0 for invalid sizes.
  */
 int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H,
                                 int64_t dk, int64_t dv, int dtype);
 
 /*
  * As kda_chunk_fwd_workspace_size for an explicit segment count (the value
- * of the KDA_FLAG_SEGMENTS bits: 0 = the library's choice, 1 = no split).
- * Returns 0 for invalid sizes or a count above 255.
+ * of the KDA_FLAG_SEGMENTS bits: 0 = the library's choice with or without
+ * KDA_FLAG_SPLIT_FULL_RERUN, 1 = no split).  Returns 0 for invalid sizes or
+ * a count above 255.
  */
 size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
                                              int64_t dk, int64_t dv, int dtype, int nseg);
@@ -184,14 +192,23 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
  * plus the chaining steps).  The recurrence is affine in the
  * state, S_end = M S_start + L, so three stream-ordered launches give the
  * same result as one pass up to fp32 rounding:
- *   1. segment 0 from initial_state (its o is final); every middle segment
- *      from a zero state (L) and its transition M (v = 0, identity start);
+ *   1. segment 0 from initial_state (its o is final); every other segment
+ *      from a zero state (L, and its o) and its transition M (v = 0,
+ *      identity start), noting the chunk after which M is exactly zero;
  *   2. the segments' initial states, chained as M S + L;
  *   3. segments 1 .. P-1 again from their initial states, writing o and
- *      (last segment) final_state.
- * The library picks P; KDA_FLAG_SEGMENTS(n) forces it (tests).  The split
- * uses the workspace; without one large enough, the automatic choice falls
- * back to one pass.
+ *      (last segment) final_state, up to that chunk only: from there on
+ *      the incoming state's image M S is zero (the decay of every channel
+ *      has underflowed fp32), so the zero-start o of step 1 stands and the
+ *      last segment's final state is its L.
+ * How far step 3 runs depends on the gates: a chunk or two when every
+ * channel decays fast, the whole segment when some channel keeps memory
+ * past its end (KDA_FLAG_SPLIT_FULL_RERUN then picks a count for that case
+ * and leaves the last segment out of step 1).  The outputs computed in
+ * step 3 and those kept from step 1 each agree with one pass to fp32
+ * rounding.  The library picks P; KDA_FLAG_SEGMENTS(n) forces it (tests).
+ * The split uses the workspace; without one large enough, the automatic
+ * choice falls back to one pass.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   const void *beta, const float *initial_state, float *final_state,

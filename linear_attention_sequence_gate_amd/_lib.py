@@ -27,6 +27,7 @@ KDA_FLAG_PAIRWISE_DIAGONAL = 2
 KDA_FLAG_SEGMENTS_SHIFT = 8
 KDA_FLAG_SEGMENTS_MASK = 0xFF00
 KDA_FLAG_TOKEN_BACKWARD = 0x10000
+KDA_FLAG_SPLIT_FULL_RERUN = 0x20000
 
 
 def kda_flag_segments(n: int) -> int:

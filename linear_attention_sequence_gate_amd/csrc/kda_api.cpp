@@ -152,16 +152,25 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H, in
     if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (nseg < 0 || nseg > 255) return 0;
-    if (nseg == 0) nseg = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16);
-    if (nseg < 2 || !kda::seq_split_supported((int)dk, (int)dv, dtype == KDA_BF16)) return kCounterBytes;
-    return kCounterBytes + kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, nseg);
+    const bool bf = dtype == KDA_BF16;
+    if (!kda::seq_split_supported((int)dk, (int)dv, bf)) return kCounterBytes;
+    if (nseg != 0) return kCounterBytes + (nseg >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, nseg) : 0);
+    // the library's count, for either scheme (with and without
+    // KDA_FLAG_SPLIT_FULL_RERUN): the same layout, sized for the larger
+    size_t ws = 0;
+    for (int rerun = 0; rerun < 2; ++rerun) {
+        const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, bf, rerun);
+        const size_t w = P >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, P) : 0;
+        if (w > ws) ws = w;
+    }
+    return kCounterBytes + ws;
 }
 
 int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                 int dtype) {
     if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
-    const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16);
+    const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16, 0);
     return P >= 2 ? kda::seq_split_effective(T, P) : 1;
 }
 
@@ -214,7 +223,8 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
                     (long long)dk, (long long)dv);
     if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
         return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs support dk in {32,64} only", who);
-    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK))
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK |
+                          KDA_FLAG_SPLIT_FULL_RERUN))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
     const bool is_bf16 = dtype == KDA_BF16;
     const bool pairwise = (flags & KDA_FLAG_PAIRWISE_DIAGONAL) != 0;
@@ -286,7 +296,8 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     }
     // sequence split: requested, or picked for these sizes when the workspace
     // holds its buffers (else one pass)
-    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16) : req_seg;
+    const int rerun = (flags & KDA_FLAG_SPLIT_FULL_RERUN) ? 1 : 0;
+    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16, rerun) : req_seg;
     void *split_ws = nullptr;
     if (nseg >= 2) {
         const size_t need = kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, nseg);
@@ -301,7 +312,7 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
                                          (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
                                          pairwise ? 1 : 0, cu_seqlens, fused ? z : nullptr,
-                                         fused ? Ag : nullptr, s);
+                                         fused ? Ag : nullptr, rerun, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }

@@ -68,9 +68,16 @@ struct ChunkArgs {
     //            nsl_v.. run the dk columns of the transition (v = 0, initial
     //            state I) into Mb[p-1]
     //   phase 3: segments p >= 1 from Sin[p-1], writing o (and ST for the last)
+    // With zc set (the stopping split) phase 1 covers every segment, writes
+    // the o of segments p >= 1 from their zero start and L of the last one
+    // too, and records in zc[(p-1) nbh + bh][j] the chunk after which
+    // transition slice j was exactly zero; phase 3 then recomputes only the
+    // chunks up to the larger of those (o later in the segment is unchanged by
+    // the incoming state, whose image M S vanished there).
     int64_t seg_len;
     int phase, seg0, nseg, nsl_v;
     float *Sin, *Lb, *Mb;
+    int *zc;
     // state pool: when set, S0 and ST are [n_slots, H, dk, dv] and sequence
     // b uses slot slots[b] (a slot outside the pool skips the sequence)
     const int *slots;
@@ -1033,7 +1040,19 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         T_ = end - tok_base;
     }
     const int64_t tbeg = (int64_t)seg * a.seg_len;
-    const int64_t tend = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
+    const int64_t tseg = tbeg + a.seg_len < T_ ? tbeg + a.seg_len : T_;
+    // the stopping split's last phase: the chunks up to the one after which
+    // the segment's transition vanished (all of them when it never did)
+    int64_t tend = tseg;
+    if (a.phase == 3 && a.zc) {
+        const int *zr = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * (DK / NV);
+        int zl = zr[0];
+#pragma unroll
+        for (int j = 1; j < DK / NV; ++j) zl = zr[j] > zl ? zr[j] : zl;
+        zl = __builtin_amdgcn_readfirstlane(zl);
+        const int64_t tz = tbeg + (int64_t)(zl + 1) * kPipeChunk;
+        if (tz < tend) tend = tz;
+    }
     const int vcol0 = (mcols ? slice - a.nsl_v : slice) * NV;
     const int64_t nchunk = (tend - tbeg + kPipeChunk - 1) / kPipeChunk;
     const bool pw = __builtin_amdgcn_readfirstlane(a.pairwise) != 0;
@@ -1479,22 +1498,28 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         void *ob = a.o;
         int spitch = DV;
         int64_t s0row = urow, strow = urow;         // caller's rows; workspace rows are bh
+        const float *lsrc = nullptr;                // final state copied from L instead
         const bool vzero = mcols;
         if (a.phase == 1) {
             const size_t vsz = (size_t)a.nbh * DK * DV, msz = (size_t)a.nbh * DK * DK;
             if (mcols) {
-                s0 = nullptr; st = a.Mb + (size_t)(seg - 1) * msz; spitch = DK; ob = nullptr;
-                strow = bh;
+                // the stopping split's last segment needs only where its
+                // transition vanishes, not the transition itself
+                s0 = nullptr; st = seg <= a.nseg - 2 ? a.Mb + (size_t)(seg - 1) * msz : nullptr;
+                spitch = DK; ob = nullptr; strow = bh;
             } else if (seg == 0) {
                 st = a.Sin; strow = bh;
             } else {
-                s0 = nullptr; st = a.Lb + (size_t)(seg - 1) * vsz; ob = nullptr;
-                strow = bh;
+                s0 = nullptr; st = a.Lb + (size_t)(seg - 1) * vsz; strow = bh;
+                if (!a.zc) ob = nullptr;            // the stopping split keeps the zero-start o
             }
         } else if (a.phase == 3) {
             s0 = a.Sin + (size_t)(seg - 1) * a.nbh * DK * DV;
             s0row = bh;
             st = seg == a.nseg - 1 ? a.ST : nullptr;
+            // stopped before the end: M of the last segment is zero, so its
+            // final state is the zero-start one, L
+            if (st && tend < tseg) lsrc = a.Lb + (size_t)(seg - 1) * a.nbh * DK * DV;
         }
         const T *__restrict__ vp = static_cast<const T *>(a.v);
         T *__restrict__ op = static_cast<T *>(ob);
@@ -1733,12 +1758,32 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             else return false;
         };
         bool stop = false;
-        for (int64_t c = 0; c <= nchunk + 1 && !stop; c += 2) {
+        int64_t c = 0;
+        for (; c <= nchunk + 1 && !stop; c += 2) {
             stop = period(c, vv0, vv1);
             if (c + 1 <= nchunk + 1) stop |= period(c + 1, vv1, vv0);
         }
         vm_wait<0>();                               // no load outlives the wave
-        if (st) {
+        if constexpr (TRANS) {
+            // the stopping split: a stop in the pair (c - 2, c - 1) saw the
+            // state zero after chunk c - 3 at the latest (the pass of period
+            // c - 1); without a stop every chunk counts
+            if (vzero && a.zc && s == 0 && lane == 0) {
+                const int64_t zl = stop && c - 3 < nchunk - 1 ? c - 3 : nchunk - 1;
+                a.zc[((size_t)(seg - 1) * a.nbh + bh) * (DK / NV) + (slice - a.nsl_v)] = (int)zl;
+            }
+        }
+        if (st && lsrc) {
+            float lv[NCB][4];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lv[cb][j] = lsrc[((size_t)bh * DK + 16 * cb + lg4 + j) * DV + ncol];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[(strow * DK + 16 * cb + lg4 + j) * spitch + ncol] = lv[cb][j];
+        } else if (st) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -2004,18 +2049,45 @@ int seq_split_effective(int64_t T, int nseg) {
     return (int)((T + len - 1) / len);
 }
 
+// Greedy placement of n1 workgroups of duration d1, then n2 of duration d2,
+// on the compute units (one workgroup each): the time the last one ends.  The
+// second kind fills the units the first kind's last partial round leaves,
+// then every unit.
+static double split_phase_time(int64_t n1, double d1, int64_t n2, double d2) {
+    constexpr int64_t kCUs = 256;             // MI355X compute units
+    const int64_t r1 = n1 / kCUs, rem = n1 % kCUs;
+    const double t = (double)r1 * d1;
+    auto rounds = [](int64_t w) { return (double)((w + kCUs - 1) / kCUs); };
+    if (n2 == 0) return rem ? t + d1 : t;
+    if (rem == 0) return t + rounds(n2) * d2;
+    const int64_t freecu = kCUs - rem, k = (int64_t)(d1 / d2);
+    if (k * freecu >= n2) {
+        const double t2 = t + (double)((n2 + freecu - 1) / freecu) * d2;
+        return t2 > t + d1 ? t2 : t + d1;
+    }
+    return t + d1 + rounds(n2 - k * freecu) * d2;
+}
+
 // The count minimising a model of the wall time, fitted to measured sweeps
-// of forced counts (B1 H8 T4096 and B1 H32 T1M: every point within 2%).
-// A launch of W workgroups runs ceil(W / CUs) rounds of one segment, and a
-// segment of n tokens costs n + 64 token-times (the pipeline's two fill
-// periods); a split adds 33 token-times per chaining step and 145 for its
-// extra launches.
-int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16) {
+// of forced counts (B1 H8 T4096 and B1 H32 T1M).  A segment of n tokens
+// costs n + 64 token-times (the pipeline's two fill periods); a split adds 33
+// token-times per chaining step and 145 for its extra launches.
+//  - Full rerun: a launch of W workgroups runs ceil(W / CUs) rounds of one
+//    segment (transitions priced at a whole segment).
+//  - Stopping split (the default): phase 1 places the v workgroups of all P
+//    segments, then the transitions; the transitions and phase 3 are priced
+//    as ending a quarter of the way into a segment (at least two chunks),
+//    an assumption about the gates: the transition vanishes once every
+//    channel's cumulative decay has underflowed, which synthetic gates of
+//    the pages' range reach within a chunk or two and gates that keep
+//    memory reach later or never (phase 3 then reruns the whole segment).
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun) {
     constexpr int64_t kCUs = 256;             // MI355X compute units
     constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
     constexpr int64_t kFillTokens = 64;       // two pipeline periods per segment
     constexpr int64_t kChainStepTokens = 33;  // one chaining step
     constexpr int64_t kSplitTokens = 145;     // the two extra launches
+    constexpr double kVanishFrac = 0.25;      // stopping split: where transitions end
     if (!seq_split_supported(dk, dv, is_bf16)) return 1;
     const int64_t bh = B * H, nsl_v = dv / 64, nsl_m = dk / 64;
     auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
@@ -2024,12 +2096,21 @@ int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16)
     int best_p = 1;
     int64_t pmax = T / kMinSegTokens;
     if (pmax > 255) pmax = 255;
-    for (int P = 3; P <= pmax; ++P) {
+    for (int P = rerun ? 3 : 2; P <= pmax; ++P) {
         const int64_t pe = seq_split_effective(T, P), len = seq_split_segment_len(T, P);
-        if (pe < 3) continue;
-        const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
-        const double cost = (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3)) +
-                            (double)kChainStepTokens * (double)(pe - 2) + (double)kSplitTokens;
+        if (pe < (rerun ? 3 : 2)) continue;
+        double cost = (double)kChainStepTokens * (double)(pe - 2) + (double)kSplitTokens;
+        if (rerun) {
+            const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
+            cost += (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3));
+        } else {
+            double part = kVanishFrac * (double)len;
+            if (part < 2.0 * kPipeChunk) part = 2.0 * kPipeChunk;
+            if (part > (double)len) part = (double)len;
+            const double dseg = (double)(len + kFillTokens), dpart = part + (double)kFillTokens;
+            cost += split_phase_time(bh * nsl_v * pe, dseg, bh * nsl_m * (pe - 1), dpart) +
+                    split_phase_time(bh * nsl_v * (pe - 1), dpart, 0, 0.0);
+        }
         if (cost < best) {
             best = cost;
             best_p = P;
@@ -2038,14 +2119,31 @@ int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16)
     return best_p;
 }
 
+// Workspace of a P-segment split (either scheme), in this order: Sin
+// (P - 1 states), Lb (P - 1), Mb (P - 2 transitions), the log-depth
+// chaining's second M buffer when it is used (L ping-pongs through the Sin
+// slots it fills last), and the stopping split's chunk records (P - 1 ints
+// per chain and transition slice).
+struct SplitLayout {
+    size_t sin, lb, mb, scan, zc, total;     // float offsets (zc: byte offset), total bytes
+};
+static SplitLayout seq_split_layout(int64_t nbh, int P, int dk, int dv) {
+    const size_t vsz = (size_t)nbh * dk * dv, msz = (size_t)nbh * dk * dk;
+    const size_t nscan = seq_split_log_chain(nbh, P, dk, dv) ? (size_t)(P - 2) * msz : 0;
+    SplitLayout l;
+    l.sin = 0;
+    l.lb = l.sin + (size_t)(P - 1) * vsz;
+    l.mb = l.lb + (size_t)(P - 1) * vsz;
+    l.scan = l.mb + (size_t)(P - 2) * msz;
+    l.zc = (l.scan + nscan) * 4;
+    l.total = l.zc + ((size_t)(P - 1) * nbh * (dk / 64) * 4 + 255) / 256 * 256;
+    return l;
+}
+
 size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg) {
     const int P = seq_split_effective(T, nseg);
     if (P < 2) return 0;
-    const size_t vsz = (size_t)B * H * dk * dv * 4, msz = (size_t)B * H * dk * dk * 4;
-    // the log-depth chaining ping-pongs M through a second buffer (L through
-    // the Sin slots it fills last)
-    const size_t scan = seq_split_log_chain(B * H, P, dk, dv) ? (size_t)(P - 2) * msz : 0;
-    return (size_t)(P - 1) * vsz + (size_t)(P - 2) * (vsz + msz) + scan;
+    return seq_split_layout(B * H, P, dk, dv).total;
 }
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -2053,7 +2151,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            hipStream_t s) {
+                            int split_rerun, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
@@ -2072,6 +2170,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.xcd_map = (args.nbh % 8 == 0) ? 1 : 0;
     args.seg_len = T; args.phase = 0; args.seg0 = 0; args.nseg = 1; args.nsl_v = args.nslice;
     args.Sin = args.Lb = args.Mb = nullptr;
+    args.zc = nullptr;
     args.slots = slots;
     args.n_slots = n_slots;
     args.pairwise = pipe && pairwise ? 1 : 0;
@@ -2082,26 +2181,32 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
     if (pipe && P >= 2) {
         if (!split_ws) return hipErrorInvalidValue;
-        const size_t vsz = (size_t)args.nbh * dk * dv;
-        args.Sin = static_cast<float *>(split_ws);
-        args.Lb = args.Sin + (size_t)(P - 1) * vsz;
-        args.Mb = args.Lb + (size_t)(P - 2) * vsz;
+        const SplitLayout lay = seq_split_layout(args.nbh, P, dk, dv);
+        float *wsf = static_cast<float *>(split_ws);
+        args.Sin = wsf + lay.sin;
+        args.Lb = wsf + lay.lb;
+        args.Mb = wsf + lay.mb;
+        // the stopping split (the default) or the full rerun of segments
+        // 1 .. P-1 in the last phase
+        args.zc = split_rerun ? nullptr
+                              : reinterpret_cast<int *>(static_cast<char *>(split_ws) + lay.zc);
         args.seg_len = seq_split_segment_len(T, P);
         args.nseg = P;
-        // first phase: segment 0 from S0; segments 1 .. P-2 from zero, plus
-        // their transitions (the last segment needs neither)
-        const int units = (P - 1) * args.nbh;
+        // first phase: segment 0 from S0; the others from zero, plus their
+        // transitions (the full rerun leaves out the last segment, whose L
+        // and M it never uses)
+        const int units1 = (split_rerun ? P - 1 : P) * args.nbh;
         args.phase = 1;
         args.nslice = args.nsl_v + dk / 64;
-        args.xcd_map = units % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(kern_tr, dim3(units * args.nslice), dim3(768), 0, s, args);
+        args.xcd_map = units1 % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(kern_tr, dim3(units1 * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (P >= 3 && seq_split_log_chain(args.nbh, P, dk, dv)) {
             // log-depth: scan levels ping-pong M between Mb and the buffer
             // after it, L between Lb and Sin[1..]; then Sin[p] = G_p(Sin[0])
             const int64_t nx = (int64_t)args.nbh * (P - 2);
-            float *Mbuf[2] = {args.Mb, args.Mb + (size_t)nx * dk * dk};
+            float *Mbuf[2] = {args.Mb, wsf + lay.scan};
             float *Lbuf[2] = {args.Lb, args.Sin + (size_t)args.nbh * dk * dv};
             int cur = 0;
             for (int64_t shift = args.nbh; shift < nx; shift *= 2) {
@@ -2121,10 +2226,12 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
             if (e != hipSuccess) return e;
         }
         // last phase: segments 1 .. P-1 from their true initial states
+        const int units3 = (P - 1) * args.nbh;
         args.phase = 3;
         args.seg0 = 1;
         args.nslice = args.nsl_v;
-        hipLaunchKernelGGL(kern, dim3(units * args.nslice), dim3(768), 0, s, args);
+        args.xcd_map = units3 % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(kern, dim3(units3 * args.nslice), dim3(768), 0, s, args);
         return hipGetLastError();
     }
     const int nblocks = args.nbh * args.nslice;

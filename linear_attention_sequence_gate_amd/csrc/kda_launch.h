@@ -28,7 +28,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            hipStream_t s);
+                            int split_rerun, hipStream_t s);
 
 // Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
 bool seq_split_supported(int dk, int dv, int is_bf16);
@@ -36,8 +36,9 @@ bool seq_split_supported(int dk, int dv, int is_bf16);
 // number of segments that length gives.
 int64_t seq_split_segment_len(int64_t T, int nseg);
 int seq_split_effective(int64_t T, int nseg);
-// Segment count picked for these sizes (1 = no split).
-int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16);
+// Segment count picked for these sizes (1 = no split), for the stopping
+// split or (rerun) the one whose last phase reruns whole segments.
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun);
 // Device bytes the split needs (0 when it does not split).
 size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg);
 

@@ -85,6 +85,8 @@ def test_chunk_validation(L):
     assert chunk(L, k=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
     assert chunk(L, o=P) == E.KDA_ERR_INVALID_ARGUMENT            # o aliases q
     assert chunk(L, flags=4) == E.KDA_ERR_INVALID_ARGUMENT        # unknown flag
+    assert chunk(L, flags=E.KDA_FLAG_SPLIT_FULL_RERUN << 1) == E.KDA_ERR_INVALID_ARGUMENT
+    assert chunk(L, flags=E.KDA_FLAG_TOKEN_BACKWARD) == E.KDA_ERR_INVALID_ARGUMENT   # backward only
     assert chunk(L, flags=E.KDA_FLAG_PAIRWISE_DIAGONAL) == E.KDA_ERR_UNSUPPORTED   # dk = 32
     assert "position-pair" in _lib.kda_last_error()
     assert chunk(L, dk=128, dv=128, flags=E.KDA_FLAG_PAIRWISE_DIAGONAL | E.KDA_FLAG_CHECK_RANGE,
@@ -107,30 +109,41 @@ def test_sequence_split_workspace_and_policy(L):
     auto = L.kda_chunk_fwd_auto_segments
 
     def split_bytes(B, H, dv, P, scan=False):
-        # (P-1) initial states, (P-2) zero-start states + transitions, and with
-        # the log-depth chaining a second buffer of (P-2) transitions
+        # (P-1) initial states, (P-1) zero-start states, (P-2) transitions,
+        # with the log-depth chaining a second buffer of (P-2) transitions,
+        # then one int per (segment after the first, chain, 64 transition
+        # columns) rounded up to 256 bytes
         vsz, msz = B * H * 128 * dv * 4, B * H * 128 * 128 * 4
-        return 256 + (P - 1) * vsz + (P - 2) * (vsz + msz) + (P - 2) * msz * scan
+        zc = -(-(P - 1) * B * H * 2 * 4 // 256) * 256
+        return 256 + 2 * (P - 1) * vsz + (P - 2) * msz + (P - 2) * msz * scan + zc
 
     # B4 H32 T32K: 256 workgroups of 64 columns fill the GPU in one pass
     assert auto(4, 32768, 32, 128, 128, 1) == 1
     assert ws(4, 32768, 32, 128, 128, 1) == 256
     # B1 H32 T1M: 64 workgroups in one pass; the split takes a few segments
+    # (the stopping split: the v workgroups of all segments in one round)
     P = auto(1, 1 << 20, 32, 128, 128, 1)
-    assert 3 <= P <= 9, P
-    assert ws(1, 1 << 20, 32, 128, 128, 1) == split_bytes(1, 32, 128, P)
+    assert P == 4, P
+    # the automatic workspace covers the count of either scheme
+    assert ws(1, 1 << 20, 32, 128, 128, 1) >= split_bytes(1, 32, 128, P)
+    assert ws(1, 1 << 20, 32, 128, 128, 1) in [split_bytes(1, 32, 128, n) for n in range(P, 10)]
     assert wss(1, 1 << 20, 32, 128, 128, 1, 0) == ws(1, 1 << 20, 32, 128, 128, 1)
+    assert wss(1, 1 << 20, 32, 128, 128, 1, P) == split_bytes(1, 32, 128, P)
     # one chain: many more segments
     P1 = auto(1, 1 << 20, 1, 128, 128, 1)
     assert P1 > 4 * P, (P1, P)
-    assert ws(1, 1 << 20, 1, 128, 128, 1) == split_bytes(1, 1, 128, P1, scan=True)
+    assert wss(1, 1 << 20, 1, 128, 128, 1, P1) == split_bytes(1, 1, 128, P1, scan=True)
+    assert ws(1, 1 << 20, 1, 128, 128, 1) >= wss(1, 1 << 20, 1, 128, 128, 1, P1)
     # few chains of a short sequence split too (segments of >= 128 tokens):
     # B1 H8 T4096 runs 16 workgroups in one pass
     P8 = auto(1, 4096, 8, 128, 128, 1)
     assert 3 <= P8 <= 32, P8
-    assert ws(1, 4096, 8, 128, 128, 1) == split_bytes(1, 8, 128, P8)
-    # enough chains to fill the GPU, or too short for three segments: one pass
-    assert auto(8, 4096, 8, 128, 128, 1) == 1
+    assert wss(1, 4096, 8, 128, 128, 1, P8) == split_bytes(1, 8, 128, P8)
+    assert ws(1, 4096, 8, 128, 128, 1) >= split_bytes(1, 8, 128, P8)
+    # half the GPU (128 workgroups): the stopping split's two segments fill it
+    assert auto(8, 4096, 8, 128, 128, 1) == 2
+    # enough chains to fill the GPU, or too short to split: one pass
+    assert auto(16, 4096, 8, 128, 128, 1) == 1
     assert auto(1, 383, 1, 128, 128, 1) == 1 and ws(1, 383, 1, 128, 128, 1) == 256
     # shapes without the pipelined kernel run in one pass
     assert auto(1, 1 << 20, 1, 64, 64, 1) == 1
@@ -240,6 +253,7 @@ def test_backward_validation(L):
         Q[0], Q[1], Q[2], Q[3], Q[4], S0, Q[6], None, dq, Q[9], Q[10], Q[11], Q[12], None,
         ws, wsb, 1, T, 1, dk, 32, dt, flags, None)
     assert bwd(flags=4) == E.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(flags=E.KDA_FLAG_SPLIT_FULL_RERUN) == E.KDA_ERR_INVALID_ARGUMENT   # prefill only
     assert "flag" in _lib.kda_last_error()
     assert bwd(flags=E.KDA_FLAG_TOKEN_BACKWARD | E.KDA_FLAG_CHECK_RANGE) == E.KDA_ERR_INVALID_ARGUMENT
     assert bwd(dq=NULL) == E.KDA_ERR_INVALID_ARGUMENT
@@ -372,3 +386,14 @@ def test_varlen_pooled_gated_validation(L):
     assert f(*args(cu_=NULL)) == E.KDA_ERR_INVALID_ARGUMENT
     assert f(*args(dk=64, dv=64)) == E.KDA_ERR_UNSUPPORTED             # fused shapes only
     assert f(*args(flags=E.KDA_FLAG_CHECK_RANGE)) == E.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_binding_constants_match_the_header():
+    """The binding's error codes and flag bits are the values include/kda.h
+    gives them."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    header = {n: int(v.rstrip("u"), 0)
+              for n, v in re.findall(r"\b(KDA_(?:OK|ERR_\w+|FLAG_\w+))\s*=\s*(-?\w+)", text)}
+    assert len(header) >= 11, header
+    for n, v in header.items():
+        assert getattr(_lib, n) == v, n

@@ -2,7 +2,10 @@
 segments; segment transitions chained as S -> M S + L) against the oracle and
 against the one-pass kernel on the same inputs: forced segment counts with
 ragged last segments, initial states, in-place continuation, the automatic
-choice for a long few-chain input, and determinism."""
+choice for a long few-chain input, and determinism.  Every forced split runs
+both schemes: the default one, whose last phase stops where a segment's
+transition became zero (keeping the first phase's zero-start o after it),
+and KDA_FLAG_SPLIT_FULL_RERUN, whose last phase reruns whole segments."""
 import numpy as np
 import pytest
 import torch
@@ -16,9 +19,26 @@ pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
 
 
-def _split(x, g, nseg, **kw):
+SCHEMES = {"stop": 0, "rerun": _lib.KDA_FLAG_SPLIT_FULL_RERUN}
+
+
+def _split(x, g, nseg, scheme="stop", **kw):
     return kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"],
-                         flags=_lib.kda_flag_segments(nseg), **kw)
+                         flags=_lib.kda_flag_segments(nseg) | SCHEMES[scheme], **kw)
+
+
+def _check_schemes(x, g, nseg, o_ref, S_ref, o_1, S_1):
+    """Both schemes of an nseg split against the oracle and one pass."""
+    for scheme in SCHEMES:
+        o_s, S_s = _split(x, g, nseg, scheme)
+        torch.cuda.synchronize()
+        ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
+        r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
+        print(f"    {scheme}: vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}",
+              flush=True)
+        assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all(), scheme
+        assert ro <= TOL[BF16] and rs <= TOL[BF16], (scheme, ro, rs)
+        assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (scheme, r1o, r1s)
 
 
 @pytest.mark.parametrize("nseg,B,T,H,dv", [
@@ -33,16 +53,10 @@ def test_forced_split_matches_oracle_and_one_pass(nseg, B, T, H, dv):
     x = prefill_device(B, T, H, 128, dv, BF16, 400 + nseg, s0_std=0.02, stress=3.0)
     g_f32 = oracle_gate_f32(x["z"], x["A"])
     g = g_f32.cuda()
-    o_s, S_s = _split(x, g, nseg)
     o_1, S_1 = _split(x, g, 1)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], x["S0"])
-    ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
-    r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
-    print(f"    vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}", flush=True)
-    assert np.isfinite(o_s.float().cpu().numpy()).all()
-    assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
-    assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (r1o, r1s)
+    _check_schemes(x, g, nseg, o_ref, S_ref, o_1, S_1)
 
 
 def test_split_in_place_state_zero_start_and_determinism():
@@ -66,7 +80,7 @@ def test_split_in_place_state_zero_start_and_determinism():
 
 def test_automatic_split_for_a_long_few_chain_input():
     """B1 H2 T12400: 4 workgroups in one pass, so the library splits on its own
-    (26 segments of 480 tokens); the whole path gate -> chunk against the
+    (23 segments of 544 tokens); the whole path gate -> chunk against the
     oracle."""
     say("automatic split B1 H2 T12400")
     B, T, H = 1, 12400, 2
@@ -102,16 +116,10 @@ def test_split_with_slow_decay_chains_the_transitions(nseg, B, T, H):
     x = prefill_device(B, T, H, 128, 128, BF16, 420 + nseg, s0_std=0.3)
     g_f32 = oracle_gate_f32(x["z"].float() - 6.0, x["A"])
     g = g_f32.cuda()
-    o_s, S_s = _split(x, g, nseg)
     o_1, S_1 = _split(x, g, 1)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], x["S0"])
-    ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
-    r1o, r1s = rho(o_s, o_1), rho(S_s, S_1)
-    print(f"    vs oracle rho(o)={ro:.3e} rho(S)={rs:.3e}; vs one pass {r1o:.3e} {r1s:.3e}", flush=True)
-    assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all()
-    assert ro <= TOL[BF16] and rs <= TOL[BF16], (ro, rs)
-    assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (r1o, r1s)
+    _check_schemes(x, g, nseg, o_ref, S_ref, o_1, S_1)
 
 
 @pytest.mark.parametrize("nseg", [4, 7])
@@ -137,11 +145,15 @@ def test_split_transitions_that_end_early_and_that_run_on(nseg):
     g = g_f32.cuda()
     o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g_f32, x["beta"], None)
     fl = _lib.kda_flag_segments
-    runs = {
-        "g input": (_split(x, g, nseg), _split(x, g, 1)),
-        "gate fused": tuple(kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"],
-                                                None, flags=fl(n)) for n in (nseg, 1)),
-    }
+    runs = {}
+    for scheme, sf in SCHEMES.items():
+        runs["g input, " + scheme] = (kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], None,
+                                                    flags=fl(nseg) | sf),
+                                      kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], None,
+                                                    flags=fl(1)))
+        runs["gate fused, " + scheme] = tuple(
+            kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], None,
+                                flags=fl(n) | (sf if n > 1 else 0)) for n in (nseg, 1))
     torch.cuda.synchronize()
     for name, ((o_s, S_s), (o_1, S_1)) in runs.items():
         ro, rs = rho(o_s, o_ref), rho(S_s, S_ref)
