@@ -1516,6 +1516,16 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         } else if (a.phase == 3) {
             s0 = a.Sin + (size_t)(seg - 1) * a.nbh * DK * DV;
             s0row = bh;
+            // the stopping split leaves Sin[p] unwritten where segment p's
+            // transition vanished before its last chunk: M_p = 0, so the
+            // state entering segment p + 1 is L_p
+            if (a.zc && seg >= 2) {
+                const int *zr = a.zc + ((size_t)(seg - 2) * a.nbh + bh) * (DK / NV);
+                bool gone = true;
+#pragma unroll
+                for (int j = 0; j < DK / NV; ++j) gone = gone && zr[j] < (int)(a.seg_len / kPipeChunk) - 1;
+                if (gone) s0 = a.Lb + (size_t)(seg - 2) * a.nbh * DK * DV;
+            }
             st = seg == a.nseg - 1 ? a.ST : nullptr;
             // stopped before the end: M of the last segment is zero, so its
             // final state is the zero-start one, L
@@ -1813,12 +1823,20 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 // both operands.  The 132-float pitch keeps each 8-lane phase of those reads
 // on distinct banks.  The next step's M and L are loaded into registers while
 // the current step's products run.
+//
+// With the stopping split's records (zc set), a step whose transition was
+// found exactly zero before the segment's last chunk has M_p = 0 (the first
+// phase stored that zero state), so Sin[p] = L_p exactly and the step depends
+// on no earlier one: it is skipped (Sin[p] stays unwritten; the last phase
+// reads L_p in its place), and the products run only for the other steps,
+// each starting from L_{p-1} when step p - 1 was skipped.
 // ===========================================================================
 template <int DK>
 __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
                                                         const float *__restrict__ Lb,
                                                         const float *__restrict__ Mb, int nbh,
-                                                        int DV, int nseg) {
+                                                        int DV, int nseg, const int *__restrict__ zc,
+                                                        int nchunk_mid) {
     constexpr int NC = 16;                          // columns per workgroup
     constexpr int LDP = DK + 4;                     // LDS pitch (floats) of M rows and S^T rows
     constexpr int NF = DK * DK / 4 / 256;           // 16-byte loads of M per thread
@@ -1832,11 +1850,44 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
     const int lr = lane & 15, lq = lane >> 4;
     const size_t vsz = (size_t)nbh * DK * DV, msz = (size_t)nbh * DK * DK;
     const size_t sbase = (size_t)bh * DK * DV + c0;     // this block in a [nbh][DK][DV] state
-
-    for (int e = tid; e < DK * NC; e += 256) {
-        const int r = e / NC, c = e % NC;
-        sST[c * LDP + r] = Sin[sbase + (size_t)r * DV + c];
-    }
+    // bit i of the word for steps p0 .. p0 + 63: step p0 + i is skipped
+    // (one record pair per lane, gathered by a ballot)
+    auto skipped_bits = [&](int p0) -> unsigned long long {
+        const int ps = p0 + lane;
+        bool v = false;
+        if (zc && ps <= nseg - 2) {
+            const int *z = zc + ((size_t)(ps - 1) * nbh + bh) * (DK / 64);
+            v = true;
+#pragma unroll
+            for (int j = 0; j < DK / 64; ++j) v = v && z[j] < nchunk_mid - 1;
+        }
+        return __builtin_amdgcn_ballot_w64(v);
+    };
+    // this thread's elements of a block: rows 32 w + 16 it + 4 lq + j, column lr
+    auto erow = [&](int it, int j) { return (size_t)(32 * wave + 16 * it + 4 * lq + j) * DV + lr; };
+    // the next step that needs a product, from p on (nseg - 1 when none)
+    int word_p0 = 1;
+    unsigned long long word = skipped_bits(1);
+    auto next_step = [&](int p) {
+        while (p <= nseg - 2) {
+            if (p - word_p0 >= 64) {
+                word_p0 = p;
+                word = skipped_bits(p);
+            }
+            if (!((word >> (p - word_p0)) & 1ull)) break;
+            ++p;
+        }
+        return p;
+    };
+    // S^T of the state entering step p: Sin[0] (p = 1), else L_{p-1} (step
+    // p - 1 was skipped)
+    auto load_state = [&](int p) {
+        const float *src = p == 1 ? Sin + sbase : Lb + (size_t)(p - 2) * vsz + sbase;
+        for (int e = tid; e < DK * NC; e += 256) {
+            const int r = e / NC, c = e % NC;
+            sST[c * LDP + r] = src[(size_t)r * DV + c];
+        }
+    };
     floatx4 mreg[NF];
     float lreg[2][4];
     auto load_step = [&](int p) {
@@ -1848,11 +1899,14 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                lreg[it][j] = L[(size_t)(32 * wave + 16 * it + 4 * lq + j) * DV + lr];
+            for (int j = 0; j < 4; ++j) lreg[it][j] = L[erow(it, j)];
     };
-    if (nseg >= 3) load_step(1);
-    for (int p = 1; p <= nseg - 2; ++p) {
+    int p = next_step(1);
+    if (p <= nseg - 2) {
+        load_state(p);
+        load_step(p);
+    }
+    while (p <= nseg - 2) {
         __syncthreads();                            // the previous step's reads are done
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
@@ -1862,7 +1916,8 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
         floatx4 acc[2];
 #pragma unroll
         for (int it = 0; it < 2; ++it) acc[it] = floatx4{lreg[it][0], lreg[it][1], lreg[it][2], lreg[it][3]};
-        if (p + 1 <= nseg - 2) load_step(p + 1);
+        const int pn = next_step(p + 1);
+        if (pn <= nseg - 2) load_step(pn);
         __syncthreads();                            // M_p is in LDS
 #pragma unroll 4
         for (int s = 0; s < DK / 16; ++s) {
@@ -1885,6 +1940,12 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *__restrict__ Sin,
 #pragma unroll
             for (int j = 0; j < 4; ++j) out[(size_t)(r + j) * DV + lr] = acc[it][j];
         }
+        // skipped steps before the next product: its state is L_{pn-1}
+        if (pn <= nseg - 2 && pn != p + 1) {
+            __syncthreads();
+            load_state(pn);
+        }
+        p = pn;
     }
 }
 
@@ -2221,7 +2282,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else if (P >= 3) {
             hipLaunchKernelGGL(seg_chain_kernel<128>, dim3(args.nbh * (dv / 16)), dim3(256), 0, s,
-                               args.Sin, args.Lb, args.Mb, args.nbh, dv, P);
+                               args.Sin, args.Lb, args.Mb, args.nbh, dv, P, args.zc,
+                               (int)(args.seg_len / kPipeChunk));
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -122,24 +122,27 @@ def test_split_with_slow_decay_chains_the_transitions(nseg, B, T, H):
     _check_schemes(x, g, nseg, o_ref, S_ref, o_1, S_1)
 
 
-@pytest.mark.parametrize("nseg", [4, 7])
+@pytest.mark.parametrize("nseg", [4, 7, 12])
 def test_split_transitions_that_end_early_and_that_run_on(nseg):
     """A middle segment's transition columns (v = 0, initial state I) stop as
     soon as their state is exactly zero.  One launch mixes the cases: head 0
     takes the plain gate (its transitions vanish within a few chunks), head 1
     a slowed gate (z - 6) on every token (they never vanish), head 2 the
-    slowed gate on the first 1500 tokens only (some stop mid-segment).  v and
-    the initial state are zero over the first 1000 tokens, so v-column
-    workgroups also carry an all-zero state for a while and must not stop.
-    Both the g-input and the fused-gate kernels, against the oracle and
-    against one pass."""
+    slowed gate on the first 1500 tokens only (some stop mid-segment), head 3
+    on the tokens from 1500 on (early transitions vanish, later ones do not:
+    the chaining copies L for the first and multiplies for the others, from
+    the copied state).  v and the initial state are zero over the first 1000
+    tokens, so v-column workgroups also carry an all-zero state for a while
+    and must not stop.  Both the g-input and the fused-gate kernels, against
+    the oracle and against one pass."""
     say("split, transitions ending early", f"nseg={nseg}")
-    B, T, H = 1, 3000, 3
+    B, T, H = 1, 3000, 4
     x = prefill_device(B, T, H, 128, 128, BF16, 430 + nseg)
     x["v"][:, :1000] = 0
     z = x["z"].float()
     z[:, :, 1] -= 6.0
     z[:, :1500, 2] -= 6.0
+    z[:, 1500:, 3] -= 6.0
     x["z"] = z.to(BF16)
     g_f32 = oracle_gate_f32(x["z"], x["A"])
     g = g_f32.cuda()
