@@ -1,7 +1,7 @@
 """A seeded random sweep of prefill cases against the oracle: dtype, dk, dv,
 batch, heads, a ragged sequence length, an initial state or none, the
 decay-stress gate or the plain one, and the path (gate fused into the chunk
-kernel, gate then chunk, a forced sequence split, the position-pair diagonal
+kernel, gate then chunk, a forced sequence split in either scheme, the position-pair diagonal
 tiles), each drawn independently, so that combinations the dedicated tests do
 not pair up are exercised.  Every case is within the oracle bar on o and the
 final state."""
@@ -45,7 +45,10 @@ def test_random_prefill_case_matches_oracle(i):
         g = kda_gate(x["z"], x["A"])
         flags = 0
         if path == "split":
-            flags = _lib.kda_flag_segments(c["nseg"])
+            # either split scheme, from a generator of its own so that the
+            # other draws stay what they were
+            rerun = random.Random(9000 + i).random() < 0.5
+            flags = _lib.kda_flag_segments(c["nseg"]) | (_lib.KDA_FLAG_SPLIT_FULL_RERUN if rerun else 0)
         elif path == "pairwise":
             flags = _lib.KDA_FLAG_PAIRWISE_DIAGONAL
         o, S = kda_chunk_fwd(x["q"], x["k"], x["v"], g, x["beta"], x["S0"], flags=flags)
