@@ -31,9 +31,11 @@
  *  - Return value: KDA_OK or a negative error code.  Host-side validation runs
  *    before any HIP call, so an invalid call touches no device memory.
  *    kda_last_error() describes the most recent failure of the calling thread.
- *  - Sizes: B, T, H, N >= 1; dk, dv in {32, 64, 128}.  fp32 inputs support
- *    dk in {32, 64} for kda_chunk_fwd (its on-chip tiles for dk = 128 exceed
- *    the 160 KiB of LDS); every other combination is supported.
+ *  - Sizes: B, T, H, N >= 1; dk, dv in {32, 64, 128}, every combination and
+ *    both dtypes.  fp32 inputs at dk = 128 in the prefill calls (a 64-token
+ *    fp32 tile set that wide exceeds the 160 KiB of LDS) run 16-token chunks
+ *    through device buffers instead: they need a workspace and take the
+ *    [B, T, H] layout only (the pooled and packed calls return UNSUPPORTED).
  *    Index-width limits (INVALID_ARGUMENT beyond them): kda_gate H*dk <= 2^28;
  *    kda_chunk_fwd B*H <= 2^24 and H*max(dk,dv)*256 < 2^32; kda_decode_step
  *    N*H < 2^31.
@@ -57,7 +59,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = -1, /* null pointer, size <= 0, overflow, misalignment, small workspace */
-    KDA_ERR_UNSUPPORTED = -2,      /* dk/dv outside {32,64,128}, unknown dtype, fp32 with dk = 128 (chunk) */
+    KDA_ERR_UNSUPPORTED = -2,      /* dk/dv outside {32,64,128}, unknown dtype, a shape a path does not take */
     KDA_ERR_HIP = -3,              /* a HIP runtime call or kernel launch failed */
     KDA_ERR_RANGE = -4             /* KDA_FLAG_CHECK_RANGE found g outside [-5, 0] or a 16-token sum < -80 */
 };
@@ -178,7 +180,9 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
  *   o             : [B, T, H, dv] dtype (output; must not alias any input)
  *   workspace     : device buffer of at least kda_chunk_fwd_workspace_size()
  *                   bytes (..._size_segments() for an explicit segment count);
- *                   required with KDA_FLAG_CHECK_RANGE or explicit segments.
+ *                   required with KDA_FLAG_CHECK_RANGE, explicit segments,
+ *                   or fp32 inputs at dk = 128 (per-chunk buffers of the
+ *                   fp32 16-token path, about 1.6 KB per token and chain).
  *                   May be NULL otherwise: the call then runs in one pass.
  * Chunks and 16-token tiles are aligned to token 0 of the call; the last
  * chunk may be partial.  Accumulation and the carried state are fp32.

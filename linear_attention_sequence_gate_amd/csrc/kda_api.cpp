@@ -153,6 +153,9 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H, in
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (nseg < 0 || nseg > 255) return 0;
     const bool bf = dtype == KDA_BF16;
+    // fp32 inputs at dk = 128: the fp32 16-token path's per-chunk buffers
+    if (!kda::chunk_fwd_supported((int)dk, (int)dv, bf))
+        return kCounterBytes + kda::cb_prefill_workspace_bytes(B, T, H, (int)dk);
     if (!kda::seq_split_supported((int)dk, (int)dv, bf)) return kCounterBytes;
     if (nseg != 0) return kCounterBytes + (nseg >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, nseg) : 0);
     // the library's count, for either scheme (with and without
@@ -221,8 +224,12 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     if (!valid_dim(dk) || !valid_dim(dv))
         return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
                     (long long)dk, (long long)dv);
-    if (!kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16))
-        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs support dk in {32,64} only", who);
+    // fp32 inputs at dk = 128 run the fp32 16-token path (the reverse mode's
+    // chunk preparation and forward pass with outputs), [B, T, H] layout only
+    const bool cbpath = !kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16);
+    if (cbpath && (slots || cu_seqlens))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs with dk = 128 take the [B, T, H] layout "
+                    "(no state pool, no packed sequences)", who);
     if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK |
                           KDA_FLAG_SPLIT_FULL_RERUN))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
@@ -293,6 +300,18 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         if (nbad)
             return fail(KDA_ERR_RANGE, "%s: %u gate values or 16-token tile sums outside [-5,0] / [-80,0]", who,
                         nbad);
+    }
+    if (cbpath) {
+        const size_t need = kCounterBytes + kda::cb_prefill_workspace_bytes(B, T, H, (int)dk);
+        if (!workspace || workspace_bytes < need)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: fp32 inputs with dk = 128 need a workspace of %zu bytes",
+                        who, need);
+        hipError_t e = kda::launch_chunk_fwd_cb(q, k, v, g, beta, initial_state, final_state, o,
+                                                static_cast<char *>(workspace) + kCounterBytes,
+                                                workspace_bytes - kCounterBytes, B, T, H, (int)dk,
+                                                (int)dv, is_bf16, s);
+        if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+        return ok();
     }
     // sequence split: requested, or picked for these sizes when the workspace
     // holds its buffers (else one pass)

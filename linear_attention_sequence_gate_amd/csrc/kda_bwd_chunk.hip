@@ -80,6 +80,8 @@ struct CbArgs {
     float *du;                                   // [nbh][nc][16][DV]
     float *sfinal;                               // cb_fwd_kernel: the state after the last
                                                  // chunk, [nbh][DK][DV] (null: not written)
+    void *o;                                     // cb_fwd_kernel<.., true>: the outputs
+                                                 // O = Q~ S + P U, [B, tseq, H, DV] in T
     int64_t T;                                   // tokens of this launch (a segment)
     int64_t tseq, toff;                          // tokens per sequence in memory; first token
     int H, DV, nc, nsl, np;                      // np = chunk pairs = ceil(nc / 2)
@@ -287,10 +289,11 @@ template <int DK> struct CbStage {
 
 __device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
 
-// fwd: r1 = K~^T (staged as token rows), r2 = K^^T; bwd: r1 = K^^T (staged as
-// token rows), r2 = Q~^T, r3 = K~^T.
+// fwd: r1 = K~^T (staged as token rows), r2 = K^^T, and with outputs (OUT)
+// r3 = Q~^T (staged as token rows) and P; bwd: r1 = K^^T (staged as token
+// rows), r2 = Q~^T, r3 = K~^T.
 // `vsrc` is v (fwd) or dO (bwd).
-template <typename T, int DK, bool BWD>
+template <typename T, int DK, bool BWD, bool OUT = false>
 __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int64_t bh, int64_t rb,
                                          int col0, int c, CbStage<DK> &st) {
     const int tid = threadIdx.x;
@@ -303,7 +306,7 @@ __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int6
         if (idx < 4 * DK) {
             st.r1[u] = ld4(op + (BWD ? kOpKhT : kOpKtT) * DK + 4 * idx);
             st.r2[u] = ld4(op + (BWD ? kOpQtT : kOpKhT) * DK + 4 * idx);
-            if (BWD) st.r3[u] = ld4(op + kOpKtT * DK + 4 * idx);
+            if (BWD || OUT) st.r3[u] = ld4(op + (BWD ? kOpKtT : kOpQtT) * DK + 4 * idx);
         }
     }
     if (tid < DK / 4) st.e = ld4(op + kOpEbc * DK + 4 * tid);
@@ -315,12 +318,19 @@ __device__ __forceinline__ void cb_fetch(const CbArgs &a, const void *vsrc, int6
     const int r = tid >> 4, cc = tid & 15;
     const float *mc = a.mat + (bh * a.nc + c) * kCbMat;
     st.x = mc[r * kCB + cc];
-    if (BWD) st.p = mc[kCB * kCB + r * kCB + cc];
+    if (BWD || OUT) st.p = mc[kCB * kCB + r * kCB + cc];
     const int tb = (tid & 15) < n ? (tid & 15) : n - 1;
     st.bet = cb_ld<T>(a.beta, rb + (t0 + tb) * a.H);
 }
 
-template <int DK, bool BWD>
+// The forward pass with outputs stages Q~ in token rows over colm2, which
+// only the reverse pass uses.
+template <int DK> __device__ __forceinline__ float *cb_rowq(CbPassLds<DK> &L, int buf) {
+    static_assert(2 * kCB * (DK + 4) <= 2 * DK * (kCB + 4), "Q~ rows fit over colm2");
+    return &L.colm2[0][0][0] + buf * kCB * (DK + 4);
+}
+
+template <int DK, bool BWD, bool OUT = false>
 __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<DK> &st, int buf,
                                                 int n) {
     const int tid = threadIdx.x;
@@ -333,6 +343,11 @@ __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<
             for (int e = 0; e < 4; ++e) L.rowm[buf][f % kCB + e][f / kCB] = st.r1[u][e];
             *reinterpret_cast<floatx4 *>(&L.colm1[buf][f / kCB][f % kCB]) = st.r2[u];
             if (BWD) *reinterpret_cast<floatx4 *>(&L.colm2[buf][f / kCB][f % kCB]) = st.r3[u];
+            if (OUT) {
+                float *rq = cb_rowq(L, buf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rq[(f % kCB + e) * (DK + 4) + f / kCB] = st.r3[u][e];
+            }
         }
     }
     if (tid < DK / 4) *reinterpret_cast<floatx4 *>(&L.ebc[buf][4 * tid]) = st.e;
@@ -343,7 +358,7 @@ __device__ __forceinline__ void cb_stage_to_lds(CbPassLds<DK> &L, const CbStage<
     }
     const int r = tid >> 4, cc = tid & 15;
     L.X[buf][r][cc] = st.x;
-    if (BWD) L.P[buf][r][cc] = st.p;
+    if (BWD || OUT) L.P[buf][r][cc] = st.p;
     if (tid < kCB) L.bet[buf][tid] = tid < n ? st.bet : 0.f;
 }
 
@@ -360,8 +375,15 @@ constexpr int kCbAhead = 2;
 // ---------------------------------------------------------------------------
 template <int DK> using CbAcc = floatx4[(DK / 16 + 3) / 4][kCbCT];
 
-template <typename T, int DK>
-__device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, CbStage<DK> &stg,
+// LDS of the forward pass; with outputs (the prefill of shapes the other
+// kernels do not take) a second cross-wave reduction for Q~ S.
+template <int DK, bool OUT> struct CbFwdLds : CbPassLds<DK> {};
+template <int DK> struct CbFwdLds<DK, true> : CbPassLds<DK> {
+    float red2[4][kCB][kCbNS + 4];
+};
+
+template <typename T, int DK, bool OUT>
+__device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbFwdLds<DK, OUT> &L, CbStage<DK> &stg,
                                             int c, int64_t bh, int64_t rb, int col0, int wave,
                                             CbAcc<DK> &s) {
     constexpr int RT = DK / 16, TPW = (RT + 3) / 4;
@@ -369,26 +391,28 @@ __device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, C
     const int buf = c & 1;
     const int64_t t0 = (int64_t)c * kCB;
     const int n = (int)(a.T - t0 < kCB ? a.T - t0 : kCB);
-    cb_stage_to_lds<DK, false>(L, stg, buf, n);
-    cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, c + kCbAhead < a.nc ? c + kCbAhead : a.nc - 1, stg);
-    // the state entering each even chunk (the gradient kernel forms the odd ones)
-    float *stc = a.st + ((bh * a.np + c / 2) * DK) * a.DV + col0 + j;
+    cb_stage_to_lds<DK, false, OUT>(L, stg, buf, n);
+    cb_fetch<T, DK, false, OUT>(a, a.v, bh, rb, col0, c + kCbAhead < a.nc ? c + kCbAhead : a.nc - 1, stg);
+    if constexpr (!OUT) {
+        // the state entering each even chunk (the gradient kernel forms the odd ones)
+        float *stc = a.st + ((bh * a.np + c / 2) * DK) * a.DV + col0 + j;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int tt = wave * TPW + u;
-        if (tt < RT && (c & 1) == 0) {
+        for (int u = 0; u < TPW; ++u) {
+            const int tt = wave * TPW + u;
+            if (tt < RT && (c & 1) == 0) {
 #pragma unroll
-            for (int v = 0; v < kCbCT; ++v)
+                for (int v = 0; v < kCbCT; ++v)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    stc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV + 16 * v] = s[u][v][i];
+                    for (int i = 0; i < 4; ++i)
+                        stc[(int64_t)(16 * tt + 4 * g4 + i) * a.DV + 16 * v] = s[u][v][i];
+            }
         }
     }
     lds_barrier();
-    // this wave's rows of K~ S
-    floatx4 wp[kCbCT];
+    // this wave's rows of K~ S (and of Q~ S, with outputs)
+    floatx4 wp[kCbCT], qp[kCbCT];
 #pragma unroll
-    for (int v = 0; v < kCbCT; ++v) wp[v] = floatx4{0, 0, 0, 0};
+    for (int v = 0; v < kCbCT; ++v) wp[v] = qp[v] = floatx4{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int tt = wave * TPW + u;
@@ -398,12 +422,22 @@ __device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, C
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int v = 0; v < kCbCT; ++v) wp[v] = mfma1(kt[i], s[u][v][i], wp[v]);
+            if constexpr (OUT) {
+                const floatx4 qt = ld4(cb_rowq<DK>(L, buf) + j * (DK + 4) + 16 * tt + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int v = 0; v < kCbCT; ++v) qp[v] = mfma1(qt[i], s[u][v][i], qp[v]);
+            }
         }
     }
 #pragma unroll
     for (int v = 0; v < kCbCT; ++v)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L.red[wave][4 * g4 + i][16 * v + j] = wp[v][i];
+        for (int i = 0; i < 4; ++i) {
+            L.red[wave][4 * g4 + i][16 * v + j] = wp[v][i];
+            if constexpr (OUT) L.red2[wave][4 * g4 + i][16 * v + j] = qp[v][i];
+        }
     lds_barrier();
     const floatx4 xr = ld4(&L.X[buf][j][4 * g4]);
     floatx4 U[kCbCT];
@@ -417,15 +451,35 @@ __device__ __forceinline__ void cb_fwd_step(const CbArgs &a, CbPassLds<DK> &L, C
             W[i] = L.vo[buf][r][cc] -
                    (L.red[0][r][cc] + L.red[1][r][cc] + L.red[2][r][cc] + L.red[3][r][cc]);
         }
-        if (wave == 0) {
-            float *wc = a.w + ((bh * a.nc + c) * kCB) * a.DV + col0 + cc;
+        if constexpr (!OUT) {
+            if (wave == 0) {
+                float *wc = a.w + ((bh * a.nc + c) * kCB) * a.DV + col0 + cc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wc[(int64_t)(4 * g4 + i) * a.DV] = W[i];
+                for (int i = 0; i < 4; ++i) wc[(int64_t)(4 * g4 + i) * a.DV] = W[i];
+            }
         }
         // U = X Diag(beta) W
         U[v] = floatx4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) U[v] = mfma1(xr[i], L.bet[buf][4 * g4 + i] * W[i], U[v]);
+        if constexpr (OUT) {
+            // O = Q~ S + P U (rows past the end are not written)
+            if (wave == 0) {
+                floatx4 O;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g4 + i;
+                    O[i] = L.red2[0][r][cc] + L.red2[1][r][cc] + L.red2[2][r][cc] + L.red2[3][r][cc];
+                }
+                const floatx4 pr = ld4(&L.P[buf][j][4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) O = mfma1(pr[i], U[v][i], O);
+                T *oc = static_cast<T *>(a.o) + (rb + t0 * a.H) * a.DV + col0 + cc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g4 + i < n) oc[(int64_t)(4 * g4 + i) * a.H * a.DV] = from_f32<T>(O[i]);
+            }
+        }
     }
     // S <- Diag(e^{b_C}) S + K^^T U
 #pragma unroll
@@ -482,9 +536,9 @@ __device__ __forceinline__ void cb_load_state(const float *src, int64_t bh, int 
     }
 }
 
-template <typename T, int DK>
+template <typename T, int DK, bool OUT = false>
 __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
-    __shared__ CbPassLds<DK> L;
+    __shared__ CbFwdLds<DK, OUT> L;
     int64_t bh;
     int sl;
     cb_slice_block(a, nbh, bh, sl);
@@ -496,11 +550,11 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
     CbStage<DK> stg[kCbAhead];
 #pragma unroll
     for (int q = 0; q < kCbAhead; ++q)
-        cb_fetch<T, DK, false>(a, a.v, bh, rb, col0, q < a.nc ? q : a.nc - 1, stg[q]);
+        cb_fetch<T, DK, false, OUT>(a, a.v, bh, rb, col0, q < a.nc ? q : a.nc - 1, stg[q]);
     for (int c0 = 0; c0 < a.nc; c0 += kCbAhead) {
 #pragma unroll
         for (int q = 0; q < kCbAhead; ++q)
-            if (c0 + q < a.nc) cb_fwd_step<T, DK>(a, L, stg[q], c0 + q, bh, rb, col0, wave, s);
+            if (c0 + q < a.nc) cb_fwd_step<T, DK, OUT>(a, L, stg[q], c0 + q, bh, rb, col0, wave, s);
     }
     if (a.sfinal) cb_store_state<DK>(a.sfinal, bh, a.DV, col0, wave, s);
 }
@@ -1224,6 +1278,47 @@ static hipError_t cb_dispatch(const CbArgs &a, int64_t nbh, int dk, int is_bf16,
         return is_bf16 ? cb_inst<bf16, 128>(a, nbh, s) : cb_inst<float, 128>(a, nbh, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Chunked prefill in fp32 arithmetic for shapes the prefill kernels do not
+// take (fp32 inputs at dk = 128): cb_prep_kernel forms X, P, At and the
+// decayed operands of every 16-token chunk, then the forward state pass runs
+// with outputs.  Workspace: those per-chunk buffers.
+size_t cb_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk) {
+    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    return r256((size_t)nbh * nc * kCbMat * sizeof(float)) +
+           r256((size_t)nbh * nc * cb_ops_floats(dk) * sizeof(float));
+}
+
+template <typename T, int DK>
+static hipError_t cb_prefill_inst(const CbArgs &a, int64_t nbh, hipStream_t s) {
+    hipLaunchKernelGGL((cb_prep_kernel<T, DK>), dim3((unsigned)(nbh * a.nc)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((cb_fwd_kernel<T, DK, true>), dim3((unsigned)(nbh * a.nsl)), dim3(256), 0, s,
+                       a, nbh);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd_cb(const void *q, const void *k, const void *v, const float *g,
+                               const void *beta, const float *S0, float *ST, void *o, void *ws,
+                               size_t ws_bytes, int64_t B, int64_t T, int64_t H, int dk, int dv,
+                               int is_bf16, hipStream_t s) {
+    if (dv % kCbNS || dk != 128 || !ws || ws_bytes < cb_prefill_workspace_bytes(B, T, H, dk))
+        return hipErrorInvalidValue;
+    const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
+    if (nbh * nc > 0x7fffffffLL) return hipErrorInvalidValue;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    CbArgs a = {};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.S0 = S0; a.sfinal = ST; a.o = o;
+    char *p = static_cast<char *>(ws);
+    a.mat = reinterpret_cast<float *>(p);
+    a.ops = reinterpret_cast<float *>(p + r256((size_t)nbh * nc * kCbMat * sizeof(float)));
+    a.T = T; a.tseq = T; a.toff = 0;
+    a.H = (int)H; a.DV = dv; a.nsl = dv / kCbNS; a.nc = (int)nc; a.np = (int)((nc + 1) / 2);
+    return is_bf16 ? cb_prefill_inst<bf16, 128>(a, nbh, s) : cb_prefill_inst<float, 128>(a, nbh, s);
 }
 
 // With a workspace for the whole sequence, one launch of each kernel.  With a

@@ -80,7 +80,12 @@ def test_chunk_validation(L):
     assert chunk(L, dk=48) == E.KDA_ERR_UNSUPPORTED
     assert chunk(L, dv=256) == E.KDA_ERR_UNSUPPORTED
     assert chunk(L, dt=7) == E.KDA_ERR_UNSUPPORTED
-    assert chunk(L, dt=0, dk=128) == E.KDA_ERR_UNSUPPORTED       # fp32 with dk = 128
+    # fp32 with dk = 128: the fp32 16-token path, which needs its per-chunk
+    # buffers in the workspace
+    assert chunk(L, dt=0, dk=128) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
+    need = L.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 32, 0)
+    assert chunk(L, dt=0, dk=128, ws=P3, wsb=need - 1) == E.KDA_ERR_INVALID_ARGUMENT
     assert chunk(L, B=1 << 30, T=1 << 30) == E.KDA_ERR_INVALID_ARGUMENT   # overflow
     assert chunk(L, k=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
     assert chunk(L, o=P) == E.KDA_ERR_INVALID_ARGUMENT            # o aliases q
@@ -98,6 +103,16 @@ def test_chunk_validation(L):
 
 def test_workspace_query(L):
     assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 32, 32, 1) >= 4
+    # fp32 at dk = 128: the counter, then X, P, At (3 x 16 x 16) and the
+    # decayed operands (49 dk) of each 16-token chunk, fp32, each rounded
+    # up to 256 bytes
+    for B, T, H, dv in ((1, 64, 1, 128), (2, 1000, 3, 32)):
+        n = B * H * -(-T // 16)
+        r256 = lambda x: -(-x // 256) * 256
+        want = 256 + r256(n * 768 * 4) + r256(n * 49 * 128 * 4)
+        assert L.kda_chunk_fwd_workspace_size(B, T, H, 128, dv, 0) == want
+        assert L.kda_chunk_fwd_workspace_size_segments(B, T, H, 128, dv, 0, 1) == want
+        assert L.kda_chunk_fwd_gated_workspace_size(B, T, H, 128, dv, 0) == want + r256(B * T * H * 128 * 4)
     assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 48, 32, 1) == 0
     assert L.kda_chunk_fwd_workspace_size(0, 64, 1, 32, 32, 1) == 0
     assert L.kda_chunk_fwd_workspace_size(1, 64, 1, 32, 32, 5) == 0
@@ -217,6 +232,9 @@ def test_pool_validation(L):
     assert ch(slots=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(ns=0) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(o=P) == E.KDA_ERR_INVALID_ARGUMENT                          # o aliases the pool
+    # fp32 at dk = 128 takes the [B, T, H] layout only
+    assert L.kda_chunk_fwd_pooled(P, P, P, P, P, P, S4, P2, P3, 1 << 20, 1, 64, 4, 1, 128, 32, 0, 0,
+                                  None) == E.KDA_ERR_UNSUPPORTED
 
     vl = lambda cu=P3, dk=128, dv=128, dt=1, flags=0, pool=P, o=P2: L.kda_chunk_fwd_varlen_pooled(
         P, P, P, P, P, pool, S4, cu, o, 2, 100, 4, 1, dk, dv, dt, flags, None)
@@ -350,7 +368,7 @@ def test_gated_validation(L):
     assert gated(L, o=P2) == E.KDA_ERR_INVALID_ARGUMENT               # o aliases A
     assert gated(L, dt=7) == E.KDA_ERR_UNSUPPORTED
     assert gated(L, dk=48) == E.KDA_ERR_UNSUPPORTED
-    assert gated(L, dt=0) == E.KDA_ERR_UNSUPPORTED                    # fp32 with dk = 128
+    assert gated(L, dt=0) == E.KDA_ERR_INVALID_ARGUMENT               # fp32, dk = 128: no workspace
     # the range check takes a caller's g; here g is the gate's own output
     assert gated(L, flags=E.KDA_FLAG_CHECK_RANGE, ws=ctypes.c_void_p(0x500000),
                  wsb=1 << 20) == E.KDA_ERR_INVALID_ARGUMENT
