@@ -34,8 +34,8 @@
  *  - Sizes: B, T, H, N >= 1; dk, dv in {32, 64, 128}, every combination and
  *    both dtypes.  fp32 inputs at dk = 128 in the prefill calls (a 64-token
  *    fp32 tile set that wide exceeds the 160 KiB of LDS) run 16-token chunks
- *    through device buffers instead: they need a workspace and take the
- *    [B, T, H] layout only (the pooled and packed calls return UNSUPPORTED).
+ *    through device buffers instead: they need a workspace (also in the
+ *    pooled call), and the packed call returns UNSUPPORTED for them.
  *    Index-width limits (INVALID_ARGUMENT beyond them): kda_gate H*dk <= 2^28;
  *    kda_chunk_fwd B*H <= 2^24 and H*max(dk,dv)*256 < 2^32; kda_decode_step
  *    N*H < 2^31.

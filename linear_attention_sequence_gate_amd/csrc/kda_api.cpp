@@ -227,9 +227,9 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     // fp32 inputs at dk = 128 run the fp32 16-token path (the reverse mode's
     // chunk preparation and forward pass with outputs), [B, T, H] layout only
     const bool cbpath = !kda::chunk_fwd_supported((int)dk, (int)dv, dtype == KDA_BF16);
-    if (cbpath && (slots || cu_seqlens))
+    if (cbpath && cu_seqlens)
         return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs with dk = 128 take the [B, T, H] layout "
-                    "(no state pool, no packed sequences)", who);
+                    "(no packed sequences)", who);
     if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK |
                           KDA_FLAG_SPLIT_FULL_RERUN))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
@@ -309,7 +309,7 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         hipError_t e = kda::launch_chunk_fwd_cb(q, k, v, g, beta, initial_state, final_state, o,
                                                 static_cast<char *>(workspace) + kCounterBytes,
                                                 workspace_bytes - kCounterBytes, B, T, H, (int)dk,
-                                                (int)dv, is_bf16, s);
+                                                (int)dv, is_bf16, slots, n_slots, s);
         if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
         return ok();
     }

@@ -82,6 +82,9 @@ struct CbArgs {
                                                  // chunk, [nbh][DK][DV] (null: not written)
     void *o;                                     // cb_fwd_kernel<.., true>: the outputs
                                                  // O = Q~ S + P U, [B, tseq, H, DV] in T
+    const int *slots;                            // cb_fwd_kernel<.., true>: with a slot table
+    int64_t n_slots;                             // the states are rows slots[b] H + h of a pool
+                                                 // (a slot outside it skips the sequence)
     int64_t T;                                   // tokens of this launch (a segment)
     int64_t tseq, toff;                          // tokens per sequence in memory; first token
     int H, DV, nc, nsl, np;                      // np = chunk pairs = ceil(nc / 2)
@@ -545,8 +548,15 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
     const int64_t rb = cb_rowbase(a, bh);
     const int col0 = sl * kCbNS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // row of the chain's states: bh, or its slot's row of a state pool
+    int64_t srow = bh;
+    if (OUT && a.slots) {
+        const int slot = a.slots[bh / a.H];
+        if (slot < 0 || slot >= a.n_slots) return;
+        srow = (int64_t)slot * a.H + bh % a.H;
+    }
     CbAcc<DK> s;
-    cb_load_state<DK>(a.S0, bh, a.DV, col0, wave, s);
+    cb_load_state<DK>(a.S0, srow, a.DV, col0, wave, s);
     CbStage<DK> stg[kCbAhead];
 #pragma unroll
     for (int q = 0; q < kCbAhead; ++q)
@@ -556,7 +566,7 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbArgs a, int64_t nbh) {
         for (int q = 0; q < kCbAhead; ++q)
             if (c0 + q < a.nc) cb_fwd_step<T, DK, OUT>(a, L, stg[q], c0 + q, bh, rb, col0, wave, s);
     }
-    if (a.sfinal) cb_store_state<DK>(a.sfinal, bh, a.DV, col0, wave, s);
+    if (a.sfinal) cb_store_state<DK>(a.sfinal, srow, a.DV, col0, wave, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1304,7 +1314,7 @@ static hipError_t cb_prefill_inst(const CbArgs &a, int64_t nbh, hipStream_t s) {
 hipError_t launch_chunk_fwd_cb(const void *q, const void *k, const void *v, const float *g,
                                const void *beta, const float *S0, float *ST, void *o, void *ws,
                                size_t ws_bytes, int64_t B, int64_t T, int64_t H, int dk, int dv,
-                               int is_bf16, hipStream_t s) {
+                               int is_bf16, const int *slots, int64_t n_slots, hipStream_t s) {
     if (dv % kCbNS || dk != 128 || !ws || ws_bytes < cb_prefill_workspace_bytes(B, T, H, dk))
         return hipErrorInvalidValue;
     const int64_t nbh = B * H, nc = (T + kCB - 1) / kCB;
@@ -1313,6 +1323,7 @@ hipError_t launch_chunk_fwd_cb(const void *q, const void *k, const void *v, cons
     CbArgs a = {};
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
     a.S0 = S0; a.sfinal = ST; a.o = o;
+    a.slots = slots; a.n_slots = n_slots;
     char *p = static_cast<char *>(ws);
     a.mat = reinterpret_cast<float *>(p);
     a.ops = reinterpret_cast<float *>(p + r256((size_t)nbh * nc * kCbMat * sizeof(float)));

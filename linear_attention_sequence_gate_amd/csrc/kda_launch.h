@@ -46,11 +46,12 @@ bool chunk_fwd_supported(int dk, int dv, int is_bf16);
 // Prefill of the shapes chunk_fwd_supported leaves out (fp32 inputs at dk =
 // 128): the reverse mode's chunk preparation and forward pass with outputs,
 // in fp32 arithmetic; it needs cb_prefill_workspace_bytes of workspace.
+// With slots, the states are rows of a pool as in the pooled calls.
 size_t cb_prefill_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk);
 hipError_t launch_chunk_fwd_cb(const void *q, const void *k, const void *v, const float *g,
                                const void *beta, const float *S0, float *ST, void *o, void *ws,
                                size_t ws_bytes, int64_t B, int64_t T, int64_t H, int dk, int dv,
-                               int is_bf16, hipStream_t s);
+                               int is_bf16, const int *slots, int64_t n_slots, hipStream_t s);
 
 // slots == nullptr: state is [N, H, dk, dv]; else state is a pool
 // [n_slots, H, dk, dv] and sequence n uses slot slots[n] (heads of a slot

@@ -232,15 +232,18 @@ def test_pool_validation(L):
     assert ch(slots=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(ns=0) == E.KDA_ERR_INVALID_ARGUMENT
     assert ch(o=P) == E.KDA_ERR_INVALID_ARGUMENT                          # o aliases the pool
-    # fp32 at dk = 128 takes the [B, T, H] layout only
-    assert L.kda_chunk_fwd_pooled(P, P, P, P, P, P, S4, P2, P3, 1 << 20, 1, 64, 4, 1, 128, 32, 0, 0,
-                                  None) == E.KDA_ERR_UNSUPPORTED
+    # fp32 at dk = 128 (the fp32 16-token path) needs its workspace here too;
+    # the packed call does not take it
+    assert L.kda_chunk_fwd_pooled(P, P, P, P, P, P3, S4, P2, NULL, 0, 1, 64, 4, 1, 128, 32, 0, 0,
+                                  None) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "workspace" in _lib.kda_last_error()
 
     vl = lambda cu=P3, dk=128, dv=128, dt=1, flags=0, pool=P, o=P2: L.kda_chunk_fwd_varlen_pooled(
         P, P, P, P, P, pool, S4, cu, o, 2, 100, 4, 1, dk, dv, dt, flags, None)
     assert vl(cu=NULL) == E.KDA_ERR_INVALID_ARGUMENT
     assert vl(cu=ctypes.c_void_p(0x300004)) == E.KDA_ERR_INVALID_ARGUMENT   # not 8-byte aligned
     assert vl(dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert vl(dt=0, dv=32) == E.KDA_ERR_UNSUPPORTED                       # fp32, dk = 128
     assert vl(dt=0) == E.KDA_ERR_UNSUPPORTED
     assert vl(flags=E.KDA_FLAG_CHECK_RANGE) == E.KDA_ERR_INVALID_ARGUMENT
     assert vl(flags=_lib.kda_flag_segments(3)) == E.KDA_ERR_INVALID_ARGUMENT
