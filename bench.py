@@ -636,11 +636,11 @@ EXTRA_TRACES = {
                  "bwd_ckpt_kernel, bwd_kernel, bwd_sum_kernel) and kda_gate_bwd."),
     "small": ("small", "kernel_trace_prefill_b1h8t4096_split.md",
               "kda_chunk_fwd_gated on B1 H8 T4096 d128 bf16 with the library's automatic "
-              "sequence split (11 segments of 384 tokens), inputs rotated over five copies (10 "
+              "sequence split (10 segments of 416 tokens), inputs rotated over five copies (10 "
               "warm-up + 5 windows of 20 timed calls).  A call is three launches: chunk32_kernel phase 1 "
-              "(segment 0 from the initial state, segments 1..10 from zero, and their "
+              "(segment 0 from the initial state, segments 1..9 from zero, and their "
               "transitions), seg_chain_kernel (serial chaining), chunk32_kernel phase 3 "
-              "(segments 1..10 up to where their transitions vanished); the workgroup count "
+              "(segments 1..9 up to where their transitions vanished); the workgroup count "
               "tells the phases apart."),
     "pairwise": ("pairwise", "kernel_trace_prefill_b4h32t32k_pairwise_diagonal.md",
                  "kda_gate once, then kda_chunk_fwd on B4 H32 T32768 d128 bf16 with the dense "

@@ -2137,18 +2137,20 @@ static double split_phase_time(int64_t n1, double d1, int64_t n2, double d2) {
 //    segment (transitions priced at a whole segment).
 //  - Stopping split (the default): phase 1 places the v workgroups of all P
 //    segments, then the transitions; the transitions and phase 3 are priced
-//    as ending a quarter of the way into a segment (at least two chunks),
-//    an assumption about the gates: the transition vanishes once every
+//    as ending 0.15 of the way into a segment (at least two chunks), an
+//    assumption about the gates: the transition vanishes once every
 //    channel's cumulative decay has underflowed, which synthetic gates of
 //    the pages' range reach within a chunk or two and gates that keep
 //    memory reach later or never (phase 3 then reruns the whole segment).
+//    The fraction is fitted to forced-count sweeps of B1 H8 T4096 (best
+//    P = 10) and B1 H32 T1M (P = 4).
 int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun) {
     constexpr int64_t kCUs = 256;             // MI355X compute units
     constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
     constexpr int64_t kFillTokens = 64;       // two pipeline periods per segment
     constexpr int64_t kChainStepTokens = 33;  // one chaining step
     constexpr int64_t kSplitTokens = 145;     // the two extra launches
-    constexpr double kVanishFrac = 0.25;      // stopping split: where transitions end
+    constexpr double kVanishFrac = 0.15;      // stopping split: where transitions end
     if (!seq_split_supported(dk, dv, is_bf16)) return 1;
     const int64_t bh = B * H, nsl_v = dv / 64, nsl_m = dk / 64;
     auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };

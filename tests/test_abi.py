@@ -147,8 +147,11 @@ def test_sequence_split_workspace_and_policy(L):
     # one chain: many more segments
     P1 = auto(1, 1 << 20, 1, 128, 128, 1)
     assert P1 > 4 * P, (P1, P)
-    assert wss(1, 1 << 20, 1, 128, 128, 1, P1) == split_bytes(1, 1, 128, P1, scan=True)
     assert ws(1, 1 << 20, 1, 128, 128, 1) >= wss(1, 1 << 20, 1, 128, 128, 1, P1)
+    # 129 segments of one chain are chained by the log-depth scan, which
+    # takes a second buffer of transitions; 9 segments serially
+    assert wss(1, 1 << 20, 1, 128, 128, 1, 129) == split_bytes(1, 1, 128, 129, scan=True)
+    assert wss(1, 1 << 20, 1, 128, 128, 1, 9) == split_bytes(1, 1, 128, 9)
     # few chains of a short sequence split too (segments of >= 128 tokens):
     # B1 H8 T4096 runs 16 workgroups in one pass
     P8 = auto(1, 4096, 8, 128, 128, 1)

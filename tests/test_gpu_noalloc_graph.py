@@ -6,7 +6,7 @@ Between replays the program does its own eager work: it clears the graph's
 output tensors with fill kernels and makes another no-allocation call on
 different inputs, which reuses the same scratch.  Every replay must equal the
 eager result bit for bit.  Cases: a long few-chain shape that takes the
-sequence split in 16 segments (its three kernels and the chaining between
+sequence split in 15 segments (its three kernels and the chaining between
 them write the scratch), a short one split in 4, and a one-pass shape."""
 import pytest
 import torch
@@ -31,7 +31,7 @@ def _outputs(x):
             torch.empty((B, H, dk, dv), device="cuda", dtype=torch.float32))
 
 
-@pytest.mark.parametrize("B,T,H,nseg", [(1, 6000, 2, 16), (2, 700, 4, 4), (8, 700, 16, 1)])
+@pytest.mark.parametrize("B,T,H,nseg", [(1, 6000, 2, 15), (2, 700, 4, 4), (8, 700, 16, 1)])
 def test_noalloc_call_replays_in_a_captured_graph(B, T, H, nseg):
     segs = _lib.kda_chunk_fwd_auto_segments(B, T, H, 128, 128, _lib.KDA_BF16)
     say("noalloc graph", f"B{B} T{T} H{H}", f"segments {segs}")
