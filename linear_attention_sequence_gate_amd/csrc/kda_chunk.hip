@@ -1767,19 +1767,22 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             if constexpr (TRANS) return __builtin_amdgcn_readfirstlane(posts) == kAllZero;
             else return false;
         };
-        bool stop = false;
+        bool stop = false, stop1 = false;
         int64_t c = 0;
         for (; c <= nchunk + 1 && !stop; c += 2) {
-            stop = period(c, vv0, vv1);
+            stop1 = period(c, vv0, vv1);
+            stop = stop1;
             if (c + 1 <= nchunk + 1) stop |= period(c + 1, vv1, vv0);
         }
         vm_wait<0>();                               // no load outlives the wave
         if constexpr (TRANS) {
             // the stopping split: a stop in the pair (c - 2, c - 1) saw the
-            // state zero after chunk c - 3 at the latest (the pass of period
-            // c - 1); without a stop every chunk counts
+            // state zero after chunk c - 4 (the pass of period c - 2) when its
+            // first period posted it, else after chunk c - 3; without a stop
+            // every chunk counts
             if (vzero && a.zc && s == 0 && lane == 0) {
-                const int64_t zl = stop && c - 3 < nchunk - 1 ? c - 3 : nchunk - 1;
+                const int64_t z0 = stop1 ? c - 4 : c - 3;
+                const int64_t zl = stop && z0 < nchunk - 1 ? z0 : nchunk - 1;
                 a.zc[((size_t)(seg - 1) * a.nbh + bh) * (DK / NV) + (slice - a.nsl_v)] = (int)zl;
             }
         }
