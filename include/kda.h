@@ -212,7 +212,11 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
  * step 3 and those kept from step 1 each agree with one pass to fp32
  * rounding.  The library picks P; KDA_FLAG_SEGMENTS(n) forces it (tests).
  * The split uses the workspace; without one large enough, the automatic
- * choice falls back to one pass.
+ * choice falls back to one pass.  Non-finite inputs stay in their chain in
+ * every path; inside it, one pass carries a NaN or Inf in the state to the
+ * end, while the stopping split applies a transition found exactly zero as
+ * zero (it takes L for M S + L and keeps the zero-start outputs), so the
+ * non-finite value does not pass such a point.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   const void *beta, const float *initial_state, float *final_state,
