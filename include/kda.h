@@ -95,7 +95,19 @@ enum {
      * segment's transition became exactly zero (see kda_chunk_fwd).  Faster
      * when the gates keep memory over more than about half a segment; the
      * segment count is then chosen for this scheme. */
-    KDA_FLAG_SPLIT_FULL_RERUN = 0x20000u
+    KDA_FLAG_SPLIT_FULL_RERUN = 0x20000u,
+    /* Workgroup layout of the pipelined chunk path at dv = 128 (bf16,
+     * dk = 128): one workgroup per chain covering all 128 state columns, so
+     * each chunk's decayed operands and scores are formed once per chain,
+     * or one per 64-column slice (two per chain, each forming them itself:
+     * twice the chips' compute units filled by as many chains).  Without
+     * either flag the library picks, with the segment count; with one it
+     * takes that layout (PER_CHAIN is rejected for other shapes and with
+     * KDA_FLAG_PAIRWISE_DIAGONAL).  Results agree to rounding order: each
+     * state column's arithmetic is the same, only which workgroup runs it
+     * differs. */
+    KDA_FLAG_WORKGROUP_PER_CHAIN = 0x40000u,
+    KDA_FLAG_WORKGROUP_PER_SLICE = 0x80000u
 };
 #define KDA_FLAG_SEGMENTS(n) ((unsigned)(n) << KDA_FLAG_SEGMENTS_SHIFT)
 
@@ -153,6 +165,22 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
  */
 int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H,
                                 int64_t dk, int64_t dv, int dtype);
+
+/*
+ * The plan kda_chunk_fwd (and kda_chunk_fwd_gated) follows for these sizes
+ * and flags when its workspace holds what the library asks for:
+ *   *segments  : segments per sequence (1 = one pass; a requested count is
+ *                reported as the count its 32-token-aligned length gives)
+ *   *per_chain : 1 when one workgroup covers a whole chain's 128 state
+ *                columns, 0 when one covers a 64-column slice (and for every
+ *                shape outside the pipelined path)
+ * The flags that matter: the segment bits, KDA_FLAG_SPLIT_FULL_RERUN,
+ * KDA_FLAG_PAIRWISE_DIAGONAL and the workgroup layout flags.  Returns KDA_OK,
+ * or the error the call would give for sizes or flags it rejects (outputs
+ * untouched).  Host only: launches nothing.
+ */
+int kda_chunk_fwd_plan(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int dtype,
+                       unsigned flags, int *segments, int *per_chain);
 
 /*
  * As kda_chunk_fwd_workspace_size for an explicit segment count (the value

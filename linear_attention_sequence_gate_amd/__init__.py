@@ -10,7 +10,7 @@ __all__ = ["kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
            "kda_chunk_fwd_gated_noalloc",
            "kda_chunk_fwd_varlen_pooled_gated",
-           "kda_chunk_fwd_auto_segments", "kda_decode_step", "kda_state_pool_reset",
+           "kda_chunk_fwd_auto_segments", "kda_chunk_fwd_plan", "kda_decode_step", "kda_state_pool_reset",
            "kda_chunk_fwd_pooled", "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_workspace_size_flags",
            "kda_gate_bwd",

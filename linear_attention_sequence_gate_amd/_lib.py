@@ -28,6 +28,8 @@ KDA_FLAG_SEGMENTS_SHIFT = 8
 KDA_FLAG_SEGMENTS_MASK = 0xFF00
 KDA_FLAG_TOKEN_BACKWARD = 0x10000
 KDA_FLAG_SPLIT_FULL_RERUN = 0x20000
+KDA_FLAG_WORKGROUP_PER_CHAIN = 0x40000
+KDA_FLAG_WORKGROUP_PER_SLICE = 0x80000
 
 
 def kda_flag_segments(n: int) -> int:
@@ -36,7 +38,7 @@ def kda_flag_segments(n: int) -> int:
 
 EXPORTED = ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
             "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
-            "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
+            "kda_chunk_fwd_plan", "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
             "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
             "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
@@ -71,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_workspace_size_segments.restype = ctypes.c_size_t
     L.kda_chunk_fwd_auto_segments.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_fwd_auto_segments.restype = c_int
+    L.kda_chunk_fwd_plan.argtypes = [i64, i64, i64, i64, i64, c_int, ctypes.c_uint,
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+    L.kda_chunk_fwd_plan.restype = c_int
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
     L.kda_chunk_fwd.restype = c_int
@@ -257,6 +262,16 @@ def kda_chunk_fwd_workspace_size(B: int, T: int, H: int, dk: int, dv: int, dtype
 def kda_chunk_fwd_auto_segments(B: int, T: int, H: int, dk: int, dv: int, dtype: int) -> int:
     """Segments per sequence the library picks for these sizes (1 = one pass)."""
     return int(load_library().kda_chunk_fwd_auto_segments(B, T, H, dk, dv, dtype))
+
+
+def kda_chunk_fwd_plan(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
+                       flags: int = 0) -> Tuple[int, bool]:
+    """(segments per sequence, one workgroup per chain?) that kda_chunk_fwd
+    follows for these sizes and flags given the workspace the library asks for."""
+    seg, per_chain = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load_library().kda_chunk_fwd_plan(B, T, H, dk, dv, dtype, flags, ctypes.byref(seg),
+                                             ctypes.byref(per_chain)))
+    return seg.value, bool(per_chain.value)
 
 
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None,

@@ -147,6 +147,14 @@ int kda_gate_bwd(const void *z, const float *A, const float *dg, float *dz, floa
 // sequence split when it is used.
 static constexpr size_t kCounterBytes = 256;
 
+// The workgroup layout the flags ask for: 1 one per chain, 0 one per
+// 64-column slice (also the position-pair path's), -1 the library's choice.
+static int layout_request(unsigned flags) {
+    if (flags & KDA_FLAG_WORKGROUP_PER_CHAIN) return 1;
+    if ((flags & KDA_FLAG_WORKGROUP_PER_SLICE) || (flags & KDA_FLAG_PAIRWISE_DIAGONAL)) return 0;
+    return -1;
+}
+
 size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H, int64_t dk,
                                              int64_t dv, int dtype, int nseg) {
     if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
@@ -159,13 +167,15 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H, in
     if (!kda::seq_split_supported((int)dk, (int)dv, bf)) return kCounterBytes;
     if (nseg != 0) return kCounterBytes + (nseg >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, nseg) : 0);
     // the library's count, for either scheme (with and without
-    // KDA_FLAG_SPLIT_FULL_RERUN): the same layout, sized for the larger
+    // KDA_FLAG_SPLIT_FULL_RERUN) and any workgroup layout flag: the same
+    // buffers, sized for the largest
     size_t ws = 0;
-    for (int rerun = 0; rerun < 2; ++rerun) {
-        const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, bf, rerun);
-        const size_t w = P >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, P) : 0;
-        if (w > ws) ws = w;
-    }
+    for (int rerun = 0; rerun < 2; ++rerun)
+        for (int layout = -1; layout <= 1; ++layout) {
+            const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, bf, rerun, layout);
+            const size_t w = P >= 2 ? kda::seq_split_workspace(B, T, H, (int)dk, (int)dv, P) : 0;
+            if (w > ws) ws = w;
+        }
     return kCounterBytes + ws;
 }
 
@@ -173,13 +183,48 @@ int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H, int64_t dk, int
                                 int dtype) {
     if (B <= 0 || T <= 0 || H <= 0 || !valid_dim(dk) || !valid_dim(dv)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
-    const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16, 0);
+    const int P = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, dtype == KDA_BF16, 0, -1);
     return P >= 2 ? kda::seq_split_effective(T, P) : 1;
 }
 
 size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                                     int dtype) {
     return kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, 0);
+}
+
+int kda_chunk_fwd_plan(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int dtype,
+                       unsigned flags, int *segments, int *per_chain) {
+    const char *who = "kda_chunk_fwd_plan";
+    if (int e = check_dtype(dtype)) return e;
+    if (!segments || !per_chain) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
+    if (!valid_dim(dk) || !valid_dim(dv))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: dk=%lld dv=%lld must be in {32,64,128}", who,
+                    (long long)dk, (long long)dv);
+    if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK |
+                          KDA_FLAG_SPLIT_FULL_RERUN | KDA_FLAG_WORKGROUP_PER_CHAIN |
+                          KDA_FLAG_WORKGROUP_PER_SLICE))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
+    const bool bf = dtype == KDA_BF16;
+    const bool pipe = kda::seq_split_supported((int)dk, (int)dv, bf);
+    const int layout = layout_request(flags);
+    const int req_seg = (int)((flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT);
+    if ((flags & KDA_FLAG_WORKGROUP_PER_CHAIN) && (flags & KDA_FLAG_WORKGROUP_PER_SLICE))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the two workgroup layout flags exclude each other", who);
+    if ((flags & KDA_FLAG_WORKGROUP_PER_CHAIN) &&
+        (!kda::seq_wide_supported((int)dk, (int)dv, bf) || (flags & KDA_FLAG_PAIRWISE_DIAGONAL)))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: one workgroup per chain needs bf16 inputs, dk = dv = 128 "
+                    "and no KDA_FLAG_PAIRWISE_DIAGONAL", who);
+    if (((flags & KDA_FLAG_PAIRWISE_DIAGONAL) || req_seg >= 2) && !pipe)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: a sequence split or the position-pair path needs bf16 "
+                    "inputs, dk = 128, dv in {64, 128}", who);
+    const int rerun = (flags & KDA_FLAG_SPLIT_FULL_RERUN) ? 1 : 0;
+    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, bf, rerun, layout) : req_seg;
+    nseg = pipe && nseg >= 2 ? kda::seq_split_effective(T, nseg) : 1;
+    *segments = nseg;
+    *per_chain = kda::seq_layout(B, T, H, (int)dk, (int)dv, bf, rerun, nseg, layout);
+    return ok();
 }
 
 // kda_chunk_fwd_gated: shapes without the fused gate stage g at the start of
@@ -231,13 +276,21 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 inputs with dk = 128 take the [B, T, H] layout "
                     "(no packed sequences)", who);
     if (flags & ~unsigned(KDA_FLAG_CHECK_RANGE | KDA_FLAG_PAIRWISE_DIAGONAL | KDA_FLAG_SEGMENTS_MASK |
-                          KDA_FLAG_SPLIT_FULL_RERUN))
+                          KDA_FLAG_SPLIT_FULL_RERUN | KDA_FLAG_WORKGROUP_PER_CHAIN |
+                          KDA_FLAG_WORKGROUP_PER_SLICE))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown flag bits 0x%x", who, flags);
+    if ((flags & KDA_FLAG_WORKGROUP_PER_CHAIN) && (flags & KDA_FLAG_WORKGROUP_PER_SLICE))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: KDA_FLAG_WORKGROUP_PER_CHAIN and "
+                    "KDA_FLAG_WORKGROUP_PER_SLICE exclude each other", who);
     const bool is_bf16 = dtype == KDA_BF16;
     const bool pairwise = (flags & KDA_FLAG_PAIRWISE_DIAGONAL) != 0;
     if (pairwise && !kda::seq_split_supported((int)dk, (int)dv, is_bf16))
         return fail(KDA_ERR_UNSUPPORTED, "%s: the position-pair diagonal path needs bf16 inputs, dk = 128, "
                     "dv in {64, 128}", who);
+    if ((flags & KDA_FLAG_WORKGROUP_PER_CHAIN) &&
+        !(kda::seq_split_supported((int)dk, (int)dv, is_bf16) && dv == 128 && !pairwise))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: one workgroup per chain needs bf16 inputs, dk = dv = 128 "
+                    "and no KDA_FLAG_PAIRWISE_DIAGONAL", who);
     if (pairwise && (flags & KDA_FLAG_CHECK_RANGE))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the position-pair diagonal path has no decay range to check", who);
     const int req_seg = (int)((flags & KDA_FLAG_SEGMENTS_MASK) >> KDA_FLAG_SEGMENTS_SHIFT);
@@ -316,7 +369,11 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
     // sequence split: requested, or picked for these sizes when the workspace
     // holds its buffers (else one pass)
     const int rerun = (flags & KDA_FLAG_SPLIT_FULL_RERUN) ? 1 : 0;
-    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16, rerun) : req_seg;
+    // workgroup layout: forced by a flag (the position-pair path runs per
+    // slice), else chosen with the segment count
+    const int layout = layout_request(flags);
+    int nseg = req_seg == 0 ? kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16, rerun, layout)
+                            : req_seg;
     void *split_ws = nullptr;
     if (nseg >= 2) {
         const size_t need = kda_chunk_fwd_workspace_size_segments(B, T, H, dk, dv, dtype, nseg);
@@ -328,10 +385,11 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
             nseg = 1;
         }
     }
+    const int wide = kda::seq_layout(B, T, H, (int)dk, (int)dv, is_bf16, rerun, nseg, layout);
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
                                          (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
                                          pairwise ? 1 : 0, cu_seqlens, fused ? z : nullptr,
-                                         fused ? Ag : nullptr, rerun, s);
+                                         fused ? Ag : nullptr, rerun, wide, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }

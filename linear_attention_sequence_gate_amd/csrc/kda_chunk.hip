@@ -977,9 +977,15 @@ template <int DK> struct PipeLds {
     static_assert(TOTAL + ZPOST_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, bool ZIN, bool TRANS>
+template <int DK, bool ZIN, bool TRANS, bool WIDE>
 __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
-    constexpr int NV = 64;
+    // a workgroup covers NV columns of its chain's state: 64 (two per chain
+    // at dv = 128, each preparing the chunk's operands itself) or, WIDE, all
+    // 128 (the operands prepared once per chain)
+    constexpr int NV = WIDE ? 128 : 64;
+    constexpr int NSW = NV / 16;                    // state waves, one 16-column block each
+    constexpr int NZR = DK / 64;                    // chunk records per chain and segment
+    constexpr int NZC = NV / 64;                    // of them, written by one workgroup
     using Lds = PipeLds<DK>;
     using PF = Perm<bf16>;
     using KF = Kc<bf16>;
@@ -1045,17 +1051,18 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     // the segment's transition vanished (all of them when it never did)
     int64_t tend = tseg;
     if (a.phase == 3 && a.zc) {
-        const int *zr = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * (DK / NV);
+        const int *zr = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * NZR;
         int zl = zr[0];
 #pragma unroll
-        for (int j = 1; j < DK / NV; ++j) zl = zr[j] > zl ? zr[j] : zl;
+        for (int j = 1; j < NZR; ++j) zl = zr[j] > zl ? zr[j] : zl;
         zl = __builtin_amdgcn_readfirstlane(zl);
         const int64_t tz = tbeg + (int64_t)(zl + 1) * kPipeChunk;
         if (tz < tend) tend = tz;
     }
     const int vcol0 = (mcols ? slice - a.nsl_v : slice) * NV;
     const int64_t nchunk = (tend - tbeg + kPipeChunk - 1) / kPipeChunk;
-    const bool pw = __builtin_amdgcn_readfirstlane(a.pairwise) != 0;
+    // (the position-pair path runs in the 64-column instances only)
+    const bool pw = !WIDE && __builtin_amdgcn_readfirstlane(a.pairwise) != 0;
     const unsigned HDK = (unsigned)H * DK, HDV = (unsigned)H * DV;
     unsigned char *const slot_base = smem + Lds::PREP;
     // Transition columns (v = 0, initial state I), TRANS instances only: once
@@ -1064,7 +1071,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     // S <- e^{b_C} 0 + K^^T 0), so the workgroup stops there and stores the
     // zero state.  Each state wave posts (one byte) whether its 16 columns
     // are all zero before a period's first barrier; every wave reads the
-    // four posts (one dword) right after that barrier and tests them after
+    // posts (one dword per four) right after that barrier and tests them after
     // the second, when the read has long returned; all waves leave after the
     // same period pair, so every wave passes the same barriers.  The next
     // posts are written after the second barrier.  The posts start at zero
@@ -1074,9 +1081,15 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     // exit gets the whole loop duplicated).  The other instances carry none
     // of this: an exit test costs the one-pass loop a few percent.
     unsigned char *const zpost = smem + Lds::ZPOST;
-    constexpr unsigned kAllZero = 0x01010101u;
+    typedef typename std::conditional<(NSW > 4), uint64_t, unsigned>::type Posts;
+    auto all_zero = [](Posts v) {
+        bool z = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v) == 0x01010101u;
+        if constexpr (NSW > 4)
+            z = z && (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32)) == 0x01010101u;
+        return z;
+    };
 
-    if (wave >= 4) {
+    if (wave >= NSW) {
         // =================================================================
         // prep role
         // =================================================================
@@ -1087,14 +1100,17 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         // eight prep waves, four per subtile: a wave covers one subtile's 16
         // tokens x 32 channels; lane = (token group pos, channel pair), 4
         // tokens x 2 channels, so each SIMD runs two prep waves whose
-        // dependency stalls interleave
+        // dependency stalls interleave.  WIDE: four prep waves (one per
+        // SIMD, beside two state waves), each covering its 32 channels in
+        // both subtiles, one after the other
         constexpr int TPL = 4;                      // tokens per lane
         constexpr int NPOS = 16 / TPL;              // token groups per subtile
-        const int p = wave - 4;
-        const int I = p >> 2;                       // subtile of this wave
+        constexpr int NSUB = WIDE ? 2 : 1;          // subtiles per prep wave
+        constexpr int NPREP = 12 - NSW;             // prep waves
+        const int p = wave - NSW;
+        const int I0 = WIDE ? 0 : p >> 2;           // first subtile of this wave
         const int pos = lane >> 4;
         const int c0 = (p & 3) * 32 + 2 * (lane & 15);   // this lane's first channel
-        const int tb = 16 * I + TPL * pos;          // first token of this lane (in the chunk)
         T *sQr = reinterpret_cast<T *>(smem + Lds::QR);
         T *sKr = reinterpret_cast<T *>(smem + Lds::KR);
         T *sKc = reinterpret_cast<T *>(smem + Lds::KC);
@@ -1115,7 +1131,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 
         // the blocks above the diagonal of P (hi, lo) and T in every slot are
         // read by the 32-deep products and never written: zero them once
-        for (int e = lane + 64 * p; e < Lds::NSLOT * 3 * 64; e += 512) {
+        for (int e = lane + 64 * p; e < Lds::NSLOT * 3 * 64; e += 64 * NPREP) {
             const int s_ = e / 192, m = (e / 64) % 3, q4 = e & 63;
             T *tile = reinterpret_cast<T *>(slot_base + s_ * Lds::SLOT +
                                             (m == 0 ? Lds::S_PH : m == 1 ? Lds::S_PL : Lds::S_XR));
@@ -1131,13 +1147,14 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             unsigned k[TPL], q[TPL];                // two bf16 each
             unsigned beta;                          // bf16 bits, zero-extended
         };
-        Raw raw0, raw1;
-        constexpr int NRAW = 3 * TPL + 1;           // loads per set
+        Raw raw0[NSUB], raw1[NSUB];                 // per subtile (beta in the first)
+        constexpr int NRAW = NSUB * 3 * TPL + 1;    // loads per set
         // byte offsets of this lane's first token row and channel pair (k, q
-        // and g); within a full chunk the lane's other rows are scalar steps
-        const unsigned off_kq = ((unsigned)tb * HDK + (unsigned)c0) * 2u;
+        // and g) in subtile I0; within a full chunk the lane's other rows are
+        // scalar steps (16 rows on to the next subtile)
+        const unsigned off_kq = ((unsigned)(16 * I0 + TPL * pos) * HDK + (unsigned)c0) * 2u;
         const unsigned off_b = (unsigned)(lane & 31) * (unsigned)H * 2u;
-        auto load_raw = [&](int64_t ch, Raw &r) {
+        auto load_raw = [&](int64_t ch, Raw (&r)[NSUB]) {
             const int64_t t0 = tbeg + ch * kPipeChunk;
             const int L = (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk);
             const int64_t tok0 = (tok_base + t0) * H + h;
@@ -1148,31 +1165,38 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             // row; last chunk: per-lane offsets from row 0, where rows past
             // the end of the sequence re-read its last row (offsets are
             // unsigned, so the base is never ahead of the address)
-            unsigned okq[TPL], ob = off_b;
+            unsigned okq[NSUB][TPL], ob = off_b;
             const bool tail = L < kPipeChunk;
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) okq[i] = off_kq;
+            for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) okq[u][i] = off_kq;
             if (tail) {
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) {
-                    const int tl = tb + i < L ? tb + i : L - 1;
-                    okq[i] = ((unsigned)tl * HDK + (unsigned)c0) * 2u;
-                }
+                for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+                    for (int i = 0; i < TPL; ++i) {
+                        const int tr = 16 * (I0 + u) + TPL * pos + i;
+                        const int tl = tr < L ? tr : L - 1;
+                        okq[u][i] = ((unsigned)tl * HDK + (unsigned)c0) * 2u;
+                    }
                 const int bl = lane & 31;
                 ob = (unsigned)(bl < L ? bl : L - 1) * (unsigned)H * 2u;
             }
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const unsigned row = tail ? 0u : (unsigned)i * HDK * 2u;
-                if constexpr (ZIN) r.g[i] = vm_load4(gb + row, okq[i]);
-                else r.g[i] = vm_load8_nt(gb + 2u * row, 2u * okq[i]);
-                r.k[i] = vm_load4(kb + row, okq[i]);
-                r.q[i] = vm_load4(qb + row, okq[i]);
-            }
-            r.beta = vm_load_u16(bb, ob);
+            for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const unsigned row = tail ? 0u : (unsigned)(16 * u + i) * HDK * 2u;
+                    if constexpr (ZIN) r[u].g[i] = vm_load4(gb + row, okq[u][i]);
+                    else r[u].g[i] = vm_load8_nt(gb + 2u * row, 2u * okq[u][i]);
+                    r[u].k[i] = vm_load4(kb + row, okq[u][i]);
+                    r[u].q[i] = vm_load4(qb + row, okq[u][i]);
+                }
+            r[0].beta = vm_load_u16(bb, ob);
         };
 
-        auto period = [&](int64_t c, Raw &raw) -> bool {
+        auto period = [&](int64_t c, Raw (&raw)[NSUB]) -> bool {
             const bool live = c < nchunk;
             const int64_t t0 = tbeg + c * kPipeChunk;
             const int L = live ? (int)((tend - t0) < kPipeChunk ? (tend - t0) : kPipeChunk) : 0;
@@ -1190,23 +1214,33 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             // chunk's (one set, NRAW loads) may still be in flight
             vm_wait_or_all<NRAW>(c + 1 < nchunk);
 #pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                vm_fence(raw.g[i]);
-                vm_fence(raw.k[i]);
-                vm_fence(raw.q[i]);
-            }
-            vm_fence(raw.beta);
-            // values carried from P1 to P2
-            floatx2 kR[TPL], qR[TPL], kEt[TPL];
+            for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    vm_fence(raw[u].g[i]);
+                    vm_fence(raw[u].k[i]);
+                    vm_fence(raw[u].q[i]);
+                }
+            vm_fence(raw[0].beta);
+            // values carried from P1 to P2 (per subtile of the wave)
+            floatx2 kR[NSUB][TPL], qR[NSUB][TPL], kEt[NSUB][TPL];
             if (live) {
+                {
+                    const float bv = lane < L ? __uint_as_float(raw[0].beta << 16) : 0.0f;
+                    if (p == 0 && lane < 32) sBeta[lane] = bv;
+                }
+#pragma unroll
+                for (int u = 0; u < NSUB; ++u) {
+                const int I = I0 + u;                       // subtile
+                const int tb = 16 * I + TPL * pos;          // first token of this lane (in the chunk)
                 // ---- P1: alpha and running products; subtile-local tiles ---
                 floatx2 R[TPL], Et[TPL], eLam;
                 // log2(alpha) = g log2(e) of this lane's elements
                 floatx2 l2a[TPL];
 #pragma unroll
                 for (int i = 0; i < TPL; ++i) {
-                    if constexpr (ZIN) l2a[i] = gate_log2_alpha2(zc, unpack2(raw.g[i]));
-                    else l2a[i] = raw.g[i] * kLog2e;
+                    if constexpr (ZIN) l2a[i] = gate_log2_alpha2(zc, unpack2(raw[u].g[i]));
+                    else l2a[i] = raw[u].g[i] * kLog2e;
                 }
                 {
                     // past the end of the sequence alpha = 1 (g = 0): e^{b_C} stops at
@@ -1258,10 +1292,6 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                     eLam = R[TPL - 1] * suf;
                 }
                 if (pos == 0) *reinterpret_cast<floatx2 *>(sEL + I * DK + c0) = eLam;
-                {
-                    const float bv = lane < L ? __uint_as_float(raw.beta << 16) : 0.0f;
-                    if (p == 0 && lane < 32) sBeta[lane] = bv;
-                }
                 if (pw) {
                     // position-pair path: the subtile-local log-decay itself
                     // (in log2 units), summed, never exponentiated here
@@ -1299,34 +1329,34 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int i = 0; i < TPL; ++i) {
                         const int tl = tb + i, r = tl - 16 * IS;
-                        const floatx2 kv = unpack2(raw.k[i]), qv = unpack2(raw.q[i]);
-                        kR[i] = kv * R[i];
-                        qR[i] = qv * R[i];
-                        kEt[i] = kv * Et[i];
+                        const floatx2 kv = unpack2(raw[u].k[i]), qv = unpack2(raw[u].q[i]);
+                        kR[u][i] = kv * R[i];
+                        qR[u][i] = qv * R[i];
+                        kEt[u][i] = kv * Et[i];
                         if constexpr (PW) {
                             // the diagonal tiles take raw k (columns) and raw
                             // q / k (rows) in the rows their dense tiles used
-                            *reinterpret_cast<unsigned *>(sKc + (32 * IS + r) * LDK + c0) = raw.k[i];
+                            *reinterpret_cast<unsigned *>(sKc + (32 * IS + r) * LDK + c0) = raw[u].k[i];
                             if constexpr (IS == 0) {
-                                *reinterpret_cast<unsigned *>(sQr + r * LDK + c0) = raw.q[i];
+                                *reinterpret_cast<unsigned *>(sQr + r * LDK + c0) = raw[u].q[i];
                             } else {
-                                store2v(sKr + tl * LDK + c0, kR[i]);
-                                store2v(sQr + tl * LDK + c0, qR[i]);
-                                *reinterpret_cast<unsigned *>(sKr + r * LDK + c0) = raw.q[i];
+                                store2v(sKr + tl * LDK + c0, kR[u][i]);
+                                store2v(sQr + tl * LDK + c0, qR[u][i]);
+                                *reinterpret_cast<unsigned *>(sKr + r * LDK + c0) = raw[u].q[i];
                             }
                         } else {
-                            store2v(sKr + tl * LDK + c0, kR[i]);
-                            store2v(sQr + tl * LDK + c0, qR[i]);
+                            store2v(sKr + tl * LDK + c0, kR[u][i]);
+                            store2v(sQr + tl * LDK + c0, qR[u][i]);
                             // diagonal pair column tile: k e^{-lam}
-                            store2v(sKc + (32 * IS + r) * LDK + c0, kEt[i] * eNegLam);
+                            store2v(sKc + (32 * IS + r) * LDK + c0, kEt[u][i] * eNegLam);
                         }
                         if constexpr (IS == 0) {
-                            store2v(sKc + (16 + r) * LDK + c0, kEt[i]);   // pair (1, 0)
-                            store2v(sKt + tl * LDKE + c0, kR[i]);          // b = lam in subtile 0
-                            store2v(sQt + tl * LDKE + c0, qR[i]);
+                            store2v(sKc + (16 + r) * LDK + c0, kEt[u][i]);   // pair (1, 0)
+                            store2v(sKt + tl * LDKE + c0, kR[u][i]);          // b = lam in subtile 0
+                            store2v(sQt + tl * LDKE + c0, qR[u][i]);
                         } else {
-                            kh[0][i] = kEt[i][0];                           // b_C - b = Lam_1 - lam
-                            kh[1][i] = kEt[i][1];
+                            kh[0][i] = kEt[u][i][0];                           // b_C - b = Lam_1 - lam
+                            kh[1][i] = kEt[u][i][1];
                         }
                     }
                     if constexpr (IS == 1) {
@@ -1341,11 +1371,12 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                     if (I == 0) tiles(std::integral_constant<int, 0>{}, std::true_type{});
                     else tiles(std::integral_constant<int, 1>{}, std::true_type{});
                 }
+                }   // subtiles
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
             lds_barrier();                                  // BAR1
-            unsigned posts = 0;
-            if constexpr (TRANS) posts = *reinterpret_cast<const unsigned *>(zpost);
+            Posts posts = 0;
+            if constexpr (TRANS) posts = *reinterpret_cast<const Posts *>(zpost);
 
             if (live) {
                 // ---- P2: scores; tiles that need the other subtile's total
@@ -1354,41 +1385,49 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 // state wave 3 (which forms the inverse meanwhile) take none,
                 // the other six take one each.
                 // Position-pair path: prep waves 0 and 1 take the dense tiles
-                // 2 and 3; the diagonal tiles are below.
-                const bool has_tile = pw ? p < 2 : (p & 3) != 3;
-                const int ti = pw ? 2 + (p & 1) : (p < 3 ? p : (p > 3 && p < 7 ? p - 1 : 0));
+                // 2 and 3; the diagonal tiles are below.  WIDE: prep wave p
+                // (SIMD p) takes both tiles of pair p, the one beside state
+                // wave 3 none.
+                constexpr int NTILE = WIDE ? 2 : 1;
+                const bool has_tile = WIDE ? p < 3 : (pw ? p < 2 : (p & 3) != 3);
+                const int ti = WIDE ? 2 * p : (pw ? 2 + (p & 1) : (p < 3 ? p : (p > 3 && p < 7 ? p - 1 : 0)));
                 const int pi = ti >> 1;
                 const int Ib = pi == 0 ? 0 : 1, J = pi == 2 ? 1 : 0;
-                const bool isP = ti & 1;
-                floatx4 sc[1] = {floatx4{0, 0, 0, 0}};
+                floatx4 sc[NTILE];
+#pragma unroll
+                for (int i = 0; i < NTILE; ++i) sc[i] = floatx4{0, 0, 0, 0};
                 if (has_tile) {
                     const int koff = (lane >> 4) * (KF::kStep / 4);
                     const T *xs = sKc + (16 * pi + lr) * LDK + koff;
-                    const T *ys = (isP ? sQr : sKr) + (16 * Ib + lr) * LDK + koff;
-                    group_mma<KF, 1, DK / 32>(
+                    const int yrow = (16 * Ib + lr) * LDK + koff;
+                    group_mma<KF, NTILE, DK / 32>(
                         sc, [&](int, int st) { return xs + st * KF::kStep; },
-                        [&](int, int st) { return ys + st * KF::kStep; });
+                        [&](int i, int st) { return (((ti + i) & 1) ? sQr : sKr) + yrow + st * KF::kStep; });
                 }
                 {
                     const floatx2 e0 = *reinterpret_cast<const floatx2 *>(sEL + c0);
                     const floatx2 e1 = *reinterpret_cast<const floatx2 *>(sEL + DK + c0);
-                    if (I == 1) {
 #pragma unroll
-                        for (int i = 0; i < TPL; ++i) {
-                            store2v(sKt + (tb + i) * LDKE + c0, kR[i] * e0);
-                            store2v(sQt + (tb + i) * LDKE + c0, qR[i] * e0);
-                        }
-                    } else {
-                        float kh[2][TPL];
+                    for (int u = 0; u < NSUB; ++u) {
+                        const int tb = 16 * (I0 + u) + TPL * pos;
+                        if (I0 + u == 1) {
 #pragma unroll
-                        for (int i = 0; i < TPL; ++i) {
-                            const floatx2 v = kEt[i] * e1;
-                            kh[0][i] = v[0];
-                            kh[1][i] = v[1];
+                            for (int i = 0; i < TPL; ++i) {
+                                store2v(sKt + (tb + i) * LDKE + c0, kR[u][i] * e0);
+                                store2v(sQt + (tb + i) * LDKE + c0, qR[u][i] * e0);
+                            }
+                        } else {
+                            float kh[2][TPL];
+#pragma unroll
+                            for (int i = 0; i < TPL; ++i) {
+                                const floatx2 v = kEt[u][i] * e1;
+                                kh[0][i] = v[0];
+                                kh[1][i] = v[1];
+                            }
+                            storeN<TPL>(sKh + c0 * LDT + tb, kh[0]);
+                            storeN<TPL>(sKh + (c0 + 1) * LDT + tb, kh[1]);
+                            if (pos == 0) *reinterpret_cast<floatx2 *>(sEbC + c0) = e0 * e1;
                         }
-                        storeN<TPL>(sKh + c0 * LDT + tb, kh[0]);
-                        storeN<TPL>(sKh + (c0 + 1) * LDT + tb, kh[1]);
-                        if (pos == 0) *reinterpret_cast<floatx2 *>(sEbC + c0) = e0 * e1;
                     }
                 }
                 if (pw) {
@@ -1424,23 +1463,27 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 if (has_tile) {
                     const int r = 16 * Ib + lr;
                     const float br = sBeta[r];
-                    const float rowscale = isP ? 1.0f : br;
-                    // causal mask of the pair: everything below the diagonal block,
-                    // s <= r (P) or s < r (A) inside it
-                    const int lim = J < Ib ? 16 : (isP ? lr + 1 : lr);
-                    floatx4 val;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float x = sc[0][j] * rowscale;
-                        val[j] = lg4 + j < lim ? x : 0.0f;
-                    }
-                    if (isP) {
-                        bf16x4 hi, lo;
-                        split_bf16(val, hi, lo);
-                        *reinterpret_cast<bf16x4 *>(sPh + r * LDT + 16 * J + lg4) = hi;
-                        *reinterpret_cast<bf16x4 *>(sPl + r * LDT + 16 * J + lg4) = lo;
-                    } else {
-                        store4v(sA + r * LDT + 16 * J + lg4, val);
+                    for (int it = 0; it < NTILE; ++it) {
+                        const bool isP = (ti + it) & 1;
+                        const float rowscale = isP ? 1.0f : br;
+                        // causal mask of the pair: everything below the diagonal block,
+                        // s <= r (P) or s < r (A) inside it
+                        const int lim = J < Ib ? 16 : (isP ? lr + 1 : lr);
+                        floatx4 val;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float x = sc[it][j] * rowscale;
+                            val[j] = lg4 + j < lim ? x : 0.0f;
+                        }
+                        if (isP) {
+                            bf16x4 hi, lo;
+                            split_bf16(val, hi, lo);
+                            *reinterpret_cast<bf16x4 *>(sPh + r * LDT + 16 * J + lg4) = hi;
+                            *reinterpret_cast<bf16x4 *>(sPl + r * LDT + 16 * J + lg4) = lo;
+                        } else {
+                            store4v(sA + r * LDT + 16 * J + lg4, val);
+                        }
                     }
                 }
             }
@@ -1473,7 +1516,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 }
             }
             lds_barrier();                                  // BAR2
-            if constexpr (TRANS) return __builtin_amdgcn_readfirstlane(posts) == kAllZero;
+            if constexpr (TRANS) return all_zero(posts);
             else return false;
         };
         if (nchunk > 0) load_raw(0, raw0);         // an empty sequence loads nothing
@@ -1520,10 +1563,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             // transition vanished before its last chunk: M_p = 0, so the
             // state entering segment p + 1 is L_p
             if (a.zc && seg >= 2) {
-                const int *zr = a.zc + ((size_t)(seg - 2) * a.nbh + bh) * (DK / NV);
+                const int *zr = a.zc + ((size_t)(seg - 2) * a.nbh + bh) * NZR;
                 bool gone = true;
 #pragma unroll
-                for (int j = 0; j < DK / NV; ++j) gone = gone && zr[j] < (int)(a.seg_len / kPipeChunk) - 1;
+                for (int j = 0; j < NZR; ++j) gone = gone && zr[j] < (int)(a.seg_len / kPipeChunk) - 1;
                 if (gone) s0 = a.Lb + (size_t)(seg - 2) * a.nbh * DK * DV;
             }
             st = seg == a.nseg - 1 ? a.ST : nullptr;
@@ -1591,8 +1634,43 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         };
         // period c: state pass of chunk c - 2 (v from cur), v of chunk c - 1
         // requested into nxt, inverse of chunk c - 1 (wave 3)
+        // WIDE: the state update of every state wave but the one forming the
+        // inverse runs after the first barrier, where those waves would
+        // otherwise wait (the first half is bound by instruction issue on
+        // every SIMD, the second by the inverse and the score tiles)
+        const bool defer = WIDE && s != 3;
+        typename PF::frag uh_d;                          // U (hi) kept for a deferred update
+        auto s_update = [&](const typename PF::frag &uh, int64_t ch) {
+            const unsigned char *slot = slot_base + (int)(ch % Lds::NSLOT) * Lds::SLOT;
+            const T *sKh = reinterpret_cast<const T *>(slot + Lds::S_KH);
+            const float *sEbC = reinterpret_cast<const float *>(slot + Lds::S_EBC);
+            // S <- Diag(e^{b_C}) S + K^T U
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const typename PF::frag kf = PF::lds(sKh + (16 * cb + lr) * LDT, 0, lg4);
+                sacc[cb] *= *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
+                PF::mma(sacc[cb], kf, uh);
+            }
+#pragma unroll
+            for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
+        };
+        // transition columns: post whether the state is zero in all 64 lanes
+        // (either sign; NaN is not)
+        auto post_zero = [&]() {
+            unsigned nz = 0;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) nz |= __float_as_uint(sacc[cb][j]) << 1;
+            const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
+            if (lane == 0) zpost[s] = zero ? 1 : 0;
+        };
         auto period = [&](int64_t c, unsigned (&cur)[2][4], unsigned (&nxt)[2][4]) -> bool {
             const bool pass = c >= 2 && c - 2 < nchunk;
+            // WIDE posts the state before this period's pass (after chunk
+            // c - 3), the same for every wave whether its update is deferred
+            // or not; the other instances post it after the pass
+            if (TRANS && WIDE && vzero) post_zero();
             // cur was requested a period ago; nothing newer is outstanding
             // except the previous period's o stores
             vm_wait<0>();
@@ -1614,11 +1692,9 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 const unsigned char *slot = slot_base + (int)(ch % Lds::NSLOT) * Lds::SLOT;
                 const T *sKt = reinterpret_cast<const T *>(slot + Lds::S_KT);
                 const T *sQt = reinterpret_cast<const T *>(slot + Lds::S_QT);
-                const T *sKh = reinterpret_cast<const T *>(slot + Lds::S_KH);
                 const T *sPh = reinterpret_cast<const T *>(slot + Lds::S_PH);
                 const T *sPl = reinterpret_cast<const T *>(slot + Lds::S_PL);
                 const T *sXr = reinterpret_cast<const T *>(slot + Lds::S_XR);
-                const float *sEbC = reinterpret_cast<const float *>(slot + Lds::S_EBC);
 
 
                 // Z = K~ S, then D = V - Z (token rows, this column block)
@@ -1674,30 +1750,13 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                             store4v(const_cast<T *>(at<T>(obase, ((unsigned)r * HDV + lg4) * 2u)), oacc[Ir]);
                     }
                 }
-                // S <- Diag(e^{b_C}) S + K^T U
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const typename PF::frag kf = PF::lds(sKh + (16 * cb + lr) * LDT, 0, lg4);
-                    sacc[cb] *= *reinterpret_cast<const floatx4 *>(sEbC + 16 * cb + lg4);
-                    PF::mma(sacc[cb], kf, uh);
-                }
-#pragma unroll
-                for (int t = 0; t < NKS; ++t) sf[t] = PF::regs(&sacc[2 * t]);
+                if (defer) uh_d = uh;
+                else s_update(uh, ch);
             }
-            if (TRANS && vzero) {
-                // transition columns: post whether the state is zero in all
-                // 64 lanes (either sign; NaN is not)
-                unsigned nz = 0;
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) nz |= __float_as_uint(sacc[cb][j]) << 1;
-                const bool zero = __builtin_amdgcn_ballot_w64(nz != 0) == 0;
-                if (lane == 0) zpost[s] = zero ? 1 : 0;
-            }
+            if (TRANS && !WIDE && vzero) post_zero();
             lds_barrier();                                  // BAR1
-            unsigned posts = 0;
-            if constexpr (TRANS) posts = *reinterpret_cast<const unsigned *>(zpost);
+            Posts posts = 0;
+            if constexpr (TRANS) posts = *reinterpret_cast<const Posts *>(zpost);
             if (s == 3 && c >= 1 && c - 1 < nchunk) {
                 // ---- X = (I + A)^-1 and T = X Diag(beta) of chunk c - 1 ------
                 const int64_t ch = c - 1;
@@ -1762,9 +1821,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 store4v(sXr + (16 + lr) * LDT + 16 + lg4, xT[1] * b1);
                 store4v(sXr + (16 + lr) * LDT + lg4, x10T * b0);
             }
+            if (defer && pass) s_update(uh_d, c - 2);
             if (pw) lds_barrier();                          // position-pair path: partials complete
             lds_barrier();                                  // BAR2
-            if constexpr (TRANS) return __builtin_amdgcn_readfirstlane(posts) == kAllZero;
+            if constexpr (TRANS) return all_zero(posts);
             else return false;
         };
         bool stop = false, stop1 = false;
@@ -1778,12 +1838,15 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         if constexpr (TRANS) {
             // the stopping split: a stop in the pair (c - 2, c - 1) saw the
             // state zero after chunk c - 4 (the pass of period c - 2) when its
-            // first period posted it, else after chunk c - 3; without a stop
-            // every chunk counts
+            // first period posted it, else after chunk c - 3 (one chunk less
+            // when the posts are of the state before the pass); without a
+            // stop every chunk counts
             if (vzero && a.zc && s == 0 && lane == 0) {
-                const int64_t z0 = stop1 ? c - 4 : c - 3;
+                const int64_t z0 = (stop1 ? c - 4 : c - 3) - (WIDE ? 1 : 0);
                 const int64_t zl = stop && z0 < nchunk - 1 ? z0 : nchunk - 1;
-                a.zc[((size_t)(seg - 1) * a.nbh + bh) * (DK / NV) + (slice - a.nsl_v)] = (int)zl;
+                int *zw = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * NZR + (slice - a.nsl_v) * NZC;
+#pragma unroll
+                for (int j = 0; j < NZC; ++j) zw[j] = (int)zl;   // one record per 64 columns
             }
         }
         if (st && lsrc) {
@@ -2132,51 +2195,88 @@ static double split_phase_time(int64_t n1, double d1, int64_t n2, double d2) {
     return t + d1 + rounds(n2 - k * freecu) * d2;
 }
 
-// The count minimising a model of the wall time, fitted to measured sweeps
-// of forced counts (B1 H8 T4096 and B1 H32 T1M).  A segment of n tokens
-// costs n + 64 token-times (the pipeline's two fill periods); a split adds 33
-// token-times per chaining step and 145 for its extra launches.
+// A model of the wall time, in token-times of a 64-column workgroup, fitted
+// to measured sweeps of forced counts and layouts (B1..B8 H32 T32768, B1 H8
+// T4096, B1 H32 T1M).  A segment of n tokens costs n + 64 token-times (the
+// pipeline's two fill periods), times 1.45 for a per-chain workgroup (its
+// period forms every column's state pass; its operands once); a split adds
+// 33 token-times per chaining step and 145 for its extra launches.
 //  - Full rerun: a launch of W workgroups runs ceil(W / CUs) rounds of one
 //    segment (transitions priced at a whole segment).
 //  - Stopping split (the default): phase 1 places the v workgroups of all P
 //    segments, then the transitions; the transitions and phase 3 are priced
-//    as ending 0.15 of the way into a segment (at least two chunks), an
+//    as ending 2% of the way into a segment (at least two chunks), an
 //    assumption about the gates: the transition vanishes once every
 //    channel's cumulative decay has underflowed, which synthetic gates of
-//    the pages' range reach within a chunk or two and gates that keep
-//    memory reach later or never (phase 3 then reruns the whole segment).
-//    The fraction is fitted to forced-count sweeps of B1 H8 T4096 (best
-//    P = 10) and B1 H32 T1M (P = 4).
-int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun) {
+//    the pages' range reach within a few chunks and gates that keep memory
+//    reach later or never (phase 3 then reruns the whole segment, and the
+//    transitions run whole after the v workgroups).
+static constexpr double kWideCost = 1.45;
+
+static double split_cost(int64_t B, int64_t T, int64_t H, int dk, int dv, int rerun, bool wide,
+                         int P) {
     constexpr int64_t kCUs = 256;             // MI355X compute units
-    constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
     constexpr int64_t kFillTokens = 64;       // two pipeline periods per segment
     constexpr int64_t kChainStepTokens = 33;  // one chaining step
     constexpr int64_t kSplitTokens = 145;     // the two extra launches
-    constexpr double kVanishFrac = 0.15;      // stopping split: where transitions end
-    if (!seq_split_supported(dk, dv, is_bf16)) return 1;
-    const int64_t bh = B * H, nsl_v = dv / 64, nsl_m = dk / 64;
+    constexpr double kVanishFrac = 0.02;      // stopping split: where transitions end
+    const int nv = wide ? 128 : 64;
+    const int64_t bh = B * H, nsl_v = dv / nv, nsl_m = dk / nv;
+    const double f = wide ? kWideCost : 1.0;
     auto rounds = [](int64_t w) { return (w + kCUs - 1) / kCUs; };
-    // a split must beat one pass by 10%
-    double best = 0.9 * (double)(T + kFillTokens) * (double)rounds(bh * nsl_v);
+    if (P < 2) return f * (double)(T + kFillTokens) * (double)rounds(bh * nsl_v);
+    const int64_t pe = seq_split_effective(T, P), len = seq_split_segment_len(T, P);
+    double cost = (double)kChainStepTokens * (double)(pe - 2) + (double)kSplitTokens;
+    if (rerun) {
+        const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
+        return cost + f * (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3));
+    }
+    double part = kVanishFrac * (double)len;
+    if (part < 2.0 * kPipeChunk) part = 2.0 * kPipeChunk;
+    if (part > (double)len) part = (double)len;
+    const double dseg = f * (double)(len + kFillTokens), dpart = f * (part + (double)kFillTokens);
+    return cost + split_phase_time(bh * nsl_v * pe, dseg, bh * nsl_m * (pe - 1), dpart) +
+           split_phase_time(bh * nsl_v * (pe - 1), dpart, 0, 0.0);
+}
+
+bool seq_wide_supported(int dk, int dv, int is_bf16) {
+    return seq_split_supported(dk, dv, is_bf16) && dv == 128;
+}
+
+int seq_layout(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun, int P,
+               int layout) {
+    if (!seq_wide_supported(dk, dv, is_bf16)) return 0;
+    if (layout >= 0) return layout;
+    const int pe = P >= 2 ? seq_split_effective(T, P) : 1;
+    return split_cost(B, T, H, dk, dv, rerun, true, pe) < split_cost(B, T, H, dk, dv, rerun, false, pe)
+               ? 1 : 0;
+}
+
+// The count minimising the model over the layouts allowed (a split must
+// beat the best one pass by 10%).
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun,
+                   int layout) {
+    constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
+    if (!seq_split_supported(dk, dv, is_bf16)) return 1;
+    const bool can_wide = seq_wide_supported(dk, dv, is_bf16);
+    const bool try_narrow = layout != 1 || !can_wide, try_wide = can_wide && layout != 0;
+    auto best_of = [&](int P) {
+        double c = 1e300;
+        if (try_narrow) c = split_cost(B, T, H, dk, dv, rerun, false, P);
+        if (try_wide) {
+            const double w = split_cost(B, T, H, dk, dv, rerun, true, P);
+            if (w < c) c = w;
+        }
+        return c;
+    };
+    double best = 0.9 * best_of(1);
     int best_p = 1;
     int64_t pmax = T / kMinSegTokens;
     if (pmax > 255) pmax = 255;
     for (int P = rerun ? 3 : 2; P <= pmax; ++P) {
-        const int64_t pe = seq_split_effective(T, P), len = seq_split_segment_len(T, P);
+        const int64_t pe = seq_split_effective(T, P);
         if (pe < (rerun ? 3 : 2)) continue;
-        double cost = (double)kChainStepTokens * (double)(pe - 2) + (double)kSplitTokens;
-        if (rerun) {
-            const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
-            cost += (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3));
-        } else {
-            double part = kVanishFrac * (double)len;
-            if (part < 2.0 * kPipeChunk) part = 2.0 * kPipeChunk;
-            if (part > (double)len) part = (double)len;
-            const double dseg = (double)(len + kFillTokens), dpart = part + (double)kFillTokens;
-            cost += split_phase_time(bh * nsl_v * pe, dseg, bh * nsl_m * (pe - 1), dpart) +
-                    split_phase_time(bh * nsl_v * (pe - 1), dpart, 0, 0.0);
-        }
+        const double cost = best_of(P);
         if (cost < best) {
             best = cost;
             best_p = P;
@@ -2217,17 +2317,26 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            int split_rerun, hipStream_t s) {
+                            int split_rerun, int wide, hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
     // the gate inside the kernel: pipelined kernel only
     const bool zin = z != nullptr;
     if (zin && (!pipe || !Ag)) return hipErrorInvalidValue;
-    auto kern = zin ? chunk32_kernel<128, true, false> : chunk32_kernel<128, false, false>;
-    // the first phase of a split, whose transition columns may end early
-    auto kern_tr = zin ? chunk32_kernel<128, true, true> : chunk32_kernel<128, false, true>;
-    const int nv = pipe ? 64 : slice_width(dk, dv, is_bf16);
+    // one workgroup per chain (all 128 columns, the chunk's operands
+    // prepared once) or per 64-column slice
+    if (wide && !(pipe && dv == 128 && !pairwise)) return hipErrorInvalidValue;
+    typedef void (*Kern)(ChunkArgs);
+    Kern kern, kern_tr;                             // kern_tr: a split's first phase
+    if (wide) {
+        kern = zin ? chunk32_kernel<128, true, false, true> : chunk32_kernel<128, false, false, true>;
+        kern_tr = zin ? chunk32_kernel<128, true, true, true> : chunk32_kernel<128, false, true, true>;
+    } else {
+        kern = zin ? chunk32_kernel<128, true, false, false> : chunk32_kernel<128, false, false, false>;
+        kern_tr = zin ? chunk32_kernel<128, true, true, false> : chunk32_kernel<128, false, true, false>;
+    }
+    const int nv = pipe ? (wide ? 128 : 64) : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
     args.S0 = S0; args.ST = ST; args.o = o;
@@ -2263,7 +2372,7 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         // and M it never uses)
         const int units1 = (split_rerun ? P - 1 : P) * args.nbh;
         args.phase = 1;
-        args.nslice = args.nsl_v + dk / 64;
+        args.nslice = args.nsl_v + dk / nv;
         args.xcd_map = units1 % 8 == 0 ? 1 : 0;
         hipLaunchKernelGGL(kern_tr, dim3(units1 * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();

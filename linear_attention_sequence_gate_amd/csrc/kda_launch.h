@@ -23,12 +23,13 @@ hipError_t launch_range_check(const float *g, int64_t B, int64_t T, int64_t H, i
 // axis (pipelined path, one pass; T is then the packed token count).
 // z != nullptr: the gate is evaluated inside the kernel from z (input dtype,
 // laid out like k) and the [H, dk] table Ag; g is not read (pipelined path).
+// wide: one workgroup per chain (pipelined path, dv = 128, not pairwise).
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            int split_rerun, hipStream_t s);
+                            int split_rerun, int wide, hipStream_t s);
 
 // Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
 bool seq_split_supported(int dk, int dv, int is_bf16);
@@ -37,8 +38,17 @@ bool seq_split_supported(int dk, int dv, int is_bf16);
 int64_t seq_split_segment_len(int64_t T, int nseg);
 int seq_split_effective(int64_t T, int nseg);
 // Segment count picked for these sizes (1 = no split), for the stopping
-// split or (rerun) the one whose last phase reruns whole segments.
-int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun);
+// split or (rerun) the one whose last phase reruns whole segments, over the
+// workgroup layouts allowed (layout: -1 either, 0 per 64-column slice, 1 per
+// chain).
+int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun,
+                   int layout);
+// One workgroup per chain: bf16, dk = dv = 128.
+bool seq_wide_supported(int dk, int dv, int is_bf16);
+// The layout (0 per slice, 1 per chain) for P segments: `layout` when it is
+// forced (>= 0), else the cheaper one in the same model.
+int seq_layout(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun, int P,
+               int layout);
 // Device bytes the split needs (0 when it does not split).
 size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg);
 

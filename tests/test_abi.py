@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
               "kda_chunk_fwd_workspace_size_segments", "kda_chunk_fwd_auto_segments",
-              "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
+              "kda_chunk_fwd_plan", "kda_decode_step", "kda_state_pool_reset", "kda_chunk_fwd_pooled",
               "kda_chunk_fwd_varlen_pooled", "kda_decode_step_pooled", "kda_chunk_bwd",
               "kda_chunk_bwd_workspace_size", "kda_gate_bwd", "kda_gate_bwd_workspace_size",
               "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size",
@@ -90,7 +90,19 @@ def test_chunk_validation(L):
     assert chunk(L, k=BAD) == E.KDA_ERR_INVALID_ARGUMENT          # misaligned
     assert chunk(L, o=P) == E.KDA_ERR_INVALID_ARGUMENT            # o aliases q
     assert chunk(L, flags=4) == E.KDA_ERR_INVALID_ARGUMENT        # unknown flag
-    assert chunk(L, flags=E.KDA_FLAG_SPLIT_FULL_RERUN << 1) == E.KDA_ERR_INVALID_ARGUMENT
+    assert chunk(L, flags=E.KDA_FLAG_WORKGROUP_PER_SLICE << 1) == E.KDA_ERR_INVALID_ARGUMENT
+    # one workgroup per chain: the pipelined path at dk = dv = 128 only, not
+    # with the position-pair path, and not together with the per-slice layout
+    both = E.KDA_FLAG_WORKGROUP_PER_CHAIN | E.KDA_FLAG_WORKGROUP_PER_SLICE
+    assert chunk(L, flags=both) == E.KDA_ERR_INVALID_ARGUMENT
+    assert "exclude" in _lib.kda_last_error()
+    assert chunk(L, flags=E.KDA_FLAG_WORKGROUP_PER_CHAIN) == E.KDA_ERR_UNSUPPORTED   # dk = 32
+    assert "per chain" in _lib.kda_last_error()
+    assert chunk(L, dk=128, dv=64, flags=E.KDA_FLAG_WORKGROUP_PER_CHAIN) == E.KDA_ERR_UNSUPPORTED
+    assert chunk(L, dk=128, dv=128, flags=E.KDA_FLAG_WORKGROUP_PER_CHAIN |
+                 E.KDA_FLAG_PAIRWISE_DIAGONAL) == E.KDA_ERR_UNSUPPORTED
+    assert chunk(L, dt=0, dk=128, dv=128, ws=P3,
+                 flags=E.KDA_FLAG_WORKGROUP_PER_CHAIN) == E.KDA_ERR_UNSUPPORTED   # fp32
     assert chunk(L, flags=E.KDA_FLAG_TOKEN_BACKWARD) == E.KDA_ERR_INVALID_ARGUMENT   # backward only
     assert chunk(L, flags=E.KDA_FLAG_PAIRWISE_DIAGONAL) == E.KDA_ERR_UNSUPPORTED   # dk = 32
     assert "position-pair" in _lib.kda_last_error()
@@ -132,16 +144,21 @@ def test_sequence_split_workspace_and_policy(L):
         zc = -(-(P - 1) * B * H * 2 * 4 // 256) * 256
         return 256 + 2 * (P - 1) * vsz + (P - 2) * msz + (P - 2) * msz * scan + zc
 
-    # B4 H32 T32K: 256 workgroups of 64 columns fill the GPU in one pass
-    assert auto(4, 32768, 32, 128, 128, 1) == 1
-    assert ws(4, 32768, 32, 128, 128, 1) == 256
-    # B1 H32 T1M: 64 workgroups in one pass; the split takes a few segments
-    # (the stopping split: the v workgroups of all segments in one round)
+    # B8 H32 T32K: 256 chains, one workgroup each, fill the GPU in one pass
+    assert auto(8, 32768, 32, 128, 128, 1) == 1
+    assert ws(8, 32768, 32, 128, 128, 1) == 256
+    # B4 H32 T32K: 128 chains; two segments of each fill the GPU with one
+    # workgroup per chain and segment (cheaper than 256 workgroups of 64
+    # columns in one pass, which form every chunk's operands twice)
+    assert auto(4, 32768, 32, 128, 128, 1) == 2
+    assert ws(4, 32768, 32, 128, 128, 1) == split_bytes(4, 32, 128, 2)
+    # B1 H32 T1M: 32 chains; the split takes eight segments (the stopping
+    # split: the v workgroups of all segments in one round)
     P = auto(1, 1 << 20, 32, 128, 128, 1)
-    assert P == 4, P
-    # the automatic workspace covers the count of either scheme
+    assert P == 8, P
+    # the automatic workspace covers the count of either scheme and layout
     assert ws(1, 1 << 20, 32, 128, 128, 1) >= split_bytes(1, 32, 128, P)
-    assert ws(1, 1 << 20, 32, 128, 128, 1) in [split_bytes(1, 32, 128, n) for n in range(P, 10)]
+    assert ws(1, 1 << 20, 32, 128, 128, 1) in [split_bytes(1, 32, 128, n) for n in range(P, 17)]
     assert wss(1, 1 << 20, 32, 128, 128, 1, 0) == ws(1, 1 << 20, 32, 128, 128, 1)
     assert wss(1, 1 << 20, 32, 128, 128, 1, P) == split_bytes(1, 32, 128, P)
     # one chain: many more segments
@@ -158,10 +175,11 @@ def test_sequence_split_workspace_and_policy(L):
     assert 3 <= P8 <= 32, P8
     assert wss(1, 4096, 8, 128, 128, 1, P8) == split_bytes(1, 8, 128, P8)
     assert ws(1, 4096, 8, 128, 128, 1) >= split_bytes(1, 8, 128, P8)
-    # half the GPU (128 workgroups): the stopping split's two segments fill it
-    assert auto(8, 4096, 8, 128, 128, 1) == 2
+    # 64 and 128 chains: four and two segments fill the GPU
+    assert auto(8, 4096, 8, 128, 128, 1) == 4
+    assert auto(16, 4096, 8, 128, 128, 1) == 2
     # enough chains to fill the GPU, or too short to split: one pass
-    assert auto(16, 4096, 8, 128, 128, 1) == 1
+    assert auto(32, 4096, 8, 128, 128, 1) == 1
     assert auto(1, 383, 1, 128, 128, 1) == 1 and ws(1, 383, 1, 128, 128, 1) == 256
     # shapes without the pipelined kernel run in one pass
     assert auto(1, 1 << 20, 1, 64, 64, 1) == 1
@@ -392,7 +410,8 @@ def test_gated_workspace_query(L):
     q = L.kda_chunk_fwd_gated_workspace_size
     base = L.kda_chunk_fwd_workspace_size
     # fused shapes: exactly what kda_chunk_fwd takes (range counter, split buffers)
-    assert q(4, 32768, 32, 128, 128, 1) == base(4, 32768, 32, 128, 128, 1) == 256
+    assert q(8, 32768, 32, 128, 128, 1) == base(8, 32768, 32, 128, 128, 1) == 256
+    assert q(4, 32768, 32, 128, 128, 1) == base(4, 32768, 32, 128, 128, 1) > 256
     assert q(1, 1 << 20, 32, 128, 128, 1) == base(1, 1 << 20, 32, 128, 128, 1) > 256
     # staged shapes: g (B T H dk fp32, rounded to 256 bytes) in front
     assert q(2, 100, 3, 64, 64, 1) == 256 + (2 * 100 * 3 * 64 * 4 + 255) // 256 * 256
@@ -421,3 +440,40 @@ def test_binding_constants_match_the_header():
     assert len(header) >= 11, header
     for n, v in header.items():
         assert getattr(_lib, n) == v, n
+
+
+def test_chunk_plan(L):
+    """The plan the chunked prefill follows: segments and workgroup layout
+    for the library's choice and under each flag (host only)."""
+    E = _lib
+    plan = _lib.kda_chunk_fwd_plan
+    CH, SL, seg = E.KDA_FLAG_WORKGROUP_PER_CHAIN, E.KDA_FLAG_WORKGROUP_PER_SLICE, E.kda_flag_segments
+    # the library's choice agrees with kda_chunk_fwd_auto_segments
+    for B, T, H in ((8, 32768, 32), (4, 32768, 32), (1, 1 << 20, 32), (1, 4096, 8), (1, 383, 1)):
+        P, _ = plan(B, T, H, 128, 128, 1)
+        assert P == L.kda_chunk_fwd_auto_segments(B, T, H, 128, 128, 1), (B, T, H)
+    # 256 chains: one workgroup each, one pass; 128 chains: two segments of each
+    assert plan(8, 32768, 32, 128, 128, 1) == (1, True)
+    assert plan(4, 32768, 32, 128, 128, 1) == (2, True)
+    # one pass forced: 256 slice workgroups beat 128 chain workgroups
+    assert plan(4, 32768, 32, 128, 128, 1, seg(1)) == (1, False)
+    # forced layouts, with the count chosen for that layout
+    assert plan(4, 32768, 32, 128, 128, 1, SL) == (1, False)
+    assert plan(4, 32768, 32, 128, 128, 1, CH | seg(1)) == (1, True)
+    assert plan(4, 32768, 32, 128, 128, 1, CH | seg(3)) == (3, True)
+    # a requested count reports the count its aligned segment length gives
+    assert plan(1, 64, 2, 128, 64, 1, seg(3)) == (2, False)
+    # per-slice only: dv = 64, the position-pair path, other shapes
+    assert plan(4, 32768, 32, 128, 64, 1)[1] is False
+    assert plan(4, 32768, 32, 128, 128, 1, E.KDA_FLAG_PAIRWISE_DIAGONAL)[1] is False
+    assert plan(4, 32768, 32, 64, 64, 1) == (1, False)
+    assert plan(4, 32768, 32, 128, 128, 0) == (1, False)       # fp32
+    # rejected as the call rejects them
+    with pytest.raises(_lib.KdaError):
+        plan(4, 32768, 32, 128, 64, 1, CH)
+    with pytest.raises(_lib.KdaError):
+        plan(4, 32768, 32, 128, 128, 1, CH | SL)
+    with pytest.raises(_lib.KdaError):
+        plan(1, 64, 1, 32, 32, 1, seg(3))
+    with pytest.raises(_lib.KdaError):
+        plan(0, 64, 1, 128, 128, 1)

@@ -31,7 +31,7 @@ def _outputs(x):
             torch.empty((B, H, dk, dv), device="cuda", dtype=torch.float32))
 
 
-@pytest.mark.parametrize("B,T,H,nseg", [(1, 6000, 2, 15), (2, 700, 4, 4), (8, 700, 16, 1)])
+@pytest.mark.parametrize("B,T,H,nseg", [(1, 6000, 2, 12), (2, 700, 4, 4), (8, 700, 16, 1)])
 def test_noalloc_call_replays_in_a_captured_graph(B, T, H, nseg):
     segs = _lib.kda_chunk_fwd_auto_segments(B, T, H, 128, 128, _lib.KDA_BF16)
     say("noalloc graph", f"B{B} T{T} H{H}", f"segments {segs}")

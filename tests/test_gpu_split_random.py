@@ -1,7 +1,8 @@
 """A seeded random sweep of the sequence split against the oracle: batch,
 heads, a ragged length, the segment count, the scheme (the last phase stopping
-where a segment's transition vanished, or rerunning whole segments), dv, an
-initial state or none, the fused gate or a given g, and per head a gate that
+where a segment's transition vanished, or rerunning whole segments), the
+workgroup layout (per chain, per 64-column slice, or the library's; dv = 128),
+dv, an initial state or none, the fused gate or a given g, and per head a gate that
 decays fast, slowly everywhere, or slowly over a random token range only, so
 that transitions vanish within a chunk or two, late, never, or in some
 segments and not in others (the chaining then mixes skipped steps and
@@ -31,8 +32,10 @@ def _draw(i):
         lo = r.randint(0, T - 1)
         hi = r.randint(lo + 1, T)
         slow.append((kind, lo, hi))
-    return dict(B=B, H=H, T=T, dv=r.choice([64, 128]), nseg=r.randint(2, 14),
+    dv = r.choice([64, 128])
+    return dict(B=B, H=H, T=T, dv=dv, nseg=r.randint(2, 14),
                 rerun=r.random() < 0.4, s0=r.random() < 0.5, fused=r.random() < 0.5,
+                layout=r.choice(["chain", "slice", "auto"]) if dv == 128 else "auto",
                 slow=slow, seed=9600 + i)
 
 
@@ -51,6 +54,8 @@ def test_random_split_case_matches_oracle(i):
             z[:, lo:hi, h] -= 6.0
     x["z"] = z.to(BF16)
     flags = _lib.kda_flag_segments(c["nseg"]) | (_lib.KDA_FLAG_SPLIT_FULL_RERUN if c["rerun"] else 0)
+    flags |= {"chain": _lib.KDA_FLAG_WORKGROUP_PER_CHAIN, "slice": _lib.KDA_FLAG_WORKGROUP_PER_SLICE,
+              "auto": 0}[c["layout"]]
     if c["fused"]:
         o, S = kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
                                    flags=flags)

@@ -26,11 +26,10 @@ def chunk_asm(tmp_path_factory):
 
 
 # every instance of the pipelined kernel: g loaded or the gate fused (z
-# loaded), each without and with the transition columns' early end
-KERNELS = ["_ZN3kda14chunk32_kernelILi128ELb0ELb0EEEvNS_9ChunkArgsE",
-           "_ZN3kda14chunk32_kernelILi128ELb1ELb0EEEvNS_9ChunkArgsE",
-           "_ZN3kda14chunk32_kernelILi128ELb0ELb1EEEvNS_9ChunkArgsE",
-           "_ZN3kda14chunk32_kernelILi128ELb1ELb1EEEvNS_9ChunkArgsE"]
+# loaded), each without and with the transition columns' early end, in the
+# 64-column and the per-chain (128-column) layout
+KERNELS = ["_ZN3kda14chunk32_kernelILi128ELb%dELb%dELb%dEEEvNS_9ChunkArgsE" % (z, t, w)
+           for w in (0, 1) for t in (0, 1) for z in (0, 1)]
 
 
 @pytest.mark.parametrize("name", KERNELS)
