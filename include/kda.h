@@ -174,13 +174,20 @@ int kda_chunk_fwd_auto_segments(int64_t B, int64_t T, int64_t H,
  *   *per_chain : 1 when one workgroup covers a whole chain's 128 state
  *                columns, 0 when one covers a 64-column slice (and for every
  *                shape outside the pipelined path)
+ *   *guarded   : 1 when the library's two-segment split is guarded: a probe
+ *                launch first runs the second segment's transitions for a
+ *                few chunks, and the split runs only if every chain's
+ *                transition vanished there; otherwise the one pass (the plan
+ *                with KDA_FLAG_SEGMENTS(1)) runs instead, decided on the
+ *                device (no host synchronisation).  Picked where gates that
+ *                keep memory would make the split slower than one pass.
  * The flags that matter: the segment bits, KDA_FLAG_SPLIT_FULL_RERUN,
  * KDA_FLAG_PAIRWISE_DIAGONAL and the workgroup layout flags.  Returns KDA_OK,
  * or the error the call would give for sizes or flags it rejects (outputs
  * untouched).  Host only: launches nothing.
  */
 int kda_chunk_fwd_plan(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int dtype,
-                       unsigned flags, int *segments, int *per_chain);
+                       unsigned flags, int *segments, int *per_chain, int *guarded);
 
 /*
  * As kda_chunk_fwd_workspace_size for an explicit segment count (the value

@@ -74,7 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kda_chunk_fwd_auto_segments.argtypes = [i64, i64, i64, i64, i64, c_int]
     L.kda_chunk_fwd_auto_segments.restype = c_int
     L.kda_chunk_fwd_plan.argtypes = [i64, i64, i64, i64, i64, c_int, ctypes.c_uint,
-                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+                                     ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
     L.kda_chunk_fwd_plan.restype = c_int
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i64, i64, i64, i64, i64, c_int, ctypes.c_uint, vp]
@@ -265,12 +265,16 @@ def kda_chunk_fwd_auto_segments(B: int, T: int, H: int, dk: int, dv: int, dtype:
 
 
 def kda_chunk_fwd_plan(B: int, T: int, H: int, dk: int, dv: int, dtype: int,
-                       flags: int = 0) -> Tuple[int, bool]:
+                       flags: int = 0, with_guard: bool = False):
     """(segments per sequence, one workgroup per chain?) that kda_chunk_fwd
-    follows for these sizes and flags given the workspace the library asks for."""
-    seg, per_chain = ctypes.c_int(0), ctypes.c_int(0)
+    follows for these sizes and flags given the workspace the library asks
+    for; with_guard adds whether a two-segment split is guarded (a probe picks
+    it or the one pass on the device)."""
+    seg, per_chain, guarded = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     _check(load_library().kda_chunk_fwd_plan(B, T, H, dk, dv, dtype, flags, ctypes.byref(seg),
-                                             ctypes.byref(per_chain)))
+                                             ctypes.byref(per_chain), ctypes.byref(guarded)))
+    if with_guard:
+        return seg.value, bool(per_chain.value), bool(guarded.value)
     return seg.value, bool(per_chain.value)
 
 

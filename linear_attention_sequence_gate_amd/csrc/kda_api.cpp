@@ -193,10 +193,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
 }
 
 int kda_chunk_fwd_plan(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int dtype,
-                       unsigned flags, int *segments, int *per_chain) {
+                       unsigned flags, int *segments, int *per_chain, int *guarded) {
     const char *who = "kda_chunk_fwd_plan";
     if (int e = check_dtype(dtype)) return e;
-    if (!segments || !per_chain) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+    if (!segments || !per_chain || !guarded) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
     if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", who);
     if (!valid_dim(dk) || !valid_dim(dv))
@@ -224,6 +224,11 @@ int kda_chunk_fwd_plan(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, 
     nseg = pipe && nseg >= 2 ? kda::seq_split_effective(T, nseg) : 1;
     *segments = nseg;
     *per_chain = kda::seq_layout(B, T, H, (int)dk, (int)dv, bf, rerun, nseg, layout);
+    *guarded = 0;
+    if (req_seg == 0 && !rerun && nseg == 2) {
+        const int fb = kda::seq_layout(B, T, H, (int)dk, (int)dv, bf, 0, 1, layout);
+        *guarded = kda::seq_split_guarded(B, T, H, (int)dk, (int)dv, bf, nseg, *per_chain, fb) ? 1 : 0;
+    }
     return ok();
 }
 
@@ -386,10 +391,17 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         }
     }
     const int wide = kda::seq_layout(B, T, H, (int)dk, (int)dv, is_bf16, rerun, nseg, layout);
+    // the library's two-segment split, guarded against gates that keep
+    // memory when one pass would then be faster
+    int guarded = 0, fallback_wide = 0;
+    if (req_seg == 0 && !rerun && split_ws) {
+        fallback_wide = kda::seq_layout(B, T, H, (int)dk, (int)dv, is_bf16, 0, 1, layout);
+        guarded = kda::seq_split_guarded(B, T, H, (int)dk, (int)dv, is_bf16, nseg, wide, fallback_wide) ? 1 : 0;
+    }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, initial_state, final_state, o, B, T, H,
                                          (int)dk, (int)dv, is_bf16, nseg, split_ws, slots, n_slots,
                                          pairwise ? 1 : 0, cu_seqlens, fused ? z : nullptr,
-                                         fused ? Ag : nullptr, rerun, wide, s);
+                                         fused ? Ag : nullptr, rerun, wide, guarded, fallback_wide, s);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
     return ok();
 }

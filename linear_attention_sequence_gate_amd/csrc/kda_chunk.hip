@@ -78,6 +78,16 @@ struct ChunkArgs {
     int phase, seg0, nseg, nsl_v;
     float *Sin, *Lb, *Mb;
     int *zc;
+    // Probe (phase 1 with transition slices only, nsl_v = 0): the transitions
+    // run at most probe_chunks chunks; one that has not vanished by then is
+    // recorded as never vanishing (the segment's last chunk).
+    int probe_chunks;
+    // Guard: with guard_mode 1 the launch runs only when every one of the
+    // guard_n records at guard is below guard_lim (each chain's transition
+    // vanished before its segment's last chunk: the split is taken), with
+    // guard_mode 2 only when not; otherwise every workgroup returns at once.
+    const int *guard;
+    int guard_n, guard_lim, guard_mode;
     // state pool: when set, S0 and ST are [n_slots, H, dk, dv] and sequence
     // b uses slot slots[b] (a slot outside the pool skips the sequence)
     const int *slots;
@@ -1000,6 +1010,14 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg4 = (lane >> 4) * 4;
+    if (a.guard_mode) {
+        // every wave reads the same records, so the whole workgroup leaves
+        // together, before any barrier
+        bool late = false;
+        for (int i = lane; i < a.guard_n; i += 64) late = late || a.guard[i] >= a.guard_lim;
+        const bool taken = __builtin_amdgcn_ballot_w64(late) == 0;
+        if (taken != (a.guard_mode == 1)) return;
+    }
 
     // block -> (unit, slice), unit -> (segment, chain); with the XCD map the
     // slices of one unit share an XCD (and its L2 for q, k, g).  With
@@ -1050,6 +1068,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     // the stopping split's last phase: the chunks up to the one after which
     // the segment's transition vanished (all of them when it never did)
     int64_t tend = tseg;
+    if (a.probe_chunks > 0) {
+        const int64_t tp = tbeg + (int64_t)a.probe_chunks * kPipeChunk;
+        if (tp < tend) tend = tp;
+    }
     if (a.phase == 3 && a.zc) {
         const int *zr = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * NZR;
         int zl = zr[0];
@@ -1843,7 +1865,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             // stop every chunk counts
             if (vzero && a.zc && s == 0 && lane == 0) {
                 const int64_t z0 = (stop1 ? c - 4 : c - 3) - (WIDE ? 1 : 0);
-                const int64_t zl = stop && z0 < nchunk - 1 ? z0 : nchunk - 1;
+                // no stop: every chunk of the segment counts (a probe that
+                // ran out of chunks has not seen the transition vanish)
+                const int64_t last = (tseg - tbeg + kPipeChunk - 1) / kPipeChunk - 1;
+                const int64_t zl = stop && z0 < nchunk - 1 ? z0 : last;
                 int *zw = a.zc + ((size_t)(seg - 1) * a.nbh + bh) * NZR + (slice - a.nsl_v) * NZC;
 #pragma unroll
                 for (int j = 0; j < NZC; ++j) zw[j] = (int)zl;   // one record per 64 columns
@@ -2213,13 +2238,14 @@ static double split_phase_time(int64_t n1, double d1, int64_t n2, double d2) {
 //    transitions run whole after the v workgroups).
 static constexpr double kWideCost = 1.45;
 
+static constexpr double kVanishFrac = 0.02;   // stopping split: where transitions end
+
 static double split_cost(int64_t B, int64_t T, int64_t H, int dk, int dv, int rerun, bool wide,
-                         int P) {
+                         int P, double vanish = kVanishFrac) {
     constexpr int64_t kCUs = 256;             // MI355X compute units
     constexpr int64_t kFillTokens = 64;       // two pipeline periods per segment
     constexpr int64_t kChainStepTokens = 33;  // one chaining step
     constexpr int64_t kSplitTokens = 145;     // the two extra launches
-    constexpr double kVanishFrac = 0.02;      // stopping split: where transitions end
     const int nv = wide ? 128 : 64;
     const int64_t bh = B * H, nsl_v = dv / nv, nsl_m = dk / nv;
     const double f = wide ? kWideCost : 1.0;
@@ -2231,12 +2257,31 @@ static double split_cost(int64_t B, int64_t T, int64_t H, int dk, int dv, int re
         const int64_t w1 = bh * (nsl_v * (pe - 1) + nsl_m * (pe - 2)), w3 = bh * nsl_v * (pe - 1);
         return cost + f * (double)(len + kFillTokens) * (double)(rounds(w1) + rounds(w3));
     }
-    double part = kVanishFrac * (double)len;
+    double part = vanish * (double)len;
     if (part < 2.0 * kPipeChunk) part = 2.0 * kPipeChunk;
     if (part > (double)len) part = (double)len;
     const double dseg = f * (double)(len + kFillTokens), dpart = f * (part + (double)kFillTokens);
     return cost + split_phase_time(bh * nsl_v * pe, dseg, bh * nsl_m * (pe - 1), dpart) +
            split_phase_time(bh * nsl_v * (pe - 1), dpart, 0, 0.0);
+}
+
+// A two-segment stopping split is guarded when its cost with transitions
+// that never vanish (the segments' workgroups, then the transitions whole,
+// then the second segment rerun whole) exceeds the best one pass: a probe of
+// the transitions decides on the device between the split and that pass.
+bool seq_split_guarded(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int P,
+                       int wide, int fallback_wide) {
+    if (!seq_split_supported(dk, dv, is_bf16) || P < 2 || seq_split_effective(T, P) != 2) return false;
+    return split_cost(B, T, H, dk, dv, 0, wide != 0, 2, 1.0) >
+           split_cost(B, T, H, dk, dv, 0, fallback_wide != 0, 1);
+}
+
+// Transition chunks a guard's probe runs: the model's vanishing point, at
+// least eight chunks (a transition is seen to vanish up to two chunks
+// before the probe's last).
+static int probe_chunks(int64_t seg_len) {
+    const int64_t n = (int64_t)(kVanishFrac * (double)(seg_len / kPipeChunk)) + 1;
+    return (int)(n < 8 ? 8 : n);
 }
 
 bool seq_wide_supported(int dk, int dv, int is_bf16) {
@@ -2317,7 +2362,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            int split_rerun, int wide, hipStream_t s) {
+                            int split_rerun, int wide, int guarded, int fallback_wide,
+                            hipStream_t s) {
     if (!chunk_fwd_supported(dk, dv, is_bf16)) return hipErrorInvalidValue;
     // bf16 with dk = 128, dv in {64, 128}: the pipelined 32-token kernel
     const bool pipe = seq_split_supported(dk, dv, is_bf16);
@@ -2326,16 +2372,18 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     if (zin && (!pipe || !Ag)) return hipErrorInvalidValue;
     // one workgroup per chain (all 128 columns, the chunk's operands
     // prepared once) or per 64-column slice
-    if (wide && !(pipe && dv == 128 && !pairwise)) return hipErrorInvalidValue;
+    if ((wide || fallback_wide) && !(pipe && dv == 128 && !pairwise)) return hipErrorInvalidValue;
     typedef void (*Kern)(ChunkArgs);
-    Kern kern, kern_tr;                             // kern_tr: a split's first phase
-    if (wide) {
-        kern = zin ? chunk32_kernel<128, true, false, true> : chunk32_kernel<128, false, false, true>;
-        kern_tr = zin ? chunk32_kernel<128, true, true, true> : chunk32_kernel<128, false, true, true>;
-    } else {
-        kern = zin ? chunk32_kernel<128, true, false, false> : chunk32_kernel<128, false, false, false>;
-        kern_tr = zin ? chunk32_kernel<128, true, true, false> : chunk32_kernel<128, false, true, false>;
-    }
+    // kern_tr: a split's first phase (transition columns that may end early)
+    auto pick = [&](bool w, bool tr) -> Kern {
+        if (w) {
+            if (tr) return zin ? chunk32_kernel<128, true, true, true> : chunk32_kernel<128, false, true, true>;
+            return zin ? chunk32_kernel<128, true, false, true> : chunk32_kernel<128, false, false, true>;
+        }
+        if (tr) return zin ? chunk32_kernel<128, true, true, false> : chunk32_kernel<128, false, true, false>;
+        return zin ? chunk32_kernel<128, true, false, false> : chunk32_kernel<128, false, false, false>;
+    };
+    const Kern kern = pick(wide, false), kern_tr = pick(wide, true);
     const int nv = pipe ? (wide ? 128 : 64) : slice_width(dk, dv, is_bf16);
     ChunkArgs args;
     args.q = q; args.k = k; args.v = v; args.g = g; args.beta = beta;
@@ -2346,6 +2394,9 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.seg_len = T; args.phase = 0; args.seg0 = 0; args.nseg = 1; args.nsl_v = args.nslice;
     args.Sin = args.Lb = args.Mb = nullptr;
     args.zc = nullptr;
+    args.probe_chunks = 0;
+    args.guard = nullptr;
+    args.guard_n = args.guard_lim = args.guard_mode = 0;
     args.slots = slots;
     args.n_slots = n_slots;
     args.pairwise = pipe && pairwise ? 1 : 0;
@@ -2354,6 +2405,64 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
     args.Ag = Ag;
     if (cu_seqlens && (!pipe || nseg >= 2)) return hipErrorInvalidValue;
     const int P = pipe ? seq_split_effective(T, nseg) : 1;
+    if (guarded && (P != 2 || split_rerun || !split_ws)) return hipErrorInvalidValue;
+    if (pipe && P >= 2 && guarded) {
+        // Two segments, guarded: (1) the second segment's transitions, at
+        // most a few chunks each, record where they vanished; (2) the split
+        // (both segments, then the second up to that chunk) runs when every
+        // chain's transition vanished there, (3) else one pass in the
+        // fallback layout.  Each launch reads the records and returns at once
+        // when it is not the path taken, so nothing waits on the host.
+        const SplitLayout lay = seq_split_layout(args.nbh, P, dk, dv);
+        float *wsf = static_cast<float *>(split_ws);
+        args.Sin = wsf + lay.sin;
+        args.Lb = wsf + lay.lb;
+        args.Mb = wsf + lay.mb;
+        args.zc = reinterpret_cast<int *>(static_cast<char *>(split_ws) + lay.zc);
+        args.seg_len = seq_split_segment_len(T, P);
+        args.nseg = P;
+        args.phase = 1;
+        args.seg0 = 1;
+        args.nsl_v = 0;
+        args.nslice = dk / nv;
+        args.probe_chunks = probe_chunks(args.seg_len);
+        args.xcd_map = args.nbh % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(kern_tr, dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        args.probe_chunks = 0;
+        args.guard = args.zc;
+        args.guard_n = args.nbh * (dk / 64);
+        // the second segment's last chunk (it may be shorter than the first):
+        // a record there means the transition never vanished before the end
+        args.guard_lim = (int)((T - args.seg_len + kPipeChunk - 1) / kPipeChunk) - 1;
+        args.guard_mode = 1;
+        // the split: both segments' v columns (no transitions: they were the
+        // probe's), then the second segment up to where its transition vanished
+        args.nsl_v = args.nslice = dv / nv;
+        args.seg0 = 0;
+        args.xcd_map = (P * args.nbh) % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(kern, dim3(P * args.nbh * args.nslice), dim3(768), 0, s, args);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        args.phase = 3;
+        args.seg0 = 1;
+        args.xcd_map = args.nbh % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(kern, dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // else: one pass
+        const int nvf = fallback_wide ? 128 : 64;
+        args.guard_mode = 2;
+        args.phase = 0;
+        args.seg0 = 0;
+        args.nseg = 1;
+        args.seg_len = T;
+        args.zc = nullptr;
+        args.Sin = args.Lb = args.Mb = nullptr;
+        args.nsl_v = args.nslice = dv / nvf;
+        args.xcd_map = args.nbh % 8 == 0 ? 1 : 0;
+        hipLaunchKernelGGL(pick(fallback_wide, false), dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
+        return hipGetLastError();
+    }
     if (pipe && P >= 2) {
         if (!split_ws) return hipErrorInvalidValue;
         const SplitLayout lay = seq_split_layout(args.nbh, P, dk, dv);

@@ -24,12 +24,16 @@ hipError_t launch_range_check(const float *g, int64_t B, int64_t T, int64_t H, i
 // z != nullptr: the gate is evaluated inside the kernel from z (input dtype,
 // laid out like k) and the [H, dk] table Ag; g is not read (pipelined path).
 // wide: one workgroup per chain (pipelined path, dv = 128, not pairwise).
+// guarded (two segments, stopping split): a probe of the second segment's
+// transitions picks on the device between the split and one pass in the
+// fallback_wide layout.
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                             const void *beta, const float *S0, float *ST, void *o, int64_t B,
                             int64_t T, int64_t H, int dk, int dv, int is_bf16, int nseg,
                             void *split_ws, const int *slots, int64_t n_slots, int pairwise,
                             const int64_t *cu_seqlens, const void *z, const float *Ag,
-                            int split_rerun, int wide, hipStream_t s);
+                            int split_rerun, int wide, int guarded, int fallback_wide,
+                            hipStream_t s);
 
 // Sequence split of the pipelined chunk path (bf16, dk = 128, dv in {64, 128}).
 bool seq_split_supported(int dk, int dv, int is_bf16);
@@ -49,6 +53,11 @@ bool seq_wide_supported(int dk, int dv, int is_bf16);
 // forced (>= 0), else the cheaper one in the same model.
 int seq_layout(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun, int P,
                int layout);
+// Whether a two-segment stopping split in layout `wide` is guarded against
+// gates that keep memory (its worst case is slower than one pass in
+// fallback_wide), P the requested count.
+bool seq_split_guarded(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int P,
+                       int wide, int fallback_wide);
 // Device bytes the split needs (0 when it does not split).
 size_t seq_split_workspace(int64_t B, int64_t T, int64_t H, int dk, int dv, int nseg);
 
