@@ -7,8 +7,10 @@ A timed step is one pass of the prefill hot path over the synthetic batch
 B4 H32 T32768 d128 bf16 (heads 16..31 with the gate near its floor):
 kda_chunk_fwd_gated (q, k, v, z, A, beta -> o, final state), the gate
 evaluated inside the chunk kernel, in the plan the library picks for these
-sizes (two segments per sequence, one workgroup per chain: two launches of
-chunk32_kernel, the split's first and last phases).  The two-kernel form of the same step
+sizes: two segments per sequence, one workgroup per chain, guarded (four
+launches of chunk32_kernel: a probe of the second segment's transitions, the
+split's first and last phases, and a one-pass launch that returns at once
+when every transition vanished in the probe).  The two-kernel form of the same step
 (kda_gate z -> g, then kda_chunk_fwd) is timed beside it.  The decode step (256 sequences x H32, d128, fp32 state of 512 MiB
 updated in place) is timed in the same run over 1000 consecutive steps with
 fresh pre-generated inputs, and reported in the same JSON line.
@@ -81,32 +83,54 @@ def _matches(name, frags):
     return any(f in name for f in frags)
 
 
-def per_step(named):
-    """[(kernel name, value)] of one kernel group in launch order -> (steps,
-    per-step sums): a step launches each distinct instance of the group once
-    (a split's phases, or the one pass)."""
+def step_groups(named):
+    """[(kernel name, value)] of one kernel group in launch order -> the
+    launches of each step: a step makes the same sequence of launches (one
+    pass; or a guarded split's probe, first phase, last phase and the
+    fallback that returns at once), so the least launched instance appears
+    once per step."""
     names = {}
     for n, _ in named:
         names[n] = names.get(n, 0) + 1
-    k = len(names)
-    steps = max(names.values()) if names else 0
-    if steps * k != len(named):
-        raise SystemExit(f"launches {len(named)} do not form steps of {k} instances: {names}")
-    return steps, [sum(v for _, v in named[i * k:(i + 1) * k]) for i in range(steps)]
+    steps = min(names.values()) if names else 0
+    if steps == 0 or len(named) % steps:
+        raise SystemExit(f"launches {len(named)} do not form steps: {names}")
+    k = len(named) // steps
+    groups = [named[i * k:(i + 1) * k] for i in range(steps)]
+    if any([n for n, _ in g] != [n for n, _ in groups[0]] for g in groups):
+        raise SystemExit(f"the steps do not launch the same sequence: {names}")
+    return groups
+
+
+def per_step(named):
+    """(steps, per-step sums) of step_groups."""
+    groups = step_groups(named)
+    return len(groups), [sum(v for _, v in g) for g in groups]
 
 
 def headline_plan():
-    """(segments, one workgroup per chain) the library picks for the step."""
+    """(segments, one workgroup per chain, guarded) the library picks for the step."""
     w = PREFILL
-    return _lib.kda_chunk_fwd_plan(w.B, w.T, w.H, w.dk, w.dv, _lib.KDA_BF16)
+    return _lib.kda_chunk_fwd_plan(w.B, w.T, w.H, w.dk, w.dv, _lib.KDA_BF16, with_guard=True)
+
+
+def plan_text(P, wide, guarded):
+    lay = "one workgroup per chain" if wide else "64-column slices"
+    if P < 2:
+        return f"one pass, {lay}"
+    if guarded:
+        return (f"{P} segments per sequence, {lay}, guarded: a probe of the second segment's "
+                "transitions, the split's two phases, and a one-pass launch in 64-column slices "
+                "that runs only if some transition had not vanished (it returns at once here)")
+    return f"{P} segments per sequence, {lay}"
 
 
 def headline_main_instance():
     """Name fragments of the step's dominant launch (the split's first phase,
     or the one pass), its v workgroups and their 32-token periods each."""
     w = PREFILL
-    P, wide = headline_plan()
-    tr = P >= 2
+    P, wide, guarded = _lib.kda_chunk_fwd_plan(w.B, w.T, w.H, w.dk, w.dv, _lib.KDA_BF16, with_guard=True)
+    tr = P >= 2 and not guarded        # a guarded split's first phase runs without transitions
     frag = (f"chunk32_kernel<128, true, {str(tr).lower()}, {str(wide).lower()}>",
             f"chunk32_kernelILi128ELb1ELb{int(tr)}ELb{int(wide)}E")
     per = -(-w.T // P)
@@ -300,12 +324,12 @@ def time_prefill_plans(reps=10, warmup=5):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    P, wide = headline_plan()
+    P, wide, guarded = headline_plan()
     out = {"one_pass_slices_ms": timed(x["z"], one)}
     zk = (x["z"].float() - 12.0).to(x["z"].dtype)
     out["gates_keep_memory"] = {"plan_ms": timed(zk, 0), "one_pass_slices_ms": timed(zk, one),
                                 "inputs": "z - 12 everywhere (g about -3e-5 per token)"}
-    out["plan"] = {"segments": P, "workgroup_per_chain": wide}
+    out["plan"] = {"segments": P, "workgroup_per_chain": wide, "guarded": guarded}
     del x, o, ST, ws, zk
     torch.cuda.empty_cache()
     return out
@@ -670,12 +694,11 @@ def ingest_pmc(fetch_dir, write_dir):
     work = prefill_work(w)
     alg = {"fused_fwd": work["fused_bytes"], "chunk_fwd": work["chunk_bytes"],
            "decode_step": decode_bytes(DECODE), "gate": work["gate_bytes"]}
-    P, wide = headline_plan()
+    P, wide, guarded = headline_plan()
     lines = ["# HBM traffic per step (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
              "Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step, then gate + chunk),",
-             f"decode 256x32 d128.  The prefill steps run the library's plan ({P} segment(s), "
-             f"{'one workgroup per chain' if wide else '64-column slices'}); a step's figure",
-             "sums its launches of the kernel (each instance once per step).",
+             f"decode 256x32 d128.  The prefill steps run the library's plan ({plan_text(P, wide, guarded)});",
+             "a step's figure sums its launches of the kernel.",
              "Each counter is scaled by the factor that maps its reading for a plain",
              "1 GiB device copy (torch `copy_` -> the runtime's copyBuffer kernel, timed",
              "in the same script) to 1 GiB.", "",
@@ -763,16 +786,13 @@ def ingest_trace(d):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    P, wide = headline_plan()
+    P, wide, guarded = headline_plan()
     lines = ["# Kernel durations (rocprofv3 kernel trace)", "",
              f"Workloads: prefill B4 H32 T32768 d128 bf16 (the fused step: {TRACE_WARMUP} warm-up "
              f"and {TRACE_STEPS} timed steps; then gate + chunk as two kernels: 2 warm-up and "
              f"{TRACE_STEPS} timed steps), decode 256x32 d128 (20 warm-up + {TRACE_DECODE} steps), "
              "plus the 1 GiB calibration copy.  The prefill steps run the library's plan for "
-             f"these sizes: {P} segment(s) per sequence, "
-             f"{'one workgroup per chain' if wide else 'one workgroup per 64-column slice'}; "
-             "a step launches each instance listed under its kernel once (a split: the first "
-             "phase, then the last).  Durations from the trace's start/end timestamps; "
+             f"these sizes: {plan_text(P, wide, guarded)}.  Durations from the trace's start/end timestamps; "
              "'timed' is the last steps, the ones the benchmark times, and a step's time sums "
              "its launches.", "",
              "Command (from the repository root):", "", "    " + TRACE_CMD,
@@ -796,14 +816,15 @@ def ingest_trace(d):
         n = min(timed_n.get(label, steps), steps)
         timed = us[-n:]
         rec[label] = sum(timed) / len(timed)
-        names = sorted({nm for nm, _ in named})
         lines.append(f"| {label}: {k} instance(s) | {len(named)} | {steps} | {sum(us) / steps:.1f} "
                      f"| {min(us):.1f} | {max(us):.1f} | {n} | {rec[label]:.1f} |")
-        for nm in names:
-            t = [v for x, v in named[-n * k:] if x == nm]
-            inst.append(f"| {label} | `{nm.split('(')[0][:70]}` | {len(t)} | {sum(t) / len(t):.1f} |")
-    lines += ["", "Instances, over the timed steps:", "",
-              "| kernel | instance | timed launches | avg (us) |", "|---|---|---|---|"] + inst
+        groups = step_groups(named)[-n:]
+        for j in range(k):
+            t = [g[j][1] for g in groups]
+            inst.append(f"| {label} | {j + 1} of {k} | `{groups[0][j][0].split('(')[0][:70]}` | "
+                        f"{len(t)} | {sum(t) / len(t):.1f} |")
+    lines += ["", "Launches of a step, over the timed steps:", "",
+              "| kernel | launch | instance | timed launches | avg (us) |", "|---|---|---|---|---|"] + inst
     if "fused_fwd" in rec:
         fb = prefill_work(PREFILL)["fused_bytes"]
         frac = fb / (rec["fused_fwd"] * 1e-6) / 1e9 / HBM_PEAK_GBS
@@ -1012,21 +1033,22 @@ def ingest_sq(dirs):
                 rows = _pmc_rows(d, ctr)
             except SystemExit:
                 continue
-            # the timed dispatches only: the last SQ_STEPS, after the warm-up
-            v = [x for n, x in rows if _matches(n, headline_main_instance()[0])][-SQ_STEPS:]
+            # the timed steps only: the last SQ_STEPS, after the warm-up; of
+            # each step's launches the split's first phase (every counter is
+            # largest there)
+            named = [(n, x) for n, x in rows if _matches(n, KERNELS["fused_fwd"][0])]
+            v = [max(x for _, x in g) for g in step_groups(named)][-SQ_STEPS:] if named else []
             if v:
                 vals[ctr] = sum(v) / len(v)
     frag, wgs, periods = headline_main_instance()
-    P, wide = headline_plan()
+    P, wide, guarded = headline_plan()
     simd_periods = wgs * 4 * periods
     lines = ["# Shader-sequencer counters, chunk32_kernel with the gate fused (rocprofv3 --pmc)", "",
-             f"Workload: prefill B4 H32 T32768 d128 bf16 in the library's plan ({P} segment(s), "
-             f"{'one workgroup per chain' if wide else '64-column slices'}); the counters are those "
-             f"of the step's main launch `{frag[0]}`: {wgs} segment workgroups of 12 waves, "
-             f"{periods} periods of 32 tokens each (the split's transition workgroups, a few "
-             f"periods each, are counted with them but not in the per-period figures' "
-             f"denominator).  Averaged over the {SQ_STEPS} timed dispatches after {SQ_WARMUP} "
-             "warm-up ones.", "",
+             f"Workload: prefill B4 H32 T32768 d128 bf16 in the library's plan ({plan_text(P, wide, guarded)}); "
+             f"the counters are those of the step's main launch `{frag[0]}` (the split's first phase): "
+             f"{wgs} segment workgroups of 12 waves, "
+             f"{periods} periods of 32 tokens each.  Averaged over the {SQ_STEPS} timed steps "
+             f"after {SQ_WARMUP} warm-up ones.", "",
              "Commands (from the repository root):", ""]
     lines += ["    " + sq_cmd(i) for i in range(len(SQ_PASSES))]
     lines += ["    python3 bench.py --ingest-sq " + " ".join(f"gpurun_out/sq{i}" for i in range(len(SQ_PASSES))), "",
@@ -1133,7 +1155,7 @@ def main():
     copy_gbs = time_copy()
     res = time_prefill(args.steps, args.warmup)
     two = time_two_kernel(res["x"], args.steps)
-    P, wide = headline_plan()
+    P, wide, guarded = headline_plan()
     w = PREFILL
     work = prefill_work(w)
     ms_per_step = res["wall_s"] * 1e3 / args.steps
@@ -1178,20 +1200,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": "KDA prefill B4 H32 T32768 d128 bf16, heads 16-31 decay-stress "
                                f"(gate + chunked prefill per step, gate fused; the library's plan: "
-                               f"{P} segment(s) per sequence, "
-                               f"{'one workgroup per chain' if wide else '64-column slices'}); "
+                               f"{plan_text(P, wide, guarded)}); "
                                "decode 256x32 d128 fp32 state",
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "dk": w.dk, "dv": w.dv,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": fused_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": fused_gbs / HBM_PEAK_GBS, "traffic": traffic["fused_fwd"],
-                     "kernel": f"chunk32_kernel<128, true, *, {str(wide).lower()}> (gate fused, "
-                               f"{'one workgroup per chain' if wide else '64-column slices'}; "
-                               f"{P} segment(s): {'the split first and last phases' if P > 1 else 'one launch'})",
+                     "kernel": f"chunk32_kernel<128, true, ...> (gate fused; {plan_text(P, wide, guarded)})",
                      "bytes_per_step": work["fused_bytes"], "avg_ms": fused_s * 1e3,
                      "scope": "the whole step (every launch), HIP events on the launch stream"},
         "prefill": {"fused_ms": fused_s * 1e3,
-                    "plan": {"segments": P, "workgroup_per_chain": wide},
+                    "plan": {"segments": P, "workgroup_per_chain": wide, "guarded": guarded},
                     "other_plans": plans_res,
                     "alg_tflops": fused_tflops,
                     "flops_per_head_token": work["flops_per_head_token"],
