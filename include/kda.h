@@ -218,17 +218,22 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
  *                   required with KDA_FLAG_CHECK_RANGE, explicit segments,
  *                   or fp32 inputs at dk = 128 (per-chunk buffers of the
  *                   fp32 16-token path, about 1.6 KB per token and chain).
- *                   May be NULL otherwise: the call then runs in one pass.
+ *                   May be NULL or smaller otherwise: the library then
+ *                   picks among the segment counts whose buffers fit (one
+ *                   pass when none does).
  * Chunks and 16-token tiles are aligned to token 0 of the call; the last
  * chunk may be partial.  Accumulation and the carried state are fp32.
  *
  * Sequence-parallel path ("Kimi K3 internal structure analysis", section
  * "Infrastructure for a 3T-class MoE": a sequence segment maps an incoming
- * state to an outgoing one).  With few chains (B H dv/64 workgroups below a
- * quarter of the GPU) and long sequences, each sequence is cut into P
- * segments of equal 32-token-aligned length (the count minimises a model of
- * the wall time: rounds of workgroups per launch times the segment length,
- * plus the chaining steps).  The recurrence is affine in the
+ * state to an outgoing one).  When the chains alone do not fill the GPU
+ * (bf16, dk = 128, dv in {64, 128}), each sequence is cut into P segments of
+ * equal 32-token-aligned length; the count and the workgroup layout (one
+ * workgroup per chain or per 64-column slice, see
+ * KDA_FLAG_WORKGROUP_PER_CHAIN) minimise a model of the wall time: rounds of
+ * workgroups per launch times the segment length, plus the chaining steps,
+ * with the transitions priced as vanishing 2% of the way into a segment
+ * (kda_chunk_fwd_plan reports the choice).  The recurrence is affine in the
  * state, S_end = M S_start + L, so three stream-ordered launches give the
  * same result as one pass up to fp32 rounding:
  *   1. segment 0 from initial_state (its o is final); every other segment
@@ -246,8 +251,17 @@ size_t kda_chunk_fwd_workspace_size_segments(int64_t B, int64_t T, int64_t H,
  * and leaves the last segment out of step 1).  The outputs computed in
  * step 3 and those kept from step 1 each agree with one pass to fp32
  * rounding.  The library picks P; KDA_FLAG_SEGMENTS(n) forces it (tests).
- * The split uses the workspace; without one large enough, the automatic
- * choice falls back to one pass.  Non-finite inputs stay in their chain in
+ * Where the library's choice is two segments and one pass would be faster
+ * if no transition vanished (chains enough to fill the GPU in one pass of
+ * 64-column slices), the split is guarded: a first launch runs each chain's
+ * second-segment transition for a few chunks (2% of the segment, at least
+ * eight) and records where it vanished; the split's launches run only if
+ * every chain's did, else a one-pass launch runs; each launch reads the
+ * records and returns at once when it is not the path taken, so the choice
+ * needs no host synchronisation.  The result is then bit-identical to the
+ * forced split or to the forced one pass.  The split uses the workspace; the
+ * automatic choice takes the best count whose buffers fit in it (one pass
+ * when none does).  Non-finite inputs stay in their chain in
  * every path; inside it, one pass carries a NaN or Inf in the state to the
  * end, while the stopping split applies a transition found exactly zero as
  * zero (it takes L for M S + L and keeps the zero-start outputs), so the
@@ -294,9 +308,9 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void 
  *  - What the scratch holds: the sequence split's per-segment states and
  *    transitions (bf16, dk = 128, dv in {64, 128}), or the staged g
  *    (B*T*H*dk*4 bytes) of shapes without the fused gate.
- *  - Sizes: the automatic segment count is taken only when its buffers fit
- *    (else one pass, as kda_chunk_fwd_gated does with a workspace too small
- *    for the split).  An explicit KDA_FLAG_SEGMENTS(n), or a staged g, that
+ *  - Sizes: the automatic segment count is the best whose buffers fit in the
+ *    array (one pass when none does, as kda_chunk_fwd_gated chooses within a
+ *    smaller workspace).  An explicit KDA_FLAG_SEGMENTS(n), or a staged g, that
  *    needs more than the array returns KDA_ERR_INVALID_ARGUMENT before any
  *    launch; kda_last_error() gives the bytes needed.
  *  - No call allocates or frees device memory, and no part of the array has

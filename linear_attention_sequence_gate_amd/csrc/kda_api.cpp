@@ -371,8 +371,8 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
         return ok();
     }
-    // sequence split: requested, or picked for these sizes when the workspace
-    // holds its buffers (else one pass)
+    // sequence split: requested, or picked for these sizes among the counts
+    // whose buffers the workspace holds (none: one pass)
     const int rerun = (flags & KDA_FLAG_SPLIT_FULL_RERUN) ? 1 : 0;
     // workgroup layout: forced by a flag (the position-pair path runs per
     // slice), else chosen with the segment count
@@ -387,7 +387,9 @@ int chunk_fwd_impl(const char *who, const void *q, const void *k, const void *v,
         } else if (req_seg >= 2) {
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: a %d-segment split needs a workspace of %zu bytes", who, nseg, need);
         } else {
-            nseg = 1;
+            const size_t cap = workspace && workspace_bytes > kCounterBytes ? workspace_bytes - kCounterBytes : 0;
+            nseg = kda::seq_split_auto(B, T, H, (int)dk, (int)dv, is_bf16, rerun, layout, cap);
+            if (nseg >= 2) split_ws = static_cast<char *>(workspace) + kCounterBytes;
         }
     }
     const int wide = kda::seq_layout(B, T, H, (int)dk, (int)dv, is_bf16, rerun, nseg, layout);

@@ -2298,9 +2298,10 @@ int seq_layout(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int
 }
 
 // The count minimising the model over the layouts allowed (a split must
-// beat the best one pass by 10%).
+// beat the best one pass by 10%), among those whose buffers fit in ws_cap
+// bytes.
 int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun,
-                   int layout) {
+                   int layout, size_t ws_cap) {
     constexpr int64_t kMinSegTokens = 128;    // four 32-token chunks
     if (!seq_split_supported(dk, dv, is_bf16)) return 1;
     const bool can_wide = seq_wide_supported(dk, dv, is_bf16);
@@ -2321,6 +2322,7 @@ int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16,
     for (int P = rerun ? 3 : 2; P <= pmax; ++P) {
         const int64_t pe = seq_split_effective(T, P);
         if (pe < (rerun ? 3 : 2)) continue;
+        if (seq_split_workspace(B, T, H, dk, dv, P) > ws_cap) continue;
         const double cost = best_of(P);
         if (cost < best) {
             best = cost;

@@ -44,9 +44,9 @@ int seq_split_effective(int64_t T, int nseg);
 // Segment count picked for these sizes (1 = no split), for the stopping
 // split or (rerun) the one whose last phase reruns whole segments, over the
 // workgroup layouts allowed (layout: -1 either, 0 per 64-column slice, 1 per
-// chain).
+// chain) and the counts whose buffers fit in ws_cap bytes.
 int seq_split_auto(int64_t B, int64_t T, int64_t H, int dk, int dv, int is_bf16, int rerun,
-                   int layout);
+                   int layout, size_t ws_cap = SIZE_MAX);
 // One workgroup per chain: bf16, dk = dv = 128.
 bool seq_wide_supported(int dk, int dv, int is_bf16);
 // The layout (0 per slice, 1 per chain) for P segments: `layout` when it is

@@ -166,3 +166,26 @@ def test_split_transitions_that_end_early_and_that_run_on(nseg):
         assert torch.isfinite(o_s.float()).all() and torch.isfinite(S_s).all()
         assert ro <= TOL[BF16] and rs <= TOL[BF16], (name, ro, rs)
         assert r1o <= TOL[BF16] and r1s <= TOL[BF16], (name, r1o, r1s)
+
+
+def test_automatic_count_within_a_smaller_workspace():
+    """B1 H4 T40000 with a workspace sized for eight segments (the library
+    would pick more): the call takes the best count whose buffers fit, and
+    its result is within the bar of the oracle (two heads checked)."""
+    say("split within a capped workspace")
+    B, T, H = 1, 40000, 4
+    x = prefill_device(B, T, H, 128, 128, torch.bfloat16, 7100, s0_std=0.1)
+    P_free = _lib.kda_chunk_fwd_auto_segments(B, T, H, 128, 128, _lib.KDA_BF16)
+    small = _lib.kda_chunk_fwd_workspace_size(B, T, H, 128, 128, _lib.KDA_BF16, 8)
+    assert P_free > 8 and small < _lib.kda_chunk_fwd_workspace_size(B, T, H, 128, 128, _lib.KDA_BF16)
+    ws = torch.empty(small, device="cuda", dtype=torch.uint8)
+    o, S = kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    for h in (0, 3):
+        xs = {n: x[n][:, :, h:h + 1].contiguous() for n in ("q", "k", "v", "z", "beta")}
+        g_ref = oracle.gate(xs["z"], x["A"][h:h + 1].contiguous())
+        o_ref, S_ref = oracle.forward(xs["q"], xs["k"], xs["v"], g_ref, xs["beta"],
+                                      x["S0"][:, h:h + 1].contiguous())
+        ro, rs = rho(o[:, :, h:h + 1], o_ref), rho(S[:, h:h + 1], S_ref)
+        print(f"    head {h}: rho(o)={ro:.3e} rho(S)={rs:.3e}", flush=True)
+        assert ro <= TOL[torch.bfloat16] and rs <= TOL[torch.bfloat16], (h, ro, rs)
