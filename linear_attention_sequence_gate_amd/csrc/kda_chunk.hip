@@ -1554,6 +1554,10 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
         // state role: column block s of the slice, chunk c - 1 in period c
         // =================================================================
         const int s = wave;
+        // per chain: the second state wave of each SIMD (the youngest two
+        // waves there are it and the prep wave, which runs at priority 1)
+        // issues beside the prep wave instead of after the older state wave
+        if (WIDE && s >= 4) __builtin_amdgcn_s_setprio(1);
         // this block's state endpoints and output (uniform): the initial
         // state is read from s0 (zero when null) or is the identity, the
         // final one goes to st (row pitch spitch) when st is set, and o is
@@ -2414,7 +2418,11 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         // (both segments, then the second up to that chunk) runs when every
         // chain's transition vanished there, (3) else one pass in the
         // fallback layout.  Each launch reads the records and returns at once
-        // when it is not the path taken, so nothing waits on the host.
+        // when it is not the path taken, so nothing waits on the host.  The
+        // two short launches (the probe, the second segment's first chunks)
+        // run in 64-column slices: twice the workgroups at a shorter period,
+        // and the probe's zero posts come one period earlier; every column's
+        // arithmetic is the same in both layouts.
         const SplitLayout lay = seq_split_layout(args.nbh, P, dk, dv);
         float *wsf = static_cast<float *>(split_ws);
         args.Sin = wsf + lay.sin;
@@ -2426,10 +2434,10 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         args.phase = 1;
         args.seg0 = 1;
         args.nsl_v = 0;
-        args.nslice = dk / nv;
+        args.nslice = dk / 64;
         args.probe_chunks = probe_chunks(args.seg_len);
         args.xcd_map = args.nbh % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(kern_tr, dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(pick(false, true), dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         args.probe_chunks = 0;
@@ -2448,8 +2456,9 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const f
         if ((e = hipGetLastError()) != hipSuccess) return e;
         args.phase = 3;
         args.seg0 = 1;
+        args.nsl_v = args.nslice = dv / 64;
         args.xcd_map = args.nbh % 8 == 0 ? 1 : 0;
-        hipLaunchKernelGGL(kern, dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
+        hipLaunchKernelGGL(pick(false, false), dim3(args.nbh * args.nslice), dim3(768), 0, s, args);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // else: one pass
         const int nvf = fallback_wide ? 128 : 64;
