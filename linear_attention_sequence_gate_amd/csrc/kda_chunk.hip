@@ -1397,6 +1397,9 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 if (c + 2 < nchunk) load_raw(c + 2, raw);   // used two periods from now
             }
             lds_barrier();                                  // BAR1
+            // per chain, second half: the score tiles and handoff rows come
+            // first; the state waves' deferred updates have slack there
+            if (WIDE) __builtin_amdgcn_s_setprio(2);
             Posts posts = 0;
             if constexpr (TRANS) posts = *reinterpret_cast<const Posts *>(zpost);
 
@@ -1538,6 +1541,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
                 }
             }
             lds_barrier();                                  // BAR2
+            if (WIDE) __builtin_amdgcn_s_setprio(1);
             if constexpr (TRANS) return all_zero(posts);
             else return false;
         };
@@ -1781,6 +1785,9 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             }
             if (TRANS && !WIDE && vzero) post_zero();
             lds_barrier();                                  // BAR1
+            // per chain, second half: the prep waves' score tiles end it, so
+            // the deferred state updates give them the issue slots
+            if (WIDE && s >= 4) __builtin_amdgcn_s_setprio(0);
             Posts posts = 0;
             if constexpr (TRANS) posts = *reinterpret_cast<const Posts *>(zpost);
             if (s == 3 && c >= 1 && c - 1 < nchunk) {
@@ -1850,6 +1857,7 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
             if (defer && pass) s_update(uh_d, c - 2);
             if (pw) lds_barrier();                          // position-pair path: partials complete
             lds_barrier();                                  // BAR2
+            if (WIDE && s >= 4) __builtin_amdgcn_s_setprio(1);
             if constexpr (TRANS) return all_zero(posts);
             else return false;
         };
