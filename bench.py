@@ -734,7 +734,9 @@ EXTRA_TRACES = {
              "kda_chunk_fwd_gated (the gate fused into the chunk kernel) on B1 H32 T1048576 "
              "d128 bf16 in one pass (64-column slices; 1 warm-up + 3 timed calls), with the "
              "library's sequence split (the same; P = 8, one workgroup per chain), and with "
-             "KDA_FLAG_SPLIT_FULL_RERUN (the same; P = 9, one workgroup per chain). A split call "
+             "KDA_FLAG_SPLIT_FULL_RERUN (the same; P = 9, one workgroup per chain). The stopping "
+             "split's segment workgroups fill the GPU, so its transitions run first in a launch of "
+             "their own (64-column slices); otherwise a split call "
              "is three launches: chunk32_kernel phase 1 (the segments "
              "from their start states, the transitions of segments 1..P-1; the full rerun "
              "leaves the last segment out), seg_chain_kernel, and chunk32_kernel phase 3 "
@@ -872,16 +874,18 @@ def ingest_trace_extra(name, d):
         if name == "pairwise" and r in chunk_rows:
             label = "dense" if chunk_rows.index(r) < len(chunk_rows) // 2 else "position pairs"
         if name == "long":
-            # one pass first (the first launch's grid), then the two split
-            # schemes with the same number of launches each
+            # one pass first (the first launch's grid), then the stopping
+            # split's calls, then the full rerun's, whose first phase is the
+            # only launch of the per-chain instance with transition columns
             first = int(chunk_rows[0]["Grid_Size_X"])
             split_rows = [x for x in rows if int(x["Grid_Size_X"]) != first
                           or "chunk32_kernel" not in x["Kernel_Name"]]
+            rr = next((i for i, x in enumerate(split_rows)
+                       if "chunk32_kernel<128, true, true, true>" in x["Kernel_Name"]), len(split_rows))
             if r not in split_rows:
                 label = "one pass"
             else:
-                label = ("stopping split" if split_rows.index(r) < len(split_rows) // 2
-                         else "full rerun")
+                label = "stopping split" if split_rows.index(r) < rr else "full rerun"
         if name == "backward" and "cb_" in kname:
             # the chunked path's launches belong to the call (whole sequence or
             # one segment) whose prep launch, with one workgroup per chunk,

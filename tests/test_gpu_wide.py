@@ -159,3 +159,29 @@ def test_library_plan_at_the_benchmark_size():
                                  flags=seg(P) | (CH if wide else SL))
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(S0, S1)
+
+
+@pytest.mark.parametrize("P", [2, 3])
+def test_split_filling_the_gpu_bit_identical(P):
+    """A split whose segment workgroups alone fill the GPU runs its
+    transitions in a launch of their own before the segments: both layouts
+    still agree bit for bit, and with the oracle on sampled chains."""
+    say("wide split filling the GPU", P)
+    B, T, H = 4, 1500, 32                           # 128 chains: P x 128 or P x 256 workgroups
+    x = inputs.make_prefill_inputs(B, T, H, 128, 128, BF16, 1800 + P, device="cuda", s0_std=0.1,
+                                   stress_heads_mean=3.0)
+    z = x["z"].float()
+    z[:, :, 5] -= 12.0                              # head 5 keeps memory in every sequence
+    x["z"] = z.to(BF16)
+
+    def run(lay):
+        return kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["z"], x["A"], x["beta"], x["S0"],
+                                   flags=lay | seg(P))
+    o, S = _both(run)
+    for b, h in ((0, 5), (3, 0), (2, 17)):
+        xs = {n: x[n][b:b + 1, :, h:h + 1].contiguous() for n in ("q", "k", "v", "z", "beta")}
+        g_ref = oracle.gate(xs["z"], x["A"][h:h + 1].contiguous())
+        o_ref, S_ref = oracle.forward(xs["q"], xs["k"], xs["v"], g_ref, xs["beta"],
+                                      x["S0"][b:b + 1, h:h + 1].contiguous())
+        ro, rs = rho(o[b:b + 1, :, h:h + 1], o_ref), rho(S[b:b + 1, h:h + 1], S_ref)
+        assert ro <= TOL[BF16] and rs <= TOL[BF16], (b, h, ro, rs)
