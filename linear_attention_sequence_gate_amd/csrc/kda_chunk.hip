@@ -1053,7 +1053,15 @@ __global__ __launch_bounds__(768, 1) void chunk32_kernel(ChunkArgs a) {
     const int H = a.H, DV = a.DV;
     const int b = bh / H, h = bh % H;
     const int64_t urow = user_state_row(a, b, h);   // row in the caller's S0 / ST
-    if (urow < 0) return;                           // slot outside the pool: skipped
+    if (urow < 0) {
+        // slot outside the pool: skipped.  Its transition records read as
+        // vanished, so a guard decides on the sequences the call computes
+        // and reads no word this call did not write.
+        if (TRANS && a.phase == 1 && a.zc && mcols && tid == 0)
+            for (int j = 0; j < NZC; ++j)
+                a.zc[((size_t)(seg - 1) * a.nbh + bh) * NZR + (slice - a.nsl_v) * NZC + j] = -1;
+        return;
+    }
     // this sequence's first token row in memory and its length (packed
     // offsets are clamped to the a.T rows that exist)
     int64_t tok_base = (int64_t)b * a.T, T_ = a.T;

@@ -477,3 +477,30 @@ def test_chunk_plan(L):
         plan(1, 64, 1, 32, 32, 1, seg(3))
     with pytest.raises(_lib.KdaError):
         plan(0, 64, 1, 128, 128, 1)
+
+
+def test_plan_and_workspace_agree_over_sizes(L):
+    """Over a grid of sizes, for the library's choice, each layout flag and
+    each split scheme: the plan's count is the automatic count, the
+    library's workspace holds the buffers of whatever count a flag set
+    leaves to the library, only a two-segment stopping split is guarded, and
+    the per-chain layout appears only where it is supported (host only)."""
+    E = _lib
+    CH, SL, RR = E.KDA_FLAG_WORKGROUP_PER_CHAIN, E.KDA_FLAG_WORKGROUP_PER_SLICE, E.KDA_FLAG_SPLIT_FULL_RERUN
+    for B in (1, 2, 4, 8, 16):
+        for H in (1, 8, 32):
+            for T in (64, 1000, 4096, 32768, 1 << 20):
+                for dv in (64, 128):
+                    if B * H * T > (1 << 24) * 4:
+                        continue
+                    ws = L.kda_chunk_fwd_workspace_size(B, T, H, 128, dv, 1)
+                    P0 = L.kda_chunk_fwd_auto_segments(B, T, H, 128, dv, 1)
+                    for fl in (0, RR, SL, SL | RR) + ((CH, CH | RR) if dv == 128 else ()):
+                        P, wide, guarded = E.kda_chunk_fwd_plan(B, T, H, 128, dv, 1, fl, with_guard=True)
+                        if fl == 0:
+                            assert P == P0, (B, T, H, dv)
+                        assert 1 <= P <= 255
+                        assert not wide or dv == 128
+                        assert not guarded or (P == 2 and not fl & RR), (B, T, H, dv, fl)
+                        need = L.kda_chunk_fwd_workspace_size_segments(B, T, H, 128, dv, 1, P)
+                        assert need <= ws, (B, T, H, dv, fl, P, need, ws)

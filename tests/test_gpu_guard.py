@@ -143,3 +143,28 @@ def test_guard_against_the_oracle():
             rs = rho(S[b:b + 1, h:h + 1], S_ref)
             assert ro <= TOL[BF16] and rs <= TOL[BF16], (case, b, h, ro, rs)
         print(f"    {case}: 16 chains within the bar", flush=True)
+
+
+def test_guard_with_a_skipped_slot():
+    """A pooled call at a guarded size whose last sequence's slot lies outside
+    the pool: the skipped sequence's transition records read as vanished, so
+    the call equals the forced split on the same pool bit for bit, and the
+    other slots are untouched."""
+    from linear_attention_sequence_gate_amd import kda_chunk_fwd_pooled
+    say("guard, pooled with a skipped slot")
+    x = _inputs(2500)
+    g = kda_gate(x["z"], x["A"])
+    n_slots = B + 2
+    gen = torch.Generator(device="cuda").manual_seed(2501)
+    pool0 = torch.randn(n_slots, H, 128, 128, device="cuda", generator=gen) * 0.1
+    slots = torch.tensor(list(range(2, B + 1)) + [-7], dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fl in (("plan", 0), ("split", CH | seg(2))):
+        pool = pool0.clone()
+        o = torch.full((B, T, H, 128), 3.0, device="cuda", dtype=BF16)
+        kda_chunk_fwd_pooled(x["q"], x["k"], x["v"], g, x["beta"], pool, slots, o=o, flags=fl)
+        torch.cuda.synchronize()
+        out[name] = (o, pool)
+    assert torch.equal(out["plan"][0], out["split"][0]) and torch.equal(out["plan"][1], out["split"][1])
+    assert (out["plan"][0][B - 1] == 3.0).all()
+    assert torch.equal(out["plan"][1][[0, 1]], pool0[[0, 1]])
