@@ -1109,7 +1109,8 @@ def ingest_sq(dirs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    # as many timed steps as the committed kernel trace takes (TRACE_STEPS)
+    ap.add_argument("--steps", type=int, default=20)
     # the first ~10 launches of a fresh process run up to 30% slower (clocks
     # ramping; visible in a kernel trace), so the default warm-up covers them
     ap.add_argument("--warmup", type=int, default=20)
