@@ -168,3 +168,28 @@ def test_guard_with_a_skipped_slot():
     assert torch.equal(out["plan"][0], out["split"][0]) and torch.equal(out["plan"][1], out["split"][1])
     assert (out["plan"][0][B - 1] == 3.0).all()
     assert torch.equal(out["plan"][1][[0, 1]], pool0[[0, 1]])
+
+
+@pytest.mark.parametrize("case", ["vanishing", "one_chain_keeps_memory"])
+def test_guard_at_dv64(case):
+    """dv = 64 (64-column slices only): the guarded split and its one-pass
+    fallback run in that layout; bit-equal to the forced split or the forced
+    one pass, and within the bar of the oracle on sampled chains."""
+    say("guard dv=64", case)
+    assert _lib.kda_chunk_fwd_plan(B, T, H, 128, 64, _lib.KDA_BF16, with_guard=True) == (2, False, True)
+    x = inputs.make_prefill_inputs(B, T, H, 128, 64, BF16, 2600, device="cuda", s0_std=0.1,
+                                   stress_heads_mean=3.0)
+    if case != "vanishing":
+        x = _keep_memory(x, [(9, 3)])
+    got = _run(x, 0)
+    ref = _run(x, seg(2)) if case == "vanishing" else _run(x, seg(1))
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), case
+    o, S = got
+    for b, h in ((9, 3), (0, 0), (15, 7)):
+        xs = {n: x[n][b:b + 1, :, h:h + 1].contiguous() for n in ("q", "k", "v", "z", "beta")}
+        g_ref = oracle.gate(xs["z"], x["A"][h:h + 1].contiguous())
+        o_ref, S_ref = oracle.forward(xs["q"], xs["k"], xs["v"], g_ref, xs["beta"],
+                                      x["S0"][b:b + 1, h:h + 1].contiguous())
+        ro, rs = rho(o[b:b + 1, :, h:h + 1], o_ref), rho(S[b:b + 1, h:h + 1], S_ref)
+        assert ro <= TOL[BF16] and rs <= TOL[BF16], (case, b, h, ro, rs)
